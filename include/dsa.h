@@ -1,0 +1,186 @@
+/*
+ * dsa.h - C ABI of the DeepSeek sparse-attention (DSA / CSA) hot path on MI355X (gfx950).
+ *
+ * The path has three steps, each a call below, plus a fused driver:
+ *   1. indexer_scores    lightning-indexer score of every query against every visible key
+ *   2. topk_select       per-query top-k of those scores
+ *   3. sparse_mla_attend MQA-mode latent attention over the selected entries (+ raw window)
+ *   0. kv_compress_mean  optional CSA step: mean-pool every m raw KV rows into one entry
+ *   *  dsa_forward       0 -> 1 -> 2 -> 3 on one stream, with scores/idx kept in a workspace
+ *
+ * Sources (web pages on the method; no code exists on them):
+ *   [P5] "DeepSeek-V3.2 sparse-attention principle and TPU adaptation" (trdm.cn news 392380):
+ *        s1.3 (lightning indexer; fine-grained sparse attention), s1.4 (MQA mode of MLA),
+ *        s3 steps 2-4 (mqa logits -> top-k with the keep-all rule -> sparse MLA with index_mask).
+ *   [P1] xhh.club "sparse" tag feed, DeepSeek-V4 CSA summary (4:1 compression, top-1024 blocks,
+ *        64-head x 128-dim ReLU-weighted FP4 indexer).
+ *   [P4] Tencent Cloud developer search "compressed sparse attention (CSA)": compress -> index
+ *        select -> core attention; window KV concatenated with compressed KV; average pooling.
+ * The page's own index-score formula image is lost; the score used here is
+ *   I[t,s] = sum_j w[t,j] * ReLU(q_I[t,j,:] . k_I[s,:]).
+ *
+ * Conventions shared by every call
+ *   - Every data pointer is a DEVICE pointer owned by the caller, contiguous row-major, 16-byte
+ *     aligned. The library never allocates, frees or synchronises and keeps no state between
+ *     calls except a per-device "is this gfx950" cache. Scratch memory comes from the caller
+ *     (`ws`, sized by dsa_workspace_bytes).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is asynchronous.
+ *   - Arguments are validated on the host before anything is launched; on any error nothing is
+ *     launched and the status says why. Device faults surface at the caller's next sync.
+ *   - Causality is expressed only through q_pos[B,T] (int32, raw 0-indexed position of each
+ *     query token): entry s (token, or block of m tokens) is visible iff s < n_vis with
+ *         n_vis = min(N, floor((q_pos + 1) / m)),
+ *     i.e. a query sees itself (m == 1) and only complete blocks (m > 1).
+ *   - Shapes use dsa_dims below. Value vectors are the first D_V columns of the key row
+ *     (MQA-mode MLA: one latent row per entry shared by all H query heads, [P5] s1.4).
+ *   - Thread safety: calls may run concurrently on different streams.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,      /* a required pointer is NULL                                   */
+  DSA_ERR_SHAPE = 2,     /* a dimension is out of range or inconsistent                  */
+  DSA_ERR_DTYPE = 3,     /* unsupported dtype or dtype combination                       */
+  DSA_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                             */
+  DSA_ERR_WORKSPACE = 5, /* workspace NULL or smaller than dsa_workspace_bytes           */
+  DSA_ERR_DEVICE = 6,    /* current HIP device is not gfx950, or the device query failed */
+  DSA_ERR_LAUNCH = 7     /* a kernel launch reported an error                            */
+} dsa_status;
+
+typedef enum dsa_dtype {
+  DSA_F32 = 0,   /* IEEE binary32                                                         */
+  DSA_BF16 = 1,  /* bfloat16 (upper half of binary32)                                     */
+  DSA_MXFP4 = 2  /* OCP MX FP4: e2m1 codes, two per byte, LOW nibble = even element;
+                    one E8M0 scale byte (2^(e-127)) per 32 consecutive elements.
+                    Only for k_I.                                                        */
+} dsa_dtype;
+
+typedef struct dsa_dims {
+  int32_t B;     /* sequences                                                          */
+  int32_t T;     /* query tokens per sequence                                          */
+  int32_t N;     /* key entries per sequence: tokens (m == 1) or compressed blocks     */
+  int32_t H_I;   /* indexer heads (64)                                                 */
+  int32_t D_I;   /* indexer head dim (128)                                             */
+  int32_t H;     /* attention query heads (128)                                        */
+  int32_t D_K;   /* shared key dim: latent + rope (576)                                */
+  int32_t D_V;   /* value dim = first D_V columns of the key row (512)                 */
+  int32_t top_k; /* entries kept per query (2048 tokens / 1024 blocks)                 */
+  int32_t m;     /* compression ratio: 1 = DSA over tokens, >1 = CSA over blocks       */
+  int32_t W;     /* raw sliding window length for CSA (0 = none)                       */
+} dsa_dims;
+
+/* Limits checked by every call. */
+#define DSA_MAX_TOPK 4096
+#define DSA_MAX_DK 1024
+
+/* Workspace query ops. */
+#define DSA_OP_TOPK 1
+#define DSA_OP_ATTEND 2
+#define DSA_OP_FORWARD 3
+
+/* Human-readable name of a status code; never NULL. */
+const char* dsa_status_str(int status);
+
+/* ABI version (major * 100 + minor). */
+int dsa_version(void);
+
+/* Bytes of device workspace `op` needs for these dims (0 = none; a NULL ws is then fine).
+ * Returns 0 for invalid dims as well; the call itself then reports the error. */
+size_t dsa_workspace_bytes(const dsa_dims* d, int op);
+
+/* Step 0 - CSA token-dimension compression ([P1]; [P4] "compress each m consecutive tokens'
+ * KV into one entry, e.g. by average pooling").
+ *   kv_c[b, j, :] = (1/m) * sum_{i<m} kv_raw[b, m*j + i, :],   j < floor(n_raw / m)
+ * kv_raw: [B, n_raw, D_K] of dtype dt (F32 or BF16); kv_c: [B, floor(n_raw/m), D_K], same dtype.
+ * Summation in fp32, one final rounding (RNE) to dt. Uses d->B, d->D_K, d->m (>= 1). */
+dsa_status kv_compress_mean(const dsa_dims* d, dsa_dtype dt, const void* kv_raw, int64_t n_raw,
+                            void* kv_c, void* stream);
+
+/* Step 1 - lightning-indexer scores ([P5] s1.3 "lightning indexer"; s3 step 2 "mqa logits").
+ *   scores[b,t,s] = sum_{j<H_I} w[b,t,j] * max(0, sum_{d<D_I} q_I[b,t,j,d] * k_I[b,s,d])
+ *                   for s < n_vis(b,t);   -inf for n_vis <= s < N.
+ * q_I:    [B,T,H_I,D_I], dtype q_dt (F32 or BF16)
+ * w:      [B,T,H_I] fp32 (any sign)
+ * k_I:    [B,N,D_I] of dtype k_dt (== q_dt), or for k_dt == MXFP4 codes [B,N,D_I/2] bytes
+ * k_scale:[B,N,D_I/32] E8M0 bytes when k_dt == MXFP4, else must be NULL
+ * q_pos:  [B,T] int32
+ * scores: [B,T,N] fp32 (written in full)
+ * Products are exact (bf16 x bf16 or dequantised FP4 x bf16), accumulation fp32. */
+dsa_status indexer_scores(const dsa_dims* d, const void* q_I, dsa_dtype q_dt, const float* w,
+                          const void* k_I, const uint8_t* k_scale, dsa_dtype k_dt,
+                          const int32_t* q_pos, float* scores, void* stream);
+
+/* Step 2 - per-query top-k ([P5] s1.3 "keep only the KV of the top-k index scores"; s3 step 3:
+ * keep every token when the context is no longer than k; index_mask of step 4).
+ *   n = n_vis(b,t). If n <= top_k: idx[b,t,0..n) = 0..n-1 (ascending).
+ *   Else: idx[b,t,:] = the top_k entries s < n with the largest scores, ties broken toward the
+ *   LOWER index (the result is the first top_k of a stable sort by descending score); the
+ *   order inside the row is unspecified.
+ *   Slots past the selected count are -1. -0.0 ranks equal to +0.0. Scores must not be NaN.
+ * scores: [B,T,N] fp32 (entries s >= n_vis are ignored); idx: [B,T,top_k] int32.
+ * ws: dsa_workspace_bytes(d, DSA_OP_TOPK) bytes (may be 0). */
+dsa_status topk_select(const dsa_dims* d, const float* scores, const int32_t* q_pos,
+                       int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 3 - sparse MQA-mode MLA attention ([P5] s1.3 "fine-grained sparse attention", s1.4,
+ * s3 step 4; [P4] window KV concatenated with the compressed KV into one core attention).
+ * For each (b,t,h) the entry set is
+ *   E = { kv[b, idx[b,t,i], :] : idx[b,t,i] >= 0 }                       (i < top_k)
+ *     u { kv_raw[b, r - raw_base, :] : max(0, p-W+1) <= r <= p,
+ *                                      raw_base <= r < raw_base + n_raw } (p = q_pos[b,t])
+ * one joint softmax over E (no de-duplication):
+ *   z_e = softmax_scale * q[b,t,h,:D_K] . K_e[:D_K];  out[b,t,h,:] = sum_e softmax(z)_e K_e[:D_V]
+ *   lse[b,t,h] = log sum_e exp(z_e).  Empty E: out = 0, lse = -inf.
+ * q: [B,T,H,D_K], kv: [B,N,D_K], kv_raw: [B,n_raw,D_K] (NULL iff W == 0), out: [B,T,H,D_V],
+ * all of dtype dt (F32 or BF16); lse: [B,T,H] fp32 or NULL. idx values must be < N.
+ * bf16: MFMA products, fp32 accumulation, online softmax, out rounded RNE.
+ * ws: dsa_workspace_bytes(d, DSA_OP_ATTEND) bytes (split partials for few-query calls). */
+dsa_status sparse_mla_attend(const dsa_dims* d, dsa_dtype dt, const void* q, const void* kv,
+                             const int32_t* idx, const void* kv_raw, int64_t raw_base,
+                             int64_t n_raw, const int32_t* q_pos, float softmax_scale,
+                             void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Arguments of dsa_forward (pointers as in the calls above). */
+typedef struct dsa_forward_args {
+  dsa_dtype dt;          /* dtype of q_I, q, kv, kv_raw, out: F32 or BF16                 */
+  dsa_dtype k_dt;        /* dtype of k_I: == dt, or MXFP4 (with dt == BF16)               */
+  const void* q_I;       /* [B,T,H_I,D_I]                                                 */
+  const float* w;        /* [B,T,H_I]                                                     */
+  const void* k_I;       /* [B,N,D_I] or MXFP4 codes [B,N,D_I/2]                          */
+  const uint8_t* k_scale;/* [B,N,D_I/32] for MXFP4, else NULL                             */
+  const void* q;         /* [B,T,H,D_K]                                                   */
+  void* kv;              /* [B,N,D_K]; written first when compress != 0                   */
+  const void* kv_raw;    /* [B,n_raw,D_K] raw rows at positions raw_base..; NULL if unused */
+  int64_t raw_base;
+  int64_t n_raw;
+  int32_t compress;      /* != 0: kv = kv_compress_mean(kv_raw) (needs raw_base == 0 and
+                            floor(n_raw / m) == N)                                       */
+  const int32_t* q_pos;  /* [B,T]                                                         */
+  float softmax_scale;
+  void* out;             /* [B,T,H,D_V]                                                   */
+  float* lse;            /* [B,T,H] or NULL                                               */
+  float* scores;         /* [B,T,N] or NULL (then scores live in ws, masked tail unwritten)*/
+  int32_t* idx;          /* [B,T,top_k] or NULL (then idx lives in ws)                    */
+} dsa_forward_args;
+
+/* Fused path: [compress] -> indexer_scores -> topk_select -> sparse_mla_attend on `stream`
+ * ([P5] key takeaways: light pre-scoring -> top-k sparse selection -> sparse MLA).
+ * When a->scores is NULL, queries are processed in chunks whose scores fit the workspace.
+ * ws: dsa_workspace_bytes(d, DSA_OP_FORWARD) bytes. Graph-capturable (no sync, no alloc). */
+dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, size_t ws_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */
