@@ -1,0 +1,364 @@
+#!/usr/bin/env python3
+"""Throughput of the DSA hot path (lightning indexer -> top-k -> sparse MQA-MLA) on one MI355X.
+
+A step is one dsa_forward over one batch of seeded synthetic inputs, already resident in HBM.
+Default workload: decode, 16 sequences x 1 new query token over an 8192-token context, indexer
+64 heads x 128 (bf16 keys), top-k 2048, sparse MQA attention with 128 heads over 576-wide
+latent rows (value = first 512 columns), bf16 storage, fp32 accumulation.
+
+The K timed steps replay HIP graphs of dsa_forward, cycling over R copies of the inputs so the
+bytes a step touches exceed the 256 MB last-level cache (cold-cache HBM traffic, as in
+multi-layer decode). A second, instrumented pass records HIP events between the kernels of the
+same graph to get each kernel's average duration; the dominant kernel's algorithmic bytes (or
+flops) over that duration give the roofline fraction. The fp64 CPU oracle, timed on this host's
+cores over the queries of one step, is reported beside it as a baseline.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "query tokens/sec (indexer+top-k+sparse MLA); % of peak HBM BW / MFMA"
+
+WORKLOAD_TEXT = {
+    "decode": "decode DSA: B=16 sequences x 1 query token, context L=8192, indexer 64 heads x 128 "
+              "(bf16 k_I), top-k 2048, sparse MQA-MLA 128 heads, key 576 / value 512 (bf16), "
+              "softmax scale 1/24",
+    "csa_decode": "CSA decode: B=4 x 1 query over 1,048,576 tokens (262,144 4:1 blocks), MXFP4 "
+                  "k_I, top-k 1024 blocks + 128-token raw window, 128 heads, key 576 / value 512",
+    "prefill": "prefill DSA: 1 sequence, L=T=32768 causal, indexer 64x128, top-k 2048, "
+               "128 heads, key 576 / value 512 (bf16)",
+    "csa_prefill": "CSA prefill: 131072 raw tokens mean-pooled 4:1 to 32768 blocks, last 8192 "
+                   "queries, top-k 1024 + 128-token window, 128 heads, key 576 / value 512",
+    "tiny": "tiny fp32 DSA: L=256, 16 queries, indexer 4x32, top-k 64, 8 heads, key 64 / value 48",
+}
+
+
+def _kernel_plan(cfg, nsplit):
+    """Kernel names of one dsa_forward (per chunk) in launch order."""
+    names = []
+    if cfg.compress:
+        names.append("compress_mean")
+    fast = cfg.dt == "bf16" and cfg.H_I == 64 and cfg.D_I == 128
+    rows = cfg.B * cfg.T
+    if fast and cfg.k_dt == "bf16" and rows >= 64:
+        names.append("indexer_prefill_mfma")
+    elif fast:
+        names.append("indexer_decode_mfma")
+    else:
+        names.append("indexer_generic")
+    names.append("topk_radix_row")
+    mfma = cfg.dt == "bf16" and cfg.D_K == 576 and cfg.D_V == 512 and cfg.H % 64 == 0
+    names.append("attend_mfma" if mfma else "attend_generic")
+    if nsplit > 1:
+        names.append("attend_combine")
+    return names
+
+
+def _algorithmic(cfg, name):
+    """(bytes, flops) the method must move / compute in one launch of `name` at this workload.
+
+    Counts causal pairs and selected entries only; scratch traffic (split partials, repeated
+    passes over the scores) is not algorithmic."""
+    B, T, N = cfg.B, cfg.T, cfg.N
+    rows = B * T
+    esz = 2 if cfg.dt == "bf16" else 4
+    kI_row = cfg.D_I // 2 + cfg.D_I // 32 if cfg.k_dt == "mxfp4" else cfg.D_I * esz
+    nvis = [min(N, (int(p) + 1) // cfg.m) for p in cfg.positions().ravel()]  # visible entries
+    pairs = float(sum(nvis))
+    sel = float(sum(min(cfg.top_k, v) for v in nvis))
+    win = 0.0
+    if cfg.W > 0:
+        base, n_raw = (0, N * cfg.m) if cfg.compress else (cfg.raw_base, cfg.n_raw)
+        for p in cfg.positions().ravel():
+            lo = max(0, int(p) - cfg.W + 1, base)
+            hi = min(int(p), base + n_raw - 1)
+            win += max(0, hi - lo + 1)
+    if name == "compress_mean":
+        return B * N * cfg.m * cfg.D_K * esz + B * N * cfg.D_K * esz, 0.0
+    if name.startswith("indexer"):
+        # every key row a sequence's queries can see is read once per sequence (decode: per query)
+        keys = B * max(nvis) if T > 1 else pairs
+        byt = keys * kI_row + rows * cfg.H_I * (cfg.D_I * esz + 4) + pairs * 4
+        return byt, pairs * cfg.H_I * cfg.D_I * 2.0
+    if name == "topk_radix_row":
+        return pairs * 4 + rows * cfg.top_k * 4, 0.0
+    if name.startswith("attend_mfma") or name == "attend_generic":
+        ents = sel + win
+        byt = ents * cfg.D_K * esz + rows * cfg.H * cfg.D_K * esz + rows * cfg.top_k * 4
+        return byt, ents * cfg.H * (cfg.D_K + cfg.D_V) * 2.0
+    if name == "attend_combine":
+        return rows * cfg.H * (cfg.D_V * esz + 4), 0.0
+    return 0.0, 0.0
+
+
+def _src_sha(kernel):
+    files = {"indexer": "indexer.hip", "topk": "topk.hip", "attend": "attend.hip",
+             "compress": "compress.hip"}
+    for k, f in files.items():
+        if kernel.startswith(k):
+            with open(os.path.join(ROOT, "lightning_indexer_top_03_amd", "csrc", f), "rb") as fh:
+                return hashlib.sha1(fh.read()).hexdigest()[:12]
+    return None
+
+
+def _traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tab = json.load(f)
+    e = tab.get(workload, {}).get(kernel)
+    if not e or e.get("src_sha") != _src_sha(kernel):
+        return None
+    return e["hbm_bytes_per_launch"]
+
+
+def _dev(a):
+    import numpy as np
+    import torch
+
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def _device_inputs(wl):
+    """Device copies of a workload (q generated in chunks straight into HBM)."""
+    import torch
+
+    c = wl.cfg
+    t = {"q_pos": _dev(wl.q_pos()), "q_I": _dev(wl.q_I()), "w": _dev(wl.w())}
+    k = wl.k_I()
+    t["k_I"] = (_dev(k[0]), _dev(k[1])) if c.k_dt == "mxfp4" else _dev(k)
+    rows = c.B * c.T
+    tdt = torch.bfloat16 if c.dt == "bf16" else torch.float32
+    q = torch.empty((c.B, c.T, c.H, c.D_K), dtype=tdt, device="cuda")
+    qf = q.view(rows, c.H, c.D_K)
+    for r0 in range(0, rows, 4096):
+        n = min(4096, rows - r0)
+        qf[r0:r0 + n] = _dev(wl.q_chunk(r0, n))
+    t["q"] = q
+    raw = wl.kv_raw()
+    t["kv_raw"] = _dev(raw) if raw is not None else None
+    wl.drop("kv_raw")
+    t["kv"] = (torch.empty((c.B, c.N, c.D_K), dtype=tdt, device="cuda") if c.compress
+               else _dev(wl.kv()))
+    wl.drop("kv")
+    return t
+
+
+def _forward(cfg, t, dsa, base):
+    return dsa.Forward(t["q_I"], t["w"], t["k_I"], t["q"], t["kv"], t["q_pos"], cfg.top_k,
+                       cfg.D_V, cfg.softmax_scale, m=cfg.m, W=cfg.W, kv_raw=t["kv_raw"],
+                       raw_base=base, compress=cfg.compress)
+
+
+def cpu_baseline(cfg, budget_s=20.0):
+    """The oracle, as it stands, over the query rows of one step (or as many as fit the budget)."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    wl = synth.make_workload(cfg)
+    run = oracle.QueryRunner(wl)
+    rows = [(b, t) for b in range(cfg.B) for t in range(cfg.T)]
+    if len(rows) > 64:
+        rng = np.random.default_rng(cfg.seed)
+        rows = [rows[i] for i in sorted(rng.choice(len(rows), 64, replace=False))]
+    t0 = time.perf_counter()
+    done = 0
+    for b, t in rows:
+        run.run(b, t)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "query tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{done} of the {cfg.B * cfg.T} query rows of one step "
+                      f"({'all' if done == cfg.B * cfg.T else 'uniform sample'}), fp64, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input copies cycled over (0: enough to exceed 2x the 256 MB MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the single-GPU path only: this build has no multi-GPU code "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import lightning_indexer_top_03_amd as dsa
+    import synth
+
+    cfg = synth.CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    wl = synth.make_workload(cfg)
+    t0 = time.time()
+    inputs = [_device_inputs(wl)]
+    print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    # input copies so that one cycle touches > 512 MB
+    touched = sum(_algorithmic(cfg, k)[0] for k in ("indexer_x", "attend_mfma"))
+    R = args.rotate or max(1, min(16, int(512e6 // max(touched, 1.0)) + 1))
+    if cfg.B * cfg.T > 64:
+        R = args.rotate or 1
+    for _ in range(1, R):
+        c = {k: (tuple(x.clone() for x in v) if isinstance(v, tuple) else
+                 (v.clone() if v is not None else None)) for k, v in inputs[0].items()}
+        inputs.append(c)
+    base = wl.raw_extent()[0]
+    fwds = [_forward(cfg, t, dsa, base) for t in inputs]
+    rows = cfg.B * cfg.T
+    # dsa_forward processes the query rows in chunks whose scores fit 256 MB
+    chunk_rows = min(rows, max(1, (256 << 20) // (cfg.N * 4)))
+    n_chunks = -(-rows // chunk_rows)
+    d = dsa.dims(B=1, T=chunk_rows, N=cfg.N, H_I=cfg.H_I, D_I=cfg.D_I, H=cfg.H, D_K=cfg.D_K,
+                 D_V=cfg.D_V, top_k=cfg.top_k, m=cfg.m, W=cfg.W)
+    split = dsa.workspace_bytes(d, dsa.OP_ATTEND) > 0  # the attention splits its entry list
+    per_chunk = _kernel_plan(cfg.with_(compress=False, B=1, T=chunk_rows), 2 if split else 1)
+    kernels = (["compress_mean"] if cfg.compress else []) + per_chunk * n_chunks
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graphs = []
+    with torch.cuda.stream(stream):
+        for f in fwds:
+            f.run()
+        torch.cuda.synchronize()
+        if not args.eager:
+            for f in fwds:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    f.run()
+                graphs.append(g)
+    torch.cuda.synchronize()
+
+    def step(i):
+        if graphs:
+            graphs[i % R].replay()
+        else:
+            fwds[i % R].run()
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = rows / (elapsed / args.steps)
+
+    # ---- instrumented pass: events between the kernels of the same call ----
+    nk = len(kernels)
+    per_kernel = [0.0] * nk
+    n_inst = min(args.steps, 200 if rows <= 64 else 10)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)]
+    mode = "graph"
+    with torch.cuda.stream(stream):
+        for f in fwds:
+            f.set_events(evs)
+        igraphs = []
+        try:
+            if args.eager:
+                raise RuntimeError("eager")
+            for f in fwds:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    f.run()
+                igraphs.append(g)
+            for i in range(n_inst):
+                igraphs[i % R].replay()
+                torch.cuda.synchronize()
+                for k in range(nk):
+                    per_kernel[k] += evs[k].elapsed_time(evs[k + 1])
+        except RuntimeError:
+            mode = "eager"
+            per_kernel = [0.0] * nk
+            for i in range(n_inst):
+                fwds[i % R].run()
+                torch.cuda.synchronize()
+                for k in range(nk):
+                    per_kernel[k] += evs[k].elapsed_time(evs[k + 1])
+        for f in fwds:
+            f.set_events(None)
+    per_kernel = [x / n_inst for x in per_kernel]  # ms per launch
+
+    # per kernel: summed over the query chunks of one step (one launch per chunk)
+    tot = {}
+    for k, name in enumerate(kernels):
+        tot[name] = tot.get(name, 0.0) + per_kernel[k]
+    kinfo = {}
+    for name, ms in tot.items():
+        byt, fl = _algorithmic(cfg, name)
+        us = ms * 1e3
+        kinfo[name] = {"us_per_step": round(us, 3), "launches_per_step": kernels.count(name),
+                       "alg_GBps": round(byt / (us * 1e-6) / 1e9, 1) if us else None,
+                       "alg_TFLOPs": round(fl / (us * 1e-6) / 1e12, 2) if us and fl else None}
+    dname = max(tot, key=lambda k: tot[k])
+    byt, fl = _algorithmic(cfg, dname)
+    dur = tot[dname] * 1e-3  # per step; equals the launch duration when there is one chunk
+    intensity = fl / byt if byt else 0.0
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if fl and intensity > ridge:
+        roof = {"bound": "mfma", "achieved": round(fl / dur / 1e12, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(byt / dur / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    tr = _traffic(dname, args.workload)
+    roof["traffic"] = tr
+    roof["kernel"] = dname
+    roof["kernel_us"] = round(dur * 1e6 / kernels.count(dname), 3)
+    roof["alg_bytes_per_step"] = byt
+    roof["alg_flops_per_step"] = fl
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16"
+        if cfg.dt == "bf16" else "f32", "data": "synthetic (seeded, counter-based generator)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload,
+                   "global_batch": rows, "seq_len": cfg.N * cfg.m, "parallelism": "single GPU",
+                   "input_copies": R, "launch": "hip graph" if graphs else "eager",
+                   "event_pass": mode},
+        "roofline": roof,
+        "kernels": kinfo,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -97,15 +97,16 @@ int dsa_version(void);
  * Returns 0 for invalid dims as well; the call itself then reports the error. */
 size_t dsa_workspace_bytes(const dsa_dims* d, int op);
 
-/* Step 0 - CSA token-dimension compression ([P1]; [P4] "compress each m consecutive tokens'
- * KV into one entry, e.g. by average pooling").
+/* Step 0 - CSA token-dimension compression ([P1] V4 CSA summary; [P4] CSA snippets: m
+ * consecutive tokens' KV pooled into one entry, average pooling named as one choice).
  *   kv_c[b, j, :] = (1/m) * sum_{i<m} kv_raw[b, m*j + i, :],   j < floor(n_raw / m)
  * kv_raw: [B, n_raw, D_K] of dtype dt (F32 or BF16); kv_c: [B, floor(n_raw/m), D_K], same dtype.
  * Summation in fp32, one final rounding (RNE) to dt. Uses d->B, d->D_K, d->m (>= 1). */
 dsa_status kv_compress_mean(const dsa_dims* d, dsa_dtype dt, const void* kv_raw, int64_t n_raw,
                             void* kv_c, void* stream);
 
-/* Step 1 - lightning-indexer scores ([P5] s1.3 "lightning indexer"; s3 step 2 "mqa logits").
+/* Step 1 - lightning-indexer scores ([P5] s1.3 lightning indexer; s3 step 2, the indexer's
+ * multi-query logits with one key shared by all indexer heads).
  *   scores[b,t,s] = sum_{j<H_I} w[b,t,j] * max(0, sum_{d<D_I} q_I[b,t,j,d] * k_I[b,s,d])
  *                   for s < n_vis(b,t);   -inf for n_vis <= s < N.
  * q_I:    [B,T,H_I,D_I], dtype q_dt (F32 or BF16)
@@ -119,8 +120,9 @@ dsa_status indexer_scores(const dsa_dims* d, const void* q_I, dsa_dtype q_dt, co
                           const void* k_I, const uint8_t* k_scale, dsa_dtype k_dt,
                           const int32_t* q_pos, float* scores, void* stream);
 
-/* Step 2 - per-query top-k ([P5] s1.3 "keep only the KV of the top-k index scores"; s3 step 3:
- * keep every token when the context is no longer than k; index_mask of step 4).
+/* Step 2 - per-query top-k ([P5] s1.3: only the KV entries with the k highest index scores
+ * take part; s3 step 3: every token is kept when the context is no longer than k; step 4's
+ * index mask).
  *   n = n_vis(b,t). If n <= top_k: idx[b,t,0..n) = 0..n-1 (ascending).
  *   Else: idx[b,t,:] = the top_k entries s < n with the largest scores, ties broken toward the
  *   LOWER index (the result is the first top_k of a stable sort by descending score); the
@@ -170,6 +172,12 @@ typedef struct dsa_forward_args {
   float* lse;            /* [B,T,H] or NULL                                               */
   float* scores;         /* [B,T,N] or NULL (then scores live in ws, masked tail unwritten)*/
   int32_t* idx;          /* [B,T,top_k] or NULL (then idx lives in ws)                    */
+  void* const* events;   /* profiling aid, or NULL: hipEvent_t handles; events[i] is recorded
+                            on `stream` right before the i-th kernel this call launches and
+                            events[K] after the last one (K kernels), as far as n_events
+                            reaches. The kernel order is: [compress], then per query chunk
+                            indexer, top-k, attention[, split combine].                  */
+  int32_t n_events;
 } dsa_forward_args;
 
 /* Fused path: [compress] -> indexer_scores -> topk_select -> sparse_mla_attend on `stream`

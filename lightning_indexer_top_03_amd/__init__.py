@@ -1,0 +1,255 @@
+"""Python binding of the DSA / CSA hot-path library (include/dsa.h, libdsa.so).
+
+Argument marshalling only: every step runs in the HIP kernels of ``csrc/``. torch tensors are
+used for device memory and streams; each call passes ``data_ptr()`` values and the current HIP
+stream to the C ABI and raises ``DsaError`` with the library's status text on failure. There is
+no fallback: without the built library the import fails.
+
+bf16 tensors are ``torch.bfloat16``; MXFP4 keys are a pair (codes uint8 [B,N,D_I/2], scales
+uint8 [B,N,D_I/32]).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple, Union
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdsa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m lightning_indexer_top_03_amd.build` "
+        "(hipcc, gfx950). There is no non-HIP fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+F32, BF16, MXFP4 = 0, 1, 2
+OP_TOPK, OP_ATTEND, OP_FORWARD = 1, 2, 3
+
+EXPORTS = ("dsa_status_str", "dsa_version", "dsa_workspace_bytes", "kv_compress_mean",
+           "indexer_scores", "topk_select", "sparse_mla_attend", "dsa_forward")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "T", "N", "H_I", "D_I", "H", "D_K", "D_V", "top_k", "m", "W")]
+
+
+class ForwardArgs(ctypes.Structure):
+    _fields_ = [("dt", ctypes.c_int), ("k_dt", ctypes.c_int),
+                ("q_I", ctypes.c_void_p), ("w", ctypes.c_void_p), ("k_I", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("q", ctypes.c_void_p), ("kv", ctypes.c_void_p),
+                ("kv_raw", ctypes.c_void_p), ("raw_base", ctypes.c_int64),
+                ("n_raw", ctypes.c_int64), ("compress", ctypes.c_int32),
+                ("q_pos", ctypes.c_void_p), ("softmax_scale", ctypes.c_float),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("scores", ctypes.c_void_p), ("idx", ctypes.c_void_p),
+                ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32)]
+
+
+_vp, _i64, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+_D = ctypes.POINTER(Dims)
+_lib.dsa_status_str.argtypes = [ctypes.c_int]
+_lib.dsa_status_str.restype = ctypes.c_char_p
+_lib.dsa_version.restype = ctypes.c_int
+_lib.dsa_workspace_bytes.argtypes = [_D, ctypes.c_int]
+_lib.dsa_workspace_bytes.restype = _sz
+_lib.kv_compress_mean.argtypes = [_D, ctypes.c_int, _vp, _i64, _vp, _vp]
+_lib.indexer_scores.argtypes = [_D, _vp, ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp]
+_lib.topk_select.argtypes = [_D, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.sparse_mla_attend.argtypes = [_D, ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
+                                   ctypes.c_float, _vp, _vp, _vp, _sz, _vp]
+_lib.dsa_forward.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]
+for _f in ("kv_compress_mean", "indexer_scores", "topk_select", "sparse_mla_attend",
+           "dsa_forward"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.dsa_status_str(status).decode()}")
+
+
+def lib():
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise DsaError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the DSA library must be contiguous")
+    return t.data_ptr()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def dims(B=1, T=1, N=1, H_I=1, D_I=8, H=1, D_K=8, D_V=8, top_k=1, m=1, W=0) -> Dims:
+    return Dims(B, T, N, H_I, D_I, H, D_K, D_V, top_k, m, W)
+
+
+def workspace_bytes(d: Dims, op: int) -> int:
+    return int(_lib.dsa_workspace_bytes(ctypes.byref(d), op))
+
+
+def _workspace(d: Dims, op: int, device) -> Optional[torch.Tensor]:
+    n = workspace_bytes(d, op)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+# ---- step 0 -----------------------------------------------------------------------------------
+
+def kv_compress_mean(kv_raw: torch.Tensor, m: int, kv_c: Optional[torch.Tensor] = None):
+    """kv_raw [B, n_raw, D] -> kv_c [B, n_raw // m, D] (mean of each m consecutive rows)."""
+    B, n_raw, D = kv_raw.shape
+    if kv_c is None:
+        kv_c = torch.empty((B, n_raw // m, D), dtype=kv_raw.dtype, device=kv_raw.device)
+    d = dims(B=B, D_K=D, m=m)
+    _check(_lib.kv_compress_mean(ctypes.byref(d), _dt(kv_raw), _ptr(kv_raw), n_raw, _ptr(kv_c),
+                                 _stream(kv_raw)), "kv_compress_mean")
+    return kv_c
+
+
+# ---- step 1 -----------------------------------------------------------------------------------
+
+KeyT = Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]
+
+
+def _keys(k_I: KeyT, q_dt: int):
+    if isinstance(k_I, tuple):
+        codes, scales = k_I
+        return codes, scales, MXFP4, codes.shape[1], codes.shape[2] * 2
+    return k_I, None, _dt(k_I), k_I.shape[1], k_I.shape[2]
+
+
+def indexer_scores(q_I: torch.Tensor, w: torch.Tensor, k_I: KeyT, q_pos: torch.Tensor,
+                   m: int = 1, scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q_I [B,T,H_I,D_I], w [B,T,H_I] fp32, k_I [B,N,D_I] or MXFP4 (codes, scales),
+    q_pos [B,T] int32 -> scores [B,T,N] fp32 (-inf where not visible)."""
+    B, T, H_I, D_I = q_I.shape
+    kt, ks, kdt, N, _ = _keys(k_I, _dt(q_I))
+    if scores is None:
+        scores = torch.empty((B, T, N), dtype=torch.float32, device=q_I.device)
+    d = dims(B=B, T=T, N=N, H_I=H_I, D_I=D_I, m=m)
+    _check(_lib.indexer_scores(ctypes.byref(d), _ptr(q_I), _dt(q_I), _ptr(w), _ptr(kt), _ptr(ks),
+                               kdt, _ptr(q_pos), _ptr(scores), _stream(q_I)), "indexer_scores")
+    return scores
+
+
+# ---- step 2 -----------------------------------------------------------------------------------
+
+def topk_select(scores: torch.Tensor, q_pos: torch.Tensor, top_k: int, m: int = 1,
+                idx: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """scores [B,T,N] fp32 -> idx [B,T,top_k] int32 (set semantics, -1 padded)."""
+    B, T, N = scores.shape
+    if idx is None:
+        idx = torch.empty((B, T, top_k), dtype=torch.int32, device=scores.device)
+    d = dims(B=B, T=T, N=N, top_k=top_k, m=m)
+    ws = _workspace(d, OP_TOPK, scores.device)
+    _check(_lib.topk_select(ctypes.byref(d), _ptr(scores), _ptr(q_pos), _ptr(idx), _ptr(ws),
+                            0 if ws is None else ws.numel(), _stream(scores)), "topk_select")
+    return idx
+
+
+# ---- step 3 -----------------------------------------------------------------------------------
+
+def sparse_mla_attend(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor, q_pos: torch.Tensor,
+                      D_V: int, softmax_scale: float, kv_raw: Optional[torch.Tensor] = None,
+                      raw_base: int = 0, W: int = 0, m: int = 1,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      want_lse: bool = True):
+    """q [B,T,H,D_K], kv [B,N,D_K], idx [B,T,k] int32, optional raw window rows kv_raw
+    [B,n_raw,D_K] at positions raw_base.. -> (out [B,T,H,D_V], lse [B,T,H] fp32)."""
+    B, T, H, D_K = q.shape
+    N = kv.shape[1]
+    k = idx.shape[2]
+    if out is None:
+        out = torch.empty((B, T, H, D_V), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    d = dims(B=B, T=T, N=N, H=H, D_K=D_K, D_V=D_V, top_k=k, m=m, W=W)
+    ws = _workspace(d, OP_ATTEND, q.device)
+    n_raw = 0 if kv_raw is None else kv_raw.shape[1]
+    _check(_lib.sparse_mla_attend(ctypes.byref(d), _dt(q), _ptr(q), _ptr(kv), _ptr(idx),
+                                  _ptr(kv_raw), raw_base, n_raw, _ptr(q_pos), softmax_scale,
+                                  _ptr(out), _ptr(lse), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(q)),
+           "sparse_mla_attend")
+    return out, lse
+
+
+# ---- fused ------------------------------------------------------------------------------------
+
+class Forward:
+    """A prepared dsa_forward call: dims, argument block and workspace built once, so that
+    ``run()`` is a single C call (cheap to time and to capture in a HIP graph)."""
+
+    def __init__(self, q_I, w, k_I: KeyT, q, kv, q_pos, top_k: int, D_V: int,
+                 softmax_scale: float, m: int = 1, W: int = 0, kv_raw=None, raw_base: int = 0,
+                 compress: bool = False, out=None, lse=None, scores=None, idx=None,
+                 want_lse: bool = True):
+        B, T, H_I, D_I = q_I.shape
+        _, _, H, D_K = q.shape
+        kt, ks, kdt, N, _ = _keys(k_I, _dt(q_I))
+        self.d = dims(B=B, T=T, N=N, H_I=H_I, D_I=D_I, H=H, D_K=D_K, D_V=D_V, top_k=top_k, m=m,
+                      W=W)
+        dev = q.device
+        self.out = out if out is not None else torch.empty((B, T, H, D_V), dtype=q.dtype, device=dev)
+        self.lse = lse if lse is not None else (
+            torch.empty((B, T, H), dtype=torch.float32, device=dev) if want_lse else None)
+        self.scores, self.idx = scores, idx
+        self.ws = _workspace(self.d, OP_FORWARD, dev)
+        self._keep = (q_I, w, kt, ks, q, kv, q_pos, kv_raw)
+        n_raw = 0 if kv_raw is None else kv_raw.shape[1]
+        self.args = ForwardArgs(_dt(q), kdt, _ptr(q_I), _ptr(w), _ptr(kt), _ptr(ks), _ptr(q),
+                                _ptr(kv), _ptr(kv_raw), raw_base, n_raw, 1 if compress else 0,
+                                _ptr(q_pos), softmax_scale, _ptr(self.out), _ptr(self.lse),
+                                _ptr(scores), _ptr(idx), None, 0)
+        self.device = dev
+
+    def set_events(self, events) -> None:
+        """Profiling aid: torch.cuda.Event objects recorded between this call's kernels
+        (events[i] before the i-th kernel, events[K] after the last). None to clear."""
+        if not events:
+            self._ev = None
+            self.args.events, self.args.n_events = None, 0
+            return
+        for e in events:
+            if e.cuda_event == 0:  # torch creates the HIP event lazily
+                e.record()
+        self._ev = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        self.args.events = ctypes.cast(self._ev, ctypes.POINTER(ctypes.c_void_p))
+        self.args.n_events = len(events)
+
+    def run(self, stream: Optional[int] = None) -> torch.Tensor:
+        st = torch.cuda.current_stream(self.device).cuda_stream if stream is None else stream
+        _check(_lib.dsa_forward(ctypes.byref(self.d), ctypes.byref(self.args), _ptr(self.ws),
+                                0 if self.ws is None else self.ws.numel(), st), "dsa_forward")
+        return self.out
+
+
+def dsa_forward(q_I, w, k_I: KeyT, q, kv, q_pos, top_k: int, D_V: int, softmax_scale: float,
+                **kw):
+    """[compress] -> indexer -> top-k -> sparse attention. Returns (out, lse, forward)."""
+    f = Forward(q_I, w, k_I, q, kv, q_pos, top_k, D_V, softmax_scale, **kw)
+    f.run()
+    return f.out, f.lse, f

@@ -1,0 +1,283 @@
+// api.cpp - the C ABI (include/dsa.h): argument validation, workspace sizing and dispatch.
+//
+// Every argument is checked on the host before anything touches HIP, so error paths launch
+// nothing (and run without a GPU). Then the current device is checked to be gfx950 (cached per
+// device), then kernels are launched on the caller's stream. No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+
+#include "dsa.h"
+#include "launch.h"
+
+using namespace dsa;
+
+namespace {
+
+constexpr int kMaxW = 4096;
+constexpr size_t kScoreChunkBytes = size_t(256) << 20;  // fused path: scores per chunk
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+dsa_status check_dims(const dsa_dims* d) {
+  if (!d) return DSA_ERR_NULL;
+  if (d->B < 1 || d->T < 1 || d->N < 1 || d->H_I < 1 || d->D_I < 1 || d->H < 1 || d->D_K < 8 ||
+      d->D_V < 1 || d->top_k < 1 || d->m < 1 || d->W < 0)
+    return DSA_ERR_SHAPE;
+  if (d->top_k > DSA_MAX_TOPK || d->D_K > DSA_MAX_DK || d->W > kMaxW) return DSA_ERR_SHAPE;
+  if (d->D_K % 8 || d->D_V % 8 || d->D_I % 8 || d->D_V > d->D_K) return DSA_ERR_SHAPE;
+  // flattened element counts must fit the kernels' 64-bit indexing and 32-bit row counts
+  const int64_t rows = (int64_t)d->B * d->T;
+  if (rows > INT32_MAX || (int64_t)d->B * d->N > ((int64_t)1 << 40)) return DSA_ERR_SHAPE;
+  return DSA_OK;
+}
+
+Shape to_shape(const dsa_dims* d) {
+  return Shape{d->B, d->T, d->N, d->H_I, d->D_I, d->H, d->D_K, d->D_V, d->top_k, d->m, d->W};
+}
+
+bool fmt_ok(dsa_dtype t) { return t == DSA_F32 || t == DSA_BF16; }
+
+// indexer argument rules shared by indexer_scores and dsa_forward
+dsa_status check_indexer(const dsa_dims* d, dsa_dtype q_dt, dsa_dtype k_dt,
+                         const uint8_t* k_scale) {
+  if (!fmt_ok(q_dt)) return DSA_ERR_DTYPE;
+  if (k_dt == DSA_MXFP4) {
+    if (!k_scale) return DSA_ERR_NULL;
+    if (d->D_I % 32) return DSA_ERR_SHAPE;
+  } else {
+    if (k_dt != q_dt) return DSA_ERR_DTYPE;
+    if (k_scale) return DSA_ERR_DTYPE;
+  }
+  const bool fast = q_dt == DSA_BF16 && d->H_I == 64 && d->D_I == 128;
+  if (!fast && (int64_t)d->H_I * d->D_I > 8192) return DSA_ERR_SHAPE;  // generic kernel LDS
+  return DSA_OK;
+}
+
+dsa_status check_attend_shape(const dsa_dims* d) {
+  // generic kernel keeps q, the logits and the row pointers of one query in LDS
+  const size_t e = (size_t)d->top_k + d->W;
+  const size_t shm = sizeof(float) * (d->D_K + e + 1) + sizeof(void*) * e + 16;
+  if (shm > 60 * 1024) return DSA_ERR_SHAPE;
+  return DSA_OK;
+}
+
+std::atomic<int> g_dev_ok[64];  // 0 unknown, 1 gfx950, 2 other
+
+dsa_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_DEVICE;
+  if (dev < 0 || dev >= 64) return DSA_ERR_DEVICE;
+  int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DSA_ERR_DEVICE;
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? DSA_OK : DSA_ERR_DEVICE;
+}
+
+inline dsa_status launched(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
+
+// Records the caller's profiling events between the kernels of one dsa_forward call.
+struct EventMarks {
+  void* const* ev;
+  int n, next = 0;
+  hipStream_t st;
+  void mark() {
+    if (ev && next < n) hipEventRecord((hipEvent_t)ev[next], st);
+    ++next;
+  }
+  hipEvent_t peek() const { return (ev && next < n) ? (hipEvent_t)ev[next] : nullptr; }
+};
+
+int64_t forward_chunk_rows(const dsa_dims* d) {
+  const int64_t rows = (int64_t)d->B * d->T;
+  const int64_t per = std::max<int64_t>(1, (int64_t)(kScoreChunkBytes / ((size_t)d->N * 4)));
+  return std::min(rows, per);
+}
+
+struct FwdLayout {
+  size_t scores, idx, attend, total;
+};
+
+FwdLayout forward_layout(const dsa_dims* d, dsa_dtype dt) {
+  const int64_t R = forward_chunk_rows(d);
+  const Shape s = to_shape(d);
+  FwdLayout L;
+  L.scores = align_up((size_t)R * d->N * sizeof(float));
+  L.idx = align_up((size_t)R * d->top_k * sizeof(int32_t));
+  // chunks have R rows except possibly the last one; the split plan depends on the row count
+  const int fmt = dt == DSA_BF16 ? FMT_BF16 : FMT_F32;
+  const int64_t rows = (int64_t)d->B * d->T;
+  const int64_t last = rows - (rows - 1) / R * R;
+  L.attend = align_up(std::max(attend_ws_bytes(s, R, fmt), attend_ws_bytes(s, last, fmt)));
+  L.total = L.scores + L.idx + L.attend + align_up(topk_ws_bytes(s, R));
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_str(int status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_NULL: return "DSA_ERR_NULL: a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: a dimension is out of range or inconsistent";
+    case DSA_ERR_DTYPE: return "DSA_ERR_DTYPE: unsupported dtype or dtype combination";
+    case DSA_ERR_ALIGN: return "DSA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+    case DSA_ERR_DEVICE: return "DSA_ERR_DEVICE: current HIP device is not gfx950";
+    case DSA_ERR_LAUNCH: return "DSA_ERR_LAUNCH: a kernel launch failed";
+    default: return "unknown dsa_status";
+  }
+}
+
+int dsa_version(void) { return 100; }
+
+size_t dsa_workspace_bytes(const dsa_dims* d, int op) {
+  if (check_dims(d) != DSA_OK) return 0;
+  const Shape s = to_shape(d);
+  const int64_t rows = (int64_t)d->B * d->T;
+  switch (op) {
+    case DSA_OP_TOPK: return topk_ws_bytes(s, rows);
+    case DSA_OP_ATTEND:
+      // the bf16 plan needs at least as much as the fp32 one
+      return std::max(attend_ws_bytes(s, rows, FMT_BF16), attend_ws_bytes(s, rows, FMT_F32));
+    case DSA_OP_FORWARD: return forward_layout(d, DSA_BF16).total;
+    default: return 0;
+  }
+}
+
+dsa_status kv_compress_mean(const dsa_dims* d, dsa_dtype dt, const void* kv_raw, int64_t n_raw,
+                            void* kv_c, void* stream) {
+  if (!d) return DSA_ERR_NULL;
+  if (d->B < 1 || d->D_K < 8 || d->D_K % 8 || d->D_K > DSA_MAX_DK || d->m < 1 || n_raw < 0)
+    return DSA_ERR_SHAPE;
+  if (!fmt_ok(dt)) return DSA_ERR_DTYPE;
+  if (!kv_raw || !kv_c) return DSA_ERR_NULL;
+  if (!aligned16(kv_raw) || !aligned16(kv_c)) return DSA_ERR_ALIGN;
+  if (dsa_status st = check_device()) return st;
+  return launched(launch_compress(d->B, n_raw, d->D_K, d->m, dt == DSA_BF16 ? FMT_BF16 : FMT_F32,
+                                  kv_raw, kv_c, (hipStream_t)stream));
+}
+
+dsa_status indexer_scores(const dsa_dims* d, const void* q_I, dsa_dtype q_dt, const float* w,
+                          const void* k_I, const uint8_t* k_scale, dsa_dtype k_dt,
+                          const int32_t* q_pos, float* scores, void* stream) {
+  if (dsa_status st = check_dims(d)) return st;
+  if (dsa_status st = check_indexer(d, q_dt, k_dt, k_scale)) return st;
+  if (!q_I || !w || !k_I || !q_pos || !scores) return DSA_ERR_NULL;
+  if (!aligned16(q_I) || !aligned16(w) || !aligned16(k_I) || !aligned16(scores) ||
+      (k_scale && ((uintptr_t)k_scale & 3u)))
+    return DSA_ERR_ALIGN;
+  if (dsa_status st = check_device()) return st;
+  const Shape s = to_shape(d);
+  return launched(launch_indexer(s, 0, (int64_t)d->B * d->T, q_I, (int)q_dt, w, k_I, k_scale,
+                                 (int)k_dt, q_pos, scores, true, (hipStream_t)stream));
+}
+
+dsa_status topk_select(const dsa_dims* d, const float* scores, const int32_t* q_pos,
+                       int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  if (dsa_status st = check_dims(d)) return st;
+  if (!scores || !q_pos || !idx) return DSA_ERR_NULL;
+  if (!aligned16(scores) || !aligned16(idx)) return DSA_ERR_ALIGN;
+  const size_t need = dsa_workspace_bytes(d, DSA_OP_TOPK);
+  if (need && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (dsa_status st = check_device()) return st;
+  return launched(launch_topk(to_shape(d), 0, (int64_t)d->B * d->T, scores, q_pos, idx, ws,
+                              (hipStream_t)stream));
+}
+
+dsa_status sparse_mla_attend(const dsa_dims* d, dsa_dtype dt, const void* q, const void* kv,
+                             const int32_t* idx, const void* kv_raw, int64_t raw_base,
+                             int64_t n_raw, const int32_t* q_pos, float softmax_scale,
+                             void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (dsa_status st = check_dims(d)) return st;
+  if (dsa_status st = check_attend_shape(d)) return st;
+  if (!fmt_ok(dt)) return DSA_ERR_DTYPE;
+  if (!q || !kv || !idx || !q_pos || !out) return DSA_ERR_NULL;
+  if (d->W > 0 && !kv_raw) return DSA_ERR_NULL;
+  if (raw_base < 0 || n_raw < 0) return DSA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (kv_raw && !aligned16(kv_raw)))
+    return DSA_ERR_ALIGN;
+  const Shape s = to_shape(d);
+  const int fmt = dt == DSA_BF16 ? FMT_BF16 : FMT_F32;
+  const size_t need = attend_ws_bytes(s, (int64_t)d->B * d->T, fmt);
+  if (need && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return DSA_ERR_ALIGN;
+  if (dsa_status st = check_device()) return st;
+  return launched(launch_attend(s, 0, (int64_t)d->B * d->T, fmt, q, kv, idx,
+                                d->W > 0 ? kv_raw : nullptr, raw_base, n_raw, q_pos,
+                                softmax_scale, out, lse, ws, (hipStream_t)stream));
+}
+
+dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (dsa_status st = check_dims(d)) return st;
+  if (!a) return DSA_ERR_NULL;
+  if (dsa_status st = check_attend_shape(d)) return st;
+  if (!fmt_ok(a->dt)) return DSA_ERR_DTYPE;
+  if (dsa_status st = check_indexer(d, a->dt, a->k_dt, a->k_scale)) return st;
+  if (!a->q_I || !a->w || !a->k_I || !a->q || !a->kv || !a->q_pos || !a->out) return DSA_ERR_NULL;
+  if ((d->W > 0 || a->compress) && !a->kv_raw) return DSA_ERR_NULL;
+  if (a->raw_base < 0 || a->n_raw < 0) return DSA_ERR_SHAPE;
+  if (a->compress && (a->raw_base != 0 || a->n_raw / d->m != d->N)) return DSA_ERR_SHAPE;
+  const void* ptrs16[] = {a->q_I, a->w, a->k_I, a->q, a->kv, a->out, a->kv_raw, a->scores,
+                          a->idx, ws};
+  for (const void* p : ptrs16)
+    if (p && !aligned16(p)) return DSA_ERR_ALIGN;
+  const FwdLayout L = forward_layout(d, a->dt);
+  if (!ws || ws_bytes < L.total) return DSA_ERR_WORKSPACE;
+  if (dsa_status st = check_device()) return st;
+
+  hipStream_t st = (hipStream_t)stream;
+  const Shape s = to_shape(d);
+  const int fmt = a->dt == DSA_BF16 ? FMT_BF16 : FMT_F32;
+  if (a->n_events < 0) return DSA_ERR_SHAPE;
+  EventMarks ev{a->events, a->n_events, 0, st};
+  ev.mark();
+  if (a->compress) {
+    if (hipError_t e = launch_compress(d->B, a->n_raw, d->D_K, d->m, fmt, a->kv_raw, a->kv, st))
+      return launched(e);
+    ev.mark();
+  }
+  char* wsb = static_cast<char*>(ws);
+  float* ws_scores = reinterpret_cast<float*>(wsb);
+  int32_t* ws_idx = reinterpret_cast<int32_t*>(wsb + L.scores);
+  void* ws_att = wsb + L.scores + L.idx;
+  void* ws_topk = wsb + L.scores + L.idx + L.attend;
+  const int64_t rows = (int64_t)d->B * d->T;
+  const int64_t R = forward_chunk_rows(d);  // the attention workspace is sized for R rows
+  const bool keep_scores = a->scores != nullptr;
+  for (int64_t q0 = 0; q0 < rows; q0 += R) {
+    const int64_t nr = std::min(R, rows - q0);
+    float* sc = keep_scores ? a->scores + (size_t)q0 * d->N : ws_scores;
+    int32_t* ix = a->idx ? a->idx + (size_t)q0 * d->top_k : ws_idx;
+    if (hipError_t e = launch_indexer(s, q0, nr, a->q_I, (int)a->dt, a->w, a->k_I, a->k_scale,
+                                      (int)a->k_dt, a->q_pos, sc, keep_scores, st))
+      return launched(e);
+    ev.mark();
+    if (hipError_t e = launch_topk(s, q0, nr, sc, a->q_pos, ix, ws_topk, st)) return launched(e);
+    ev.mark();
+    const bool split = attend_splits(s, nr, fmt) > 1;
+    if (hipError_t e = launch_attend(s, q0, nr, fmt, a->q, a->kv, ix,
+                                     d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw,
+                                     a->q_pos, a->softmax_scale, a->out, a->lse, ws_att, st,
+                                     split ? ev.peek() : nullptr))
+      return launched(e);
+    if (split) ++ev.next;
+    ev.mark();
+  }
+  return DSA_OK;
+}
+
+}  // extern "C"

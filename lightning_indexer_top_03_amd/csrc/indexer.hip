@@ -1,0 +1,376 @@
+// indexer.hip - lightning-indexer scores on gfx950.
+//
+//   I[t,s] = sum_j w[t,j] * ReLU(q_I[t,j,:] . k_I[s,:])     for s < n_vis(t), else -inf
+//
+// ("DeepSeek-V3.2 sparse-attention principle and TPU adaptation", s1.3 lightning indexer:
+// a low-dimensional per-token key, a ReLU instead of a softmax for throughput; s3 step 2:
+// "mqa logits", the key is shared by all indexer heads.)
+//
+// Three kernels:
+//  * indexer_decode_mfma  - few query rows, long key ranges: the query's 64x128 q_I stays in
+//    registers as MFMA A operands; every wave streams its own 32-key tiles of k_I straight
+//    from HBM into B operands (16-byte loads, two tiles in flight). bf16 or MXFP4 keys (FP4
+//    codes dequantised by v_cvt_scalef32_pk_bf16_fp4 into exact bf16).
+//  * indexer_prefill_mfma - many query rows of one sequence: each wave keeps 64 keys of k_I
+//    in registers, the workgroup walks 32 queries whose q_I is staged in LDS.
+//  * indexer_generic      - any H_I / D_I, fp32 or bf16 (and MXFP4) inputs; scalar fp32.
+// All three fuse ReLU, the head weights and the 64-head reduction into the epilogue, so the
+// [H_I x N] per-head products never leave registers.
+#include "common.h"
+#include "launch.h"
+
+#include <algorithm>
+
+namespace dsa {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// E8M0 byte -> fp32 scale 2^(e-127).
+__device__ __forceinline__ float e8m0_scale(uint32_t e) {
+  return e == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode-shaped kernel. H_I = 64, D_I = 128.
+//
+// MFMA v_mfma_f32_32x32x16_bf16, C[32 heads x 32 keys] += A[heads x 16] * B[16 x keys].
+// Lane l = (n = l % 32, h = l / 32). The contraction index of MFMA kk, slot i is dim
+// 64*h + 8*kk + i for both operands, so a lane reads 128 contiguous bytes of its q_I row
+// (A) and of its key row (B). Output: acc[hb][4*j + i] = head hb*32 + 8*j + 4*h + i, key n.
+// ------------------------------------------------------------------------------------------
+template <int KFMT>
+struct KeyTile {
+  u32x4_t v[8];
+};
+
+template <int KFMT>
+__device__ __forceinline__ void load_key_tile(KeyTile<KFMT>& kt, const uint8_t* __restrict__ kI,
+                                              const uint8_t* __restrict__ ksc, size_t row, int h,
+                                              float& s_lo, float& s_hi) {
+  if constexpr (KFMT == FMT_BF16) {
+    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(kI + row * 256 + 128 * h);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) kt.v[kk] = __builtin_nontemporal_load(p + kk);
+  } else {
+    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(kI + row * 64 + 32 * h);
+    kt.v[0] = __builtin_nontemporal_load(p);
+    kt.v[1] = __builtin_nontemporal_load(p + 1);
+    uint32_t sc = *reinterpret_cast<const uint16_t*>(ksc + row * 4 + 2 * h);
+    s_lo = e8m0_scale(sc & 0xffu);
+    s_hi = e8m0_scale(sc >> 8);
+  }
+}
+
+template <int KFMT>
+__device__ __forceinline__ bf16x8_t key_operand(const KeyTile<KFMT>& kt, int kk, float s_lo,
+                                                float s_hi) {
+  if constexpr (KFMT == FMT_BF16) {
+    return as_bf16x8(kt.v[kk]);
+  } else {
+    // dims 64h + 8kk .. +7 are code bytes 4kk .. 4kk+3 of the lane's 32-byte chunk
+    uint32_t cw = kt.v[kk >> 2][kk & 3];
+    float sc = kk < 4 ? s_lo : s_hi;
+    bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 0);
+    bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 1);
+    bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 2);
+    bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 3);
+    bf16x8_t r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+  }
+}
+
+template <int KFMT>
+__global__ __launch_bounds__(256) void indexer_decode_mfma(
+    const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
+    const uint8_t* __restrict__ ksc, const int32_t* __restrict__ q_pos, int T, int N, int m,
+    int64_t qi0, int iters, float* __restrict__ scores, int fill_masked) {
+  const int64_t row = blockIdx.y;
+  const int64_t qi = qi0 + row;
+  const int b = (int)(qi / T);
+  const int nv = n_visible(q_pos[qi], m, N);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n = lane & 31, h = lane >> 5;
+  const int keys_per_wave = 32 * iters;
+  const int key0 = (blockIdx.x * 4 + wv) * keys_per_wave;
+  float* __restrict__ srow = scores + (size_t)row * N;
+
+  if (key0 >= nv) {
+    if (fill_masked)
+      for (int s = key0 + lane; s < min(key0 + keys_per_wave, N); s += 64) srow[s] = kNegInf;
+    return;
+  }
+
+  // q_I fragments (A operands) and the weights of the heads this lane's outputs belong to.
+  const uint16_t* qrow = qI + (size_t)qi * (64 * 128);
+  u32x4_t qa[2][8];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qa[hb][kk] = *reinterpret_cast<const u32x4_t*>(qrow + (hb * 32 + n) * 128 + 64 * h + 8 * kk);
+  float wr[2][16];
+  const float* wrow = w + (size_t)qi * 64;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wr[hb][r] = wrow[hb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
+
+  const size_t base_row = (size_t)b * N;
+  const int last = min(key0 + keys_per_wave, nv);  // exclusive end of computed keys
+  KeyTile<KFMT> cur, nxt;
+  float lo_c = 0.f, hi_c = 0.f, lo_n = 0.f, hi_n = 0.f;
+  load_key_tile<KFMT>(cur, kI, ksc, base_row + min(key0 + n, N - 1), h, lo_c, hi_c);
+  for (int s0 = key0; s0 < last; s0 += 32) {
+    const bool more = s0 + 32 < last;
+    if (more) load_key_tile<KFMT>(nxt, kI, ksc, base_row + min(s0 + 32 + n, N - 1), h, lo_n, hi_n);
+    f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      bf16x8_t kb = key_operand<KFMT>(cur, kk, lo_c, hi_c);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[0][kk]), kb, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[1][kk]), kb, acc1, 0, 0, 0);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      part += wr[0][r] * fmaxf(acc0[r], 0.f);
+      part += wr[1][r] * fmaxf(acc1[r], 0.f);
+    }
+    part += __shfl_xor(part, 32, 64);
+    const int s = s0 + n;
+    if (h == 0 && s < N) srow[s] = (s < nv) ? part : kNegInf;
+    if (more) {
+      cur = nxt;
+      lo_c = lo_n;
+      hi_c = hi_n;
+    }
+  }
+  if (fill_masked) {
+    // keys of this wave's range past the visible end, in whole 32-key tiles not computed above
+    int s_start = key0 + ((last - key0 + 31) / 32) * 32;
+    for (int s = s_start + lane; s < min(key0 + keys_per_wave, N); s += 64) srow[s] = kNegInf;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Prefill-shaped kernel (bf16). H_I = 64, D_I = 128. Workgroup = 256 keys x QT queries of one
+// sequence. Wave wv holds keys kbase + 64*wv + 32*kb + n (kb = 0, 1) as B operands; the
+// query's q_I (64 x 128) and w (64) are staged in LDS, double-buffered, and read as A operands.
+// ------------------------------------------------------------------------------------------
+constexpr int kPfKeys = 256;
+constexpr int kPfQ = 32;
+constexpr int kQStride = 128 + 8;  // bf16 elements per LDS q_I row (16-byte pad)
+
+__global__ __launch_bounds__(256) void indexer_prefill_mfma(
+    const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
+    const int32_t* __restrict__ q_pos, int T, int N, int m, int b, int t0, int nt,
+    float* __restrict__ scores, int fill_masked) {
+  __shared__ __attribute__((aligned(16))) uint16_t sq[2][64 * kQStride];
+  __shared__ float sw[2][64];
+  __shared__ int snv[kPfQ];
+  __shared__ int smax;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 31, h = lane >> 5;
+  const int kbase = blockIdx.x * kPfKeys;
+  const int r0 = blockIdx.y * kPfQ;  // first row (relative to t0) of this tile
+  const int nrows = min(kPfQ, nt - r0);
+  const int64_t qi0 = (int64_t)b * T + t0 + r0;
+
+  if (tid == 0) smax = 0;
+  __syncthreads();
+  if (tid < nrows) {
+    int v = n_visible(q_pos[qi0 + tid], m, N);
+    snv[tid] = v;
+    atomicMax(&smax, v);
+  }
+  __syncthreads();
+  const int maxnv = smax;
+  if (kbase >= maxnv) {
+    if (fill_masked)
+      for (int r = 0; r < nrows; ++r)
+        for (int s = kbase + tid; s < min(kbase + kPfKeys, N); s += 256)
+          scores[(size_t)(r0 + r) * N + s] = kNegInf;
+    return;
+  }
+
+  // this wave's keys as B operands: kb[0..1][kk]
+  const size_t base_row = (size_t)b * N;
+  u32x4_t kf[2][8];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    int s = min(kbase + 64 * wv + 32 * kb + n, N - 1);
+    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(kI + (base_row + s) * 128 + 64 * h);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) kf[kb][kk] = p[kk];
+  }
+
+  // stage query r (relative) into buffer buf: 64 rows x 256 B = 1024 chunks of 16 B
+  auto stage = [&](int r, int buf) {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(qI + (size_t)(qi0 + r) * (64 * 128));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int c = tid + 256 * j;
+      int hr = c >> 4, cc = c & 15;
+      *reinterpret_cast<u32x4_t*>(&sq[buf][hr * kQStride + cc * 8]) = src[c];
+    }
+    if (tid < 64) sw[buf][tid] = w[(size_t)(qi0 + r) * 64 + tid];
+  };
+
+  stage(0, 0);
+  __syncthreads();
+  for (int r = 0; r < nrows; ++r) {
+    const int buf = r & 1;
+    if (r + 1 < nrows) stage(r + 1, buf ^ 1);
+    const int nv = snv[r];
+    float* srow = scores + (size_t)(r0 + r) * N;
+    if (kbase < nv) {
+      f32x16_t acc[2][2] = {};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          bf16x8_t a = as_bf16x8(
+              *reinterpret_cast<const u32x4_t*>(&sq[buf][(hb * 32 + n) * kQStride + 64 * h + 8 * kk]));
+          acc[hb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(kf[0][kk]), acc[hb][0], 0, 0, 0);
+          acc[hb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(kf[1][kk]), acc[hb][1], 0, 0, 0);
+        }
+      }
+      float part[2] = {0.f, 0.f};
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float wv_ = sw[buf][hb * 32 + 8 * (i >> 2) + 4 * h + (i & 3)];
+          part[0] += wv_ * fmaxf(acc[hb][0][i], 0.f);
+          part[1] += wv_ * fmaxf(acc[hb][1][i], 0.f);
+        }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float v = part[kb] + __shfl_xor(part[kb], 32, 64);
+        int s = kbase + 64 * wv + 32 * kb + n;
+        if (h == 0 && s < N && (fill_masked || s < nv)) srow[s] = (s < nv) ? v : kNegInf;
+      }
+    } else if (fill_masked) {
+      for (int s = kbase + tid; s < min(kbase + kPfKeys, N); s += 256) srow[s] = kNegInf;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Generic scalar kernel: any H_I * D_I <= 16384, fp32 / bf16 queries, fp32 / bf16 / MXFP4 keys.
+// One thread per key; q_I and w of the query row in LDS (as fp32).
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float load_val(const void* p, size_t i, int fmt) {
+  return fmt == FMT_F32 ? reinterpret_cast<const float*>(p)[i]
+                        : bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+}
+
+__device__ __forceinline__ float fp4_val(uint32_t code) {
+  // e2m1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0
+  uint32_t e = (code >> 1) & 3u, mb = code & 1u;
+  float mag = e == 0 ? 0.5f * (float)mb : ldexpf(1.0f + 0.5f * (float)mb, (int)e - 1);
+  return (code & 8u) ? -mag : mag;
+}
+
+__global__ __launch_bounds__(256) void indexer_generic(
+    const void* __restrict__ qI, int q_fmt, const float* __restrict__ w,
+    const void* __restrict__ kI, const uint8_t* __restrict__ ksc, int k_fmt,
+    const int32_t* __restrict__ q_pos, int T, int N, int m, int H_I, int D_I, int64_t qi0,
+    float* __restrict__ scores, int fill_masked) {
+  extern __shared__ float sm[];  // [H_I*D_I] q, [H_I] w
+  const int64_t row = blockIdx.y;
+  const int64_t qi = qi0 + row;
+  const int b = (int)(qi / T);
+  const int nv = n_visible(q_pos[qi], m, N);
+  float* sqf = sm;
+  float* swf = sm + H_I * D_I;
+  for (int i = threadIdx.x; i < H_I * D_I; i += blockDim.x)
+    sqf[i] = load_val(qI, (size_t)qi * H_I * D_I + i, q_fmt);
+  for (int i = threadIdx.x; i < H_I; i += blockDim.x) swf[i] = w[(size_t)qi * H_I + i];
+  __syncthreads();
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= N) return;
+  float* srow = scores + (size_t)row * N;
+  if (s >= nv) {
+    if (fill_masked) srow[s] = kNegInf;
+    return;
+  }
+  const size_t krow = (size_t)b * N + s;
+  float acc = 0.f;
+  for (int j = 0; j < H_I; ++j) {
+    float dot = 0.f;
+    for (int d = 0; d < D_I; ++d) {
+      float kv;
+      if (k_fmt == FMT_MXFP4) {
+        uint32_t byte = reinterpret_cast<const uint8_t*>(kI)[krow * (D_I / 2) + d / 2];
+        uint32_t code = (d & 1) ? (byte >> 4) : (byte & 15u);
+        kv = fp4_val(code) * e8m0_scale(ksc[krow * (D_I / 32) + d / 32]);
+      } else {
+        kv = load_val(kI, krow * D_I + d, k_fmt);
+      }
+      dot += sqf[j * D_I + d] * kv;
+    }
+    acc += swf[j] * fmaxf(dot, 0.f);
+  }
+  srow[s] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void* q_I, int q_fmt,
+                          const float* w, const void* k_I, const uint8_t* k_scale, int k_fmt,
+                          const int32_t* q_pos, float* scores, bool fill_masked,
+                          hipStream_t st) {
+  if (nrows <= 0) return hipSuccess;
+  const bool fast = q_fmt == FMT_BF16 && (k_fmt == FMT_BF16 || k_fmt == FMT_MXFP4) &&
+                    s.H_I == 64 && s.D_I == 128;
+  const int fm = fill_masked ? 1 : 0;
+  if (fast && k_fmt == FMT_BF16 && nrows >= 64) {
+    // prefill: one launch per sequence segment (a workgroup's queries share one sequence)
+    for (int64_t q = qi0; q < qi0 + nrows;) {
+      const int b = (int)(q / s.T);
+      const int64_t seg_end = std::min<int64_t>(qi0 + nrows, (int64_t)(b + 1) * s.T);
+      const int t0 = (int)(q - (int64_t)b * s.T);
+      const int nt = (int)(seg_end - q);
+      dim3 grid((s.N + kPfKeys - 1) / kPfKeys, (nt + kPfQ - 1) / kPfQ);
+      indexer_prefill_mfma<<<grid, 256, 0, st>>>(
+          static_cast<const uint16_t*>(q_I), w, static_cast<const uint16_t*>(k_I), q_pos, s.T,
+          s.N, s.m, b, t0, nt, scores + (size_t)(q - qi0) * s.N, fm);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      q = seg_end;
+    }
+    return hipSuccess;
+  }
+  if (fast) {
+    // keys per wave: enough work per wave to amortise the q_I fragments, while the grid still
+    // fills the chip (~1024 workgroups)
+    const int64_t total = nrows * (int64_t)s.N;
+    int64_t it = total / (32LL * 4 * 1024);
+    const int iters = (int)std::max<int64_t>(1, std::min<int64_t>(16, it));
+    const int keys_per_wg = 4 * 32 * iters;
+    dim3 grid((s.N + keys_per_wg - 1) / keys_per_wg, (unsigned)nrows);
+    if (k_fmt == FMT_BF16)
+      indexer_decode_mfma<FMT_BF16><<<grid, 256, 0, st>>>(
+          static_cast<const uint16_t*>(q_I), w, static_cast<const uint8_t*>(k_I), k_scale, q_pos,
+          s.T, s.N, s.m, qi0, iters, scores, fm);
+    else
+      indexer_decode_mfma<FMT_MXFP4><<<grid, 256, 0, st>>>(
+          static_cast<const uint16_t*>(q_I), w, static_cast<const uint8_t*>(k_I), k_scale, q_pos,
+          s.T, s.N, s.m, qi0, iters, scores, fm);
+    return hipGetLastError();
+  }
+  dim3 grid((s.N + 255) / 256, (unsigned)nrows);
+  size_t shm = sizeof(float) * ((size_t)s.H_I * s.D_I + s.H_I);
+  indexer_generic<<<grid, 256, shm, st>>>(q_I, q_fmt, w, k_I, k_scale, k_fmt, q_pos, s.T, s.N, s.m,
+                                          s.H_I, s.D_I, qi0, scores, fm);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

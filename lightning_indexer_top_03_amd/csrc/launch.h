@@ -1,0 +1,45 @@
+// launch.h - host-side launch interface between the C ABI (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+enum Fmt { FMT_F32 = 0, FMT_BF16 = 1, FMT_MXFP4 = 2 };
+
+struct Shape {
+  int B, T, N, H_I, D_I, H, D_K, D_V, top_k, m, W;
+};
+
+// Query-side tensors are indexed by the flattened row qi = b*T + t; a call covers the rows
+// qi0 .. qi0+nrows-1, and its row-relative buffers (scores, idx) start at row qi0.
+
+// ---- step 0 ----
+hipError_t launch_compress(int B, int64_t n_raw, int D, int m, int fmt, const void* kv_raw,
+                           void* kv_c, hipStream_t st);
+
+// ---- step 1 ----
+// scores: [nrows, N] row-relative. fill_masked: write -inf for s >= n_vis.
+hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void* q_I, int q_fmt,
+                          const float* w,
+                          const void* k_I, const uint8_t* k_scale, int k_fmt, const int32_t* q_pos,
+                          float* scores, bool fill_masked, hipStream_t st);
+
+// ---- step 2 ----
+// scores: [nrows, N] row-relative, idx: [nrows, top_k] row-relative, rows qi0 .. qi0+nrows-1.
+size_t topk_ws_bytes(const Shape& s, int64_t nrows);
+hipError_t launch_topk(const Shape& s, int64_t qi0, int64_t nrows, const float* scores,
+                       const int32_t* q_pos, int32_t* idx, void* ws, hipStream_t st);
+
+// ---- step 3 ----
+// idx: [nrows, top_k] row-relative; q/out/lse indexed by the flattened row qi.
+int attend_splits(const Shape& s, int64_t nrows, int fmt);
+size_t attend_ws_bytes(const Shape& s, int64_t nrows, int fmt);
+hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, const void* q,
+                         const void* kv, const int32_t* idx, const void* kv_raw, int64_t raw_base,
+                         int64_t n_raw, const int32_t* q_pos, float scale, void* out, float* lse,
+                         void* ws, hipStream_t st, hipEvent_t between = nullptr);
+
+}  // namespace dsa

@@ -1,0 +1,141 @@
+"""C-ABI contract of libdsa.so, on the host: symbols, status codes, validation, workspace sizing.
+
+Every call here fails validation (or the gfx950 device check) before any kernel is launched,
+so these run without a GPU; the pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import lightning_indexer_top_03_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+P = 0x10000  # a 16-byte-aligned dummy address
+L = dsa.lib()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)) -
+                  {"sizeof", "defined", "floor", "min", "max"})
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert set(names) == set(dsa.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    for code in range(8):
+        s = L.dsa_status_str(code).decode()
+        assert s.startswith("DSA_"), s
+    assert L.dsa_status_str(99).decode() == "unknown dsa_status"
+    assert L.dsa_version() == 100
+
+
+def _dims(**kw):
+    base = dict(B=2, T=3, N=100, H_I=64, D_I=128, H=128, D_K=576, D_V=512, top_k=32, m=1, W=0)
+    base.update(kw)
+    return dsa.Dims(*[base[n] for n, _ in dsa.Dims._fields_])
+
+
+def _idx_call(d, q_dt=dsa.BF16, k_dt=dsa.BF16, q_I=P, w=P, k_I=P, k_scale=None, q_pos=P, sc=P):
+    return L.indexer_scores(ctypes.byref(d), q_I, q_dt, w, k_I, k_scale, k_dt, q_pos, sc, None)
+
+
+def test_indexer_validation():
+    d = _dims()
+    assert L.indexer_scores(None, P, 1, P, P, None, 1, P, P, None) == 1      # NULL dims
+    assert _idx_call(d, q_I=None) == 1                                         # NULL q_I
+    assert _idx_call(d, q_pos=None) == 1
+    assert _idx_call(_dims(N=0)) == 2                                          # bad shape
+    assert _idx_call(_dims(top_k=5000)) == 2
+    assert _idx_call(d, q_dt=dsa.MXFP4) == 3                                   # bad q dtype
+    assert _idx_call(d, q_dt=dsa.F32, k_dt=dsa.BF16) == 3                      # mixed
+    assert _idx_call(d, k_dt=dsa.MXFP4) == 1                                   # FP4 w/o scales
+    assert _idx_call(_dims(D_I=48), k_dt=dsa.MXFP4, k_scale=P) == 2            # D_I % 32
+    assert _idx_call(d, k_scale=P) == 3                                        # scales w/o FP4
+    assert _idx_call(_dims(H_I=128, D_I=128), q_dt=dsa.F32, k_dt=dsa.F32) == 2 # generic LDS cap
+    assert _idx_call(d, q_I=P + 8) == 4                                        # misaligned
+    assert _idx_call(d, sc=P + 4) == 4
+
+
+def test_topk_validation():
+    d = _dims()
+    assert L.topk_select(ctypes.byref(d), None, P, P, None, 0, None) == 1
+    assert L.topk_select(ctypes.byref(d), P + 4, P, P, None, 0, None) == 4
+    assert L.topk_select(ctypes.byref(_dims(top_k=0)), P, P, P, None, 0, None) == 2
+    assert L.topk_select(ctypes.byref(_dims(m=0)), P, P, P, None, 0, None) == 2
+
+
+def _att(d, dt=dsa.BF16, q=P, kv=P, idx=P, raw=None, base=0, nraw=0, ws=None, wsb=0, out=P):
+    return L.sparse_mla_attend(ctypes.byref(d), dt, q, kv, idx, raw, base, nraw, P, 0.1, out,
+                               None, ws, wsb, None)
+
+
+def test_attend_validation():
+    d = _dims()
+    assert _att(d, q=None) == 1
+    assert _att(_dims(W=16)) == 1                  # window without kv_raw
+    assert _att(_dims(D_V=600)) == 2               # D_V > D_K
+    assert _att(_dims(D_K=1028)) == 2
+    assert _att(d, dt=dsa.MXFP4) == 3
+    assert _att(d, out=P + 2) == 4
+    assert _att(_dims(W=16), raw=P, base=-1) == 2
+    # few queries -> split partials need a workspace
+    dd = _dims(B=1, T=1, top_k=2048)
+    need = L.dsa_workspace_bytes(ctypes.byref(dd), dsa.OP_ATTEND)
+    assert need > 0
+    assert _att(dd) == 5
+    assert _att(dd, ws=P, wsb=need - 1) == 5
+
+
+def test_forward_validation_and_workspace():
+    d = _dims()
+    a = dsa.ForwardArgs(dsa.BF16, dsa.BF16, P, P, P, None, P, P, None, 0, 0, 0, P, 0.1, P, None,
+                        None, None, None, 0)
+    need = L.dsa_workspace_bytes(ctypes.byref(d), dsa.OP_FORWARD)
+    assert need >= 2 * 3 * 100 * 4 + 2 * 3 * 32 * 4
+    assert L.dsa_forward(ctypes.byref(d), None, P, need, None) == 1
+    assert L.dsa_forward(ctypes.byref(d), ctypes.byref(a), None, 0, None) == 5
+    assert L.dsa_forward(ctypes.byref(d), ctypes.byref(a), P, need - 1, None) == 5
+    a.compress = 1
+    assert L.dsa_forward(ctypes.byref(d), ctypes.byref(a), P, need, None) == 1  # no kv_raw
+    a.kv_raw, a.n_raw = P, 399
+    assert L.dsa_forward(ctypes.byref(_dims(m=4)), ctypes.byref(a), P, need, None) == 2  # 399//4 != 100
+    a.compress, a.kv_raw, a.n_raw = 0, None, 0
+    a.q_I = P + 8
+    assert L.dsa_forward(ctypes.byref(d), ctypes.byref(a), P, need, None) == 4
+
+
+def test_compress_validation():
+    d = _dims(m=4)
+    assert L.kv_compress_mean(ctypes.byref(d), dsa.BF16, None, 400, P, None) == 1
+    assert L.kv_compress_mean(ctypes.byref(d), dsa.MXFP4, P, 400, P, None) == 3
+    assert L.kv_compress_mean(ctypes.byref(_dims(m=0)), dsa.BF16, P, 400, P, None) == 2
+    assert L.kv_compress_mean(ctypes.byref(d), dsa.BF16, P, -1, P, None) == 2
+
+
+def test_workspace_sizes():
+    # decode-shaped calls split the entry list; large prefill calls do not need partials
+    dec = _dims(B=16, T=1, N=8192, top_k=2048)
+    pre = _dims(B=1, T=4096, N=4096, top_k=2048)
+    assert L.dsa_workspace_bytes(ctypes.byref(dec), dsa.OP_ATTEND) > 0
+    assert L.dsa_workspace_bytes(ctypes.byref(pre), dsa.OP_ATTEND) == 0
+    assert L.dsa_workspace_bytes(ctypes.byref(_dims(N=0)), dsa.OP_FORWARD) == 0
+    big = _dims(B=1, T=32768, N=32768, top_k=2048)
+    # fused prefill chunks its score rows to a bounded workspace (< 0.6 GB)
+    assert L.dsa_workspace_bytes(ctypes.byref(big), dsa.OP_FORWARD) < 600 << 20
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU device error path")
+def test_valid_call_without_gpu_reports_device_error():
+    d = _dims(B=1, T=1, N=64, top_k=8)
+    assert L.topk_select(ctypes.byref(d), P, P, P, None, 0, None) == 6

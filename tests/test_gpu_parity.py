@@ -1,0 +1,226 @@
+"""GPU parity of each C-ABI call against the fp64 oracle, on the same seeded inputs.
+
+Sizes span several tiles with ragged tails and run in seconds; the full-size workloads are in
+test_gpu_workloads.py. Every call goes through the C ABI (lightning_indexer_top_03_amd).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (check_attention, check_scores, check_topk, log, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import lightning_indexer_top_03_amd as dsa
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def _cfg(name, **kw):
+    return synth.CONFIGS[name].with_(**kw)
+
+
+# --------------------------------------------------------------------------- compression ----
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_compress_mean(dt):
+    c = _cfg("csa_prefill", B=2, N=1000, n_raw=4003, dt=dt, name="compress_" + dt)
+    raw = synth.normal(c.seed, synth.TID_KV, (2, 4003, 576), 1.0 / 24, dt)
+    log(f"[compress {dt}] n_raw=4003 m=4")
+    out = to_host(dsa.kv_compress_mean(to_dev(raw), 4))
+    torch.cuda.synchronize()
+    assert out.shape == (2, 1000, 576)
+    for b in range(2):
+        ref = oracle.compress_mean(raw[b], 4)
+        got = oracle.decode(out[b])
+        if dt == "f32":
+            np.testing.assert_allclose(got, ref, rtol=2e-7, atol=1e-12)
+        else:
+            # one RNE rounding of an fp32 sum: within one bf16 ulp of the exact mean
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+            assert (np.abs(got - ref) <= ulp).all()
+            assert (np.abs(got - ref) <= 0.5 * ulp * (1 + 1e-6)).mean() > 0.999
+
+
+# ------------------------------------------------------------------------------- indexer ----
+
+def _run_indexer(c, label):
+    wl = synth.make_workload(c)
+    k = wl.k_I()
+    kdev = (to_dev(k[0]), to_dev(k[1])) if c.k_dt == "mxfp4" else to_dev(k)
+    log(f"[indexer {label}] B={c.B} T={c.T} N={c.N} k_dt={c.k_dt}")
+    sc = dsa.indexer_scores(to_dev(wl.q_I()), to_dev(wl.w()), kdev, to_dev(wl.q_pos()), m=c.m)
+    torch.cuda.synchronize()
+    sc = to_host(sc)
+    run = oracle.QueryRunner(wl)
+    worst = 0.0
+    rows = [(b, t) for b in range(c.B) for t in range(c.T)]
+    if len(rows) > 48:
+        rng = np.random.default_rng(0)
+        pick = rng.choice(len(rows), 40, replace=False)
+        rows = sorted({rows[i] for i in pick} | {rows[0], rows[-1]})
+    for b, t in rows:
+        ref = run.scores(b, t)
+        nv = oracle.n_vis(int(wl.q_pos()[b, t]), c.m, c.N)
+        worst = max(worst, check_scores(sc[b, t], ref, nv, what=f"{label} b={b} t={t}"))
+    log(f"[indexer {label}] max rel err {worst:.2e}")
+    return sc
+
+
+def test_indexer_decode_bf16_ragged():
+    # decode-shaped (MFMA streaming kernel): ragged N, a partially visible row
+    c = _cfg("decode", B=3, N=3001, name="idx_decode")
+    c = c.with_(pos0=3000)
+    _run_indexer(c, "decode")
+    _run_indexer(c.with_(pos0=1234, name="idx_decode_partial"), "decode-partial")
+
+
+def test_indexer_prefill_bf16_causal():
+    # prefill-shaped (MFMA, keys in registers, queries through LDS): causal triangle, ragged
+    c = _cfg("prefill", B=2, T=700, N=700, name="idx_prefill")
+    _run_indexer(c, "prefill")
+
+
+def test_indexer_prefill_csa_blocks():
+    c = _cfg("csa_prefill", B=1, T=300, N=900, pos0=3300, pos_stride=2, compress=False,
+             n_raw=0, W=0, name="idx_csa")
+    _run_indexer(c, "csa")
+
+
+def test_indexer_mxfp4_keys():
+    c = _cfg("csa_decode", B=2, N=5003, pos0=4 * 5003 - 1, name="idx_fp4")
+    _run_indexer(c, "mxfp4")
+    _run_indexer(c.with_(pos0=4 * 4000 + 2, name="idx_fp4_partial"), "mxfp4-partial")
+
+
+def test_indexer_generic_fp32_and_small_heads():
+    _run_indexer(synth.CONFIGS["tiny"], "tiny-f32")
+    _run_indexer(_cfg("tiny", dt="bf16", k_dt="bf16", name="tiny_bf16"), "tiny-bf16")
+    _run_indexer(_cfg("tiny", dt="bf16", k_dt="mxfp4", name="tiny_fp4"), "tiny-fp4")
+
+
+# --------------------------------------------------------------------------------- top-k ----
+
+def _topk_case(label, n_rows, N, k, m=1, ties=False, pos=None, seed=0):
+    rng = np.random.default_rng(seed)
+    s = synth.normal(50 + seed, 1, (n_rows, N), 1.0, "f32")
+    if ties:
+        s = (np.round(s * 8) / 8).astype(np.float32)
+        s[0, : N // 2] = 0.5  # one row with a very wide tie
+    if pos is None:
+        pos = rng.integers(0, N * m, n_rows).astype(np.int32)
+        pos[0] = N * m - 1
+    pos = pos.reshape(n_rows, 1).astype(np.int32)
+    log(f"[topk {label}] rows={n_rows} N={N} k={k} m={m} ties={ties}")
+    idx = to_host(dsa.topk_select(to_dev(s.reshape(n_rows, 1, N)), to_dev(pos), k, m=m))
+    torch.cuda.synchronize()
+    for r in range(n_rows):
+        nv = oracle.n_vis(int(pos[r, 0]), m, N)
+        ref, cnt = oracle.topk_row(s[r].astype(np.float64), nv, k)
+        got = idx[r, 0]
+        # same fp32 values on both sides: the set is unique (lowest index wins exact ties)
+        assert np.array_equal(np.sort(got[got >= 0]), ref[ref >= 0]), f"{label} row {r}"
+        assert (got < 0).sum() == k - cnt
+
+
+def test_topk_exact_sets():
+    _topk_case("decode", 16, 8192, 2048)
+    _topk_case("ragged", 9, 3001, 512, seed=1)
+    _topk_case("small-k", 5, 777, 7, seed=2)
+    _topk_case("keep-all", 4, 1500, 2048, seed=3)
+    _topk_case("csa", 6, 4000, 1024, m=4, seed=4)
+    _topk_case("long", 2, 262144, 1024, seed=5)
+
+
+def test_topk_ties_take_lowest_index():
+    _topk_case("ties", 8, 5000, 1000, ties=True, seed=6)
+    # all-equal row: exactly the first k indices
+    s = np.zeros((1, 1, 3000), np.float32)
+    s[0, 0, ::2] = -0.0  # -0 ranks equal to +0
+    idx = to_host(dsa.topk_select(to_dev(s), to_dev(np.array([[2999]], np.int32)), 100))
+    assert np.array_equal(np.sort(idx[0, 0]), np.arange(100))
+
+
+# ----------------------------------------------------------------------------- attention ----
+
+def _attend_case(c, label, seed=0, frac_masked=0.05):
+    wl = synth.make_workload(c)
+    rng = np.random.default_rng(seed)
+    B, T, k = c.B, c.T, c.top_k
+    pos = wl.q_pos()
+    idx = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            nv = oracle.n_vis(int(pos[b, t]), c.m, c.N)
+            n = min(k, nv)
+            sel = rng.choice(nv, n, replace=False).astype(np.int32)
+            drop = rng.random(n) < frac_masked
+            sel[drop] = -1
+            idx[b, t, :n] = sel
+            rng.shuffle(idx[b, t])
+    kv = wl.kv() if not c.compress else None
+    raw = wl.kv_raw()
+    base, n_raw = wl.raw_extent()
+    log(f"[attend {label}] B={B} T={T} N={c.N} k={k} W={c.W} dt={c.dt}")
+    out, lse = dsa.sparse_mla_attend(to_dev(wl.q()), to_dev(kv), to_dev(idx), to_dev(pos), c.D_V,
+                                     c.softmax_scale, kv_raw=to_dev(raw) if raw is not None else None,
+                                     raw_base=base, W=c.W, m=c.m)
+    torch.cuda.synchronize()
+    out, lse = oracle.decode(to_host(out)), to_host(lse)
+    worst = (0.0, 0.0)
+    for b in range(B):
+        for t in range(T):
+            ro, rl = oracle.attend_row(wl.q()[b, t], kv[b], idx[b, t], c.D_V, c.softmax_scale,
+                                       p=int(pos[b, t]), W=c.W,
+                                       kv_raw=raw[b] if raw is not None else None, raw_base=base)
+            mx, sc = check_attention(out[b, t], lse[b, t], ro, rl, what=f"{label} b={b} t={t}")
+            worst = max(worst, (mx, sc))
+    log(f"[attend {label}] max abs err {worst[0]:.3e} (max|ref| {worst[1]:.3e})")
+
+
+def test_attend_decode_split():
+    c = _cfg("decode", B=4, N=3001, pos0=3000, name="att_decode")
+    _attend_case(c, "decode")
+    _attend_case(c.sharp(), "decode-sharp", seed=1)
+
+
+def test_attend_prefill_many_rows_ragged_k():
+    # enough rows for the no-split plan; k not a multiple of the 32-entry tile
+    c = _cfg("decode", B=1, T=300, N=2000, top_k=1000, pos0=1700, name="att_rows")
+    _attend_case(c.sharp(), "rows-sharp", seed=2)
+
+
+def test_attend_window_csa():
+    c = _cfg("csa_decode", B=2, N=2500, pos0=4 * 2500 - 1, n_raw=128,
+             raw_base=4 * 2500 - 128, name="att_win")
+    _attend_case(c, "window")
+    _attend_case(c.sharp(), "window-sharp", seed=3)
+    # window clipped at position 0 and partly outside kv_raw
+    c2 = _cfg("csa_decode", B=1, N=100, pos0=40, n_raw=30, raw_base=20, top_k=64, name="att_clip")
+    _attend_case(c2.sharp(), "window-clip", seed=4)
+
+
+def test_attend_generic_fp32():
+    _attend_case(synth.CONFIGS["tiny"], "tiny-f32")
+    _attend_case(synth.CONFIGS["tiny"].sharp(), "tiny-f32-sharp", seed=5)
+    _attend_case(_cfg("tiny", dt="bf16", name="tiny_bf16").sharp(), "tiny-bf16-sharp", seed=6)
+
+
+def test_attend_all_masked_row_gives_zero():
+    c = _cfg("decode", B=1, N=500, top_k=64, pos0=499, name="att_empty")
+    wl = synth.make_workload(c)
+    idx = np.full((1, 1, 64), -1, np.int32)
+    out, lse = dsa.sparse_mla_attend(to_dev(wl.q()), to_dev(wl.kv()), to_dev(idx),
+                                     to_dev(wl.q_pos()), 512, c.softmax_scale)
+    torch.cuda.synchronize()
+    assert (to_host(out.float()) == 0).all()
+    assert np.isneginf(to_host(lse)).all()
