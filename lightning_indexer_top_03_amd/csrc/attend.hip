@@ -222,6 +222,254 @@ __global__ __launch_bounds__(256, 1) void attend_mfma(
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// attend_mfma_dma: same math as attend_mfma for D_K = 576, D_V = 512, but the gather goes
+// straight from HBM into an NS-stage LDS ring with global_load_lds_dwordx4 (no register staging),
+// and the P V B operand is read from the row-major tile with ds_read_b64_tr_b16 (no transposed
+// copy of V). Per 32-entry tile and wave (8 rows): 8 row DMAs of the 1024-byte latent part (one
+// row per instruction, fully coalesced) and one DMA of the 8 rows' 128-byte rope parts.
+// LDS tile layout: latent rows at a 1040-byte stride (16-byte pad: conflict-free 16-byte reads by
+// 8 consecutive rows), then the rope parts as [32 rows][8 chunks of 16 B] with the chunk slot
+// XOR-swizzled by (row % 8). Waits are explicit (s_waitcnt vmcnt + s_barrier without a fence),
+// so the DMAs of the next NS-1 tiles stay in flight while the current tile is computed.
+//
+// ds_read_b64_tr_b16, within each group of 16 lanes: if lane j reads the 4 bf16 M[j][0..3],
+// lane 4a+b receives {M[a][b], M[a+4][b], M[a+8][b], M[a+12][b]}. Lane j of group g reading row
+// 4g + j/4 at column 16*db + 4*(j%4) therefore receives, in lane n of the group, V[4g+0..3][16db+n]:
+// the B-operand slots 0..3 of v_mfma_f32_16x16x32_bf16 for dim n (entries 4g..4g+3), which is the
+// same slot -> entry map as the P operand taken from the S^T accumulators.
+// ------------------------------------------------------------------------------------------
+constexpr int kLatStride = 1040;                 // bytes per latent row in LDS
+constexpr int kStageLat = kTile * kLatStride;    // 33280
+constexpr int kStageRope = kTile * 128;          // 4096
+constexpr int kStage = kStageLat + kStageRope;   // 37376
+
+template <int N_>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N_) : "memory");
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 8 ds_read_b64_tr_b16 for dim blocks d0 .. d0+3 (entry halves 4g.. and 16+4g..), waited for
+// inside the same asm block. Written as asm because the builtin carries no memory operand, which
+// makes the compiler wait for every LDS DMA still in flight before it.
+#define DSA_TR(i, off) "ds_read_b64_tr_b16 %" #i ", %8 offset:" #off "\n"
+#define DSA_TR_BLOCK(D0)                                                                        \
+  case D0:                                                                                      \
+    asm volatile(DSA_TR(0, D0 * 32) DSA_TR(1, 16640 + D0 * 32) DSA_TR(2, D0 * 32 + 32)          \
+                 DSA_TR(3, 16640 + D0 * 32 + 32) DSA_TR(4, D0 * 32 + 64)                        \
+                 DSA_TR(5, 16640 + D0 * 32 + 64) DSA_TR(6, D0 * 32 + 96)                        \
+                 DSA_TR(7, 16640 + D0 * 32 + 96) "s_waitcnt lgkmcnt(0)"                         \
+                 : "=&v"(tr[0]), "=&v"(tr[1]), "=&v"(tr[2]), "=&v"(tr[3]), "=&v"(tr[4]),         \
+                   "=&v"(tr[5]), "=&v"(tr[6]), "=&v"(tr[7])                                     \
+                 : "v"(vaddr)                                                                   \
+                 : "memory");                                                                   \
+    break;
+__device__ __forceinline__ void tr_read_block(u32x2_t* tr, uint32_t vaddr, int d0) {
+  switch (d0) {
+    DSA_TR_BLOCK(0) DSA_TR_BLOCK(4) DSA_TR_BLOCK(8) DSA_TR_BLOCK(12)
+    DSA_TR_BLOCK(16) DSA_TR_BLOCK(20) DSA_TR_BLOCK(24) DSA_TR_BLOCK(28)
+  }
+}
+#undef DSA_TR_BLOCK
+#undef DSA_TR
+
+template <int NS>
+__global__ __launch_bounds__(256, NS == 2 ? 2 : 1) void attend_mfma_dma(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw, int64_t raw_base,
+    int64_t n_raw, const int32_t* __restrict__ q_pos, int T, int N, int H, int top_k, int W,
+    float scale_log2, int64_t qi0, int nsplit, int per_split, uint16_t* __restrict__ out,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  constexpr int DK = 576, DV = 512, KK = DK / 32, DB = DV / 16;
+  constexpr int DMAS = 9;  // DMA instructions per wave per tile
+  __shared__ __attribute__((aligned(16))) char smem[NS * kStage];
+  __shared__ int sValid[NS][kTile];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t row = blockIdx.z;
+  const int64_t qi = qi0 + row;
+  const int b = (int)(qi / T);
+  const int p = q_pos[qi];
+  const int split = blockIdx.x;
+  const int h0 = blockIdx.y * 64 + wv * 16;
+  const int E = top_k + W;
+  const int e_begin = split * per_split;
+  const int e_end = min(E, e_begin + per_split);
+  const int ntiles = e_end > e_begin ? (e_end - e_begin + kTile - 1) / kTile : 0;
+  const int32_t* __restrict__ idxrow = idx + row * (int64_t)top_k;
+  const uint16_t* fallback = kv + (size_t)b * N * DK;  // any valid row; masked in the softmax
+
+  u32x4_t qf[KK];
+  {
+    const uint16_t* qh = q + ((size_t)qi * H + h0 + n) * DK + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const u32x4_t*>(qh + 32 * kk);
+    // complete the q loads here, so that no wait for them lands inside the DMA pipeline below
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qf[kk]));
+  }
+  f32x4_t acc[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) acc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+
+  // issue the DMAs of tile t (this wave's rows 8*wv .. 8*wv+7)
+  auto issue = [&](int t) {
+    const int stage = t % NS;
+    // the DMA destination goes through an opaque wave-uniform integer: the waits for these
+    // transfers are the explicit vmcnt waits of the pipeline below
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_void_t*)(smem + stage * kStage));
+    const int e0 = e_begin + kTile * t + 8 * wv;
+    const uint16_t* rp[8];
+    uint32_t okm = 0;
+#pragma unroll
+    for (int r8 = 0; r8 < 8; ++r8) {
+      const int e = e0 + r8;
+      const uint16_t* src = e < e_end ? entry_row<uint16_t>(e, idxrow, top_k, kv, b, N, DK,
+                                                            kv_raw, raw_base, n_raw, p, W)
+                                      : nullptr;
+      okm |= (src != nullptr ? 1u : 0u) << r8;
+      rp[r8] = src ? src : fallback;
+    }
+#pragma unroll
+    for (int r8 = 0; r8 < 8; ++r8)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(rp[r8] + 8 * lane),
+          (lds_void_t*)(uintptr_t)(sbase + (8 * wv + r8) * kLatStride), 16, 0, 0);
+    const int rr = lane >> 3;  // row within the wave's 8
+    const uint16_t* mine = rp[0];
+#pragma unroll
+    for (int r8 = 1; r8 < 8; ++r8) mine = rr == r8 ? rp[r8] : mine;
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const void*>(mine + 512 + 8 * ((lane & 7) ^ rr)),
+        (lds_void_t*)(uintptr_t)(sbase + kStageLat + wv * 1024), 16, 0, 0);
+    if (lane < 8) sValid[stage][8 * wv + lane] = (okm >> lane) & 1u;
+  };
+
+  for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t);
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + NS - 1 < ntiles) issue(t + NS - 1);
+    const int later = min(NS - 1, ntiles - 1 - t);
+    if (later >= 2) wait_vm<2 * DMAS>();
+    else if (later == 1) wait_vm<DMAS>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+
+    const int stage = t % NS;
+    const char* sb = smem + stage * kStage;
+    f32x4_t st[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb) {
+      const int R = eb * 16 + n;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const char* ap;
+        if (kk < 16) {
+          ap = sb + R * kLatStride + (32 * kk + 8 * g) * 2;
+        } else {
+          const int c = 4 * (kk - 16) + g;
+          ap = sb + kStageLat + R * 128 + ((c ^ (R & 7)) * 16);
+        }
+        bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(ap));
+        st[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(qf[kk]), st[eb], 0, 0, 0);
+      }
+    }
+    float z[8];
+    float mx = kNegInf;
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = eb * 16 + 4 * g + i;
+        float v = sValid[stage][e] ? st[eb][i] * scale_log2 : kNegInf;
+        z[eb * 4 + i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    float alpha, psum = 0.f;
+    uint32_t pk[4];
+    if (m_new == kNegInf) {
+      alpha = 1.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[i] = 0u;
+    } else {
+      alpha = exp2f(m_run - m_new);
+      float pe[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pe[i] = exp2f(z[i] - m_new);
+        psum += pe[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pe[2 * i], pe[2 * i + 1]);
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    float ai[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i, 64);
+    const bf16x8_t pa = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+    // transposed V reads: rows 4g + n/4 (entries 4g..4g+3) and 16 + 4g + n/4, column 4*(n%4)
+    const uint32_t vaddr = (uint32_t)(uintptr_t)(lds_void_t*)(sb + (4 * g + (n >> 2)) * kLatStride +
+                                                             8 * (n & 3));
+#pragma unroll
+    for (int d0 = 0; d0 < DB; d0 += 4) {
+      u32x2_t tr[8];
+      tr_read_block(tr, vaddr, d0);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[d0 + d][i] *= ai[i];
+        const u32x4_t bw = {tr[2 * d][0], tr[2 * d][1], tr[2 * d + 1][0], tr[2 * d + 1][1]};
+        acc[d0 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(bw), acc[d0 + d], 0, 0, 0);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+  }
+
+  float li[4], mi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    li[i] = __shfl(l_run, 4 * g + i, 64);
+    mi[i] = __shfl(m_run, 4 * g + i, 64);
+  }
+  if (nsplit == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float inv = li[i] > 0.f ? 1.f / li[i] : 0.f;
+      uint16_t* orow = out + ((size_t)qi * H + h0 + 4 * g + i) * DV + n;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) orow[16 * d] = f32_to_bf16(acc[d][i] * inv);
+    }
+    if (g == 0 && lse)
+      lse[(size_t)qi * H + h0 + n] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t hrow = ((size_t)row * H + h0 + 4 * g + i) * nsplit + split;
+      float* po = part_o + hrow * DV + n;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) po[16 * d] = acc[d][i];
+      if (n == 0) {
+        part_ml[hrow * 2] = mi[i];
+        part_ml[hrow * 2 + 1] = li[i];
+      }
+    }
+  }
+}
+
 // Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 template <typename OT>
 __global__ __launch_bounds__(128) void attend_combine(
@@ -364,13 +612,13 @@ hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, co
     float* part_o = static_cast<float*>(ws);
     float* part_ml = ns > 1 ? part_o + (size_t)nrows * s.H * ns * s.D_V : nullptr;
     dim3 grid(ns, s.H / 64, (unsigned)nrows);
-    attend_mfma<576, 512><<<grid, 256, 0, st>>>(
+    attend_mfma_dma<2><<<grid, 256, 0, st>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
         static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H, s.top_k, s.W,
         scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse, part_o, part_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
-    if (between) hipEventRecord(between, st);
+    if (between) (void)hipEventRecord(between, st);
     attend_combine<uint16_t><<<dim3(s.H, (unsigned)nrows), 128, 0, st>>>(
         part_o, part_ml, qi0, s.H, s.D_V, ns, static_cast<uint16_t*>(out), lse);
     return hipGetLastError();

@@ -117,7 +117,11 @@ __global__ __launch_bounds__(256) void indexer_decode_mfma(
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) wr[hb][r] = wrow[hb * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
+    for (int j = 0; j < 4; ++j) {
+      const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(wrow + hb * 32 + 8 * j + 4 * h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wr[hb][4 * j + i] = w4[i];
+    }
 
   const size_t base_row = (size_t)b * N;
   const int last = min(key0 + keys_per_wave, nv);  // exclusive end of computed keys
@@ -352,7 +356,7 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
     // keys per wave: enough work per wave to amortise the q_I fragments, while the grid still
     // fills the chip (~1024 workgroups)
     const int64_t total = nrows * (int64_t)s.N;
-    int64_t it = total / (32LL * 4 * 1024);
+    int64_t it = total / (32LL * 1024);  // ~1024 waves in flight
     const int iters = (int)std::max<int64_t>(1, std::min<int64_t>(16, it));
     const int keys_per_wg = 4 * 32 * iters;
     dim3 grid((s.N + keys_per_wg - 1) / keys_per_wg, (unsigned)nrows);
