@@ -310,9 +310,10 @@ __global__ __launch_bounds__(256, NS == 2 ? 2 : 1) void attend_mfma_dma(
     const uint16_t* qh = q + ((size_t)qi * H + h0 + n) * DK + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const u32x4_t*>(qh + 32 * kk);
-    // complete the q loads here, so that no wait for them lands inside the DMA pipeline below
+    // complete the q loads here and make the values opaque: no wait for them inside the DMA
+    // pipeline below, and no re-loading next to each use
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qf[kk]));
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(qf[kk]));
   }
   f32x4_t acc[DB];
 #pragma unroll

@@ -83,20 +83,24 @@ __device__ __forceinline__ bf16x8_t key_operand(const KeyTile<KFMT>& kt, int kk,
   }
 }
 
-template <int KFMT>
+constexpr int kDecodeMaxIters = 16;  // 32-key tiles per wave
+
+template <int KFMT, int ITERS>
 __global__ __launch_bounds__(256) void indexer_decode_mfma(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
     const uint8_t* __restrict__ ksc, const int32_t* __restrict__ q_pos, int T, int N, int m,
-    int64_t qi0, int iters, float* __restrict__ scores, int fill_masked) {
+    int64_t qi0, float* __restrict__ scores, int fill_masked) {
   const int64_t row = blockIdx.y;
   const int64_t qi = qi0 + row;
   const int b = (int)(qi / T);
   const int nv = n_visible(q_pos[qi], m, N);
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h = lane >> 5;
-  const int keys_per_wave = 32 * iters;
+  constexpr int keys_per_wave = 32 * ITERS;
   const int key0 = (blockIdx.x * 4 + wv) * keys_per_wave;
   float* __restrict__ srow = scores + (size_t)row * N;
+  __shared__ float sres[4][32 * ITERS];
 
   if (key0 >= nv) {
     if (fill_masked)
@@ -122,19 +126,31 @@ __global__ __launch_bounds__(256) void indexer_decode_mfma(
 #pragma unroll
       for (int i = 0; i < 4; ++i) wr[hb][4 * j + i] = w4[i];
     }
+  // complete the q_I / w loads before the key pipeline and make the values opaque, so that the
+  // compiler neither waits for them inside the pipeline (draining the prefetched tile) nor
+  // re-loads them next to each use
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+v"(qa[hb][kk]));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(wr[hb][r]));
+  }
 
   const size_t base_row = (size_t)b * N;
   const int last = min(key0 + keys_per_wave, nv);  // exclusive end of computed keys
-  KeyTile<KFMT> cur, nxt;
-  float lo_c = 0.f, hi_c = 0.f, lo_n = 0.f, hi_n = 0.f;
-  load_key_tile<KFMT>(cur, kI, ksc, base_row + min(key0 + n, N - 1), h, lo_c, hi_c);
-  for (int s0 = key0; s0 < last; s0 += 32) {
-    const bool more = s0 + 32 < last;
-    if (more) load_key_tile<KFMT>(nxt, kI, ksc, base_row + min(s0 + 32 + n, N - 1), h, lo_n, hi_n);
+  const int ntiles = (last - key0 + 31) / 32;      // wave-uniform
+  // Two register buffers, ping-pong: the next tile is always requested (rows clamped to the
+  // sequence) before the current one is consumed, with no branch around the loads, so the
+  // wait for the current tile leaves the next one in flight.
+  KeyTile<KFMT> ta, tb;
+  float lo_a = 0.f, hi_a = 0.f, lo_b = 0.f, hi_b = 0.f;
+  auto tile_row = [&](int t) { return base_row + min(key0 + 32 * t + n, N - 1); };
+  auto consume = [&](const KeyTile<KFMT>& kt, float slo, float shi, int t) {
     f32x16_t acc0 = {}, acc1 = {};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      bf16x8_t kb = key_operand<KFMT>(cur, kk, lo_c, hi_c);
+      bf16x8_t kb = key_operand<KFMT>(kt, kk, slo, shi);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[0][kk]), kb, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[1][kk]), kb, acc1, 0, 0, 0);
     }
@@ -145,18 +161,33 @@ __global__ __launch_bounds__(256) void indexer_decode_mfma(
       part += wr[1][r] * fmaxf(acc1[r], 0.f);
     }
     part += __shfl_xor(part, 32, 64);
-    const int s = s0 + n;
-    if (h == 0 && s < N) srow[s] = (s < nv) ? part : kNegInf;
-    if (more) {
-      cur = nxt;
-      lo_c = lo_n;
-      hi_c = hi_n;
+    // scores go to LDS (no vector-memory counter traffic inside the pipeline), flushed below
+    if (h == 0) sres[wv][32 * t + n] = part;
+  };
+  // Straight-line, branch-free (ITERS is a compile-time count): the loads of tile t+1 are issued
+  // before tile t is consumed. Rows past the wave's visible range are clamped and their results
+  // never flushed; computing them keeps the code free of branches the loads could sink into.
+  load_key_tile<KFMT>(ta, kI, ksc, tile_row(0), h, lo_a, hi_a);
+#pragma unroll
+  for (int t = 0; t < ITERS; ++t) {
+    if (t % 2 == 0) {
+      if (t + 1 < ITERS) load_key_tile<KFMT>(tb, kI, ksc, tile_row(t + 1), h, lo_b, hi_b);
+      __builtin_amdgcn_sched_barrier(0);  // keep the next tile's loads ahead of this tile's use
+      consume(ta, lo_a, hi_a, t);
+    } else {
+      if (t + 1 < ITERS) load_key_tile<KFMT>(ta, kI, ksc, tile_row(t + 1), h, lo_a, hi_a);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(tb, lo_b, hi_b, t);
     }
   }
-  if (fill_masked) {
-    // keys of this wave's range past the visible end, in whole 32-key tiles not computed above
-    int s_start = key0 + ((last - key0 + 31) / 32) * 32;
-    for (int s = s_start + lane; s < min(key0 + keys_per_wave, N); s += 64) srow[s] = kNegInf;
+  // flush this wave's scores: computed keys (masked past n_vis), then -inf past the visible end
+  const int kend = min(key0 + keys_per_wave, N);
+  for (int s = key0 + lane; s < kend; s += 64) {
+    const int o = s - key0;
+    if (o < 32 * ntiles)
+      srow[s] = s < nv ? sres[wv][o] : kNegInf;
+    else if (fill_masked)
+      srow[s] = kNegInf;
   }
 }
 
@@ -356,18 +387,31 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
     // keys per wave: enough work per wave to amortise the q_I fragments, while the grid still
     // fills the chip (~1024 workgroups)
     const int64_t total = nrows * (int64_t)s.N;
-    int64_t it = total / (32LL * 1024);  // ~1024 waves in flight
-    const int iters = (int)std::max<int64_t>(1, std::min<int64_t>(16, it));
+    int64_t it = total / (32LL * 2048);  // ~2048 waves: two per SIMD
+    int iters = 1;
+    while (iters < kDecodeMaxIters && 2 * iters <= it) iters *= 2;
     const int keys_per_wg = 4 * 32 * iters;
     dim3 grid((s.N + keys_per_wg - 1) / keys_per_wg, (unsigned)nrows);
-    if (k_fmt == FMT_BF16)
-      indexer_decode_mfma<FMT_BF16><<<grid, 256, 0, st>>>(
-          static_cast<const uint16_t*>(q_I), w, static_cast<const uint8_t*>(k_I), k_scale, q_pos,
-          s.T, s.N, s.m, qi0, iters, scores, fm);
-    else
-      indexer_decode_mfma<FMT_MXFP4><<<grid, 256, 0, st>>>(
-          static_cast<const uint16_t*>(q_I), w, static_cast<const uint8_t*>(k_I), k_scale, q_pos,
-          s.T, s.N, s.m, qi0, iters, scores, fm);
+    const uint16_t* qp = static_cast<const uint16_t*>(q_I);
+    const uint8_t* kp = static_cast<const uint8_t*>(k_I);
+#define DSA_DEC(F, I)                                                                   \
+  indexer_decode_mfma<F, I><<<grid, 256, 0, st>>>(qp, w, kp, k_scale, q_pos, s.T, s.N, s.m, \
+                                                  qi0, scores, fm)
+#define DSA_DEC_ITERS(F)                \
+  switch (iters) {                      \
+    case 1: DSA_DEC(F, 1); break;       \
+    case 2: DSA_DEC(F, 2); break;       \
+    case 4: DSA_DEC(F, 4); break;       \
+    case 8: DSA_DEC(F, 8); break;       \
+    default: DSA_DEC(F, 16); break;     \
+  }
+    if (k_fmt == FMT_BF16) {
+      DSA_DEC_ITERS(FMT_BF16)
+    } else {
+      DSA_DEC_ITERS(FMT_MXFP4)
+    }
+#undef DSA_DEC_ITERS
+#undef DSA_DEC
     return hipGetLastError();
   }
   dim3 grid((s.N + 255) / 256, (unsigned)nrows);

@@ -5,13 +5,16 @@
 // context is no longer than k every token is kept.)
 //
 // Radix select on an order-preserving uint32 image of the fp32 scores, one workgroup per query
-// row: three histogram passes (bits 31..21, 20..10, 9..0) narrow the k-th largest key down to
-// one exact value tau and the count `need` of tau-valued entries to take; a final pass emits
-// every entry above tau and the `need` LOWEST-index entries equal to tau (a block-wide ordered
-// scan, only when tau is tied), so the set equals the first k of a stable descending sort.
+// row: histogram passes over 12-bit digits of the bits that vary within the row narrow the k-th
+// largest key down to one exact value tau and the count `need` of tau-valued entries to take;
+// a final pass emits every entry above tau and the `need` LOWEST-index entries equal to tau (a
+// block-wide ordered scan, only when tau is tied), so the set equals the first k of a stable
+// descending sort.
 // Rows whose n_vis <= k take every visible entry. Unused slots are -1.
 #include "common.h"
 #include "launch.h"
+
+#include <mutex>
 
 namespace dsa {
 
@@ -19,140 +22,72 @@ namespace {
 
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / 64;
-constexpr int kBins = 2048;
+constexpr int kDigit = 12;               // bits per radix digit
+constexpr int kBins = 1 << kDigit;       // 4096 bins, 4 per thread
+constexpr int kLdsMaxN = 32768;          // rows up to this many entries are staged in LDS
 
-struct TkShared {
+struct __attribute__((aligned(16))) TkShared {
   uint32_t hist[kBins];
-  uint32_t wave_cnt[kTkWaves];
+  uint32_t wave_tot[kTkWaves];
+  uint32_t red_and[kTkWaves], red_or[kTkWaves];
   uint32_t bin, above, pos, taken_eq;
 };
 
-// Find, among the bins of hist, the one holding the need-th largest element counting from the
-// top; the lane that finds it writes the bin and the count strictly above it to LDS. Run by
-// wave 0 only. The bins hold at least `need` elements in total, so exactly one lane hits.
-__device__ __forceinline__ void find_bin(const uint32_t* hist, int nbins, uint32_t need,
-                                         uint32_t* bin_out, uint32_t* above_out) {
-  const int lane = threadIdx.x & 63;
-  const int per = nbins / 64;  // bins per lane; lane 63 owns the highest bins
-  uint32_t local = 0;
-  for (int i = 0; i < per; ++i) local += hist[lane * per + i];
-  // inclusive suffix sum over lanes: lane L holds the count of lanes L..63
-  uint32_t suf = local;
+// Block-wide search of the bin holding the need-th largest element counting from the top:
+// thread t owns bins 4t .. 4t+3; a suffix scan over threads (shuffles within a wave, wave totals
+// through LDS) finds the owning thread, which writes the bin and the count strictly above it.
+// The bins hold at least `need` elements, so exactly one thread hits. Ends with a barrier.
+__device__ __forceinline__ void find_bin(TkShared& sh, uint32_t need) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const u32x4_t c = *reinterpret_cast<const u32x4_t*>(&sh.hist[4 * tid]);
+  const uint32_t local = c[0] + c[1] + c[2] + c[3];
+  uint32_t suf = local;  // inclusive suffix over lanes lane..63
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     uint32_t v = __shfl_down(suf, o, 64);
     if (lane + o < 64) suf += v;
   }
-  if (suf >= need && suf - local < need) {
-    uint32_t above = suf - local;
-    for (int i = per - 1; i >= 0; --i) {
-      uint32_t c = hist[lane * per + i];
-      if (above + c >= need) {
-        *bin_out = (uint32_t)(lane * per + i);
-        *above_out = above;
+  if (lane == 0) sh.wave_tot[wv] = suf;
+  __syncthreads();
+  for (int w = wv + 1; w < kTkWaves; ++w) suf += sh.wave_tot[w];
+  const uint32_t excl = suf - local;
+  if (suf >= need && excl < need) {
+    uint32_t a = excl;
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      if (a + c[j] >= need) {
+        sh.bin = (uint32_t)(4 * tid + j);
+        sh.above = a;
         break;
       }
-      above += c;
+      a += c[j];
     }
   }
+  __syncthreads();
 }
 
+// One workgroup per query row. LDS_KEYS: the row's order keys are staged in LDS (rows of at
+// most kLdsMaxN entries); otherwise every pass re-reads the scores from global memory (L2).
+// The bits every visible key shares (block-wide AND / OR) are skipped, so the first digit
+// already splits the row: scores of one row typically share sign and exponent, and digits over
+// those bits would put the whole row into a handful of bins and serialise the LDS atomics.
+template <bool LDS_KEYS>
 __global__ __launch_bounds__(kTkThreads) void topk_radix_row(
     const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int64_t qi0, int N,
     int m, int k, int32_t* __restrict__ idx) {
+  extern __shared__ uint32_t skey[];  // [n] when LDS_KEYS
   __shared__ TkShared sh;
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const int n = n_visible(q_pos[qi0 + row], m, N);
-  int32_t* __restrict__ out = idx + row * (int64_t)k;
-  const float* __restrict__ s = scores + row * (int64_t)N;
-
-  if (n <= k) {
-    for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
-    return;
-  }
-
-  // ---- radix passes: (shift, bits) = (21, 11), (10, 11), (0, 10) ----
-  uint32_t prefix = 0, pmask = 0, need = (uint32_t)k, cnt_eq = 0;
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = shifts[pass];
-    const uint32_t bmask = (1u << widths[pass]) - 1u;
-    for (int i = tid; i < kBins; i += kTkThreads) sh.hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kTkThreads) {
-      uint32_t u = order_key(s[i]);
-      if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & bmask], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) find_bin(sh.hist, kBins, need, &sh.bin, &sh.above);
-    __syncthreads();
-    const uint32_t bin = sh.bin;
-    prefix |= bin << shift;
-    need -= sh.above;
-    pmask |= bmask << shift;
-    cnt_eq = sh.hist[bin];
-    __syncthreads();
-  }
-  const uint32_t tau = prefix;
-
-  // ---- emission ----
-  if (tid == 0) {
-    sh.pos = 0;
-    sh.taken_eq = 0;
-  }
-  __syncthreads();
-  if (cnt_eq == need) {
-    for (int i = tid; i < n; i += kTkThreads) {
-      uint32_t u = order_key(s[i]);
-      if (u >= tau) out[atomicAdd(&sh.pos, 1u)] = i;
-    }
-    return;
-  }
-  // tau is tied beyond what is needed: entries above tau in any order, the tau-valued ones in
-  // ascending index order until `need` are taken.
-  const int lane = tid & 63, wv = tid >> 6;
-  for (int base = 0; base < n; base += kTkThreads) {
-    const int i = base + tid;
-    uint32_t u = i < n ? order_key(s[i]) : 0u;
-    if (i < n && u > tau) out[atomicAdd(&sh.pos, 1u)] = i;
-    const bool eq = i < n && u == tau;
-    const unsigned long long bal = __ballot(eq);
-    if (lane == 0) sh.wave_cnt[wv] = (uint32_t)__popcll(bal);
-    __syncthreads();
-    uint32_t before = sh.taken_eq;
-    for (int j = 0; j < wv; ++j) before += sh.wave_cnt[j];
-    before += (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-    if (eq && before < need) out[atomicAdd(&sh.pos, 1u)] = i;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t tot = 0;
-      for (int j = 0; j < kTkWaves; ++j) tot += sh.wave_cnt[j];
-      sh.taken_eq += tot;
-    }
-    __syncthreads();
-  }
-}
-
-// LDS-resident variant for rows of at most kLdsMaxN entries: the row's keys are staged in LDS
-// once and every pass reads them from there. The bits every visible key shares (a block-wide
-// AND / OR) are skipped, so the first 11-bit digit already splits the row (scores of one row
-// typically share sign and exponent; digits over those bits would put the whole row into a
-// handful of bins and serialise the LDS atomics).
-constexpr int kLdsMaxN = 32768;
-
-__global__ __launch_bounds__(kTkThreads) void topk_radix_row_lds(
-    const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int64_t qi0, int N,
-    int m, int k, int32_t* __restrict__ idx) {
-  extern __shared__ uint32_t skey[];  // [n]
-  __shared__ TkShared sh;
-  __shared__ uint32_t red_and[kTkWaves], red_or[kTkWaves];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t row = blockIdx.x;
   const int n = n_visible(q_pos[qi0 + row], m, N);
   int32_t* __restrict__ out = idx + row * (int64_t)k;
   const float* __restrict__ s = scores + row * (int64_t)N;
+  auto key = [&](int i) -> uint32_t {
+    if constexpr (LDS_KEYS)
+      return skey[i];
+    else
+      return order_key(s[i]);
+  };
 
   if (n <= k) {
     for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
@@ -161,7 +96,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_radix_row_lds(
   uint32_t kand = 0xffffffffu, kor = 0u;
   for (int i = tid; i < n; i += kTkThreads) {
     const uint32_t u = order_key(s[i]);
-    skey[i] = u;
+    if constexpr (LDS_KEYS) skey[i] = u;
     kand &= u;
     kor |= u;
   }
@@ -171,8 +106,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_radix_row_lds(
     kor |= __shfl_xor(kor, o, 64);
   }
   if (lane == 0) {
-    red_and[wv] = kand;
-    red_or[wv] = kor;
+    sh.red_and[wv] = kand;
+    sh.red_or[wv] = kor;
   }
   if (tid == 0) {
     sh.pos = 0;
@@ -183,29 +118,28 @@ __global__ __launch_bounds__(kTkThreads) void topk_radix_row_lds(
   kor = 0u;
 #pragma unroll
   for (int w = 0; w < kTkWaves; ++w) {
-    kand &= red_and[w];
-    kor |= red_or[w];
+    kand &= sh.red_and[w];
+    kor |= sh.red_or[w];
   }
   const uint32_t diff = kand ^ kor;  // bits that vary across the visible row
-  uint32_t prefix = kand;            // all bits equal when diff == 0
+  uint32_t prefix = kand;            // every bit is shared when diff == 0
   uint32_t need = (uint32_t)k, cnt_eq = (uint32_t)n;
   if (diff != 0) {
     const int top = 31 - __clz(diff);  // highest varying bit
     uint32_t pmask = top == 31 ? 0u : (~0u << (top + 1));
     prefix = kand & pmask;
-    for (int hi = top; hi >= 0; hi -= 11) {
-      const int width = hi + 1 < 11 ? hi + 1 : 11;
+    for (int hi = top; hi >= 0; hi -= kDigit) {
+      const int width = hi + 1 < kDigit ? hi + 1 : kDigit;
       const int shift = hi + 1 - width;
       const uint32_t bmask = (1u << width) - 1u;
-      for (int i = tid; i < kBins; i += kTkThreads) sh.hist[i] = 0;
+      *reinterpret_cast<u32x4_t*>(&sh.hist[4 * tid]) = u32x4_t{0u, 0u, 0u, 0u};
       __syncthreads();
       for (int i = tid; i < n; i += kTkThreads) {
-        const uint32_t u = skey[i];
+        const uint32_t u = key(i);
         if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & bmask], 1u);
       }
       __syncthreads();
-      if (tid < 64) find_bin(sh.hist, kBins, need, &sh.bin, &sh.above);
-      __syncthreads();
+      find_bin(sh, need);
       const uint32_t bin = sh.bin;
       prefix |= bin << shift;
       need -= sh.above;
@@ -217,26 +151,26 @@ __global__ __launch_bounds__(kTkThreads) void topk_radix_row_lds(
   const uint32_t tau = prefix;
   if (cnt_eq == need) {
     for (int i = tid; i < n; i += kTkThreads)
-      if (skey[i] >= tau) out[atomicAdd(&sh.pos, 1u)] = i;
+      if (key(i) >= tau) out[atomicAdd(&sh.pos, 1u)] = i;
     return;
   }
   // tau tied beyond what is needed: keys above tau in any order, tau-valued ones by index
   for (int base = 0; base < n; base += kTkThreads) {
     const int i = base + tid;
-    const uint32_t u = i < n ? skey[i] : 0u;
+    const uint32_t u = i < n ? key(i) : 0u;
     if (i < n && u > tau) out[atomicAdd(&sh.pos, 1u)] = i;
     const bool eq = i < n && u == tau;
     const unsigned long long bal = __ballot(eq);
-    if (lane == 0) sh.wave_cnt[wv] = (uint32_t)__popcll(bal);
+    if (lane == 0) sh.wave_tot[wv] = (uint32_t)__popcll(bal);
     __syncthreads();
     uint32_t before = sh.taken_eq;
-    for (int w = 0; w < wv; ++w) before += sh.wave_cnt[w];
+    for (int w = 0; w < wv; ++w) before += sh.wave_tot[w];
     before += (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
     if (eq && before < need) out[atomicAdd(&sh.pos, 1u)] = i;
     __syncthreads();
     if (tid == 0) {
       uint32_t tot = 0;
-      for (int w = 0; w < kTkWaves; ++w) tot += sh.wave_cnt[w];
+      for (int w = 0; w < kTkWaves; ++w) tot += sh.wave_tot[w];
       sh.taken_eq += tot;
     }
     __syncthreads();
@@ -252,18 +186,16 @@ hipError_t launch_topk(const Shape& s, int64_t qi0, int64_t nrows, const float* 
   if (nrows <= 0) return hipSuccess;
   // rows hold at most N visible entries
   if (s.N <= kLdsMaxN) {
-    const size_t shm = sizeof(uint32_t) * (size_t)s.N;
-    static bool attr_set = false;  // raise the dynamic LDS limit once (128 KB at N = 32768)
-    if (!attr_set) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_radix_row_lds),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMaxN * 4);
-      attr_set = true;
-    }
-    topk_radix_row_lds<<<dim3((unsigned)nrows), kTkThreads, shm, st>>>(scores, q_pos, qi0, s.N,
-                                                                       s.m, s.top_k, idx);
+    static std::once_flag once;  // allow up to 128 KB of dynamic LDS for the staged keys
+    std::call_once(once, [] {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_radix_row<true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMaxN * 4);
+    });
+    topk_radix_row<true><<<dim3((unsigned)nrows), kTkThreads, sizeof(uint32_t) * (size_t)s.N,
+                           st>>>(scores, q_pos, qi0, s.N, s.m, s.top_k, idx);
   } else {
-    topk_radix_row<<<dim3((unsigned)nrows), kTkThreads, 0, st>>>(scores, q_pos, qi0, s.N, s.m,
-                                                                 s.top_k, idx);
+    topk_radix_row<false><<<dim3((unsigned)nrows), kTkThreads, 0, st>>>(scores, q_pos, qi0, s.N,
+                                                                         s.m, s.top_k, idx);
   }
   return hipGetLastError();
 }
