@@ -18,8 +18,10 @@
 // online softmax in the exp2 domain, fp32 accumulators. Few-query calls split the entry list
 // and merge the (m, l, O) partials in attend_combine.
 // attend_generic: any dims, fp32 or bf16; one workgroup per (query, head), scalar fp32.
-#include "common.h"
-#include "launch.h"
+#include "../lightning_indexer_top_03_amd/csrc/common.h"
+#include "../lightning_indexer_top_03_amd/csrc/launch.h"
+
+#include <mutex>
 
 namespace dsa {
 
@@ -30,6 +32,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 constexpr int kTile = 32;       // entries per tile
+constexpr float kRefSlack = 8.f;  // log2 headroom of the lazily moved softmax reference
 constexpr int kVtStride = 36;   // bf16 per transposed-V row (32 entries + pad): conflict-free b64 reads
 
 // Source row of entry e of query (b, p); returns nullptr for a masked entry.
@@ -48,178 +51,18 @@ __device__ __forceinline__ const T* entry_row(int e, const int32_t* __restrict__
   return kv_raw + ((size_t)b * n_raw + (r - raw_base)) * DK;
 }
 
-template <int DK, int DV>
-__global__ __launch_bounds__(256, 1) void attend_mfma(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
-    const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw, int64_t raw_base,
-    int64_t n_raw, const int32_t* __restrict__ q_pos, int T, int N, int H, int top_k, int W,
-    float scale_log2, int64_t qi0, int nsplit, int per_split, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
-  constexpr int KS = DK + 8;          // bf16 per row-major K row in LDS (16-byte pad)
-  constexpr int CPR = DK / 8;         // 16-byte chunks per row
-  constexpr int JPT = CPR / 8;        // chunks per thread per tile (8 threads per entry)
-  constexpr int KK = DK / 32;         // MFMA k-steps for S
-  constexpr int DB = DV / 16;         // 16-wide output column blocks
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kTile * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[DV * kVtStride];
-  __shared__ int sValid[kTile];
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int64_t row = blockIdx.z;
-  const int64_t qi = qi0 + row;
-  const int b = (int)(qi / T);
-  const int p = q_pos[qi];
-  const int split = blockIdx.x;
-  const int h0 = blockIdx.y * 64 + wv * 16;
-  const int E = top_k + W;
-  const int e_begin = split * per_split;
-  const int e_end = min(E, e_begin + per_split);
-  const int32_t* __restrict__ idxrow = idx + row * (int64_t)top_k;
-
-  // q fragments: lane (head n, group g) holds q[h0+n][32kk + 8g .. +7]
-  u32x4_t qf[KK];
-  {
-    const uint16_t* qh = q + ((size_t)qi * H + h0 + n) * DK + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const u32x4_t*>(qh + 32 * kk);
+// Entry codes: >= 0 a row of kv (within the sequence), <= -2 a raw window row (-code-2 within
+// kv_raw's rows of the sequence), -1 masked.
+__device__ __forceinline__ int entry_code(int e, const int32_t* __restrict__ idxrow, int top_k,
+                                          int N, int64_t raw_base, int64_t n_raw, int p, int W,
+                                          bool has_raw) {
+  if (e < top_k) {
+    const int j = idxrow[e];
+    return (j >= 0 && j < N) ? j : -1;
   }
-
-  f32x4_t acc[DB];
-#pragma unroll
-  for (int d = 0; d < DB; ++d) acc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
-
-  // gather mapping: thread handles entry r = tid & 31 of every tile, chunks cg + 8j
-  const int r = tid & 31, cg = tid >> 5;
-  u32x4_t pre[JPT];
-  int pre_ok = 0;
-  auto fetch = [&](int e0) {
-    const int e = e0 + r;
-    const uint16_t* src = e < e_end ? entry_row<uint16_t>(e, idxrow, top_k, kv, b, N, DK, kv_raw,
-                                                          raw_base, n_raw, p, W)
-                                    : nullptr;
-    pre_ok = src != nullptr;
-#pragma unroll
-    for (int j = 0; j < JPT; ++j)
-      pre[j] = src ? *reinterpret_cast<const u32x4_t*>(src + 8 * (cg + 8 * j))
-                   : u32x4_t{0u, 0u, 0u, 0u};
-  };
-
-  if (e_begin < e_end) fetch(e_begin);
-  for (int e0 = e_begin; e0 < e_end; e0 += kTile) {
-    // commit the prefetched rows: row-major K and transposed V
-#pragma unroll
-    for (int j = 0; j < JPT; ++j) {
-      const int cc = cg + 8 * j;
-      *reinterpret_cast<u32x4_t*>(&sK[r * KS + 8 * cc]) = pre[j];
-      if (8 * cc < DV) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t wd = pre[j][i];
-          sVt[(8 * cc + 2 * i) * kVtStride + r] = (uint16_t)(wd & 0xffffu);
-          sVt[(8 * cc + 2 * i + 1) * kVtStride + r] = (uint16_t)(wd >> 16);
-        }
-      }
-    }
-    if (cg == 0) sValid[r] = pre_ok;
-    __syncthreads();
-    if (e0 + kTile < e_end) fetch(e0 + kTile);
-
-    // S^T[entry, head] for two 16-entry blocks
-    f32x4_t st[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int eb = 0; eb < 2; ++eb) {
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&sK[(eb * 16 + n) * KS + 32 * kk + 8 * g]));
-        st[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(qf[kk]), st[eb], 0, 0, 0);
-      }
-    }
-    // lane (head n, g): st[eb][i] = entry eb*16 + 4g + i
-    float z[8];
-    float mx = kNegInf;
-#pragma unroll
-    for (int eb = 0; eb < 2; ++eb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = eb * 16 + 4 * g + i;
-        float v = sValid[e] ? st[eb][i] * scale_log2 : kNegInf;
-        z[eb * 4 + i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    float alpha, psum = 0.f;
-    uint32_t pk[4];
-    if (m_new == kNegInf) {
-      alpha = 1.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = 0u;
-    } else {
-      alpha = exp2f(m_run - m_new);
-      float pe[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pe[i] = exp2f(z[i] - m_new);
-        psum += pe[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pe[2 * i], pe[2 * i + 1]);
-    }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // rows of acc are heads 4g + i: fetch their alpha from lane (4g + i)
-    float ai[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i, 64);
-    const bf16x8_t pa = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-#pragma unroll
-    for (int d = 0; d < DB; ++d) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[d][i] *= ai[i];
-      const uint16_t* vrow = &sVt[(16 * d + n) * kVtStride];
-      u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + 4 * g);
-      u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16 + 4 * g);
-      bf16x8_t bv = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-      acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, acc[d], 0, 0, 0);
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue ----
-  float li[4], mi[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    li[i] = __shfl(l_run, 4 * g + i, 64);
-    mi[i] = __shfl(m_run, 4 * g + i, 64);
-  }
-  if (nsplit == 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float inv = li[i] > 0.f ? 1.f / li[i] : 0.f;
-      uint16_t* orow = out + ((size_t)qi * H + h0 + 4 * g + i) * DV + n;
-#pragma unroll
-      for (int d = 0; d < DB; ++d) orow[16 * d] = f32_to_bf16(acc[d][i] * inv);
-    }
-    if (g == 0 && lse)
-      lse[(size_t)qi * H + h0 + n] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t hrow = ((size_t)row * H + h0 + 4 * g + i) * nsplit + split;
-      float* po = part_o + hrow * DV + n;
-#pragma unroll
-      for (int d = 0; d < DB; ++d) po[16 * d] = acc[d][i];
-      if (n == 0) {
-        part_ml[hrow * 2] = mi[i];
-        part_ml[hrow * 2 + 1] = li[i];
-      }
-    }
-  }
+  const int64_t r = (int64_t)p - W + 1 + (e - top_k);
+  if (!has_raw || r < 0 || r < raw_base || r >= raw_base + n_raw) return -1;
+  return -(int)(r - raw_base) - 2;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -253,32 +96,35 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// 8 ds_read_b64_tr_b16 for dim blocks d0 .. d0+3 (entry halves 4g.. and 16+4g..), waited for
+// 16 ds_read_b64_tr_b16 for dim blocks d0 .. d0+7 (entry halves 4g.. and 16+4g..), waited for
 // inside the same asm block. Written as asm because the builtin carries no memory operand, which
 // makes the compiler wait for every LDS DMA still in flight before it.
-#define DSA_TR(i, off) "ds_read_b64_tr_b16 %" #i ", %8 offset:" #off "\n"
+#define DSA_TR(i, off) "ds_read_b64_tr_b16 %" #i ", %16 offset:" #off "\n"
+#define DSA_TR_PAIR(i0, i1, D) DSA_TR(i0, (D) * 32) DSA_TR(i1, 16640 + (D) * 32)
 #define DSA_TR_BLOCK(D0)                                                                        \
   case D0:                                                                                      \
-    asm volatile(DSA_TR(0, D0 * 32) DSA_TR(1, 16640 + D0 * 32) DSA_TR(2, D0 * 32 + 32)          \
-                 DSA_TR(3, 16640 + D0 * 32 + 32) DSA_TR(4, D0 * 32 + 64)                        \
-                 DSA_TR(5, 16640 + D0 * 32 + 64) DSA_TR(6, D0 * 32 + 96)                        \
-                 DSA_TR(7, 16640 + D0 * 32 + 96) "s_waitcnt lgkmcnt(0)"                         \
+    asm volatile(DSA_TR_PAIR(0, 1, D0) DSA_TR_PAIR(2, 3, D0 + 1) DSA_TR_PAIR(4, 5, D0 + 2)      \
+                 DSA_TR_PAIR(6, 7, D0 + 3) DSA_TR_PAIR(8, 9, D0 + 4) DSA_TR_PAIR(10, 11, D0 + 5) \
+                 DSA_TR_PAIR(12, 13, D0 + 6) DSA_TR_PAIR(14, 15, D0 + 7)                        \
+                 "s_waitcnt lgkmcnt(0)"                                                         \
                  : "=&v"(tr[0]), "=&v"(tr[1]), "=&v"(tr[2]), "=&v"(tr[3]), "=&v"(tr[4]),         \
-                   "=&v"(tr[5]), "=&v"(tr[6]), "=&v"(tr[7])                                     \
+                   "=&v"(tr[5]), "=&v"(tr[6]), "=&v"(tr[7]), "=&v"(tr[8]), "=&v"(tr[9]),         \
+                   "=&v"(tr[10]), "=&v"(tr[11]), "=&v"(tr[12]), "=&v"(tr[13]), "=&v"(tr[14]),    \
+                   "=&v"(tr[15])                                                                \
                  : "v"(vaddr)                                                                   \
                  : "memory");                                                                   \
     break;
 __device__ __forceinline__ void tr_read_block(u32x2_t* tr, uint32_t vaddr, int d0) {
   switch (d0) {
-    DSA_TR_BLOCK(0) DSA_TR_BLOCK(4) DSA_TR_BLOCK(8) DSA_TR_BLOCK(12)
-    DSA_TR_BLOCK(16) DSA_TR_BLOCK(20) DSA_TR_BLOCK(24) DSA_TR_BLOCK(28)
+    DSA_TR_BLOCK(0) DSA_TR_BLOCK(8) DSA_TR_BLOCK(16) DSA_TR_BLOCK(24)
   }
 }
 #undef DSA_TR_BLOCK
+#undef DSA_TR_PAIR
 #undef DSA_TR
 
 template <int NS>
-__global__ __launch_bounds__(256, NS == 2 ? 2 : 1) void attend_mfma_dma(
+__global__ __launch_bounds__(256, 1) void attend_mfma_dma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw, int64_t raw_base,
     int64_t n_raw, const int32_t* __restrict__ q_pos, int T, int N, int H, int top_k, int W,
@@ -287,7 +133,7 @@ __global__ __launch_bounds__(256, NS == 2 ? 2 : 1) void attend_mfma_dma(
   constexpr int DK = 576, DV = 512, KK = DK / 32, DB = DV / 16;
   constexpr int DMAS = 9;  // DMA instructions per wave per tile
   __shared__ __attribute__((aligned(16))) char smem[NS * kStage];
-  __shared__ int sValid[NS][kTile];
+  extern __shared__ int scode[];  // entry codes of this split, padded to whole tiles
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -315,6 +161,20 @@ __global__ __launch_bounds__(256, NS == 2 ? 2 : 1) void attend_mfma_dma(
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(qf[kk]));
   }
+  // resolve the split's entries once: idx -> row code (masked rows keep a valid fallback address
+  // for their DMA and are excluded in the softmax)
+  for (int i = tid; i < ntiles * kTile; i += 256) {
+    const int e = e_begin + i;
+    scode[i] = e < e_end ? entry_code(e, idxrow, top_k, N, raw_base, n_raw, p, W, kv_raw != nullptr)
+                         : -1;
+  }
+  __syncthreads();
+  auto rowptr = [&](int code) -> const uint16_t* {
+    if (code >= 0) return kv + ((size_t)b * N + code) * DK;
+    if (code <= -2) return kv_raw + ((size_t)b * n_raw + (-code - 2)) * DK;
+    return fallback;
+  };
+
   f32x4_t acc[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) acc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -327,31 +187,23 @@ __global__ __launch_bounds__(256, NS == 2 ? 2 : 1) void attend_mfma_dma(
     // transfers are the explicit vmcnt waits of the pipeline below
     const uint32_t sbase = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(lds_void_t*)(smem + stage * kStage));
-    const int e0 = e_begin + kTile * t + 8 * wv;
-    const uint16_t* rp[8];
-    uint32_t okm = 0;
+    const int c0 = kTile * t + 8 * wv;  // this wave's first row in the code table
+    // lane l resolves row l & 7 (latent DMAs, via readlane) and row l >> 3 (its rope chunk)
+    const uint64_t pl = (uint64_t)(uintptr_t)rowptr(scode[c0 + (lane & 7)]);
+    const uint16_t* pr = rowptr(scode[c0 + (lane >> 3)]);
 #pragma unroll
     for (int r8 = 0; r8 < 8; ++r8) {
-      const int e = e0 + r8;
-      const uint16_t* src = e < e_end ? entry_row<uint16_t>(e, idxrow, top_k, kv, b, N, DK,
-                                                            kv_raw, raw_base, n_raw, p, W)
-                                      : nullptr;
-      okm |= (src != nullptr ? 1u : 0u) << r8;
-      rp[r8] = src ? src : fallback;
-    }
-#pragma unroll
-    for (int r8 = 0; r8 < 8; ++r8)
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pl, r8);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(pl >> 32), r8);
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
       __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(rp[r8] + 8 * lane),
+          reinterpret_cast<const void*>(src + 8 * lane),
           (lds_void_t*)(uintptr_t)(sbase + (8 * wv + r8) * kLatStride), 16, 0, 0);
-    const int rr = lane >> 3;  // row within the wave's 8
-    const uint16_t* mine = rp[0];
-#pragma unroll
-    for (int r8 = 1; r8 < 8; ++r8) mine = rr == r8 ? rp[r8] : mine;
+    }
+    const int rr = lane >> 3;
     __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const void*>(mine + 512 + 8 * ((lane & 7) ^ rr)),
+        reinterpret_cast<const void*>(pr + 512 + 8 * ((lane & 7) ^ rr)),
         (lds_void_t*)(uintptr_t)(sbase + kStageLat + wv * 1024), 16, 0, 0);
-    if (lane < 8) sValid[stage][8 * wv + lane] = (okm >> lane) & 1u;
   };
 
   for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t);
@@ -365,10 +217,13 @@ __global__ __launch_bounds__(256, NS == 2 ? 2 : 1) void attend_mfma_dma(
 
     const int stage = t % NS;
     const char* sb = smem + stage * kStage;
-    f32x4_t st[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    // S^T per 16-entry block: its 18 A-operand reads issued first, then two independent MFMA
+    // chains (even / odd k-step)
+    f32x4_t sp[2][2] = {};
 #pragma unroll
     for (int eb = 0; eb < 2; ++eb) {
       const int R = eb * 16 + n;
+      u32x4_t av[KK];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const char* ap;
@@ -378,10 +233,15 @@ __global__ __launch_bounds__(256, NS == 2 ? 2 : 1) void attend_mfma_dma(
           const int c = 4 * (kk - 16) + g;
           ap = sb + kStageLat + R * 128 + ((c ^ (R & 7)) * 16);
         }
-        bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(ap));
-        st[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(qf[kk]), st[eb], 0, 0, 0);
+        av[kk] = *reinterpret_cast<const u32x4_t*>(ap);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        sp[eb][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[kk]), as_bf16x8(qf[kk]),
+                                                                 sp[eb][kk & 1], 0, 0, 0);
     }
+    f32x4_t st[2] = {sp[0][0] + sp[0][1], sp[1][0] + sp[1][1]};
     float z[8];
     float mx = kNegInf;
 #pragma unroll
@@ -389,25 +249,37 @@ __global__ __launch_bounds__(256, NS == 2 ? 2 : 1) void attend_mfma_dma(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = eb * 16 + 4 * g + i;
-        float v = sValid[stage][e] ? st[eb][i] * scale_log2 : kNegInf;
+        float v = scode[kTile * t + e] != -1 ? st[eb][i] * scale_log2 : kNegInf;
         z[eb * 4 + i] = v;
         mx = fmaxf(mx, v);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    float alpha, psum = 0.f;
-    uint32_t pk[4];
-    if (m_new == kNegInf) {
-      alpha = 1.f;
+    // Lazily moved softmax reference: m_run only moves (and the accumulators are rescaled) when
+    // a head's tile maximum exceeds it by more than kRefSlack (log2 units), so p <= 2^kRefSlack
+    // and the rescale of the 128 accumulators, which live in AGPRs, is rare.
+    const bool grow = mx > m_run + kRefSlack;
+    if (__ballot(grow) != 0) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+      float ai[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = 0u;
-    } else {
-      alpha = exp2f(m_run - m_new);
+      for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i, 64);
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[d][i] *= ai[i];
+    }
+    float psum = 0.f;
+    uint32_t pk[4];
+    {
       float pe[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        pe[i] = exp2f(z[i] - m_new);
+        // m_run == -inf only while every entry so far is masked (z == -inf as well)
+        pe[i] = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(z[i] - m_run);
         psum += pe[i];
       }
 #pragma unroll
@@ -415,23 +287,17 @@ __global__ __launch_bounds__(256, NS == 2 ? 2 : 1) void attend_mfma_dma(
     }
     psum += __shfl_xor(psum, 16, 64);
     psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    float ai[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i, 64);
+    l_run += psum;
     const bf16x8_t pa = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
     // transposed V reads: rows 4g + n/4 (entries 4g..4g+3) and 16 + 4g + n/4, column 4*(n%4)
     const uint32_t vaddr = (uint32_t)(uintptr_t)(lds_void_t*)(sb + (4 * g + (n >> 2)) * kLatStride +
                                                              8 * (n & 3));
 #pragma unroll
-    for (int d0 = 0; d0 < DB; d0 += 4) {
-      u32x2_t tr[8];
+    for (int d0 = 0; d0 < DB; d0 += 8) {
+      u32x2_t tr[16];
       tr_read_block(tr, vaddr, d0);
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[d0 + d][i] *= ai[i];
+      for (int d = 0; d < 8; ++d) {
         const u32x4_t bw = {tr[2 * d][0], tr[2 * d][1], tr[2 * d + 1][0], tr[2 * d + 1][1]};
         acc[d0 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(bw), acc[d0 + d], 0, 0, 0);
       }
@@ -461,7 +327,6 @@ __global__ __launch_bounds__(256, NS == 2 ? 2 : 1) void attend_mfma_dma(
     for (int i = 0; i < 4; ++i) {
       const size_t hrow = ((size_t)row * H + h0 + 4 * g + i) * nsplit + split;
       float* po = part_o + hrow * DV + n;
-#pragma unroll
       for (int d = 0; d < DB; ++d) po[16 * d] = acc[d][i];
       if (n == 0) {
         part_ml[hrow * 2] = mi[i];
@@ -471,7 +336,9 @@ __global__ __launch_bounds__(256, NS == 2 ? 2 : 1) void attend_mfma_dma(
   }
 }
 
-// Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+// One workgroup of D_V/4 threads per (row, head); each thread owns 4 consecutive columns and
+// reads every split's float4 (fully coalesced 2 KB per split).
 template <typename OT>
 __global__ __launch_bounds__(128) void attend_combine(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int64_t qi0, int H,
@@ -482,23 +349,27 @@ __global__ __launch_bounds__(128) void attend_combine(
   float M = kNegInf;
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(hrow + s) * 2]);
   float L = 0.f;
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+  const int d = 4 * threadIdx.x;
   for (int s = 0; s < nsplit; ++s) {
-    float ms = part_ml[(hrow + s) * 2];
-    if (ms != kNegInf) L += exp2f(ms - M) * part_ml[(hrow + s) * 2 + 1];
+    const float ms = part_ml[(hrow + s) * 2];
+    const float sc = ms == kNegInf ? 0.f : exp2f(ms - M);
+    L += sc * part_ml[(hrow + s) * 2 + 1];
+    if (d < DV) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(part_o + (hrow + s) * DV + d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] += sc * v[i];
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   const size_t orow = ((size_t)(qi0 + row) * H + h) * DV;
-  for (int d = threadIdx.x; d < DV; d += blockDim.x) {
-    float a = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      float ms = part_ml[(hrow + s) * 2];
-      if (ms != kNegInf) a += exp2f(ms - M) * part_o[(hrow + s) * DV + d];
+  if (d < DV) {
+    if constexpr (sizeof(OT) == 2) {
+      *reinterpret_cast<u32x2_t*>(out + orow + d) =
+          u32x2_t{pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv)};
+    } else {
+      *reinterpret_cast<f32x4_t*>(out + orow + d) = f32x4_t{a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv};
     }
-    a *= inv;
-    if constexpr (sizeof(OT) == 2)
-      out[orow + d] = f32_to_bf16(a);
-    else
-      out[orow + d] = a;
   }
   if (threadIdx.x == 0 && lse)
     lse[(size_t)(qi0 + row) * H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
@@ -613,7 +484,13 @@ hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, co
     float* part_o = static_cast<float*>(ws);
     float* part_ml = ns > 1 ? part_o + (size_t)nrows * s.H * ns * s.D_V : nullptr;
     dim3 grid(ns, s.H / 64, (unsigned)nrows);
-    attend_mfma_dma<2><<<grid, 256, 0, st>>>(
+    const size_t code_bytes = sizeof(int) * (size_t)per;  // per is a multiple of the tile
+    static std::once_flag once;  // the code table can take the block past 64 KB of LDS
+    std::call_once(once, [] {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_mfma_dma<2>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 48 * 1024);
+    });
+    attend_mfma_dma<2><<<grid, 256, code_bytes, st>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
         static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H, s.top_k, s.W,
         scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse, part_o, part_ml);

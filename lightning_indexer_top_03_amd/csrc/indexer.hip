@@ -192,6 +192,149 @@ __global__ __launch_bounds__(256) void indexer_decode_mfma(
 }
 
 // ------------------------------------------------------------------------------------------
+// Decode-shaped kernel, bf16 keys, streamed through LDS. Reading rows straight into the MFMA
+// operand layout (each lane 16 B of its own 256-byte row per load) makes every load instruction
+// touch 64 rows and runs at a fraction of HBM speed, so all global traffic here is fully
+// coalesced DMA (global_load_lds_dwordx4: lane l of instruction j moves 16 bytes at 1024*j+16*l):
+//  * the query's q_I (64 rows x 256 B) is staged once per workgroup and read back as A operands;
+//  * each of the 8 waves streams its own 32-key tiles (8 KB) through a 2-stage LDS ring.
+// Row r of a staged block keeps its 16-byte chunk c in slot c ^ (r % 16), so the 8 lanes a
+// ds_read_b128 phase serves hit distinct banks. Key-ring stages are only read by the wave that
+// filled them, after an explicit s_waitcnt vmcnt; q_I is shared behind one barrier.
+// ------------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int kDecWaves = 8;
+
+__device__ __forceinline__ float relu_bits(float x) {
+  // max(x, 0) on the IEEE bit pattern: negative values (sign bit set) are negative as int32
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+template <int ITERS>
+__global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_dma(
+    const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
+    const int32_t* __restrict__ q_pos, int T, int N, int m, int64_t qi0,
+    float* __restrict__ scores, int fill_masked) {
+  __shared__ __attribute__((aligned(16))) char sq[64 * 256];
+  __shared__ __attribute__((aligned(16))) char sk[kDecWaves][2][32 * 256];
+  __shared__ float sres[kDecWaves][32 * ITERS];
+  const int64_t row = blockIdx.y;
+  const int64_t qi = qi0 + row;
+  const int b = (int)(qi / T);
+  const int nv = n_visible(q_pos[qi], m, N);
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  constexpr int keys_per_wave = 32 * ITERS;
+  const int key0_wg = blockIdx.x * kDecWaves * keys_per_wave;
+  const int key0 = key0_wg + wv * keys_per_wave;
+  float* __restrict__ srow = scores + (size_t)row * N;
+
+  if (key0_wg >= nv) {  // the whole workgroup is past the visible range
+    if (fill_masked)
+      for (int s = key0_wg + (int)threadIdx.x; s < min(key0_wg + kDecWaves * keys_per_wave, N);
+           s += kDecWaves * 64)
+        srow[s] = kNegInf;
+    return;
+  }
+  const size_t base_row = (size_t)b * N;
+  const uint32_t ring = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)&sk[wv][0][0]);
+  const uint32_t qlds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)&sq[0]);
+  const int r4 = lane >> 4, c16 = lane & 15;
+  auto issue = [&](int t) {  // tile t of this wave into stage t % 2
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + r4;
+      const size_t krow = base_row + min(key0 + 32 * t + r, N - 1);
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(kI + krow * 256 + 16 * (c16 ^ (r & 15))),
+          (lds_void_t*)(uintptr_t)(ring + (t & 1) * (32 * 256) + 1024 * j), 16, 0, 0);
+    }
+  };
+  issue(0);
+  if (ITERS > 1) issue(1);
+  {  // q_I: 16 KB, two 1 KB DMAs per wave (rows 8*wv .. 8*wv+7)
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(qI + (size_t)qi * (64 * 128));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = 8 * wv + 4 * j + r4;
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(qsrc + r * 256 + 16 * (c16 ^ (r & 15))),
+          (lds_void_t*)(uintptr_t)(qlds + (8 * wv + 4 * j) * 256), 16, 0, 0);
+    }
+  }
+  float wr[2][16];
+  const float* wrow = w + (size_t)qi * 64;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(wrow + hb * 32 + 8 * j + 4 * h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wr[hb][4 * j + i] = w4[i];
+    }
+  // Everything issued so far has landed once this returns (the counter drains in order).
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(wr[hb][r]));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();  // every wave's share of q_I is in LDS
+  u32x4_t qa[2][8];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int r = hb * 32 + n;
+      qa[hb][kk] = *reinterpret_cast<const u32x4_t*>(&sq[r * 256 + 16 * ((8 * h + kk) ^ (r & 15))]);
+    }
+
+  const int last = min(key0 + keys_per_wave, nv);
+  const int ntiles = last > key0 ? (last - key0 + 31) / 32 : 0;
+#pragma unroll
+  for (int t = 0; t < ITERS; ++t) {
+    if (t >= 2) {
+      if (t + 1 < ITERS)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // tile t landed, tile t+1 in flight
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    const char* st = &sk[wv][t & 1][0];
+    u32x4_t kb[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      kb[kk] = *reinterpret_cast<const u32x4_t*>(st + n * 256 + 16 * ((8 * h + kk) ^ (n & 15)));
+    __builtin_amdgcn_sched_barrier(0);  // all eight LDS reads in flight before the MFMAs
+    f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[0][kk]), as_bf16x8(kb[kk]), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[1][kk]), as_bf16x8(kb[kk]), acc1, 0, 0, 0);
+    }
+    if (t + 2 < ITERS) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's reads are done
+      issue(t + 2);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      part += wr[0][r] * relu_bits(acc0[r]);
+      part += wr[1][r] * relu_bits(acc1[r]);
+    }
+    part += __shfl_xor(part, 32, 64);
+    if (h == 0) sres[wv][32 * t + n] = part;
+  }
+  const int kend = min(key0 + keys_per_wave, N);
+  for (int s = key0 + lane; s < kend; s += 64) {
+    const int o = s - key0;
+    if (o < 32 * ntiles)
+      srow[s] = s < nv ? sres[wv][o] : kNegInf;
+    else if (fill_masked)
+      srow[s] = kNegInf;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // Prefill-shaped kernel (bf16). H_I = 64, D_I = 128. Workgroup = 256 keys x QT queries of one
 // sequence. Wave wv holds keys kbase + 64*wv + 32*kb + n (kb = 0, 1) as B operands; the
 // query's q_I (64 x 128) and w (64) are staged in LDS, double-buffered, and read as A operands.
@@ -406,7 +549,23 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
     default: DSA_DEC(F, 16); break;     \
   }
     if (k_fmt == FMT_BF16) {
-      DSA_DEC_ITERS(FMT_BF16)
+      // 8 waves per workgroup, ~2 tiles per wave: 256 workgroups at 16 x 8192 keys
+      int it2 = 1;
+      while (it2 < 16 && (int64_t)2 * it2 * 32 * kDecWaves * 256 <= total) it2 *= 2;
+      const int kpw = kDecWaves * 32 * it2;
+      dim3 g2((s.N + kpw - 1) / kpw, (unsigned)nrows);
+      const uint8_t* kb = static_cast<const uint8_t*>(k_I);
+#define DSA_DMA(I)                                                                            \
+  indexer_decode_dma<I><<<g2, kDecWaves * 64, 0, st>>>(qp, w, kb, q_pos, s.T, s.N, s.m, qi0,  \
+                                                       scores, fm)
+      switch (it2) {
+        case 1: DSA_DMA(1); break;
+        case 2: DSA_DMA(2); break;
+        case 4: DSA_DMA(4); break;
+        case 8: DSA_DMA(8); break;
+        default: DSA_DMA(16); break;
+      }
+#undef DSA_DMA
     } else {
       DSA_DEC_ITERS(FMT_MXFP4)
     }

@@ -66,6 +66,19 @@ __device__ __forceinline__ void find_bin(TkShared& sh, uint32_t need) {
   __syncthreads();
 }
 
+// Append index i to out for every lane with take set: one LDS atomic per wave (the ballot's
+// popcount), each lane then writes at base + its rank among the taking lanes.
+__device__ __forceinline__ void append(bool take, int i, uint32_t* pos, int32_t* __restrict__ out) {
+  const unsigned long long bal = __ballot(take);
+  if (bal == 0) return;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((long long)bal) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(pos, (uint32_t)__popcll(bal));
+  base = __shfl(base, leader, 64);
+  if (take) out[base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull))] = i;
+}
+
 // One workgroup per query row. LDS_KEYS: the row's order keys are staged in LDS (rows of at
 // most kLdsMaxN entries); otherwise every pass re-reads the scores from global memory (L2).
 // The bits every visible key shares (block-wide AND / OR) are skipped, so the first digit
@@ -150,15 +163,17 @@ __global__ __launch_bounds__(kTkThreads) void topk_radix_row(
   }
   const uint32_t tau = prefix;
   if (cnt_eq == need) {
-    for (int i = tid; i < n; i += kTkThreads)
-      if (key(i) >= tau) out[atomicAdd(&sh.pos, 1u)] = i;
+    for (int base = 0; base < n; base += kTkThreads) {  // block-uniform trip count
+      const int i = base + tid;
+      append(i < n && key(i) >= tau, i, &sh.pos, out);
+    }
     return;
   }
   // tau tied beyond what is needed: keys above tau in any order, tau-valued ones by index
   for (int base = 0; base < n; base += kTkThreads) {
     const int i = base + tid;
     const uint32_t u = i < n ? key(i) : 0u;
-    if (i < n && u > tau) out[atomicAdd(&sh.pos, 1u)] = i;
+    append(i < n && u > tau, i, &sh.pos, out);
     const bool eq = i < n && u == tau;
     const unsigned long long bal = __ballot(eq);
     if (lane == 0) sh.wave_tot[wv] = (uint32_t)__popcll(bal);
@@ -166,7 +181,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_radix_row(
     uint32_t before = sh.taken_eq;
     for (int w = 0; w < wv; ++w) before += sh.wave_tot[w];
     before += (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-    if (eq && before < need) out[atomicAdd(&sh.pos, 1u)] = i;
+    append(eq && before < need, i, &sh.pos, out);
     __syncthreads();
     if (tid == 0) {
       uint32_t tot = 0;
