@@ -9,17 +9,12 @@
 // For query row qi and head h, over E = {kv[b, idx[qi, i]] : idx >= 0} u {raw window rows}:
 //   z_e = scale * q[qi,h,:] . K_e,  out[qi,h,:] = sum_e softmax(z)_e * K_e[:D_V],  lse = log sum exp z
 //
-// attend_mfma (bf16, D_K % 64 == 0, D_V % 16 == 0, H % 64 == 0): a workgroup = 4 waves = 64
-// heads of one query over a split of its entry list. Per 32-entry tile the workgroup gathers the
-// rows into LDS twice - row-major (the S^T = K Q^T A operand) and transposed for the first D_V
-// columns (the P V B operand) - while the next tile's rows are already in flight in registers.
-// Each wave owns 16 heads: q stays in registers (B operand of v_mfma_f32_16x16x32_bf16), the
-// S^T accumulator layout is exactly the A-operand layout P needs, so P never leaves registers;
-// online softmax in the exp2 domain, fp32 accumulators. Few-query calls split the entry list
-// and merge the (m, l, O) partials in attend_combine.
+// attend_mfma_dma (bf16, D_K = 576, D_V = 512, H % 64 == 0): a workgroup = 8 waves = 64 heads
+// of one query over a split of its entry list; tiles of 32 entries stream from HBM into an LDS
+// ring by DMA, wave pairs split D_K for S = q K^T and D_V for P V (details at the kernel).
 // attend_generic: any dims, fp32 or bf16; one workgroup per (query, head), scalar fp32.
-#include "../lightning_indexer_top_03_amd/csrc/common.h"
-#include "../lightning_indexer_top_03_amd/csrc/launch.h"
+#include "common.h"
+#include "launch.h"
 
 #include <mutex>
 
@@ -33,7 +28,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 constexpr int kTile = 32;       // entries per tile
 constexpr float kRefSlack = 8.f;  // log2 headroom of the lazily moved softmax reference
-constexpr int kVtStride = 36;   // bf16 per transposed-V row (32 entries + pad): conflict-free b64 reads
 
 // Source row of entry e of query (b, p); returns nullptr for a masked entry.
 template <typename T>
@@ -66,41 +60,78 @@ __device__ __forceinline__ int entry_code(int e, const int32_t* __restrict__ idx
 }
 
 // ------------------------------------------------------------------------------------------
-// attend_mfma_dma: same math as attend_mfma for D_K = 576, D_V = 512, but the gather goes
-// straight from HBM into an NS-stage LDS ring with global_load_lds_dwordx4 (no register staging),
-// and the P V B operand is read from the row-major tile with ds_read_b64_tr_b16 (no transposed
-// copy of V). Per 32-entry tile and wave (8 rows): 8 row DMAs of the 1024-byte latent part (one
-// row per instruction, fully coalesced) and one DMA of the 8 rows' 128-byte rope parts.
-// LDS tile layout: latent rows at a 1040-byte stride (16-byte pad: conflict-free 16-byte reads by
-// 8 consecutive rows), then the rope parts as [32 rows][8 chunks of 16 B] with the chunk slot
-// XOR-swizzled by (row % 8). Waits are explicit (s_waitcnt vmcnt + s_barrier without a fence),
-// so the DMAs of the next NS-1 tiles stay in flight while the current tile is computed.
-//
-// ds_read_b64_tr_b16, within each group of 16 lanes: if lane j reads the 4 bf16 M[j][0..3],
-// lane 4a+b receives {M[a][b], M[a+4][b], M[a+8][b], M[a+12][b]}. Lane j of group g reading row
-// 4g + j/4 at column 16*db + 4*(j%4) therefore receives, in lane n of the group, V[4g+0..3][16db+n]:
-// the B-operand slots 0..3 of v_mfma_f32_16x16x32_bf16 for dim n (entries 4g..4g+3), which is the
-// same slot -> entry map as the P operand taken from the S^T accumulators.
+// attend_mfma_dma (bf16, D_K = 576, D_V = 512, H % 64 == 0): one workgroup = 8 waves = 64 heads
+// of one query over a split of its entry list, 32-entry tiles.
+//  * Gather: each tile goes straight from HBM into a 3-stage LDS ring with global_load_lds_dwordx4
+//    (no register staging): one DMA per row for the 1024-byte latent part (fully coalesced) and
+//    one per 8 rows for their 128-byte rope parts. Latent rows sit at a 1056-byte stride: both
+//    the row-per-lane 16-byte reads of S and the transposed 8-byte reads of P V are then free of
+//    bank conflicts. The rope parts are [32 rows][8 chunks of 16 B], chunk c of row R at slot
+//    c ^ ((R >> 1) & 7), again conflict-free for the row-per-lane reads. Waits are explicit
+//    (s_waitcnt vmcnt + s_barrier, no fence), so two tiles' DMAs stay in flight behind the one
+//    being computed.
+//  * Wave (hb, half) and its partner (hb, 1 - half) own heads h0 + 16*hb .. +15. Each computes
+//    S^T = K Q^T for its 16 entries of the tile (entries 16*half ..) with 18
+//    v_mfma_f32_16x16x32_bf16, q in registers as the B operand; the two 16x16 blocks are swapped
+//    through LDS, and both waves run the same online softmax over all 32 entries (identical
+//    state, no further exchange). The S^T accumulator layout (lane: head n, entries 4g..4g+3)
+//    is the A-operand layout of P, so P is built in registers: slots 0..3 = entries 4g..4g+3,
+//    slots 4..7 = entries 16+4g..16+4g+3.
+//  * P V: each wave accumulates its half of the 512 value columns (16 MFMAs per tile). The B
+//    operands come straight from the row-major tile through ds_read_b64_tr_b16: within each
+//    group of 16 lanes, if lane j reads M[j][0..3], lane 4a+b receives {M[a][b], M[a+4][b],
+//    M[a+8][b], M[a+12][b]}. Lane j of group g reading entry 4g + j/4 at column c + 4*(j%4)
+//    therefore receives, in lane n, V[4g+0..3][c+n] (B slots 0..3 in P's order); a second read
+//    16 rows further supplies slots 4..7.
+//  * Online softmax in the exp2 domain with a lazily moved reference (the accumulators are only
+//    rescaled when a head's maximum grows by more than kRefSlack); head maxima are reduced across
+//    lane groups with v_permlane16_swap / v_permlane32_swap (no LDS round trip). Few-query calls
+//    split the entry list and merge the (m, l, O) partials in attend_combine.
+//  * Workgroups are numbered so that each XCD (workgroup id mod 8) gets a contiguous run of
+//    (row, head group, split): the splits of a query share that XCD's L2 for q and the tiles.
 // ------------------------------------------------------------------------------------------
-constexpr int kLatStride = 1040;                 // bytes per latent row in LDS
-constexpr int kStageLat = kTile * kLatStride;    // 33280
+constexpr int kLatStride = 1056;                 // bytes per latent row in LDS
+constexpr int kStageLat = kTile * kLatStride;    // 33792
 constexpr int kStageRope = kTile * 128;          // 4096
-constexpr int kStage = kStageLat + kStageRope;   // 37376
+constexpr int kStage = kStageLat + kStageRope;   // 37888
+constexpr int kStages = 3;
+constexpr int kAtWaves = 8;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 template <int N_>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N_) : "memory");
 }
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
+// max / sum over the four 16-lane groups, on the VALU (permlane swaps exchange rows of 16 and
+// halves of 32 lanes between two registers)
+__device__ __forceinline__ float group_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
-// 16 ds_read_b64_tr_b16 for dim blocks d0 .. d0+7 (entry halves 4g.. and 16+4g..), waited for
-// inside the same asm block. Written as asm because the builtin carries no memory operand, which
-// makes the compiler wait for every LDS DMA still in flight before it.
+// Workgroup id -> work item, XCD-major: with T % 8 == 0, XCD x (id % 8) runs items
+// x*T/8 .. (x+1)*T/8 - 1 in order.
+__device__ __forceinline__ int xcd_item(int lin, int T) {
+  const int remapped = (lin & 7) * (T >> 3) + (lin >> 3);
+  return (T & 7) ? lin : remapped;
+}
+
+// 16 ds_read_b64_tr_b16 for value-column blocks d0 .. d0+7 (entries 4g.. and 16+4g..), waited
+// for inside the same asm block. Written as asm because the builtin carries no memory operand,
+// which makes the compiler wait for every LDS DMA still in flight before it.
 #define DSA_TR(i, off) "ds_read_b64_tr_b16 %" #i ", %16 offset:" #off "\n"
-#define DSA_TR_PAIR(i0, i1, D) DSA_TR(i0, (D) * 32) DSA_TR(i1, 16640 + (D) * 32)
+#define DSA_TR_PAIR(i0, i1, D) DSA_TR(i0, (D) * 32) DSA_TR(i1, 16896 + (D) * 32)
 #define DSA_TR_BLOCK(D0)                                                                        \
   case D0:                                                                                      \
     asm volatile(DSA_TR_PAIR(0, 1, D0) DSA_TR_PAIR(2, 3, D0 + 1) DSA_TR_PAIR(4, 5, D0 + 2)      \
@@ -116,184 +147,246 @@ typedef __attribute__((address_space(3))) void lds_void_t;
     break;
 __device__ __forceinline__ void tr_read_block(u32x2_t* tr, uint32_t vaddr, int d0) {
   switch (d0) {
-    DSA_TR_BLOCK(0) DSA_TR_BLOCK(8) DSA_TR_BLOCK(16) DSA_TR_BLOCK(24)
+    DSA_TR_BLOCK(0) DSA_TR_BLOCK(8)
   }
 }
 #undef DSA_TR_BLOCK
 #undef DSA_TR_PAIR
 #undef DSA_TR
 
-template <int NS>
-__global__ __launch_bounds__(256, 1) void attend_mfma_dma(
+__global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw, int64_t raw_base,
     int64_t n_raw, const int32_t* __restrict__ q_pos, int T, int N, int H, int top_k, int W,
     float scale_log2, int64_t qi0, int nsplit, int per_split, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
-  constexpr int DK = 576, DV = 512, KK = DK / 32, DB = DV / 16;
-  constexpr int DMAS = 9;  // DMA instructions per wave per tile
-  __shared__ __attribute__((aligned(16))) char smem[NS * kStage];
-  extern __shared__ int scode[];  // entry codes of this split, padded to whole tiles
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int nitems) {
+  constexpr int DK = 576, DV = 512, KS = DK / 32, DH = DV / 16 / 2;
+  __shared__ __attribute__((aligned(16))) char smem[kStages * kStage];
+  __shared__ __attribute__((aligned(16))) f32x4_t sx[kAtWaves][64];  // S^T blocks of the pairs
+  extern __shared__ __attribute__((aligned(16))) int scode[];    // entry codes, whole tiles
 
+  // all kernel arguments in one scalar round trip (the compiler otherwise loads them lazily,
+  // in several dependent batches)
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  asm volatile(""
+               : "+s"(bx), "+s"(by), "+s"(bz)
+               : "s"(q), "s"(kv), "s"(idx), "s"(kv_raw), "s"(q_pos), "s"(qi0), "s"(raw_base),
+                 "s"(n_raw), "s"(T), "s"(N), "s"(H), "s"(top_k), "s"(W), "s"(nsplit),
+                 "s"(per_split), "s"(nitems));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hb = wv & 3, half = wv >> 2;
   const int n = lane & 15, g = lane >> 4;
-  const int64_t row = blockIdx.z;
+  const int HG = H / 64;
+  const int item = xcd_item(bx + nsplit * (by + HG * bz), nitems);
+  const int split = item % nsplit;
+  const int hg = (item / nsplit) % HG;
+  const int64_t row = item / (nsplit * HG);
   const int64_t qi = qi0 + row;
-  const int b = (int)(qi / T);
-  const int p = q_pos[qi];
-  const int split = blockIdx.x;
-  const int h0 = blockIdx.y * 64 + wv * 16;
+  const int b = (int)((uint32_t)qi / (uint32_t)T);  // query rows < 2^31
+  const int h0 = hg * 64 + hb * 16;
   const int E = top_k + W;
   const int e_begin = split * per_split;
   const int e_end = min(E, e_begin + per_split);
   const int ntiles = e_end > e_begin ? (e_end - e_begin + kTile - 1) / kTile : 0;
+  const int ncode = ntiles * kTile;
   const int32_t* __restrict__ idxrow = idx + row * (int64_t)top_k;
-  const uint16_t* fallback = kv + (size_t)b * N * DK;  // any valid row; masked in the softmax
 
-  u32x4_t qf[KK];
+  // Prologue: the idx reads of this thread's first two code slots (unconditional, clamped
+  // address) and then the q loads are all issued before the first wait.
+  int raw[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) raw[j] = idxrow[min(e_begin + tid + j * kAtWaves * 64, top_k - 1)];
+  // q fragments: lane (head n, group g) holds q[h0+n][32kk + 8g .. +7]
+  u32x4_t qf[KS];
   {
     const uint16_t* qh = q + ((size_t)qi * H + h0 + n) * DK + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const u32x4_t*>(qh + 32 * kk);
-    // complete the q loads here and make the values opaque: no wait for them inside the DMA
-    // pipeline below, and no re-loading next to each use
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(qf[kk]));
+    for (int kk = 0; kk < KS; ++kk) qf[kk] = *reinterpret_cast<const u32x4_t*>(qh + 32 * kk);
   }
-  // resolve the split's entries once: idx -> row code (masked rows keep a valid fallback address
-  // for their DMA and are excluded in the softmax)
-  for (int i = tid; i < ntiles * kTile; i += 256) {
+  const int p = q_pos[qi];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    asm volatile("" : "+v"(raw[j]));  // keep the reads above, not sunk into the branches below
+    const int i = tid + j * kAtWaves * 64;
+    const int e = e_begin + i;
+    int code = -1;
+    if (e < e_end) {
+      if (e < top_k) {
+        code = (raw[j] >= 0 && raw[j] < N) ? raw[j] : -1;
+      } else {
+        const int64_t r = (int64_t)p - W + 1 + (e - top_k);
+        if (kv_raw != nullptr && r >= 0 && r >= raw_base && r < raw_base + n_raw)
+          code = -(int)(r - raw_base) - 2;
+      }
+    }
+    if (i < ncode) scode[i] = code;
+  }
+  for (int i = tid + 2 * kAtWaves * 64; i < ncode; i += kAtWaves * 64) {
     const int e = e_begin + i;
     scode[i] = e < e_end ? entry_code(e, idxrow, top_k, N, raw_base, n_raw, p, W, kv_raw != nullptr)
                          : -1;
   }
-  __syncthreads();
-  auto rowptr = [&](int code) -> const uint16_t* {
-    if (code >= 0) return kv + ((size_t)b * N + code) * DK;
-    if (code <= -2) return kv_raw + ((size_t)b * n_raw + (-code - 2)) * DK;
-    return fallback;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+
+  // row address of an entry code (masked entries read row 0 of the sequence; excluded in the
+  // softmax)
+  const uint16_t* kv_b = kv + (size_t)b * N * DK;
+  const uint16_t* raw_b = kv_raw + (size_t)b * n_raw * DK;
+  auto rowaddr = [&](int code) -> uint64_t {
+    const uint64_t a = (uint64_t)(uintptr_t)(kv_b + (size_t)max(code, 0) * DK);
+    const uint64_t r = (uint64_t)(uintptr_t)(raw_b + (size_t)max(-code - 2, 0) * DK);
+    return code <= -2 ? r : a;
   };
-
-  f32x4_t acc[DB];
-#pragma unroll
-  for (int d = 0; d < DB; ++d) acc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
-
-  // issue the DMAs of tile t (this wave's rows 8*wv .. 8*wv+7)
-  auto issue = [&](int t) {
-    const int stage = t % NS;
-    // the DMA destination goes through an opaque wave-uniform integer: the waits for these
-    // transfers are the explicit vmcnt waits of the pipeline below
+  // DMAs of tile t: wave w moves rows 4w .. 4w+3 (latent), waves 0..3 also the rope parts of
+  // rows 8w .. 8w+7. Per tile: 5 DMA instructions for waves 0..3, 4 for waves 4..7. The codes
+  // of the rows are read from LDS one tile ahead (fetch), so the issue never waits on LDS.
+  int nx_lat = -1, nx_rope = -1;
+  auto fetch = [&](int t) {
+    const int c0 = kTile * t;
+    nx_lat = scode[c0 + 4 * wv + (lane & 3)];
+    nx_rope = wv < 4 ? scode[c0 + 8 * wv + (lane >> 3)] : -1;
+  };
+  // one DMA of tile t: step 0..3 = latent row 4w + step, step 4 = the rope parts (waves 0..3)
+  auto issue_step = [&](int t, uint64_t pl, int step) {
     const uint32_t sbase = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(lds_void_t*)(smem + stage * kStage));
-    const int c0 = kTile * t + 8 * wv;  // this wave's first row in the code table
-    // lane l resolves row l & 7 (latent DMAs, via readlane) and row l >> 3 (its rope chunk)
-    const uint64_t pl = (uint64_t)(uintptr_t)rowptr(scode[c0 + (lane & 7)]);
-    const uint16_t* pr = rowptr(scode[c0 + (lane >> 3)]);
-#pragma unroll
-    for (int r8 = 0; r8 < 8; ++r8) {
-      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pl, r8);
-      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(pl >> 32), r8);
+        (uint32_t)(uintptr_t)(lds_void_t*)(smem + (t % kStages) * kStage));
+    if (step < 4) {
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pl, step);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(pl >> 32), step);
       const uint16_t* src = reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
       __builtin_amdgcn_global_load_lds(
           reinterpret_cast<const void*>(src + 8 * lane),
-          (lds_void_t*)(uintptr_t)(sbase + (8 * wv + r8) * kLatStride), 16, 0, 0);
+          (lds_void_t*)(uintptr_t)(sbase + (4 * wv + step) * kLatStride), 16, 0, 0);
+    } else if (wv < 4) {
+      const int R = 8 * wv + (lane >> 3);
+      const uint16_t* pr = reinterpret_cast<const uint16_t*>(rowaddr(nx_rope));
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(pr + 512 + 8 * ((lane & 7) ^ ((R >> 1) & 7))),
+          (lds_void_t*)(uintptr_t)(sbase + kStageLat + wv * 1024), 16, 0, 0);
     }
-    const int rr = lane >> 3;
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const void*>(pr + 512 + 8 * ((lane & 7) ^ rr)),
-        (lds_void_t*)(uintptr_t)(sbase + kStageLat + wv * 1024), 16, 0, 0);
+  };
+  auto issue = [&](int t) {
+    const uint64_t pl = rowaddr(nx_lat);
+#pragma unroll
+    for (int step = 0; step < 5; ++step) issue_step(t, pl, step);
   };
 
-  for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t);
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + NS - 1 < ntiles) issue(t + NS - 1);
-    const int later = min(NS - 1, ntiles - 1 - t);
-    if (later >= 2) wait_vm<2 * DMAS>();
-    else if (later == 1) wait_vm<DMAS>();
-    else wait_vm<0>();
-    __builtin_amdgcn_s_barrier();
+  if (ntiles > 0) { fetch(0); issue(0); }
+  if (ntiles > 1) { fetch(1); issue(1); }
+  if (ntiles > 2) fetch(2);
+  // complete the q loads here and make the values opaque: no wait for them inside the DMA
+  // pipeline below, and no re-loading next to each use
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qf[kk]));
 
-    const int stage = t % NS;
-    const char* sb = smem + stage * kStage;
-    // S^T per 16-entry block: its 18 A-operand reads issued first, then two independent MFMA
-    // chains (even / odd k-step)
-    f32x4_t sp[2][2] = {};
+  f32x4_t acc[DH];  // columns 256*half + 16d + n, heads 4g+i
 #pragma unroll
-    for (int eb = 0; eb < 2; ++eb) {
-      const int R = eb * 16 + n;
-      u32x4_t av[KK];
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const char* ap;
-        if (kk < 16) {
-          ap = sb + R * kLatStride + (32 * kk + 8 * g) * 2;
-        } else {
-          const int c = 4 * (kk - 16) + g;
-          ap = sb + kStageLat + R * 128 + ((c ^ (R & 7)) * 16);
-        }
-        av[kk] = *reinterpret_cast<const u32x4_t*>(ap);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        sp[eb][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[kk]), as_bf16x8(qf[kk]),
-                                                                 sp[eb][kk & 1], 0, 0, 0);
+  for (int d = 0; d < DH; ++d) acc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf;  // per head n (same in the four lane groups and in both waves)
+  float l_run = 0.f;      // this lane's share: entries 4g.., 16+4g.. of every tile
+
+  const int R0 = 16 * half + n;  // S^T row (entry) read by this lane
+  for (int t = 0; t < ntiles; ++t) {
+    // tile t landed (tile t+1 may still be in flight) and every wave is done with tile t-1
+    if (t + 1 < ntiles) {
+      if (wv < 4) wait_vm<5>(); else wait_vm<4>();
+    } else {
+      wait_vm<0>();
     }
-    f32x4_t st[2] = {sp[0][0] + sp[0][1], sp[1][0] + sp[1][1]};
+    __builtin_amdgcn_s_barrier();
+    // DMAs of tile t+2 (into the stage tile t-1 used) are spread over the S MFMAs below so that
+    // the wave never stalls on a full address queue
+    const bool pf = t + 2 < ntiles;
+    const uint64_t pl = rowaddr(nx_lat);
+
+    const char* sb = smem + (t % kStages) * kStage;
+    const i32x4_t cd0 = *reinterpret_cast<const i32x4_t*>(scode + kTile * t + 4 * g);
+    const i32x4_t cd1 = *reinterpret_cast<const i32x4_t*>(scode + kTile * t + 16 + 4 * g);
+    // S^T for this wave's 16 entries x 16 heads over 4 accumulators (k-steps kk % 4), so that 4
+    // independent MFMA chains are in flight: 12 reads, the first 6 MFMAs, the last 6 reads, the
+    // remaining 12 MFMAs
+    auto ld = [&](int kk) -> u32x4_t {
+      const char* ap;
+      if (kk < 16) {
+        ap = sb + R0 * kLatStride + 64 * kk + 16 * g;
+      } else {
+        const int c = 4 * (kk - 16) + g;
+        ap = sb + kStageLat + R0 * 128 + ((c ^ ((R0 >> 1) & 7)) * 16);
+      }
+      return *reinterpret_cast<const u32x4_t*>(ap);
+    };
+    f32x4_t sa[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sa[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    u32x4_t av[KS];
+#pragma unroll
+    for (int kk = 0; kk < 12; ++kk) av[kk] = ld(kk);
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      sa[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[kk]), as_bf16x8(qf[kk]), sa[kk & 3], 0, 0, 0);
+      if (pf && kk < 5) issue_step(t + 2, pl, kk);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 12; kk < KS; ++kk) av[kk] = ld(kk);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 6; kk < KS; ++kk)
+      sa[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[kk]), as_bf16x8(qf[kk]), sa[kk & 3], 0, 0, 0);
+    if (pf && t + 3 < ntiles) fetch(t + 3);
+    const f32x4_t st = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+    // swap the S^T blocks with the partner wave
+    sx[wv][lane] = st;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    const f32x4_t so = sx[wv ^ 4][lane];
+    // lane (head n, g): entries 4g+i (z[i]) and 16+4g+i (z[4+i])
     float z[8];
     float mx = kNegInf;
 #pragma unroll
-    for (int eb = 0; eb < 2; ++eb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = eb * 16 + 4 * g + i;
-        float v = scode[kTile * t + e] != -1 ? st[eb][i] * scale_log2 : kNegInf;
-        z[eb * 4 + i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    for (int i = 0; i < 4; ++i) {
+      const float s0 = half ? so[i] : st[i], s1 = half ? st[i] : so[i];
+      z[i] = cd0[i] != -1 ? s0 * scale_log2 : kNegInf;
+      z[4 + i] = cd1[i] != -1 ? s1 * scale_log2 : kNegInf;
+      mx = fmaxf(mx, fmaxf(z[i], z[4 + i]));
+    }
+    mx = group_max(mx);
     // Lazily moved softmax reference: m_run only moves (and the accumulators are rescaled) when
-    // a head's tile maximum exceeds it by more than kRefSlack (log2 units), so p <= 2^kRefSlack
-    // and the rescale of the 128 accumulators, which live in AGPRs, is rare.
+    // a head's tile maximum exceeds it by more than kRefSlack (log2 units), so p <= 2^kRefSlack.
     const bool grow = mx > m_run + kRefSlack;
     if (__ballot(grow) != 0) {
       const float m_new = grow ? mx : m_run;
       const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
       m_run = m_new;
+      // accumulator rows are heads 4g+i
       float ai[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i, 64);
 #pragma unroll
-      for (int d = 0; d < DB; ++d)
+      for (int d = 0; d < DH; ++d)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[d][i] *= ai[i];
     }
-    float psum = 0.f;
     uint32_t pk[4];
-    {
-      float pe[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // m_run == -inf only while every entry so far is masked (z == -inf as well)
-        pe[i] = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(z[i] - m_run);
-        psum += pe[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pe[2 * i], pe[2 * i + 1]);
+    for (int i = 0; i < 4; ++i) {
+      // m_run == -inf only while every entry so far is masked (z == -inf as well)
+      const float e0 = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(z[2 * i] - m_run);
+      const float e1 = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(z[2 * i + 1] - m_run);
+      l_run += e0 + e1;
+      pk[i] = pack_bf16x2(e0, e1);
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run += psum;
     const bf16x8_t pa = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-    // transposed V reads: rows 4g + n/4 (entries 4g..4g+3) and 16 + 4g + n/4, column 4*(n%4)
-    const uint32_t vaddr = (uint32_t)(uintptr_t)(lds_void_t*)(sb + (4 * g + (n >> 2)) * kLatStride +
-                                                             8 * (n & 3));
+    // transposed V reads: entry 4g + n/4 (and 16 rows on), column 256*half + 16d + 4*(n%4)
+    const uint32_t vaddr = (uint32_t)(uintptr_t)(lds_void_t*)(
+        sb + (4 * g + (n >> 2)) * kLatStride + 512 * half + 8 * (n & 3));
 #pragma unroll
-    for (int d0 = 0; d0 < DB; d0 += 8) {
+    for (int d0 = 0; d0 < DH; d0 += 8) {
       u32x2_t tr[16];
       tr_read_block(tr, vaddr, d0);
 #pragma unroll
@@ -302,77 +395,121 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_dma(
         acc[d0 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(bw), acc[d0 + d], 0, 0, 0);
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
   }
 
+  // ---- epilogue: this wave's 256 columns of its 16 heads ----
+  const float l_head = group_sum(l_run);  // per head n
   float li[4], mi[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    li[i] = __shfl(l_run, 4 * g + i, 64);
+    li[i] = __shfl(l_head, 4 * g + i, 64);
     mi[i] = __shfl(m_run, 4 * g + i, 64);
   }
   if (nsplit == 1) {
+    const int c0 = 256 * half + n;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float inv = li[i] > 0.f ? 1.f / li[i] : 0.f;
-      uint16_t* orow = out + ((size_t)qi * H + h0 + 4 * g + i) * DV + n;
+      uint16_t* orow = out + ((size_t)qi * H + h0 + 4 * g + i) * DV + c0;
 #pragma unroll
-      for (int d = 0; d < DB; ++d) orow[16 * d] = f32_to_bf16(acc[d][i] * inv);
+      for (int d = 0; d < DH; ++d) orow[16 * d] = f32_to_bf16(acc[d][i] * inv);
     }
-    if (g == 0 && lse)
-      lse[(size_t)qi * H + h0 + n] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
+    if (half == 0 && g == 0 && lse)
+      lse[(size_t)qi * H + h0 + n] = l_head > 0.f ? (m_run + __log2f(l_head)) * kLn2 : kNegInf;
   } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t hrow = ((size_t)row * H + h0 + 4 * g + i) * nsplit + split;
-      float* po = part_o + hrow * DV + n;
-      for (int d = 0; d < DB; ++d) po[16 * d] = acc[d][i];
-      if (n == 0) {
-        part_ml[hrow * 2] = mi[i];
-        part_ml[hrow * 2 + 1] = li[i];
-      }
+    if (half == 0 && g == 0) {
+      const size_t hrow = ((size_t)row * H + h0 + n) * nsplit + split;
+      part_ml[hrow * 2] = m_run;
+      part_ml[hrow * 2 + 1] = l_head;
     }
+    // O partials (fp32, relative to this split's m) in register order:
+    // [row][head group][split][wave][16 column blocks][64 lanes] x 4 heads (4g..4g+3 of column
+    // 16d + n): whole 1 KB stores
+    f32x4_t* po = reinterpret_cast<f32x4_t*>(part_o) +
+                  ((((size_t)row * HG + hg) * nsplit + split) * 8 + wv) * DH * 64 + lane;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) po[d * 64] = acc[d];
   }
 }
 
-// Merge split partials: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
-// One workgroup of D_V/4 threads per (row, head); each thread owns 4 consecutive columns and
-// reads every split's float4 (fully coalesced 2 KB per split).
-template <typename OT>
-__global__ __launch_bounds__(128) void attend_combine(
+// Merge split partials: out = sum_s w_s O_s, w_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s,
+// M = max_s m_s. One workgroup per (wave slot, head group, row): 16 heads x 256 columns, the
+// block written by one wave of attend_mfma_dma per split. Partials are read as whole 1 KB rows
+// of f32x4; the bf16 result goes through LDS so that each row of the output is written with
+// 16-byte stores.
+constexpr int kMaxSplits = 8;
+__global__ __launch_bounds__(256) void attend_combine(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int64_t qi0, int H,
-    int DV, int nsplit, OT* __restrict__ out, float* __restrict__ lse) {
-  const int h = blockIdx.x;
-  const int64_t row = blockIdx.y;
-  const size_t hrow = ((size_t)row * H + h) * nsplit;
-  float M = kNegInf;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(hrow + s) * 2]);
-  float L = 0.f;
-  float a[4] = {0.f, 0.f, 0.f, 0.f};
-  const int d = 4 * threadIdx.x;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = part_ml[(hrow + s) * 2];
-    const float sc = ms == kNegInf ? 0.f : exp2f(ms - M);
-    L += sc * part_ml[(hrow + s) * 2 + 1];
-    if (d < DV) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(part_o + (hrow + s) * DV + d);
+    int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse, int nitems) {
+  constexpr int DV = 512;
+  __shared__ float wsc[kMaxSplits][16];
+  __shared__ __attribute__((aligned(16))) uint16_t sout[16][256 + 8];
+  const int HG = H / 64;
+  const int item = xcd_item(blockIdx.x + 8 * (blockIdx.y + HG * blockIdx.z), nitems);
+  const int ws = item & 7, hg = (item >> 3) % HG;
+  const int64_t row = item / (8 * HG);
+  const int64_t qi = qi0 + row;
+  const int h0 = hg * 64 + 16 * (ws & 3), c0 = 256 * (ws >> 2);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 4, n = lane & 15;
+  // every load is issued before the first use: partial O blocks for all splits (predicated on
+  // nsplit, a runtime value <= kMaxSplits) and the (m, l) pairs, one per thread
+  const f32x4_t* base = reinterpret_cast<const f32x4_t*>(part_o) +
+                        (((size_t)row * HG + hg) * nsplit * 8 + ws) * 16 * 64;
+  f32x4_t v[4][kMaxSplits];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] += sc * v[i];
+  for (int k = 0; k < 4; ++k) {
+    const int d = (tid >> 6) + 4 * k;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+      v[k][s] = s < nsplit ? base[(size_t)s * 8 * 16 * 64 + d * 64 + lane] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  float ml_m = kNegInf, ml_l = 0.f;
+  {
+    const int hh = tid >> 3, s = tid & 7;  // 16 heads x 8 splits = threads 0..127
+    if (tid < 128 && s < nsplit) {
+      const size_t hrow = ((size_t)row * H + h0 + hh) * nsplit + s;
+      ml_m = part_ml[hrow * 2];
+      ml_l = part_ml[hrow * 2 + 1];
     }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  const size_t orow = ((size_t)(qi0 + row) * H + h) * DV;
-  if (d < DV) {
-    if constexpr (sizeof(OT) == 2) {
-      *reinterpret_cast<u32x2_t*>(out + orow + d) =
-          u32x2_t{pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv)};
-    } else {
-      *reinterpret_cast<f32x4_t*>(out + orow + d) = f32x4_t{a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv};
-    }
+  // per head: M = max_s m_s, L = sum_s 2^(m_s - M) l_s, over the 8 lanes of each head
+  float M = ml_m;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  const float wm = ml_m == kNegInf ? 0.f : exp2f(ml_m - M);
+  const float wl = wm * ml_l;
+  float L = wl;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) L += __shfl_xor(L, o, 64);
+  if (tid < 128) {
+    const int hh = tid >> 3, s = tid & 7;
+    wsc[s][hh] = L > 0.f ? wm / L : 0.f;
+    if (s == 0 && lse) lse[(size_t)qi * H + h0 + hh] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
   }
-  if (threadIdx.x == 0 && lse)
-    lse[(size_t)(qi0 + row) * H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int d = (tid >> 6) + 4 * k;
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      if (s < nsplit) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] += wsc[s][4 * g + i] * v[k][s][i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sout[4 * g + i][16 * d + n] = f32_to_bf16(a[i]);
+  }
+  __syncthreads();
+  // 16 rows x 512 bytes: 2 chunks of 16 bytes per thread
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = tid + 256 * k, r = c >> 5, col = (c & 31) * 8;
+    *reinterpret_cast<u32x4_t*>(out + ((size_t)qi * H + h0 + r) * DV + c0 + col) =
+        *reinterpret_cast<const u32x4_t*>(&sout[r][col]);
+  }
 }
 
 // ---- generic scalar path ----
@@ -462,13 +599,14 @@ int attend_splits(const Shape& s, int64_t nrows, int fmt) {
   int64_t want = (512 + wgs - 1) / wgs;
   int64_t maxs = (E + 255) / 256;  // at least 256 entries per split
   int64_t ns = want < maxs ? want : maxs;
-  if (ns > 8) ns = 8;
+  if (ns > kMaxSplits) ns = kMaxSplits;
   return ns < 1 ? 1 : (int)ns;
 }
 
 size_t attend_ws_bytes(const Shape& s, int64_t nrows, int fmt) {
   const int ns = attend_splits(s, nrows, fmt);
   if (ns <= 1) return 0;
+  // fp32 O partials, then (m, l) pairs
   return (size_t)nrows * s.H * ns * ((size_t)s.D_V + 2) * sizeof(float);
 }
 
@@ -485,20 +623,29 @@ hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, co
     float* part_ml = ns > 1 ? part_o + (size_t)nrows * s.H * ns * s.D_V : nullptr;
     dim3 grid(ns, s.H / 64, (unsigned)nrows);
     const size_t code_bytes = sizeof(int) * (size_t)per;  // per is a multiple of the tile
-    static std::once_flag once;  // the code table can take the block past 64 KB of LDS
+    // the entry-code table is dynamic LDS on top of the static stages: allow up to the 160 KB
+    // a workgroup can hold
+    constexpr size_t kLdsMax = 160 * 1024;
+    constexpr size_t kStatic = kStages * kStage + sizeof(f32x4_t) * kAtWaves * 64;
+    if (code_bytes > kLdsMax - kStatic) return hipErrorInvalidValue;
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_mfma_dma<2>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 48 * 1024);
+      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_mfma_dma),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsMax - kStatic));
     });
-    attend_mfma_dma<2><<<grid, 256, code_bytes, st>>>(
+    if (attr != hipSuccess) return attr;
+    attend_mfma_dma<<<grid, kAtWaves * 64, code_bytes, st>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
         static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H, s.top_k, s.W,
-        scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse, part_o, part_ml);
+        scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse, part_o, part_ml,
+        (int)(ns * (s.H / 64) * nrows));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
     if (between) (void)hipEventRecord(between, st);
-    attend_combine<uint16_t><<<dim3(s.H, (unsigned)nrows), 128, 0, st>>>(
-        part_o, part_ml, qi0, s.H, s.D_V, ns, static_cast<uint16_t*>(out), lse);
+    attend_combine<<<dim3(8, s.H / 64, (unsigned)nrows), 256, 0, st>>>(
+        part_o, part_ml, qi0, s.H, ns, static_cast<uint16_t*>(out), lse,
+        (int)(8 * (s.H / 64) * nrows));
     return hipGetLastError();
   }
   const int E = s.top_k + s.W;
