@@ -54,13 +54,15 @@ def _kernel_plan(cfg, nsplit):
     rows = cfg.B * cfg.T
     if fast and cfg.k_dt == "bf16" and rows >= 64:
         names.append("indexer_prefill_mfma")
+    elif fast and cfg.k_dt == "bf16":
+        names.append("indexer_decode_dma")
     elif fast:
         names.append("indexer_decode_mfma")
     else:
         names.append("indexer_generic")
     names.append("topk_radix_row")
     mfma = cfg.dt == "bf16" and cfg.D_K == 576 and cfg.D_V == 512 and cfg.H % 64 == 0
-    names.append("attend_mfma" if mfma else "attend_generic")
+    names.append("attend_mfma_dma" if mfma else "attend_generic")
     if nsplit > 1:
         names.append("attend_combine")
     return names
@@ -225,7 +227,7 @@ def main():
     print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     # input copies so that one cycle touches > 512 MB
-    touched = sum(_algorithmic(cfg, k)[0] for k in ("indexer_x", "attend_mfma"))
+    touched = sum(_algorithmic(cfg, k)[0] for k in ("indexer_x", "attend_mfma_dma"))
     R = args.rotate or max(1, min(16, int(512e6 // max(touched, 1.0)) + 1))
     if cfg.B * cfg.T > 64:
         R = args.rotate or 1

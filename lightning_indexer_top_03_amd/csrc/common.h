@@ -20,17 +20,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN): v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// Two fp32 -> packed bf16x2 (low half = a), RNE.
+// Two fp32 -> packed bf16x2 (low half = a), round to nearest even, one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // Visible entries of a query at raw position p with compression m over N entries.
