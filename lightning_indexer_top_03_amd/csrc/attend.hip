@@ -61,40 +61,42 @@ __device__ __forceinline__ int entry_code(int e, const int32_t* __restrict__ idx
 
 // ------------------------------------------------------------------------------------------
 // attend_mfma_dma (bf16, D_K = 576, D_V = 512, H % 64 == 0): one workgroup = 8 waves = 64 heads
-// of one query over a split of its entry list, 32-entry tiles.
-//  * Gather: each tile goes straight from HBM into a 3-stage LDS ring with global_load_lds_dwordx4
-//    (no register staging): one DMA per row for the 1024-byte latent part (fully coalesced) and
-//    one per 8 rows for their 128-byte rope parts. Latent rows sit at a 1056-byte stride: both
-//    the row-per-lane 16-byte reads of S and the transposed 8-byte reads of P V are then free of
-//    bank conflicts. The rope parts are [32 rows][8 chunks of 16 B], chunk c of row R at slot
-//    c ^ ((R >> 1) & 7), again conflict-free for the row-per-lane reads. Waits are explicit
-//    (s_waitcnt vmcnt + s_barrier, no fence), so two tiles' DMAs stay in flight behind the one
-//    being computed.
-//  * Wave (hb, half) and its partner (hb, 1 - half) own heads h0 + 16*hb .. +15. Each computes
-//    S^T = K Q^T for its 16 entries of the tile (entries 16*half ..) with 18
-//    v_mfma_f32_16x16x32_bf16, q in registers as the B operand; the two 16x16 blocks are swapped
-//    through LDS, and both waves run the same online softmax over all 32 entries (identical
-//    state, no further exchange). The S^T accumulator layout (lane: head n, entries 4g..4g+3)
-//    is the A-operand layout of P, so P is built in registers: slots 0..3 = entries 4g..4g+3,
-//    slots 4..7 = entries 16+4g..16+4g+3.
-//  * P V: each wave accumulates its half of the 512 value columns (16 MFMAs per tile). The B
-//    operands come straight from the row-major tile through ds_read_b64_tr_b16: within each
-//    group of 16 lanes, if lane j reads M[j][0..3], lane 4a+b receives {M[a][b], M[a+4][b],
-//    M[a+8][b], M[a+12][b]}. Lane j of group g reading entry 4g + j/4 at column c + 4*(j%4)
-//    therefore receives, in lane n, V[4g+0..3][c+n] (B slots 0..3 in P's order); a second read
-//    16 rows further supplies slots 4..7.
-//  * Online softmax in the exp2 domain with a lazily moved reference (the accumulators are only
-//    rescaled when a head's maximum grows by more than kRefSlack); head maxima are reduced across
-//    lane groups with v_permlane16_swap / v_permlane32_swap (no LDS round trip). Few-query calls
-//    split the entry list and merge the (m, l, O) partials in attend_combine.
-//  * Workgroups are numbered so that each XCD (workgroup id mod 8) gets a contiguous run of
+// of one query over a split of its entry list, 32-entry tiles, software-pipelined across two
+// kinds of wave so that every SIMD runs one of each:
+//  * Gather: each tile goes straight from HBM into an NS-stage LDS ring with
+//    global_load_lds_dwordx4 (no register staging): one DMA per row for the 1024-byte latent part
+//    (fully coalesced) and one per 8 rows for their 128-byte rope parts. Latent rows sit at a
+//    1056-byte stride: both the row-per-lane 16-byte reads of S and the transposed 8-byte reads
+//    of P V are then free of bank conflicts. The rope parts are [32 rows][8 chunks of 16 B],
+//    chunk c of row R at slot c ^ ((R >> 1) & 7), again conflict-free for the row-per-lane reads.
+//    Waits are explicit (s_waitcnt vmcnt + s_barrier, no fence).
+//  * Score waves 0..3 (head block hb = wave): in iteration i, S^T = K Q^T for the 32 entries of
+//    tile i (two 16-entry blocks, 8 independent chains of v_mfma_f32_16x16x32_bf16 with q in
+//    registers as the B operand) and the online softmax (exp2 domain; the reference moves only
+//    when a head's maximum grows by more than kRefSlack; head maxima reduced with
+//    v_permlane16_swap / v_permlane32_swap). The S^T accumulator layout (lane: head n, entries
+//    4g..4g+3) is the A-operand layout of P, so each lane hands its packed P (slots 0..3 =
+//    entries 4g.., slots 4..7 = entries 16+4g..) to its value wave through LDS unchanged, with
+//    the rescale factors when the reference moved.
+//  * Value waves 4..7: in iteration i, P V for tile i-1; wave 4+v owns 32 heads (head blocks
+//    2*(v&1), 2*(v&1)+1) and value columns 256*(v>>1).. +255, so each pair of transposed V
+//    reads feeds two MFMAs (32 MFMAs per tile, V read from LDS once per 32 heads). The B operands come straight from the row-major tile through
+//    ds_read_b64_tr_b16: within each group of 16 lanes, if lane j reads M[j][0..3], lane 4a+b
+//    receives {M[a][b], M[a+4][b], M[a+8][b], M[a+12][b]}. Lane j of group g reading entry
+//    4g + j/4 at column c + 4*(j%4) therefore receives, in lane n, V[4g+0..3][c+n] (B slots 0..3
+//    in P's order); a second read 16 rows further supplies slots 4..7.
+//  * One barrier per iteration; the two kinds of wave run separate loops with the same barrier
+//    count, so the register allocator never holds q and the accumulators at once. The ring is
+//    4 stages deep when the split's entry table fits beside it (two tiles in flight ahead of the
+//    score waves), else 3.
+//  * Few-query calls split the entry list and merge the (m, l, O) partials in attend_combine.
+//    Workgroups are numbered so that each XCD (workgroup id mod 8) gets a contiguous run of
 //    (row, head group, split): the splits of a query share that XCD's L2 for q and the tiles.
 // ------------------------------------------------------------------------------------------
 constexpr int kLatStride = 1056;                 // bytes per latent row in LDS
 constexpr int kStageLat = kTile * kLatStride;    // 33792
 constexpr int kStageRope = kTile * 128;          // 4096
 constexpr int kStage = kStageLat + kStageRope;   // 37888
-constexpr int kStages = 3;
 constexpr int kAtWaves = 8;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -128,8 +130,8 @@ __device__ __forceinline__ int xcd_item(int lin, int T) {
 }
 
 // 16 ds_read_b64_tr_b16 for value-column blocks d0 .. d0+7 (entries 4g.. and 16+4g..), waited
-// for inside the same asm block. Written as asm because the builtin carries no memory operand,
-// which makes the compiler wait for every LDS DMA still in flight before it.
+// for inside the same asm block. Written as asm because the builtin carries no memory operand, which makes the compiler wait
+// for every LDS DMA still in flight before it.
 #define DSA_TR(i, off) "ds_read_b64_tr_b16 %" #i ", %16 offset:" #off "\n"
 #define DSA_TR_PAIR(i0, i1, D) DSA_TR(i0, (D) * 32) DSA_TR(i1, 16896 + (D) * 32)
 #define DSA_TR_BLOCK(D0)                                                                        \
@@ -154,6 +156,7 @@ __device__ __forceinline__ void tr_read_block(u32x2_t* tr, uint32_t vaddr, int d
 #undef DSA_TR_PAIR
 #undef DSA_TR
 
+template <int NS>
 __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw, int64_t raw_base,
@@ -161,10 +164,13 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     float scale_log2, int64_t qi0, int nsplit, int per_split, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml,
     int nitems) {
-  constexpr int DK = 576, DV = 512, KS = DK / 32, DH = DV / 16 / 2;
-  __shared__ __attribute__((aligned(16))) char smem[kStages * kStage];
-  __shared__ __attribute__((aligned(16))) f32x4_t sx[kAtWaves][64];  // S^T blocks of the pairs
-  extern __shared__ __attribute__((aligned(16))) int scode[];    // entry codes, whole tiles
+  constexpr int DK = 576, DV = 512, KS = DK / 32, DB = DV / 16;
+  __shared__ __attribute__((aligned(16))) char smem[NS * kStage];
+  __shared__ __attribute__((aligned(16))) u32x4_t pbuf[2][4][64];  // P, per head block
+  __shared__ float abuf[2][4][16];   // rescale factor per head when the reference moved
+  __shared__ uint32_t fbuf[2][4];    // did the reference move (per head block)
+  __shared__ float sml[4][2][16];    // final (m, l) per head
+  extern __shared__ __attribute__((aligned(16))) int scode[];  // entry codes, whole tiles
 
   // all kernel arguments in one scalar round trip (the compiler otherwise loads them lazily,
   // in several dependent batches)
@@ -176,7 +182,8 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
                  "s"(per_split), "s"(nitems));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hb = wv & 3, half = wv >> 2;
+  const bool score_wave = wv < 4;
+  const int hb = wv & 3;
   const int n = lane & 15, g = lane >> 4;
   const int HG = H / 64;
   const int item = xcd_item(bx + nsplit * (by + HG * bz), nitems);
@@ -194,13 +201,13 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
   const int32_t* __restrict__ idxrow = idx + row * (int64_t)top_k;
 
   // Prologue: the idx reads of this thread's first two code slots (unconditional, clamped
-  // address) and then the q loads are all issued before the first wait.
+  // address) and, on the score waves, the q loads are all issued before the first wait.
   int raw[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) raw[j] = idxrow[min(e_begin + tid + j * kAtWaves * 64, top_k - 1)];
-  // q fragments: lane (head n, group g) holds q[h0+n][32kk + 8g .. +7]
+  // q fragments (score waves): lane (head n, group g) holds q[h0+n][32kk + 8g .. +7]
   u32x4_t qf[KS];
-  {
+  if (score_wave) {
     const uint16_t* qh = q + ((size_t)qi * H + h0 + n) * DK + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) qf[kk] = *reinterpret_cast<const u32x4_t*>(qh + 32 * kk);
@@ -241,26 +248,28 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     return code <= -2 ? r : a;
   };
   // DMAs of tile t: wave w moves rows 4w .. 4w+3 (latent), waves 0..3 also the rope parts of
-  // rows 8w .. 8w+7. Per tile: 5 DMA instructions for waves 0..3, 4 for waves 4..7. The codes
+  // rows 8w .. 8w+7: 5 DMA instructions per tile for waves 0..3, 4 for waves 4..7. The codes
   // of the rows are read from LDS one tile ahead (fetch), so the issue never waits on LDS.
   int nx_lat = -1, nx_rope = -1;
   auto fetch = [&](int t) {
     const int c0 = kTile * t;
     nx_lat = scode[c0 + 4 * wv + (lane & 3)];
-    nx_rope = wv < 4 ? scode[c0 + 8 * wv + (lane >> 3)] : -1;
+    nx_rope = score_wave ? scode[c0 + 8 * wv + (lane >> 3)] : -1;
   };
-  // one DMA of tile t: step 0..3 = latent row 4w + step, step 4 = the rope parts (waves 0..3)
-  auto issue_step = [&](int t, uint64_t pl, int step) {
+  auto issue = [&](int t) {
     const uint32_t sbase = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(lds_void_t*)(smem + (t % kStages) * kStage));
-    if (step < 4) {
-      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pl, step);
-      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(pl >> 32), step);
+        (uint32_t)(uintptr_t)(lds_void_t*)(smem + (t % NS) * kStage));
+    const uint64_t pl = rowaddr(nx_lat);
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pl, r4);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(pl >> 32), r4);
       const uint16_t* src = reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
       __builtin_amdgcn_global_load_lds(
           reinterpret_cast<const void*>(src + 8 * lane),
-          (lds_void_t*)(uintptr_t)(sbase + (4 * wv + step) * kLatStride), 16, 0, 0);
-    } else if (wv < 4) {
+          (lds_void_t*)(uintptr_t)(sbase + (4 * wv + r4) * kLatStride), 16, 0, 0);
+    }
+    if (score_wave) {
       const int R = 8 * wv + (lane >> 3);
       const uint16_t* pr = reinterpret_cast<const uint16_t*>(rowaddr(nx_rope));
       __builtin_amdgcn_global_load_lds(
@@ -268,123 +277,169 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
           (lds_void_t*)(uintptr_t)(sbase + kStageLat + wv * 1024), 16, 0, 0);
     }
   };
-  auto issue = [&](int t) {
-    const uint64_t pl = rowaddr(nx_lat);
+  // the ring runs NS-2 tiles ahead of the score waves: tiles 0 .. NS-3 now, tile i + NS - 2 at
+  // the top of iteration i (into the stage the value waves finished with in iteration i-1)
 #pragma unroll
-    for (int step = 0; step < 5; ++step) issue_step(t, pl, step);
+  for (int t = 0; t < NS - 2; ++t)
+    if (t < ntiles) { fetch(t); issue(t); }
+  if (NS - 2 < ntiles) fetch(NS - 2);
+  // top of iteration i: wait until tile i has landed (tiles i+1 .. i+NS-3 may be in flight),
+  // barrier, then issue tile i + NS - 2
+  auto ring_top = [&](int i) {
+    if (i < ntiles) {
+      if (NS == 4 && i + 1 < ntiles) {
+        if (score_wave) wait_vm<5>(); else wait_vm<4>();
+      } else {
+        wait_vm<0>();
+      }
+    }
+    __builtin_amdgcn_s_barrier();
+    if (i + NS - 2 < ntiles) {
+      issue(i + NS - 2);
+      if (i + NS - 1 < ntiles) fetch(i + NS - 1);
+    }
   };
 
-  if (ntiles > 0) { fetch(0); issue(0); }
-  if (ntiles > 1) { fetch(1); issue(1); }
-  if (ntiles > 2) fetch(2);
-  // complete the q loads here and make the values opaque: no wait for them inside the DMA
-  // pipeline below, and no re-loading next to each use
+  if (score_wave) {
+    // the score waves are the critical path of each iteration: their instructions (the S MFMAs
+    // above all) issue ahead of the value waves', which fill the gaps
+    __builtin_amdgcn_s_setprio(1);
+    // complete the q loads here and make the values opaque: no wait for them inside the DMA
+    // pipeline below, and no re-loading next to each use
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qf[kk]));
-
-  f32x4_t acc[DH];  // columns 256*half + 16d + n, heads 4g+i
+    for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qf[kk]));
+    float m_run = kNegInf;  // per head n (same in the four lane groups)
+    float l_run = 0.f;      // this lane's share: entries 4g.., 16+4g.. of every tile
+    for (int i = 0; i <= ntiles; ++i) {
+      ring_top(i);
+      if (i == ntiles) break;
+      const char* sb = smem + (i % NS) * kStage;
+      const i32x4_t cd0 = *reinterpret_cast<const i32x4_t*>(scode + kTile * i + 4 * g);
+      const i32x4_t cd1 = *reinterpret_cast<const i32x4_t*>(scode + kTile * i + 16 + 4 * g);
+      auto ld = [&](int R, int kk) -> u32x4_t {
+        const char* ap;
+        if (kk < 16) {
+          ap = sb + R * kLatStride + 64 * kk + 16 * g;
+        } else {
+          const int c = 4 * (kk - 16) + g;
+          ap = sb + kStageLat + R * 128 + ((c ^ ((R >> 1) & 7)) * 16);
+        }
+        return *reinterpret_cast<const u32x4_t*>(ap);
+      };
+      // S^T for entries 0..15 (sa) and 16..31 (sc), each over 4 accumulators (k-step % 4)
+      f32x4_t sa[4], sc[4];
 #pragma unroll
-  for (int d = 0; d < DH; ++d) acc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf;  // per head n (same in the four lane groups and in both waves)
-  float l_run = 0.f;      // this lane's share: entries 4g.., 16+4g.. of every tile
-
-  const int R0 = 16 * half + n;  // S^T row (entry) read by this lane
-  for (int t = 0; t < ntiles; ++t) {
-    // tile t landed (tile t+1 may still be in flight) and every wave is done with tile t-1
-    if (t + 1 < ntiles) {
-      if (wv < 4) wait_vm<5>(); else wait_vm<4>();
-    } else {
-      wait_vm<0>();
-    }
-    __builtin_amdgcn_s_barrier();
-    // DMAs of tile t+2 (into the stage tile t-1 used) are spread over the S MFMAs below so that
-    // the wave never stalls on a full address queue
-    const bool pf = t + 2 < ntiles;
-    const uint64_t pl = rowaddr(nx_lat);
-
-    const char* sb = smem + (t % kStages) * kStage;
-    const i32x4_t cd0 = *reinterpret_cast<const i32x4_t*>(scode + kTile * t + 4 * g);
-    const i32x4_t cd1 = *reinterpret_cast<const i32x4_t*>(scode + kTile * t + 16 + 4 * g);
-    // S^T for this wave's 16 entries x 16 heads over 4 accumulators (k-steps kk % 4), so that 4
-    // independent MFMA chains are in flight: 12 reads, the first 6 MFMAs, the last 6 reads, the
-    // remaining 12 MFMAs
-    auto ld = [&](int kk) -> u32x4_t {
-      const char* ap;
-      if (kk < 16) {
-        ap = sb + R0 * kLatStride + 64 * kk + 16 * g;
-      } else {
-        const int c = 4 * (kk - 16) + g;
-        ap = sb + kStageLat + R0 * 128 + ((c ^ ((R0 >> 1) & 7)) * 16);
+      for (int c = 0; c < 4; ++c) sa[c] = sc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      {
+        constexpr int KB = 3;  // k-steps per block of reads, one block ahead of the MFMAs
+        u32x4_t a0[KS], a1[KS];
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+          a0[kk] = ld(n, kk);
+          a1[kk] = ld(16 + n, kk);
+        }
+#pragma unroll
+        for (int blk = 0; blk < KS / KB; ++blk) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (blk + 1 < KS / KB) {
+#pragma unroll
+            for (int kk = KB * blk + KB; kk < KB * blk + 2 * KB; ++kk) {
+              a0[kk] = ld(n, kk);
+              a1[kk] = ld(16 + n, kk);
+            }
+          }
+#pragma unroll
+          for (int kk = KB * blk; kk < KB * blk + KB; ++kk) {
+            sa[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0[kk]), as_bf16x8(qf[kk]), sa[kk & 3], 0, 0, 0);
+            sc[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1[kk]), as_bf16x8(qf[kk]), sc[kk & 3], 0, 0, 0);
+          }
+        }
       }
-      return *reinterpret_cast<const u32x4_t*>(ap);
-    };
-    f32x4_t sa[4];
+      const f32x4_t st0 = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+      const f32x4_t st1 = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+      // lane (head n, g): entries 4g+j (z[j]) and 16+4g+j (z[4+j])
+      float z[8];
+      float mx = kNegInf;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sa[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    u32x4_t av[KS];
+      for (int j = 0; j < 4; ++j) {
+        z[j] = cd0[j] != -1 ? st0[j] * scale_log2 : kNegInf;
+        z[4 + j] = cd1[j] != -1 ? st1[j] * scale_log2 : kNegInf;
+        mx = fmaxf(mx, fmaxf(z[j], z[4 + j]));
+      }
+      mx = group_max(mx);
+      // Lazily moved softmax reference: m_run only moves (and the value waves rescale their
+      // accumulators) when a head's tile maximum exceeds it by more than kRefSlack (log2
+      // units), so p <= 2^kRefSlack.
+      const bool grow = mx > m_run + kRefSlack;
+      const bool moved = __ballot(grow) != 0;
+      if (moved) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+        if (g == 0) abuf[i & 1][hb][n] = alpha;
+      }
+      if (lane == 0) fbuf[i & 1][hb] = moved ? 1u : 0u;
+      uint32_t pk[4];
 #pragma unroll
-    for (int kk = 0; kk < 12; ++kk) av[kk] = ld(kk);
-#pragma unroll
-    for (int kk = 0; kk < 6; ++kk) {
-      __builtin_amdgcn_sched_barrier(0);
-      sa[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[kk]), as_bf16x8(qf[kk]), sa[kk & 3], 0, 0, 0);
-      if (pf && kk < 5) issue_step(t + 2, pl, kk);
+      for (int j = 0; j < 4; ++j) {
+        // m_run == -inf only while every entry so far is masked (z == -inf as well)
+        const float e0 = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(z[2 * j] - m_run);
+        const float e1 = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(z[2 * j + 1] - m_run);
+        l_run += e0 + e1;
+        pk[j] = pack_bf16x2(e0, e1);
+      }
+      pbuf[i & 1][hb][lane] = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 12; kk < KS; ++kk) av[kk] = ld(kk);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 6; kk < KS; ++kk)
-      sa[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[kk]), as_bf16x8(qf[kk]), sa[kk & 3], 0, 0, 0);
-    if (pf && t + 3 < ntiles) fetch(t + 3);
-    const f32x4_t st = (sa[0] + sa[1]) + (sa[2] + sa[3]);
-    // swap the S^T blocks with the partner wave
-    sx[wv][lane] = st;
+    // final (m, l) per head for the value waves, and lse / the split's (m, l)
+    const float l_head = group_sum(l_run);
+    if (g == 0) {
+      sml[hb][0][n] = m_run;
+      sml[hb][1][n] = l_head;
+      if (nsplit == 1) {
+        if (lse) lse[(size_t)qi * H + h0 + n] = l_head > 0.f ? (m_run + __log2f(l_head)) * kLn2 : kNegInf;
+      } else {
+        const size_t hrow = ((size_t)row * H + h0 + n) * nsplit + split;
+        part_ml[hrow * 2] = m_run;
+        part_ml[hrow * 2 + 1] = l_head;
+      }
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    const f32x4_t so = sx[wv ^ 4][lane];
-    // lane (head n, g): entries 4g+i (z[i]) and 16+4g+i (z[4+i])
-    float z[8];
-    float mx = kNegInf;
+    return;
+  }
+
+  // ---- value waves: wave 4 + v owns heads of blocks 2*(v&1) and 2*(v&1)+1 (32 heads) and
+  // value columns 256*(v>>1) .. +255, so each pair of transposed V reads feeds two MFMAs ----
+  const int vw = wv - 4;
+  const int hb0 = 2 * (vw & 1), dh = vw >> 1;
+  constexpr int DH = DB / 2;  // 16 column blocks of this wave
+  f32x4_t acc[2][DH];         // [head block hb0 + k][column block 16*dh + d]: heads 4g+j, col n
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float s0 = half ? so[i] : st[i], s1 = half ? st[i] : so[i];
-      z[i] = cd0[i] != -1 ? s0 * scale_log2 : kNegInf;
-      z[4 + i] = cd1[i] != -1 ? s1 * scale_log2 : kNegInf;
-      mx = fmaxf(mx, fmaxf(z[i], z[4 + i]));
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int d = 0; d < DH; ++d) acc[k][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // transposed V reads: entry 4g + n/4 (and 16 rows on), column 256*dh + 16d + 4*(n%4)
+  const uint32_t voff = (4 * g + (n >> 2)) * kLatStride + 512 * dh + 8 * (n & 3);
+  for (int i = 0; i <= ntiles; ++i) {
+    ring_top(i);
+    if (i == 0) continue;
+    const int t = i - 1;
+    const bf16x8_t pa0 = as_bf16x8(pbuf[t & 1][hb0][lane]);
+    const bf16x8_t pa1 = as_bf16x8(pbuf[t & 1][hb0 + 1][lane]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (fbuf[t & 1][hb0 + k] != 0) {
+        float ai[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ai[j] = abuf[t & 1][hb0 + k][4 * g + j];
+#pragma unroll
+        for (int d = 0; d < DH; ++d)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[k][d][j] *= ai[j];
+      }
     }
-    mx = group_max(mx);
-    // Lazily moved softmax reference: m_run only moves (and the accumulators are rescaled) when
-    // a head's tile maximum exceeds it by more than kRefSlack (log2 units), so p <= 2^kRefSlack.
-    const bool grow = mx > m_run + kRefSlack;
-    if (__ballot(grow) != 0) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
-      // accumulator rows are heads 4g+i
-      float ai[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i, 64);
-#pragma unroll
-      for (int d = 0; d < DH; ++d)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[d][i] *= ai[i];
-    }
-    uint32_t pk[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // m_run == -inf only while every entry so far is masked (z == -inf as well)
-      const float e0 = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(z[2 * i] - m_run);
-      const float e1 = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(z[2 * i + 1] - m_run);
-      l_run += e0 + e1;
-      pk[i] = pack_bf16x2(e0, e1);
-    }
-    const bf16x8_t pa = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-    // transposed V reads: entry 4g + n/4 (and 16 rows on), column 256*half + 16d + 4*(n%4)
-    const uint32_t vaddr = (uint32_t)(uintptr_t)(lds_void_t*)(
-        sb + (4 * g + (n >> 2)) * kLatStride + 512 * half + 8 * (n & 3));
+    const uint32_t vaddr = (uint32_t)(uintptr_t)(lds_void_t*)(smem + (t % NS) * kStage) + voff;
 #pragma unroll
     for (int d0 = 0; d0 < DH; d0 += 8) {
       u32x2_t tr[16];
@@ -392,43 +447,50 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         const u32x4_t bw = {tr[2 * d][0], tr[2 * d][1], tr[2 * d + 1][0], tr[2 * d + 1][1]};
-        acc[d0 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(bw), acc[d0 + d], 0, 0, 0);
+        acc[0][d0 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa0, as_bf16x8(bw), acc[0][d0 + d], 0, 0, 0);
+        acc[1][d0 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa1, as_bf16x8(bw), acc[1][d0 + d], 0, 0, 0);
       }
     }
   }
-
-  // ---- epilogue: this wave's 256 columns of its 16 heads ----
-  const float l_head = group_sum(l_run);  // per head n
-  float li[4], mi[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    li[i] = __shfl(l_head, 4 * g + i, 64);
-    mi[i] = __shfl(m_run, 4 * g + i, 64);
-  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();  // the score waves' final (m, l) are in sml
   if (nsplit == 1) {
-    const int c0 = 256 * half + n;
+    // normalise, round to bf16 and stage this wave's 32 x 256 block through the (idle) ring
+    // memory (a region of its own) so that each output row is written with 16-byte stores
+    uint16_t* so = reinterpret_cast<uint16_t*>(smem) + vw * 32 * (256 + 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float inv = li[i] > 0.f ? 1.f / li[i] : 0.f;
-      uint16_t* orow = out + ((size_t)qi * H + h0 + 4 * g + i) * DV + c0;
+    for (int k = 0; k < 2; ++k) {
+      float inv[4];
 #pragma unroll
-      for (int d = 0; d < DH; ++d) orow[16 * d] = f32_to_bf16(acc[d][i] * inv);
+      for (int j = 0; j < 4; ++j) {
+        const float l = sml[hb0 + k][1][4 * g + j];
+        inv[j] = l > 0.f ? 1.f / l : 0.f;
+      }
+#pragma unroll
+      for (int d = 0; d < DH; ++d)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          so[(16 * k + 4 * g + j) * (256 + 8) + 16 * d + n] = f32_to_bf16(acc[k][d][j] * inv[j]);
     }
-    if (half == 0 && g == 0 && lse)
-      lse[(size_t)qi * H + h0 + n] = l_head > 0.f ? (m_run + __log2f(l_head)) * kLn2 : kNegInf;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // 32 rows x 512 bytes: 16 chunks of 16 bytes per lane
+    const int hbase = hg * 64 + hb0 * 16;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int c = lane + 64 * k, r = c >> 5, col = (c & 31) * 8;
+      *reinterpret_cast<u32x4_t*>(out + ((size_t)qi * H + hbase + r) * DV + 256 * dh + col) =
+          *reinterpret_cast<const u32x4_t*>(so + r * (256 + 8) + col);
+    }
   } else {
-    if (half == 0 && g == 0) {
-      const size_t hrow = ((size_t)row * H + h0 + n) * nsplit + split;
-      part_ml[hrow * 2] = m_run;
-      part_ml[hrow * 2 + 1] = l_head;
-    }
     // O partials (fp32, relative to this split's m) in register order:
-    // [row][head group][split][wave][16 column blocks][64 lanes] x 4 heads (4g..4g+3 of column
-    // 16d + n): whole 1 KB stores
+    // [row][head group][split][slot 8][16 column blocks][64 lanes] x 4 heads (4g..4g+3 of column
+    // 16d + n); slot = head block + 4 * (column half). Whole 1 KB stores.
     f32x4_t* po = reinterpret_cast<f32x4_t*>(part_o) +
-                  ((((size_t)row * HG + hg) * nsplit + split) * 8 + wv) * DH * 64 + lane;
+                  (((size_t)row * HG + hg) * nsplit + split) * 8 * 16 * 64 + lane;
 #pragma unroll
-    for (int d = 0; d < DH; ++d) po[d * 64] = acc[d];
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int d = 0; d < DH; ++d) po[((hb0 + k + 4 * dh) * 16 + d) * 64] = acc[k][d];
   }
 }
 
@@ -623,23 +685,37 @@ hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, co
     float* part_ml = ns > 1 ? part_o + (size_t)nrows * s.H * ns * s.D_V : nullptr;
     dim3 grid(ns, s.H / 64, (unsigned)nrows);
     const size_t code_bytes = sizeof(int) * (size_t)per;  // per is a multiple of the tile
-    // the entry-code table is dynamic LDS on top of the static stages: allow up to the 160 KB
-    // a workgroup can hold
+    // the entry-code table is dynamic LDS beside the static ring: a 4-stage ring when it fits
+    // in the 160 KB a workgroup can hold, else 3 stages
     constexpr size_t kLdsMax = 160 * 1024;
-    constexpr size_t kStatic = kStages * kStage + sizeof(f32x4_t) * kAtWaves * 64;
-    if (code_bytes > kLdsMax - kStatic) return hipErrorInvalidValue;
+    constexpr size_t kFixed = sizeof(u32x4_t) * 2 * 4 * 64 + sizeof(float) * 2 * 4 * 16 +
+                              sizeof(uint32_t) * 2 * 4 + sizeof(float) * 4 * 2 * 16;
+    constexpr size_t kStatic4 = 4 * kStage + kFixed, kStatic3 = 3 * kStage + kFixed;
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
-      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_mfma_dma),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsMax - kStatic));
+      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_mfma_dma<4>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsMax - kStatic4));
+      if (attr == hipSuccess)
+        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_mfma_dma<3>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)(kLdsMax - kStatic3));
     });
     if (attr != hipSuccess) return attr;
-    attend_mfma_dma<<<grid, kAtWaves * 64, code_bytes, st>>>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
-        static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H, s.top_k, s.W,
-        scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse, part_o, part_ml,
-        (int)(ns * (s.H / 64) * nrows));
+    const int nitems = (int)(ns * (s.H / 64) * nrows);
+    if (code_bytes <= kLdsMax - kStatic4) {
+      attend_mfma_dma<4><<<grid, kAtWaves * 64, code_bytes, st>>>(
+          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
+          static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H, s.top_k, s.W,
+          scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse, part_o, part_ml, nitems);
+    } else if (code_bytes <= kLdsMax - kStatic3) {
+      attend_mfma_dma<3><<<grid, kAtWaves * 64, code_bytes, st>>>(
+          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
+          static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H, s.top_k, s.W,
+          scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse, part_o, part_ml, nitems);
+    } else {
+      return hipErrorInvalidValue;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns == 1) return e;
     if (between) (void)hipEventRecord(between, st);
