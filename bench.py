@@ -45,6 +45,13 @@ WORKLOAD_TEXT = {
 }
 
 
+def _fused_topk(cfg):
+    """dsa_forward selects the top-k inside the attention kernel (bf16 MFMA shapes, N <= 32768,
+    at most 128 query rows per chunk; cfg describes one chunk)."""
+    return (cfg.dt == "bf16" and cfg.D_K == 576 and cfg.D_V == 512 and cfg.H % 64 == 0
+            and cfg.N <= 32768 and cfg.B * cfg.T <= 128)
+
+
 def _kernel_plan(cfg, nsplit):
     """Kernel names of one dsa_forward (per chunk) in launch order."""
     names = []
@@ -60,8 +67,9 @@ def _kernel_plan(cfg, nsplit):
         names.append("indexer_decode_mfma")
     else:
         names.append("indexer_generic")
-    names.append("topk_radix_row")
     mfma = cfg.dt == "bf16" and cfg.D_K == 576 and cfg.D_V == 512 and cfg.H % 64 == 0
+    if not _fused_topk(cfg):
+        names.append("topk_radix_reg" if cfg.N <= 32768 else "topk_radix_row")
     names.append("attend_mfma_dma" if mfma else "attend_generic")
     if nsplit > 1:
         names.append("attend_combine")
@@ -94,11 +102,16 @@ def _algorithmic(cfg, name):
         keys = B * max(nvis) if T > 1 else pairs
         byt = keys * kI_row + rows * cfg.H_I * (cfg.D_I * esz + 4) + pairs * 4
         return byt, pairs * cfg.H_I * cfg.D_I * 2.0
-    if name == "topk_radix_row":
+    if name.startswith("topk"):
         return pairs * 4 + rows * cfg.top_k * 4, 0.0
     if name.startswith("attend_mfma") or name == "attend_generic":
         ents = sel + win
-        byt = ents * cfg.D_K * esz + rows * cfg.H * cfg.D_K * esz + rows * cfg.top_k * 4
+        # each gathered row must cross HBM once per step: once per query at decode, but rows
+        # shared by the queries of one sequence (prefill) count once
+        rows_kv = min(sel, float(B * N)) + min(win, float(B * (T + cfg.W - 1)) if cfg.W else 0.0)
+        byt = rows_kv * cfg.D_K * esz + rows * cfg.H * cfg.D_K * esz + rows * cfg.top_k * 4
+        if name.startswith("attend_mfma") and _fused_topk(cfg):
+            byt += pairs * 4  # the kernel selects the entries from the scores itself
         return byt, ents * cfg.H * (cfg.D_K + cfg.D_V) * 2.0
     if name == "attend_combine":
         return rows * cfg.H * (cfg.D_V * esz + 4), 0.0

@@ -176,12 +176,19 @@ typedef struct dsa_forward_args {
                             on `stream` right before the i-th kernel this call launches and
                             events[K] after the last one (K kernels), as far as n_events
                             reaches. The kernel order is: [compress], then per query chunk
-                            indexer, top-k, attention[, split combine].                  */
+                            indexer, [top-k,] attention[, split combine]; the top-k is a
+                            kernel of its own unless the attention selects the entries
+                            itself (MFMA shapes, N <= 32768, at most 128 query rows per
+                            chunk: the decode case). */
   int32_t n_events;
 } dsa_forward_args;
 
 /* Fused path: [compress] -> indexer_scores -> topk_select -> sparse_mla_attend on `stream`
- * ([P5] key takeaways: light pre-scoring -> top-k sparse selection -> sparse MLA).
+ * ([P5] key takeaways: light pre-scoring -> top-k sparse selection -> sparse MLA). For bf16
+ * MFMA shapes with N <= 32768 and at most 128 query rows per chunk (decode) the attention
+ * kernel performs the top-k selection itself (same selection as topk_select: ties to the
+ * lowest indices, idx in ascending order); longer chunks run the top-k kernel, since every
+ * workgroup of a row would repeat the selection.
  * When a->scores is NULL, queries are processed in chunks whose scores fit the workspace.
  * ws: dsa_workspace_bytes(d, DSA_OP_FORWARD) bytes. Graph-capturable (no sync, no alloc). */
 dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, size_t ws_bytes,

@@ -266,14 +266,25 @@ dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
                                       (int)a->k_dt, a->q_pos, sc, keep_scores, st))
       return launched(e);
     ev.mark();
-    if (hipError_t e = launch_topk(s, q0, nr, sc, a->q_pos, ix, ws_topk, st)) return launched(e);
-    ev.mark();
     const bool split = attend_splits(s, nr, fmt) > 1;
-    if (hipError_t e = launch_attend(s, q0, nr, fmt, a->q, a->kv, ix,
-                                     d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw,
-                                     a->q_pos, a->softmax_scale, a->out, a->lse, ws_att, st,
-                                     split ? ev.peek() : nullptr))
-      return launched(e);
+    if (attend_fused_ok(s, fmt, nr)) {
+      // top-k inside the attention kernel: idx is written only when the caller wants it
+      if (hipError_t e = launch_attend_fused(s, q0, nr, a->q, a->kv, sc,
+                                             a->idx ? a->idx + (size_t)q0 * d->top_k : nullptr,
+                                             d->W > 0 ? a->kv_raw : nullptr, a->raw_base,
+                                             a->n_raw, a->q_pos, a->softmax_scale, a->out, a->lse,
+                                             ws_att, st, split ? ev.peek() : nullptr))
+        return launched(e);
+    } else {
+      if (hipError_t e = launch_topk(s, q0, nr, sc, a->q_pos, ix, ws_topk, st))
+        return launched(e);
+      ev.mark();
+      if (hipError_t e = launch_attend(s, q0, nr, fmt, a->q, a->kv, ix,
+                                       d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw,
+                                       a->q_pos, a->softmax_scale, a->out, a->lse, ws_att, st,
+                                       split ? ev.peek() : nullptr))
+        return launched(e);
+    }
     if (split) ++ev.next;
     ev.mark();
   }

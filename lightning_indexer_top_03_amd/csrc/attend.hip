@@ -15,6 +15,7 @@
 // attend_generic: any dims, fp32 or bf16; one workgroup per (query, head), scalar fp32.
 #include "common.h"
 #include "launch.h"
+#include "select.h"
 
 #include <mutex>
 
@@ -156,14 +157,18 @@ __device__ __forceinline__ void tr_read_block(u32x2_t* tr, uint32_t vaddr, int d
 #undef DSA_TR_PAIR
 #undef DSA_TR
 
-template <int NS>
+// PER == 0: the entries come from idx. PER > 0 (fused top-k): they come straight from the
+// indexer scores; every workgroup of a row selects the row's top-k (block_threshold /
+// block_ranks of select.h, PER entries per thread, in ascending index order) and keeps its own
+// split's slice; the workgroup of split 0 / head group 0 also writes the row of idx_out.
+template <int NS, int PER>
 __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw, int64_t raw_base,
     int64_t n_raw, const int32_t* __restrict__ q_pos, int T, int N, int H, int top_k, int W,
     float scale_log2, int64_t qi0, int nsplit, int per_split, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int nitems) {
+    int nitems, const float* __restrict__ scores, int m, int32_t* __restrict__ idx_out) {
   constexpr int DK = 576, DV = 512, KS = DK / 32, DB = DV / 16;
   __shared__ __attribute__((aligned(16))) char smem[NS * kStage];
   __shared__ __attribute__((aligned(16))) u32x4_t pbuf[2][4][64];  // P, per head block
@@ -200,40 +205,89 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
   const int ncode = ntiles * kTile;
   const int32_t* __restrict__ idxrow = idx + row * (int64_t)top_k;
 
-  // Prologue: the idx reads of this thread's first two code slots (unconditional, clamped
-  // address) and, on the score waves, the q loads are all issued before the first wait.
-  int raw[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) raw[j] = idxrow[min(e_begin + tid + j * kAtWaves * 64, top_k - 1)];
   // q fragments (score waves): lane (head n, group g) holds q[h0+n][32kk + 8g .. +7]
   u32x4_t qf[KS];
-  if (score_wave) {
-    const uint16_t* qh = q + ((size_t)qi * H + h0 + n) * DK + 8 * g;
+  auto load_q = [&]() {
+    if (score_wave) {
+      const uint16_t* qh = q + ((size_t)qi * H + h0 + n) * DK + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[kk] = *reinterpret_cast<const u32x4_t*>(qh + 32 * kk);
-  }
-  const int p = q_pos[qi];
+      for (int kk = 0; kk < KS; ++kk) qf[kk] = *reinterpret_cast<const u32x4_t*>(qh + 32 * kk);
+    }
+  };
+  // window entry e >= top_k: raw row p - W + 1 + (e - top_k) if held in kv_raw
+  auto window_code = [&](int e, int p) -> int {
+    const int64_t r = (int64_t)p - W + 1 + (e - top_k);
+    if (kv_raw != nullptr && r >= 0 && r >= raw_base && r < raw_base + n_raw)
+      return -(int)(r - raw_base) - 2;
+    return -1;
+  };
+  if constexpr (PER == 0) {
+    // Prologue: the idx reads of this thread's first two code slots (unconditional, clamped
+    // address) and, on the score waves, the q loads are all issued before the first wait.
+    int raw[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    asm volatile("" : "+v"(raw[j]));  // keep the reads above, not sunk into the branches below
-    const int i = tid + j * kAtWaves * 64;
-    const int e = e_begin + i;
-    int code = -1;
-    if (e < e_end) {
-      if (e < top_k) {
-        code = (raw[j] >= 0 && raw[j] < N) ? raw[j] : -1;
-      } else {
-        const int64_t r = (int64_t)p - W + 1 + (e - top_k);
-        if (kv_raw != nullptr && r >= 0 && r >= raw_base && r < raw_base + n_raw)
-          code = -(int)(r - raw_base) - 2;
+    for (int j = 0; j < 2; ++j) raw[j] = idxrow[min(e_begin + tid + j * kAtWaves * 64, top_k - 1)];
+    load_q();
+    const int p = q_pos[qi];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      asm volatile("" : "+v"(raw[j]));  // keep the reads above, not sunk into the branches below
+      const int i = tid + j * kAtWaves * 64;
+      const int e = e_begin + i;
+      int code = -1;
+      if (e < e_end) code = e < top_k ? ((raw[j] >= 0 && raw[j] < N) ? raw[j] : -1) : window_code(e, p);
+      if (i < ncode) scode[i] = code;
+    }
+    for (int i = tid + 2 * kAtWaves * 64; i < ncode; i += kAtWaves * 64) {
+      const int e = e_begin + i;
+      scode[i] = e < e_end ? entry_code(e, idxrow, top_k, N, raw_base, n_raw, p, W, kv_raw != nullptr)
+                           : -1;
+    }
+  } else {
+    // Fused top-k: the row's scores (in flight with the q loads), its selection, this split's
+    // slice of it. The selection's LDS scratch is the ring memory, idle until the first DMA.
+    const int p = q_pos[qi];
+    const int nvis = n_visible(p, m, N);
+    const float* __restrict__ srow = scores + row * (int64_t)N;
+    uint32_t key[PER];
+    int nv = 0;
+    if (nvis > top_k) nv = load_keys<PER>(srow, N, nvis, key);
+    load_q();
+    int32_t* __restrict__ orow =
+        (idx_out != nullptr && split == 0 && hg == 0) ? idx_out + row * (int64_t)top_k : nullptr;
+    // every slot first: window entries, keep-all rows (rank = index), -1 elsewhere; ranks of a
+    // selected row are filled in below (after the selection's first barrier)
+    for (int i = tid; i < ncode; i += kAtWaves * 64) {
+      const int e = e_begin + i;
+      int code = -1;
+      if (e < e_end) code = e >= top_k ? window_code(e, p) : (nvis <= top_k && e < nvis ? e : -1);
+      scode[i] = code;
+    }
+    if (nvis <= top_k) {
+      if (orow)
+        for (int i = tid; i < top_k; i += kAtWaves * 64) orow[i] = i < nvis ? i : -1;
+    } else {
+      SelShared<kAtWaves>& sh = *reinterpret_cast<SelShared<kAtWaves>*>(smem);
+      uint32_t tau, need, cnt_eq;
+      block_threshold<kAtWaves, PER>(key, nv, (uint32_t)top_k, sh, tau, need, cnt_eq, (uint32_t)nvis);
+      uint32_t base, take_eq;
+      block_ranks<kAtWaves, PER>(key, nv, tau, need, cnt_eq, sh, base, take_eq);
+      const int e0 = PER * tid;
+      uint32_t r = base, te = 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if (j < nv) {
+          const bool gt = key[j] > tau;
+          const bool eq = key[j] == tau && te < take_eq;
+          te += key[j] == tau ? 1u : 0u;
+          if (gt || eq) {
+            if ((int)r >= e_begin && (int)r < e_end) scode[r - e_begin] = e0 + j;
+            if (orow) orow[r] = e0 + j;
+            ++r;
+          }
+        }
       }
     }
-    if (i < ncode) scode[i] = code;
-  }
-  for (int i = tid + 2 * kAtWaves * 64; i < ncode; i += kAtWaves * 64) {
-    const int e = e_begin + i;
-    scode[i] = e < e_end ? entry_code(e, idxrow, top_k, N, raw_base, n_raw, p, W, kv_raw != nullptr)
-                         : -1;
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -672,58 +726,103 @@ size_t attend_ws_bytes(const Shape& s, int64_t nrows, int fmt) {
   return (size_t)nrows * s.H * ns * ((size_t)s.D_V + 2) * sizeof(float);
 }
 
+// The MFMA attention for rows qi0 .. qi0+nrows-1 (+ the split merge). scores != nullptr selects
+// the fused top-k variant (entries straight from the indexer scores, idx_out optional).
+static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows, const void* q,
+                                     const void* kv, const int32_t* idx, const float* scores,
+                                     int32_t* idx_out, const void* kv_raw, int64_t raw_base,
+                                     int64_t n_raw, const int32_t* q_pos, float scale, void* out,
+                                     float* lse, void* ws, hipStream_t st, hipEvent_t between) {
+  const int ns = attend_splits(s, nrows, FMT_BF16);
+  const int E = s.top_k + s.W;
+  const int per = ((E + ns - 1) / ns + kTile - 1) / kTile * kTile;
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = ns > 1 ? part_o + (size_t)nrows * s.H * ns * s.D_V : nullptr;
+  dim3 grid(ns, s.H / 64, (unsigned)nrows);
+  const size_t code_bytes = sizeof(int) * (size_t)per;  // per is a multiple of the tile
+  // the entry-code table is dynamic LDS beside the static ring: a 4-stage ring when it fits
+  // in the 160 KB a workgroup can hold, else 3 stages
+  constexpr size_t kLdsMax = 160 * 1024;
+  constexpr size_t kFixed = sizeof(u32x4_t) * 2 * 4 * 64 + sizeof(float) * 2 * 4 * 16 +
+                            sizeof(uint32_t) * 2 * 4 + sizeof(float) * 4 * 2 * 16;
+  constexpr size_t kStatic4 = 4 * kStage + kFixed, kStatic3 = 3 * kStage + kFixed;
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    const void* k4[] = {reinterpret_cast<const void*>(&attend_mfma_dma<4, 0>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 16>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 64>)};
+    const void* k3[] = {reinterpret_cast<const void*>(&attend_mfma_dma<3, 0>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 16>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 64>)};
+    for (const void* f : k4)
+      if (attr == hipSuccess)
+        attr = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)(kLdsMax - kStatic4));
+    for (const void* f : k3)
+      if (attr == hipSuccess)
+        attr = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)(kLdsMax - kStatic3));
+  });
+  if (attr != hipSuccess) return attr;
+  const int nitems = (int)(ns * (s.H / 64) * nrows);
+  const int per_thread = scores == nullptr ? 0 : (s.N <= 16 * kAtWaves * 64 ? 16 : 64);
+  if (scores != nullptr && s.N > 64 * kAtWaves * 64) return hipErrorInvalidValue;
+#define DSA_ATT(NS_, PER_)                                                                      \
+  attend_mfma_dma<NS_, PER_><<<grid, kAtWaves * 64, code_bytes, st>>>(                          \
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,                   \
+      static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H, s.top_k, s.W, \
+      scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse, part_o, part_ml, nitems,   \
+      scores, s.m, idx_out)
+  if (code_bytes <= kLdsMax - kStatic4) {
+    if (per_thread == 0) DSA_ATT(4, 0);
+    else if (per_thread == 16) DSA_ATT(4, 16);
+    else DSA_ATT(4, 64);
+  } else if (code_bytes <= kLdsMax - kStatic3) {
+    if (per_thread == 0) DSA_ATT(3, 0);
+    else if (per_thread == 16) DSA_ATT(3, 16);
+    else DSA_ATT(3, 64);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef DSA_ATT
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ns == 1) return e;
+  if (between) (void)hipEventRecord(between, st);
+  attend_combine<<<dim3(8, s.H / 64, (unsigned)nrows), 256, 0, st>>>(
+      part_o, part_ml, qi0, s.H, ns, static_cast<uint16_t*>(out), lse,
+      (int)(8 * (s.H / 64) * nrows));
+  return hipGetLastError();
+}
+
+// Each of a row's workgroups (splits x head groups) repeats the row's selection in its
+// prologue, which pays only while the separate top-k launch is a large share of the step: a
+// few rows (decode), not a prefill chunk, where it would double the selection work.
+constexpr int64_t kFusedMaxRows = 128;
+
+bool attend_fused_ok(const Shape& s, int fmt, int64_t nrows) {
+  return mfma_ok(s, fmt) && s.N <= 64 * kAtWaves * 64 && nrows <= kFusedMaxRows;
+}
+
+hipError_t launch_attend_fused(const Shape& s, int64_t qi0, int64_t nrows, const void* q,
+                               const void* kv, const float* scores, int32_t* idx_out,
+                               const void* kv_raw, int64_t raw_base, int64_t n_raw,
+                               const int32_t* q_pos, float scale, void* out, float* lse, void* ws,
+                               hipStream_t st, hipEvent_t between) {
+  if (nrows <= 0) return hipSuccess;
+  if (!attend_fused_ok(s, FMT_BF16, nrows)) return hipErrorInvalidValue;
+  return launch_attend_mfma(s, qi0, nrows, q, kv, nullptr, scores, idx_out, kv_raw, raw_base,
+                            n_raw, q_pos, scale, out, lse, ws, st, between);
+}
+
 hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, const void* q,
                          const void* kv, const int32_t* idx, const void* kv_raw, int64_t raw_base,
                          int64_t n_raw, const int32_t* q_pos, float scale, void* out, float* lse,
                          void* ws, hipStream_t st, hipEvent_t between) {
   if (nrows <= 0) return hipSuccess;
-  if (mfma_ok(s, fmt)) {
-    const int ns = attend_splits(s, nrows, fmt);
-    const int E = s.top_k + s.W;
-    const int per = ((E + ns - 1) / ns + kTile - 1) / kTile * kTile;
-    float* part_o = static_cast<float*>(ws);
-    float* part_ml = ns > 1 ? part_o + (size_t)nrows * s.H * ns * s.D_V : nullptr;
-    dim3 grid(ns, s.H / 64, (unsigned)nrows);
-    const size_t code_bytes = sizeof(int) * (size_t)per;  // per is a multiple of the tile
-    // the entry-code table is dynamic LDS beside the static ring: a 4-stage ring when it fits
-    // in the 160 KB a workgroup can hold, else 3 stages
-    constexpr size_t kLdsMax = 160 * 1024;
-    constexpr size_t kFixed = sizeof(u32x4_t) * 2 * 4 * 64 + sizeof(float) * 2 * 4 * 16 +
-                              sizeof(uint32_t) * 2 * 4 + sizeof(float) * 4 * 2 * 16;
-    constexpr size_t kStatic4 = 4 * kStage + kFixed, kStatic3 = 3 * kStage + kFixed;
-    static std::once_flag once;
-    static hipError_t attr = hipSuccess;
-    std::call_once(once, [] {
-      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_mfma_dma<4>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsMax - kStatic4));
-      if (attr == hipSuccess)
-        attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_mfma_dma<3>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)(kLdsMax - kStatic3));
-    });
-    if (attr != hipSuccess) return attr;
-    const int nitems = (int)(ns * (s.H / 64) * nrows);
-    if (code_bytes <= kLdsMax - kStatic4) {
-      attend_mfma_dma<4><<<grid, kAtWaves * 64, code_bytes, st>>>(
-          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
-          static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H, s.top_k, s.W,
-          scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse, part_o, part_ml, nitems);
-    } else if (code_bytes <= kLdsMax - kStatic3) {
-      attend_mfma_dma<3><<<grid, kAtWaves * 64, code_bytes, st>>>(
-          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
-          static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H, s.top_k, s.W,
-          scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse, part_o, part_ml, nitems);
-    } else {
-      return hipErrorInvalidValue;
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || ns == 1) return e;
-    if (between) (void)hipEventRecord(between, st);
-    attend_combine<<<dim3(8, s.H / 64, (unsigned)nrows), 256, 0, st>>>(
-        part_o, part_ml, qi0, s.H, ns, static_cast<uint16_t*>(out), lse,
-        (int)(8 * (s.H / 64) * nrows));
-    return hipGetLastError();
-  }
+  if (mfma_ok(s, fmt))
+    return launch_attend_mfma(s, qi0, nrows, q, kv, idx, nullptr, nullptr, kv_raw, raw_base,
+                              n_raw, q_pos, scale, out, lse, ws, st, between);
   const int E = s.top_k + s.W;
   size_t shm = sizeof(float) * (s.D_K + E + 1) + sizeof(void*) * E + 16;
   dim3 grid(s.H, (unsigned)nrows);

@@ -42,4 +42,15 @@ hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, co
                          int64_t n_raw, const int32_t* q_pos, float scale, void* out, float* lse,
                          void* ws, hipStream_t st, hipEvent_t between = nullptr);
 
+// Fused top-k + attention (dsa_forward): every workgroup of a row selects the row's top-k from
+// the indexer scores itself and attends over its split of it; idx_out (nullable) receives the
+// selection in ascending index order. attend_fused_ok: bf16 MFMA shapes with N <= 32768 and at
+// most 128 query rows per launch.
+bool attend_fused_ok(const Shape& s, int fmt, int64_t nrows);
+hipError_t launch_attend_fused(const Shape& s, int64_t qi0, int64_t nrows, const void* q,
+                               const void* kv, const float* scores, int32_t* idx_out,
+                               const void* kv_raw, int64_t raw_base, int64_t n_raw,
+                               const int32_t* q_pos, float scale, void* out, float* lse, void* ws,
+                               hipStream_t st, hipEvent_t between = nullptr);
+
 }  // namespace dsa

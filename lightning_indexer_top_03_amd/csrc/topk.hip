@@ -13,6 +13,7 @@
 // Rows whose n_vis <= k take every visible entry. Unused slots are -1.
 #include "common.h"
 #include "launch.h"
+#include "select.h"
 
 #include <mutex>
 
@@ -221,67 +222,19 @@ __global__ __launch_bounds__(kTkThreads) void topk_radix_row(
 }
 
 // ------------------------------------------------------------------------------------------
-// topk_radix_reg<PER>: rows of at most 1024*PER visible entries. Thread t owns the contiguous
-// entries PER*t .. PER*t+PER-1 and keeps their order keys in registers for the whole kernel.
-//  * The bits every visible key shares (block AND / OR) are skipped; the rest are resolved 8
-//    bits at a time: each wave counts into its own 256-bin histogram in LDS (no atomics shared
-//    between waves, no clearing barrier), then wave 0 sums the 16 histograms and finds the bin
-//    holding the need-th largest key with one DPP prefix scan over bins in descending order.
-//  * The selection is written in ascending index order by two block prefix scans: one over
-//    each thread's count of keys equal to tau (only when tau is tied beyond what is needed, so
-//    that the lowest-index ones are taken) and one over each thread's count of selected keys.
-//    The output order is therefore deterministic.
+// topk_radix_reg<PER>: rows of at most 1024*PER visible entries, one 1024-thread workgroup per
+// row. Thread t owns the contiguous entries PER*t .. PER*t+PER-1 and keeps their order keys in
+// registers for the whole kernel; the threshold and the ranks come from select.h
+// (block_threshold: 8-bit digits into per-wave 256-bin LDS histograms reduced by one wave with a
+// DPP scan; block_ranks: two block prefix scans). The selection is written in ascending index
+// order, so the output order is deterministic.
 // ------------------------------------------------------------------------------------------
-constexpr int kRgDigit = 8;
-constexpr int kRgBins = 1 << kRgDigit;
-
-// inclusive prefix sum over the 64 lanes of a wave with DPP (row shifts, then row broadcasts)
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return x;
-}
-
-// exclusive prefix sum over the block (1024 threads) of v; also returns the block total.
-// wtot: 16 words of LDS. Ends with a barrier, so wtot can be reused at once.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wtot, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint32_t inc = wave_incl_scan(v);
-  if (lane == 63) wtot[wv] = inc;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-  const u32x4_t* w4 = reinterpret_cast<const u32x4_t*>(wtot);
-#pragma unroll
-  for (int q4 = 0; q4 < kTkWaves / 4; ++q4) {
-    const u32x4_t t4 = w4[q4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      before += 4 * q4 + j < wv ? t4[j] : 0u;
-      tot += t4[j];
-    }
-  }
-  __syncthreads();
-  total = tot;
-  return before + inc - v;
-}
-
-struct __attribute__((aligned(16))) RgShared {
-  uint32_t hist[kTkWaves][kRgBins];
-  uint32_t wtot[kTkWaves];
-  uint32_t red_and[kTkWaves], red_or[kTkWaves];
-  uint32_t bin, above, cnt;
-};
-
 template <int PER>
 __global__ __launch_bounds__(kTkThreads) void topk_radix_reg(
     const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int64_t qi0, int N,
     int m, int k, int32_t* __restrict__ idx) {
-  __shared__ RgShared sh;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ SelShared<kTkWaves> sh;
+  const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int n = n_visible(q_pos[qi0 + row], m, N);
   int32_t* __restrict__ out = idx + row * (int64_t)k;
@@ -290,119 +243,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_radix_reg(
     for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
     return;
   }
-  // this thread's entries: PER*tid + j for j < nv
-  const int e0 = PER * tid;
-  const int nv = max(0, min(PER, n - e0));
   uint32_t key[PER];
-  if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(s) & 15) == 0) {
-#pragma unroll
-    for (int j = 0; j < PER; j += 4) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(s + min(e0 + j, ((n - 1) & ~3)));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) key[j + i] = order_key(v[i]);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) key[j] = order_key(s[min(e0 + j, n - 1)]);
-  }
-  uint32_t kand = 0xffffffffu, kor = 0u;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    if (j < nv) {
-      kand &= key[j];
-      kor |= key[j];
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kand &= __shfl_xor(kand, o, 64);
-    kor |= __shfl_xor(kor, o, 64);
-  }
-  if (lane == 0) {
-    sh.red_and[wv] = kand;
-    sh.red_or[wv] = kor;
-  }
-  __syncthreads();
-  kand = 0xffffffffu;
-  kor = 0u;
-#pragma unroll
-  for (int w = 0; w < kTkWaves; ++w) {
-    kand &= sh.red_and[w];
-    kor |= sh.red_or[w];
-  }
-  const uint32_t diff = kand ^ kor;  // bits that vary across the visible row
-  uint32_t prefix = kand, pmask = 0xffffffffu;
-  uint32_t need = (uint32_t)k, cnt_eq = (uint32_t)n;
-  if (diff != 0) {
-    const int top = 31 - __clz(diff);  // highest varying bit
-    pmask = top == 31 ? 0u : (~0u << (top + 1));
-    prefix = kand & pmask;
-    for (int hi = top; hi >= 0; hi -= kRgDigit) {
-      const int width = hi + 1 < kRgDigit ? hi + 1 : kRgDigit;
-      const int shift = hi + 1 - width;
-      const uint32_t bmask = (1u << width) - 1u;
-      uint32_t* h = sh.hist[wv];
-      // this wave's histogram: cleared and filled by the wave alone (LDS ops of a wave are
-      // performed in order)
-      *reinterpret_cast<u32x4_t*>(&h[4 * lane]) = u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int j = 0; j < PER; ++j)
-        if (j < nv && (key[j] & pmask) == prefix) atomicAdd(&h[(key[j] >> shift) & bmask], 1u);
-      __syncthreads();
-      if (wv == 0) {
-        // lane l: bins 255-4l .. 252-4l, highest first, summed over the 16 wave histograms
-        uint32_t c[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int w = 0; w < kTkWaves; ++w) {
-          const u32x4_t t4 = *reinterpret_cast<const u32x4_t*>(&sh.hist[w][252 - 4 * lane]);
-          c[0] += t4[3];  // bin 255 - 4l
-          c[1] += t4[2];
-          c[2] += t4[1];
-          c[3] += t4[0];  // bin 252 - 4l
-        }
-        const uint32_t local = c[0] + c[1] + c[2] + c[3];
-        const uint32_t inc = wave_incl_scan(local);  // keys in bins >= 252 - 4l
-        const uint32_t excl = inc - local;
-        if (inc >= need && excl < need) {
-          uint32_t a = excl;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (a + c[j] >= need) {
-              sh.bin = (uint32_t)(255 - 4 * lane - j);
-              sh.above = a;
-              sh.cnt = c[j];
-              break;
-            }
-            a += c[j];
-          }
-        }
-      }
-      __syncthreads();
-      const uint32_t bin = sh.bin;
-      prefix |= bin << shift;
-      need -= sh.above;
-      pmask |= bmask << shift;
-      cnt_eq = sh.cnt;
-      __syncthreads();  // before the next pass clears the histograms
-    }
-  }
-  const uint32_t tau = prefix;
-  uint32_t n_gt = 0, n_eq = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    if (j < nv) {
-      n_gt += key[j] > tau ? 1u : 0u;
-      n_eq += key[j] == tau ? 1u : 0u;
-    }
-  }
-  uint32_t tot;
-  // tau-valued keys to take from this thread: the lowest-index ones overall
-  uint32_t take_eq = n_eq;
-  if (cnt_eq != need) {
-    const uint32_t eq_before = block_excl_scan(n_eq, sh.wtot, tot);
-    take_eq = eq_before >= need ? 0u : min(n_eq, need - eq_before);
-  }
-  const uint32_t base = block_excl_scan(n_gt + take_eq, sh.wtot, tot);
+  const int nv = load_keys<PER>(s, N, n, key);
+  uint32_t tau, need, cnt_eq;
+  block_threshold<kTkWaves, PER>(key, nv, (uint32_t)k, sh, tau, need, cnt_eq, (uint32_t)n);
+  uint32_t base, take_eq;
+  block_ranks<kTkWaves, PER>(key, nv, tau, need, cnt_eq, sh, base, take_eq);
+  const int e0 = PER * tid;
   uint32_t r = 0, te = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {

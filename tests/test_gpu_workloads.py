@@ -94,3 +94,58 @@ def test_csa_prefill():
 def test_csa_prefill_sharp_small():
     c = synth.CONFIGS["csa_prefill"].with_(N=8192, T=2048, pos0=32768 - 2048).sharp()
     _run(c, n_sample=12)
+
+
+def _run_fused(c, periodic=0):
+    """dsa_forward on few query rows with N <= 32768, where the attention kernel selects the
+    top-k itself. The selection is checked exactly against the oracle's top-k over the GPU's own
+    fp32 scores (the same decision in the same precision: the set is unique, exact ties go to the
+    lowest index), the row in ascending index order with -1 padding, and attention against the
+    oracle. periodic > 0 repeats the indexer keys with that period, so whole groups of entries
+    tie at the k-th score."""
+    wl = synth.make_workload(c)
+    if periodic:
+        k = wl.k_I()
+        wl._cache["k_I"] = np.ascontiguousarray(np.tile(k[:, :periodic], (1, -(-c.N // periodic), 1))[:, :c.N])
+    dw = DeviceWorkload(wl)
+    f = dw.forward(keep_scores=True, keep_idx=True)
+    log(f"[{c.name}] fused dsa_forward B={c.B} T={c.T} N={c.N} k={c.top_k} m={c.m} W={c.W} "
+        f"periodic={periodic}")
+    f.run()
+    torch.cuda.synchronize()
+    run = oracle.QueryRunner(wl)
+    worst = 0.0
+    for b in range(c.B):
+        for t in range(c.T):
+            what = f"{c.name} b={b} t={t}"
+            sc = to_host(f.scores[b, t])
+            ix = to_host(f.idx[b, t])
+            nv = oracle.n_vis(int(wl.q_pos()[b, t]), c.m, c.N)
+            cnt = min(nv, c.top_k)
+            ref, rcnt = oracle.topk_row(sc[:nv].astype(np.float64), nv, c.top_k)
+            assert rcnt == cnt
+            assert np.array_equal(ix[:cnt], ref[:cnt]), f"{what}: selection differs"
+            assert (ix[cnt:] == -1).all(), f"{what}: padding"
+            if b == 0 or t % 7 == 0:
+                worst = max(worst, check_scores(sc, run.scores(b, t), nv, what=what))
+                out = oracle.decode(to_host(f.out[b, t]))
+                ro, rl = run.attend(b, t, ix)
+                check_attention(out, to_host(f.lse[b, t]), ro, rl, what=what)
+    log(f"[{c.name}] fused selection exact on {c.B * c.T} rows, score rel err {worst:.2e}")
+    del f, dw
+
+
+def test_fused_selection_ragged():
+    # 96 rows at positions 100..2967 of a 3001-entry context: rows up to 2047 keep everything
+    c = synth.CONFIGS["decode"].with_(B=2, T=48, N=3001, pos0=100, pos_stride=61, name="fused")
+    _run_fused(c)
+    _run_fused(c.with_(name="fused_ties", seed=7), periodic=97)
+
+
+def test_fused_selection_csa_window():
+    # CSA blocks (m=4, mxfp4 keys) with a 128-token raw window; N=5003 is not a multiple of 4
+    p0 = 4 * 3000
+    c = synth.CONFIGS["csa_decode"].with_(B=2, T=40, N=5003, pos0=p0, pos_stride=203,
+                                          raw_base=p0 - 127, n_raw=203 * 39 + 128,
+                                          name="fused_csa")
+    _run_fused(c)
