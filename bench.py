@@ -8,9 +8,10 @@ latent rows (value = first 512 columns), bf16 storage, fp32 accumulation.
 
 The K timed steps replay HIP graphs of dsa_forward, cycling over R copies of the inputs so the
 bytes a step touches exceed the 256 MB last-level cache (cold-cache HBM traffic, as in
-multi-layer decode). A second, instrumented pass records HIP events between the kernels of the
-same graph to get each kernel's average duration; the dominant kernel's algorithmic bytes (or
-flops) over that duration give the roofline fraction. The fp64 CPU oracle, timed on this host's
+multi-layer decode). A second, instrumented pass runs the same dsa_forward calls eagerly with
+a pair of HIP events per kernel, stamped by hipExtLaunchKernel with that dispatch's start and
+end, to get each kernel's average duration; the dominant kernel's algorithmic bytes (or flops)
+over that duration give the roofline fraction. The fp64 CPU oracle, timed on this host's
 cores over the queries of one step, is reported beside it as a baseline.
 
 Prints ONE JSON line.
@@ -119,12 +120,17 @@ def _algorithmic(cfg, name):
 
 
 def _src_sha(kernel):
+    """Hash of the sources a kernel is built from (its file and the shared device headers)."""
     files = {"indexer": "indexer.hip", "topk": "topk.hip", "attend": "attend.hip",
              "compress": "compress.hip"}
     for k, f in files.items():
         if kernel.startswith(k):
-            with open(os.path.join(ROOT, "lightning_indexer_top_03_amd", "csrc", f), "rb") as fh:
-                return hashlib.sha1(fh.read()).hexdigest()[:12]
+            h = hashlib.sha1()
+            for name in (f, "common.h", "select.h"):
+                with open(os.path.join(ROOT, "lightning_indexer_top_03_amd", "csrc", name),
+                          "rb") as fh:
+                    h.update(fh.read())
+            return h.hexdigest()[:12]
     return None
 
 
@@ -220,6 +226,9 @@ def main():
                     help="input copies cycled over (0: enough to exceed 2x the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run a plain elementwise copy of 256 MiB (read) + 256 MiB "
+                         "(written) three times, the reference for HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -260,6 +269,16 @@ def main():
     per_chunk = _kernel_plan(cfg.with_(compress=False, B=1, T=chunk_rows), 2 if split else 1)
     kernels = (["compress_mean"] if cfg.compress else []) + per_chunk * n_chunks
 
+    if args.copy_probe:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"# copy probe: torch.neg over {src.numel() * 4} bytes read and written per "
+              "launch, 3 launches", file=sys.stderr, flush=True)
+        del src, dst
+
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
     graphs = []
@@ -293,24 +312,26 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     value = rows / (elapsed / args.steps)
 
-    # ---- instrumented pass: events between the kernels of the same call ----
-    # Eager launches (events recorded inside captured graphs do not time on this stack). Each
-    # instrumented step is queued behind a ~1 ms spin kernel, so the host has enqueued all of
-    # the step's kernels and events before the GPU reaches them: they run back to back, as in
-    # the graph replays, and each event pair brackets exactly one kernel.
+    # ---- instrumented pass: each kernel's own start / end events ----
+    # dsa_forward hands event pair i to the i-th kernel's hipExtLaunchKernel, which stamps them
+    # with that dispatch's start and end on the stream it runs on; nothing is inserted between
+    # the kernels. Eager launches (graphs are captured without events). Each instrumented step
+    # is queued behind a ~1 ms spin kernel, so the host has enqueued all of the step's kernels
+    # before the GPU reaches them: they run back to back, as in the graph replays.
     nk = len(kernels)
     per_kernel = [0.0] * nk
     n_inst = min(args.steps, 200 if rows <= 64 else 10)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)]
     with torch.cuda.stream(stream):
         for f in fwds:
             f.set_events(evs)
+        torch.cuda.synchronize()
         for i in range(n_inst):
             torch.cuda._sleep(2_000_000)
             fwds[i % R].run()
             torch.cuda.synchronize()
             for k in range(nk):
-                per_kernel[k] += evs[k].elapsed_time(evs[k + 1])
+                per_kernel[k] += evs[2 * k].elapsed_time(evs[2 * k + 1])
         for f in fwds:
             f.set_events(None)
     per_kernel = [x / n_inst for x in per_kernel]  # ms per launch

@@ -172,14 +172,16 @@ typedef struct dsa_forward_args {
   float* lse;            /* [B,T,H] or NULL                                               */
   float* scores;         /* [B,T,N] or NULL (then scores live in ws, masked tail unwritten)*/
   int32_t* idx;          /* [B,T,top_k] or NULL (then idx lives in ws)                    */
-  void* const* events;   /* profiling aid, or NULL: hipEvent_t handles; events[i] is recorded
-                            on `stream` right before the i-th kernel this call launches and
-                            events[K] after the last one (K kernels), as far as n_events
-                            reaches. The kernel order is: [compress], then per query chunk
-                            indexer, [top-k,] attention[, split combine]; the top-k is a
-                            kernel of its own unless the attention selects the entries
-                            itself (MFMA shapes, N <= 32768, at most 128 query rows per
-                            chunk: the decode case). */
+  void* const* events;   /* profiling aid, or NULL: timing-enabled hipEvent_t handles;
+                            events[2i] and events[2i+1] receive the start and the end of the
+                            i-th kernel this call launches (hipExtLaunchKernel stamps them with
+                            that dispatch's own times, so nothing is inserted between the
+                            kernels), as far as n_events reaches. The kernel order is:
+                            [compress], then per query chunk indexer (one launch per sequence
+                            segment of the chunk in prefill), [top-k,] attention[, split
+                            combine]; the top-k is a kernel of its own unless the attention
+                            selects the entries itself (MFMA shapes, N <= 32768, at most 128
+                            query rows per chunk: the decode case). */
   int32_t n_events;
 } dsa_forward_args;
 

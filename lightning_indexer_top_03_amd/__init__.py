@@ -227,16 +227,22 @@ class Forward:
         self.device = dev
 
     def set_events(self, events) -> None:
-        """Profiling aid: torch.cuda.Event objects recorded between this call's kernels
-        (events[i] before the i-th kernel, events[K] after the last). None to clear."""
+        """Profiling aid: timing events for this call's kernels (events[2i] and events[2i+1]
+        receive the start and the end of the i-th kernel), as torch.cuda.Event objects or raw
+        hipEvent_t handles (int). None to clear."""
         if not events:
             self._ev = None
             self.args.events, self.args.n_events = None, 0
             return
+        handles = []
         for e in events:
+            if isinstance(e, int):
+                handles.append(e)
+                continue
             if e.cuda_event == 0:  # torch creates the HIP event lazily
                 e.record()
-        self._ev = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+            handles.append(e.cuda_event)
+        self._ev = (ctypes.c_void_p * len(handles))(*handles)
         self.args.events = ctypes.cast(self._ev, ctypes.POINTER(ctypes.c_void_p))
         self.args.n_events = len(events)
 

@@ -15,6 +15,8 @@
 
 using namespace dsa;
 
+thread_local KernelTimer* dsa::g_kernel_timer = nullptr;
+
 namespace {
 
 constexpr int kMaxW = 4096;
@@ -86,16 +88,14 @@ dsa_status check_device() {
 
 inline dsa_status launched(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
 
-// Records the caller's profiling events between the kernels of one dsa_forward call.
-struct EventMarks {
-  void* const* ev;
-  int n, next = 0;
-  hipStream_t st;
-  void mark() {
-    if (ev && next < n) hipEventRecord((hipEvent_t)ev[next], st);
-    ++next;
+// Installs the caller's profiling events for the kernels of one dsa_forward call (launch()
+// stamps pair i with the i-th kernel's start and end).
+struct TimerScope {
+  KernelTimer t;
+  TimerScope(void* const* ev, int n) : t{ev, n, 0} {
+    if (ev != nullptr && n > 0) g_kernel_timer = &t;
   }
-  hipEvent_t peek() const { return (ev && next < n) ? (hipEvent_t)ev[next] : nullptr; }
+  ~TimerScope() { g_kernel_timer = nullptr; }
 };
 
 int64_t forward_chunk_rows(const dsa_dims* d) {
@@ -243,12 +243,10 @@ dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
   const Shape s = to_shape(d);
   const int fmt = a->dt == DSA_BF16 ? FMT_BF16 : FMT_F32;
   if (a->n_events < 0) return DSA_ERR_SHAPE;
-  EventMarks ev{a->events, a->n_events, 0, st};
-  ev.mark();
+  TimerScope timer(a->events, a->n_events);
   if (a->compress) {
     if (hipError_t e = launch_compress(d->B, a->n_raw, d->D_K, d->m, fmt, a->kv_raw, a->kv, st))
       return launched(e);
-    ev.mark();
   }
   char* wsb = static_cast<char*>(ws);
   float* ws_scores = reinterpret_cast<float*>(wsb);
@@ -265,28 +263,22 @@ dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
     if (hipError_t e = launch_indexer(s, q0, nr, a->q_I, (int)a->dt, a->w, a->k_I, a->k_scale,
                                       (int)a->k_dt, a->q_pos, sc, keep_scores, st))
       return launched(e);
-    ev.mark();
-    const bool split = attend_splits(s, nr, fmt) > 1;
     if (attend_fused_ok(s, fmt, nr)) {
       // top-k inside the attention kernel: idx is written only when the caller wants it
       if (hipError_t e = launch_attend_fused(s, q0, nr, a->q, a->kv, sc,
                                              a->idx ? a->idx + (size_t)q0 * d->top_k : nullptr,
                                              d->W > 0 ? a->kv_raw : nullptr, a->raw_base,
                                              a->n_raw, a->q_pos, a->softmax_scale, a->out, a->lse,
-                                             ws_att, st, split ? ev.peek() : nullptr))
+                                             ws_att, st))
         return launched(e);
     } else {
       if (hipError_t e = launch_topk(s, q0, nr, sc, a->q_pos, ix, ws_topk, st))
         return launched(e);
-      ev.mark();
       if (hipError_t e = launch_attend(s, q0, nr, fmt, a->q, a->kv, ix,
                                        d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw,
-                                       a->q_pos, a->softmax_scale, a->out, a->lse, ws_att, st,
-                                       split ? ev.peek() : nullptr))
+                                       a->q_pos, a->softmax_scale, a->out, a->lse, ws_att, st))
         return launched(e);
     }
-    if (split) ++ev.next;
-    ev.mark();
   }
   return DSA_OK;
 }

@@ -732,7 +732,7 @@ static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows,
                                      const void* kv, const int32_t* idx, const float* scores,
                                      int32_t* idx_out, const void* kv_raw, int64_t raw_base,
                                      int64_t n_raw, const int32_t* q_pos, float scale, void* out,
-                                     float* lse, void* ws, hipStream_t st, hipEvent_t between) {
+                                     float* lse, void* ws, hipStream_t st) {
   const int ns = attend_splits(s, nrows, FMT_BF16);
   const int E = s.top_k + s.W;
   const int per = ((E + ns - 1) / ns + kTile - 1) / kTile * kTile;
@@ -768,12 +768,13 @@ static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows,
   const int nitems = (int)(ns * (s.H / 64) * nrows);
   const int per_thread = scores == nullptr ? 0 : (s.N <= 16 * kAtWaves * 64 ? 16 : 64);
   if (scores != nullptr && s.N > 64 * kAtWaves * 64) return hipErrorInvalidValue;
-#define DSA_ATT(NS_, PER_)                                                                      \
-  attend_mfma_dma<NS_, PER_><<<grid, kAtWaves * 64, code_bytes, st>>>(                          \
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,                   \
-      static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H, s.top_k, s.W, \
-      scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse, part_o, part_ml, nitems,   \
-      scores, s.m, idx_out)
+  hipError_t e;
+#define DSA_ATT(NS_, PER_)                                                                       \
+  e = launch(attend_mfma_dma<NS_, PER_>, grid, kAtWaves * 64, code_bytes, st,                    \
+             static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,             \
+             static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H,        \
+             s.top_k, s.W, scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse,       \
+             part_o, part_ml, nitems, scores, s.m, idx_out)
   if (code_bytes <= kLdsMax - kStatic4) {
     if (per_thread == 0) DSA_ATT(4, 0);
     else if (per_thread == 16) DSA_ATT(4, 16);
@@ -786,13 +787,9 @@ static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows,
     return hipErrorInvalidValue;
   }
 #undef DSA_ATT
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
-  if (between) (void)hipEventRecord(between, st);
-  attend_combine<<<dim3(8, s.H / 64, (unsigned)nrows), 256, 0, st>>>(
-      part_o, part_ml, qi0, s.H, ns, static_cast<uint16_t*>(out), lse,
-      (int)(8 * (s.H / 64) * nrows));
-  return hipGetLastError();
+  return launch(attend_combine, dim3(8, s.H / 64, (unsigned)nrows), 256, 0, st, part_o, part_ml,
+                qi0, s.H, ns, static_cast<uint16_t*>(out), lse, (int)(8 * (s.H / 64) * nrows));
 }
 
 // Each of a row's workgroups (splits x head groups) repeats the row's selection in its
@@ -808,35 +805,33 @@ hipError_t launch_attend_fused(const Shape& s, int64_t qi0, int64_t nrows, const
                                const void* kv, const float* scores, int32_t* idx_out,
                                const void* kv_raw, int64_t raw_base, int64_t n_raw,
                                const int32_t* q_pos, float scale, void* out, float* lse, void* ws,
-                               hipStream_t st, hipEvent_t between) {
+                               hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   if (!attend_fused_ok(s, FMT_BF16, nrows)) return hipErrorInvalidValue;
   return launch_attend_mfma(s, qi0, nrows, q, kv, nullptr, scores, idx_out, kv_raw, raw_base,
-                            n_raw, q_pos, scale, out, lse, ws, st, between);
+                            n_raw, q_pos, scale, out, lse, ws, st);
 }
 
 hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, const void* q,
                          const void* kv, const int32_t* idx, const void* kv_raw, int64_t raw_base,
                          int64_t n_raw, const int32_t* q_pos, float scale, void* out, float* lse,
-                         void* ws, hipStream_t st, hipEvent_t between) {
+                         void* ws, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   if (mfma_ok(s, fmt))
     return launch_attend_mfma(s, qi0, nrows, q, kv, idx, nullptr, nullptr, kv_raw, raw_base,
-                              n_raw, q_pos, scale, out, lse, ws, st, between);
+                              n_raw, q_pos, scale, out, lse, ws, st);
   const int E = s.top_k + s.W;
   size_t shm = sizeof(float) * (s.D_K + E + 1) + sizeof(void*) * E + 16;
   dim3 grid(s.H, (unsigned)nrows);
   if (fmt == FMT_BF16)
-    attend_generic<uint16_t><<<grid, 256, shm, st>>>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
-        static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H, s.D_K, s.D_V,
-        s.top_k, s.W, scale, qi0, static_cast<uint16_t*>(out), lse);
-  else
-    attend_generic<float><<<grid, 256, shm, st>>>(
-        static_cast<const float*>(q), static_cast<const float*>(kv), idx,
-        static_cast<const float*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H, s.D_K, s.D_V,
-        s.top_k, s.W, scale, qi0, static_cast<float*>(out), lse);
-  return hipGetLastError();
+    return launch(attend_generic<uint16_t>, grid, 256, shm, st, static_cast<const uint16_t*>(q),
+                  static_cast<const uint16_t*>(kv), idx, static_cast<const uint16_t*>(kv_raw),
+                  raw_base, n_raw, q_pos, s.T, s.N, s.H, s.D_K, s.D_V, s.top_k, s.W, scale, qi0,
+                  static_cast<uint16_t*>(out), lse);
+  return launch(attend_generic<float>, grid, 256, shm, st, static_cast<const float*>(q),
+                static_cast<const float*>(kv), idx, static_cast<const float*>(kv_raw), raw_base,
+                n_raw, q_pos, s.T, s.N, s.H, s.D_K, s.D_V, s.top_k, s.W, scale, qi0,
+                static_cast<float*>(out), lse);
 }
 
 }  // namespace dsa

@@ -66,12 +66,10 @@ hipError_t launch_compress(int B, int64_t n_raw, int D, int m, int fmt, const vo
   const int64_t total = (int64_t)B * nc * (fmt == FMT_BF16 ? D / 8 : D / 4);
   const unsigned blocks = (unsigned)((total + 255) / 256);
   if (fmt == FMT_BF16)
-    compress_mean_bf16<<<blocks, 256, 0, st>>>(static_cast<const uint16_t*>(kv_raw), n_raw, D, m,
-                                               nc, total, static_cast<uint16_t*>(kv_c));
-  else
-    compress_mean_f32<<<blocks, 256, 0, st>>>(static_cast<const float*>(kv_raw), n_raw, D, m, nc,
-                                              total, static_cast<float*>(kv_c));
-  return hipGetLastError();
+    return launch(compress_mean_bf16, blocks, 256, 0, st, static_cast<const uint16_t*>(kv_raw),
+                  n_raw, D, m, nc, total, static_cast<uint16_t*>(kv_c));
+  return launch(compress_mean_f32, blocks, 256, 0, st, static_cast<const float*>(kv_raw), n_raw, D,
+                m, nc, total, static_cast<float*>(kv_c));
 }
 
 }  // namespace dsa

@@ -517,10 +517,10 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
       const int t0 = (int)(q - (int64_t)b * s.T);
       const int nt = (int)(seg_end - q);
       dim3 grid((s.N + kPfKeys - 1) / kPfKeys, (nt + kPfQ - 1) / kPfQ);
-      indexer_prefill_mfma<<<grid, 256, 0, st>>>(
-          static_cast<const uint16_t*>(q_I), w, static_cast<const uint16_t*>(k_I), q_pos, s.T,
-          s.N, s.m, b, t0, nt, scores + (size_t)(q - qi0) * s.N, fm);
-      hipError_t e = hipGetLastError();
+      hipError_t e = launch(indexer_prefill_mfma, grid, 256, 0, st,
+                            static_cast<const uint16_t*>(q_I), w,
+                            static_cast<const uint16_t*>(k_I), q_pos, s.T, s.N, s.m, b, t0, nt,
+                            scores + (size_t)(q - qi0) * s.N, fm);
       if (e != hipSuccess) return e;
       q = seg_end;
     }
@@ -537,16 +537,16 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
     dim3 grid((s.N + keys_per_wg - 1) / keys_per_wg, (unsigned)nrows);
     const uint16_t* qp = static_cast<const uint16_t*>(q_I);
     const uint8_t* kp = static_cast<const uint8_t*>(k_I);
-#define DSA_DEC(F, I)                                                                   \
-  indexer_decode_mfma<F, I><<<grid, 256, 0, st>>>(qp, w, kp, k_scale, q_pos, s.T, s.N, s.m, \
-                                                  qi0, scores, fm)
-#define DSA_DEC_ITERS(F)                \
-  switch (iters) {                      \
-    case 1: DSA_DEC(F, 1); break;       \
-    case 2: DSA_DEC(F, 2); break;       \
-    case 4: DSA_DEC(F, 4); break;       \
-    case 8: DSA_DEC(F, 8); break;       \
-    default: DSA_DEC(F, 16); break;     \
+#define DSA_DEC(F, I)                                                                     \
+  return launch(indexer_decode_mfma<F, I>, grid, 256, 0, st, qp, w, kp, k_scale, q_pos, s.T, \
+                s.N, s.m, qi0, scores, fm)
+#define DSA_DEC_ITERS(F)        \
+  switch (iters) {              \
+    case 1: DSA_DEC(F, 1);      \
+    case 2: DSA_DEC(F, 2);      \
+    case 4: DSA_DEC(F, 4);      \
+    case 8: DSA_DEC(F, 8);      \
+    default: DSA_DEC(F, 16);    \
   }
     if (k_fmt == FMT_BF16) {
       // 8 waves per workgroup, ~2 tiles per wave: 256 workgroups at 16 x 8192 keys
@@ -555,29 +555,26 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
       const int kpw = kDecWaves * 32 * it2;
       dim3 g2((s.N + kpw - 1) / kpw, (unsigned)nrows);
       const uint8_t* kb = static_cast<const uint8_t*>(k_I);
-#define DSA_DMA(I)                                                                            \
-  indexer_decode_dma<I><<<g2, kDecWaves * 64, 0, st>>>(qp, w, kb, q_pos, s.T, s.N, s.m, qi0,  \
-                                                       scores, fm)
+#define DSA_DMA(I)                                                                          \
+  return launch(indexer_decode_dma<I>, g2, kDecWaves * 64, 0, st, qp, w, kb, q_pos, s.T, s.N, \
+                s.m, qi0, scores, fm)
       switch (it2) {
-        case 1: DSA_DMA(1); break;
-        case 2: DSA_DMA(2); break;
-        case 4: DSA_DMA(4); break;
-        case 8: DSA_DMA(8); break;
-        default: DSA_DMA(16); break;
+        case 1: DSA_DMA(1);
+        case 2: DSA_DMA(2);
+        case 4: DSA_DMA(4);
+        case 8: DSA_DMA(8);
+        default: DSA_DMA(16);
       }
 #undef DSA_DMA
-    } else {
-      DSA_DEC_ITERS(FMT_MXFP4)
     }
+    DSA_DEC_ITERS(FMT_MXFP4)
 #undef DSA_DEC_ITERS
 #undef DSA_DEC
-    return hipGetLastError();
   }
   dim3 grid((s.N + 255) / 256, (unsigned)nrows);
   size_t shm = sizeof(float) * ((size_t)s.H_I * s.D_I + s.H_I);
-  indexer_generic<<<grid, 256, shm, st>>>(q_I, q_fmt, w, k_I, k_scale, k_fmt, q_pos, s.T, s.N, s.m,
-                                          s.H_I, s.D_I, qi0, scores, fm);
-  return hipGetLastError();
+  return launch(indexer_generic, grid, 256, shm, st, q_I, q_fmt, w, k_I, k_scale, k_fmt, q_pos, s.T,
+                s.N, s.m, s.H_I, s.D_I, qi0, scores, fm);
 }
 
 }  // namespace dsa

@@ -1,11 +1,49 @@
 // launch.h - host-side launch interface between the C ABI (api.cpp) and the kernel files.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+
 namespace dsa {
+
+// Per-kernel timing for a caller's profiling events. While a KernelTimer is installed on the
+// calling thread, every launch() takes the next two events of its list and passes them to
+// hipExtLaunchKernel, which stamps them with that dispatch's own start and end times: no
+// marker packet sits between the kernels, so they run as in an untimed call.
+struct KernelTimer {
+  void* const* ev;
+  int n, next;
+};
+extern thread_local KernelTimer* g_kernel_timer;
+
+// k<<<grid, block, shm, st>>>(a...), timed when a KernelTimer is installed.
+template <typename... P, typename... A>
+inline hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, size_t shm, hipStream_t st,
+                         A... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  if (KernelTimer* t = g_kernel_timer) {
+    const int i = t->next;
+    t->next += 2;
+    hipEvent_t e0 = i < t->n ? static_cast<hipEvent_t>(t->ev[i]) : nullptr;
+    hipEvent_t e1 = i + 1 < t->n ? static_cast<hipEvent_t>(t->ev[i + 1]) : nullptr;
+    if (e0 != nullptr || e1 != nullptr) {
+      std::tuple<P...> v{static_cast<P>(a)...};
+      void* args[sizeof...(P) + 1];
+      std::apply([&args](auto&... x) {
+        int j = 0;
+        ((args[j++] = static_cast<void*>(&x)), ...);
+      }, v);
+      return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, shm, st, e0,
+                                e1, 0);
+    }
+  }
+  k<<<grid, block, shm, st>>>(static_cast<P>(a)...);
+  return hipGetLastError();
+}
 
 enum Fmt { FMT_F32 = 0, FMT_BF16 = 1, FMT_MXFP4 = 2 };
 
@@ -40,7 +78,7 @@ size_t attend_ws_bytes(const Shape& s, int64_t nrows, int fmt);
 hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, const void* q,
                          const void* kv, const int32_t* idx, const void* kv_raw, int64_t raw_base,
                          int64_t n_raw, const int32_t* q_pos, float scale, void* out, float* lse,
-                         void* ws, hipStream_t st, hipEvent_t between = nullptr);
+                         void* ws, hipStream_t st);
 
 // Fused top-k + attention (dsa_forward): every workgroup of a row selects the row's top-k from
 // the indexer scores itself and attends over its split of it; idx_out (nullable) receives the
@@ -51,6 +89,6 @@ hipError_t launch_attend_fused(const Shape& s, int64_t qi0, int64_t nrows, const
                                const void* kv, const float* scores, int32_t* idx_out,
                                const void* kv_raw, int64_t raw_base, int64_t n_raw,
                                const int32_t* q_pos, float scale, void* out, float* lse, void* ws,
-                               hipStream_t st, hipEvent_t between = nullptr);
+                               hipStream_t st);
 
 }  // namespace dsa

@@ -271,16 +271,17 @@ hipError_t launch_topk(const Shape& s, int64_t qi0, int64_t nrows, const float* 
   if (nrows <= 0) return hipSuccess;
   // rows hold at most N visible entries
   const dim3 grid((unsigned)nrows);
-  if (s.N <= 8 * kTkThreads) {
-    topk_radix_reg<8><<<grid, kTkThreads, 0, st>>>(scores, q_pos, qi0, s.N, s.m, s.top_k, idx);
-  } else if (s.N <= 16 * kTkThreads) {
-    topk_radix_reg<16><<<grid, kTkThreads, 0, st>>>(scores, q_pos, qi0, s.N, s.m, s.top_k, idx);
-  } else if (s.N <= kLdsMaxN) {
-    topk_radix_reg<32><<<grid, kTkThreads, 0, st>>>(scores, q_pos, qi0, s.N, s.m, s.top_k, idx);
-  } else {
-    topk_radix_row<false><<<grid, kTkThreads, 0, st>>>(scores, q_pos, qi0, s.N, s.m, s.top_k, idx);
-  }
-  return hipGetLastError();
+  if (s.N <= 8 * kTkThreads)
+    return launch(topk_radix_reg<8>, grid, kTkThreads, 0, st, scores, q_pos, qi0, s.N, s.m,
+                  s.top_k, idx);
+  if (s.N <= 16 * kTkThreads)
+    return launch(topk_radix_reg<16>, grid, kTkThreads, 0, st, scores, q_pos, qi0, s.N, s.m,
+                  s.top_k, idx);
+  if (s.N <= kLdsMaxN)
+    return launch(topk_radix_reg<32>, grid, kTkThreads, 0, st, scores, q_pos, qi0, s.N, s.m,
+                  s.top_k, idx);
+  return launch(topk_radix_row<false>, grid, kTkThreads, 0, st, scores, q_pos, qi0, s.N, s.m,
+                s.top_k, idx);
 }
 
 }  // namespace dsa
