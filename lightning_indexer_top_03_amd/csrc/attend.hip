@@ -157,6 +157,20 @@ __device__ __forceinline__ void tr_read_block(u32x2_t* tr, uint32_t vaddr, int d
 #undef DSA_TR_PAIR
 #undef DSA_TR
 
+// max over the 16 lanes of a DPP row (lane groups of 16)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f32<0xb1>(x));   // quad_perm 1,0,3,2
+  x = fmaxf(x, dpp_f32<0x4e>(x));   // quad_perm 2,3,0,1
+  x = fmaxf(x, dpp_f32<0x141>(x));  // row_half_mirror: the other quad of the half row
+  x = fmaxf(x, dpp_f32<0x140>(x));  // row_mirror: the other half row
+  return x;
+}
+
 // PER == 0: the entries come from idx. PER > 0 (fused top-k): they come straight from the
 // indexer scores; every workgroup of a row selects the row's top-k (block_threshold /
 // block_ranks of select.h, PER entries per thread, in ascending index order) and keeps its own
@@ -167,7 +181,7 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw, int64_t raw_base,
     int64_t n_raw, const int32_t* __restrict__ q_pos, int T, int N, int H, int top_k, int W,
     float scale_log2, int64_t qi0, int nsplit, int per_split, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml,
+    float* __restrict__ lse, f16x4_t* __restrict__ part_o, float* __restrict__ part_ml,
     int nitems, const float* __restrict__ scores, int m, int32_t* __restrict__ idx_out) {
   constexpr int DK = 576, DV = 512, KS = DK / 32, DB = DV / 16;
   __shared__ __attribute__((aligned(16))) char smem[NS * kStage];
@@ -454,8 +468,8 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
         if (lse) lse[(size_t)qi * H + h0 + n] = l_head > 0.f ? (m_run + __log2f(l_head)) * kLn2 : kNegInf;
       } else {
         const size_t hrow = ((size_t)row * H + h0 + n) * nsplit + split;
-        part_ml[hrow * 2] = m_run;
-        part_ml[hrow * 2 + 1] = l_head;
+        part_ml[hrow * 4] = m_run;
+        part_ml[hrow * 4 + 1] = l_head;
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -536,26 +550,45 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
           *reinterpret_cast<const u32x4_t*>(so + r * (256 + 8) + col);
     }
   } else {
-    // O partials (fp32, relative to this split's m) in register order:
-    // [row][head group][split][slot 8][16 column blocks][64 lanes] x 4 heads (4g..4g+3 of column
-    // 16d + n); slot = head block + 4 * (column half). Whole 1 KB stores.
-    f32x4_t* po = reinterpret_cast<f32x4_t*>(part_o) +
-                  (((size_t)row * HG + hg) * nsplit + split) * 8 * 16 * 64 + lane;
+    // O partials (relative to this split's m) as fp16, each head's 256 columns divided by their
+    // largest magnitude c (so every value lies in [-1, 1]; c goes beside the split's (m, l)), in
+    // register order: [row][head group][split][slot 8][16 column blocks][64 lanes] x 4 heads
+    // (4g..4g+3 of column 16d + n); slot = head block + 4 * (column half). 512-byte stores.
+    f16x4_t* po = part_o + (((size_t)row * HG + hg) * nsplit + split) * 8 * 16 * 64 + lane;
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < 2; ++k) {
+      float c[4] = {0.f, 0.f, 0.f, 0.f}, inv[4];
 #pragma unroll
-      for (int d = 0; d < DH; ++d) po[((hb0 + k + 4 * dh) * 16 + d) * 64] = acc[k][d];
+      for (int d = 0; d < DH; ++d)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[j] = fmaxf(c[j], fabsf(acc[k][d][j]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = row16_max(c[j]);  // over the 16 columns n of the lane group
+        inv[j] = c[j] > 0.f ? 1.f / c[j] : 0.f;
+      }
+#pragma unroll
+      for (int d = 0; d < DH; ++d) {
+        const f32x4_t a = acc[k][d] * f32x4_t{inv[0], inv[1], inv[2], inv[3]};
+        po[((hb0 + k + 4 * dh) * 16 + d) * 64] = __builtin_convertvector(a, f16x4_t);
+      }
+      if (n < 4) {
+        const float cn = n == 0 ? c[0] : n == 1 ? c[1] : n == 2 ? c[2] : c[3];
+        const size_t hrow = ((size_t)row * H + hg * 64 + (hb0 + k) * 16 + 4 * g + n) * nsplit + split;
+        part_ml[hrow * 4 + 2 + dh] = cn;
+      }
+    }
   }
 }
 
 // Merge split partials: out = sum_s w_s O_s, w_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s,
-// M = max_s m_s. One workgroup per (wave slot, head group, row): 16 heads x 256 columns, the
-// block written by one wave of attend_mfma_dma per split. Partials are read as whole 1 KB rows
-// of f32x4; the bf16 result goes through LDS so that each row of the output is written with
-// 16-byte stores.
+// M = max_s m_s, with O_s = c_s x (its fp16 partial). One workgroup per (wave slot, head group,
+// row): 16 heads x 256 columns, the block written by one wave of attend_mfma_dma per split.
+// Partials are read as whole 512-byte rows of f16x4; the bf16 result goes through LDS so that
+// each row of the output is written with 16-byte stores.
 constexpr int kMaxSplits = 8;
 __global__ __launch_bounds__(256) void attend_combine(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, int64_t qi0, int H,
+    const f16x4_t* __restrict__ part_o, const float* __restrict__ part_ml, int64_t qi0, int H,
     int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse, int nitems) {
   constexpr int DV = 512;
   __shared__ float wsc[kMaxSplits][16];
@@ -570,23 +603,23 @@ __global__ __launch_bounds__(256) void attend_combine(
   const int lane = tid & 63, g = lane >> 4, n = lane & 15;
   // every load is issued before the first use: partial O blocks for all splits (predicated on
   // nsplit, a runtime value <= kMaxSplits) and the (m, l) pairs, one per thread
-  const f32x4_t* base = reinterpret_cast<const f32x4_t*>(part_o) +
-                        (((size_t)row * HG + hg) * nsplit * 8 + ws) * 16 * 64;
-  f32x4_t v[4][kMaxSplits];
+  const f16x4_t* base = part_o + (((size_t)row * HG + hg) * nsplit * 8 + ws) * 16 * 64;
+  f16x4_t v[4][kMaxSplits];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int d = (tid >> 6) + 4 * k;
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s)
-      v[k][s] = s < nsplit ? base[(size_t)s * 8 * 16 * 64 + d * 64 + lane] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      v[k][s] = s < nsplit ? base[(size_t)s * 8 * 16 * 64 + d * 64 + lane] : f16x4_t{0, 0, 0, 0};
   }
-  float ml_m = kNegInf, ml_l = 0.f;
+  float ml_m = kNegInf, ml_l = 0.f, ml_c = 0.f;
   {
     const int hh = tid >> 3, s = tid & 7;  // 16 heads x 8 splits = threads 0..127
     if (tid < 128 && s < nsplit) {
       const size_t hrow = ((size_t)row * H + h0 + hh) * nsplit + s;
-      ml_m = part_ml[hrow * 2];
-      ml_l = part_ml[hrow * 2 + 1];
+      ml_m = part_ml[hrow * 4];
+      ml_l = part_ml[hrow * 4 + 1];
+      ml_c = part_ml[hrow * 4 + 2 + (ws >> 2)];  // scale of this column half
     }
   }
   // per head: M = max_s m_s, L = sum_s 2^(m_s - M) l_s, over the 8 lanes of each head
@@ -600,7 +633,7 @@ __global__ __launch_bounds__(256) void attend_combine(
   for (int o = 1; o < 8; o <<= 1) L += __shfl_xor(L, o, 64);
   if (tid < 128) {
     const int hh = tid >> 3, s = tid & 7;
-    wsc[s][hh] = L > 0.f ? wm / L : 0.f;
+    wsc[s][hh] = L > 0.f ? wm / L * ml_c : 0.f;
     if (s == 0 && lse) lse[(size_t)qi * H + h0 + hh] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
   }
   __syncthreads();
@@ -612,7 +645,7 @@ __global__ __launch_bounds__(256) void attend_combine(
     for (int s = 0; s < kMaxSplits; ++s) {
       if (s < nsplit) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] += wsc[s][4 * g + i] * v[k][s][i];
+        for (int i = 0; i < 4; ++i) a[i] += wsc[s][4 * g + i] * (float)v[k][s][i];
       }
     }
 #pragma unroll
@@ -722,8 +755,8 @@ int attend_splits(const Shape& s, int64_t nrows, int fmt) {
 size_t attend_ws_bytes(const Shape& s, int64_t nrows, int fmt) {
   const int ns = attend_splits(s, nrows, fmt);
   if (ns <= 1) return 0;
-  // fp32 O partials, then (m, l) pairs
-  return (size_t)nrows * s.H * ns * ((size_t)s.D_V + 2) * sizeof(float);
+  // fp16 O partials, then (m, l, c_0, c_1) per split
+  return (size_t)nrows * s.H * ns * ((size_t)s.D_V * 2 + 4 * sizeof(float));
 }
 
 // The MFMA attention for rows qi0 .. qi0+nrows-1 (+ the split merge). scores != nullptr selects
@@ -736,8 +769,10 @@ static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows,
   const int ns = attend_splits(s, nrows, FMT_BF16);
   const int E = s.top_k + s.W;
   const int per = ((E + ns - 1) / ns + kTile - 1) / kTile * kTile;
-  float* part_o = static_cast<float*>(ws);
-  float* part_ml = ns > 1 ? part_o + (size_t)nrows * s.H * ns * s.D_V : nullptr;
+  f16x4_t* part_o = static_cast<f16x4_t*>(ws);
+  float* part_ml = ns > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                                     (size_t)nrows * s.H * ns * s.D_V * 2)
+                          : nullptr;
   dim3 grid(ns, s.H / 64, (unsigned)nrows);
   const size_t code_bytes = sizeof(int) * (size_t)per;  // per is a multiple of the tile
   // the entry-code table is dynamic LDS beside the static ring: a 4-stage ring when it fits
