@@ -284,20 +284,18 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
       SelShared<kAtWaves>& sh = *reinterpret_cast<SelShared<kAtWaves>*>(smem);
       uint32_t tau, need, cnt_eq;
       block_threshold<kAtWaves, PER>(key, nv, (uint32_t)top_k, sh, tau, need, cnt_eq, (uint32_t)nvis);
-      uint32_t base, take_eq;
-      block_ranks<kAtWaves, PER>(key, nv, tau, need, cnt_eq, sh, base, take_eq);
+      uint32_t base, take_eq, nsel;
+      block_ranks<kAtWaves, PER>(key, nv, tau, need, sh, base, take_eq, nsel);
       const int e0 = PER * tid;
-      uint32_t r = base, te = 0;
+      // only threads whose selected entries reach this split's slice (or that write idx_out)
+      if (orow != nullptr || ((int)base < e_end && (int)(base + nsel) > e_begin)) {
+        const auto sel = select_mask<PER>(key, nv, tau, take_eq);
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if (j < nv) {
-          const bool gt = key[j] > tau;
-          const bool eq = key[j] == tau && te < take_eq;
-          te += key[j] == tau ? 1u : 0u;
-          if (gt || eq) {
-            if ((int)r >= e_begin && (int)r < e_end) scode[r - e_begin] = e0 + j;
+        for (int j = 0; j < PER; ++j) {
+          if ((sel >> j) & 1) {
+            const int r = (int)(base + sel_rank(sel, j));
+            if (r >= e_begin && r < e_end) scode[r - e_begin] = e0 + j;
             if (orow) orow[r] = e0 + j;
-            ++r;
           }
         }
       }

@@ -225,9 +225,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_radix_row(
 // topk_radix_reg<PER>: rows of at most 1024*PER visible entries, one 1024-thread workgroup per
 // row. Thread t owns the contiguous entries PER*t .. PER*t+PER-1 and keeps their order keys in
 // registers for the whole kernel; the threshold and the ranks come from select.h
-// (block_threshold: 8-bit digits into per-wave 256-bin LDS histograms reduced by one wave with a
-// DPP scan; block_ranks: two block prefix scans). The selection is written in ascending index
-// order, so the output order is deterministic.
+// (block_threshold: 8-bit digits into a shared LDS histogram, one barrier per pass, small
+// boundary bins ranked directly; block_ranks: one block prefix scan). The selection is written
+// in ascending index order, so the output order is deterministic.
 // ------------------------------------------------------------------------------------------
 template <int PER>
 __global__ __launch_bounds__(kTkThreads) void topk_radix_reg(
@@ -247,19 +247,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_radix_reg(
   const int nv = load_keys<PER>(s, N, n, key);
   uint32_t tau, need, cnt_eq;
   block_threshold<kTkWaves, PER>(key, nv, (uint32_t)k, sh, tau, need, cnt_eq, (uint32_t)n);
-  uint32_t base, take_eq;
-  block_ranks<kTkWaves, PER>(key, nv, tau, need, cnt_eq, sh, base, take_eq);
+  uint32_t base, take_eq, nsel;
+  block_ranks<kTkWaves, PER>(key, nv, tau, need, sh, base, take_eq, nsel);
   const int e0 = PER * tid;
-  uint32_t r = 0, te = 0;
+  const auto sel = select_mask<PER>(key, nv, tau, take_eq);
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    if (j < nv) {
-      const bool gt = key[j] > tau;
-      const bool eq = key[j] == tau && te < take_eq;
-      te += key[j] == tau ? 1u : 0u;
-      if (gt || eq) out[base + r++] = e0 + j;
-    }
-  }
+  for (int j = 0; j < PER; ++j)
+    if ((sel >> j) & 1) out[base + sel_rank(sel, j)] = e0 + j;
 }
 
 }  // namespace
