@@ -20,11 +20,15 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
     "-Wno-unused-command-line-argument",
 ]
+# Per-file additions. The indexer's MFMA accumulators feed a VALU epilogue (ReLU, head weights)
+# right away: in VGPR form there is no v_accvgpr_read per value, and the kernels need fewer
+# registers (more waves per SIMD to overlap the epilogue with other waves' MFMAs).
+FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, obj_dir: str) -> str:
     obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
