@@ -335,15 +335,19 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_dma(
 }
 
 // ------------------------------------------------------------------------------------------
-// Prefill-shaped kernel (bf16). H_I = 64, D_I = 128. Workgroup = 256 keys x kPfQ queries of one
-// sequence. Wave wv holds keys kbase + 64*wv + 32*kb + n (kb = 0, 1) as B operands in registers
-// for the whole tile; the queries' q_I (64 x 128, 16 KB) and w (64) stream through a 3-stage LDS
-// ring by DMA, two queries ahead of the MFMAs (row hr keeps its 16-byte chunk c in slot
-// c ^ (hr % 16): the A-operand reads are conflict-free). One barrier per query; the DMA waits
-// are explicit, so the barrier never drains the queries in flight.
+// Prefill-shaped kernel (bf16). H_I = 64, D_I = 128. Workgroup = kPfQ queries of one sequence x
+// the key blocks (256 keys) blockIdx.x, blockIdx.x + gridDim.x, ... below the queries' visible
+// range: a grid of every (key block, query block) pair would be mostly blocks past the causal
+// edge, and dispatching those alone costs more than a tenth of the kernel. Per key block, wave
+// wv holds keys kbase + 64*wv + 32*kb + n (kb = 0, 1) as B operands in registers; the queries'
+// q_I (64 x 128, 16 KB) and w (64) stream through a 3-stage LDS ring by DMA, two queries ahead
+// of the MFMAs (row hr keeps its 16-byte chunk c in slot c ^ (hr % 16): the A-operand reads are
+// conflict-free). One barrier per query; the DMA waits are explicit, so the barrier never
+// drains the queries in flight.
 // ------------------------------------------------------------------------------------------
 constexpr int kPfKeys = 256;
 constexpr int kPfQ = 32;
+constexpr int kPfKeyGroups = 16;  // workgroups per query block
 
 __global__ __launch_bounds__(256) void indexer_prefill_mfma(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
@@ -357,7 +361,6 @@ __global__ __launch_bounds__(256) void indexer_prefill_mfma(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
-  const int kbase = blockIdx.x * kPfKeys;
   const int r0 = blockIdx.y * kPfQ;  // first row (relative to t0) of this tile
   const int nrows = min(kPfQ, nt - r0);
   const int64_t qi0 = (int64_t)b * T + t0 + r0;
@@ -371,102 +374,108 @@ __global__ __launch_bounds__(256) void indexer_prefill_mfma(
   }
   __syncthreads();
   const int maxnv = smax;
-  if (kbase >= maxnv) {
-    if (fill_masked)
-      for (int r = 0; r < nrows; ++r)
-        for (int s = kbase + tid; s < min(kbase + kPfKeys, N); s += 256)
-          scores[(size_t)(r0 + r) * N + s] = kNegInf;
-    return;
-  }
-
-  // this wave's keys as B operands: kf[0..1][kk]
   const size_t base_row = (size_t)b * N;
-  u32x4_t kf[2][8];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    int s = min(kbase + 64 * wv + 32 * kb + n, N - 1);
-    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(kI + (base_row + s) * 128 + 64 * h);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) kf[kb][kk] = p[kk];
-  }
-
-  // DMA of query r into stage buf: wave wv moves q_I rows 16*wv .. 16*wv+15 (four 1 KB
-  // instructions); wave 0 also moves w (16 lanes x 16 B). Wave 0 issues 5 instructions per
-  // query, the others 4.
   const uint32_t qlds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)&sq[0][0]);
   const uint32_t wlds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)&sw[0][0]);
-  auto stage = [&](int r, int buf) {
-    const char* src = reinterpret_cast<const char*>(qI + (size_t)(qi0 + r) * (64 * 128));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int hr = 16 * wv + 4 * j + (lane >> 4), c = lane & 15;
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(src + hr * 256 + 16 * (c ^ (hr & 15))),
-          (lds_void_t*)(uintptr_t)(qlds + buf * (64 * 256) + (16 * wv + 4 * j) * 256), 16, 0, 0);
+  for (int kblk = blockIdx.x; kblk * kPfKeys < N; kblk += gridDim.x) {
+    const int kbase = kblk * kPfKeys;
+    if (kbase >= maxnv) {
+      if (fill_masked)
+        for (int r = 0; r < nrows; ++r)
+          for (int s = kbase + tid; s < min(kbase + kPfKeys, N); s += 256)
+            scores[(size_t)(r0 + r) * N + s] = kNegInf;
+      continue;
     }
-    if (wv == 0 && lane < 16)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(w + (size_t)(qi0 + r) * 64 + 4 * lane),
-          (lds_void_t*)(uintptr_t)(wlds + buf * 256), 16, 0, 0);
-  };
-  stage(0, 0);
-  if (nrows > 1) stage(1, 1);
 
-  for (int r = 0; r < nrows; ++r) {
-    const int buf = r % 3;
-    // query r landed (query r+1's DMAs may still be in flight), then every wave's share is
-    // visible after the barrier; stage (r+2)%3 was last read in iteration r-1
-    if (r + 1 < nrows) {
-      if (wv == 0) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // this wave's keys as B operands: kf[0..1][kk]
+    u32x4_t kf[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      int s = min(kbase + 64 * wv + 32 * kb + n, N - 1);
+      const u32x4_t* p = reinterpret_cast<const u32x4_t*>(kI + (base_row + s) * 128 + 64 * h);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) kf[kb][kk] = p[kk];
     }
+
+    // DMA of query r into stage buf: wave wv moves q_I rows 16*wv .. 16*wv+15 (four 1 KB
+    // instructions); wave 0 also moves w (16 lanes x 16 B). Wave 0 issues 5 instructions per
+    // query, the others 4.
+    auto stage = [&](int r, int buf) {
+      const char* src = reinterpret_cast<const char*>(qI + (size_t)(qi0 + r) * (64 * 128));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int hr = 16 * wv + 4 * j + (lane >> 4), c = lane & 15;
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(src + hr * 256 + 16 * (c ^ (hr & 15))),
+            (lds_void_t*)(uintptr_t)(qlds + buf * (64 * 256) + (16 * wv + 4 * j) * 256), 16, 0, 0);
+      }
+      if (wv == 0 && lane < 16)
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(w + (size_t)(qi0 + r) * 64 + 4 * lane),
+            (lds_void_t*)(uintptr_t)(wlds + buf * 256), 16, 0, 0);
+    };
+    stage(0, 0);
+    if (nrows > 1) stage(1, 1);
+
+    for (int r = 0; r < nrows; ++r) {
+      const int buf = r % 3;
+      // query r landed (query r+1's DMAs may still be in flight), then every wave's share is
+      // visible after the barrier; stage (r+2)%3 was last read in iteration r-1
+      if (r + 1 < nrows) {
+        if (wv == 0) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      if (r + 2 < nrows) stage(r + 2, (r + 2) % 3);
+      const int nv = snv[r];
+      float* srow = scores + (size_t)(r0 + r) * N;
+      if (kbase < nv) {
+        const char* qb = &sq[buf][0];
+        u32x4_t a[2][8];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            const int hr = hb * 32 + n;
+            a[hb][kk] = *reinterpret_cast<const u32x4_t*>(qb + hr * 256 + 16 * ((8 * h + kk) ^ (hr & 15)));
+          }
+        f32x16_t acc[2][2] = {};
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            acc[hb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[hb][kk]), as_bf16x8(kf[0][kk]), acc[hb][0], 0, 0, 0);
+            acc[hb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[hb][kk]), as_bf16x8(kf[1][kk]), acc[hb][1], 0, 0, 0);
+          }
+        // lane (n, h) holds rows 8*(i/4) + 4*h + i%4 of each 32-head block: w of those heads
+        float part[2] = {0.f, 0.f};
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(&sw[buf][hb * 32 + 8 * q4 + 4 * h]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              part[0] += w4[i] * relu_bits(acc[hb][0][4 * q4 + i]);
+              part[1] += w4[i] * relu_bits(acc[hb][1][4 * q4 + i]);
+            }
+          }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          float v = part[kb] + __shfl_xor(part[kb], 32, 64);
+          int s = kbase + 64 * wv + 32 * kb + n;
+          if (h == 0 && s < N && (fill_masked || s < nv)) srow[s] = (s < nv) ? v : kNegInf;
+        }
+      } else if (fill_masked) {
+        for (int s = kbase + tid; s < min(kbase + kPfKeys, N); s += 256) srow[s] = kNegInf;
+      }
+    }
+    // every wave is done with the ring before the next key block restages it
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    if (r + 2 < nrows) stage(r + 2, (r + 2) % 3);
-    const int nv = snv[r];
-    float* srow = scores + (size_t)(r0 + r) * N;
-    if (kbase < nv) {
-      const char* qb = &sq[buf][0];
-      u32x4_t a[2][8];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const int hr = hb * 32 + n;
-          a[hb][kk] = *reinterpret_cast<const u32x4_t*>(qb + hr * 256 + 16 * ((8 * h + kk) ^ (hr & 15)));
-        }
-      f32x16_t acc[2][2] = {};
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          acc[hb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[hb][kk]), as_bf16x8(kf[0][kk]), acc[hb][0], 0, 0, 0);
-          acc[hb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[hb][kk]), as_bf16x8(kf[1][kk]), acc[hb][1], 0, 0, 0);
-        }
-      // lane (n, h) holds rows 8*(i/4) + 4*h + i%4 of each 32-head block: w of those heads
-      float part[2] = {0.f, 0.f};
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(&sw[buf][hb * 32 + 8 * q4 + 4 * h]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            part[0] += w4[i] * relu_bits(acc[hb][0][4 * q4 + i]);
-            part[1] += w4[i] * relu_bits(acc[hb][1][4 * q4 + i]);
-          }
-        }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float v = part[kb] + __shfl_xor(part[kb], 32, 64);
-        int s = kbase + 64 * wv + 32 * kb + n;
-        if (h == 0 && s < N && (fill_masked || s < nv)) srow[s] = (s < nv) ? v : kNegInf;
-      }
-    } else if (fill_masked) {
-      for (int s = kbase + tid; s < min(kbase + kPfKeys, N); s += 256) srow[s] = kNegInf;
-    }
   }
 }
 
@@ -546,7 +555,7 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
       const int64_t seg_end = std::min<int64_t>(qi0 + nrows, (int64_t)(b + 1) * s.T);
       const int t0 = (int)(q - (int64_t)b * s.T);
       const int nt = (int)(seg_end - q);
-      dim3 grid((s.N + kPfKeys - 1) / kPfKeys, (nt + kPfQ - 1) / kPfQ);
+      dim3 grid(std::min((s.N + kPfKeys - 1) / kPfKeys, kPfKeyGroups), (nt + kPfQ - 1) / kPfQ);
       hipError_t e = launch(indexer_prefill_mfma, grid, 256, 0, st,
                             static_cast<const uint16_t*>(q_I), w,
                             static_cast<const uint16_t*>(k_I), q_pos, s.T, s.N, s.m, b, t0, nt,
