@@ -123,12 +123,6 @@ __device__ __forceinline__ float group_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Workgroup id -> work item, XCD-major: with T % 8 == 0, XCD x (id % 8) runs items
-// x*T/8 .. (x+1)*T/8 - 1 in order.
-__device__ __forceinline__ int xcd_item(int lin, int T) {
-  const int remapped = (lin & 7) * (T >> 3) + (lin >> 3);
-  return (T & 7) ? lin : remapped;
-}
 
 // 16 ds_read_b64_tr_b16 for value-column blocks d0 .. d0+7 (entries 4g.. and 16+4g..), waited
 // for inside the same asm block. Written as asm because the builtin carries no memory operand, which makes the compiler wait

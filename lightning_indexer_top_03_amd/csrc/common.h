@@ -40,6 +40,14 @@ __device__ __forceinline__ int n_visible(int p, int m, int N) {
 }
 
 // Order-preserving map fp32 -> uint32 (larger float <=> larger key); -0 ranks as +0.
+// Workgroup id -> work item, XCD-major: workgroups are dealt to the 8 XCDs round-robin
+// (id % 8), so with T % 8 == 0 XCD x runs items x*T/8 .. (x+1)*T/8 - 1 in order and work items
+// that share data stay in one XCD's L2.
+__device__ __forceinline__ int xcd_item(int lin, int T) {
+  const int remapped = (lin & 7) * (T >> 3) + (lin >> 3);
+  return (T & 7) ? lin : remapped;
+}
+
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);

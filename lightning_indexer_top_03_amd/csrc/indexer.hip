@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_dma(
 
 // ------------------------------------------------------------------------------------------
 // Prefill-shaped kernel (bf16). H_I = 64, D_I = 128. Workgroup = kPfQ queries of one sequence x
-// the key blocks (256 keys) blockIdx.x, blockIdx.x + gridDim.x, ... below the queries' visible
+// the key blocks (256 keys) g, g + gridDim.x, ... (g: its key group) below the queries' visible
 // range: a grid of every (key block, query block) pair would be mostly blocks past the causal
 // edge, and dispatching those alone costs more than a tenth of the kernel. Per key block, wave
 // wv holds keys kbase + 64*wv + 32*kb + n (kb = 0, 1) as B operands in registers; the queries'
@@ -361,7 +361,11 @@ __global__ __launch_bounds__(256) void indexer_prefill_mfma(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
-  const int r0 = blockIdx.y * kPfQ;  // first row (relative to t0) of this tile
+  // the gridDim.x workgroups of a query block are consecutive work items, one XCD's: they
+  // stream the same q_I rows, which then stay in that XCD's L2
+  const int item = xcd_item(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int kgrp = item % gridDim.x;
+  const int r0 = (item / gridDim.x) * kPfQ;  // first row (relative to t0) of this tile
   const int nrows = min(kPfQ, nt - r0);
   const int64_t qi0 = (int64_t)b * T + t0 + r0;
 
@@ -377,7 +381,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_mfma(
   const size_t base_row = (size_t)b * N;
   const uint32_t qlds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)&sq[0][0]);
   const uint32_t wlds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)&sw[0][0]);
-  for (int kblk = blockIdx.x; kblk * kPfKeys < N; kblk += gridDim.x) {
+  for (int kblk = kgrp; kblk * kPfKeys < N; kblk += gridDim.x) {
     const int kbase = kblk * kPfKeys;
     if (kbase >= maxnv) {
       if (fill_masked)
