@@ -70,7 +70,7 @@ def _kernel_plan(cfg, nsplit):
         names.append("indexer_generic")
     mfma = cfg.dt == "bf16" and cfg.D_K == 576 and cfg.D_V == 512 and cfg.H % 64 == 0
     if not _fused_topk(cfg):
-        names.append("topk_radix_reg" if cfg.N <= 32768 else "topk_radix_row")
+        names += ["topk_radix_reg"] if cfg.N <= 32768 else ["topk_long_filter", "topk_long_select"]
     names.append("attend_mfma_dma" if mfma else "attend_generic")
     if nsplit > 1:
         names.append("attend_combine")
@@ -103,6 +103,10 @@ def _algorithmic(cfg, name):
         keys = B * max(nvis) if T > 1 else pairs
         byt = keys * kI_row + rows * cfg.H_I * (cfg.D_I * esz + 4) + pairs * 4
         return byt, pairs * cfg.H_I * cfg.D_I * 2.0
+    if name == "topk_long_filter":
+        return pairs * 4, 0.0  # reads every visible score; its candidates are scratch
+    if name == "topk_long_select":
+        return rows * cfg.top_k * 4, 0.0
     if name.startswith("topk"):
         return pairs * 4 + rows * cfg.top_k * 4, 0.0
     if name.startswith("attend_mfma") or name == "attend_generic":

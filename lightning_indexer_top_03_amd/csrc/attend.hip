@@ -578,7 +578,7 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
 // row): 16 heads x 256 columns, the block written by one wave of attend_mfma_dma per split.
 // Partials are read as whole 512-byte rows of f16x4; the bf16 result goes through LDS so that
 // each row of the output is written with 16-byte stores.
-constexpr int kMaxSplits = 8;
+constexpr int kMaxSplits = 16;
 __global__ __launch_bounds__(256) void attend_combine(
     const f16x4_t* __restrict__ part_o, const float* __restrict__ part_ml, int64_t qi0, int H,
     int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse, int nitems) {
@@ -606,25 +606,25 @@ __global__ __launch_bounds__(256) void attend_combine(
   }
   float ml_m = kNegInf, ml_l = 0.f, ml_c = 0.f;
   {
-    const int hh = tid >> 3, s = tid & 7;  // 16 heads x 8 splits = threads 0..127
-    if (tid < 128 && s < nsplit) {
+    const int hh = tid >> 4, s = tid & 15;  // 16 heads x 16 splits = the 256 threads
+    if (s < nsplit) {
       const size_t hrow = ((size_t)row * H + h0 + hh) * nsplit + s;
       ml_m = part_ml[hrow * 4];
       ml_l = part_ml[hrow * 4 + 1];
       ml_c = part_ml[hrow * 4 + 2 + (ws >> 2)];  // scale of this column half
     }
   }
-  // per head: M = max_s m_s, L = sum_s 2^(m_s - M) l_s, over the 8 lanes of each head
+  // per head: M = max_s m_s, L = sum_s 2^(m_s - M) l_s, over the 16 lanes of each head
   float M = ml_m;
 #pragma unroll
-  for (int o = 1; o < 8; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   const float wm = ml_m == kNegInf ? 0.f : exp2f(ml_m - M);
   const float wl = wm * ml_l;
   float L = wl;
 #pragma unroll
-  for (int o = 1; o < 8; o <<= 1) L += __shfl_xor(L, o, 64);
-  if (tid < 128) {
-    const int hh = tid >> 3, s = tid & 7;
+  for (int o = 1; o < 16; o <<= 1) L += __shfl_xor(L, o, 64);
+  {
+    const int hh = tid >> 4, s = tid & 15;
     wsc[s][hh] = L > 0.f ? wm / L * ml_c : 0.f;
     if (s == 0 && lse) lse[(size_t)qi * H + h0 + hh] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
   }
@@ -738,7 +738,10 @@ int attend_splits(const Shape& s, int64_t nrows, int fmt) {
   if (wgs >= 512) return 1;
   const int E = s.top_k + s.W;
   int64_t want = (512 + wgs - 1) / wgs;
-  int64_t maxs = (E + 255) / 256;  // at least 256 entries per split
+  // at least 256 entries per split (each workgroup's prologue is a fixed cost); 128 when even
+  // that leaves most of the GPU idle (a handful of rows, as in long-context CSA decode)
+  const int min_per = wgs * ((E + 255) / 256) >= 256 ? 256 : 128;
+  int64_t maxs = (E + min_per - 1) / min_per;
   int64_t ns = want < maxs ? want : maxs;
   if (ns > kMaxSplits) ns = kMaxSplits;
   return ns < 1 ? 1 : (int)ns;

@@ -80,65 +80,27 @@ __device__ __forceinline__ void append(bool take, int i, uint32_t* pos, int32_t*
   if (take) out[base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull))] = i;
 }
 
-// One workgroup per query row. LDS_KEYS: the row's order keys are staged in LDS (rows of at
-// most kLdsMaxN entries); otherwise every pass re-reads the scores from global memory (L2).
-// The bits every visible key shares (block-wide AND / OR) are skipped, so the first digit
-// already splits the row: scores of one row typically share sign and exponent, and digits over
-// those bits would put the whole row into a handful of bins and serialise the LDS atomics.
-template <bool LDS_KEYS>
-__global__ __launch_bounds__(kTkThreads) void topk_radix_row(
-    const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int64_t qi0, int N,
-    int m, int k, int32_t* __restrict__ idx) {
-  extern __shared__ uint32_t skey[];  // [n] when LDS_KEYS
-  __shared__ TkShared sh;
+// Exact radix select over one whole row of n > k visible scores, re-read from global memory
+// (L2) on every pass; one 1024-thread workgroup. The bits every visible key shares (block-wide
+// AND / OR) are skipped, so the first digit already splits the row: scores of one row typically
+// share sign and exponent, and digits over those bits would put the whole row into a handful of
+// bins and serialise the LDS atomics. Used for long rows only when the filtered path below
+// cannot prove its candidate set complete.
+__device__ void radix_row_exact(const float* __restrict__ s, int n, int k,
+                                int32_t* __restrict__ out, TkShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t row = blockIdx.x;
-  const int n = n_visible(q_pos[qi0 + row], m, N);
-  int32_t* __restrict__ out = idx + row * (int64_t)k;
-  const float* __restrict__ s = scores + row * (int64_t)N;
-  auto key = [&](int i) -> uint32_t {
-    if constexpr (LDS_KEYS)
-      return skey[i];
-    else
-      return order_key(s[i]);
-  };
-
-  if (n <= k) {
-    for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
-    return;
-  }
+  auto key = [&](int i) -> uint32_t { return order_key(s[i]); };
   uint32_t kand = 0xffffffffu, kor = 0u;
-  if constexpr (LDS_KEYS) {
-    // every load in flight before the first use (clamped addresses, no branches): a loop over
-    // the runtime n would wait for each load in turn
-    constexpr int kPer = kLdsMaxN / kTkThreads;
-    float v[kPer];
+  for (int base = 0; base < n; base += 8 * kTkThreads) {
+    float v[8];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      if (j * kTkThreads < n) v[j] = s[min(tid + j * kTkThreads, n - 1)];
-    }
+    for (int j = 0; j < 8; ++j) v[j] = s[min(base + tid + j * kTkThreads, n - 1)];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = tid + j * kTkThreads;
-      if (i < n) {
+    for (int j = 0; j < 8; ++j) {
+      if (base + tid + j * kTkThreads < n) {
         const uint32_t u = order_key(v[j]);
-        skey[i] = u;
         kand &= u;
         kor |= u;
-      }
-    }
-  } else {
-    for (int base = 0; base < n; base += 8 * kTkThreads) {
-      float v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = s[min(base + tid + j * kTkThreads, n - 1)];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (base + tid + j * kTkThreads < n) {
-          const uint32_t u = order_key(v[j]);
-          kand &= u;
-          kor |= u;
-        }
       }
     }
   }
@@ -222,6 +184,217 @@ __global__ __launch_bounds__(kTkThreads) void topk_radix_row(
 }
 
 // ------------------------------------------------------------------------------------------
+// Rows longer than kLdsMaxN (CSA decode: 262144 blocks per row) in two launches, so that the
+// whole GPU works on a handful of rows instead of one workgroup per row:
+//  * topk_long_filter, one 512-thread workgroup per kLongChunk entries of a row: the chunk's
+//    local threshold tau_g = its r-th largest key with r = ceil(2k * chunk / n) + 16 (about
+//    twice the chunk's fair share of the top k), then every key >= tau_g of the chunk goes, in
+//    index order, to the chunk's candidate segment (indices and keys), with its count and tau_g.
+//  * topk_long_select, one 1024-thread workgroup per row: the segments are concatenated in
+//    chunk order (so candidate order is index order) into LDS and the top k of the candidates
+//    are selected with the same ties-to-lowest-index rule. The result is exact whenever the
+//    selected threshold tau >= tau_g for every chunk: an entry that is not a candidate lies
+//    below its chunk's tau_g <= tau, so every entry >= tau is a candidate. When that check
+//    fails, or a segment overflowed, or there are more candidates than the registers hold, the
+//    workgroup falls back to the exact whole-row radix select above.
+// ------------------------------------------------------------------------------------------
+constexpr int kLongChunk = 4096;                // entries per filter workgroup
+constexpr int kFiltThreads = 512;               // 8 entries per thread
+constexpr int kLongSeg = 1024;                  // candidate slots per chunk
+constexpr int kLongCap = 8 * kTkThreads;        // candidates ranked in registers by the select
+constexpr int kLongMaxChunks = 4 * kTkThreads;  // chunks per row the select kernel can scan
+
+// Per-row workspace of the long-row path: counts[G], taus[G], cand_idx[G][kLongSeg],
+// cand_key[G][kLongSeg].
+__host__ __device__ inline size_t long_row_bytes(int G) {
+  return (size_t)G * (8 + 8 * (size_t)kLongSeg);
+}
+
+__global__ __launch_bounds__(kFiltThreads) void topk_long_filter(
+    const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int64_t qi0, int N,
+    int m, int k, int G, uint8_t* __restrict__ ws) {
+  constexpr int NW = kFiltThreads / 64, PER = kLongChunk / kFiltThreads;
+  __shared__ SelShared<NW> sh;
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const int c0 = g * kLongChunk;
+  // the chunk's loads depend on N only (clamped to the row), so they are in flight while
+  // q_pos is read; entries at or past n_vis are masked below
+  uint32_t key[PER];
+  load_keys<PER>(scores + row * (int64_t)N + c0, N, min(kLongChunk, N - c0), key);
+  const int n = n_visible(q_pos[qi0 + row], m, N);
+  if (n <= k) return;  // the select kernel keeps every visible entry
+  uint8_t* rws = ws + row * long_row_bytes(G);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(rws);
+  uint32_t* taus = counts + G;
+  int32_t* cidx = reinterpret_cast<int32_t*>(taus + G) + (size_t)g * kLongSeg;
+  uint32_t* ckey = reinterpret_cast<uint32_t*>(taus + G) + (size_t)G * kLongSeg + (size_t)g * kLongSeg;
+  if (c0 >= n) {
+    if (tid == 0) {
+      counts[g] = 0u;
+      taus[g] = 0u;
+    }
+    return;
+  }
+  const int cn = min(kLongChunk, n - c0);
+  const int nv = max(0, min(PER, cn - PER * tid));
+  const int64_t r64 = (2 * (int64_t)k * cn + n - 1) / n + 16;
+  uint32_t tau = 0u;  // every key >= 0: the whole chunk is a candidate
+  if (r64 < cn) {
+    uint32_t need, cnt_eq;
+    block_threshold<NW, PER>(key, nv, (uint32_t)r64, sh, tau, need, cnt_eq, (uint32_t)cn);
+  }
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) cnt += (j < nv && key[j] >= tau) ? 1u : 0u;
+  uint32_t total;
+  const uint32_t pos = block_excl_scan<NW>(cnt, sh, total);
+  if (total <= (uint32_t)kLongSeg) {
+    uint32_t o = pos;
+    const int e0 = c0 + PER * tid;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (j < nv && key[j] >= tau) {
+        cidx[o] = e0 + j;
+        ckey[o] = key[j];
+        ++o;
+      }
+    }
+  }
+  if (tid == 0) {
+    counts[g] = total <= (uint32_t)kLongSeg ? total : 0xffffffffu;  // overflow marker
+    taus[g] = tau;
+  }
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_long_select(
+    const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int64_t qi0, int N,
+    int m, int k, int G, const uint8_t* __restrict__ ws, int32_t* __restrict__ idx) {
+  constexpr int PER = kLongCap / kTkThreads;
+  struct Fast {
+    SelShared<kTkWaves> sel;
+    uint32_t off[kLongMaxChunks], cnt[kLongMaxChunks];
+    int32_t cidx[kLongCap];
+    uint32_t ckey[kLongCap];
+    uint32_t tau_max, bad;
+  };
+  __shared__ __attribute__((aligned(16))) char smem[sizeof(Fast) > sizeof(TkShared) ? sizeof(Fast) : sizeof(TkShared)];
+  Fast& f = *reinterpret_cast<Fast*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const uint8_t* rws = ws + row * long_row_bytes(G);
+  const uint32_t* counts = reinterpret_cast<const uint32_t*>(rws);
+  const uint32_t* taus = counts + G;
+  const int32_t* sidx = reinterpret_cast<const int32_t*>(taus + G);
+  const uint32_t* skey = reinterpret_cast<const uint32_t*>(taus + G) + (size_t)G * kLongSeg;
+  // Everything the fast path reads is requested up front, at addresses that depend on G only
+  // (in flight together with q_pos): this thread's four counts and tau_g, and for wave w the
+  // first 64 slots of segments w, w + 16, w + 32, w + 48 (slots past a segment's count hold
+  // stale values and are dropped).
+  constexpr int U = 4;
+  uint32_t c[4], t4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int gj = min(4 * tid + j, G - 1);
+    c[j] = counts[gj];
+    t4[j] = taus[gj];
+  }
+  int32_t pi[U];
+  uint32_t pk[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const size_t gj = (size_t)min(wv + kTkWaves * u, G - 1);
+    pi[u] = sidx[gj * kLongSeg + lane];
+    pk[u] = skey[gj * kLongSeg + lane];
+  }
+  const int n = n_visible(q_pos[qi0 + row], m, N);
+  int32_t* __restrict__ out = idx + row * (int64_t)k;
+  const float* __restrict__ s = scores + row * (int64_t)N;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const int Gn = (n + kLongChunk - 1) / kLongChunk;  // chunks holding visible entries
+  bool fast = Gn <= kLongMaxChunks;
+  uint32_t total = 0;
+  if (fast) {
+    // thread t owns chunks 4t .. 4t+3: their counts, running offsets and the largest tau_g
+    uint32_t local = 0, tmax = 0, bad = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = 4 * tid + j < Gn;
+      c[j] = in ? c[j] : 0u;
+      bad |= c[j] > (uint32_t)kLongSeg ? 1u : 0u;
+      c[j] = c[j] > (uint32_t)kLongSeg ? 0u : c[j];
+      tmax = max(tmax, in ? t4[j] : 0u);
+      local += c[j];
+    }
+    if (tid == 0) {
+      f.tau_max = 0u;
+      f.bad = 0u;
+    }
+    const uint32_t before = block_excl_scan<kTkWaves>(local, f.sel, total);
+    uint32_t o = before;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gj = 4 * tid + j;
+      if (gj < Gn) {
+        f.off[gj] = o;
+        f.cnt[gj] = c[j];
+      }
+      o += c[j];
+    }
+    tmax = wave_max(tmax);
+    bad = wave_max(bad);
+    if (lane == 0) {
+      atomicMax(&f.tau_max, tmax);
+      atomicOr(&f.bad, bad);
+    }
+    __syncthreads();
+    fast = f.bad == 0u && total >= (uint32_t)k && total <= (uint32_t)kLongCap;
+    if (fast) {
+      // concatenate the segments in chunk order: the prefetched slots first, then whatever
+      // lies beyond them (segments past 64, slots past 64)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int gj = wv + kTkWaves * u;
+        if (gj < Gn && (uint32_t)lane < f.cnt[gj]) {
+          f.cidx[f.off[gj] + lane] = pi[u];
+          f.ckey[f.off[gj] + lane] = pk[u];
+        }
+      }
+      for (int gj = wv; gj < Gn; gj += kTkWaves) {
+        const uint32_t cg = f.cnt[gj], og = f.off[gj];
+        for (uint32_t i = (gj < U * kTkWaves ? 64u : 0u) + lane; i < cg; i += 64) {
+          f.cidx[og + i] = sidx[(size_t)gj * kLongSeg + i];
+          f.ckey[og + i] = skey[(size_t)gj * kLongSeg + i];
+        }
+      }
+      __syncthreads();
+      uint32_t key[PER];
+      const int e0 = PER * tid;
+      const int nv = max(0, min(PER, (int)total - e0));
+#pragma unroll
+      for (int j = 0; j < PER; ++j) key[j] = f.ckey[min(e0 + j, (int)total - 1)];
+      uint32_t tau, need, cnt_eq;
+      block_threshold<kTkWaves, PER>(key, nv, (uint32_t)k, f.sel, tau, need, cnt_eq, total);
+      if (tau >= f.tau_max) {  // block-uniform: the candidate set holds the row's top k
+        uint32_t base, take_eq, nsel;
+        block_ranks<kTkWaves, PER>(key, nv, tau, need, f.sel, base, take_eq, nsel);
+        const auto sel = select_mask<PER>(key, nv, tau, take_eq);
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+          if ((sel >> j) & 1) out[base + sel_rank(sel, j)] = f.cidx[e0 + j];
+        return;
+      }
+    }
+    __syncthreads();  // the fallback reuses the shared memory
+  }
+  radix_row_exact(s, n, k, out, *reinterpret_cast<TkShared*>(smem));
+}
+
+// ------------------------------------------------------------------------------------------
 // topk_radix_reg<PER>: rows of at most 1024*PER visible entries, one 1024-thread workgroup per
 // row. Thread t owns the contiguous entries PER*t .. PER*t+PER-1 and keeps their order keys in
 // registers for the whole kernel; the threshold and the ranks come from select.h
@@ -258,10 +431,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_radix_reg(
 
 }  // namespace
 
-size_t topk_ws_bytes(const Shape&, int64_t) { return 0; }
+size_t topk_ws_bytes(const Shape& s, int64_t nrows) {
+  if (s.N <= kLdsMaxN) return 0;
+  const int G = (s.N + kLongChunk - 1) / kLongChunk;
+  return (size_t)nrows * long_row_bytes(G);
+}
 
 hipError_t launch_topk(const Shape& s, int64_t qi0, int64_t nrows, const float* scores,
-                       const int32_t* q_pos, int32_t* idx, void*, hipStream_t st) {
+                       const int32_t* q_pos, int32_t* idx, void* ws, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   // rows hold at most N visible entries
   const dim3 grid((unsigned)nrows);
@@ -274,8 +451,13 @@ hipError_t launch_topk(const Shape& s, int64_t qi0, int64_t nrows, const float* 
   if (s.N <= kLdsMaxN)
     return launch(topk_radix_reg<32>, grid, kTkThreads, 0, st, scores, q_pos, qi0, s.N, s.m,
                   s.top_k, idx);
-  return launch(topk_radix_row<false>, grid, kTkThreads, 0, st, scores, q_pos, qi0, s.N, s.m,
-                s.top_k, idx);
+  const int G = (s.N + kLongChunk - 1) / kLongChunk;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  if (hipError_t e = launch(topk_long_filter, dim3((unsigned)G, (unsigned)nrows), kFiltThreads,
+                            0, st, scores, q_pos, qi0, s.N, s.m, s.top_k, G, w))
+    return e;
+  return launch(topk_long_select, grid, kTkThreads, 0, st, scores, q_pos, qi0, s.N, s.m,
+                s.top_k, G, static_cast<const uint8_t*>(w), idx);
 }
 
 }  // namespace dsa

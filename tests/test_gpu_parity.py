@@ -112,12 +112,18 @@ def test_indexer_generic_fp32_and_small_heads():
 
 # --------------------------------------------------------------------------------- top-k ----
 
-def _topk_case(label, n_rows, N, k, m=1, ties=False, pos=None, seed=0):
+def _topk_case(label, n_rows, N, k, m=1, ties=False, pos=None, seed=0, order=None):
     rng = np.random.default_rng(seed)
     s = synth.normal(50 + seed, 1, (n_rows, N), 1.0, "f32")
     if ties:
         s = (np.round(s * 8) / 8).astype(np.float32)
         s[0, : N // 2] = 0.5  # one row with a very wide tie
+    if order == "sorted":
+        # row 0 ascending, row 1 descending, row 2 constant: the top k crowd into one end of
+        # the row (or tie everywhere), which defeats any per-chunk shortcut
+        s[0] = np.sort(s[0])
+        s[1] = np.sort(s[1])[::-1]
+        s[2] = 1.25
     if pos is None:
         pos = rng.integers(0, N * m, n_rows).astype(np.int32)
         pos[0] = N * m - 1
@@ -141,6 +147,17 @@ def test_topk_exact_sets():
     _topk_case("keep-all", 4, 1500, 2048, seed=3)
     _topk_case("csa", 6, 4000, 1024, m=4, seed=4)
     _topk_case("long", 2, 262144, 1024, seed=5)
+
+
+def test_topk_long_rows():
+    # rows longer than 32768 entries: filtered candidates per 4096-entry chunk, then a select
+    # over the candidates, with the exact whole-row select as fallback
+    _topk_case("long-mixed-nvis", 7, 40000, 1000, seed=7,
+               pos=np.array([39999, 999, 1000, 1001, 20000, 32768, 36863], np.int32))
+    _topk_case("long-m4", 3, 70001, 1024, m=4, seed=8)
+    _topk_case("long-ties", 3, 50000, 1024, ties=True, seed=9)
+    _topk_case("long-sorted", 3, 65536, 1024, seed=10, pos=np.full(3, 65535, np.int32))
+    _topk_case("long-k4096", 2, 300000, 4096, seed=11)
 
 
 def test_topk_ties_take_lowest_index():
