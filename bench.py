@@ -65,7 +65,7 @@ def _kernel_plan(cfg, nsplit):
     elif fast and cfg.k_dt == "bf16":
         names.append("indexer_decode_dma")
     elif fast:
-        names.append("indexer_decode_mfma")
+        names.append("indexer_decode_fp4_dma")
     else:
         names.append("indexer_generic")
     mfma = cfg.dt == "bf16" and cfg.D_K == 576 and cfg.D_V == 512 and cfg.H % 64 == 0

@@ -6,15 +6,17 @@
 // a low-dimensional per-token key, a ReLU instead of a softmax for throughput; s3 step 2:
 // "mqa logits", the key is shared by all indexer heads.)
 //
-// Three kernels:
-//  * indexer_decode_mfma  - few query rows, long key ranges: the query's 64x128 q_I stays in
-//    registers as MFMA A operands; every wave streams its own 32-key tiles of k_I straight
-//    from HBM into B operands (16-byte loads, two tiles in flight). bf16 or MXFP4 keys (FP4
-//    codes dequantised by v_cvt_scalef32_pk_bf16_fp4 into exact bf16).
-//  * indexer_prefill_mfma - many query rows of one sequence: each wave keeps 64 keys of k_I
+// Kernels:
+//  * indexer_decode_dma     - few query rows, bf16 keys: the query's 64x128 q_I is staged once
+//    per workgroup and held as MFMA A operands; every wave streams its own 32-key tiles of k_I
+//    from HBM into a private LDS ring by DMA (v_mfma_f32_32x32x16_bf16).
+//  * indexer_decode_fp4_dma - few query rows, MXFP4 keys: the same ring of 64-key tiles, fed
+//    to the block-scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4 with the FP4 codes and E8M0
+//    scales as stored and q_I split into two scaled fp8 operands.
+//  * indexer_prefill_mfma   - many query rows of one sequence: each wave keeps 64 keys of k_I
 //    in registers, the workgroup walks 32 queries whose q_I is staged in LDS.
-//  * indexer_generic      - any H_I / D_I, fp32 or bf16 (and MXFP4) inputs; scalar fp32.
-// All three fuse ReLU, the head weights and the 64-head reduction into the epilogue, so the
+//  * indexer_generic        - any H_I / D_I, fp32 or bf16 (and MXFP4) inputs; scalar fp32.
+// All of them fuse ReLU, the head weights and the 64-head reduction into the epilogue, so the
 // [H_I x N] per-head products never leave registers.
 #include "common.h"
 #include "launch.h"
@@ -30,165 +32,6 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // E8M0 byte -> fp32 scale 2^(e-127).
 __device__ __forceinline__ float e8m0_scale(uint32_t e) {
   return e == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);
-}
-
-// ------------------------------------------------------------------------------------------
-// Decode-shaped kernel. H_I = 64, D_I = 128.
-//
-// MFMA v_mfma_f32_32x32x16_bf16, C[32 heads x 32 keys] += A[heads x 16] * B[16 x keys].
-// Lane l = (n = l % 32, h = l / 32). The contraction index of MFMA kk, slot i is dim
-// 64*h + 8*kk + i for both operands, so a lane reads 128 contiguous bytes of its q_I row
-// (A) and of its key row (B). Output: acc[hb][4*j + i] = head hb*32 + 8*j + 4*h + i, key n.
-// ------------------------------------------------------------------------------------------
-template <int KFMT>
-struct KeyTile {
-  u32x4_t v[8];
-};
-
-template <int KFMT>
-__device__ __forceinline__ void load_key_tile(KeyTile<KFMT>& kt, const uint8_t* __restrict__ kI,
-                                              const uint8_t* __restrict__ ksc, size_t row, int h,
-                                              float& s_lo, float& s_hi) {
-  if constexpr (KFMT == FMT_BF16) {
-    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(kI + row * 256 + 128 * h);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) kt.v[kk] = __builtin_nontemporal_load(p + kk);
-  } else {
-    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(kI + row * 64 + 32 * h);
-    kt.v[0] = __builtin_nontemporal_load(p);
-    kt.v[1] = __builtin_nontemporal_load(p + 1);
-    uint32_t sc = *reinterpret_cast<const uint16_t*>(ksc + row * 4 + 2 * h);
-    s_lo = e8m0_scale(sc & 0xffu);
-    s_hi = e8m0_scale(sc >> 8);
-  }
-}
-
-template <int KFMT>
-__device__ __forceinline__ bf16x8_t key_operand(const KeyTile<KFMT>& kt, int kk, float s_lo,
-                                                float s_hi) {
-  if constexpr (KFMT == FMT_BF16) {
-    return as_bf16x8(kt.v[kk]);
-  } else {
-    // dims 64h + 8kk .. +7 are code bytes 4kk .. 4kk+3 of the lane's 32-byte chunk
-    uint32_t cw = kt.v[kk >> 2][kk & 3];
-    float sc = kk < 4 ? s_lo : s_hi;
-    bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 0);
-    bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 1);
-    bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 2);
-    bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 3);
-    bf16x8_t r;
-    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-    return r;
-  }
-}
-
-constexpr int kDecodeMaxIters = 16;  // 32-key tiles per wave
-
-template <int KFMT, int ITERS>
-__global__ __launch_bounds__(256) void indexer_decode_mfma(
-    const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
-    const uint8_t* __restrict__ ksc, const int32_t* __restrict__ q_pos, int T, int N, int m,
-    int64_t qi0, float* __restrict__ scores, int fill_masked) {
-  const int64_t row = blockIdx.y;
-  const int64_t qi = qi0 + row;
-  const int b = (int)(qi / T);
-  const int nv = n_visible(q_pos[qi], m, N);
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 31, h = lane >> 5;
-  constexpr int keys_per_wave = 32 * ITERS;
-  const int key0 = (blockIdx.x * 4 + wv) * keys_per_wave;
-  float* __restrict__ srow = scores + (size_t)row * N;
-  __shared__ float sres[4][32 * ITERS];
-
-  if (key0 >= nv) {
-    if (fill_masked)
-      for (int s = key0 + lane; s < min(key0 + keys_per_wave, N); s += 64) srow[s] = kNegInf;
-    return;
-  }
-
-  // q_I fragments (A operands) and the weights of the heads this lane's outputs belong to.
-  const uint16_t* qrow = qI + (size_t)qi * (64 * 128);
-  u32x4_t qa[2][8];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qa[hb][kk] = *reinterpret_cast<const u32x4_t*>(qrow + (hb * 32 + n) * 128 + 64 * h + 8 * kk);
-  float wr[2][16];
-  const float* wrow = w + (size_t)qi * 64;
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(wrow + hb * 32 + 8 * j + 4 * h);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wr[hb][4 * j + i] = w4[i];
-    }
-  // complete the q_I / w loads before the key pipeline and make the values opaque, so that the
-  // compiler neither waits for them inside the pipeline (draining the prefetched tile) nor
-  // re-loads them next to each use
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) asm volatile("" : "+v"(qa[hb][kk]));
-#pragma unroll
-    for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(wr[hb][r]));
-  }
-
-  const size_t base_row = (size_t)b * N;
-  const int last = min(key0 + keys_per_wave, nv);  // exclusive end of computed keys
-  const int ntiles = (last - key0 + 31) / 32;      // wave-uniform
-  // Two register buffers, ping-pong: the next tile is always requested (rows clamped to the
-  // sequence) before the current one is consumed, with no branch around the loads, so the
-  // wait for the current tile leaves the next one in flight.
-  KeyTile<KFMT> ta, tb;
-  float lo_a = 0.f, hi_a = 0.f, lo_b = 0.f, hi_b = 0.f;
-  auto tile_row = [&](int t) { return base_row + min(key0 + 32 * t + n, N - 1); };
-  auto consume = [&](const KeyTile<KFMT>& kt, float slo, float shi, int t) {
-    f32x16_t acc0 = {}, acc1 = {};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      bf16x8_t kb = key_operand<KFMT>(kt, kk, slo, shi);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[0][kk]), kb, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[1][kk]), kb, acc1, 0, 0, 0);
-    }
-    float part = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      part += wr[0][r] * fmaxf(acc0[r], 0.f);
-      part += wr[1][r] * fmaxf(acc1[r], 0.f);
-    }
-    part += __shfl_xor(part, 32, 64);
-    // scores go to LDS (no vector-memory counter traffic inside the pipeline), flushed below
-    if (h == 0) sres[wv][32 * t + n] = part;
-  };
-  // Straight-line, branch-free (ITERS is a compile-time count): the loads of tile t+1 are issued
-  // before tile t is consumed. Rows past the wave's visible range are clamped and their results
-  // never flushed; computing them keeps the code free of branches the loads could sink into.
-  load_key_tile<KFMT>(ta, kI, ksc, tile_row(0), h, lo_a, hi_a);
-#pragma unroll
-  for (int t = 0; t < ITERS; ++t) {
-    if (t % 2 == 0) {
-      if (t + 1 < ITERS) load_key_tile<KFMT>(tb, kI, ksc, tile_row(t + 1), h, lo_b, hi_b);
-      __builtin_amdgcn_sched_barrier(0);  // keep the next tile's loads ahead of this tile's use
-      consume(ta, lo_a, hi_a, t);
-    } else {
-      if (t + 1 < ITERS) load_key_tile<KFMT>(ta, kI, ksc, tile_row(t + 1), h, lo_a, hi_a);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(tb, lo_b, hi_b, t);
-    }
-  }
-  // flush this wave's scores: computed keys (masked past n_vis), then -inf past the visible end
-  const int kend = min(key0 + keys_per_wave, N);
-  for (int s = key0 + lane; s < kend; s += 64) {
-    const int o = s - key0;
-    if (o < 32 * ntiles)
-      srow[s] = s < nv ? sres[wv][o] : kNegInf;
-    else if (fill_masked)
-      srow[s] = kNegInf;
-  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -331,6 +174,256 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_dma(
       srow[s] = s < nv ? sres[wv][o] : kNegInf;
     else if (fill_masked)
       srow[s] = kNegInf;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode-shaped kernel, MXFP4 keys (64 code bytes + 4 E8M0 scale bytes per key), on the
+// block-scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4, which takes the FP4 codes and their E8M0
+// scales as they are stored (no per-element conversion).
+//  * q_I (bf16) enters as two fp8 (e4m3) operands, q = hi + lo, each with its own E8M0 scale
+//    per 32 dims: with e the exponent of the block's largest |q|, hi = RNE(q / 2^(e-7)) and
+//    lo = RNE((q - hi 2^(e-7)) / 2^(e-11)). A bf16 value has 8 significant bits and hi keeps 4,
+//    so the remainder has at most 4 and lo holds it exactly, except for values more than 2^13
+//    below the block maximum, where the error stays below 2^(e-21). The products of fp8 and
+//    fp4 values are exact and accumulate in fp32.
+//  * Operand layouts of the instruction (checked on gfx950): B (fp4, 16 bytes per lane): lane
+//    (n, h) holds key n, contraction indices 32h .. 32h+31 in nibble order; A (fp8, 32 bytes
+//    per lane): lane (i, h) holds row i, indices 16h .. 16h+15 in bytes 0..15 and 32+16h ..
+//    47+16h in bytes 16..31; the scale of (row or key c, index block b) comes from lane c + 32b.
+//    Contraction step s covers dims 64s .. 64s+63, so each index block is one MX block of k_I.
+//  * Keys stream through LDS exactly as in indexer_decode_dma: each of the 8 waves runs its
+//    own 4-stage ring of 64-key tiles (4 KB of codes in four fully coalesced 1 KB DMAs, 256 B of
+//    scales in one 4-byte-per-lane DMA). Row r of a tile keeps its 16-byte chunk c in slot
+//    c ^ ((r >> 2) & 3), so the 16 lanes of a ds_read_b128 phase cover all 64 banks once.
+// ------------------------------------------------------------------------------------------
+constexpr int kF4Tile = 64;                              // keys per tile
+constexpr int kF4Stages = 4;                             // ring stages per wave
+constexpr int kF4Stage = kF4Tile * 64 + kF4Tile * 4;     // codes + scales: 4352 bytes
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+template <int ITERS>
+__global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_fp4_dma(
+    const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
+    const uint8_t* __restrict__ ksc, const int32_t* __restrict__ q_pos, int T, int N, int m,
+    int64_t qi0, float* __restrict__ scores, int fill_masked) {
+  static_assert(ITERS <= 8, "the scores of a wave are staged in the q_I operand buffer");
+  // sq: fp8 codes of q_I, [part][head][8 chunks of 16 B] (chunk c of head r in slot c ^ (r & 7)),
+  // then reused for the scores
+  __shared__ __attribute__((aligned(16))) char sq[2 * 64 * 128];
+  __shared__ uint32_t sqs[2][64];  // E8M0 scale bytes of q_I: [part][head] x 4 blocks
+  __shared__ __attribute__((aligned(16))) char sk[kDecWaves][kF4Stages][kF4Stage];
+  float (*sres)[kF4Tile * ITERS] = reinterpret_cast<float (*)[kF4Tile * ITERS]>(&sq[0]);
+  const int64_t row = blockIdx.y;
+  const int64_t qi = qi0 + row;
+  const int b = (int)(qi / T);
+  const int nv = n_visible(q_pos[qi], m, N);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  // Tiles are dealt round-robin over the row's waves (tile t of wave gw: keys
+  // (t GW + gw) * 64 ..), so at any moment the whole grid streams one contiguous window of
+  // the key cache: a cold read of this size runs ~25% faster that way than when every wave
+  // streams a contiguous range of its own.
+  const int gw = blockIdx.x * kDecWaves + wv, GW = gridDim.x * kDecWaves;
+  auto tile_key = [&](int t) { return (t * GW + gw) * kF4Tile; };
+  float* __restrict__ srow = scores + (size_t)row * N;
+
+  if (blockIdx.x * kDecWaves * kF4Tile >= nv) {  // every tile of the workgroup is masked
+    if (fill_masked)
+      for (int t = 0; t < ITERS; ++t)
+        if (tile_key(t) + lane < N) srow[tile_key(t) + lane] = kNegInf;
+    return;
+  }
+  const size_t base_row = (size_t)b * N;
+  const uint32_t ring = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)&sk[wv][0][0]);
+  // head weights of the rows this lane's accumulators hold
+  float wr[2][16];
+  const float* wrow = w + (size_t)qi * 64;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(wrow + hb * 32 + 8 * j + 4 * h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wr[hb][4 * j + i] = w4[i];
+    }
+  // q_I: thread t converts head t / 8, dims 16 (t % 8) .. +15
+  const int qh = tid >> 3, qc = tid & 7;
+  const u32x4_t* qsrc = reinterpret_cast<const u32x4_t*>(qI + (size_t)qi * (64 * 128) + qh * 128 + 16 * qc);
+  const u32x4_t q0 = qsrc[0], q1 = qsrc[1];
+  // tile t of this wave into stage t % kF4Stages: 5 DMA instructions
+  auto issue = [&](int t) {
+    const uint32_t sb = ring + (t % kF4Stages) * kF4Stage;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * j + (lane >> 2), c = lane & 3;
+      // keys past the visible range re-read the last visible row (served by L2)
+      const size_t krow = base_row + min(tile_key(t) + r, nv - 1);
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(kI + krow * 64 + 16 * (c ^ ((r >> 2) & 3))),
+          (lds_void_t*)(uintptr_t)(sb + 1024 * j), 16, 0, 0);
+    }
+    const size_t srow_k = base_row + min(tile_key(t) + lane, nv - 1);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ksc + srow_k * 4),
+                                     (lds_void_t*)(uintptr_t)(sb + kF4Tile * 64), 4, 0, 0);
+  };
+  constexpr int kPre = ITERS < kF4Stages ? ITERS : kF4Stages;
+#pragma unroll
+  for (int t = 0; t < kPre; ++t) issue(t);
+  // w and q_I have landed once only the prefetched tiles are outstanding
+  switch (kPre) {
+    case 1: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+  }
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(wr[hb][r]));
+  {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32((uint16_t)(q0[i] & 0xffffu));
+      v[2 * i + 1] = bf16_to_f32((uint16_t)(q0[i] >> 16));
+      v[8 + 2 * i] = bf16_to_f32((uint16_t)(q1[i] & 0xffffu));
+      v[8 + 2 * i + 1] = bf16_to_f32((uint16_t)(q1[i] >> 16));
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));  // the other 16 dims of the 32-dim block
+    // exponent of the block maximum (clamped so both scale bytes stay in range)
+    const int e = amax > 0.f ? max(((int)(__float_as_uint(amax) >> 23) & 0xff) - 127, -100) : 0;
+    const float inv_hi = __uint_as_float((uint32_t)(127 - (e - 7)) << 23);  // 2^-(e-7)
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t hp = 0, lp = 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float a = v[4 * i + 2 * j] * inv_hi, c = v[4 * i + 2 * j + 1] * inv_hi;
+        const uint32_t hc = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, c, 0, false) & 0xffffu;
+        const float ra = (a - __builtin_amdgcn_cvt_f32_fp8(hc, 0)) * 16.f;
+        const float rc = (c - __builtin_amdgcn_cvt_f32_fp8(hc, 1)) * 16.f;
+        const uint32_t lc = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ra, rc, 0, false) & 0xffffu;
+        hp |= hc << (16 * j);
+        lp |= lc << (16 * j);
+      }
+      hw[i] = hp;
+      lw[i] = lp;
+    }
+    const int slot = qc ^ (qh & 7);
+    *reinterpret_cast<u32x4_t*>(&sq[qh * 128 + 16 * slot]) = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+    *reinterpret_cast<u32x4_t*>(&sq[64 * 128 + qh * 128 + 16 * slot]) = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+    if ((qc & 1) == 0) {  // one scale byte per 32-dim block: hi 2^(e-7), lo 2^(e-11)
+      reinterpret_cast<uint8_t*>(&sqs[0][qh])[qc >> 1] = (uint8_t)(e + 120);
+      reinterpret_cast<uint8_t*>(&sqs[1][qh])[qc >> 1] = (uint8_t)(e + 116);
+    }
+  }
+  __syncthreads();
+  // A operands: qa[part][hb][s] = row 32hb + n, dims 64s + 16h .. +15 and 64s + 32 + 16h .. +15
+  i32x8_t qa[2][2][2];
+  int qs[2][2][2];
+#pragma unroll
+  for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int r = 32 * hb + n;
+      const uint32_t sc4 = sqs[pt][r];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int c0 = 4 * s2 + h, c1 = 4 * s2 + 2 + h;  // 16-byte chunks
+        const u32x4_t lo4 = *reinterpret_cast<const u32x4_t*>(&sq[pt * 64 * 128 + r * 128 + 16 * (c0 ^ (r & 7))]);
+        const u32x4_t hi4 = *reinterpret_cast<const u32x4_t*>(&sq[pt * 64 * 128 + r * 128 + 16 * (c1 ^ (r & 7))]);
+        qa[pt][hb][s2] = i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                                 (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+        qs[pt][hb][s2] = (int)((sc4 >> (8 * (2 * s2 + h))) & 0xffu);  // block 2s + h
+      }
+    }
+  // every wave holds its A operands before the buffer is reused for the scores
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+
+  // Software pipeline over the 2 * ITERS groups of 32 keys (group g: tile g / 2, keys
+  // 32 (g % 2) ..): the MFMAs of group g + 1 are issued before the epilogue of group g, one
+  // MFMA per eight epilogue instructions, so this wave's VALU work runs while its own next
+  // MFMAs execute. Two accumulator pairs alternate.
+  auto tile_ready = [&](int t) {
+    if (t > 0 && t + kF4Stages - 1 < ITERS) {
+      // stage (t-1) % kF4Stages: its B-operand reads completed before their MFMAs issued
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(t + kF4Stages - 1);
+    }
+    // tile t landed; the tiles after it (up to three) may still be in flight
+    const int after = min(ITERS - 1 - t, kF4Stages - 1);
+    switch (after) {
+      case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+    }
+  };
+  auto mfma_group = [&](int g, f32x16_t& acc0, f32x16_t& acc1) {
+    const char* st = &sk[wv][(g >> 1) % kF4Stages][0];
+    const int r = 32 * (g & 1) + n;
+    // B operands: key r, step s: 16-byte chunk 2s + h of its codes and scale byte 2s + h
+    const u32x4_t b0 = *reinterpret_cast<const u32x4_t*>(st + r * 64 + 16 * ((h) ^ ((r >> 2) & 3)));
+    const u32x4_t b1 = *reinterpret_cast<const u32x4_t*>(st + r * 64 + 16 * ((2 + h) ^ ((r >> 2) & 3)));
+    const uint32_t ks = *reinterpret_cast<const uint32_t*>(st + kF4Tile * 64 + 4 * r);
+    const i32x8_t kb0 = i32x8_t{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], 0, 0, 0, 0};
+    const i32x8_t kb1 = i32x8_t{(int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3], 0, 0, 0, 0};
+    const int ks0 = (int)((ks >> (8 * h)) & 0xffu), ks1 = (int)((ks >> (8 * (2 + h))) & 0xffu);
+    acc0 = f32x16_t{};
+    acc1 = f32x16_t{};
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[pt][0][0], kb0, acc0, 0, 4, 0, qs[pt][0][0], 0, ks0);
+      acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[pt][1][0], kb0, acc1, 0, 4, 0, qs[pt][1][0], 0, ks0);
+      acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[pt][0][1], kb1, acc0, 0, 4, 0, qs[pt][0][1], 0, ks1);
+      acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[pt][1][1], kb1, acc1, 0, 4, 0, qs[pt][1][1], 0, ks1);
+    }
+  };
+  auto epilogue = [&](int g, const f32x16_t& acc0, const f32x16_t& acc1) {
+    float p4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p4[i & 3] += wr[0][i] * relu_bits(acc0[i]);
+      p4[(i + 2) & 3] += wr[1][i] * relu_bits(acc1[i]);
+    }
+    float part = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // both halves: heads 4h.. of every 8
+    if (h == 0) sres[wv][32 * g + n] = part;
+  };
+  f32x16_t accA0, accA1, accB0, accB1;
+  tile_ready(0);
+  mfma_group(0, accA0, accA1);
+#pragma unroll
+  for (int g = 0; g < 2 * ITERS; ++g) {
+    if (g + 1 < 2 * ITERS) {
+      if (((g + 1) & 1) == 0) tile_ready((g + 1) >> 1);
+      if (g & 1) mfma_group(g + 1, accA0, accA1);
+      else mfma_group(g + 1, accB0, accB1);
+    }
+    if (g & 1) epilogue(g, accB0, accB1);
+    else epilogue(g, accA0, accA1);
+    if (g + 1 < 2 * ITERS) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // eight VALU
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < ITERS; ++t) {
+    const int s = tile_key(t) + lane;
+    if (s < nv) srow[s] = sres[wv][kF4Tile * t + lane];
+    else if (fill_masked && s < N) srow[s] = kNegInf;
   }
 }
 
@@ -570,36 +663,17 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
     return hipSuccess;
   }
   if (fast) {
-    // keys per wave: enough work per wave to amortise the q_I fragments, while the grid still
-    // fills the chip (~1024 workgroups)
     const int64_t total = nrows * (int64_t)s.N;
-    int64_t it = total / (32LL * 2048);  // ~2048 waves: two per SIMD
-    int iters = 1;
-    while (iters < kDecodeMaxIters && 2 * iters <= it) iters *= 2;
-    const int keys_per_wg = 4 * 32 * iters;
-    dim3 grid((s.N + keys_per_wg - 1) / keys_per_wg, (unsigned)nrows);
     const uint16_t* qp = static_cast<const uint16_t*>(q_I);
     const uint8_t* kp = static_cast<const uint8_t*>(k_I);
-#define DSA_DEC(F, I)                                                                     \
-  return launch(indexer_decode_mfma<F, I>, grid, 256, 0, st, qp, w, kp, k_scale, q_pos, s.T, \
-                s.N, s.m, qi0, scores, fm)
-#define DSA_DEC_ITERS(F)        \
-  switch (iters) {              \
-    case 1: DSA_DEC(F, 1);      \
-    case 2: DSA_DEC(F, 2);      \
-    case 4: DSA_DEC(F, 4);      \
-    case 8: DSA_DEC(F, 8);      \
-    default: DSA_DEC(F, 16);    \
-  }
     if (k_fmt == FMT_BF16) {
       // 8 waves per workgroup, ~2 tiles per wave: 256 workgroups at 16 x 8192 keys
       int it2 = 1;
       while (it2 < 16 && (int64_t)2 * it2 * 32 * kDecWaves * 256 <= total) it2 *= 2;
       const int kpw = kDecWaves * 32 * it2;
       dim3 g2((s.N + kpw - 1) / kpw, (unsigned)nrows);
-      const uint8_t* kb = static_cast<const uint8_t*>(k_I);
 #define DSA_DMA(I)                                                                          \
-  return launch(indexer_decode_dma<I>, g2, kDecWaves * 64, 0, st, qp, w, kb, q_pos, s.T, s.N, \
+  return launch(indexer_decode_dma<I>, g2, kDecWaves * 64, 0, st, qp, w, kp, q_pos, s.T, s.N, \
                 s.m, qi0, scores, fm)
       switch (it2) {
         case 1: DSA_DMA(1);
@@ -610,9 +684,23 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
       }
 #undef DSA_DMA
     }
-    DSA_DEC_ITERS(FMT_MXFP4)
-#undef DSA_DEC_ITERS
-#undef DSA_DEC
+    {
+      // MXFP4: 8 waves per workgroup, 64-key tiles, ~256 workgroups
+      int it4 = 1;
+      while (it4 < 8 && (int64_t)2 * it4 * kF4Tile * kDecWaves * 256 <= total) it4 *= 2;
+      const int kpw = kDecWaves * kF4Tile * it4;
+      dim3 g4((s.N + kpw - 1) / kpw, (unsigned)nrows);
+#define DSA_F4(I)                                                                              \
+  return launch(indexer_decode_fp4_dma<I>, g4, kDecWaves * 64, 0, st, qp, w, kp, k_scale,      \
+                q_pos, s.T, s.N, s.m, qi0, scores, fm)
+      switch (it4) {
+        case 1: DSA_F4(1);
+        case 2: DSA_F4(2);
+        case 4: DSA_F4(4);
+        default: DSA_F4(8);
+      }
+#undef DSA_F4
+    }
   }
   dim3 grid((s.N + 255) / 256, (unsigned)nrows);
   size_t shm = sizeof(float) * ((size_t)s.H_I * s.D_I + s.H_I);
