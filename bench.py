@@ -43,14 +43,19 @@ WORKLOAD_TEXT = {
     "csa_prefill": "CSA prefill: 131072 raw tokens mean-pooled 4:1 to 32768 blocks, last 8192 "
                    "queries, top-k 1024 + 128-token window, 128 heads, key 576 / value 512",
     "tiny": "tiny fp32 DSA: L=256, 16 queries, indexer 4x32, top-k 64, 8 heads, key 64 / value 48",
+    "hca_decode": "HCA decode: B=4 x 1 query over 1,048,576 tokens compressed 128:1 (8192 blocks), "
+                  "dense attention over every visible block + 128-token raw window, 128 heads, "
+                  "key 576 / value 512 (bf16)",
+    "hca_prefill": "HCA prefill: 131072 raw tokens mean-pooled 128:1 to 1024 blocks, last 8192 "
+                   "queries, dense attention over the visible blocks + 128-token window, 128 heads",
 }
 
 
 def _fused_topk(cfg):
     """dsa_forward selects the top-k inside the attention kernel (bf16 MFMA shapes, N <= 32768,
     at most 128 query rows per chunk; cfg describes one chunk)."""
-    return (cfg.dt == "bf16" and cfg.D_K == 576 and cfg.D_V == 512 and cfg.H % 64 == 0
-            and cfg.N <= 32768 and cfg.B * cfg.T <= 128)
+    return (not cfg.dense and cfg.dt == "bf16" and cfg.D_K == 576 and cfg.D_V == 512
+            and cfg.H % 64 == 0 and cfg.N <= 32768 and cfg.B * cfg.T <= 128)
 
 
 def _kernel_plan(cfg, nsplit):
@@ -58,6 +63,10 @@ def _kernel_plan(cfg, nsplit):
     names = []
     if cfg.compress:
         names.append("compress_mean")
+    mfma = cfg.dt == "bf16" and cfg.D_K == 576 and cfg.D_V == 512 and cfg.H % 64 == 0
+    if cfg.dense:  # HCA: attention over every visible block, no indexer or top-k
+        return names + ["attend_mfma_dma" if mfma else "attend_generic"] + (
+            ["attend_combine"] if nsplit > 1 else [])
     fast = cfg.dt == "bf16" and cfg.H_I == 64 and cfg.D_I == 128
     rows = cfg.B * cfg.T
     if fast and cfg.k_dt == "bf16" and rows >= 64:
@@ -114,7 +123,9 @@ def _algorithmic(cfg, name):
         # each gathered row must cross HBM once per step: once per query at decode, but rows
         # shared by the queries of one sequence (prefill) count once
         rows_kv = min(sel, float(B * N)) + min(win, float(B * (T + cfg.W - 1)) if cfg.W else 0.0)
-        byt = rows_kv * cfg.D_K * esz + rows * cfg.H * cfg.D_K * esz + rows * cfg.top_k * 4
+        byt = rows_kv * cfg.D_K * esz + rows * cfg.H * cfg.D_K * esz
+        if not cfg.dense:
+            byt += rows * cfg.top_k * 4  # the index list (HCA has none)
         if name.startswith("attend_mfma") and _fused_topk(cfg):
             byt += pairs * 4  # the kernel selects the entries from the scores itself
         return byt, ents * cfg.H * (cfg.D_K + cfg.D_V) * 2.0
@@ -166,9 +177,11 @@ def _device_inputs(wl):
     import torch
 
     c = wl.cfg
-    t = {"q_pos": _dev(wl.q_pos()), "q_I": _dev(wl.q_I()), "w": _dev(wl.w())}
-    k = wl.k_I()
-    t["k_I"] = (_dev(k[0]), _dev(k[1])) if c.k_dt == "mxfp4" else _dev(k)
+    t = {"q_pos": _dev(wl.q_pos())}
+    if not c.dense:  # HCA has no indexer
+        t["q_I"], t["w"] = _dev(wl.q_I()), _dev(wl.w())
+        k = wl.k_I()
+        t["k_I"] = (_dev(k[0]), _dev(k[1])) if c.k_dt == "mxfp4" else _dev(k)
     rows = c.B * c.T
     tdt = torch.bfloat16 if c.dt == "bf16" else torch.float32
     q = torch.empty((c.B, c.T, c.H, c.D_K), dtype=tdt, device="cuda")
@@ -187,6 +200,9 @@ def _device_inputs(wl):
 
 
 def _forward(cfg, t, dsa, base):
+    if cfg.dense:
+        return dsa.HcaForward(t["q"], t["kv"], t["q_pos"], cfg.D_V, cfg.softmax_scale, cfg.m,
+                              W=cfg.W, kv_raw=t["kv_raw"], raw_base=base, compress=cfg.compress)
     return dsa.Forward(t["q_I"], t["w"], t["k_I"], t["q"], t["kv"], t["q_pos"], cfg.top_k,
                        cfg.D_V, cfg.softmax_scale, m=cfg.m, W=cfg.W, kv_raw=t["kv_raw"],
                        raw_base=base, compress=cfg.compress)
@@ -208,7 +224,10 @@ def cpu_baseline(cfg, budget_s=20.0):
     t0 = time.perf_counter()
     done = 0
     for b, t in rows:
-        run.run(b, t)
+        if cfg.dense:
+            run.run_dense(b, t)
+        else:
+            run.run(b, t)
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -253,7 +272,8 @@ def main():
     print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     # input copies so that one cycle touches > 512 MB
-    touched = sum(_algorithmic(cfg, k)[0] for k in ("indexer_x", "attend_mfma_dma"))
+    touched = sum(_algorithmic(cfg, k)[0] for k in
+                  (("attend_mfma_dma",) if cfg.dense else ("indexer_x", "attend_mfma_dma")))
     R = args.rotate or max(1, min(16, int(512e6 // max(touched, 1.0)) + 1))
     if cfg.B * cfg.T > 64:
         R = args.rotate or 1
@@ -269,7 +289,8 @@ def main():
     n_chunks = -(-rows // chunk_rows)
     d = dsa.dims(B=1, T=chunk_rows, N=cfg.N, H_I=cfg.H_I, D_I=cfg.D_I, H=cfg.H, D_K=cfg.D_K,
                  D_V=cfg.D_V, top_k=cfg.top_k, m=cfg.m, W=cfg.W)
-    split = dsa.workspace_bytes(d, dsa.OP_ATTEND) > 0  # the attention splits its entry list
+    # the attention splits its entry list
+    split = dsa.workspace_bytes(d, dsa.OP_HCA if cfg.dense else dsa.OP_ATTEND) > 0
     per_chunk = _kernel_plan(cfg.with_(compress=False, B=1, T=chunk_rows), 2 if split else 1)
     kernels = (["compress_mean"] if cfg.compress else []) + per_chunk * n_chunks
 

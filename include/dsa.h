@@ -7,6 +7,8 @@
  *   3. sparse_mla_attend MQA-mode latent attention over the selected entries (+ raw window)
  *   0. kv_compress_mean  optional CSA step: mean-pool every m raw KV rows into one entry
  *   *  dsa_forward       0 -> 1 -> 2 -> 3 on one stream, with scores/idx kept in a workspace
+ *   *  hca_forward       heavily compressed attention: 0 -> dense attention over every visible
+ *                        compressed entry (+ raw window); no indexer, no selection
  *
  * Sources (web pages on the method; no code exists on them):
  *   [P5] "DeepSeek-V3.2 sparse-attention principle and TPU adaptation" (trdm.cn news 392380):
@@ -86,6 +88,9 @@ typedef struct dsa_dims {
 #define DSA_OP_TOPK 1
 #define DSA_OP_ATTEND 2
 #define DSA_OP_FORWARD 3
+#define DSA_OP_HCA 4
+/* hca_forward: compressed entries plus window rows one query attends over (N + W) */
+#define DSA_MAX_HCA_ENTRIES 10240
 
 /* Human-readable name of a status code; never NULL. */
 const char* dsa_status_str(int status);
@@ -194,6 +199,23 @@ typedef struct dsa_forward_args {
  * When a->scores is NULL, queries are processed in chunks whose scores fit the workspace.
  * ws: dsa_workspace_bytes(d, DSA_OP_FORWARD) bytes. Graph-capturable (no sync, no alloc). */
 dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Heavily compressed attention, HCA ([P4] Tencent Cloud CSA/HCA snippets: the second,
+ * heavier compression of DeepSeek-V4 -- ratio m' = 128 against CSA's m = 4 -- runs dense
+ * attention on the compressed sequence, with no sparse selection; the CSA snippets concatenate
+ * the sliding-window KV with the compressed KV, and the same window is offered here, W >= 0).
+ * For each (b,t,h), with p = q_pos[b,t] and n = n_vis = min(N, floor((p+1)/m)):
+ *   E = { kv[b, j, :] : 0 <= j < n } u { the raw window rows of sparse_mla_attend },
+ * one joint softmax over E as in sparse_mla_attend. a->compress != 0 first writes
+ * kv = kv_compress_mean(kv_raw) (needs raw_base == 0, floor(n_raw / m) == N).
+ * Uses from `a`: dt (F32 or BF16), q, kv, kv_raw, raw_base, n_raw, compress, q_pos,
+ * softmax_scale, out, lse, events / n_events (kernel order: [compress,] attention[, split
+ * combine]); the indexer fields (q_I, w, k_I, k_scale, k_dt, scores, idx) are ignored, and so
+ * are d->top_k, d->H_I and d->D_I. Needs N + W <= DSA_MAX_HCA_ENTRIES (DSA_ERR_SHAPE otherwise).
+ * ws: dsa_workspace_bytes(d, DSA_OP_HCA) bytes (split partials for few-query calls; may be 0).
+ * Graph-capturable (no sync, no alloc). */
+dsa_status hca_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, size_t ws_bytes,
                        void* stream);
 
 #ifdef __cplusplus

@@ -27,10 +27,10 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 F32, BF16, MXFP4 = 0, 1, 2
-OP_TOPK, OP_ATTEND, OP_FORWARD = 1, 2, 3
+OP_TOPK, OP_ATTEND, OP_FORWARD, OP_HCA = 1, 2, 3, 4
 
 EXPORTS = ("dsa_status_str", "dsa_version", "dsa_workspace_bytes", "kv_compress_mean",
-           "indexer_scores", "topk_select", "sparse_mla_attend", "dsa_forward")
+           "indexer_scores", "topk_select", "sparse_mla_attend", "dsa_forward", "hca_forward")
 
 
 class Dims(ctypes.Structure):
@@ -63,8 +63,9 @@ _lib.topk_select.argtypes = [_D, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.sparse_mla_attend.argtypes = [_D, ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
                                    ctypes.c_float, _vp, _vp, _vp, _sz, _vp]
 _lib.dsa_forward.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]
+_lib.hca_forward.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]
 for _f in ("kv_compress_mean", "indexer_scores", "topk_select", "sparse_mla_attend",
-           "dsa_forward"):
+           "dsa_forward", "hca_forward"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -257,5 +258,45 @@ def dsa_forward(q_I, w, k_I: KeyT, q, kv, q_pos, top_k: int, D_V: int, softmax_s
                 **kw):
     """[compress] -> indexer -> top-k -> sparse attention. Returns (out, lse, forward)."""
     f = Forward(q_I, w, k_I, q, kv, q_pos, top_k, D_V, softmax_scale, **kw)
+    f.run()
+    return f.out, f.lse, f
+
+
+# ---- heavily compressed attention -------------------------------------------------------------
+
+class HcaForward(Forward):
+    """A prepared hca_forward call: [compress] -> dense attention over every visible compressed
+    entry (+ raw window). ``run()`` is a single C call."""
+
+    def __init__(self, q, kv, q_pos, D_V: int, softmax_scale: float, m: int, W: int = 0,
+                 kv_raw=None, raw_base: int = 0, compress: bool = False, out=None, lse=None,
+                 want_lse: bool = True):
+        B, T, H, D_K = q.shape
+        N = kv.shape[1]
+        self.d = dims(B=B, T=T, N=N, H=H, D_K=D_K, D_V=D_V, m=m, W=W)
+        dev = q.device
+        self.out = out if out is not None else torch.empty((B, T, H, D_V), dtype=q.dtype, device=dev)
+        self.lse = lse if lse is not None else (
+            torch.empty((B, T, H), dtype=torch.float32, device=dev) if want_lse else None)
+        self.scores = self.idx = None
+        self.ws = _workspace(self.d, OP_HCA, dev)
+        self._keep = (q, kv, q_pos, kv_raw)
+        n_raw = 0 if kv_raw is None else kv_raw.shape[1]
+        self.args = ForwardArgs(_dt(q), _dt(q), None, None, None, None, _ptr(q), _ptr(kv),
+                                _ptr(kv_raw), raw_base, n_raw, 1 if compress else 0,
+                                _ptr(q_pos), softmax_scale, _ptr(self.out), _ptr(self.lse),
+                                None, None, None, 0)
+        self.device = dev
+
+    def run(self, stream: Optional[int] = None) -> torch.Tensor:
+        st = torch.cuda.current_stream(self.device).cuda_stream if stream is None else stream
+        _check(_lib.hca_forward(ctypes.byref(self.d), ctypes.byref(self.args), _ptr(self.ws),
+                                0 if self.ws is None else self.ws.numel(), st), "hca_forward")
+        return self.out
+
+
+def hca_forward(q, kv, q_pos, D_V: int, softmax_scale: float, m: int, **kw):
+    """[compress] -> dense attention over every visible compressed entry. Returns (out, lse, f)."""
+    f = HcaForward(q, kv, q_pos, D_V, softmax_scale, m, **kw)
     f.run()
     return f.out, f.lse, f

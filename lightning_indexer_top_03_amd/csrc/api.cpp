@@ -123,6 +123,25 @@ FwdLayout forward_layout(const dsa_dims* d, dsa_dtype dt) {
   return L;
 }
 
+// HCA: the dims rules of the other calls except top_k (unused: every visible entry takes part),
+// and a bound on the entries one query attends over.
+dsa_status check_hca_dims(const dsa_dims* d) {
+  if (!d) return DSA_ERR_NULL;
+  dsa_dims c = *d;
+  c.top_k = 1;
+  if (dsa_status st = check_dims(&c)) return st;
+  if ((int64_t)d->N + d->W > DSA_MAX_HCA_ENTRIES) return DSA_ERR_SHAPE;
+  return DSA_OK;
+}
+
+// The attention kernels see HCA as "top_k = N entries with no index list" (idx == nullptr):
+// entry j < N is compressed entry j itself, masked from n_vis on.
+Shape hca_shape(const dsa_dims* d) {
+  Shape s = to_shape(d);
+  s.top_k = d->N;
+  return s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,6 +163,12 @@ const char* dsa_status_str(int status) {
 int dsa_version(void) { return 100; }
 
 size_t dsa_workspace_bytes(const dsa_dims* d, int op) {
+  if (op == DSA_OP_HCA) {
+    if (check_hca_dims(d) != DSA_OK) return 0;
+    const Shape s = hca_shape(d);
+    const int64_t rows = (int64_t)d->B * d->T;
+    return std::max(attend_ws_bytes(s, rows, FMT_BF16), attend_ws_bytes(s, rows, FMT_F32));
+  }
   if (check_dims(d) != DSA_OK) return 0;
   const Shape s = to_shape(d);
   const int64_t rows = (int64_t)d->B * d->T;
@@ -281,6 +306,42 @@ dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
     }
   }
   return DSA_OK;
+}
+
+dsa_status hca_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (dsa_status st = check_hca_dims(d)) return st;
+  if (!a) return DSA_ERR_NULL;
+  if (!fmt_ok(a->dt)) return DSA_ERR_DTYPE;
+  if (!a->q || !a->kv || !a->q_pos || !a->out) return DSA_ERR_NULL;
+  if ((d->W > 0 || a->compress) && !a->kv_raw) return DSA_ERR_NULL;
+  if (a->raw_base < 0 || a->n_raw < 0) return DSA_ERR_SHAPE;
+  if (a->compress && (a->raw_base != 0 || a->n_raw / d->m != d->N)) return DSA_ERR_SHAPE;
+  const Shape s = hca_shape(d);
+  const int fmt = a->dt == DSA_BF16 ? FMT_BF16 : FMT_F32;
+  if (fmt == FMT_F32 || !(s.D_K == 576 && s.D_V == 512 && s.H % 64 == 0)) {
+    // the scalar kernel keeps a query's logits and row pointers in LDS
+    dsa_dims c = *d;
+    c.top_k = d->N;
+    if (dsa_status st = check_attend_shape(&c)) return st;
+  }
+  const void* ptrs16[] = {a->q, a->kv, a->out, a->kv_raw, ws};
+  for (const void* p : ptrs16)
+    if (p && !aligned16(p)) return DSA_ERR_ALIGN;
+  const int64_t rows = (int64_t)d->B * d->T;
+  const size_t need = attend_ws_bytes(s, rows, fmt);
+  if (need && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (a->n_events < 0) return DSA_ERR_SHAPE;
+  if (dsa_status st = check_device()) return st;
+  hipStream_t st = (hipStream_t)stream;
+  TimerScope timer(a->events, a->n_events);
+  if (a->compress) {
+    if (hipError_t e = launch_compress(d->B, a->n_raw, d->D_K, d->m, fmt, a->kv_raw, a->kv, st))
+      return launched(e);
+  }
+  return launched(launch_attend(s, 0, rows, fmt, a->q, a->kv, nullptr,
+                                d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw, a->q_pos,
+                                a->softmax_scale, a->out, a->lse, ws, st));
 }
 
 }  // extern "C"

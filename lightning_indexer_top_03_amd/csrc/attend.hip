@@ -30,15 +30,17 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTile = 32;       // entries per tile
 constexpr float kRefSlack = 8.f;  // log2 headroom of the lazily moved softmax reference
 
-// Source row of entry e of query (b, p); returns nullptr for a masked entry.
+// Source row of entry e of query (b, p); returns nullptr for a masked entry. idxrow == nullptr:
+// every visible entry (entry e < top_k is entry e itself when e < lim = n_vis), else entries
+// come from idxrow (lim = N).
 template <typename T>
 __device__ __forceinline__ const T* entry_row(int e, const int32_t* __restrict__ idxrow, int top_k,
                                               const T* __restrict__ kv, int b, int N, int DK,
                                               const T* __restrict__ kv_raw, int64_t raw_base,
-                                              int64_t n_raw, int p, int W) {
+                                              int64_t n_raw, int p, int W, int lim) {
   if (e < top_k) {
-    int j = idxrow[e];
-    if (j < 0 || j >= N) return nullptr;
+    int j = idxrow != nullptr ? idxrow[e] : e;
+    if (j < 0 || j >= lim) return nullptr;
     return kv + ((size_t)b * N + j) * DK;
   }
   int64_t r = (int64_t)p - W + 1 + (e - top_k);
@@ -47,13 +49,13 @@ __device__ __forceinline__ const T* entry_row(int e, const int32_t* __restrict__
 }
 
 // Entry codes: >= 0 a row of kv (within the sequence), <= -2 a raw window row (-code-2 within
-// kv_raw's rows of the sequence), -1 masked.
+// kv_raw's rows of the sequence), -1 masked. idxrow == nullptr and lim as in entry_row.
 __device__ __forceinline__ int entry_code(int e, const int32_t* __restrict__ idxrow, int top_k,
-                                          int N, int64_t raw_base, int64_t n_raw, int p, int W,
+                                          int lim, int64_t raw_base, int64_t n_raw, int p, int W,
                                           bool has_raw) {
   if (e < top_k) {
-    const int j = idxrow[e];
-    return (j >= 0 && j < N) ? j : -1;
+    const int j = idxrow != nullptr ? idxrow[e] : e;
+    return (j >= 0 && j < lim) ? j : -1;
   }
   const int64_t r = (int64_t)p - W + 1 + (e - top_k);
   if (!has_raw || r < 0 || r < raw_base || r >= raw_base + n_raw) return -1;
@@ -211,7 +213,9 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
   const int e_end = min(E, e_begin + per_split);
   const int ntiles = e_end > e_begin ? (e_end - e_begin + kTile - 1) / kTile : 0;
   const int ncode = ntiles * kTile;
-  const int32_t* __restrict__ idxrow = idx + row * (int64_t)top_k;
+  // idx == nullptr: every visible entry takes part (dense attention over the compressed
+  // sequence, no selection)
+  const int32_t* __restrict__ idxrow = idx != nullptr ? idx + row * (int64_t)top_k : nullptr;
 
   // q fragments (score waves): lane (head n, group g) holds q[h0+n][32kk + 8g .. +7]
   u32x4_t qf[KS];
@@ -234,21 +238,24 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     // address) and, on the score waves, the q loads are all issued before the first wait.
     int raw[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) raw[j] = idxrow[min(e_begin + tid + j * kAtWaves * 64, top_k - 1)];
+    for (int j = 0; j < 2; ++j)
+      raw[j] = idxrow != nullptr ? idxrow[min(e_begin + tid + j * kAtWaves * 64, top_k - 1)]
+                                 : e_begin + tid + j * kAtWaves * 64;
     load_q();
     const int p = q_pos[qi];
+    const int lim = idxrow != nullptr ? N : n_visible(p, m, N);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       asm volatile("" : "+v"(raw[j]));  // keep the reads above, not sunk into the branches below
       const int i = tid + j * kAtWaves * 64;
       const int e = e_begin + i;
       int code = -1;
-      if (e < e_end) code = e < top_k ? ((raw[j] >= 0 && raw[j] < N) ? raw[j] : -1) : window_code(e, p);
+      if (e < e_end) code = e < top_k ? ((raw[j] >= 0 && raw[j] < lim) ? raw[j] : -1) : window_code(e, p);
       if (i < ncode) scode[i] = code;
     }
     for (int i = tid + 2 * kAtWaves * 64; i < ncode; i += kAtWaves * 64) {
       const int e = e_begin + i;
-      scode[i] = e < e_end ? entry_code(e, idxrow, top_k, N, raw_base, n_raw, p, W, kv_raw != nullptr)
+      scode[i] = e < e_end ? entry_code(e, idxrow, top_k, lim, raw_base, n_raw, p, W, kv_raw != nullptr)
                            : -1;
     }
   } else {
@@ -667,7 +674,7 @@ __global__ __launch_bounds__(256) void attend_generic(
     const T* __restrict__ q, const T* __restrict__ kv, const int32_t* __restrict__ idx,
     const T* __restrict__ kv_raw, int64_t raw_base, int64_t n_raw,
     const int32_t* __restrict__ q_pos, int T_, int N, int H, int DK, int DV, int top_k, int W,
-    float scale, int64_t qi0, T* __restrict__ out, float* __restrict__ lse) {
+    float scale, int64_t qi0, T* __restrict__ out, float* __restrict__ lse, int m) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int E = top_k + W;
   float* sq = reinterpret_cast<float*>(smem);   // [DK]
@@ -679,12 +686,13 @@ __global__ __launch_bounds__(256) void attend_generic(
   const int64_t qi = qi0 + row;
   const int b = (int)(qi / T_);
   const int p = q_pos[qi];
-  const int32_t* idxrow = idx + row * (int64_t)top_k;
+  const int32_t* idxrow = idx != nullptr ? idx + row * (int64_t)top_k : nullptr;
+  const int lim = idx != nullptr ? N : n_visible(p, m, N);
   for (int d = threadIdx.x; d < DK; d += blockDim.x) sq[d] = ldv(q, ((size_t)qi * H + h) * DK + d);
   __syncthreads();
   float mx = kNegInf;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const T* src = entry_row<T>(e, idxrow, top_k, kv, b, N, DK, kv_raw, raw_base, n_raw, p, W);
+    const T* src = entry_row<T>(e, idxrow, top_k, kv, b, N, DK, kv_raw, raw_base, n_raw, p, W, lim);
     ssrc[e] = src;
     float z = kNegInf;
     if (src) {
@@ -857,11 +865,11 @@ hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, co
     return launch(attend_generic<uint16_t>, grid, 256, shm, st, static_cast<const uint16_t*>(q),
                   static_cast<const uint16_t*>(kv), idx, static_cast<const uint16_t*>(kv_raw),
                   raw_base, n_raw, q_pos, s.T, s.N, s.H, s.D_K, s.D_V, s.top_k, s.W, scale, qi0,
-                  static_cast<uint16_t*>(out), lse);
+                  static_cast<uint16_t*>(out), lse, s.m);
   return launch(attend_generic<float>, grid, 256, shm, st, static_cast<const float*>(q),
                 static_cast<const float*>(kv), idx, static_cast<const float*>(kv_raw), raw_base,
                 n_raw, q_pos, s.T, s.N, s.H, s.D_K, s.D_V, s.top_k, s.W, scale, qi0,
-                static_cast<float*>(out), lse);
+                static_cast<float*>(out), lse, s.m);
 }
 
 }  // namespace dsa

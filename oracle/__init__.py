@@ -192,6 +192,15 @@ def attend_row(q: np.ndarray, kv: Optional[np.ndarray], idx: np.ndarray, D_V: in
     return out, lse
 
 
+def dense_entries(n_visible: int, N: int) -> np.ndarray:
+    """Entry list of heavily compressed attention (HCA; Tencent Cloud CSA/HCA snippets: the
+    compressed sequence is attended densely, with no sparse selection): every visible
+    compressed entry, 0 .. n_visible-1, padded with -1 to N (at least one slot)."""
+    idx = np.full(max(int(N), 1), -1, np.int32)
+    idx[: int(n_visible)] = np.arange(int(n_visible), dtype=np.int32)
+    return idx
+
+
 def max_threads() -> int:
     return int(lib().orc_max_threads())
 
@@ -250,6 +259,14 @@ class QueryRunner:
         idx, cnt = topk_row(sc, nv, c.top_k)
         out, lse = self.attend(b, t, idx)
         return dict(scores=sc, idx=idx, count=cnt, out=out, lse=lse, n_vis=nv, p=p)
+
+    def run_dense(self, b: int, t: int) -> Dict[str, np.ndarray]:
+        """HCA: attention over every visible compressed entry (+ the raw window)."""
+        c = self.cfg
+        p = int(self.wl.q_pos()[b, t])
+        nv = n_vis(p, c.m, c.N)
+        out, lse = self.attend(b, t, dense_entries(nv, c.N))
+        return dict(out=out, lse=lse, n_vis=nv, p=p)
 
     def run_many(self, queries: Sequence[Tuple[int, int]]):
         return [self.run(b, t) for (b, t) in queries]

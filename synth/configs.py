@@ -13,6 +13,11 @@ Recipes (all seeded; seed = workload id, "sharp" variants use seed 100 + id):
   csa_decode   B=4 T=1 N=262144 blocks of a 1,048,576-token context; k_I MXFP4 of N(0,1);
             q_I bf16; kv_c ~ N(0,1)/48 (the law of a 4-token mean of N(0,1)/24); the 128 raw
             window rows ~ N(0,1)/24; position 1048575; k=1024; W=128
+  hca_decode   B=4 T=1 N=8192 blocks of a 1,048,576-token context compressed 128:1 (HCA: no
+            indexer, every visible block attends); kv_c ~ N(0,1)/(24 sqrt(128)) (the law of a
+            128-token mean of N(0,1)/24); the 128 raw window rows ~ N(0,1)/24; position 1048575
+  hca_prefill  raw 131072 tokens (kv_raw ~ N(0,1)/24) -> m=128 -> N=1024 blocks; last 8192
+            queries (positions 122880..131071); W=128
   sharp variants: q, kv ~ N(0,1) and softmax scale 4/sqrt(D_K), so that attention outputs are
             O(1) and a wrong gather moves them by far more than the tolerance.
 """
@@ -54,6 +59,7 @@ class Config:
     raw_base: int = 0
     kv_std: float = 0.0       # std of stored kv entries (0 -> qkv_std)
     win_std: float = 0.0      # std of raw window rows (0 -> qkv_std)
+    dense: bool = False       # HCA: no indexer / top-k, every visible entry attends
 
     @property
     def softmax_scale(self) -> float:
@@ -73,7 +79,8 @@ class Config:
 
     def sharp(self) -> "Config":
         """Same shapes, q and kv ~ N(0,1), softmax scale 4/sqrt(D_K)."""
-        kv = 0.5 if self.kv_std else 0.0  # a 4-token mean of N(0,1) has std 1/2
+        # pooled entries keep their ratio to the raw rows (a 4-token mean of N(0,1) has std 1/2)
+        kv = self.kv_std / self.q_std if self.kv_std else 0.0
         return dataclasses.replace(self, name=self.name + "_sharp", seed=100 + self.seed,
                                    qkv_std=1.0, scale=4.0 / math.sqrt(self.D_K), kv_std=kv,
                                    win_std=1.0 if self.win_std else 0.0)
@@ -104,6 +111,13 @@ CONFIGS: Dict[str, Config] = {
     "csa_decode": Config("csa_decode", 5, B=4, T=1, N=262144, H_I=64, D_I=128, H=128, D_K=576,
                          D_V=512, top_k=1024, m=4, W=128, k_dt="mxfp4", pos0=1048575,
                          n_raw=128, raw_base=1048576 - 128, kv_std=1.0 / 48, win_std=1.0 / 24),
+    "hca_decode": Config("hca_decode", 6, B=4, T=1, N=8192, H_I=64, D_I=128, H=128, D_K=576,
+                         D_V=512, top_k=8192, m=128, W=128, pos0=1048575, n_raw=128,
+                         raw_base=1048576 - 128, kv_std=1.0 / (24 * math.sqrt(128)),
+                         win_std=1.0 / 24, dense=True),
+    "hca_prefill": Config("hca_prefill", 7, B=1, T=8192, N=1024, H_I=64, D_I=128, H=128,
+                          D_K=576, D_V=512, top_k=1024, m=128, W=128, pos0=122880,
+                          compress=True, n_raw=131072, dense=True),
 }
 
 

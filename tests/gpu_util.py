@@ -54,10 +54,11 @@ class DeviceWorkload:
         self.wl, self.cfg = wl, c
         t0 = time.time()
         self.q_pos = to_dev(wl.q_pos())
-        self.q_I = to_dev(wl.q_I())
-        self.w = to_dev(wl.w())
-        k = wl.k_I()
-        self.k_I = (to_dev(k[0]), to_dev(k[1])) if c.k_dt == "mxfp4" else to_dev(k)
+        if not c.dense:  # HCA has no indexer
+            self.q_I = to_dev(wl.q_I())
+            self.w = to_dev(wl.w())
+            k = wl.k_I()
+            self.k_I = (to_dev(k[0]), to_dev(k[1])) if c.k_dt == "mxfp4" else to_dev(k)
         rows = c.B * c.T
         if rows * c.H * c.D_K > (1 << 28):
             # generate q in chunks straight into the device tensor
@@ -90,6 +91,13 @@ class DeviceWorkload:
                         c.softmax_scale, m=c.m, W=c.W, kv_raw=self.kv_raw,
                         raw_base=self.raw_base, compress=c.compress, scores=scores, idx=idx)
         return f
+
+
+    def hca(self):
+        import lightning_indexer_top_03_amd as dsa
+        c = self.cfg
+        return dsa.HcaForward(self.q, self.kv, self.q_pos, c.D_V, c.softmax_scale, c.m, W=c.W,
+                              kv_raw=self.kv_raw, raw_base=self.raw_base, compress=c.compress)
 
 
 def check_scores(gpu: np.ndarray, ref: np.ndarray, n_vis: int, full_row: bool = True, what=""):
@@ -142,6 +150,25 @@ def check_attention(gpu_out: np.ndarray, gpu_lse, ref_out: np.ndarray, ref_lse, 
             le = float(np.abs(gpu_lse[fin] - ref_lse[fin]).max())
             assert le <= LSE_ABS, f"{what}: lse error {le}"
     return mx, scale
+
+
+def check_compressed(dw, run) -> None:
+    """Chained check of a call that compresses kv_raw itself: the GPU's pooled entries must lie
+    within one bf16 ulp of the oracle's fp64 means (rounding a mean to the stored dtype is the
+    only difference the step allows), and the runner then attends over those validated bytes,
+    so the attention comparison is not charged with the storage rounding of the cache."""
+    c = dw.cfg
+    for b in range(c.B):
+        ref = oracle.compress_mean(dw.wl.kv_raw()[b], c.m)
+        got = to_host(dw.kv[b])
+        got = oracle.decode(got) if c.dt == "bf16" else got.astype(np.float64)
+        if c.dt == "bf16":
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+            assert (np.abs(got - ref) <= ulp).all(), f"{c.name} b={b}: compressed entries"
+        else:
+            mag = oracle.compress_mean(np.abs(dw.wl.kv_raw()[b]).astype(np.float32), c.m)
+            assert (np.abs(got - ref) <= 2.0 ** -20 * mag + 1e-30).all(), f"{c.name} b={b}"
+        run._kvc[b] = got
 
 
 def bf16_decode(a: np.ndarray) -> np.ndarray:

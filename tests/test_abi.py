@@ -115,6 +115,29 @@ def test_forward_validation_and_workspace():
     assert L.dsa_forward(ctypes.byref(d), ctypes.byref(a), P, need, None) == 4
 
 
+def test_hca_validation_and_workspace():
+    # the indexer fields are ignored (NULL here); top_k plays no part
+    a = dsa.ForwardArgs(dsa.BF16, dsa.BF16, None, None, None, None, P, P, None, 0, 0, 0, P, 0.1,
+                        P, None, None, None, None, 0)
+    dec = _dims(B=2, T=1, N=8192, H=128, D_K=576, D_V=512, top_k=1, m=128, W=128)
+    assert L.dsa_workspace_bytes(ctypes.byref(dec), dsa.OP_HCA) > 0  # few rows: split partials
+    many = _dims(B=1, T=4096, N=1024, H=128, D_K=576, D_V=512, top_k=99999, m=128, W=128)
+    assert L.dsa_workspace_bytes(ctypes.byref(many), dsa.OP_HCA) == 0
+    need = L.dsa_workspace_bytes(ctypes.byref(dec), dsa.OP_HCA)
+    assert L.hca_forward(ctypes.byref(dec), None, P, need, None) == 1
+    assert L.hca_forward(ctypes.byref(dec), ctypes.byref(a), P, need, None) == 1  # W > 0, no kv_raw
+    a.kv_raw, a.n_raw = P, 128
+    assert L.hca_forward(ctypes.byref(dec), ctypes.byref(a), None, 0, None) == 5
+    assert L.hca_forward(ctypes.byref(dec), ctypes.byref(a), P, need - 1, None) == 5
+    too_many = _dims(B=2, T=1, N=10240, H=128, D_K=576, D_V=512, m=128, W=1)
+    assert L.hca_forward(ctypes.byref(too_many), ctypes.byref(a), P, 1 << 30, None) == 2
+    assert L.dsa_workspace_bytes(ctypes.byref(too_many), dsa.OP_HCA) == 0
+    a.compress = 1  # compression needs raw_base == 0 and n_raw / m == N
+    assert L.hca_forward(ctypes.byref(dec), ctypes.byref(a), P, need, None) == 2
+    a.compress, a.q = 0, P + 4
+    assert L.hca_forward(ctypes.byref(dec), ctypes.byref(a), P, need, None) == 4
+
+
 def test_compress_validation():
     d = _dims(m=4)
     assert L.kv_compress_mean(ctypes.byref(d), dsa.BF16, None, 400, P, None) == 1

@@ -11,7 +11,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import (check_attention, check_scores, check_topk, log, to_dev, to_host)
+from gpu_util import (DeviceWorkload, check_attention, check_compressed, check_scores,
+                      check_topk, log, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -243,3 +244,45 @@ def test_attend_all_masked_row_gives_zero():
     torch.cuda.synchronize()
     assert (to_host(out.float()) == 0).all()
     assert np.isneginf(to_host(lse)).all()
+
+
+# ------------------------------------------------------------ heavily compressed attention ----
+
+def _hca_case(c):
+    wl = synth.make_workload(c)
+    dw = DeviceWorkload(wl)
+    f = dw.hca()
+    log(f"[hca {c.name}] B={c.B} T={c.T} N={c.N} m={c.m} W={c.W} dt={c.dt} compress={c.compress}")
+    f.run()
+    torch.cuda.synchronize()
+    run = oracle.QueryRunner(wl)
+    if c.compress:
+        check_compressed(dw, run)
+    for b in range(c.B):
+        for t in range(c.T):
+            r = run.run_dense(b, t)
+            out = to_host(f.out[b, t])
+            out = oracle.decode(out) if c.dt == "bf16" else out.astype(np.float64)
+            check_attention(out, to_host(f.lse[b, t]), r["out"], r["lse"],
+                            what=f"hca {c.name} b={b} t={t} n_vis={r['n_vis']}")
+    del f, dw
+
+
+def test_hca_ragged_window_and_compress():
+    base = synth.CONFIGS["hca_decode"]
+    # stored blocks; positions from before the first complete block (window only) to past N
+    _hca_case(base.with_(B=2, T=7, N=300, m=8, pos0=3, pos_stride=397, raw_base=0, n_raw=2386,
+                         name="hca_small").sharp())
+    # few rows split the entry list; many rows do not
+    _hca_case(base.with_(B=1, T=3, N=2900, m=8, W=0, pos0=8 * 2900 - 3, n_raw=0, raw_base=0,
+                         name="hca_nowin"))
+    # blocks produced from raw rows in the same call, 140 query rows; the sharp variant has no
+    # window: with one, its N(0,1) raw rows outweigh the 16-token means and the outputs reach
+    # ~4, where bf16 output rounding alone (up to 1.6e-2) uses up most of the 2e-2 bound
+    hp = synth.CONFIGS["hca_prefill"].with_(T=140, N=40, m=16, pos0=16 * 40 - 140, n_raw=640,
+                                            name="hca_compress")
+    _hca_case(hp)
+    _hca_case(hp.with_(W=0).sharp())
+    # fp32 (scalar kernel)
+    _hca_case(base.with_(B=2, T=5, N=77, m=4, H=8, D_K=64, D_V=48, dt="f32", k_dt="f32",
+                         pos0=1, pos_stride=71, raw_base=0, n_raw=300, name="hca_f32"))

@@ -11,7 +11,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import (DeviceWorkload, check_attention, check_scores, check_topk, log, to_host)
+from gpu_util import (DeviceWorkload, check_attention, check_compressed, check_scores,
+                      check_topk, log, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -149,3 +150,36 @@ def test_fused_selection_csa_window():
                                           raw_base=p0 - 127, n_raw=203 * 39 + 128,
                                           name="fused_csa")
     _run_fused(c)
+
+
+# ------------------------------------------------------------ heavily compressed attention ----
+
+def _run_hca(c, n_sample=16):
+    """hca_forward against the oracle's dense composition (every visible block + window)."""
+    wl = synth.make_workload(c)
+    dw = DeviceWorkload(wl)
+    f = dw.hca()
+    log(f"[{c.name}] hca_forward B={c.B} T={c.T} N={c.N} m={c.m} W={c.W} compress={c.compress}")
+    f.run()
+    torch.cuda.synchronize()
+    run = oracle.QueryRunner(wl)
+    if c.compress:
+        check_compressed(dw, run)
+    worst = (0.0, 0.0)
+    for b, t in _sample_rows(c, n_sample):
+        r = run.run_dense(b, t)
+        out = oracle.decode(to_host(f.out[b, t]))
+        worst = max(worst, check_attention(out, to_host(f.lse[b, t]), r["out"], r["lse"],
+                                           what=f"{c.name} b={b} t={t} n_vis={r['n_vis']}"))
+    log(f"[{c.name}] attention max abs err {worst[0]:.3e} (max|ref| {worst[1]:.3e})")
+    del f, dw
+
+
+def test_hca_decode():
+    _run_hca(synth.CONFIGS["hca_decode"])
+    _run_hca(synth.CONFIGS["hca_decode"].sharp())
+
+
+def test_hca_prefill():
+    _run_hca(synth.CONFIGS["hca_prefill"], n_sample=12)
+    _run_hca(synth.CONFIGS["hca_prefill"].with_(T=1024, pos0=131072 - 1024).sharp(), n_sample=12)

@@ -292,6 +292,40 @@ def test_h3_csa_golden():
         assert out[0, 0] == pytest.approx(case["out"], abs=1e-14), case
 
 
+def test_h5_hca_golden():
+    g = _load("h5_hca.json")
+    raw = np.array(g["kv_raw"], np.float64)
+    comp = oracle.compress_mean(raw, g["m"])
+    np.testing.assert_allclose(comp, np.array(g["compressed"]), rtol=0, atol=1e-15)
+    for case in g["cases"]:
+        nv = oracle.n_vis(case["p"], g["m"], comp.shape[0])
+        assert nv == case["n_vis"]
+        idx = oracle.dense_entries(nv, comp.shape[0])
+        assert list(idx[:nv]) == list(range(nv)) and (idx[nv:] == -1).all()
+        out, lse = oracle.attend_row(np.array(g["q"]), comp, idx, g["D_V"], g["scale"],
+                                     p=case["p"], W=case["W"], kv_raw=raw, raw_base=0)
+        assert out[0, 0] == pytest.approx(case["out"], abs=1e-12), case
+        if nv == 0 and case["W"] == 0:
+            assert lse[0] == -np.inf
+
+
+def test_hca_reduces_to_dense_attention_over_compressed_sequence():
+    """HCA with no window = causal MQA attention over the mean-pooled sequence (torch SDPA, fp64),
+    masked to the complete blocks."""
+    rng = np.random.default_rng(12)
+    H, D_K, D_V, m, n_raw = 5, 24, 16, 8, 203
+    raw = rng.standard_normal((n_raw, D_K))
+    comp = raw[: n_raw // m * m].reshape(-1, m, D_K).mean(axis=1)  # pooling written out here
+    N = comp.shape[0]
+    for p in (7, 8, 100, n_raw - 1):
+        q = rng.standard_normal((H, D_K))
+        nv = oracle.n_vis(p, m, N)
+        out, _ = oracle.attend_row(q, oracle.compress_mean(raw, m),
+                                   oracle.dense_entries(nv, N), D_V, 0.4)
+        mask = np.arange(N) < (p + 1) // m
+        np.testing.assert_allclose(out, _dense_sdpa(q, comp, D_V, 0.4, mask), rtol=1e-12, atol=1e-12)
+
+
 def test_compress_identity_constant_and_mean():
     rng = np.random.default_rng(8)
     raw = rng.standard_normal((41, 9))
