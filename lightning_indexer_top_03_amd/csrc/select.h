@@ -46,6 +46,31 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   return x;
 }
 
+// AND / OR over the 64 lanes of a wave without LDS: DPP swaps within rows of 16, then the
+// permlane swaps across rows (16) and halves (32); every lane ends with the wave result.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ void wave_and_or(uint32_t& a, uint32_t& o) {
+  a &= dpp_u32<0xb1>(a);   // quad_perm 1,0,3,2
+  o |= dpp_u32<0xb1>(o);
+  a &= dpp_u32<0x4e>(a);   // quad_perm 2,3,0,1
+  o |= dpp_u32<0x4e>(o);
+  a &= dpp_u32<0x141>(a);  // row_half_mirror
+  o |= dpp_u32<0x141>(o);
+  a &= dpp_u32<0x140>(a);  // row_mirror
+  o |= dpp_u32<0x140>(o);
+  const auto a16 = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+  const auto o16 = __builtin_amdgcn_permlane16_swap(o, o, false, false);
+  a = a16[0] & a16[1];
+  o = o16[0] | o16[1];
+  const auto a32 = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  const auto o32 = __builtin_amdgcn_permlane32_swap(o, o, false, false);
+  a = a32[0] & a32[1];
+  o = o32[0] | o32[1];
+}
+
 template <int NW>
 struct __attribute__((aligned(16))) SelShared {
   uint32_t hist[3][256 * 4];  // pass p counts into hist[p % 3]: bin b, copy c at 4b + c
@@ -95,11 +120,7 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[PER], int 
       kor |= key[j];
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kand &= __shfl_xor(kand, o, 64);
-    kor |= __shfl_xor(kor, o, 64);
-  }
+  wave_and_or(kand, kor);
   if (lane == 0) {
     sh.red_and[wv] = kand;
     sh.red_or[wv] = kor;
