@@ -43,6 +43,9 @@ WORKLOAD_TEXT = {
     "csa_prefill": "CSA prefill: 131072 raw tokens mean-pooled 4:1 to 32768 blocks, last 8192 "
                    "queries, top-k 1024 + 128-token window, 128 heads, key 576 / value 512",
     "tiny": "tiny fp32 DSA: L=256, 16 queries, indexer 4x32, top-k 64, 8 heads, key 64 / value 48",
+    "decode_fp8": "decode DSA with an MXFP8 indexer (e4m3 q_I and k_I, one E8M0 scale per 32): "
+                  "B=16 x 1 query, context L=8192, indexer 64x128, top-k 2048, sparse MQA-MLA "
+                  "128 heads, key 576 / value 512 (bf16)",
     "hca_decode": "HCA decode: B=4 x 1 query over 1,048,576 tokens compressed 128:1 (8192 blocks), "
                   "dense attention over every visible block + 128-token raw window, 128 heads, "
                   "key 576 / value 512 (bf16)",
@@ -74,7 +77,7 @@ def _kernel_plan(cfg, nsplit):
     elif fast and cfg.k_dt == "bf16":
         names.append("indexer_decode_dma")
     elif fast:
-        names.append("indexer_decode_fp4_dma")
+        names.append("indexer_decode_mx_dma")
     else:
         names.append("indexer_generic")
     mfma = cfg.dt == "bf16" and cfg.D_K == 576 and cfg.D_V == 512 and cfg.H % 64 == 0
@@ -94,7 +97,9 @@ def _algorithmic(cfg, name):
     B, T, N = cfg.B, cfg.T, cfg.N
     rows = B * T
     esz = 2 if cfg.dt == "bf16" else 4
-    kI_row = cfg.D_I // 2 + cfg.D_I // 32 if cfg.k_dt == "mxfp4" else cfg.D_I * esz
+    kI_row = {"mxfp4": cfg.D_I // 2 + cfg.D_I // 32,
+              "mxfp8": cfg.D_I + cfg.D_I // 32}.get(cfg.k_dt, cfg.D_I * esz)
+    qI_row = cfg.D_I + cfg.D_I // 32 if cfg.qi_dt == "mxfp8" else cfg.D_I * esz
     nvis = [min(N, (int(p) + 1) // cfg.m) for p in cfg.positions().ravel()]  # visible entries
     pairs = float(sum(nvis))
     sel = float(sum(min(cfg.top_k, v) for v in nvis))
@@ -110,7 +115,7 @@ def _algorithmic(cfg, name):
     if name.startswith("indexer"):
         # every key row a sequence's queries can see is read once per sequence (decode: per query)
         keys = B * max(nvis) if T > 1 else pairs
-        byt = keys * kI_row + rows * cfg.H_I * (cfg.D_I * esz + 4) + pairs * 4
+        byt = keys * kI_row + rows * cfg.H_I * (qI_row + 4) + pairs * 4
         return byt, pairs * cfg.H_I * cfg.D_I * 2.0
     if name == "topk_long_filter":
         return pairs * 4, 0.0  # reads every visible score; its candidates are scratch
@@ -179,9 +184,11 @@ def _device_inputs(wl):
     c = wl.cfg
     t = {"q_pos": _dev(wl.q_pos())}
     if not c.dense:  # HCA has no indexer
-        t["q_I"], t["w"] = _dev(wl.q_I()), _dev(wl.w())
+        q = wl.q_I()
+        t["q_I"] = (_dev(q[0]), _dev(q[1])) if c.qi_dt == "mxfp8" else _dev(q)
+        t["w"] = _dev(wl.w())
         k = wl.k_I()
-        t["k_I"] = (_dev(k[0]), _dev(k[1])) if c.k_dt == "mxfp4" else _dev(k)
+        t["k_I"] = (_dev(k[0]), _dev(k[1])) if c.k_dt in ("mxfp4", "mxfp8") else _dev(k)
     rows = c.B * c.T
     tdt = torch.bfloat16 if c.dt == "bf16" else torch.float32
     q = torch.empty((c.B, c.T, c.H, c.D_K), dtype=tdt, device="cuda")

@@ -61,9 +61,11 @@ typedef enum dsa_status {
 typedef enum dsa_dtype {
   DSA_F32 = 0,   /* IEEE binary32                                                         */
   DSA_BF16 = 1,  /* bfloat16 (upper half of binary32)                                     */
-  DSA_MXFP4 = 2  /* OCP MX FP4: e2m1 codes, two per byte, LOW nibble = even element;
+  DSA_MXFP4 = 2, /* OCP MX FP4: e2m1 codes, two per byte, LOW nibble = even element;
                     one E8M0 scale byte (2^(e-127)) per 32 consecutive elements.
                     Only for k_I.                                                        */
+  DSA_MXFP8 = 3  /* OCP MX FP8: e4m3 (E4M3FN) codes, one per byte; one E8M0 scale byte
+                    per 32 consecutive elements. For k_I and q_I (the indexer only).     */
 } dsa_dtype;
 
 typedef struct dsa_dims {
@@ -114,16 +116,25 @@ dsa_status kv_compress_mean(const dsa_dims* d, dsa_dtype dt, const void* kv_raw,
  * multi-query logits with one key shared by all indexer heads).
  *   scores[b,t,s] = sum_{j<H_I} w[b,t,j] * max(0, sum_{d<D_I} q_I[b,t,j,d] * k_I[b,s,d])
  *                   for s < n_vis(b,t);   -inf for n_vis <= s < N.
- * q_I:    [B,T,H_I,D_I], dtype q_dt (F32 or BF16)
+ * q_I:    [B,T,H_I,D_I], dtype q_dt (F32 or BF16), or for q_dt == MXFP8 e4m3 codes
+ *         [B,T,H_I,D_I] bytes
+ * q_scale:[B,T,H_I,D_I/32] E8M0 bytes when q_dt == MXFP8, else must be NULL
  * w:      [B,T,H_I] fp32 (any sign)
- * k_I:    [B,N,D_I] of dtype k_dt (== q_dt), or for k_dt == MXFP4 codes [B,N,D_I/2] bytes
- * k_scale:[B,N,D_I/32] E8M0 bytes when k_dt == MXFP4, else must be NULL
+ * k_I:    [B,N,D_I] of dtype k_dt (== q_dt), or for k_dt == MXFP4 codes [B,N,D_I/2] bytes,
+ *         for k_dt == MXFP8 codes [B,N,D_I] bytes
+ * k_scale:[B,N,D_I/32] E8M0 bytes when k_dt is MXFP4 or MXFP8, else must be NULL
  * q_pos:  [B,T] int32
  * scores: [B,T,N] fp32 (written in full)
- * Products are exact (bf16 x bf16 or dequantised FP4 x bf16), accumulation fp32. */
-dsa_status indexer_scores(const dsa_dims* d, const void* q_I, dsa_dtype q_dt, const float* w,
-                          const void* k_I, const uint8_t* k_scale, dsa_dtype k_dt,
-                          const int32_t* q_pos, float* scores, void* stream);
+ * (q_dt, k_dt) pairs: (F32, F32), (BF16, BF16), (BF16, MXFP4), (BF16, MXFP8), (MXFP8, MXFP4),
+ * (MXFP8, MXFP8); others give DSA_ERR_DTYPE. MX formats need D_I % 32 == 0.
+ * Products are exact (every element is an exactly decoded stored value), accumulation fp32;
+ * a bf16 q_I against MX keys enters the block-scaled MFMA as two fp8 parts (hi + lo, exact
+ * except for values more than 2^13 below their 32-value block's largest, error < 2^-21 of it).
+ */
+dsa_status indexer_scores(const dsa_dims* d, const void* q_I, dsa_dtype q_dt,
+                          const uint8_t* q_scale, const float* w, const void* k_I,
+                          const uint8_t* k_scale, dsa_dtype k_dt, const int32_t* q_pos,
+                          float* scores, void* stream);
 
 /* Step 2 - per-query top-k ([P5] s1.3: only the KV entries with the k highest index scores
  * take part; s3 step 3: every token is kept when the context is no longer than k; step 4's
@@ -159,7 +170,7 @@ dsa_status sparse_mla_attend(const dsa_dims* d, dsa_dtype dt, const void* q, con
 /* Arguments of dsa_forward (pointers as in the calls above). */
 typedef struct dsa_forward_args {
   dsa_dtype dt;          /* dtype of q_I, q, kv, kv_raw, out: F32 or BF16                 */
-  dsa_dtype k_dt;        /* dtype of k_I: == dt, or MXFP4 (with dt == BF16)               */
+  dsa_dtype k_dt;        /* dtype of k_I: == dt, or MXFP4 / MXFP8 (with dt == BF16)       */
   const void* q_I;       /* [B,T,H_I,D_I]                                                 */
   const float* w;        /* [B,T,H_I]                                                     */
   const void* k_I;       /* [B,N,D_I] or MXFP4 codes [B,N,D_I/2]                          */
@@ -188,6 +199,8 @@ typedef struct dsa_forward_args {
                             selects the entries itself (MFMA shapes, N <= 32768, at most 128
                             query rows per chunk: the decode case). */
   int32_t n_events;
+  const uint8_t* q_scale;/* NULL, or the E8M0 scales [B,T,H_I,D_I/32] of an MXFP8 q_I (then q_I
+                            holds e4m3 codes [B,T,H_I,D_I]); indexer only                 */
 } dsa_forward_args;
 
 /* Fused path: [compress] -> indexer_scores -> topk_select -> sparse_mla_attend on `stream`

@@ -5,8 +5,9 @@ used for device memory and streams; each call passes ``data_ptr()`` values and t
 stream to the C ABI and raises ``DsaError`` with the library's status text on failure. There is
 no fallback: without the built library the import fails.
 
-bf16 tensors are ``torch.bfloat16``; MXFP4 keys are a pair (codes uint8 [B,N,D_I/2], scales
-uint8 [B,N,D_I/32]).
+bf16 tensors are ``torch.bfloat16``; MX keys are pairs (codes uint8, MXFP4 [B,N,D_I/2] or MXFP8
+[B,N,D_I], scales uint8 [B,N,D_I/32]); an MXFP8 q_I is (codes [B,T,H_I,D_I], scales
+[B,T,H_I,D_I/32]).
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-F32, BF16, MXFP4 = 0, 1, 2
+F32, BF16, MXFP4, MXFP8 = 0, 1, 2, 3
 OP_TOPK, OP_ATTEND, OP_FORWARD, OP_HCA = 1, 2, 3, 4
 
 EXPORTS = ("dsa_status_str", "dsa_version", "dsa_workspace_bytes", "kv_compress_mean",
@@ -47,7 +48,8 @@ class ForwardArgs(ctypes.Structure):
                 ("q_pos", ctypes.c_void_p), ("softmax_scale", ctypes.c_float),
                 ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
                 ("scores", ctypes.c_void_p), ("idx", ctypes.c_void_p),
-                ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32)]
+                ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32),
+                ("q_scale", ctypes.c_void_p)]
 
 
 _vp, _i64, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
@@ -58,7 +60,8 @@ _lib.dsa_version.restype = ctypes.c_int
 _lib.dsa_workspace_bytes.argtypes = [_D, ctypes.c_int]
 _lib.dsa_workspace_bytes.restype = _sz
 _lib.kv_compress_mean.argtypes = [_D, ctypes.c_int, _vp, _i64, _vp, _vp]
-_lib.indexer_scores.argtypes = [_D, _vp, ctypes.c_int, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp]
+_lib.indexer_scores.argtypes = [_D, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
+                                _vp]
 _lib.topk_select.argtypes = [_D, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.sparse_mla_attend.argtypes = [_D, ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
                                    ctypes.c_float, _vp, _vp, _vp, _sz, _vp]
@@ -136,23 +139,37 @@ KeyT = Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]
 
 
 def _keys(k_I: KeyT, q_dt: int):
+    """-> (codes or values, scales or None, dtype, N, D_I); MX keys are (codes, scales) pairs:
+    MXFP4 codes [B,N,D_I/2] or MXFP8 codes [B,N,D_I], scales [B,N,D_I/32]."""
     if isinstance(k_I, tuple):
         codes, scales = k_I
-        return codes, scales, MXFP4, codes.shape[1], codes.shape[2] * 2
+        if codes.shape[2] == 16 * scales.shape[2]:
+            return codes, scales, MXFP4, codes.shape[1], codes.shape[2] * 2
+        return codes, scales, MXFP8, codes.shape[1], codes.shape[2]
     return k_I, None, _dt(k_I), k_I.shape[1], k_I.shape[2]
 
 
-def indexer_scores(q_I: torch.Tensor, w: torch.Tensor, k_I: KeyT, q_pos: torch.Tensor,
+def _queries(q_I: KeyT):
+    """-> (codes or values, scales or None, dtype); an MXFP8 q_I is (codes [B,T,H_I,D_I] uint8,
+    scales [B,T,H_I,D_I/32] uint8)."""
+    if isinstance(q_I, tuple):
+        return q_I[0], q_I[1], MXFP8
+    return q_I, None, _dt(q_I)
+
+
+def indexer_scores(q_I: KeyT, w: torch.Tensor, k_I: KeyT, q_pos: torch.Tensor,
                    m: int = 1, scores: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """q_I [B,T,H_I,D_I], w [B,T,H_I] fp32, k_I [B,N,D_I] or MXFP4 (codes, scales),
-    q_pos [B,T] int32 -> scores [B,T,N] fp32 (-inf where not visible)."""
-    B, T, H_I, D_I = q_I.shape
-    kt, ks, kdt, N, _ = _keys(k_I, _dt(q_I))
+    """q_I [B,T,H_I,D_I] or MXFP8 (codes, scales), w [B,T,H_I] fp32, k_I [B,N,D_I] or MX
+    (codes, scales), q_pos [B,T] int32 -> scores [B,T,N] fp32 (-inf where not visible)."""
+    qt, qs, qdt = _queries(q_I)
+    B, T, H_I, D_I = qt.shape
+    kt, ks, kdt, N, _ = _keys(k_I, qdt)
     if scores is None:
-        scores = torch.empty((B, T, N), dtype=torch.float32, device=q_I.device)
+        scores = torch.empty((B, T, N), dtype=torch.float32, device=qt.device)
     d = dims(B=B, T=T, N=N, H_I=H_I, D_I=D_I, m=m)
-    _check(_lib.indexer_scores(ctypes.byref(d), _ptr(q_I), _dt(q_I), _ptr(w), _ptr(kt), _ptr(ks),
-                               kdt, _ptr(q_pos), _ptr(scores), _stream(q_I)), "indexer_scores")
+    _check(_lib.indexer_scores(ctypes.byref(d), _ptr(qt), qdt, _ptr(qs), _ptr(w), _ptr(kt),
+                               _ptr(ks), kdt, _ptr(q_pos), _ptr(scores), _stream(qt)),
+           "indexer_scores")
     return scores
 
 
@@ -208,9 +225,10 @@ class Forward:
                  softmax_scale: float, m: int = 1, W: int = 0, kv_raw=None, raw_base: int = 0,
                  compress: bool = False, out=None, lse=None, scores=None, idx=None,
                  want_lse: bool = True):
-        B, T, H_I, D_I = q_I.shape
+        qt, qs, qdt = _queries(q_I)
+        B, T, H_I, D_I = qt.shape
         _, _, H, D_K = q.shape
-        kt, ks, kdt, N, _ = _keys(k_I, _dt(q_I))
+        kt, ks, kdt, N, _ = _keys(k_I, qdt)
         self.d = dims(B=B, T=T, N=N, H_I=H_I, D_I=D_I, H=H, D_K=D_K, D_V=D_V, top_k=top_k, m=m,
                       W=W)
         dev = q.device
@@ -219,12 +237,12 @@ class Forward:
             torch.empty((B, T, H), dtype=torch.float32, device=dev) if want_lse else None)
         self.scores, self.idx = scores, idx
         self.ws = _workspace(self.d, OP_FORWARD, dev)
-        self._keep = (q_I, w, kt, ks, q, kv, q_pos, kv_raw)
+        self._keep = (qt, qs, w, kt, ks, q, kv, q_pos, kv_raw)
         n_raw = 0 if kv_raw is None else kv_raw.shape[1]
-        self.args = ForwardArgs(_dt(q), kdt, _ptr(q_I), _ptr(w), _ptr(kt), _ptr(ks), _ptr(q),
+        self.args = ForwardArgs(_dt(q), kdt, _ptr(qt), _ptr(w), _ptr(kt), _ptr(ks), _ptr(q),
                                 _ptr(kv), _ptr(kv_raw), raw_base, n_raw, 1 if compress else 0,
                                 _ptr(q_pos), softmax_scale, _ptr(self.out), _ptr(self.lse),
-                                _ptr(scores), _ptr(idx), None, 0)
+                                _ptr(scores), _ptr(idx), None, 0, _ptr(qs))
         self.device = dev
 
     def set_events(self, events) -> None:
@@ -285,7 +303,7 @@ class HcaForward(Forward):
         self.args = ForwardArgs(_dt(q), _dt(q), None, None, None, None, _ptr(q), _ptr(kv),
                                 _ptr(kv_raw), raw_base, n_raw, 1 if compress else 0,
                                 _ptr(q_pos), softmax_scale, _ptr(self.out), _ptr(self.lse),
-                                None, None, None, 0)
+                                None, None, None, 0, None)
         self.device = dev
 
     def run(self, stream: Optional[int] = None) -> torch.Tensor:

@@ -47,17 +47,19 @@ Shape to_shape(const dsa_dims* d) {
 bool fmt_ok(dsa_dtype t) { return t == DSA_F32 || t == DSA_BF16; }
 
 // indexer argument rules shared by indexer_scores and dsa_forward
-dsa_status check_indexer(const dsa_dims* d, dsa_dtype q_dt, dsa_dtype k_dt,
-                         const uint8_t* k_scale) {
-  if (!fmt_ok(q_dt)) return DSA_ERR_DTYPE;
-  if (k_dt == DSA_MXFP4) {
-    if (!k_scale) return DSA_ERR_NULL;
-    if (d->D_I % 32) return DSA_ERR_SHAPE;
-  } else {
-    if (k_dt != q_dt) return DSA_ERR_DTYPE;
-    if (k_scale) return DSA_ERR_DTYPE;
+dsa_status check_indexer(const dsa_dims* d, dsa_dtype q_dt, const uint8_t* q_scale,
+                         dsa_dtype k_dt, const uint8_t* k_scale) {
+  const bool qmx = q_dt == DSA_MXFP8, kmx = k_dt == DSA_MXFP4 || k_dt == DSA_MXFP8;
+  if (!fmt_ok(q_dt) && !qmx) return DSA_ERR_DTYPE;
+  if (qmx != (q_scale != nullptr)) return qmx ? DSA_ERR_NULL : DSA_ERR_DTYPE;
+  if (kmx != (k_scale != nullptr)) return kmx ? DSA_ERR_NULL : DSA_ERR_DTYPE;
+  if (kmx) {
+    if (q_dt != DSA_BF16 && !qmx) return DSA_ERR_DTYPE;  // MX keys pair with bf16 or MXFP8 q_I
+  } else if (k_dt != q_dt) {
+    return DSA_ERR_DTYPE;  // includes MXFP8 q_I against plain keys
   }
-  const bool fast = q_dt == DSA_BF16 && d->H_I == 64 && d->D_I == 128;
+  if ((qmx || kmx) && d->D_I % 32) return DSA_ERR_SHAPE;
+  const bool fast = (q_dt == DSA_BF16 || qmx) && d->H_I == 64 && d->D_I == 128;
   if (!fast && (int64_t)d->H_I * d->D_I > 8192) return DSA_ERR_SHAPE;  // generic kernel LDS
   return DSA_OK;
 }
@@ -195,19 +197,20 @@ dsa_status kv_compress_mean(const dsa_dims* d, dsa_dtype dt, const void* kv_raw,
                                   kv_raw, kv_c, (hipStream_t)stream));
 }
 
-dsa_status indexer_scores(const dsa_dims* d, const void* q_I, dsa_dtype q_dt, const float* w,
-                          const void* k_I, const uint8_t* k_scale, dsa_dtype k_dt,
-                          const int32_t* q_pos, float* scores, void* stream) {
+dsa_status indexer_scores(const dsa_dims* d, const void* q_I, dsa_dtype q_dt,
+                          const uint8_t* q_scale, const float* w, const void* k_I,
+                          const uint8_t* k_scale, dsa_dtype k_dt, const int32_t* q_pos,
+                          float* scores, void* stream) {
   if (dsa_status st = check_dims(d)) return st;
-  if (dsa_status st = check_indexer(d, q_dt, k_dt, k_scale)) return st;
+  if (dsa_status st = check_indexer(d, q_dt, q_scale, k_dt, k_scale)) return st;
   if (!q_I || !w || !k_I || !q_pos || !scores) return DSA_ERR_NULL;
   if (!aligned16(q_I) || !aligned16(w) || !aligned16(k_I) || !aligned16(scores) ||
-      (k_scale && ((uintptr_t)k_scale & 3u)))
+      (k_scale && ((uintptr_t)k_scale & 3u)) || (q_scale && ((uintptr_t)q_scale & 3u)))
     return DSA_ERR_ALIGN;
   if (dsa_status st = check_device()) return st;
   const Shape s = to_shape(d);
-  return launched(launch_indexer(s, 0, (int64_t)d->B * d->T, q_I, (int)q_dt, w, k_I, k_scale,
-                                 (int)k_dt, q_pos, scores, true, (hipStream_t)stream));
+  return launched(launch_indexer(s, 0, (int64_t)d->B * d->T, q_I, (int)q_dt, q_scale, w, k_I,
+                                 k_scale, (int)k_dt, q_pos, scores, true, (hipStream_t)stream));
 }
 
 dsa_status topk_select(const dsa_dims* d, const float* scores, const int32_t* q_pos,
@@ -251,7 +254,10 @@ dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
   if (!a) return DSA_ERR_NULL;
   if (dsa_status st = check_attend_shape(d)) return st;
   if (!fmt_ok(a->dt)) return DSA_ERR_DTYPE;
-  if (dsa_status st = check_indexer(d, a->dt, a->k_dt, a->k_scale)) return st;
+  const dsa_dtype qi_dt = a->q_scale != nullptr ? DSA_MXFP8 : a->dt;
+  if (a->q_scale && a->dt != DSA_BF16) return DSA_ERR_DTYPE;
+  if (dsa_status st = check_indexer(d, qi_dt, a->q_scale, a->k_dt, a->k_scale)) return st;
+  if (a->q_scale && ((uintptr_t)a->q_scale & 3u)) return DSA_ERR_ALIGN;
   if (!a->q_I || !a->w || !a->k_I || !a->q || !a->kv || !a->q_pos || !a->out) return DSA_ERR_NULL;
   if ((d->W > 0 || a->compress) && !a->kv_raw) return DSA_ERR_NULL;
   if (a->raw_base < 0 || a->n_raw < 0) return DSA_ERR_SHAPE;
@@ -285,7 +291,8 @@ dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
     const int64_t nr = std::min(R, rows - q0);
     float* sc = keep_scores ? a->scores + (size_t)q0 * d->N : ws_scores;
     int32_t* ix = a->idx ? a->idx + (size_t)q0 * d->top_k : ws_idx;
-    if (hipError_t e = launch_indexer(s, q0, nr, a->q_I, (int)a->dt, a->w, a->k_I, a->k_scale,
+    if (hipError_t e = launch_indexer(s, q0, nr, a->q_I, (int)qi_dt, a->q_scale, a->w, a->k_I,
+                                      a->k_scale,
                                       (int)a->k_dt, a->q_pos, sc, keep_scores, st))
       return launched(e);
     if (attend_fused_ok(s, fmt, nr)) {

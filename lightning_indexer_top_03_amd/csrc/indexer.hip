@@ -178,43 +178,66 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_dma(
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode-shaped kernel, MXFP4 keys (64 code bytes + 4 E8M0 scale bytes per key), on the
-// block-scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4, which takes the FP4 codes and their E8M0
-// scales as they are stored (no per-element conversion).
-//  * q_I (bf16) enters as two fp8 (e4m3) operands, q = hi + lo, each with its own E8M0 scale
-//    per 32 dims: with e the exponent of the block's largest |q|, hi = RNE(q / 2^(e-7)) and
+// Decode-shaped kernel, MX keys (MXFP4: 64 code bytes per key; MXFP8: 128 code bytes per key;
+// both with 4 E8M0 scale bytes per key), on the block-scaled MFMA
+// v_mfma_scale_f32_32x32x64_f8f6f4, which takes the codes and their E8M0 scales as they are
+// stored (no per-element conversion).
+//  * q_I either is MXFP8 itself (QMX: codes and scales go straight into the A operands) or is
+//    bf16 and enters as two fp8 (e4m3) operands, q = hi + lo, each with its own E8M0 scale per
+//    32 dims: with e the exponent of the block's largest |q|, hi = RNE(q / 2^(e-7)) and
 //    lo = RNE((q - hi 2^(e-7)) / 2^(e-11)). A bf16 value has 8 significant bits and hi keeps 4,
 //    so the remainder has at most 4 and lo holds it exactly, except for values more than 2^13
-//    below the block maximum, where the error stays below 2^(e-21). The products of fp8 and
-//    fp4 values are exact and accumulate in fp32.
-//  * Operand layouts of the instruction (checked on gfx950): B (fp4, 16 bytes per lane): lane
-//    (n, h) holds key n, contraction indices 32h .. 32h+31 in nibble order; A (fp8, 32 bytes
-//    per lane): lane (i, h) holds row i, indices 16h .. 16h+15 in bytes 0..15 and 32+16h ..
-//    47+16h in bytes 16..31; the scale of (row or key c, index block b) comes from lane c + 32b.
-//    Contraction step s covers dims 64s .. 64s+63, so each index block is one MX block of k_I.
-//  * Keys stream through LDS exactly as in indexer_decode_dma: each of the 8 waves runs its
-//    own 4-stage ring of 64-key tiles (4 KB of codes in four fully coalesced 1 KB DMAs, 256 B of
-//    scales in one 4-byte-per-lane DMA). Row r of a tile keeps its 16-byte chunk c in slot
-//    c ^ ((r >> 2) & 3), so the 16 lanes of a ds_read_b128 phase cover all 64 banks once.
+//    below the block maximum, where the error stays below 2^(e-21). Products of fp8 and fp4 /
+//    fp8 values are exact and accumulate in fp32.
+//  * Operand layouts of the instruction (checked on gfx950): an fp4 operand (16 bytes per lane)
+//    has lane (c, h) = row or key c, contraction indices 32h .. 32h+31 in nibble order; an fp8
+//    operand (32 bytes per lane) has indices 16h .. 16h+15 in bytes 0..15 and 32+16h .. 47+16h
+//    in bytes 16..31; the scale of (row or key c, index block b) comes from lane c + 32b.
+//    Contraction step s covers dims 64s .. 64s+63, so each index block is one MX block.
+//  * Keys stream through LDS: each of the 8 waves runs its own 4-stage ring of tiles (64 FP4
+//    keys or 32 FP8 keys: 4 KB of codes in four fully coalesced 1 KB DMAs, scales in one
+//    4-byte-per-lane DMA), dealt round-robin over the row's waves so that at any moment the
+//    whole grid streams one contiguous window of the key cache (a cold read of this size runs
+//    ~25% faster that way than when every wave streams a contiguous range of its own). The
+//    16-byte chunks of a code row are XOR-swizzled so that the 16 lanes of a ds_read_b128 phase
+//    cover all 64 banks once.
+//  * The MFMAs of a 32-key group are issued before the epilogue of the previous group, one
+//    MFMA per eight epilogue instructions, so the VALU work overlaps this wave's own MFMAs.
 // ------------------------------------------------------------------------------------------
-constexpr int kF4Tile = 64;                              // keys per tile
-constexpr int kF4Stages = 4;                             // ring stages per wave
-constexpr int kF4Stage = kF4Tile * 64 + kF4Tile * 4;     // codes + scales: 4352 bytes
+constexpr int kMxStages = 4;          // ring stages per wave
+constexpr int kMxStage = 4096 + 256;  // codes + scales per stage
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-template <int ITERS>
-__global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_fp4_dma(
-    const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
-    const uint8_t* __restrict__ ksc, const int32_t* __restrict__ q_pos, int T, int N, int m,
-    int64_t qi0, float* __restrict__ scores, int fill_masked) {
-  static_assert(ITERS <= 8, "the scores of a wave are staged in the q_I operand buffer");
-  // sq: fp8 codes of q_I, [part][head][8 chunks of 16 B] (chunk c of head r in slot c ^ (r & 7)),
-  // then reused for the scores
+template <int KFMT>
+struct MxKeys {
+  static constexpr int kTile = KFMT == FMT_MXFP4 ? 64 : 32;  // keys per tile
+  static constexpr int kRow = KFMT == FMT_MXFP4 ? 64 : 128;  // code bytes per key
+  static constexpr int kChunks = kRow / 16;
+  static constexpr int kGroups = kTile / 32;                 // 32-key groups per tile
+  static constexpr int kFmt = KFMT == FMT_MXFP4 ? 4 : 0;     // MFMA operand format
+  // swizzled slot of 16-byte chunk c of tile row r
+  __device__ static int slot(int r, int c) {
+    return KFMT == FMT_MXFP4 ? (c ^ ((r >> 2) & 3)) : (c ^ ((r >> 1) & 7));
+  }
+};
+
+template <int KFMT, bool QMX, int ITERS>
+__global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_mx_dma(
+    const void* __restrict__ qI, const uint8_t* __restrict__ qsc, const float* __restrict__ w,
+    const uint8_t* __restrict__ kI, const uint8_t* __restrict__ ksc,
+    const int32_t* __restrict__ q_pos, int T, int N, int m, int64_t qi0,
+    float* __restrict__ scores, int fill_masked) {
+  using K = MxKeys<KFMT>;
+  constexpr int TK = K::kTile;
+  constexpr int NP = QMX ? 1 : 2;  // q parts: the MXFP8 q_I itself, or hi + lo
+  static_assert(ITERS * TK <= 512, "the scores of a wave are staged in the q_I operand buffer");
+  // sq: fp8 codes of a bf16 q_I's two parts, [part][head][8 chunks of 16 B] (chunk c of head r
+  // in slot c ^ (r & 7)); then reused for the scores
   __shared__ __attribute__((aligned(16))) char sq[2 * 64 * 128];
-  __shared__ uint32_t sqs[2][64];  // E8M0 scale bytes of q_I: [part][head] x 4 blocks
-  __shared__ __attribute__((aligned(16))) char sk[kDecWaves][kF4Stages][kF4Stage];
-  float (*sres)[kF4Tile * ITERS] = reinterpret_cast<float (*)[kF4Tile * ITERS]>(&sq[0]);
+  __shared__ uint32_t sqs[2][64];  // their E8M0 scale bytes: [part][head] x 4 blocks
+  __shared__ __attribute__((aligned(16))) char sk[kDecWaves][kMxStages][kMxStage];
+  float (*sres)[ITERS * TK] = reinterpret_cast<float (*)[ITERS * TK]>(&sq[0]);
   const int64_t row = blockIdx.y;
   const int64_t qi = qi0 + row;
   const int b = (int)(qi / T);
@@ -222,18 +245,15 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_fp4_dma(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
-  // Tiles are dealt round-robin over the row's waves (tile t of wave gw: keys
-  // (t GW + gw) * 64 ..), so at any moment the whole grid streams one contiguous window of
-  // the key cache: a cold read of this size runs ~25% faster that way than when every wave
-  // streams a contiguous range of its own.
+  // tile t of wave gw: keys (t GW + gw) * TK ..
   const int gw = blockIdx.x * kDecWaves + wv, GW = gridDim.x * kDecWaves;
-  auto tile_key = [&](int t) { return (t * GW + gw) * kF4Tile; };
+  auto tile_key = [&](int t) { return (t * GW + gw) * TK; };
   float* __restrict__ srow = scores + (size_t)row * N;
 
-  if (blockIdx.x * kDecWaves * kF4Tile >= nv) {  // every tile of the workgroup is masked
+  if (blockIdx.x * kDecWaves * TK >= nv) {  // every tile of the workgroup is masked
     if (fill_masked)
       for (int t = 0; t < ITERS; ++t)
-        if (tile_key(t) + lane < N) srow[tile_key(t) + lane] = kNegInf;
+        if (lane < TK && tile_key(t) + lane < N) srow[tile_key(t) + lane] = kNegInf;
     return;
   }
   const size_t base_row = (size_t)b * N;
@@ -249,27 +269,50 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_fp4_dma(
 #pragma unroll
       for (int i = 0; i < 4; ++i) wr[hb][4 * j + i] = w4[i];
     }
-  // q_I: thread t converts head t / 8, dims 16 (t % 8) .. +15
+  // q_I loads: an MXFP8 q_I straight into the A operands (row 32hb + n, dims 64s + 16h .. +15
+  // and 64s + 32 + 16h .. +15, scale of block 2s + h); a bf16 q_I per thread for the split
+  i32x8_t qa[NP][2][2];
+  int qs[NP][2][2];
+  u32x4_t q0 = {}, q1 = {};
+  uint32_t qsw[2] = {0u, 0u};
   const int qh = tid >> 3, qc = tid & 7;
-  const u32x4_t* qsrc = reinterpret_cast<const u32x4_t*>(qI + (size_t)qi * (64 * 128) + qh * 128 + 16 * qc);
-  const u32x4_t q0 = qsrc[0], q1 = qsrc[1];
-  // tile t of this wave into stage t % kF4Stages: 5 DMA instructions
+  if constexpr (QMX) {
+    const uint8_t* qrow = static_cast<const uint8_t*>(qI) + (size_t)qi * (64 * 128);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const uint8_t* qr = qrow + (32 * hb + n) * 128;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const u32x4_t lo4 = *reinterpret_cast<const u32x4_t*>(qr + 64 * s2 + 16 * h);
+        const u32x4_t hi4 = *reinterpret_cast<const u32x4_t*>(qr + 64 * s2 + 32 + 16 * h);
+        qa[0][hb][s2] = i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                                (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+      }
+      qsw[hb] = *reinterpret_cast<const uint32_t*>(qsc + ((size_t)qi * 64 + 32 * hb + n) * 4);
+    }
+  } else {
+    const u32x4_t* qsrc = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(qI) +
+                                                           (size_t)qi * (64 * 128) + qh * 128 + 16 * qc);
+    q0 = qsrc[0];
+    q1 = qsrc[1];
+  }
+  // tile t of this wave into stage t % kMxStages: 5 DMA instructions
   auto issue = [&](int t) {
-    const uint32_t sb = ring + (t % kF4Stages) * kF4Stage;
+    const uint32_t sb = ring + (t % kMxStages) * kMxStage;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = 16 * j + (lane >> 2), c = lane & 3;
+      const int r = (1024 / K::kRow) * j + lane / K::kChunks, c = lane % K::kChunks;
       // keys past the visible range re-read the last visible row (served by L2)
       const size_t krow = base_row + min(tile_key(t) + r, nv - 1);
       __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(kI + krow * 64 + 16 * (c ^ ((r >> 2) & 3))),
+          reinterpret_cast<const void*>(kI + krow * K::kRow + 16 * K::slot(r, c)),
           (lds_void_t*)(uintptr_t)(sb + 1024 * j), 16, 0, 0);
     }
     const size_t srow_k = base_row + min(tile_key(t) + lane, nv - 1);
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(ksc + srow_k * 4),
-                                     (lds_void_t*)(uintptr_t)(sb + kF4Tile * 64), 4, 0, 0);
+                                     (lds_void_t*)(uintptr_t)(sb + 4096), 4, 0, 0);
   };
-  constexpr int kPre = ITERS < kF4Stages ? ITERS : kF4Stages;
+  constexpr int kPre = ITERS < kMxStages ? ITERS : kMxStages;
 #pragma unroll
   for (int t = 0; t < kPre; ++t) issue(t);
   // w and q_I have landed once only the prefetched tiles are outstanding
@@ -283,7 +326,13 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_fp4_dma(
   for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(wr[hb][r]));
-  {
+  if constexpr (QMX) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) qs[0][hb][s2] = (int)((qsw[hb] >> (8 * (2 * s2 + h))) & 0xffu);
+  } else {
+    // thread t converts head t / 8, dims 16 (t % 8) .. +15 into the two fp8 parts
     float v[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -323,43 +372,41 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_fp4_dma(
       reinterpret_cast<uint8_t*>(&sqs[0][qh])[qc >> 1] = (uint8_t)(e + 120);
       reinterpret_cast<uint8_t*>(&sqs[1][qh])[qc >> 1] = (uint8_t)(e + 116);
     }
-  }
-  __syncthreads();
-  // A operands: qa[part][hb][s] = row 32hb + n, dims 64s + 16h .. +15 and 64s + 32 + 16h .. +15
-  i32x8_t qa[2][2][2];
-  int qs[2][2][2];
+    __syncthreads();
 #pragma unroll
-  for (int pt = 0; pt < 2; ++pt)
+    for (int pt = 0; pt < NP; ++pt)
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int r = 32 * hb + n;
-      const uint32_t sc4 = sqs[pt][r];
+      for (int hb = 0; hb < 2; ++hb) {
+        const int r = 32 * hb + n;
+        const uint32_t sc4 = sqs[pt][r];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int c0 = 4 * s2 + h, c1 = 4 * s2 + 2 + h;  // 16-byte chunks
-        const u32x4_t lo4 = *reinterpret_cast<const u32x4_t*>(&sq[pt * 64 * 128 + r * 128 + 16 * (c0 ^ (r & 7))]);
-        const u32x4_t hi4 = *reinterpret_cast<const u32x4_t*>(&sq[pt * 64 * 128 + r * 128 + 16 * (c1 ^ (r & 7))]);
-        qa[pt][hb][s2] = i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                                 (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
-        qs[pt][hb][s2] = (int)((sc4 >> (8 * (2 * s2 + h))) & 0xffu);  // block 2s + h
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int c0 = 4 * s2 + h, c1 = 4 * s2 + 2 + h;  // 16-byte chunks
+          const u32x4_t lo4 = *reinterpret_cast<const u32x4_t*>(&sq[pt * 64 * 128 + r * 128 + 16 * (c0 ^ (r & 7))]);
+          const u32x4_t hi4 = *reinterpret_cast<const u32x4_t*>(&sq[pt * 64 * 128 + r * 128 + 16 * (c1 ^ (r & 7))]);
+          qa[pt][hb][s2] = i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                                   (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+          qs[pt][hb][s2] = (int)((sc4 >> (8 * (2 * s2 + h))) & 0xffu);  // block 2s + h
+        }
       }
-    }
+  }
   // every wave holds its A operands before the buffer is reused for the scores
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
 
-  // Software pipeline over the 2 * ITERS groups of 32 keys (group g: tile g / 2, keys
-  // 32 (g % 2) ..): the MFMAs of group g + 1 are issued before the epilogue of group g, one
-  // MFMA per eight epilogue instructions, so this wave's VALU work runs while its own next
-  // MFMAs execute. Two accumulator pairs alternate.
+  // Software pipeline over the K::kGroups * ITERS groups of 32 keys (group g: tile
+  // g / kGroups, keys 32 (g % kGroups) ..): the MFMAs of group g + 1 are issued before the
+  // epilogue of group g, one MFMA per eight epilogue instructions. Two accumulator pairs
+  // alternate.
+  constexpr int G = K::kGroups * ITERS;
   auto tile_ready = [&](int t) {
-    if (t > 0 && t + kF4Stages - 1 < ITERS) {
-      // stage (t-1) % kF4Stages: its B-operand reads completed before their MFMAs issued
+    if (t > 0 && t + kMxStages - 1 < ITERS) {
+      // stage (t-1) % kMxStages: its B-operand reads completed before their MFMAs issued
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      issue(t + kF4Stages - 1);
+      issue(t + kMxStages - 1);
     }
     // tile t landed; the tiles after it (up to three) may still be in flight
-    const int after = min(ITERS - 1 - t, kF4Stages - 1);
+    const int after = min(ITERS - 1 - t, kMxStages - 1);
     switch (after) {
       case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
       case 1: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
@@ -368,24 +415,35 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_fp4_dma(
     }
   };
   auto mfma_group = [&](int g, f32x16_t& acc0, f32x16_t& acc1) {
-    const char* st = &sk[wv][(g >> 1) % kF4Stages][0];
-    const int r = 32 * (g & 1) + n;
-    // B operands: key r, step s: 16-byte chunk 2s + h of its codes and scale byte 2s + h
-    const u32x4_t b0 = *reinterpret_cast<const u32x4_t*>(st + r * 64 + 16 * ((h) ^ ((r >> 2) & 3)));
-    const u32x4_t b1 = *reinterpret_cast<const u32x4_t*>(st + r * 64 + 16 * ((2 + h) ^ ((r >> 2) & 3)));
-    const uint32_t ks = *reinterpret_cast<const uint32_t*>(st + kF4Tile * 64 + 4 * r);
-    const i32x8_t kb0 = i32x8_t{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], 0, 0, 0, 0};
-    const i32x8_t kb1 = i32x8_t{(int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3], 0, 0, 0, 0};
-    const int ks0 = (int)((ks >> (8 * h)) & 0xffu), ks1 = (int)((ks >> (8 * (2 + h))) & 0xffu);
+    const char* st = &sk[wv][(g / K::kGroups) % kMxStages][0];
+    const int r = 32 * (g % K::kGroups) + n;
+    const uint32_t ks = *reinterpret_cast<const uint32_t*>(st + 4096 + 4 * r);
+    i32x8_t kb[2];
+    int kss[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      kss[s2] = (int)((ks >> (8 * (2 * s2 + h))) & 0xffu);  // scale of block 2s + h
+      if constexpr (KFMT == FMT_MXFP4) {
+        // key r, step s: 16-byte chunk 2s + h of its codes
+        const u32x4_t c4 = *reinterpret_cast<const u32x4_t*>(st + r * 64 + 16 * K::slot(r, 2 * s2 + h));
+        kb[s2] = i32x8_t{(int)c4[0], (int)c4[1], (int)c4[2], (int)c4[3], 0, 0, 0, 0};
+      } else {
+        // key r, step s: chunks 4s + h and 4s + 2 + h (the fp8 operand layout)
+        const u32x4_t lo4 = *reinterpret_cast<const u32x4_t*>(st + r * 128 + 16 * K::slot(r, 4 * s2 + h));
+        const u32x4_t hi4 = *reinterpret_cast<const u32x4_t*>(st + r * 128 + 16 * K::slot(r, 4 * s2 + 2 + h));
+        kb[s2] = i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                         (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+      }
+    }
     acc0 = f32x16_t{};
     acc1 = f32x16_t{};
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
-      acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[pt][0][0], kb0, acc0, 0, 4, 0, qs[pt][0][0], 0, ks0);
-      acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[pt][1][0], kb0, acc1, 0, 4, 0, qs[pt][1][0], 0, ks0);
-      acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[pt][0][1], kb1, acc0, 0, 4, 0, qs[pt][0][1], 0, ks1);
-      acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[pt][1][1], kb1, acc1, 0, 4, 0, qs[pt][1][1], 0, ks1);
-    }
+    for (int pt = 0; pt < NP; ++pt)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[pt][0][s2], kb[s2], acc0, 0, K::kFmt, 0, qs[pt][0][s2], 0, kss[s2]);
+        acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[pt][1][s2], kb[s2], acc1, 0, K::kFmt, 0, qs[pt][1][s2], 0, kss[s2]);
+      }
   };
   auto epilogue = [&](int g, const f32x16_t& acc0, const f32x16_t& acc1) {
     float p4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
@@ -403,27 +461,29 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_fp4_dma(
   tile_ready(0);
   mfma_group(0, accA0, accA1);
 #pragma unroll
-  for (int g = 0; g < 2 * ITERS; ++g) {
-    if (g + 1 < 2 * ITERS) {
-      if (((g + 1) & 1) == 0) tile_ready((g + 1) >> 1);
+  for (int g = 0; g < G; ++g) {
+    if (g + 1 < G) {
+      if ((g + 1) % K::kGroups == 0) tile_ready((g + 1) / K::kGroups);
       if (g & 1) mfma_group(g + 1, accA0, accA1);
       else mfma_group(g + 1, accB0, accB1);
     }
     if (g & 1) epilogue(g, accB0, accB1);
     else epilogue(g, accA0, accA1);
-    if (g + 1 < 2 * ITERS) {
+    if (g + 1 < G) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 4 * NP; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // eight VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 16 / NP, 0);  // epilogue instructions
       }
     }
   }
 #pragma unroll
   for (int t = 0; t < ITERS; ++t) {
     const int s = tile_key(t) + lane;
-    if (s < nv) srow[s] = sres[wv][kF4Tile * t + lane];
-    else if (fill_masked && s < N) srow[s] = kNegInf;
+    if (lane < TK) {
+      if (s < nv) srow[s] = sres[wv][TK * t + lane];
+      else if (fill_masked && s < N) srow[s] = kNegInf;
+    }
   }
 }
 
@@ -585,6 +645,13 @@ __device__ __forceinline__ float load_val(const void* p, size_t i, int fmt) {
                         : bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
 }
 
+// e4m3 (OCP E4M3FN) code -> value: sign bit 7, exponent bits 6..3 (bias 7), mantissa 2..0
+__device__ __forceinline__ float fp8_val(uint32_t code) {
+  const uint32_t e = (code >> 3) & 15u, mb = code & 7u;
+  const float mag = e == 0 ? ldexpf((float)mb, -9) : ldexpf(1.0f + 0.125f * (float)mb, (int)e - 7);
+  return (code & 0x80u) ? -mag : mag;
+}
+
 __device__ __forceinline__ float fp4_val(uint32_t code) {
   // e2m1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0
   uint32_t e = (code >> 1) & 3u, mb = code & 1u;
@@ -593,8 +660,9 @@ __device__ __forceinline__ float fp4_val(uint32_t code) {
 }
 
 __global__ __launch_bounds__(256) void indexer_generic(
-    const void* __restrict__ qI, int q_fmt, const float* __restrict__ w,
-    const void* __restrict__ kI, const uint8_t* __restrict__ ksc, int k_fmt,
+    const void* __restrict__ qI, int q_fmt, const uint8_t* __restrict__ qsc,
+    const float* __restrict__ w, const void* __restrict__ kI, const uint8_t* __restrict__ ksc,
+    int k_fmt,
     const int32_t* __restrict__ q_pos, int T, int N, int m, int H_I, int D_I, int64_t qi0,
     float* __restrict__ scores, int fill_masked) {
   extern __shared__ float sm[];  // [H_I*D_I] q, [H_I] w
@@ -604,8 +672,12 @@ __global__ __launch_bounds__(256) void indexer_generic(
   const int nv = n_visible(q_pos[qi], m, N);
   float* sqf = sm;
   float* swf = sm + H_I * D_I;
-  for (int i = threadIdx.x; i < H_I * D_I; i += blockDim.x)
-    sqf[i] = load_val(qI, (size_t)qi * H_I * D_I + i, q_fmt);
+  for (int i = threadIdx.x; i < H_I * D_I; i += blockDim.x) {
+    const size_t e = (size_t)qi * H_I * D_I + i;
+    sqf[i] = q_fmt == FMT_MXFP8
+                 ? fp8_val(static_cast<const uint8_t*>(qI)[e]) * e8m0_scale(qsc[e / 32])
+                 : load_val(qI, e, q_fmt);
+  }
   for (int i = threadIdx.x; i < H_I; i += blockDim.x) swf[i] = w[(size_t)qi * H_I + i];
   __syncthreads();
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
@@ -625,6 +697,9 @@ __global__ __launch_bounds__(256) void indexer_generic(
         uint32_t byte = reinterpret_cast<const uint8_t*>(kI)[krow * (D_I / 2) + d / 2];
         uint32_t code = (d & 1) ? (byte >> 4) : (byte & 15u);
         kv = fp4_val(code) * e8m0_scale(ksc[krow * (D_I / 32) + d / 32]);
+      } else if (k_fmt == FMT_MXFP8) {
+        kv = fp8_val(reinterpret_cast<const uint8_t*>(kI)[krow * D_I + d]) *
+             e8m0_scale(ksc[krow * (D_I / 32) + d / 32]);
       } else {
         kv = load_val(kI, krow * D_I + d, k_fmt);
       }
@@ -638,14 +713,14 @@ __global__ __launch_bounds__(256) void indexer_generic(
 }  // namespace
 
 hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void* q_I, int q_fmt,
-                          const float* w, const void* k_I, const uint8_t* k_scale, int k_fmt,
-                          const int32_t* q_pos, float* scores, bool fill_masked,
-                          hipStream_t st) {
+                          const uint8_t* q_scale, const float* w, const void* k_I,
+                          const uint8_t* k_scale, int k_fmt, const int32_t* q_pos, float* scores,
+                          bool fill_masked, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
-  const bool fast = q_fmt == FMT_BF16 && (k_fmt == FMT_BF16 || k_fmt == FMT_MXFP4) &&
-                    s.H_I == 64 && s.D_I == 128;
+  const bool shape_ok = s.H_I == 64 && s.D_I == 128;
+  const bool kmx = k_fmt == FMT_MXFP4 || k_fmt == FMT_MXFP8;
   const int fm = fill_masked ? 1 : 0;
-  if (fast && k_fmt == FMT_BF16 && nrows >= 64) {
+  if (shape_ok && q_fmt == FMT_BF16 && k_fmt == FMT_BF16 && nrows >= 64) {
     // prefill: one launch per sequence segment (a workgroup's queries share one sequence)
     for (int64_t q = qi0; q < qi0 + nrows;) {
       const int b = (int)(q / s.T);
@@ -662,50 +737,60 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
     }
     return hipSuccess;
   }
-  if (fast) {
-    const int64_t total = nrows * (int64_t)s.N;
+  const int64_t total = nrows * (int64_t)s.N;
+  const uint8_t* kp = static_cast<const uint8_t*>(k_I);
+  if (shape_ok && q_fmt == FMT_BF16 && k_fmt == FMT_BF16) {
+    // 8 waves per workgroup, ~2 tiles per wave: 256 workgroups at 16 x 8192 keys
     const uint16_t* qp = static_cast<const uint16_t*>(q_I);
-    const uint8_t* kp = static_cast<const uint8_t*>(k_I);
-    if (k_fmt == FMT_BF16) {
-      // 8 waves per workgroup, ~2 tiles per wave: 256 workgroups at 16 x 8192 keys
-      int it2 = 1;
-      while (it2 < 16 && (int64_t)2 * it2 * 32 * kDecWaves * 256 <= total) it2 *= 2;
-      const int kpw = kDecWaves * 32 * it2;
-      dim3 g2((s.N + kpw - 1) / kpw, (unsigned)nrows);
+    int it2 = 1;
+    while (it2 < 16 && (int64_t)2 * it2 * 32 * kDecWaves * 256 <= total) it2 *= 2;
+    const int kpw = kDecWaves * 32 * it2;
+    dim3 g2((s.N + kpw - 1) / kpw, (unsigned)nrows);
 #define DSA_DMA(I)                                                                          \
   return launch(indexer_decode_dma<I>, g2, kDecWaves * 64, 0, st, qp, w, kp, q_pos, s.T, s.N, \
                 s.m, qi0, scores, fm)
-      switch (it2) {
-        case 1: DSA_DMA(1);
-        case 2: DSA_DMA(2);
-        case 4: DSA_DMA(4);
-        case 8: DSA_DMA(8);
-        default: DSA_DMA(16);
-      }
+    switch (it2) {
+      case 1: DSA_DMA(1);
+      case 2: DSA_DMA(2);
+      case 4: DSA_DMA(4);
+      case 8: DSA_DMA(8);
+      default: DSA_DMA(16);
+    }
 #undef DSA_DMA
+  }
+  if (shape_ok && kmx && (q_fmt == FMT_BF16 || q_fmt == FMT_MXFP8)) {
+    // MX keys: 8 waves per workgroup, tiles of 64 (FP4) or 32 (FP8) keys, ~256 workgroups
+    const int tk = k_fmt == FMT_MXFP4 ? 64 : 32, max_it = 512 / tk;
+    int it = 1;
+    while (it < max_it && (int64_t)2 * it * tk * kDecWaves * 256 <= total) it *= 2;
+    const int kpw = kDecWaves * tk * it;
+    dim3 g((s.N + kpw - 1) / kpw, (unsigned)nrows);
+#define DSA_MX(KF, QM, I)                                                                     \
+  return launch(indexer_decode_mx_dma<KF, QM, I>, g, kDecWaves * 64, 0, st, q_I, q_scale, w, kp, \
+                k_scale, q_pos, s.T, s.N, s.m, qi0, scores, fm)
+#define DSA_MX_IT(KF, QM)        \
+  switch (it) {                  \
+    case 1: DSA_MX(KF, QM, 1);   \
+    case 2: DSA_MX(KF, QM, 2);   \
+    case 4: DSA_MX(KF, QM, 4);   \
+    case 8: DSA_MX(KF, QM, 8);   \
+    default:                     \
+      if constexpr (KF == FMT_MXFP8) { DSA_MX(KF, QM, 16); }  \
+      else { DSA_MX(KF, QM, 8); } \
+  }
+    if (k_fmt == FMT_MXFP4) {
+      if (q_fmt == FMT_MXFP8) DSA_MX_IT(FMT_MXFP4, true)
+      DSA_MX_IT(FMT_MXFP4, false)
     }
-    {
-      // MXFP4: 8 waves per workgroup, 64-key tiles, ~256 workgroups
-      int it4 = 1;
-      while (it4 < 8 && (int64_t)2 * it4 * kF4Tile * kDecWaves * 256 <= total) it4 *= 2;
-      const int kpw = kDecWaves * kF4Tile * it4;
-      dim3 g4((s.N + kpw - 1) / kpw, (unsigned)nrows);
-#define DSA_F4(I)                                                                              \
-  return launch(indexer_decode_fp4_dma<I>, g4, kDecWaves * 64, 0, st, qp, w, kp, k_scale,      \
-                q_pos, s.T, s.N, s.m, qi0, scores, fm)
-      switch (it4) {
-        case 1: DSA_F4(1);
-        case 2: DSA_F4(2);
-        case 4: DSA_F4(4);
-        default: DSA_F4(8);
-      }
-#undef DSA_F4
-    }
+    if (q_fmt == FMT_MXFP8) DSA_MX_IT(FMT_MXFP8, true)
+    DSA_MX_IT(FMT_MXFP8, false)
+#undef DSA_MX_IT
+#undef DSA_MX
   }
   dim3 grid((s.N + 255) / 256, (unsigned)nrows);
   size_t shm = sizeof(float) * ((size_t)s.H_I * s.D_I + s.H_I);
-  return launch(indexer_generic, grid, 256, shm, st, q_I, q_fmt, w, k_I, k_scale, k_fmt, q_pos, s.T,
-                s.N, s.m, s.H_I, s.D_I, qi0, scores, fm);
+  return launch(indexer_generic, grid, 256, shm, st, q_I, q_fmt, q_scale, w, k_I, k_scale, k_fmt,
+                q_pos, s.T, s.N, s.m, s.H_I, s.D_I, qi0, scores, fm);
 }
 
 }  // namespace dsa

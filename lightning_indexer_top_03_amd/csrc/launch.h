@@ -45,7 +45,7 @@ inline hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, size_t shm, hip
   return hipGetLastError();
 }
 
-enum Fmt { FMT_F32 = 0, FMT_BF16 = 1, FMT_MXFP4 = 2 };
+enum Fmt { FMT_F32 = 0, FMT_BF16 = 1, FMT_MXFP4 = 2, FMT_MXFP8 = 3 };
 
 struct Shape {
   int B, T, N, H_I, D_I, H, D_K, D_V, top_k, m, W;
@@ -61,9 +61,9 @@ hipError_t launch_compress(int B, int64_t n_raw, int D, int m, int fmt, const vo
 // ---- step 1 ----
 // scores: [nrows, N] row-relative. fill_masked: write -inf for s >= n_vis.
 hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void* q_I, int q_fmt,
-                          const float* w,
-                          const void* k_I, const uint8_t* k_scale, int k_fmt, const int32_t* q_pos,
-                          float* scores, bool fill_masked, hipStream_t st);
+                          const uint8_t* q_scale, const float* w, const void* k_I,
+                          const uint8_t* k_scale, int k_fmt, const int32_t* q_pos, float* scores,
+                          bool fill_masked, hipStream_t st);
 
 // ---- step 2 ----
 // scores: [nrows, N] row-relative, idx: [nrows, top_k] row-relative, rows qi0 .. qi0+nrows-1.

@@ -22,8 +22,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, MXFP4, F64 = 0, 1, 2, 3
-_DT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "f64": F64}
+F32, BF16, MXFP4, F64, MXFP8 = 0, 1, 2, 3, 4
+_DT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "f64": F64, "mxfp8": MXFP8}
 
 
 def build(force: bool = True) -> str:
@@ -50,20 +50,24 @@ def lib():
         L.orc_bf16_to_double.restype = dbl
         L.orc_e2m1_to_double.argtypes = [i32]
         L.orc_e2m1_to_double.restype = dbl
+        L.orc_e4m3_to_double.argtypes = [i32]
+        L.orc_e4m3_to_double.restype = dbl
         L.orc_e8m0_to_double.argtypes = [i32]
         L.orc_e8m0_to_double.restype = dbl
         L.orc_decode.argtypes = [i32, vp, i64, vp]
         L.orc_decode_mxfp4_row.argtypes = [vp, vp, i32, vp]
+        L.orc_decode_mxfp8_row.argtypes = [vp, vp, i32, vp]
         L.orc_compress_mean.argtypes = [i64, i32, i32, i32, vp, vp]
         L.orc_n_vis.argtypes = [i64, i32, i64]
         L.orc_n_vis.restype = i64
-        L.orc_scores_row.argtypes = [i32, i32, i64, i64, i32, vp, vp, i32, vp, vp, vp]
+        L.orc_scores_row.argtypes = [i32, i32, i64, i64, i32, vp, vp, vp, i32, vp, vp, vp]
         L.orc_topk_row.argtypes = [vp, i64, i32, vp]
         L.orc_topk_row.restype = i32
         L.orc_attend_row.argtypes = [i32, i32, i32, i32, vp, i32, vp, vp, i32, i32, vp, i64,
                                      i64, i64, i32, dbl, vp, vp]
         L.orc_max_threads.restype = i32
-        for f in ("orc_decode", "orc_decode_mxfp4_row", "orc_compress_mean", "orc_scores_row",
+        for f in ("orc_decode", "orc_decode_mxfp4_row", "orc_decode_mxfp8_row",
+                  "orc_compress_mean", "orc_scores_row",
                   "orc_attend_row"):
             getattr(L, f).restype = None
         _lib = L
@@ -112,6 +116,23 @@ def decode_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return out.reshape(codes.shape[:-1] + (D,))
 
 
+def decode_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP8 rows (e4m3 codes [..., D], scales [..., D/32]) -> fp64 [..., D]."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    D = codes.shape[-1]
+    c2 = codes.reshape(-1, D)
+    s2 = scales.reshape(-1, D // 32)
+    out = np.empty((c2.shape[0], D), np.float64)
+    for r in range(c2.shape[0]):
+        lib().orc_decode_mxfp8_row(_p(c2[r]), _p(s2[r]), D, _p(out[r]))
+    return out.reshape(codes.shape[:-1] + (D,))
+
+
+def e4m3(code: int) -> float:
+    return lib().orc_e4m3_to_double(code)
+
+
 def e2m1(code: int) -> float:
     return lib().orc_e2m1_to_double(code)
 
@@ -134,24 +155,36 @@ def n_vis(p: int, m: int, N: int) -> int:
 
 
 def scores_row(q_I: np.ndarray, w: np.ndarray, k_I, n_visible: int,
-               k_scale: Optional[np.ndarray] = None) -> np.ndarray:
-    """One query: q_I [H_I, D_I], w [H_I] fp32, k_I [N, D_I] (or MXFP4 codes [N, D_I/2] with
+               k_scale: Optional[np.ndarray] = None,
+               q_scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """One query: q_I [H_I, D_I] (or MXFP8 codes [H_I, D_I] uint8 with q_scale [H_I, D_I/32]),
+    w [H_I] fp32, k_I [N, D_I] (or MXFP4 codes [N, D_I/2] / MXFP8 codes [N, D_I], uint8, with
     k_scale [N, D_I/32]) -> fp64 scores [N] (-inf for s >= n_visible)."""
     q_I = np.ascontiguousarray(q_I)
     w = np.ascontiguousarray(w, np.float32)
     H_I, D_I = q_I.shape
+    if q_scale is not None:
+        qdt = MXFP8
+        q_I = np.ascontiguousarray(q_I, np.uint8)
+        q_scale = np.ascontiguousarray(q_scale, np.uint8)
+        assert q_scale.shape == (H_I, D_I // 32)
+    else:
+        qdt = _dt_of(q_I)
     k_I = np.ascontiguousarray(k_I)
+    N = k_I.shape[0]
     if k_scale is not None:
-        kdt = MXFP4
         k_scale = np.ascontiguousarray(k_scale, np.uint8)
-        N = k_I.shape[0]
-        assert k_I.shape[1] * 2 == D_I and k_scale.shape == (N, D_I // 32)
+        assert k_I.dtype == np.uint8 and k_scale.shape == (N, D_I // 32)
+        if k_I.shape[1] * 2 == D_I:
+            kdt = MXFP4
+        else:
+            assert k_I.shape[1] == D_I
+            kdt = MXFP8
     else:
         kdt = _dt_of(k_I)
-        N = k_I.shape[0]
         assert k_I.shape[1] == D_I
     out = np.empty(N, np.float64)
-    lib().orc_scores_row(H_I, D_I, N, int(n_visible), _dt_of(q_I), _p(q_I), _p(w), kdt,
+    lib().orc_scores_row(H_I, D_I, N, int(n_visible), qdt, _p(q_I), _p(q_scale), _p(w), kdt,
                          _p(k_I), _p(k_scale), _p(out))
     return out
 
@@ -236,12 +269,17 @@ class QueryRunner:
         c = self.cfg
         p = int(self.wl.q_pos()[b, t])
         nv = n_vis(p, c.m, c.N)
-        qI = self.wl.q_I()[b, t] if "q_I" in self.wl._cache else self.wl.q_I_rows(b, t)
         w = self.wl.w()[b, t]
-        if c.k_dt == "mxfp4":
+        qs = None
+        if c.qi_dt == "mxfp8":
+            qc, qsc = self.wl.q_I()
+            qI, qs = qc[b, t], qsc[b, t]
+        else:
+            qI = self.wl.q_I()[b, t] if "q_I" in self.wl._cache else self.wl.q_I_rows(b, t)
+        if c.k_dt in ("mxfp4", "mxfp8"):
             codes, sc = self.wl.k_I()
-            return scores_row(qI, w, codes[b], nv, k_scale=sc[b])
-        return scores_row(qI, w, self.wl.k_I()[b], nv)
+            return scores_row(qI, w, codes[b], nv, k_scale=sc[b], q_scale=qs)
+        return scores_row(qI, w, self.wl.k_I()[b], nv, q_scale=qs)
 
     def attend(self, b: int, t: int, idx: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
         c = self.cfg

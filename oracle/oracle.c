@@ -22,14 +22,15 @@
  * Sources: [P5] "DeepSeek-V3.2 sparse-attention principle and TPU adaptation" (trdm.cn);
  *          [P1] xhh.club "sparse" tag feed, DeepSeek-V4 CSA summary;
  *          [P4] Tencent Cloud developer search "compressed sparse attention (CSA)".
- * MXFP4 decoding follows the OCP Microscaling Formats spec v1.0 (e2m1 elements, E8M0 scales).
+ * MXFP4 / MXFP8 decoding follows the OCP Microscaling Formats spec v1.0 (e2m1 and e4m3
+ * elements, one E8M0 scale per 32 elements).
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_MXFP4 = 2, ORC_F64 = 3 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_MXFP4 = 2, ORC_F64 = 3, ORC_MXFP8 = 4 };
 
 /* ---- stored-value decoding (exact) ------------------------------------------------------ */
 
@@ -45,6 +46,15 @@ double orc_e2m1_to_double(int code) {
   int s = (code >> 3) & 1, e = (code >> 1) & 3, mbit = code & 1;
   double mag = (e == 0) ? 0.5 * mbit                      /* subnormal: 0 or 0.5 */
                         : ldexp(1.0 + 0.5 * mbit, e - 1); /* 1, 1.5, 2, 3, 4, 6 */
+  return s ? -mag : mag;
+}
+
+/* OCP e4m3 (FP8 "E4M3FN"): bit 7 sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa;
+ * exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN (no infinities). */
+double orc_e4m3_to_double(int code) {
+  int s = (code >> 7) & 1, e = (code >> 3) & 15, mant = code & 7;
+  if (e == 15 && mant == 7) return NAN;
+  double mag = (e == 0) ? ldexp(mant / 8.0, -6) : ldexp(1.0 + mant / 8.0, e - 7);
   return s ? -mag : mag;
 }
 
@@ -76,6 +86,11 @@ void orc_decode_mxfp4_row(const uint8_t* codes, const uint8_t* scales, int D, do
   }
 }
 
+/* One MXFP8 row of D values: e4m3 codes [D], scales [D/32]. */
+void orc_decode_mxfp8_row(const uint8_t* codes, const uint8_t* scales, int D, double* out) {
+  for (int i = 0; i < D; ++i) out[i] = orc_e4m3_to_double(codes[i]) * orc_e8m0_to_double(scales[i / 32]);
+}
+
 /* ---- step 0: CSA compression ------------------------------------------------------------ */
 
 /* One sequence: raw [n_raw, D] of dtype dt -> out [floor(n_raw/m), D] fp64 means. */
@@ -101,12 +116,19 @@ int64_t orc_n_vis(int64_t p, int m, int64_t N) {
 
 /* ---- step 1: lightning-indexer scores of one query -------------------------------------- */
 
-/* qI [H_I, D_I] (dtype qdt), w [H_I], kI [N, D_I] (dtype kdt; MXFP4: codes [N, D_I/2] and
- * kscale [N, D_I/32]) -> out[s] = score for s < n_vis, -inf for n_vis <= s < N. */
+/* qI [H_I, D_I] (dtype qdt; MXFP8: codes [H_I, D_I] and qscale [H_I, D_I/32]), w [H_I],
+ * kI [N, D_I] (dtype kdt; MXFP4: codes [N, D_I/2] and kscale [N, D_I/32]; MXFP8: codes
+ * [N, D_I] and kscale [N, D_I/32]) -> out[s] = score for s < n_vis, -inf for n_vis <= s < N. */
 void orc_scores_row(int H_I, int D_I, int64_t N, int64_t n_vis, int qdt, const void* qI,
-                    const float* w, int kdt, const void* kI, const uint8_t* kscale, double* out) {
+                    const uint8_t* qscale, const float* w, int kdt, const void* kI,
+                    const uint8_t* kscale, double* out) {
   double* q = (double*)malloc(sizeof(double) * (size_t)H_I * D_I);
-  orc_decode(qdt, qI, (int64_t)H_I * D_I, q);
+  if (qdt == ORC_MXFP8)
+    for (int j = 0; j < H_I; ++j)
+      orc_decode_mxfp8_row((const uint8_t*)qI + (int64_t)j * D_I, qscale + (int64_t)j * (D_I / 32),
+                           D_I, q + (int64_t)j * D_I);
+  else
+    orc_decode(qdt, qI, (int64_t)H_I * D_I, q);
 #pragma omp parallel
   {
     double* k = (double*)malloc(sizeof(double) * (size_t)D_I);
@@ -118,6 +140,8 @@ void orc_scores_row(int H_I, int D_I, int64_t N, int64_t n_vis, int qdt, const v
       }
       if (kdt == ORC_MXFP4)
         orc_decode_mxfp4_row((const uint8_t*)kI + s * (D_I / 2), kscale + s * (D_I / 32), D_I, k);
+      else if (kdt == ORC_MXFP8)
+        orc_decode_mxfp8_row((const uint8_t*)kI + s * D_I, kscale + s * (D_I / 32), D_I, k);
       else
         for (int d = 0; d < D_I; ++d) k[d] = ld(kdt, kI, s * (int64_t)D_I + d);
       double I = 0.0;

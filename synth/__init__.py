@@ -50,6 +50,8 @@ def lib():
         L.synth_uniform_f32.argtypes = [u64, u64, i64, i64, dbl, dbl, vp]
         L.synth_normal_mxfp4.argtypes = [u64, u64, i64, i64, ctypes.c_int, dbl, vp, vp]
         L.synth_mxfp4_block.argtypes = [vp, vp, vp]
+        L.synth_normal_mxfp8.argtypes = [u64, u64, i64, i64, ctypes.c_int, dbl, vp, vp]
+        L.synth_mxfp8_block.argtypes = [vp, vp, vp]
         L.synth_bf16_from_double.argtypes = [dbl]
         L.synth_bf16_from_double.restype = ctypes.c_uint16
         L.synth_splitmix64.argtypes = [u64]
@@ -59,7 +61,8 @@ def lib():
         L.synth_normal_at.argtypes = [u64, u64, i64]
         L.synth_normal_at.restype = dbl
         for f in ("synth_normal_f32", "synth_normal_bf16", "synth_uniform_f32",
-                  "synth_normal_mxfp4", "synth_mxfp4_block"):
+                  "synth_normal_mxfp4", "synth_mxfp4_block", "synth_normal_mxfp8",
+                  "synth_mxfp8_block"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -107,6 +110,25 @@ def mxfp4_block(x: np.ndarray):
     codes = np.empty(16, np.uint8)
     sc = np.empty(1, np.uint8)
     lib().synth_mxfp4_block(_ptr(x), _ptr(codes), _ptr(sc))
+    return codes, int(sc[0])
+
+
+def normal_mxfp8(seed: int, tid: int, rows: int, D: int, scale: float = 1.0, start_row: int = 0):
+    """MXFP8 rows of N(0,1)*scale: (e4m3 codes [rows, D] uint8, scales [rows, D/32] uint8)."""
+    assert D % 32 == 0
+    codes = np.empty((rows, D), np.uint8)
+    scales = np.empty((rows, D // 32), np.uint8)
+    lib().synth_normal_mxfp8(seed, tid, start_row, rows, D, scale, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def mxfp8_block(x: np.ndarray):
+    """Quantise 32 fp64 values to (32 e4m3 code bytes, 1 scale byte)."""
+    x = np.ascontiguousarray(x, np.float64)
+    assert x.shape == (32,)
+    codes = np.empty(32, np.uint8)
+    sc = np.empty(1, np.uint8)
+    lib().synth_mxfp8_block(_ptr(x), _ptr(codes), _ptr(sc))
     return codes, int(sc[0])
 
 

@@ -16,6 +16,8 @@ Recipes (all seeded; seed = workload id, "sharp" variants use seed 100 + id):
   hca_decode   B=4 T=1 N=8192 blocks of a 1,048,576-token context compressed 128:1 (HCA: no
             indexer, every visible block attends); kv_c ~ N(0,1)/(24 sqrt(128)) (the law of a
             128-token mean of N(0,1)/24); the 128 raw window rows ~ N(0,1)/24; position 1048575
+  decode_fp8   decode with an MXFP8 indexer: q_I and k_I N(0,1) quantised to e4m3 with one
+            E8M0 scale per 32 (2^(floor(log2 amax) - 8), RNE, saturating at 448)
   hca_prefill  raw 131072 tokens (kv_raw ~ N(0,1)/24) -> m=128 -> N=1024 blocks; last 8192
             queries (positions 122880..131071); W=128
   sharp variants: q, kv ~ N(0,1) and softmax scale 4/sqrt(D_K), so that attention outputs are
@@ -29,7 +31,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-from . import (TID_KI, TID_KV, TID_Q, TID_QI, TID_W, TID_WIN, normal, normal_mxfp4,
+from . import (TID_KI, TID_KV, TID_Q, TID_QI, TID_W, TID_WIN, normal, normal_mxfp4, normal_mxfp8,
                uniform)
 
 
@@ -49,7 +51,8 @@ class Config:
     m: int = 1
     W: int = 0
     dt: str = "bf16"          # dtype of q_I, q, kv, kv_raw, out
-    k_dt: str = "bf16"        # dtype of k_I: dt or "mxfp4"
+    k_dt: str = "bf16"        # dtype of k_I: dt, "mxfp4" or "mxfp8"
+    qi_dt: str = ""           # dtype of q_I: dt ("" ) or "mxfp8"
     pos0: int = 0             # q_pos[b, t] = pos0 + pos_stride * t
     pos_stride: int = 1
     qkv_std: float = 0.0      # std of q and kv rows (0 -> 1/sqrt(D_K))
@@ -111,6 +114,8 @@ CONFIGS: Dict[str, Config] = {
     "csa_decode": Config("csa_decode", 5, B=4, T=1, N=262144, H_I=64, D_I=128, H=128, D_K=576,
                          D_V=512, top_k=1024, m=4, W=128, k_dt="mxfp4", pos0=1048575,
                          n_raw=128, raw_base=1048576 - 128, kv_std=1.0 / 48, win_std=1.0 / 24),
+    "decode_fp8": Config("decode_fp8", 8, B=16, T=1, N=8192, H_I=64, D_I=128, H=128, D_K=576,
+                         D_V=512, top_k=2048, pos0=8191, qi_dt="mxfp8", k_dt="mxfp8"),
     "hca_decode": Config("hca_decode", 6, B=4, T=1, N=8192, H_I=64, D_I=128, H=128, D_K=576,
                          D_V=512, top_k=8192, m=128, W=128, pos0=1048575, n_raw=128,
                          raw_base=1048576 - 128, kv_std=1.0 / (24 * math.sqrt(128)),
@@ -135,8 +140,15 @@ class Workload:
     def q_pos(self) -> np.ndarray:
         return self.cfg.positions()
 
-    def q_I(self) -> np.ndarray:
+    def q_I(self):
+        """[B,T,H_I,D_I] in dt, or (codes [B,T,H_I,D_I], scales [B,T,H_I,D_I/32]) for MXFP8."""
         c = self.cfg
+        if c.qi_dt == "mxfp8":
+            def mk():
+                codes, sc = normal_mxfp8(c.seed, TID_QI, c.B * c.T * c.H_I, c.D_I, 1.0)
+                return (codes.reshape(c.B, c.T, c.H_I, c.D_I),
+                        sc.reshape(c.B, c.T, c.H_I, c.D_I // 32))
+            return self._get("q_I", mk)
         return self._get("q_I", lambda: normal(c.seed, TID_QI, (c.B, c.T, c.H_I, c.D_I), 1.0, c.dt))
 
     def w(self) -> np.ndarray:
@@ -144,8 +156,14 @@ class Workload:
         return self._get("w", lambda: uniform(c.seed, TID_W, (c.B, c.T, c.H_I), 0.0, 1.0))
 
     def k_I(self):
-        """[B,N,D_I] in dt, or (codes [B,N,D_I/2], scales [B,N,D_I/32]) for MXFP4."""
+        """[B,N,D_I] in dt, or (codes [B,N,D_I/2], scales [B,N,D_I/32]) for MXFP4, or
+        (codes [B,N,D_I], scales [B,N,D_I/32]) for MXFP8."""
         c = self.cfg
+        if c.k_dt == "mxfp8":
+            def mk8():
+                codes, sc = normal_mxfp8(c.seed, TID_KI, c.B * c.N, c.D_I, 1.0)
+                return codes.reshape(c.B, c.N, c.D_I), sc.reshape(c.B, c.N, c.D_I // 32)
+            return self._get("k_I", mk8)
         if c.k_dt == "mxfp4":
             def mk():
                 codes, sc = normal_mxfp4(c.seed, TID_KI, c.B * c.N, c.D_I, 1.0)
@@ -192,6 +210,7 @@ class Workload:
 
     def q_I_rows(self, b: int, t: int) -> np.ndarray:
         c = self.cfg
+        assert c.qi_dt != "mxfp8", "MXFP8 q_I is generated whole"
         start = ((b * c.T + t) * c.H_I) * c.D_I
         return normal(c.seed, TID_QI, (c.H_I, c.D_I), 1.0, c.dt, start=start)
 

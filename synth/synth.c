@@ -146,6 +146,60 @@ void synth_normal_mxfp4(uint64_t seed, uint64_t tensor_id, int64_t start_row, in
 }
 
 /* Raw words, for generator self-tests. */
+/* |a| -> e4m3 (OCP E4M3FN) code 0..0x7E, round-to-nearest-even, saturating at 448. */
+static int e4m3_code(double a) {
+  if (a >= 448.0) return 0x7E;
+  if (a < ldexp(1.0, -6)) {               /* subnormal grid: multiples of 2^-9 */
+    double n = rint(a * 512.0);            /* 0 .. 8; 8 is the smallest normal */
+    return (int)n;                          /* code 8 == exponent field 1, mantissa 0 */
+  }
+  int k;
+  frexp(a, &k);                            /* a = f 2^k, f in [0.5, 1) */
+  int e = k - 1;                           /* floor(log2 a), -6 .. 8 */
+  double n = rint(ldexp(a, 3 - e));        /* 8 .. 16 on the grid 2^(e-3) */
+  if (n == 16.0) {
+    e += 1;
+    n = 8.0;
+  }
+  if (e > 8 || (e == 8 && n > 14.0)) return 0x7E;
+  return ((e + 7) << 3) | ((int)n - 8);
+}
+
+/* One MXFP8 block: 32 values -> 32 e4m3 codes + one E8M0 scale (OCP MX: scale
+ * 2^(floor(log2 amax) - 8), the largest e4m3 binade, magnitudes saturating at 448). */
+void synth_mxfp8_block(const double* x, uint8_t* codes32, uint8_t* scale) {
+  double amax = 0.0;
+  for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(x[i]));
+  int e;
+  if (amax == 0.0) {
+    e = -127;
+  } else {
+    int k;
+    frexp(amax, &k);
+    e = k - 1 - 8;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+  }
+  *scale = (uint8_t)(e + 127);
+  for (int i = 0; i < 32; ++i) {
+    double v = ldexp(x[i], -e);
+    codes32[i] = (uint8_t)(e4m3_code(fabs(v)) | (v < 0 ? 0x80 : 0));
+  }
+}
+
+void synth_normal_mxfp8(uint64_t seed, uint64_t tensor_id, int64_t start_row, int64_t rows,
+                        int D, double scale, uint8_t* codes, uint8_t* scales) {
+  const uint64_t key = stream_key(seed, tensor_id);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    double blk[32];
+    for (int b = 0; b < D / 32; ++b) {
+      for (int i = 0; i < 32; ++i) blk[i] = scale * normal(key, (start_row + r) * (int64_t)D + 32 * b + i);
+      synth_mxfp8_block(blk, codes + r * (int64_t)D + 32 * b, scales + r * (int64_t)(D / 32) + b);
+    }
+  }
+}
+
 uint64_t synth_splitmix64(uint64_t x) { return splitmix64(x); }
 double synth_uniform_at(uint64_t seed, uint64_t tensor_id, int64_t i, int j) {
   return unif(stream_key(seed, tensor_id), i, j);

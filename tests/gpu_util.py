@@ -55,10 +55,11 @@ class DeviceWorkload:
         t0 = time.time()
         self.q_pos = to_dev(wl.q_pos())
         if not c.dense:  # HCA has no indexer
-            self.q_I = to_dev(wl.q_I())
+            q = wl.q_I()
+            self.q_I = (to_dev(q[0]), to_dev(q[1])) if c.qi_dt == "mxfp8" else to_dev(q)
             self.w = to_dev(wl.w())
             k = wl.k_I()
-            self.k_I = (to_dev(k[0]), to_dev(k[1])) if c.k_dt == "mxfp4" else to_dev(k)
+            self.k_I = (to_dev(k[0]), to_dev(k[1])) if c.k_dt in ("mxfp4", "mxfp8") else to_dev(k)
         rows = c.B * c.T
         if rows * c.H * c.D_K > (1 << 28):
             # generate q in chunks straight into the device tensor

@@ -46,13 +46,15 @@ def _dims(**kw):
     return dsa.Dims(*[base[n] for n, _ in dsa.Dims._fields_])
 
 
-def _idx_call(d, q_dt=dsa.BF16, k_dt=dsa.BF16, q_I=P, w=P, k_I=P, k_scale=None, q_pos=P, sc=P):
-    return L.indexer_scores(ctypes.byref(d), q_I, q_dt, w, k_I, k_scale, k_dt, q_pos, sc, None)
+def _idx_call(d, q_dt=dsa.BF16, k_dt=dsa.BF16, q_I=P, w=P, k_I=P, k_scale=None, q_pos=P, sc=P,
+              q_scale=None):
+    return L.indexer_scores(ctypes.byref(d), q_I, q_dt, q_scale, w, k_I, k_scale, k_dt, q_pos, sc,
+                            None)
 
 
 def test_indexer_validation():
     d = _dims()
-    assert L.indexer_scores(None, P, 1, P, P, None, 1, P, P, None) == 1      # NULL dims
+    assert L.indexer_scores(None, P, 1, None, P, P, None, 1, P, P, None) == 1  # NULL dims
     assert _idx_call(d, q_I=None) == 1                                         # NULL q_I
     assert _idx_call(d, q_pos=None) == 1
     assert _idx_call(_dims(N=0)) == 2                                          # bad shape
@@ -65,6 +67,15 @@ def test_indexer_validation():
     assert _idx_call(_dims(H_I=128, D_I=128), q_dt=dsa.F32, k_dt=dsa.F32) == 2 # generic LDS cap
     assert _idx_call(d, q_I=P + 8) == 4                                        # misaligned
     assert _idx_call(d, sc=P + 4) == 4
+    # MXFP8: q_I and/or k_I, each with its scales
+    mx = dict(k_dt=dsa.MXFP8, k_scale=P)
+    assert _idx_call(d, k_dt=dsa.MXFP8) == 1                                   # FP8 w/o scales
+    assert _idx_call(d, q_dt=dsa.MXFP8, **mx) == 1                             # q w/o scales
+    assert _idx_call(d, q_dt=dsa.MXFP8, q_scale=P, k_dt=dsa.BF16) == 3         # fp8 q, bf16 k
+    assert _idx_call(d, q_dt=dsa.F32, **mx) == 3                               # fp32 q, MX k
+    assert _idx_call(d, q_scale=P, **mx) == 3                                  # scales, bf16 q
+    assert _idx_call(_dims(D_I=48), q_dt=dsa.MXFP8, q_scale=P, **mx) == 2      # D_I % 32
+    assert _idx_call(d, q_dt=dsa.MXFP8, q_scale=P + 2, **mx) == 4              # scale alignment
 
 
 def test_topk_validation():

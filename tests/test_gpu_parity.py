@@ -59,9 +59,11 @@ def test_compress_mean(dt):
 def _run_indexer(c, label):
     wl = synth.make_workload(c)
     k = wl.k_I()
-    kdev = (to_dev(k[0]), to_dev(k[1])) if c.k_dt == "mxfp4" else to_dev(k)
-    log(f"[indexer {label}] B={c.B} T={c.T} N={c.N} k_dt={c.k_dt}")
-    sc = dsa.indexer_scores(to_dev(wl.q_I()), to_dev(wl.w()), kdev, to_dev(wl.q_pos()), m=c.m)
+    kdev = (to_dev(k[0]), to_dev(k[1])) if c.k_dt in ("mxfp4", "mxfp8") else to_dev(k)
+    q = wl.q_I()
+    qdev = (to_dev(q[0]), to_dev(q[1])) if c.qi_dt == "mxfp8" else to_dev(q)
+    log(f"[indexer {label}] B={c.B} T={c.T} N={c.N} q_I={c.qi_dt or c.dt} k_dt={c.k_dt}")
+    sc = dsa.indexer_scores(qdev, to_dev(wl.w()), kdev, to_dev(wl.q_pos()), m=c.m)
     torch.cuda.synchronize()
     sc = to_host(sc)
     run = oracle.QueryRunner(wl)
@@ -103,6 +105,23 @@ def test_indexer_mxfp4_keys():
     c = _cfg("csa_decode", B=2, N=5003, pos0=4 * 5003 - 1, name="idx_fp4")
     _run_indexer(c, "mxfp4")
     _run_indexer(c.with_(pos0=4 * 4000 + 2, name="idx_fp4_partial"), "mxfp4-partial")
+
+
+def test_indexer_mxfp8_keys_and_queries():
+    # fp8 keys against bf16 queries (two-part split) and against fp8 queries (one MFMA / step),
+    # ragged N, positions before and past the end of the keys
+    c = _cfg("decode", B=3, N=5003, pos0=4999, k_dt="mxfp8", name="idx_fp8")
+    _run_indexer(c, "mxfp8-keys")
+    _run_indexer(c.with_(qi_dt="mxfp8", pos0=3001, name="idx_fp8q"), "mxfp8-both")
+    # fp8 queries against FP4 blocks (CSA), many rows in one call
+    _run_indexer(_cfg("csa_decode", B=1, T=96, N=3001, pos0=4 * 2900, pos_stride=5,
+                      qi_dt="mxfp8", name="idx_fp8q_fp4k"), "mxfp8-q-fp4-k")
+    _run_indexer(_cfg("decode", B=1, T=70, N=2100, pos0=2030, qi_dt="mxfp8", k_dt="mxfp8",
+                      name="idx_fp8_rows"), "mxfp8-rows")
+    # the scalar kernel (4 heads x 32 dims)
+    _run_indexer(_cfg("tiny", dt="bf16", k_dt="mxfp8", name="tiny_fp8"), "tiny-fp8")
+    _run_indexer(_cfg("tiny", dt="bf16", k_dt="mxfp8", qi_dt="mxfp8", name="tiny_fp8q"),
+                 "tiny-fp8-both")
 
 
 def test_indexer_generic_fp32_and_small_heads():

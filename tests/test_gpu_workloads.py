@@ -74,6 +74,11 @@ def test_decode():
     _run(synth.CONFIGS["decode"].sharp())
 
 
+def test_decode_fp8_indexer():
+    _run(synth.CONFIGS["decode_fp8"])
+    _run(synth.CONFIGS["decode_fp8"].sharp())
+
+
 def test_csa_decode_fp4():
     _run(synth.CONFIGS["csa_decode"])
     _run(synth.CONFIGS["csa_decode"].sharp())

@@ -89,6 +89,58 @@ def _h1():
     return g, k, q, w
 
 
+def test_e4m3_every_code_matches_torch_float8():
+    """OCP e4m3 (E4M3FN) decoding against torch's own float8_e4m3fn dtype, all 256 codes."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.e4m3(int(c)) for c in codes])
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ref[fin], got[fin])
+    assert np.array_equal(np.signbit(ref[fin]), np.signbit(got[fin]))  # -0 for 0x80
+
+
+def test_e8m0_matches_torch_float8_e8m0():
+    b = np.arange(255, dtype=np.uint8)  # 0xFF is NaN
+    ref = torch.from_numpy(b).view(torch.float8_e8m0fnu).double().numpy()
+    assert np.array_equal(ref, np.array([oracle.e8m0(int(x)) for x in b]))
+
+
+def test_mxfp8_hand_bytes_and_one_scale_per_32():
+    # 0x38 = +1.0, 0xFE = -448 (largest finite), 0x01 = 2^-9 (smallest subnormal)
+    codes = np.array([[0x38] * 32 + [0xFE] * 31 + [0x01]], np.uint8)
+    scales = np.array([[127, 130]], np.uint8)  # 2^0, 2^3
+    row = oracle.decode_mxfp8(codes, scales)[0]
+    assert (row[:32] == 1.0).all() and (row[32:63] == -448.0 * 8).all()
+    assert row[63] == 2.0 ** -9 * 8
+
+
+def test_mxfp8_quantiser_rounds_like_torch():
+    """The generator's e4m3 rounding (RNE, saturating at 448) against torch's cast, on random
+    values, exact ties between neighbouring codes and the saturation edge."""
+    rng = np.random.default_rng(3)
+    grid = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    ties = (grid[1:] + grid[:-1]) / 2
+    x = np.concatenate([rng.standard_normal(4000) * 50, ties, -ties, [447.0, 448.0, 460.0, 463.9]])
+    for i in range(0, x.size - x.size % 32, 32):
+        blk = x[i:i + 32].copy()
+        blk[0] = 300.0  # pin the block scale to 2^0 so that codes are e4m3 of the values
+        codes, sc = synth.mxfp8_block(blk)
+        assert sc == 127
+        ref = torch.from_numpy(blk).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(codes, ref), (blk, codes, ref)
+
+
+def test_scores_mxfp8_paths_equal_decoded_values():
+    kc, ks = synth.normal_mxfp8(7, 2, 64, 128)
+    qc, qs = synth.normal_mxfp8(7, 1, 4, 128)
+    w = synth.uniform(7, 3, (4,), 0.0, 1.0)
+    got = oracle.scores_row(qc, w, kc, 60, k_scale=ks, q_scale=qs)
+    ref = oracle.scores_row(oracle.decode_mxfp8(qc, qs), w, oracle.decode_mxfp8(kc, ks), 60)
+    np.testing.assert_array_equal(got, ref)
+    assert np.isneginf(got[60:]).all()
+
+
 def test_h1_scores_and_masking():
     g, k, q, w = _h1()
     for case in g["cases"]:
