@@ -30,6 +30,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0  # dense fp8 MFMA (the block-scaled fp8 x fp8 / fp8 x fp4 instructions)
+FP8_KERNELS = ("indexer_prefill_mx", "indexer_decode_mx_dma")
 METRIC = "query tokens/sec (indexer+top-k+sparse MLA); % of peak HBM BW / MFMA"
 
 WORKLOAD_TEXT = {
@@ -46,6 +48,9 @@ WORKLOAD_TEXT = {
     "decode_fp8": "decode DSA with an MXFP8 indexer (e4m3 q_I and k_I, one E8M0 scale per 32): "
                   "B=16 x 1 query, context L=8192, indexer 64x128, top-k 2048, sparse MQA-MLA "
                   "128 heads, key 576 / value 512 (bf16)",
+    "prefill_fp8": "prefill DSA with an MXFP8 indexer (e4m3 q_I and k_I, one E8M0 scale per "
+                   "32): 1 sequence, L=T=32768 causal, top-k 2048, 128 heads, key 576 / value "
+                   "512 (bf16)",
     "hca_decode": "HCA decode: B=4 x 1 query over 1,048,576 tokens compressed 128:1 (8192 blocks), "
                   "dense attention over every visible block + 128-token raw window, 128 heads, "
                   "key 576 / value 512 (bf16)",
@@ -74,6 +79,8 @@ def _kernel_plan(cfg, nsplit):
     rows = cfg.B * cfg.T
     if fast and cfg.k_dt == "bf16" and rows >= 64:
         names.append("indexer_prefill_mfma")
+    elif fast and cfg.qi_dt == "mxfp8" and rows >= 64:
+        names.append("indexer_prefill_mx")
     elif fast and cfg.k_dt == "bf16":
         names.append("indexer_decode_dma")
     elif fast:
@@ -384,9 +391,11 @@ def main():
     byt, fl = _algorithmic(cfg, dname)
     dur = tot[dname] * 1e-3  # per step; equals the launch duration when there is one chunk
     intensity = fl / byt if byt else 0.0
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    # a contraction is held to the peak of the dtype its MFMAs take
+    peak = FP8_PEAK_TFLOPS if dname in FP8_KERNELS else BF16_PEAK_TFLOPS
+    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     if fl and intensity > ridge:
-        roof = {"bound": "mfma", "achieved": round(fl / dur / 1e12, 2), "peak": BF16_PEAK_TFLOPS,
+        roof = {"bound": "mfma", "achieved": round(fl / dur / 1e12, 2), "peak": peak,
                 "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": round(byt / dur / 1e9, 1), "peak": HBM_PEAK_GBS,

@@ -637,6 +637,182 @@ __global__ __launch_bounds__(256) void indexer_prefill_mfma(
 }
 
 // ------------------------------------------------------------------------------------------
+// Prefill-shaped kernel, MXFP8 q_I with MX keys (MXFP8 or MXFP4), on the block-scaled MFMA:
+// the structure of indexer_prefill_mfma (a workgroup = kPfQ queries of one sequence x the key
+// blocks g, g + gridDim.x, ..., each wave holding 64 keys as B operands in registers, q_I and w
+// streamed through a 3-stage LDS ring by DMA two queries ahead), with the operands in their
+// stored codes: per query and wave, 8 v_mfma_scale_f32_32x32x64_f8f6f4 (2 head blocks x 2 key
+// blocks x 2 steps of 64 dims) in place of 32 v_mfma_f32_32x32x16_bf16. Operand layouts as in
+// indexer_decode_mx_dma. A query's ring stage: 8 KB of e4m3 codes (row hr keeps its 16-byte
+// chunk c in slot c ^ ((hr >> 1) & 7)), its 256 scale bytes and its 64 weights.
+// ------------------------------------------------------------------------------------------
+constexpr int kPfMxStage = 64 * 128 + 256 + 256;
+
+template <int KFMT>
+__global__ __launch_bounds__(256) void indexer_prefill_mx(
+    const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qsc, const float* __restrict__ w,
+    const uint8_t* __restrict__ kI, const uint8_t* __restrict__ ksc,
+    const int32_t* __restrict__ q_pos, int T, int N, int m, int b, int t0, int nt,
+    float* __restrict__ scores, int fill_masked) {
+  using K = MxKeys<KFMT>;
+  __shared__ __attribute__((aligned(16))) char sq[3][kPfMxStage];
+  __shared__ int snv[kPfQ];
+  __shared__ int smax;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int item = xcd_item(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+  const int kgrp = item % gridDim.x;
+  const int r0 = (item / gridDim.x) * kPfQ;  // first row (relative to t0) of this tile
+  const int nrows = min(kPfQ, nt - r0);
+  const int64_t qi0 = (int64_t)b * T + t0 + r0;
+
+  if (tid == 0) smax = 0;
+  __syncthreads();
+  if (tid < nrows) {
+    int v = n_visible(q_pos[qi0 + tid], m, N);
+    snv[tid] = v;
+    atomicMax(&smax, v);
+  }
+  __syncthreads();
+  const int maxnv = smax;
+  const size_t base_row = (size_t)b * N;
+  const uint32_t qlds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)&sq[0][0]);
+  for (int kblk = kgrp; kblk * kPfKeys < N; kblk += gridDim.x) {
+    const int kbase = kblk * kPfKeys;
+    if (kbase >= maxnv) {
+      if (fill_masked)
+        for (int r = 0; r < nrows; ++r)
+          for (int s = kbase + tid; s < min(kbase + kPfKeys, N); s += 256)
+            scores[(size_t)(r0 + r) * N + s] = kNegInf;
+      continue;
+    }
+
+    // this wave's keys as B operands: key kbase + 64 wv + 32 kb + n, step s2
+    i32x8_t kf[2][2];
+    uint32_t ksw[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const size_t krow = base_row + min(kbase + 64 * wv + 32 * kb + n, N - 1);
+      const uint8_t* p = kI + krow * K::kRow;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        if constexpr (KFMT == FMT_MXFP4) {
+          const u32x4_t c4 = *reinterpret_cast<const u32x4_t*>(p + 16 * (2 * s2 + h));
+          kf[kb][s2] = i32x8_t{(int)c4[0], (int)c4[1], (int)c4[2], (int)c4[3], 0, 0, 0, 0};
+        } else {
+          const u32x4_t lo4 = *reinterpret_cast<const u32x4_t*>(p + 16 * (4 * s2 + h));
+          const u32x4_t hi4 = *reinterpret_cast<const u32x4_t*>(p + 16 * (4 * s2 + 2 + h));
+          kf[kb][s2] = i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                               (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+        }
+      }
+      ksw[kb] = *reinterpret_cast<const uint32_t*>(ksc + krow * 4);
+    }
+
+    // DMA of query r into stage buf: wave wv moves code rows 16 wv .. 16 wv + 15 (two 1 KB
+    // instructions); wave 0 also moves w (16 lanes x 16 B), wave 1 the scales (64 lanes x 4 B).
+    // Waves 0 and 1 issue 3 instructions per query, waves 2 and 3 two.
+    auto stage = [&](int r, int buf) {
+      const uint8_t* src = qI + (size_t)(qi0 + r) * (64 * 128);
+      const uint32_t sb = qlds + buf * kPfMxStage;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int u = 2 * wv + j, hr = 8 * u + (lane >> 3), c = lane & 7;
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(src + hr * 128 + 16 * (c ^ ((hr >> 1) & 7))),
+            (lds_void_t*)(uintptr_t)(sb + 1024 * u), 16, 0, 0);
+      }
+      if (wv == 0 && lane < 16)
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(w + (size_t)(qi0 + r) * 64 + 4 * lane),
+            (lds_void_t*)(uintptr_t)(sb + 8192 + 256), 16, 0, 0);
+      if (wv == 1)
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(qsc + ((size_t)(qi0 + r) * 64 + lane) * 4),
+            (lds_void_t*)(uintptr_t)(sb + 8192), 4, 0, 0);
+    };
+    stage(0, 0);
+    if (nrows > 1) stage(1, 1);
+
+    for (int r = 0; r < nrows; ++r) {
+      const int buf = r % 3;
+      // query r landed (query r+1's DMAs may still be in flight), then every wave's share is
+      // visible after the barrier; stage (r+2)%3 was last read in iteration r-1
+      if (r + 1 < nrows) {
+        if (wv < 2) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      if (r + 2 < nrows) stage(r + 2, (r + 2) % 3);
+      const int nv = snv[r];
+      float* srow = scores + (size_t)(r0 + r) * N;
+      if (kbase < nv) {
+        const char* qb = &sq[buf][0];
+        i32x8_t a[2][2];
+        uint32_t qsw[2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int hr = 32 * hb + n;
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int c0 = 4 * s2 + h, c1 = 4 * s2 + 2 + h;
+            const u32x4_t lo4 = *reinterpret_cast<const u32x4_t*>(qb + hr * 128 + 16 * (c0 ^ ((hr >> 1) & 7)));
+            const u32x4_t hi4 = *reinterpret_cast<const u32x4_t*>(qb + hr * 128 + 16 * (c1 ^ ((hr >> 1) & 7)));
+            a[hb][s2] = i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                                (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+          }
+          qsw[hb] = *reinterpret_cast<const uint32_t*>(qb + 8192 + 4 * hr);
+        }
+        f32x16_t acc[2][2] = {};
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int qs = (int)((qsw[hb] >> (8 * (2 * s2 + h))) & 0xffu);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              const int ks = (int)((ksw[kb] >> (8 * (2 * s2 + h))) & 0xffu);
+              acc[hb][kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  a[hb][s2], kf[kb][s2], acc[hb][kb], 0, K::kFmt, 0, qs, 0, ks);
+            }
+          }
+        // lane (n, h) holds rows 8*(i/4) + 4*h + i%4 of each 32-head block: w of those heads
+        const float* wb = reinterpret_cast<const float*>(qb + 8192 + 256);
+        float part[2] = {0.f, 0.f};
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(wb + hb * 32 + 8 * q4 + 4 * h);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              part[0] += w4[i] * relu_bits(acc[hb][0][4 * q4 + i]);
+              part[1] += w4[i] * relu_bits(acc[hb][1][4 * q4 + i]);
+            }
+          }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[kb]), __float_as_uint(part[kb]), false, false);
+          const float v = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
+          int s = kbase + 64 * wv + 32 * kb + n;
+          if (h == 0 && s < N && (fill_masked || s < nv)) srow[s] = (s < nv) ? v : kNegInf;
+        }
+      } else if (fill_masked) {
+        for (int s = kbase + tid; s < min(kbase + kPfKeys, N); s += 256) srow[s] = kNegInf;
+      }
+    }
+    // every wave is done with the ring before the next key block restages it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // Generic scalar kernel: any H_I * D_I <= 16384, fp32 / bf16 queries, fp32 / bf16 / MXFP4 keys.
 // One thread per key; q_I and w of the query row in LDS (as fp32).
 // ------------------------------------------------------------------------------------------
@@ -732,6 +908,27 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
                             static_cast<const uint16_t*>(q_I), w,
                             static_cast<const uint16_t*>(k_I), q_pos, s.T, s.N, s.m, b, t0, nt,
                             scores + (size_t)(q - qi0) * s.N, fm);
+      if (e != hipSuccess) return e;
+      q = seg_end;
+    }
+    return hipSuccess;
+  }
+  if (shape_ok && q_fmt == FMT_MXFP8 && kmx && nrows >= 64) {
+    // prefill with an MXFP8 q_I: one launch per sequence segment, as above
+    for (int64_t q = qi0; q < qi0 + nrows;) {
+      const int b = (int)(q / s.T);
+      const int64_t seg_end = std::min<int64_t>(qi0 + nrows, (int64_t)(b + 1) * s.T);
+      const int t0 = (int)(q - (int64_t)b * s.T);
+      const int nt = (int)(seg_end - q);
+      dim3 grid(std::min((s.N + kPfKeys - 1) / kPfKeys, kPfKeyGroups), (nt + kPfQ - 1) / kPfQ);
+      const uint8_t* qp = static_cast<const uint8_t*>(q_I);
+      const uint8_t* kp = static_cast<const uint8_t*>(k_I);
+      float* sc = scores + (size_t)(q - qi0) * s.N;
+      hipError_t e = k_fmt == FMT_MXFP4
+          ? launch(indexer_prefill_mx<FMT_MXFP4>, grid, 256, 0, st, qp, q_scale, w, kp, k_scale,
+                   q_pos, s.T, s.N, s.m, b, t0, nt, sc, fm)
+          : launch(indexer_prefill_mx<FMT_MXFP8>, grid, 256, 0, st, qp, q_scale, w, kp, k_scale,
+                   q_pos, s.T, s.N, s.m, b, t0, nt, sc, fm);
       if (e != hipSuccess) return e;
       q = seg_end;
     }

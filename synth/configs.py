@@ -16,8 +16,9 @@ Recipes (all seeded; seed = workload id, "sharp" variants use seed 100 + id):
   hca_decode   B=4 T=1 N=8192 blocks of a 1,048,576-token context compressed 128:1 (HCA: no
             indexer, every visible block attends); kv_c ~ N(0,1)/(24 sqrt(128)) (the law of a
             128-token mean of N(0,1)/24); the 128 raw window rows ~ N(0,1)/24; position 1048575
-  decode_fp8   decode with an MXFP8 indexer: q_I and k_I N(0,1) quantised to e4m3 with one
-            E8M0 scale per 32 (2^(floor(log2 amax) - 8), RNE, saturating at 448)
+  decode_fp8 / prefill_fp8   decode / prefill with an MXFP8 indexer: q_I and k_I N(0,1)
+            quantised to e4m3 with one E8M0 scale per 32 (2^(floor(log2 amax) - 8), RNE,
+            saturating at 448)
   hca_prefill  raw 131072 tokens (kv_raw ~ N(0,1)/24) -> m=128 -> N=1024 blocks; last 8192
             queries (positions 122880..131071); W=128
   sharp variants: q, kv ~ N(0,1) and softmax scale 4/sqrt(D_K), so that attention outputs are
@@ -116,6 +117,8 @@ CONFIGS: Dict[str, Config] = {
                          n_raw=128, raw_base=1048576 - 128, kv_std=1.0 / 48, win_std=1.0 / 24),
     "decode_fp8": Config("decode_fp8", 8, B=16, T=1, N=8192, H_I=64, D_I=128, H=128, D_K=576,
                          D_V=512, top_k=2048, pos0=8191, qi_dt="mxfp8", k_dt="mxfp8"),
+    "prefill_fp8": Config("prefill_fp8", 9, B=1, T=32768, N=32768, H_I=64, D_I=128, H=128,
+                          D_K=576, D_V=512, top_k=2048, pos0=0, qi_dt="mxfp8", k_dt="mxfp8"),
     "hca_decode": Config("hca_decode", 6, B=4, T=1, N=8192, H_I=64, D_I=128, H=128, D_K=576,
                          D_V=512, top_k=8192, m=128, W=128, pos0=1048575, n_raw=128,
                          raw_base=1048576 - 128, kv_std=1.0 / (24 * math.sqrt(128)),

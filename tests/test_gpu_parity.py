@@ -118,6 +118,9 @@ def test_indexer_mxfp8_keys_and_queries():
                       qi_dt="mxfp8", name="idx_fp8q_fp4k"), "mxfp8-q-fp4-k")
     _run_indexer(_cfg("decode", B=1, T=70, N=2100, pos0=2030, qi_dt="mxfp8", k_dt="mxfp8",
                       name="idx_fp8_rows"), "mxfp8-rows")
+    # causal prefill with fp8 queries and keys: several key blocks, ragged tail
+    _run_indexer(_cfg("prefill", T=2100, N=2100, qi_dt="mxfp8", k_dt="mxfp8",
+                      name="idx_fp8_prefill"), "mxfp8-prefill")
     # the scalar kernel (4 heads x 32 dims)
     _run_indexer(_cfg("tiny", dt="bf16", k_dt="mxfp8", name="tiny_fp8"), "tiny-fp8")
     _run_indexer(_cfg("tiny", dt="bf16", k_dt="mxfp8", qi_dt="mxfp8", name="tiny_fp8q"),

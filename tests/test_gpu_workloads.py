@@ -79,6 +79,10 @@ def test_decode_fp8_indexer():
     _run(synth.CONFIGS["decode_fp8"].sharp())
 
 
+def test_prefill_fp8_indexer():
+    _run(synth.CONFIGS["prefill_fp8"], n_sample=12, always=(0, 2047, 2048, 32767))
+
+
 def test_csa_decode_fp4():
     _run(synth.CONFIGS["csa_decode"])
     _run(synth.CONFIGS["csa_decode"].sharp())
