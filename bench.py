@@ -96,11 +96,12 @@ def _kernel_plan(cfg, nsplit):
     return names
 
 
-def _algorithmic(cfg, name):
+def _algorithmic(cfg, name, split=False):
     """(bytes, flops) the method must move / compute in one launch of `name` at this workload.
 
     Counts causal pairs and selected entries only; scratch traffic (split partials, repeated
-    passes over the scores) is not algorithmic."""
+    passes over the scores) is not algorithmic. `split`: the attention hands its partials to
+    attend_combine, which then writes the output (else the attention kernel writes it)."""
     B, T, N = cfg.B, cfg.T, cfg.N
     rows = B * T
     esz = 2 if cfg.dt == "bf16" else 4
@@ -140,6 +141,8 @@ def _algorithmic(cfg, name):
             byt += rows * cfg.top_k * 4  # the index list (HCA has none)
         if name.startswith("attend_mfma") and _fused_topk(cfg):
             byt += pairs * 4  # the kernel selects the entries from the scores itself
+        if not split:
+            byt += rows * cfg.H * (cfg.D_V * esz + 4)  # output and log-sum-exp
         return byt, ents * cfg.H * (cfg.D_K + cfg.D_V) * 2.0
     if name == "attend_combine":
         return rows * cfg.H * (cfg.D_V * esz + 4), 0.0
@@ -382,13 +385,13 @@ def main():
         tot[name] = tot.get(name, 0.0) + per_kernel[k]
     kinfo = {}
     for name, ms in tot.items():
-        byt, fl = _algorithmic(cfg, name)
+        byt, fl = _algorithmic(cfg, name, "attend_combine" in tot)
         us = ms * 1e3
         kinfo[name] = {"us_per_step": round(us, 3), "launches_per_step": kernels.count(name),
                        "alg_GBps": round(byt / (us * 1e-6) / 1e9, 1) if us else None,
                        "alg_TFLOPs": round(fl / (us * 1e-6) / 1e12, 2) if us and fl else None}
     dname = max(tot, key=lambda k: tot[k])
-    byt, fl = _algorithmic(cfg, dname)
+    byt, fl = _algorithmic(cfg, dname, "attend_combine" in tot)
     dur = tot[dname] * 1e-3  # per step; equals the launch duration when there is one chunk
     intensity = fl / byt if byt else 0.0
     # a contraction is held to the peak of the dtype its MFMAs take
