@@ -67,10 +67,10 @@ __device__ __forceinline__ int entry_code(int e, const int32_t* __restrict__ idx
 // of one query over a split of its entry list, 32-entry tiles, software-pipelined across two
 // kinds of wave so that every SIMD runs one of each:
 //  * Gather: each tile goes straight from HBM into an NS-stage LDS ring with
-//    global_load_lds_dwordx4 (no register staging): one DMA per row for the 1024-byte latent part
-//    (fully coalesced) and one per 8 rows for their 128-byte rope parts. Latent rows sit at a
-//    1056-byte stride: both the row-per-lane 16-byte reads of S and the transposed 8-byte reads
-//    of P V are then free of bank conflicts. The rope parts are [32 rows][8 chunks of 16 B],
+//    global_load_lds_dwordx4 (no register staging), issued by the value waves only: one DMA per
+//    row for the 1024-byte latent part (fully coalesced) and one per 8 rows for their 128-byte
+//    rope parts. Latent rows sit at a 1056-byte stride: both the row-per-lane 16-byte reads of
+//    S and the transposed 8-byte reads of P V are then free of bank conflicts. The rope parts are [32 rows][8 chunks of 16 B],
 //    chunk c of row R at slot c ^ ((R >> 1) & 7), again conflict-free for the row-per-lane reads.
 //    Waits are explicit (s_waitcnt vmcnt + s_barrier, no fence).
 //  * Score waves 0..3 (head block hb = wave): in iteration i, S^T = K Q^T for the 32 entries of
@@ -88,10 +88,12 @@ __device__ __forceinline__ int entry_code(int e, const int32_t* __restrict__ idx
 //    receives {M[a][b], M[a+4][b], M[a+8][b], M[a+12][b]}. Lane j of group g reading entry
 //    4g + j/4 at column c + 4*(j%4) therefore receives, in lane n, V[4g+0..3][c+n] (B slots 0..3
 //    in P's order); a second read 16 rows further supplies slots 4..7.
-//  * One barrier per iteration; the two kinds of wave run separate loops with the same barrier
-//    count, so the register allocator never holds q and the accumulators at once. The ring is
-//    4 stages deep when the split's entry table fits beside it (two tiles in flight ahead of the
-//    score waves), else 3.
+//  * Two barriers per iteration: after the first (tile i has landed) the score waves run the S
+//    MFMAs of tile i alone on the matrix cores while the value waves issue the DMAs of the next
+//    tile; after the second, the score waves' softmax (VALU) overlaps the value waves' P V MFMAs.
+//    The two kinds of wave run separate loops with the same barrier count, so the register
+//    allocator never holds q and the accumulators at once. The ring is 4 stages deep when the
+//    split's entry table fits beside it (two tiles in flight ahead of the score waves), else 3.
 //  * Few-query calls split the entry list and merge the (m, l, O) partials in attend_combine.
 //    Workgroups are numbered so that each XCD (workgroup id mod 8) gets a contiguous run of
 //    (row, head group, split): the splits of a query share that XCD's L2 for q and the tiles.
@@ -182,8 +184,8 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
   constexpr int DK = 576, DV = 512, KS = DK / 32, DB = DV / 16;
   __shared__ __attribute__((aligned(16))) char smem[NS * kStage];
   __shared__ __attribute__((aligned(16))) u32x4_t pbuf[2][4][64];  // P, per head block
-  __shared__ float abuf[2][4][16];   // rescale factor per head when the reference moved
-  __shared__ uint32_t fbuf[2][4];    // did the reference move (per head block)
+  __shared__ __attribute__((aligned(16))) float abuf[2][4][16];  // rescale factor per head when the reference moved
+  __shared__ __attribute__((aligned(16))) uint32_t fbuf[2][4];   // did the reference move (per head block)
   __shared__ float sml[4][2][16];    // final (m, l) per head
   extern __shared__ __attribute__((aligned(16))) int scode[];  // entry codes, whole tiles
 
@@ -314,57 +316,86 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     const uint64_t r = (uint64_t)(uintptr_t)(raw_b + (size_t)max(-code - 2, 0) * DK);
     return code <= -2 ? r : a;
   };
-  // DMAs of tile t: wave w moves rows 4w .. 4w+3 (latent), waves 0..3 also the rope parts of
-  // rows 8w .. 8w+7: 5 DMA instructions per tile for waves 0..3, 4 for waves 4..7. The codes
-  // of the rows are read from LDS one tile ahead (fetch), so the issue never waits on LDS.
+  // DMAs of tile t, all issued by the value waves: wave 4 + v moves rows 8v .. 8v+7, one DMA
+  // per 1024-byte latent part and one for the eight 128-byte rope parts (9 per tile). The
+  // codes of the rows are read from LDS one tile ahead (fetch), so the issue never waits on
+  // LDS. The CU's address unit takes a 1 KB DMA instruction in ~20 cycles and stalls the
+  // issuing wave while its queue is full, so the DMAs go to the waves that are otherwise idle
+  // while the score waves' S MFMAs run: the score waves issue no memory instruction in the loop.
   int nx_lat = -1, nx_rope = -1;
+  const int vrow = 8 * (wv & 3);  // first tile row of a value wave's DMAs
   auto fetch = [&](int t) {
-    const int c0 = kTile * t;
-    nx_lat = scode[c0 + 4 * wv + (lane & 3)];
-    nx_rope = score_wave ? scode[c0 + 8 * wv + (lane >> 3)] : -1;
+    if (!score_wave) {
+      const int c0 = kTile * t + vrow;
+      nx_lat = scode[c0 + (lane & 7)];
+      nx_rope = scode[c0 + (lane >> 3)];
+    }
   };
-  auto issue = [&](int t) {
-    const uint32_t sbase = __builtin_amdgcn_readfirstlane(
+  uint32_t d_sbase = 0;
+  uint64_t d_lat = 0;
+  const uint16_t* d_rope = nullptr;
+  auto prep = [&](int t) {
+    d_sbase = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(lds_void_t*)(smem + (t % NS) * kStage));
-    const uint64_t pl = rowaddr(nx_lat);
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)pl, r4);
-      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(pl >> 32), r4);
+    d_lat = rowaddr(nx_lat);
+    d_rope = reinterpret_cast<const uint16_t*>(rowaddr(nx_rope));
+  };
+  // DMA r of the prepared tile: r < 8 the latent part of row vrow + r, r == 8 the rope parts
+  // of rows vrow .. vrow+7 (chunk c of row R at slot c ^ ((R >> 1) & 7))
+  auto dma = [&](int r) {
+    if (r < 8) {
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)d_lat, r);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(d_lat >> 32), r);
       const uint16_t* src = reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
       __builtin_amdgcn_global_load_lds(
           reinterpret_cast<const void*>(src + 8 * lane),
-          (lds_void_t*)(uintptr_t)(sbase + (4 * wv + r4) * kLatStride), 16, 0, 0);
-    }
-    if (score_wave) {
-      const int R = 8 * wv + (lane >> 3);
-      const uint16_t* pr = reinterpret_cast<const uint16_t*>(rowaddr(nx_rope));
+          (lds_void_t*)(uintptr_t)(d_sbase + (vrow + r) * kLatStride), 16, 0, 0);
+    } else {
+      const int R = vrow + (lane >> 3);
       __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(pr + 512 + 8 * ((lane & 7) ^ ((R >> 1) & 7))),
-          (lds_void_t*)(uintptr_t)(sbase + kStageLat + wv * 1024), 16, 0, 0);
+          reinterpret_cast<const void*>(d_rope + 512 + 8 * ((lane & 7) ^ ((R >> 1) & 7))),
+          (lds_void_t*)(uintptr_t)(d_sbase + kStageLat + vrow * 128), 16, 0, 0);
     }
   };
-  // the ring runs NS-2 tiles ahead of the score waves: tiles 0 .. NS-3 now, tile i + NS - 2 at
-  // the top of iteration i (into the stage the value waves finished with in iteration i-1)
+  constexpr int kDmas = 9;
+  auto issue_all = [&]() {
+    if (!score_wave)
+#pragma unroll
+      for (int r = 0; r < kDmas; ++r) dma(r);
+  };
+  // the ring runs NS-2 tiles ahead of the score waves: tiles 0 .. NS-3 now, tile i + NS - 2
+  // during iteration i (into the stage the value waves finished with in iteration i-1)
 #pragma unroll
   for (int t = 0; t < NS - 2; ++t)
-    if (t < ntiles) { fetch(t); issue(t); }
+    if (t < ntiles) { fetch(t); prep(t); issue_all(); }
   if (NS - 2 < ntiles) fetch(NS - 2);
   // top of iteration i: wait until tile i has landed (tiles i+1 .. i+NS-3 may be in flight),
-  // barrier, then issue tile i + NS - 2
-  auto ring_top = [&](int i) {
+  // barrier, then form the addresses of tile i + NS - 2; returns whether its DMAs are due in
+  // this iteration
+  auto ring_top = [&](int i) -> bool {
     if (i < ntiles) {
-      if (NS == 4 && i + 1 < ntiles) {
-        if (score_wave) wait_vm<5>(); else wait_vm<4>();
+      if (NS == 4 && i + 1 < ntiles && !score_wave) {
+        wait_vm<kDmas>();
       } else {
         wait_vm<0>();
       }
     }
     __builtin_amdgcn_s_barrier();
     if (i + NS - 2 < ntiles) {
-      issue(i + NS - 2);
+      prep(i + NS - 2);
       if (i + NS - 1 < ntiles) fetch(i + NS - 1);
+      return true;
     }
+    return false;
+  };
+  // Each iteration is two phases split by a second barrier: first the score waves' S MFMAs
+  // (alone on the matrix cores; the value waves issue their DMAs meanwhile), then the score
+  // waves' softmax (VALU) overlapped with the value waves' P V MFMAs. Without it the two kinds
+  // of MFMA interleave and the softmax runs after both, with the matrix cores idle.
+  auto mid_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   if (score_wave) {
@@ -379,7 +410,10 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     float l_run = 0.f;      // this lane's share: entries 4g.., 16+4g.. of every tile
     for (int i = 0; i <= ntiles; ++i) {
       ring_top(i);
-      if (i == ntiles) break;
+      if (i == ntiles) {
+        mid_barrier();
+        break;
+      }
       const char* sb = smem + (i % NS) * kStage;
       const i32x4_t cd0 = *reinterpret_cast<const i32x4_t*>(scode + kTile * i + 4 * g);
       const i32x4_t cd1 = *reinterpret_cast<const i32x4_t*>(scode + kTile * i + 16 + 4 * g);
@@ -422,6 +456,7 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
           }
         }
       }
+      mid_barrier();
       const f32x4_t st0 = (sa[0] + sa[1]) + (sa[2] + sa[3]);
       const f32x4_t st1 = (sc[0] + sc[1]) + (sc[2] + sc[3]);
       // lane (head n, g): entries 4g+j (z[j]) and 16+4g+j (z[4+j])
@@ -489,23 +524,30 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
   // transposed V reads: entry 4g + n/4 (and 16 rows on), column 256*dh + 16d + 4*(n%4)
   const uint32_t voff = (4 * g + (n >> 2)) * kLatStride + 512 * dh + 8 * (n & 3);
   for (int i = 0; i <= ntiles; ++i) {
-    ring_top(i);
-    if (i == 0) continue;
+    // the value waves issue their DMAs while the score waves' S MFMAs run; P, the moved flags
+    // and the rescale factors are read first, so their LDS round trip hides under the issue
+    const bool due = ring_top(i);
+    if (i == 0) {
+      if (due) issue_all();
+      mid_barrier();
+      continue;
+    }
     const int t = i - 1;
     const bf16x8_t pa0 = as_bf16x8(pbuf[t & 1][hb0][lane]);
     const bf16x8_t pa1 = as_bf16x8(pbuf[t & 1][hb0 + 1][lane]);
+    const u32x2_t moved = *reinterpret_cast<const u32x2_t*>(&fbuf[t & 1][hb0]);
+    const f32x4_t alpha[2] = {*reinterpret_cast<const f32x4_t*>(&abuf[t & 1][hb0][4 * g]),
+                              *reinterpret_cast<const f32x4_t*>(&abuf[t & 1][hb0 + 1][4 * g])};
+    __builtin_amdgcn_sched_barrier(0);
+    if (due) issue_all();
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      if (fbuf[t & 1][hb0 + k] != 0) {
-        float ai[4];
+      if (moved[k] != 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ai[j] = abuf[t & 1][hb0 + k][4 * g + j];
-#pragma unroll
-        for (int d = 0; d < DH; ++d)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[k][d][j] *= ai[j];
+        for (int d = 0; d < DH; ++d) acc[k][d] *= alpha[k];
       }
     }
+    mid_barrier();
     const uint32_t vaddr = (uint32_t)(uintptr_t)(lds_void_t*)(smem + (t % NS) * kStage) + voff;
 #pragma unroll
     for (int d0 = 0; d0 < DH; d0 += 8) {
