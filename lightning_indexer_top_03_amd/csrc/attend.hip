@@ -623,64 +623,69 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
 }
 
 // Merge split partials: out = sum_s w_s O_s, w_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s,
-// M = max_s m_s, with O_s = c_s x (its fp16 partial). One workgroup per (wave slot, head group,
-// row): 16 heads x 256 columns, the block written by one wave of attend_mfma_dma per split.
-// Partials are read as whole 512-byte rows of f16x4; the bf16 result goes through LDS so that
-// each row of the output is written with 16-byte stores.
-constexpr int kMaxSplits = 16;
+// M = max_s m_s, with O_s = c_s x (its fp16 partial). One workgroup per (wave slot, column
+// quarter, head group, row): 16 heads x 128 columns, half of the block one wave of
+// attend_mfma_dma writes per split. Every partial is loaded before the first use (up to 32
+// splits: 64 f16x4 per thread); the bf16 result goes through LDS so that each row of the output
+// is written with 16-byte stores.
+constexpr int kMaxSplits = 32;
 __global__ __launch_bounds__(256) void attend_combine(
     const f16x4_t* __restrict__ part_o, const float* __restrict__ part_ml, int64_t qi0, int H,
     int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse, int nitems) {
   constexpr int DV = 512;
   __shared__ float wsc[kMaxSplits][16];
-  __shared__ __attribute__((aligned(16))) uint16_t sout[16][256 + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sout[16][128 + 8];
   const int HG = H / 64;
-  const int item = xcd_item(blockIdx.x + 8 * (blockIdx.y + HG * blockIdx.z), nitems);
-  const int ws = item & 7, hg = (item >> 3) % HG;
-  const int64_t row = item / (8 * HG);
+  const int item = xcd_item(blockIdx.x + 16 * (blockIdx.y + HG * blockIdx.z), nitems);
+  const int ws = (item & 15) >> 1, cq = item & 1, hg = (item >> 4) % HG;
+  const int64_t row = item / (16 * HG);
   const int64_t qi = qi0 + row;
-  const int h0 = hg * 64 + 16 * (ws & 3), c0 = 256 * (ws >> 2);
+  const int h0 = hg * 64 + 16 * (ws & 3), c0 = 256 * (ws >> 2) + 128 * cq;
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 4, n = lane & 15;
-  // every load is issued before the first use: partial O blocks for all splits (predicated on
-  // nsplit, a runtime value <= kMaxSplits) and the (m, l) pairs, one per thread
+  // column blocks 8 cq + (tid >> 6) + 4 k of the wave slot's 256 columns
   const f16x4_t* base = part_o + (((size_t)row * HG + hg) * nsplit * 8 + ws) * 16 * 64;
-  f16x4_t v[4][kMaxSplits];
+  f16x4_t v[2][kMaxSplits];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int d = (tid >> 6) + 4 * k;
+  for (int k = 0; k < 2; ++k) {
+    const int d = 8 * cq + (tid >> 6) + 4 * k;
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s)
       v[k][s] = s < nsplit ? base[(size_t)s * 8 * 16 * 64 + d * 64 + lane] : f16x4_t{0, 0, 0, 0};
   }
-  float ml_m = kNegInf, ml_l = 0.f, ml_c = 0.f;
-  {
-    const int hh = tid >> 4, s = tid & 15;  // 16 heads x 16 splits = the 256 threads
+  // thread (head hh, sl) holds the (m, l, c) of splits sl and sl + 16
+  const int hh = tid >> 4, sl = tid & 15;
+  float ml_m[2] = {kNegInf, kNegInf}, ml_l[2] = {0.f, 0.f}, ml_c[2] = {0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int s = sl + 16 * j;
     if (s < nsplit) {
       const size_t hrow = ((size_t)row * H + h0 + hh) * nsplit + s;
-      ml_m = part_ml[hrow * 4];
-      ml_l = part_ml[hrow * 4 + 1];
-      ml_c = part_ml[hrow * 4 + 2 + (ws >> 2)];  // scale of this column half
+      ml_m[j] = part_ml[hrow * 4];
+      ml_l[j] = part_ml[hrow * 4 + 1];
+      ml_c[j] = part_ml[hrow * 4 + 2 + (ws >> 2)];  // scale of this column half
     }
   }
   // per head: M = max_s m_s, L = sum_s 2^(m_s - M) l_s, over the 16 lanes of each head
-  float M = ml_m;
+  float M = fmaxf(ml_m[0], ml_m[1]);
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  const float wm = ml_m == kNegInf ? 0.f : exp2f(ml_m - M);
-  const float wl = wm * ml_l;
-  float L = wl;
+  float wm[2], L = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    wm[j] = ml_m[j] == kNegInf ? 0.f : exp2f(ml_m[j] - M);
+    L += wm[j] * ml_l[j];
+  }
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) L += __shfl_xor(L, o, 64);
-  {
-    const int hh = tid >> 4, s = tid & 15;
-    wsc[s][hh] = L > 0.f ? wm / L * ml_c : 0.f;
-    if (s == 0 && lse) lse[(size_t)qi * H + h0 + hh] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
-  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) wsc[sl + 16 * j][hh] = L > 0.f ? wm[j] / L * ml_c[j] : 0.f;
+  if (sl == 0 && cq == 0 && lse)
+    lse[(size_t)qi * H + h0 + hh] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int d = (tid >> 6) + 4 * k;
+  for (int k = 0; k < 2; ++k) {
+    const int d = (tid >> 6) + 4 * k;  // column block within this quarter
     float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) {
@@ -693,16 +698,14 @@ __global__ __launch_bounds__(256) void attend_combine(
     for (int i = 0; i < 4; ++i) sout[4 * g + i][16 * d + n] = f32_to_bf16(a[i]);
   }
   __syncthreads();
-  // 16 rows x 512 bytes: 2 chunks of 16 bytes per thread
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int c = tid + 256 * k, r = c >> 5, col = (c & 31) * 8;
+  // 16 rows x 256 bytes: one chunk of 16 bytes per thread
+  {
+    const int r = tid >> 4, col = (tid & 15) * 8;
     *reinterpret_cast<u32x4_t*>(out + ((size_t)qi * H + h0 + r) * DV + c0 + col) =
         *reinterpret_cast<const u32x4_t*>(&sout[r][col]);
   }
 }
 
-// ---- generic scalar path ----
 template <typename T>
 __device__ __forceinline__ float ldv(const T* p, size_t i) {
   if constexpr (sizeof(T) == 2)
@@ -868,8 +871,8 @@ static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows,
   }
 #undef DSA_ATT
   if (e != hipSuccess || ns == 1) return e;
-  return launch(attend_combine, dim3(8, s.H / 64, (unsigned)nrows), 256, 0, st, part_o, part_ml,
-                qi0, s.H, ns, static_cast<uint16_t*>(out), lse, (int)(8 * (s.H / 64) * nrows));
+  return launch(attend_combine, dim3(16, s.H / 64, (unsigned)nrows), 256, 0, st, part_o, part_ml,
+                qi0, s.H, ns, static_cast<uint16_t*>(out), lse, (int)(16 * (s.H / 64) * nrows));
 }
 
 // Each of a row's workgroups (splits x head groups) repeats the row's selection in its

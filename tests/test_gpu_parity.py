@@ -298,6 +298,9 @@ def test_hca_ragged_window_and_compress():
     # few rows split the entry list; many rows do not
     _hca_case(base.with_(B=1, T=3, N=2900, m=8, W=0, pos0=8 * 2900 - 3, n_raw=0, raw_base=0,
                          name="hca_nowin"))
+    # the most splits the merge takes (32), the last one ragged
+    _hca_case(base.with_(B=1, T=2, N=5000, m=8, W=0, pos0=8 * 5000 - 9, n_raw=0, raw_base=0,
+                         name="hca_32split"))
     # blocks produced from raw rows in the same call, 140 query rows; the sharp variant has no
     # window: with one, its N(0,1) raw rows outweigh the 16-token means and the outputs reach
     # ~4, where bf16 output rounding alone (up to 1.6e-2) uses up most of the 2e-2 bound
