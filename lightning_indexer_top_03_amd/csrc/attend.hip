@@ -379,6 +379,8 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
       } else {
         wait_vm<0>();
       }
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's P / flag writes
     }
     __builtin_amdgcn_s_barrier();
     if (i + NS - 2 < ntiles) {

@@ -93,6 +93,10 @@ def test_indexer_prefill_bf16_causal():
     # prefill-shaped (MFMA, keys in registers, queries through LDS): causal triangle, ragged
     c = _cfg("prefill", B=2, T=700, N=700, name="idx_prefill")
     _run_indexer(c, "prefill")
+    # N % 4 != 0: score rows are not 16-byte aligned (per-element stores); queries start
+    # mid-sequence so a key block is visible to some rows of a query block and not others
+    _run_indexer(_cfg("prefill", B=1, T=333, N=1001, pos0=600, name="idx_prefill_odd"),
+                 "prefill-odd")
 
 
 def test_indexer_prefill_csa_blocks():
