@@ -793,9 +793,10 @@ int attend_splits(const Shape& s, int64_t nrows, int fmt) {
   if (wgs >= 512) return 1;
   const int E = s.top_k + s.W;
   int64_t want = (512 + wgs - 1) / wgs;
-  // at least 256 entries per split (each workgroup's prologue is a fixed cost); 128 when even
-  // that leaves most of the GPU idle (a handful of rows, as in long-context CSA decode)
-  const int min_per = wgs * ((E + 255) / 256) >= 256 ? 256 : 128;
+  // at least 256 entries per split (each workgroup's prologue is a fixed cost); 128, then 64,
+  // when even that leaves most of the GPU idle (a handful of rows, as in long-context CSA
+  // decode)
+  const int min_per = wgs * ((E + 255) / 256) >= 256 ? 256 : wgs * ((E + 127) / 128) >= 256 ? 128 : 64;
   int64_t maxs = (E + min_per - 1) / min_per;
   int64_t ns = want < maxs ? want : maxs;
   if (ns > kMaxSplits) ns = kMaxSplits;

@@ -313,19 +313,26 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_mx_dma(
                                      (lds_void_t*)(uintptr_t)(sb + 4096), 4, 0, 0);
   };
   constexpr int kPre = ITERS < kMxStages ? ITERS : kMxStages;
+  constexpr int kHead = kPre < 2 ? kPre : 2;
+  // Every wave's q_I and w loads enter the CU's address queue ahead of all the key DMAs
+  // (queued behind the other waves' DMAs they would wait out tens of them). Their first use
+  // makes the compiler wait for every memory instruction in flight (it cannot count LDS DMAs
+  // out of a partial wait), so only the first kHead tiles are issued before it, the rest once
+  // q_I is in its operand registers.
+  __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int t = 0; t < kPre; ++t) issue(t);
-  // w and q_I have landed once only the prefetched tiles are outstanding
-  switch (kPre) {
-    case 1: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
-  }
+  for (int t = 0; t < kHead; ++t) issue(t);
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(wr[hb][r]));
+  asm volatile("" : "+v"(q0), "+v"(q1), "+v"(qsw[0]), "+v"(qsw[1]));
+  if constexpr (QMX) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) asm volatile("" : "+v"(qa[0][hb][s2]));
+  }
   if constexpr (QMX) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
@@ -390,6 +397,9 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_mx_dma(
         }
       }
   }
+  // the other prefetched tiles, after the last LDS read the compiler would hold behind them
+#pragma unroll
+  for (int t = kHead; t < kPre; ++t) issue(t);
   // every wave holds its A operands before the buffer is reused for the scores
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
