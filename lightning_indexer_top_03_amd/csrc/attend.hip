@@ -744,7 +744,8 @@ __global__ __launch_bounds__(256) void attend_generic(
     float z = kNegInf;
     if (src) {
       float dot = 0.f;
-      for (int d = 0; d < DK; ++d) dot += sq[d] * ldv(src, d);
+#pragma unroll 8
+      for (int d = 0; d < DK; ++d) dot += sq[d] * ldv(src, d);  // 8 loads in flight at a time
       z = dot * scale;
     }
     sz[e] = z;
@@ -770,6 +771,7 @@ __global__ __launch_bounds__(256) void attend_generic(
   const float inv = sum > 0.f ? 1.f / sum : 0.f;
   for (int d = threadIdx.x; d < DV; d += blockDim.x) {
     float a = 0.f;
+#pragma unroll 8
     for (int e = 0; e < E; ++e)
       if (ssrc[e]) a += sz[e] * ldv(ssrc[e], d);
     a *= inv;

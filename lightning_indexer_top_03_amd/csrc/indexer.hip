@@ -874,24 +874,40 @@ __global__ __launch_bounds__(256) void indexer_generic(
     return;
   }
   const size_t krow = (size_t)b * N + s;
-  float acc = 0.f;
-  for (int j = 0; j < H_I; ++j) {
-    float dot = 0.f;
-    for (int d = 0; d < D_I; ++d) {
-      float kv;
-      if (k_fmt == FMT_MXFP4) {
-        uint32_t byte = reinterpret_cast<const uint8_t*>(kI)[krow * (D_I / 2) + d / 2];
-        uint32_t code = (d & 1) ? (byte >> 4) : (byte & 15u);
-        kv = fp4_val(code) * e8m0_scale(ksc[krow * (D_I / 32) + d / 32]);
-      } else if (k_fmt == FMT_MXFP8) {
-        kv = fp8_val(reinterpret_cast<const uint8_t*>(kI)[krow * D_I + d]) *
-             e8m0_scale(ksc[krow * (D_I / 32) + d / 32]);
-      } else {
-        kv = load_val(kI, krow * D_I + d, k_fmt);
-      }
-      dot += sqf[j * D_I + d] * kv;
+  auto kval = [&](int d) -> float {
+    if (k_fmt == FMT_MXFP4) {
+      uint32_t byte = reinterpret_cast<const uint8_t*>(kI)[krow * (D_I / 2) + d / 2];
+      uint32_t code = (d & 1) ? (byte >> 4) : (byte & 15u);
+      return fp4_val(code) * e8m0_scale(ksc[krow * (D_I / 32) + d / 32]);
     }
-    acc += swf[j] * fmaxf(dot, 0.f);
+    if (k_fmt == FMT_MXFP8)
+      return fp8_val(reinterpret_cast<const uint8_t*>(kI)[krow * D_I + d]) *
+             e8m0_scale(ksc[krow * (D_I / 32) + d / 32]);
+    return load_val(kI, krow * D_I + d, k_fmt);
+  };
+  float acc = 0.f;
+  if (H_I <= 8) {
+    // few heads: each key value is loaded once and feeds every head's dot product; the loads
+    // of a block of dims are in flight together (one at a time, every product waited out a
+    // cache round trip)
+    float dot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int d = 0; d < D_I; ++d) {
+      const float kv = kval(d);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < H_I) dot[j] += sqf[j * D_I + d] * kv;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < H_I) acc += swf[j] * fmaxf(dot[j], 0.f);
+  } else {
+    for (int j = 0; j < H_I; ++j) {
+      float dot = 0.f;
+#pragma unroll 8
+      for (int d = 0; d < D_I; ++d) dot += sqf[j * D_I + d] * kval(d);
+      acc += swf[j] * fmaxf(dot, 0.f);
+    }
   }
   srow[s] = acc;
 }
