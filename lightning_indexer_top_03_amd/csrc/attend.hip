@@ -263,12 +263,15 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
   } else {
     // Fused top-k: the row's scores (in flight with the q loads), its selection, this split's
     // slice of it. The selection's LDS scratch is the ring memory, idle until the first DMA.
-    const int p = q_pos[qi];
-    const int nvis = n_visible(p, m, N);
+    // The score loads do not wait for q_pos: they cover the whole row (addresses clamped to
+    // N), and the visible count only trims them afterwards (one memory round trip fewer).
+    int p = q_pos[qi];
     const float* __restrict__ srow = scores + row * (int64_t)N;
     uint32_t key[PER];
-    int nv = 0;
-    if (nvis > top_k) nv = load_keys<PER>(srow, N, nvis, key);
+    load_keys<PER>(srow, N, N, key);
+    asm volatile("" : "+v"(p));
+    const int nvis = n_visible(p, m, N);
+    const int nv = nvis > top_k ? max(0, min(PER, nvis - PER * tid)) : 0;
     load_q();
     int32_t* __restrict__ orow =
         (idx_out != nullptr && split == 0 && hg == 0) ? idx_out + row * (int64_t)top_k : nullptr;
