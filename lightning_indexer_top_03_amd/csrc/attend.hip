@@ -70,8 +70,9 @@ __device__ __forceinline__ int entry_code(int e, const int32_t* __restrict__ idx
 //    global_load_lds_dwordx4 (no register staging), issued by the value waves only: one DMA per
 //    row for the 1024-byte latent part (fully coalesced) and one per 8 rows for their 128-byte
 //    rope parts. Latent rows sit at a 1056-byte stride: both the row-per-lane 16-byte reads of
-//    S and the transposed 8-byte reads of P V are then free of bank conflicts. The rope parts are [32 rows][8 chunks of 16 B],
-//    chunk c of row R at slot c ^ ((R >> 1) & 7), again conflict-free for the row-per-lane reads.
+//    S and the transposed 8-byte reads of P V are then free of bank conflicts. The rope parts
+//    are [32 rows][8 chunks of 16 B], chunk c of row R at slot c ^ ((R >> 1) & 7), again
+//    conflict-free for the row-per-lane reads.
 //    Waits are explicit (s_waitcnt vmcnt + s_barrier, no fence).
 //  * Score waves 0..3 (head block hb = wave): in iteration i, S^T = K Q^T for the 32 entries of
 //    tile i (two 16-entry blocks, 8 independent chains of v_mfma_f32_16x16x32_bf16 with q in
@@ -83,8 +84,9 @@ __device__ __forceinline__ int entry_code(int e, const int32_t* __restrict__ idx
 //    the rescale factors when the reference moved.
 //  * Value waves 4..7: in iteration i, P V for tile i-1; wave 4+v owns 32 heads (head blocks
 //    2*(v&1), 2*(v&1)+1) and value columns 256*(v>>1).. +255, so each pair of transposed V
-//    reads feeds two MFMAs (32 MFMAs per tile, V read from LDS once per 32 heads). The B operands come straight from the row-major tile through
-//    ds_read_b64_tr_b16: within each group of 16 lanes, if lane j reads M[j][0..3], lane 4a+b
+//    reads feeds two MFMAs (32 MFMAs per tile, V read from LDS once per 32 heads). The B
+//    operands come straight from the row-major tile through ds_read_b64_tr_b16: within each
+//    group of 16 lanes, if lane j reads M[j][0..3], lane 4a+b
 //    receives {M[a][b], M[a+4][b], M[a+8][b], M[a+12][b]}. Lane j of group g reading entry
 //    4g + j/4 at column c + 4*(j%4) therefore receives, in lane n, V[4g+0..3][c+n] (B slots 0..3
 //    in P's order); a second read 16 rows further supplies slots 4..7.
@@ -129,8 +131,8 @@ __device__ __forceinline__ float group_sum(float v) {
 
 
 // 16 ds_read_b64_tr_b16 for value-column blocks d0 .. d0+7 (entries 4g.. and 16+4g..), waited
-// for inside the same asm block. Written as asm because the builtin carries no memory operand, which makes the compiler wait
-// for every LDS DMA still in flight before it.
+// for inside the same asm block. Written as asm because the builtin carries no memory operand,
+// which makes the compiler wait for every LDS DMA still in flight before it.
 #define DSA_TR(i, off) "ds_read_b64_tr_b16 %" #i ", %16 offset:" #off "\n"
 #define DSA_TR_PAIR(i0, i1, D) DSA_TR(i0, (D) * 32) DSA_TR(i1, 16896 + (D) * 32)
 #define DSA_TR_BLOCK(D0)                                                                        \
@@ -184,8 +186,9 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
   constexpr int DK = 576, DV = 512, KS = DK / 32, DB = DV / 16;
   __shared__ __attribute__((aligned(16))) char smem[NS * kStage];
   __shared__ __attribute__((aligned(16))) u32x4_t pbuf[2][4][64];  // P, per head block
-  __shared__ __attribute__((aligned(16))) float abuf[2][4][16];  // rescale factor per head when the reference moved
-  __shared__ __attribute__((aligned(16))) uint32_t fbuf[2][4];   // did the reference move (per head block)
+  // rescale factor per head when the reference moved, and whether it moved (per head block)
+  __shared__ __attribute__((aligned(16))) float abuf[2][4][16];
+  __shared__ __attribute__((aligned(16))) uint32_t fbuf[2][4];
   __shared__ float sml[4][2][16];    // final (m, l) per head
   extern __shared__ __attribute__((aligned(16))) int scode[];  // entry codes, whole tiles
 
