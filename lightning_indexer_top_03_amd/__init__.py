@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libdsa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m lightning_indexer_top_03_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python lightning_indexer_top_03_amd/build.py` "
         "(hipcc, gfx950). There is no non-HIP fallback.")
 
 _lib = ctypes.CDLL(LIB_PATH)
