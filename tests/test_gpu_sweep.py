@@ -1,0 +1,58 @@
+"""Seeded random shapes through dsa_forward, every row against the fp64 oracle.
+
+The workload tests run the five configurations and hand-picked edge cases; this sweep draws
+batch, query count, context length, positions, top-k, compression ratio and key / query storage
+at random (one fixed seed, so every run checks the same cases) to reach combinations the
+hand-picked cases do not: small and odd top-k, contexts shorter than k, queries that see
+nothing yet, decode- and prefill-sized row counts, bf16 / MXFP4 / MXFP8 indexer inputs, and
+sharp attention inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from test_gpu_workloads import _run
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    yield
+    torch.cuda.empty_cache()
+
+
+def _cases(n=14, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        base = ["decode", "prefill", "csa_decode", "decode_fp8"][i % 4]
+        c = synth.CONFIGS[base]
+        m = 4 if base == "csa_decode" else int(rng.choice([1, 1, 4]))
+        N = int(rng.integers(200, 4000))
+        top_k = int(rng.choice([32, 100, 257, 1024, 2048]))
+        if base == "prefill":
+            B, T = 1, int(rng.integers(65, 200))    # prefill-shaped kernels (>= 64 rows)
+        else:
+            B, T = int(rng.integers(1, 4)), int(rng.integers(1, 24))
+        span = N * m
+        pos0 = 0 if i % 5 == 0 else int(rng.integers(0, max(1, span // 2)))
+        stride = int(rng.integers(1, max(2, (span - pos0) // max(T, 1))))
+        k_dt = c.k_dt if base in ("csa_decode", "decode_fp8") else "bf16"
+        cfg = c.with_(B=B, T=T, N=N, m=m, top_k=top_k, pos0=pos0, pos_stride=stride, W=0,
+                      n_raw=0, raw_base=0, compress=False, k_dt=k_dt, seed=500 + i,
+                      name=f"sweep{i}_{base}_m{m}_k{top_k}")
+        if i % 3 == 2:
+            cfg = cfg.sharp()
+        cases.append(cfg)
+    return cases
+
+
+@pytest.mark.parametrize("cfg", _cases(), ids=lambda c: c.name)
+def test_random_shapes(cfg):
+    # sharp rows that see only a handful of entries have outputs of several units: their bar
+    # carries the bf16 rounding of P and of the stored output (see check_attention)
+    _run(cfg, n_sample=48, always=(0,), bf16_scale_allowance=cfg.name.endswith("_sharp"))

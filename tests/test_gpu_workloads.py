@@ -36,7 +36,7 @@ def _sample_rows(c, n, always=()):
     return sorted(pick)
 
 
-def _run(c, n_sample=16, always=()):
+def _run(c, n_sample=16, always=(), bf16_scale_allowance=False):
     wl = synth.make_workload(c)
     dw = DeviceWorkload(wl)
     f = dw.forward(keep_scores=True, keep_idx=True)
@@ -57,7 +57,8 @@ def _run(c, n_sample=16, always=()):
         worst_s = max(worst_s, check_scores(sc, ref_sc, nv, what=what))
         swaps += check_topk(ix, ref_sc, nv, c.top_k, what=what)
         ro, rl = run.attend(b, t, ix)
-        mx, s = check_attention(out, lse, ro, rl, what=what)
+        mx, s = check_attention(out, lse, ro, rl, what=what,
+                                bf16_scale_allowance=bf16_scale_allowance)
         worst_a = max(worst_a, (mx, s))
     log(f"[{c.name}] rows={len(rows)} score rel err {worst_s:.2e}, tie swaps {swaps}, "
         f"attention max abs err {worst_a[0]:.3e} (max|ref| {worst_a[1]:.3e})")
