@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import synth
+from test_gpu_parity import _hca_case
 from test_gpu_workloads import _run
 
 pytestmark = pytest.mark.gpu
@@ -56,3 +57,51 @@ def test_random_shapes(cfg):
     # sharp rows that see only a handful of entries have outputs of several units: their bar
     # carries the bf16 rounding of P and of the stored output (see check_attention)
     _run(cfg, n_sample=48, always=(0,), bf16_scale_allowance=cfg.name.endswith("_sharp"))
+
+
+def _window_cases(n=4, seed=2025):
+    # CSA blocks with the 128-token raw window: the raw rows held start at the first window row
+    # of the first query and end at the last query
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        c = synth.CONFIGS["csa_decode"]
+        N = int(rng.integers(300, 4000))
+        top_k = int(rng.choice([64, 257, 1024]))
+        B, T = int(rng.integers(1, 3)), int(rng.integers(2, 30))
+        p0 = int(rng.integers(0, 2 * N))
+        stride = int(rng.integers(1, max(2, (4 * N - p0) // T)))
+        base = max(0, p0 - 127)
+        last = p0 + stride * (T - 1)
+        cfg = c.with_(B=B, T=T, N=N, top_k=top_k, pos0=p0, pos_stride=stride, raw_base=base,
+                      n_raw=last - base + 1, seed=600 + i, name=f"sweepw{i}_k{top_k}")
+        cases.append(cfg.sharp() if i % 2 else cfg)
+    return cases
+
+
+@pytest.mark.parametrize("cfg", _window_cases(), ids=lambda c: c.name)
+def test_random_window_shapes(cfg):
+    _run(cfg, n_sample=48, always=(0,), bf16_scale_allowance=cfg.name.endswith("_sharp"))
+
+
+def _hca_cases(n=4, seed=2026):
+    # HCA: every visible compressed entry plus the window, entry counts across the split rule
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        c = synth.CONFIGS["hca_decode"]
+        m = int(rng.choice([8, 16, 128]))
+        N = int(rng.integers(50, 3000))
+        B, T = int(rng.integers(1, 3)), int(rng.integers(1, 9))
+        p0 = int(rng.integers(0, N * m))
+        stride = int(rng.integers(1, max(2, (N * m - p0) // T)))
+        base = max(0, p0 - 127)
+        last = p0 + stride * (T - 1)
+        cases.append(c.with_(B=B, T=T, N=N, m=m, pos0=p0, pos_stride=stride, raw_base=base,
+                             n_raw=last - base + 1, seed=700 + i, name=f"sweeph{i}_m{m}"))
+    return cases
+
+
+@pytest.mark.parametrize("cfg", _hca_cases(), ids=lambda c: c.name)
+def test_random_hca_shapes(cfg):
+    _hca_case(cfg)
