@@ -105,3 +105,28 @@ def _hca_cases(n=4, seed=2026):
 @pytest.mark.parametrize("cfg", _hca_cases(), ids=lambda c: c.name)
 def test_random_hca_shapes(cfg):
     _hca_case(cfg)
+
+
+def _scalar_cases(n=4, seed=2027):
+    # the scalar kernels: fp32 inputs, small head counts and dims (the tiny configuration's
+    # shapes), bf16 with heads or dims the MFMA kernels do not take
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        c = synth.CONFIGS["tiny"]
+        N = int(rng.integers(20, 900))
+        top_k = int(rng.choice([1, 7, 64, 300]))
+        T = int(rng.integers(1, 40))
+        p0 = int(rng.integers(0, N))
+        stride = int(rng.integers(1, max(2, (N - p0) // T)))
+        kw = dict(B=int(rng.integers(1, 3)), T=T, N=N, top_k=top_k, pos0=p0, pos_stride=stride,
+                  seed=800 + i, name=f"sweeps{i}_k{top_k}")
+        if i % 2:
+            kw.update(dt="bf16", k_dt="bf16", H=16, H_I=8, D_I=64, name=kw["name"] + "_bf16")
+        cases.append(c.with_(**kw))
+    return cases
+
+
+@pytest.mark.parametrize("cfg", _scalar_cases(), ids=lambda c: c.name)
+def test_random_scalar_shapes(cfg):
+    _run(cfg, n_sample=48, always=(0,))
