@@ -94,8 +94,6 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_dma(
           (lds_void_t*)(uintptr_t)(ring + (t & 1) * (32 * 256) + 1024 * j), 16, 0, 0);
     }
   };
-  issue(0);
-  if (ITERS > 1) issue(1);
   {  // q_I: 16 KB, two 1 KB DMAs per wave (rows 8*wv .. 8*wv+7)
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(qI + (size_t)qi * (64 * 128));
 #pragma unroll
@@ -116,12 +114,18 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_dma(
 #pragma unroll
       for (int i = 0; i < 4; ++i) wr[hb][4 * j + i] = w4[i];
     }
-  // Everything issued so far has landed once this returns (the counter drains in order).
+  // Every wave's q_I DMAs and w loads enter the CU's address queue ahead of all key DMAs (behind
+  // them, they would wait out every wave's two tiles); only tile 0 is issued before the full
+  // wait the first use of w needs (the compiler cannot count LDS DMAs out of a partial wait),
+  // tile 1 right after it.
+  __builtin_amdgcn_s_barrier();
+  issue(0);
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(wr[hb][r]));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (ITERS > 1) issue(1);
   __builtin_amdgcn_s_barrier();  // every wave's share of q_I is in LDS
   u32x4_t qa[2][8];
 #pragma unroll
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_dma(
   const int ntiles = last > key0 ? (last - key0 + 31) / 32 : 0;
 #pragma unroll
   for (int t = 0; t < ITERS; ++t) {
-    if (t >= 2) {
+    if (t >= 1) {  // (tile 0 landed in the prologue's wait)
       if (t + 1 < ITERS)
         asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // tile t landed, tile t+1 in flight
       else
