@@ -2,13 +2,15 @@
 """Throughput of the DSA hot path (lightning indexer -> top-k -> sparse MQA-MLA) on one MI355X.
 
 A step is one dsa_forward over one batch of seeded synthetic inputs, already resident in HBM.
-Default workload: decode, 16 sequences x 1 new query token over an 8192-token context, indexer
-64 heads x 128 (bf16 keys), top-k 2048, sparse MQA attention with 128 heads over 576-wide
-latent rows (value = first 512 columns), bf16 storage, fp32 accumulation.
+Default workload (the largest single-GPU configuration): prefill, one sequence of 32768 tokens
+with all 32768 queries causal, indexer 64 heads x 128 (bf16), top-k 2048, sparse MQA attention
+with 128 heads over 576-wide latent rows (value = first 512 columns), bf16 storage, fp32
+accumulation. The same line carries a per-config block for the four other workloads (tiny fp32,
+decode, CSA prefill, CSA decode), each timed the same way.
 
-The K timed steps replay HIP graphs of dsa_forward, cycling over R copies of the inputs so the
-bytes a step touches exceed the 256 MB last-level cache (cold-cache HBM traffic, as in
-multi-layer decode). A second, instrumented pass runs the same dsa_forward calls eagerly with
+The K timed steps replay HIP graphs of dsa_forward (after at least R warm-up replays), cycling
+over R copies of the inputs so the bytes a step touches exceed the 256 MB last-level cache
+(cold-cache HBM traffic, as in multi-layer decode). A second, instrumented pass runs the same dsa_forward calls eagerly with
 a pair of HIP events per kernel, stamped by hipExtLaunchKernel with that dispatch's start and
 end, to get each kernel's average duration; the dominant kernel's algorithmic bytes (or flops)
 over that duration give the roofline fraction. The fp64 CPU oracle, timed on this host's
@@ -225,19 +227,48 @@ def _forward(cfg, t, dsa, base):
                        raw_base=base, compress=cfg.compress)
 
 
-def cpu_baseline(cfg, budget_s=20.0):
-    """The oracle, as it stands, over the query rows of one step (or as many as fit the budget)."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# query positions every prefill CPU sample includes: the first rows, both sides of the keep-all
+# edge (k = 2048) and the last row
+PREFILL_ALWAYS = (0, 1, 2046, 2047, 2048, 2049, 32767)
+
+
+def cpu_sample_rows(cfg):
+    """Query rows the CPU baseline visits, in visiting order: every row of one step when there
+    are at most 64, else a uniform sample (128 rows for the 32768-query prefill, always with the
+    positions of PREFILL_ALWAYS; 64 elsewhere), drawn with the workload's seed and visited in
+    random order so that a budget cut still leaves a uniform sample."""
     import numpy as np
 
+    rows = [(b, t) for b in range(cfg.B) for t in range(cfg.T)]
+    rng = np.random.default_rng(cfg.seed)
+    if len(rows) > 64:
+        n = 128 if cfg.T >= 32768 else 64
+        always = [t for t in PREFILL_ALWAYS if t < cfg.T] if cfg.T >= 32768 else []
+        rest = [int(i) for i in rng.permutation(len(rows)) if int(i) not in always]
+        rows = [rows[i] for i in sorted(set(always) | set(rest[: n - len(always)]))]
+    return [rows[int(i)] for i in rng.permutation(len(rows))]
+
+
+def cpu_baseline(cfg, budget_s=20.0):
+    """The oracle, as it stands, over the query rows of cpu_sample_rows (as many as fit the
+    budget)."""
     import oracle
     import synth
 
     wl = synth.make_workload(cfg)
     run = oracle.QueryRunner(wl)
-    rows = [(b, t) for b in range(cfg.B) for t in range(cfg.T)]
-    if len(rows) > 64:
-        rng = np.random.default_rng(cfg.seed)
-        rows = [rows[i] for i in sorted(rng.choice(len(rows), 64, replace=False))]
+    rows = cpu_sample_rows(cfg)
     t0 = time.perf_counter()
     done = 0
     for b, t in rows:
@@ -250,50 +281,37 @@ def cpu_baseline(cfg, budget_s=20.0):
             break
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "query tokens/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"{done} of the {cfg.B * cfg.T} query rows of one step "
-                      f"({'all' if done == cfg.B * cfg.T else 'uniform sample'}), fp64, "
-                      f"{dt:.1f} s wall"}
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "sample": f"{done} of {len(rows)} query rows drawn from the {cfg.B * cfg.T} of one "
+                      f"step ({'all' if len(rows) == cfg.B * cfg.T else 'uniform sample'}"
+                      f"{', incl. positions ' + str(PREFILL_ALWAYS) if cfg.T >= 32768 else ''}, "
+                      f"random order), fp64, {dt:.1f} s wall"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--rotate", type=int, default=0,
-                    help="input copies cycled over (0: enough to exceed 2x the 256 MB MALL)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="first run a plain elementwise copy of 256 MiB (read) + 256 MiB "
-                         "(written) three times, the reference for HBM byte counters")
-    args = ap.parse_args()
+def log(msg):
+    print(f"# {msg}", file=sys.stderr, flush=True)
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
 
+def measure(name, steps, warmup, rotate=0, eager=False, copy_probe=False, n_inst=None):
+    """Time `steps` dsa_forward steps of workload `name` (inputs resident in HBM) and the
+    per-kernel durations of an instrumented pass. Returns the figures of one bench line."""
     import torch
 
     import lightning_indexer_top_03_amd as dsa
     import synth
 
-    cfg = synth.CONFIGS[args.workload]
-    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS[name]
     wl = synth.make_workload(cfg)
     t0 = time.time()
     inputs = [_device_inputs(wl)]
-    print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    log(f"[{name}] inputs ready in {time.time() - t0:.1f}s")
 
     # input copies so that one cycle touches > 512 MB
     touched = sum(_algorithmic(cfg, k)[0] for k in
                   (("attend_mfma_dma",) if cfg.dense else ("indexer_x", "attend_mfma_dma")))
-    R = args.rotate or max(1, min(16, int(512e6 // max(touched, 1.0)) + 1))
+    R = rotate or max(1, min(16, int(512e6 // max(touched, 1.0)) + 1))
     if cfg.B * cfg.T > 64:
-        R = args.rotate or 1
+        R = rotate or 1
     for _ in range(1, R):
         c = {k: (tuple(x.clone() for x in v) if isinstance(v, tuple) else
                  (v.clone() if v is not None else None)) for k, v in inputs[0].items()}
@@ -311,14 +329,14 @@ def main():
     per_chunk = _kernel_plan(cfg.with_(compress=False, B=1, T=chunk_rows), 2 if split else 1)
     kernels = (["compress_mean"] if cfg.compress else []) + per_chunk * n_chunks
 
-    if args.copy_probe:
+    if copy_probe:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        print(f"# copy probe: torch.neg over {src.numel() * 4} bytes read and written per "
-              "launch, 3 launches", file=sys.stderr, flush=True)
+        log("copy probe: torch.neg over {} bytes read and written per launch, 3 launches"
+            .format(src.numel() * 4))
         del src, dst
 
     stream = torch.cuda.Stream()
@@ -328,7 +346,7 @@ def main():
         for f in fwds:
             f.run()
         torch.cuda.synchronize()
-        if not args.eager:
+        if not eager:
             for f in fwds:
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=stream):
@@ -342,17 +360,20 @@ def main():
         else:
             fwds[i % R].run()
 
+    # every captured graph is replayed at least once before the timed steps
+    warmup = max(warmup, R)
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
+        for i in range(warmup):
             step(i)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             step(i)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = rows / (elapsed / args.steps)
+    ms_per_step = elapsed * 1e3 / steps
+    value = rows / (elapsed / steps)
+    log(f"[{name}] {steps} steps: {ms_per_step:.4f} ms/step, {value:.1f} query tokens/s")
 
     # ---- instrumented pass: each kernel's own start / end events ----
     # dsa_forward hands event pair i to the i-th kernel's hipExtLaunchKernel, which stamps them
@@ -362,7 +383,9 @@ def main():
     # before the GPU reaches them: they run back to back, as in the graph replays.
     nk = len(kernels)
     per_kernel = [0.0] * nk
-    n_inst = min(args.steps, 200 if rows <= 64 else 10)
+    if n_inst is None:
+        n_inst = 200 if rows <= 64 else 10
+    n_inst = min(steps, n_inst)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)]
     with torch.cuda.stream(stream):
         for f in fwds:
@@ -377,19 +400,21 @@ def main():
         for f in fwds:
             f.set_events(None)
     per_kernel = [x / n_inst for x in per_kernel]  # ms per launch
-    mode = "eager behind a spin kernel"
 
     # per kernel: summed over the query chunks of one step (one launch per chunk)
     tot = {}
-    for k, name in enumerate(kernels):
-        tot[name] = tot.get(name, 0.0) + per_kernel[k]
+    for k, kname in enumerate(kernels):
+        tot[kname] = tot.get(kname, 0.0) + per_kernel[k]
     kinfo = {}
-    for name, ms in tot.items():
-        byt, fl = _algorithmic(cfg, name, "attend_combine" in tot)
+    step_bytes = step_flops = 0.0
+    for kname, ms in tot.items():
+        byt, fl = _algorithmic(cfg, kname, "attend_combine" in tot)
+        step_bytes += byt
+        step_flops += fl
         us = ms * 1e3
-        kinfo[name] = {"us_per_step": round(us, 3), "launches_per_step": kernels.count(name),
-                       "alg_GBps": round(byt / (us * 1e-6) / 1e9, 1) if us else None,
-                       "alg_TFLOPs": round(fl / (us * 1e-6) / 1e12, 2) if us and fl else None}
+        kinfo[kname] = {"us_per_step": round(us, 3), "launches_per_step": kernels.count(kname),
+                        "alg_GBps": round(byt / (us * 1e-6) / 1e9, 1) if us else None,
+                        "alg_TFLOPs": round(fl / (us * 1e-6) / 1e12, 2) if us and fl else None}
     dname = max(tot, key=lambda k: tot[k])
     byt, fl = _algorithmic(cfg, dname, "attend_combine" in tot)
     dur = tot[dname] * 1e-3  # per step; equals the launch duration when there is one chunk
@@ -404,26 +429,89 @@ def main():
         roof = {"bound": "hbm", "achieved": round(byt / dur / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    tr = _traffic(dname, args.workload)
-    roof["traffic"] = tr
+    roof["traffic"] = _traffic(dname, name)
     roof["kernel"] = dname
     roof["kernel_us"] = round(dur * 1e6 / kernels.count(dname), 3)
-    roof["alg_bytes_per_step"] = byt
-    roof["alg_flops_per_step"] = fl
+    roof["launches_per_step"] = kernels.count(dname)
+    roof["kernel_alg_bytes_per_step"] = byt
+    roof["kernel_alg_flops_per_step"] = fl
+    # the whole step: every kernel's algorithmic bytes / flops, and what the step's time gives
+    roof["step_alg_bytes"] = step_bytes
+    roof["step_alg_flops"] = step_flops
+    roof["step_GBps"] = round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1)
+    roof["step_TFLOPs"] = round(step_flops / (ms_per_step * 1e-3) / 1e12, 2)
+    res = {"cfg": cfg, "value": value, "ms_per_step": ms_per_step, "steps": steps,
+           "warmup": warmup, "R": R, "graphs": bool(graphs), "roofline": roof, "kernels": kinfo}
+    del graphs, fwds, inputs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
+
+# the per-config block: the other four workloads the performance targets are stated for, with
+# the steps each one times (decode-sized steps are short, so more of them)
+OTHER_CONFIGS = {"tiny": 200, "decode": 400, "csa_prefill": 20, "csa_decode": 400}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input copies cycled over (0: enough to exceed 2x the 256 MB MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config block (the other four workloads)")
+    ap.add_argument("--eager", action="store_true", help="launch without HIP graphs")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run a plain elementwise copy of 256 MiB (read) + 256 MiB "
+                         "(written) three times, the reference for HBM byte counters")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    torch.cuda.set_device(0)
+    h = measure(args.workload, args.steps, args.warmup, rotate=args.rotate, eager=args.eager,
+                copy_probe=args.copy_probe)
+    cfg = h["cfg"]
+    rows = cfg.B * cfg.T
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "query tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "metric": METRIC, "value": round(h["value"], 1), "unit": "query tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": h["warmup"], "ms_per_step": round(h["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16"
         if cfg.dt == "bf16" else "f32", "data": "synthetic (seeded, counter-based generator)",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "name": args.workload,
                    "global_batch": rows, "seq_len": cfg.N * cfg.m, "parallelism": "single GPU",
-                   "input_copies": R, "launch": "hip graph" if graphs else "eager",
-                   "event_pass": mode},
-        "roofline": roof,
-        "kernels": kinfo,
+                   "input_copies": h["R"], "launch": "hip graph" if h["graphs"] else "eager",
+                   "event_pass": "eager behind a spin kernel"},
+        "roofline": h["roofline"],
+        "kernels": h["kernels"],
     }
+    if not args.no_configs:
+        block = {}
+        for name, steps in OTHER_CONFIGS.items():
+            if name == args.workload:
+                continue
+            r = measure(name, steps, args.warmup, eager=args.eager)
+            ro = r["roofline"]
+            block[name] = {"workload": WORKLOAD_TEXT[name], "value": round(r["value"], 1),
+                           "unit": "query tokens/s", "ms_per_step": round(r["ms_per_step"], 5),
+                           "steps": steps, "warmup": r["warmup"], "input_copies": r["R"],
+                           "dominant_kernel": ro["kernel"], "bound": ro["bound"],
+                           "achieved": ro["achieved"], "unit_roofline": ro["unit"],
+                           "frac": ro["frac"], "step_GBps": ro["step_GBps"],
+                           "step_TFLOPs": ro["step_TFLOPs"],
+                           "kernels": {k: v["us_per_step"] for k, v in r["kernels"].items()}}
+        line["configs"] = block
     if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)
 

@@ -23,6 +23,9 @@ Recipes (all seeded; seed = workload id, "sharp" variants use seed 100 + id):
             queries (positions 122880..131071); W=128
   sharp variants: q, kv ~ N(0,1) and softmax scale 4/sqrt(D_K), so that attention outputs are
             O(1) and a wrong gather moves them by far more than the tolerance.
+  w_lo < 0: head weights w ~ U(w_lo, 1) (the weights come from a learned projection, so their
+            sign is not fixed): index scores of either sign, and rows whose top-k threshold is
+            negative.
 """
 from __future__ import annotations
 
@@ -64,6 +67,7 @@ class Config:
     kv_std: float = 0.0       # std of stored kv entries (0 -> qkv_std)
     win_std: float = 0.0      # std of raw window rows (0 -> qkv_std)
     dense: bool = False       # HCA: no indexer / top-k, every visible entry attends
+    w_lo: float = 0.0         # head weights w ~ U(w_lo, 1): a negative w_lo gives mixed signs
 
     @property
     def softmax_scale(self) -> float:
@@ -156,7 +160,7 @@ class Workload:
 
     def w(self) -> np.ndarray:
         c = self.cfg
-        return self._get("w", lambda: uniform(c.seed, TID_W, (c.B, c.T, c.H_I), 0.0, 1.0))
+        return self._get("w", lambda: uniform(c.seed, TID_W, (c.B, c.T, c.H_I), c.w_lo, 1.0))
 
     def k_I(self):
         """[B,N,D_I] in dt, or (codes [B,N,D_I/2], scales [B,N,D_I/32]) for MXFP4, or

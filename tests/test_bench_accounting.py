@@ -69,3 +69,20 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_sample_rows():
+    # prefill: 128 distinct rows, always with the first rows, both sides of the k = 2048 edge
+    # and the last row; decode: every row
+    rows = bench.cpu_sample_rows(C["prefill"])
+    assert len(rows) == 128 and len(set(rows)) == 128
+    ts = {t for _, t in rows}
+    assert set(bench.PREFILL_ALWAYS) <= ts
+    assert rows == bench.cpu_sample_rows(C["prefill"])  # seeded
+    assert sorted(bench.cpu_sample_rows(C["decode"])) == [(b, 0) for b in range(16)]
+    assert len(bench.cpu_sample_rows(C["csa_prefill"])) == 64
+
+
+def test_default_workload_is_the_largest_config():
+    ap_src = open(os.path.join(ROOT, "bench.py")).read()
+    assert 'ap.add_argument("--workload", default="prefill"' in ap_src

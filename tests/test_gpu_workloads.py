@@ -12,7 +12,7 @@ import torch
 import oracle
 import synth
 from gpu_util import (DeviceWorkload, check_attention, check_compressed, check_scores,
-                      check_topk, log, to_host)
+                      check_topk, log, score_mass, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -193,3 +193,112 @@ def test_hca_decode():
 def test_hca_prefill():
     _run_hca(synth.CONFIGS["hca_prefill"], n_sample=12)
     _run_hca(synth.CONFIGS["hca_prefill"].with_(T=1024, pos0=131072 - 1024).sharp(), n_sample=12)
+
+
+# ------------------------------------------------------------- head weights of either sign ----
+# The head weights come from a learned projection, so their sign is free: scores of either sign,
+# top-k thresholds below zero, and rows of exact +-0 scores (a zero key row scores exactly 0 for
+# every query; a zero weight row scores 0 everywhere). Each shape below reaches one selection
+# kernel: <= 128 rows with N <= 32768 the fused selection inside the attention kernel, more
+# rows the register radix select, N > 32768 the chunk filter + candidate select (MXFP4 keys).
+
+def _plant_special_rows(wl):
+    """Rewrite the host inputs (before upload; the oracle sees the same bytes):
+      sequence 1: every weight negative, every 7th key zero (fewer zero keys than k: all of them
+                  are selected, at the top of a row of negative scores);
+      sequence 2: every weight zero (the whole row scores exactly 0: the first k are taken);
+      sequence 3: every weight negative and the first 3000 keys zero (a tie at 0 across more
+                  entries than k: the lowest zero-key indices are taken);
+      sequence 4: half of the weights -0.0, the rest negative (scores of -0 and +0 rank equal).
+    Sequences beyond B are skipped."""
+    c = wl.cfg
+    w = wl.w().copy()
+    k = wl.k_I()
+    if isinstance(k, tuple):
+        k = (k[0].copy(), k[1])
+        codes = k[0]
+    else:
+        k = k.copy()
+        codes = k
+    if c.B > 1:
+        w[1] = -np.abs(w[1])
+        codes[1, ::7] = 0
+    if c.B > 2:
+        w[2] = 0.0
+    if c.B > 3:
+        w[3] = -np.abs(w[3])
+        codes[3, :3000] = 0
+    if c.B > 4:
+        w[4] = -np.abs(w[4])
+        w[4, :, : c.H_I // 2] = -0.0
+    wl._cache["w"] = np.ascontiguousarray(w, np.float32)
+    wl._cache["k_I"] = k
+
+
+def _run_exact_selection(c, n_attend=8):
+    """dsa_forward with every row's selection checked exactly: the oracle's top-k over the GPU's
+    own fp32 scores (the same decision in the same precision, so the set is unique; exact ties
+    go to the lowest index), count and -1 padding; the scores of sampled rows against the
+    oracle's, and attention on the GPU's set for sampled rows."""
+    wl = synth.make_workload(c)
+    _plant_special_rows(wl)
+    dw = DeviceWorkload(wl)
+    f = dw.forward(keep_scores=True, keep_idx=True)
+    log(f"[{c.name}] dsa_forward B={c.B} T={c.T} N={c.N} k={c.top_k} m={c.m} W={c.W} "
+        f"w ~ U({c.w_lo}, 1) with planted rows")
+    f.run()
+    torch.cuda.synchronize()
+    run = oracle.QueryRunner(wl)
+    rows = [(b, t) for b in range(c.B) for t in range(c.T)]
+    check = set(_sample_rows(c, n_attend)) | {(b, 0) for b in range(min(c.B, 5))}
+    worst, worst_b, negative_tau, zero_tau = 0.0, 0.0, 0, 0
+    for b, t in rows:
+        what = f"{c.name} b={b} t={t}"
+        sc = to_host(f.scores[b, t])
+        ix = to_host(f.idx[b, t])
+        nv = oracle.n_vis(int(wl.q_pos()[b, t]), c.m, c.N)
+        cnt = min(nv, c.top_k)
+        ref, rcnt = oracle.topk_row(sc[:nv].astype(np.float64), nv, c.top_k)
+        assert rcnt == cnt
+        assert np.array_equal(np.sort(ix[:cnt]), ref[:cnt]), f"{what}: selection differs"
+        assert (ix[cnt:] == -1).all(), f"{what}: padding"
+        if nv > c.top_k:
+            tau = sc[ref[:cnt]].min()
+            negative_tau += int(tau < 0)
+            zero_tau += int(tau == 0)
+        if (b, t) in check:
+            mass = score_mass(wl, b, t)
+            e = check_scores(sc, run.scores(b, t), nv, what=what, mass=mass,
+                             dims=(c.H_I, c.D_I))
+            if mass is None:
+                worst = max(worst, e)
+            else:
+                worst_b = max(worst_b, e)
+            out = oracle.decode(to_host(f.out[b, t]))
+            ro, rl = run.attend(b, t, ix)
+            check_attention(out, to_host(f.lse[b, t]), ro, rl, what=what)
+    log(f"[{c.name}] selection exact on {len(rows)} rows ({negative_tau} with a negative and "
+        f"{zero_tau} with a zero threshold), score rel err {worst:.2e} (positive weights), "
+        f"largest error / fp32 accumulation bound {worst_b:.2e} (mixed signs)")
+    assert negative_tau > 0 and zero_tau > 0
+    del f, dw
+
+
+def test_mixed_sign_weights_fused_decode():
+    # the decode workload's shape (16 rows, N = 8192): selection inside the attention kernel
+    _run_exact_selection(synth.CONFIGS["decode"].with_(w_lo=-1.0, name="decode_mixed_w"))
+
+
+def test_mixed_sign_weights_prefill_rows():
+    # 5 x 60 = 300 rows in one call: the register radix select of topk_select
+    c = synth.CONFIGS["decode"].with_(B=5, T=60, N=3500, pos0=100, pos_stride=57, top_k=1024,
+                                      w_lo=-1.0, name="prefill_rows_mixed_w")
+    _run_exact_selection(c, n_attend=12)
+
+
+def test_mixed_sign_weights_csa_decode_fp4():
+    # MXFP4 keys over N = 40000 blocks (> 32768): chunk filter + candidate select, CSA window
+    p = 4 * 40000 - 1
+    c = synth.CONFIGS["csa_decode"].with_(B=5, N=40000, pos0=p, raw_base=p + 1 - 128, w_lo=-1.0,
+                                          name="csa_decode_mixed_w")
+    _run_exact_selection(c)
