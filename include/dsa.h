@@ -55,7 +55,9 @@ typedef enum dsa_status {
   DSA_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                             */
   DSA_ERR_WORKSPACE = 5, /* workspace NULL or smaller than dsa_workspace_bytes           */
   DSA_ERR_DEVICE = 6,    /* current HIP device is not gfx950, or the device query failed */
-  DSA_ERR_LAUNCH = 7     /* a kernel launch reported an error                            */
+  DSA_ERR_LAUNCH = 7,    /* a kernel launch reported an error                            */
+  DSA_ERR_SCRATCH = 8    /* dsa_forward_noalloc: the call needs more workspace than the
+                            static scratch array holds (DSA_NOALLOC_SCRATCH_BYTES)        */
 } dsa_status;
 
 typedef enum dsa_dtype {
@@ -230,6 +232,28 @@ dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
  * Graph-capturable (no sync, no alloc). */
 dsa_status hca_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* Bytes of the static per-GPU scratch array behind dsa_forward_noalloc. */
+#define DSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* dsa_forward for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. The same launches and results as
+ * dsa_forward, with the workspace taken from a static device array of
+ * DSA_NOALLOC_SCRATCH_BYTES bytes (one per GPU the library runs on, held until the process
+ * ends) instead of a caller's buffer. The caller still passes inputs and outputs in `a`.
+ * No hipMalloc / hipFree and no allocating library call, on any path. The array's address on
+ * the current device is looked up once per device, on the first call there.
+ *   - Returns DSA_ERR_SCRATCH, launching nothing, when dsa_workspace_bytes(d, DSA_OP_FORWARD)
+ *     exceeds DSA_NOALLOC_SCRATCH_BYTES (the decode-sized workloads fit; a 32768-query
+ *     prefill, whose scores alone take 256 MB, does not).
+ *   - Every call on one GPU shares that GPU's array and finds the previous call's contents in
+ *     it (nothing in it needs to start at zero). Calls that overlap in time on one GPU (two
+ *     streams, two host threads) race on the array: serialise them.
+ * Other errors as dsa_forward. */
+dsa_status dsa_forward_noalloc(const dsa_dims* d, const dsa_forward_args* a, void* stream);
+
+/* DSA_NOALLOC_SCRATCH_BYTES, for bindings that cannot read the macro. */
+size_t dsa_noalloc_scratch_bytes(void);
 
 #ifdef __cplusplus
 }

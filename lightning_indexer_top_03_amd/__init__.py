@@ -28,10 +28,12 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 F32, BF16, MXFP4, MXFP8 = 0, 1, 2, 3
+ERR_WORKSPACE, ERR_SCRATCH = 5, 8
 OP_TOPK, OP_ATTEND, OP_FORWARD, OP_HCA = 1, 2, 3, 4
 
 EXPORTS = ("dsa_status_str", "dsa_version", "dsa_workspace_bytes", "kv_compress_mean",
-           "indexer_scores", "topk_select", "sparse_mla_attend", "dsa_forward", "hca_forward")
+           "indexer_scores", "topk_select", "sparse_mla_attend", "dsa_forward", "hca_forward",
+           "dsa_forward_noalloc", "dsa_noalloc_scratch_bytes")
 
 
 class Dims(ctypes.Structure):
@@ -67,8 +69,10 @@ _lib.sparse_mla_attend.argtypes = [_D, ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _
                                    ctypes.c_float, _vp, _vp, _vp, _sz, _vp]
 _lib.dsa_forward.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]
 _lib.hca_forward.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]
+_lib.dsa_forward_noalloc.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp]
+_lib.dsa_noalloc_scratch_bytes.restype = _sz
 for _f in ("kv_compress_mean", "indexer_scores", "topk_select", "sparse_mla_attend",
-           "dsa_forward", "hca_forward"):
+           "dsa_forward", "hca_forward", "dsa_forward_noalloc"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -269,6 +273,14 @@ class Forward:
         st = torch.cuda.current_stream(self.device).cuda_stream if stream is None else stream
         _check(_lib.dsa_forward(ctypes.byref(self.d), ctypes.byref(self.args), _ptr(self.ws),
                                 0 if self.ws is None else self.ws.numel(), st), "dsa_forward")
+        return self.out
+
+    def run_noalloc(self, stream: Optional[int] = None) -> torch.Tensor:
+        """The same call through dsa_forward_noalloc: the library's static per-GPU scratch array
+        instead of this object's workspace (calls on one GPU must not overlap)."""
+        st = torch.cuda.current_stream(self.device).cuda_stream if stream is None else stream
+        _check(_lib.dsa_forward_noalloc(ctypes.byref(self.d), ctypes.byref(self.args), st),
+               "dsa_forward_noalloc")
         return self.out
 
 

@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "dsa.h"
 #include "launch.h"
@@ -73,6 +74,24 @@ dsa_status check_attend_shape(const dsa_dims* d) {
 }
 
 std::atomic<int> g_dev_ok[64];  // 0 unknown, 1 gfx950, 2 other
+
+// Workspace of dsa_forward_noalloc: one array per GPU, held until the process ends. In host code
+// `scratch` names a host-side stand-in, never the device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device (looked up once per device).
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_ptr[64];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (nullptr when the lookup fails).
+void* scratch_ptr(int dev) {
+  if (void* p = g_scratch_ptr[dev].load(std::memory_order_acquire)) return p;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (void* p = g_scratch_ptr[dev].load(std::memory_order_relaxed)) return p;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
 
 dsa_status check_device() {
   int dev = 0;
@@ -144,6 +163,74 @@ Shape hca_shape(const dsa_dims* d) {
   return s;
 }
 
+// Argument rules of dsa_forward (everything but the workspace).
+dsa_status check_forward(const dsa_dims* d, const dsa_forward_args* a) {
+  if (dsa_status st = check_dims(d)) return st;
+  if (!a) return DSA_ERR_NULL;
+  if (dsa_status st = check_attend_shape(d)) return st;
+  if (!fmt_ok(a->dt)) return DSA_ERR_DTYPE;
+  const dsa_dtype qi_dt = a->q_scale != nullptr ? DSA_MXFP8 : a->dt;
+  if (a->q_scale && a->dt != DSA_BF16) return DSA_ERR_DTYPE;
+  if (dsa_status st = check_indexer(d, qi_dt, a->q_scale, a->k_dt, a->k_scale)) return st;
+  if (a->q_scale && ((uintptr_t)a->q_scale & 3u)) return DSA_ERR_ALIGN;
+  if (!a->q_I || !a->w || !a->k_I || !a->q || !a->kv || !a->q_pos || !a->out) return DSA_ERR_NULL;
+  if ((d->W > 0 || a->compress) && !a->kv_raw) return DSA_ERR_NULL;
+  if (a->raw_base < 0 || a->n_raw < 0) return DSA_ERR_SHAPE;
+  if (a->compress && (a->raw_base != 0 || a->n_raw / d->m != d->N)) return DSA_ERR_SHAPE;
+  const void* ptrs16[] = {a->q_I, a->w, a->k_I, a->q, a->kv, a->out, a->kv_raw, a->scores,
+                          a->idx};
+  for (const void* p : ptrs16)
+    if (p && !aligned16(p)) return DSA_ERR_ALIGN;
+  if (a->n_events < 0) return DSA_ERR_SHAPE;
+  return DSA_OK;
+}
+
+// The launches of dsa_forward on a validated call, with workspace ws (forward_layout bytes).
+dsa_status run_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, hipStream_t st) {
+  const FwdLayout L = forward_layout(d, a->dt);
+  const dsa_dtype qi_dt = a->q_scale != nullptr ? DSA_MXFP8 : a->dt;
+  const Shape s = to_shape(d);
+  const int fmt = a->dt == DSA_BF16 ? FMT_BF16 : FMT_F32;
+  TimerScope timer(a->events, a->n_events);
+  if (a->compress) {
+    if (hipError_t e = launch_compress(d->B, a->n_raw, d->D_K, d->m, fmt, a->kv_raw, a->kv, st))
+      return launched(e);
+  }
+  char* wsb = static_cast<char*>(ws);
+  float* ws_scores = reinterpret_cast<float*>(wsb);
+  int32_t* ws_idx = reinterpret_cast<int32_t*>(wsb + L.scores);
+  void* ws_att = wsb + L.scores + L.idx;
+  void* ws_topk = wsb + L.scores + L.idx + L.attend;
+  const int64_t rows = (int64_t)d->B * d->T;
+  const int64_t R = forward_chunk_rows(d);  // the attention workspace is sized for R rows
+  const bool keep_scores = a->scores != nullptr;
+  for (int64_t q0 = 0; q0 < rows; q0 += R) {
+    const int64_t nr = std::min(R, rows - q0);
+    float* sc = keep_scores ? a->scores + (size_t)q0 * d->N : ws_scores;
+    int32_t* ix = a->idx ? a->idx + (size_t)q0 * d->top_k : ws_idx;
+    if (hipError_t e = launch_indexer(s, q0, nr, a->q_I, (int)qi_dt, a->q_scale, a->w, a->k_I,
+                                      a->k_scale, (int)a->k_dt, a->q_pos, sc, keep_scores, st))
+      return launched(e);
+    if (attend_fused_ok(s, fmt, nr)) {
+      // top-k inside the attention kernel: idx is written only when the caller wants it
+      if (hipError_t e = launch_attend_fused(s, q0, nr, a->q, a->kv, sc,
+                                             a->idx ? a->idx + (size_t)q0 * d->top_k : nullptr,
+                                             d->W > 0 ? a->kv_raw : nullptr, a->raw_base,
+                                             a->n_raw, a->q_pos, a->softmax_scale, a->out, a->lse,
+                                             ws_att, st))
+        return launched(e);
+    } else {
+      if (hipError_t e = launch_topk(s, q0, nr, sc, a->q_pos, ix, ws_topk, st))
+        return launched(e);
+      if (hipError_t e = launch_attend(s, q0, nr, fmt, a->q, a->kv, ix,
+                                       d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw,
+                                       a->q_pos, a->softmax_scale, a->out, a->lse, ws_att, st))
+        return launched(e);
+    }
+  }
+  return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -158,11 +245,13 @@ const char* dsa_status_str(int status) {
     case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
     case DSA_ERR_DEVICE: return "DSA_ERR_DEVICE: current HIP device is not gfx950";
     case DSA_ERR_LAUNCH: return "DSA_ERR_LAUNCH: a kernel launch failed";
+    case DSA_ERR_SCRATCH:
+      return "DSA_ERR_SCRATCH: the call needs more workspace than the static scratch array holds";
     default: return "unknown dsa_status";
   }
 }
 
-int dsa_version(void) { return 100; }
+int dsa_version(void) { return 101; }
 
 size_t dsa_workspace_bytes(const dsa_dims* d, int op) {
   if (op == DSA_OP_HCA) {
@@ -250,69 +339,24 @@ dsa_status sparse_mla_attend(const dsa_dims* d, dsa_dtype dt, const void* q, con
 
 dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, size_t ws_bytes,
                        void* stream) {
-  if (dsa_status st = check_dims(d)) return st;
-  if (!a) return DSA_ERR_NULL;
-  if (dsa_status st = check_attend_shape(d)) return st;
-  if (!fmt_ok(a->dt)) return DSA_ERR_DTYPE;
-  const dsa_dtype qi_dt = a->q_scale != nullptr ? DSA_MXFP8 : a->dt;
-  if (a->q_scale && a->dt != DSA_BF16) return DSA_ERR_DTYPE;
-  if (dsa_status st = check_indexer(d, qi_dt, a->q_scale, a->k_dt, a->k_scale)) return st;
-  if (a->q_scale && ((uintptr_t)a->q_scale & 3u)) return DSA_ERR_ALIGN;
-  if (!a->q_I || !a->w || !a->k_I || !a->q || !a->kv || !a->q_pos || !a->out) return DSA_ERR_NULL;
-  if ((d->W > 0 || a->compress) && !a->kv_raw) return DSA_ERR_NULL;
-  if (a->raw_base < 0 || a->n_raw < 0) return DSA_ERR_SHAPE;
-  if (a->compress && (a->raw_base != 0 || a->n_raw / d->m != d->N)) return DSA_ERR_SHAPE;
-  const void* ptrs16[] = {a->q_I, a->w, a->k_I, a->q, a->kv, a->out, a->kv_raw, a->scores,
-                          a->idx, ws};
-  for (const void* p : ptrs16)
-    if (p && !aligned16(p)) return DSA_ERR_ALIGN;
-  const FwdLayout L = forward_layout(d, a->dt);
-  if (!ws || ws_bytes < L.total) return DSA_ERR_WORKSPACE;
+  if (dsa_status st = check_forward(d, a)) return st;
+  if (ws && !aligned16(ws)) return DSA_ERR_ALIGN;
+  if (!ws || ws_bytes < forward_layout(d, a->dt).total) return DSA_ERR_WORKSPACE;
   if (dsa_status st = check_device()) return st;
+  return run_forward(d, a, ws, (hipStream_t)stream);
+}
 
-  hipStream_t st = (hipStream_t)stream;
-  const Shape s = to_shape(d);
-  const int fmt = a->dt == DSA_BF16 ? FMT_BF16 : FMT_F32;
-  if (a->n_events < 0) return DSA_ERR_SHAPE;
-  TimerScope timer(a->events, a->n_events);
-  if (a->compress) {
-    if (hipError_t e = launch_compress(d->B, a->n_raw, d->D_K, d->m, fmt, a->kv_raw, a->kv, st))
-      return launched(e);
-  }
-  char* wsb = static_cast<char*>(ws);
-  float* ws_scores = reinterpret_cast<float*>(wsb);
-  int32_t* ws_idx = reinterpret_cast<int32_t*>(wsb + L.scores);
-  void* ws_att = wsb + L.scores + L.idx;
-  void* ws_topk = wsb + L.scores + L.idx + L.attend;
-  const int64_t rows = (int64_t)d->B * d->T;
-  const int64_t R = forward_chunk_rows(d);  // the attention workspace is sized for R rows
-  const bool keep_scores = a->scores != nullptr;
-  for (int64_t q0 = 0; q0 < rows; q0 += R) {
-    const int64_t nr = std::min(R, rows - q0);
-    float* sc = keep_scores ? a->scores + (size_t)q0 * d->N : ws_scores;
-    int32_t* ix = a->idx ? a->idx + (size_t)q0 * d->top_k : ws_idx;
-    if (hipError_t e = launch_indexer(s, q0, nr, a->q_I, (int)qi_dt, a->q_scale, a->w, a->k_I,
-                                      a->k_scale,
-                                      (int)a->k_dt, a->q_pos, sc, keep_scores, st))
-      return launched(e);
-    if (attend_fused_ok(s, fmt, nr)) {
-      // top-k inside the attention kernel: idx is written only when the caller wants it
-      if (hipError_t e = launch_attend_fused(s, q0, nr, a->q, a->kv, sc,
-                                             a->idx ? a->idx + (size_t)q0 * d->top_k : nullptr,
-                                             d->W > 0 ? a->kv_raw : nullptr, a->raw_base,
-                                             a->n_raw, a->q_pos, a->softmax_scale, a->out, a->lse,
-                                             ws_att, st))
-        return launched(e);
-    } else {
-      if (hipError_t e = launch_topk(s, q0, nr, sc, a->q_pos, ix, ws_topk, st))
-        return launched(e);
-      if (hipError_t e = launch_attend(s, q0, nr, fmt, a->q, a->kv, ix,
-                                       d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw,
-                                       a->q_pos, a->softmax_scale, a->out, a->lse, ws_att, st))
-        return launched(e);
-    }
-  }
-  return DSA_OK;
+size_t dsa_noalloc_scratch_bytes(void) { return DSA_NOALLOC_SCRATCH_BYTES; }
+
+dsa_status dsa_forward_noalloc(const dsa_dims* d, const dsa_forward_args* a, void* stream) {
+  if (dsa_status st = check_forward(d, a)) return st;
+  if (forward_layout(d, a->dt).total > (size_t)DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_SCRATCH;
+  if (dsa_status st = check_device()) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_DEVICE;
+  void* ws = scratch_ptr(dev);
+  if (ws == nullptr) return DSA_ERR_DEVICE;
+  return run_forward(d, a, ws, (hipStream_t)stream);
 }
 
 dsa_status hca_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, size_t ws_bytes,

@@ -33,11 +33,11 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    for code in range(8):
+    for code in range(9):
         s = L.dsa_status_str(code).decode()
         assert s.startswith("DSA_"), s
     assert L.dsa_status_str(99).decode() == "unknown dsa_status"
-    assert L.dsa_version() == 100
+    assert L.dsa_version() == 101
 
 
 def _dims(**kw):
@@ -124,6 +124,27 @@ def test_forward_validation_and_workspace():
     a.compress, a.kv_raw, a.n_raw = 0, None, 0
     a.q_I = P + 8
     assert L.dsa_forward(ctypes.byref(d), ctypes.byref(a), P, need, None) == 4
+
+
+def test_forward_noalloc_validation():
+    # the same argument rules as dsa_forward, and a clear error (nothing launched) when the call
+    # needs more workspace than the static scratch array holds
+    cap = L.dsa_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    a = dsa.ForwardArgs(dsa.BF16, dsa.BF16, P, P, P, None, P, P, None, 0, 0, 0, P, 0.1, P, None,
+                        None, None, None, 0)
+    dec = _dims(B=16, T=1, N=8192, top_k=2048)
+    assert 0 < L.dsa_workspace_bytes(ctypes.byref(dec), dsa.OP_FORWARD) <= cap
+    big = _dims(B=1, T=32768, N=32768, top_k=2048)
+    assert L.dsa_workspace_bytes(ctypes.byref(big), dsa.OP_FORWARD) > cap
+    assert L.dsa_forward_noalloc(ctypes.byref(big), ctypes.byref(a), None) == dsa.ERR_SCRATCH
+    assert L.dsa_forward_noalloc(ctypes.byref(dec), None, None) == 1
+    assert L.dsa_forward_noalloc(ctypes.byref(_dims(N=0)), ctypes.byref(a), None) == 2
+    a.q = P + 4
+    assert L.dsa_forward_noalloc(ctypes.byref(dec), ctypes.byref(a), None) == 4
+    a.q = P
+    if not torch.cuda.is_available():
+        assert L.dsa_forward_noalloc(ctypes.byref(dec), ctypes.byref(a), None) == 6
 
 
 def test_hca_validation_and_workspace():

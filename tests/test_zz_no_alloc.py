@@ -1,0 +1,50 @@
+"""dsa_forward_noalloc (the workspace in the library's static per-GPU scratch array) against
+dsa_forward (a caller's workspace) on the same inputs: the same kernels run on the same bytes,
+so every output must match bit for bit. Two calls in a row, the second with a smaller input
+(the scratch array keeps the first call's contents), then a CSA decode call whose long rows use
+the top-k candidate region of the workspace as well."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import DeviceWorkload, log, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    yield
+    torch.cuda.empty_cache()
+
+
+def _outputs(f):
+    return [to_host(t) for t in (f.out, f.lse, f.scores, f.idx)]
+
+
+def _compare(c):
+    dw = DeviceWorkload(synth.make_workload(c))
+    ref = dw.forward(keep_scores=True, keep_idx=True)
+    got = dw.forward(keep_scores=True, keep_idx=True)
+    for t in (got.out, got.lse, got.scores, got.idx):
+        t.fill_(7)  # anything stale would show
+    log(f"[{c.name}] dsa_forward and dsa_forward_noalloc B={c.B} T={c.T} N={c.N} k={c.top_k}")
+    ref.run()
+    got.run_noalloc()
+    torch.cuda.synchronize()
+    for name, a, b in zip(("out", "lse", "scores", "idx"), _outputs(ref), _outputs(got)):
+        assert a.shape == b.shape
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{c.name}: {name} differs"
+    del ref, got, dw
+
+
+def test_noalloc_matches_dsa_forward_twice():
+    _compare(synth.CONFIGS["decode"].with_(name="noalloc_decode"))
+    _compare(synth.CONFIGS["decode"].with_(B=3, N=3001, pos0=3000, top_k=1024,
+                                           name="noalloc_smaller").sharp())
+    p = 4 * 40000 - 1
+    _compare(synth.CONFIGS["csa_decode"].with_(B=2, N=40000, pos0=p, raw_base=p + 1 - 128,
+                                               name="noalloc_csa"))
