@@ -18,6 +18,8 @@
  *        64-head x 128-dim ReLU-weighted FP4 indexer).
  *   [P4] Tencent Cloud developer search "compressed sparse attention (CSA)": compress -> index
  *        select -> core attention; window KV concatenated with compressed KV; average pooling.
+ *   [P3] wiki.gxlh.xyz "sparse attention" tag page, GLM-5.3 summary (IndexShare: one index
+ *        selection reused by several layers).
  * The page's own index-score formula image is lost; the score used here is
  *   I[t,s] = sum_j w[t,j] * ReLU(q_I[t,j,:] . k_I[s,:]).
  *
@@ -33,6 +35,9 @@
  *     query token): entry s (token, or block of m tokens) is visible iff s < n_vis with
  *         n_vis = min(N, floor((q_pos + 1) / m)),
  *     i.e. a query sees itself (m == 1) and only complete blocks (m > 1).
+ *   - Ragged batches: where a call takes seq_len[B] (int32, nullable), sequence b holds only
+ *     seq_len[b] entries of its N-entry storage, and n_vis = min(N, floor((q_pos+1)/m),
+ *     seq_len[b]) (a negative seq_len counts as 0). NULL = every sequence holds N.
  *   - Shapes use dsa_dims below. Value vectors are the first D_V columns of the key row
  *     (MQA-mode MLA: one latent row per entry shared by all H query heads, [P5] s1.4).
  *   - Thread safety: calls may run concurrently on different streams.
@@ -106,6 +111,18 @@ int dsa_version(void);
  * Returns 0 for invalid dims as well; the call itself then reports the error. */
 size_t dsa_workspace_bytes(const dsa_dims* d, int op);
 
+/* Incremental compression for decoding ([P1] V4 CSA summary: one compressed entry per m
+ * tokens; a decoder appends one as each block of m raw tokens completes). For every sequence b
+ * and block j0 <= j < j1:
+ *   kv_c[b, j, :] = (1/m) * sum_{i<m} kv_raw[b, m*j + i, :]
+ * kv_raw: [B, raw_stride, D_K] of dtype dt (F32 or BF16); kv_c: [B, c_stride, D_K], same dtype;
+ * needs j1 <= c_stride and m*j1 <= raw_stride (DSA_ERR_SHAPE otherwise). Arithmetic as
+ * kv_compress_mean (fp32 sum, one RNE rounding); entries outside [j0, j1) are not touched.
+ * Uses d->B, d->D_K, d->m. */
+dsa_status kv_compress_blocks(const dsa_dims* d, dsa_dtype dt, const void* kv_raw,
+                              int64_t raw_stride, void* kv_c, int64_t c_stride, int64_t j0,
+                              int64_t j1, void* stream);
+
 /* Step 0 - CSA token-dimension compression ([P1] V4 CSA summary; [P4] CSA snippets: m
  * consecutive tokens' KV pooled into one entry, average pooling named as one choice).
  *   kv_c[b, j, :] = (1/m) * sum_{i<m} kv_raw[b, m*j + i, :],   j < floor(n_raw / m)
@@ -126,6 +143,7 @@ dsa_status kv_compress_mean(const dsa_dims* d, dsa_dtype dt, const void* kv_raw,
  *         for k_dt == MXFP8 codes [B,N,D_I] bytes
  * k_scale:[B,N,D_I/32] E8M0 bytes when k_dt is MXFP4 or MXFP8, else must be NULL
  * q_pos:  [B,T] int32
+ * seq_len:[B] int32 or NULL (ragged batch, see the conventions)
  * scores: [B,T,N] fp32 (written in full)
  * (q_dt, k_dt) pairs: (F32, F32), (BF16, BF16), (BF16, MXFP4), (BF16, MXFP8), (MXFP8, MXFP4),
  * (MXFP8, MXFP8); others give DSA_ERR_DTYPE. MX formats need D_I % 32 == 0.
@@ -136,7 +154,7 @@ dsa_status kv_compress_mean(const dsa_dims* d, dsa_dtype dt, const void* kv_raw,
 dsa_status indexer_scores(const dsa_dims* d, const void* q_I, dsa_dtype q_dt,
                           const uint8_t* q_scale, const float* w, const void* k_I,
                           const uint8_t* k_scale, dsa_dtype k_dt, const int32_t* q_pos,
-                          float* scores, void* stream);
+                          const int32_t* seq_len, float* scores, void* stream);
 
 /* Step 2 - per-query top-k ([P5] s1.3: only the KV entries with the k highest index scores
  * take part; s3 step 3: every token is kept when the context is no longer than k; step 4's
@@ -146,10 +164,12 @@ dsa_status indexer_scores(const dsa_dims* d, const void* q_I, dsa_dtype q_dt,
  *   LOWER index (the result is the first top_k of a stable sort by descending score); the
  *   order inside the row is unspecified.
  *   Slots past the selected count are -1. -0.0 ranks equal to +0.0. Scores must not be NaN.
- * scores: [B,T,N] fp32 (entries s >= n_vis are ignored); idx: [B,T,top_k] int32.
+ * scores: [B,T,N] fp32 (entries s >= n_vis are ignored); idx: [B,T,top_k] int32; seq_len:
+ * [B] int32 or NULL (ragged batch).
  * ws: dsa_workspace_bytes(d, DSA_OP_TOPK) bytes (may be 0). */
 dsa_status topk_select(const dsa_dims* d, const float* scores, const int32_t* q_pos,
-                       int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+                       const int32_t* seq_len, int32_t* idx, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* Step 3 - sparse MQA-mode MLA attention ([P5] s1.3 "fine-grained sparse attention", s1.4,
  * s3 step 4; [P4] window KV concatenated with the compressed KV into one core attention).
@@ -160,6 +180,12 @@ dsa_status topk_select(const dsa_dims* d, const float* scores, const int32_t* q_
  * one joint softmax over E (no de-duplication):
  *   z_e = softmax_scale * q[b,t,h,:D_K] . K_e[:D_K];  out[b,t,h,:] = sum_e softmax(z)_e K_e[:D_V]
  *   lse[b,t,h] = log sum_e exp(z_e).  Empty E: out = 0, lse = -inf.
+ * Attention sink ([P4] CSA snippet 4.3: sliding window plus an attention sink): sink [H] fp32 or
+ * NULL, one logit per head (not multiplied by softmax_scale) that joins the softmax with a zero
+ * value vector: out = sum_e exp(z_e) K_e[:D_V] / (sum_e exp(z_e) + exp(sink[h])),
+ * lse = log(sum_e exp(z_e) + exp(sink[h])); empty E then gives out = 0, lse = sink[h].
+ * IndexShare ([P3] GLM-5.3 summary: layers reuse one index selection): a later layer passes the
+ * idx a dsa_forward call returned (a->idx) with its own q / kv.
  * q: [B,T,H,D_K], kv: [B,N,D_K], kv_raw: [B,n_raw,D_K] (NULL iff W == 0), out: [B,T,H,D_V],
  * all of dtype dt (F32 or BF16); lse: [B,T,H] fp32 or NULL. idx values must be < N.
  * bf16: MFMA products, fp32 accumulation, online softmax, out rounded RNE.
@@ -167,7 +193,8 @@ dsa_status topk_select(const dsa_dims* d, const float* scores, const int32_t* q_
 dsa_status sparse_mla_attend(const dsa_dims* d, dsa_dtype dt, const void* q, const void* kv,
                              const int32_t* idx, const void* kv_raw, int64_t raw_base,
                              int64_t n_raw, const int32_t* q_pos, float softmax_scale,
-                             void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+                             const float* sink, void* out, float* lse, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* Arguments of dsa_forward (pointers as in the calls above). */
 typedef struct dsa_forward_args {
@@ -203,6 +230,8 @@ typedef struct dsa_forward_args {
   int32_t n_events;
   const uint8_t* q_scale;/* NULL, or the E8M0 scales [B,T,H_I,D_I/32] of an MXFP8 q_I (then q_I
                             holds e4m3 codes [B,T,H_I,D_I]); indexer only                 */
+  const int32_t* seq_len;/* [B] or NULL: entries held per sequence (ragged batch)           */
+  const float* sink;     /* [H] or NULL: attention-sink logit per head (sparse_mla_attend)  */
 } dsa_forward_args;
 
 /* Fused path: [compress] -> indexer_scores -> topk_select -> sparse_mla_attend on `stream`
@@ -224,8 +253,8 @@ dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
  *   E = { kv[b, j, :] : 0 <= j < n } u { the raw window rows of sparse_mla_attend },
  * one joint softmax over E as in sparse_mla_attend. a->compress != 0 first writes
  * kv = kv_compress_mean(kv_raw) (needs raw_base == 0, floor(n_raw / m) == N).
- * Uses from `a`: dt (F32 or BF16), q, kv, kv_raw, raw_base, n_raw, compress, q_pos,
- * softmax_scale, out, lse, events / n_events (kernel order: [compress,] attention[, split
+ * Uses from `a`: dt (F32 or BF16), q, kv, kv_raw, raw_base, n_raw, compress, q_pos, seq_len
+ * (ragged batch), sink, softmax_scale, out, lse, events / n_events (kernel order: [compress,] attention[, split
  * combine]); the indexer fields (q_I, w, k_I, k_scale, k_dt, scores, idx) are ignored, and so
  * are d->top_k, d->H_I and d->D_I. Needs N + W <= DSA_MAX_HCA_ENTRIES (DSA_ERR_SHAPE otherwise).
  * ws: dsa_workspace_bytes(d, DSA_OP_HCA) bytes (split partials for few-query calls; may be 0).

@@ -32,8 +32,8 @@ ERR_WORKSPACE, ERR_SCRATCH = 5, 8
 OP_TOPK, OP_ATTEND, OP_FORWARD, OP_HCA = 1, 2, 3, 4
 
 EXPORTS = ("dsa_status_str", "dsa_version", "dsa_workspace_bytes", "kv_compress_mean",
-           "indexer_scores", "topk_select", "sparse_mla_attend", "dsa_forward", "hca_forward",
-           "dsa_forward_noalloc", "dsa_noalloc_scratch_bytes")
+           "kv_compress_blocks", "indexer_scores", "topk_select", "sparse_mla_attend",
+           "dsa_forward", "hca_forward", "dsa_forward_noalloc", "dsa_noalloc_scratch_bytes")
 
 
 class Dims(ctypes.Structure):
@@ -51,7 +51,8 @@ class ForwardArgs(ctypes.Structure):
                 ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
                 ("scores", ctypes.c_void_p), ("idx", ctypes.c_void_p),
                 ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32),
-                ("q_scale", ctypes.c_void_p)]
+                ("q_scale", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
+                ("sink", ctypes.c_void_p)]
 
 
 _vp, _i64, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
@@ -62,17 +63,18 @@ _lib.dsa_version.restype = ctypes.c_int
 _lib.dsa_workspace_bytes.argtypes = [_D, ctypes.c_int]
 _lib.dsa_workspace_bytes.restype = _sz
 _lib.kv_compress_mean.argtypes = [_D, ctypes.c_int, _vp, _i64, _vp, _vp]
+_lib.kv_compress_blocks.argtypes = [_D, ctypes.c_int, _vp, _i64, _vp, _i64, _i64, _i64, _vp]
 _lib.indexer_scores.argtypes = [_D, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp,
-                                _vp]
-_lib.topk_select.argtypes = [_D, _vp, _vp, _vp, _vp, _sz, _vp]
+                                _vp, _vp]
+_lib.topk_select.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.sparse_mla_attend.argtypes = [_D, ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
-                                   ctypes.c_float, _vp, _vp, _vp, _sz, _vp]
+                                   ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.dsa_forward.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]
 _lib.hca_forward.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]
 _lib.dsa_forward_noalloc.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp]
 _lib.dsa_noalloc_scratch_bytes.restype = _sz
-for _f in ("kv_compress_mean", "indexer_scores", "topk_select", "sparse_mla_attend",
-           "dsa_forward", "hca_forward", "dsa_forward_noalloc"):
+for _f in ("kv_compress_mean", "kv_compress_blocks", "indexer_scores", "topk_select",
+           "sparse_mla_attend", "dsa_forward", "hca_forward", "dsa_forward_noalloc"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -137,6 +139,17 @@ def kv_compress_mean(kv_raw: torch.Tensor, m: int, kv_c: Optional[torch.Tensor] 
     return kv_c
 
 
+def kv_compress_blocks(kv_raw: torch.Tensor, m: int, kv_c: torch.Tensor, j0: int, j1: int):
+    """Blocks j0 .. j1-1 of every sequence: kv_c[:, j] = mean of kv_raw[:, m*j .. m*j+m-1]
+    (kv_raw [B, raw_stride, D], kv_c [B, c_stride, D]); the rest of kv_c is left alone."""
+    B, raw_stride, D = kv_raw.shape
+    d = dims(B=B, D_K=D, m=m)
+    _check(_lib.kv_compress_blocks(ctypes.byref(d), _dt(kv_raw), _ptr(kv_raw), raw_stride,
+                                   _ptr(kv_c), kv_c.shape[1], j0, j1, _stream(kv_raw)),
+           "kv_compress_blocks")
+    return kv_c
+
+
 # ---- step 1 -----------------------------------------------------------------------------------
 
 KeyT = Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]
@@ -162,9 +175,11 @@ def _queries(q_I: KeyT):
 
 
 def indexer_scores(q_I: KeyT, w: torch.Tensor, k_I: KeyT, q_pos: torch.Tensor,
-                   m: int = 1, scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+                   m: int = 1, scores: Optional[torch.Tensor] = None,
+                   seq_len: Optional[torch.Tensor] = None) -> torch.Tensor:
     """q_I [B,T,H_I,D_I] or MXFP8 (codes, scales), w [B,T,H_I] fp32, k_I [B,N,D_I] or MX
-    (codes, scales), q_pos [B,T] int32 -> scores [B,T,N] fp32 (-inf where not visible)."""
+    (codes, scales), q_pos [B,T] int32, seq_len [B] int32 (ragged batch) or None -> scores
+    [B,T,N] fp32 (-inf where not visible)."""
     qt, qs, qdt = _queries(q_I)
     B, T, H_I, D_I = qt.shape
     kt, ks, kdt, N, _ = _keys(k_I, qdt)
@@ -172,7 +187,8 @@ def indexer_scores(q_I: KeyT, w: torch.Tensor, k_I: KeyT, q_pos: torch.Tensor,
         scores = torch.empty((B, T, N), dtype=torch.float32, device=qt.device)
     d = dims(B=B, T=T, N=N, H_I=H_I, D_I=D_I, m=m)
     _check(_lib.indexer_scores(ctypes.byref(d), _ptr(qt), qdt, _ptr(qs), _ptr(w), _ptr(kt),
-                               _ptr(ks), kdt, _ptr(q_pos), _ptr(scores), _stream(qt)),
+                               _ptr(ks), kdt, _ptr(q_pos), _ptr(seq_len), _ptr(scores),
+                               _stream(qt)),
            "indexer_scores")
     return scores
 
@@ -180,15 +196,18 @@ def indexer_scores(q_I: KeyT, w: torch.Tensor, k_I: KeyT, q_pos: torch.Tensor,
 # ---- step 2 -----------------------------------------------------------------------------------
 
 def topk_select(scores: torch.Tensor, q_pos: torch.Tensor, top_k: int, m: int = 1,
-                idx: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """scores [B,T,N] fp32 -> idx [B,T,top_k] int32 (set semantics, -1 padded)."""
+                idx: Optional[torch.Tensor] = None,
+                seq_len: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """scores [B,T,N] fp32 -> idx [B,T,top_k] int32 (set semantics, -1 padded); seq_len [B]
+    int32 (ragged batch) or None."""
     B, T, N = scores.shape
     if idx is None:
         idx = torch.empty((B, T, top_k), dtype=torch.int32, device=scores.device)
     d = dims(B=B, T=T, N=N, top_k=top_k, m=m)
     ws = _workspace(d, OP_TOPK, scores.device)
-    _check(_lib.topk_select(ctypes.byref(d), _ptr(scores), _ptr(q_pos), _ptr(idx), _ptr(ws),
-                            0 if ws is None else ws.numel(), _stream(scores)), "topk_select")
+    _check(_lib.topk_select(ctypes.byref(d), _ptr(scores), _ptr(q_pos), _ptr(seq_len), _ptr(idx),
+                            _ptr(ws), 0 if ws is None else ws.numel(), _stream(scores)),
+           "topk_select")
     return idx
 
 
@@ -198,9 +217,10 @@ def sparse_mla_attend(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor, q_po
                       D_V: int, softmax_scale: float, kv_raw: Optional[torch.Tensor] = None,
                       raw_base: int = 0, W: int = 0, m: int = 1,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                      want_lse: bool = True):
+                      want_lse: bool = True, sink: Optional[torch.Tensor] = None):
     """q [B,T,H,D_K], kv [B,N,D_K], idx [B,T,k] int32, optional raw window rows kv_raw
-    [B,n_raw,D_K] at positions raw_base.. -> (out [B,T,H,D_V], lse [B,T,H] fp32)."""
+    [B,n_raw,D_K] at positions raw_base.., optional attention-sink logits sink [H] fp32 ->
+    (out [B,T,H,D_V], lse [B,T,H] fp32)."""
     B, T, H, D_K = q.shape
     N = kv.shape[1]
     k = idx.shape[2]
@@ -213,7 +233,7 @@ def sparse_mla_attend(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor, q_po
     n_raw = 0 if kv_raw is None else kv_raw.shape[1]
     _check(_lib.sparse_mla_attend(ctypes.byref(d), _dt(q), _ptr(q), _ptr(kv), _ptr(idx),
                                   _ptr(kv_raw), raw_base, n_raw, _ptr(q_pos), softmax_scale,
-                                  _ptr(out), _ptr(lse), _ptr(ws),
+                                  _ptr(sink), _ptr(out), _ptr(lse), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(q)),
            "sparse_mla_attend")
     return out, lse
@@ -228,7 +248,7 @@ class Forward:
     def __init__(self, q_I, w, k_I: KeyT, q, kv, q_pos, top_k: int, D_V: int,
                  softmax_scale: float, m: int = 1, W: int = 0, kv_raw=None, raw_base: int = 0,
                  compress: bool = False, out=None, lse=None, scores=None, idx=None,
-                 want_lse: bool = True):
+                 want_lse: bool = True, seq_len=None, sink=None):
         qt, qs, qdt = _queries(q_I)
         B, T, H_I, D_I = qt.shape
         _, _, H, D_K = q.shape
@@ -241,12 +261,13 @@ class Forward:
             torch.empty((B, T, H), dtype=torch.float32, device=dev) if want_lse else None)
         self.scores, self.idx = scores, idx
         self.ws = _workspace(self.d, OP_FORWARD, dev)
-        self._keep = (qt, qs, w, kt, ks, q, kv, q_pos, kv_raw)
+        self._keep = (qt, qs, w, kt, ks, q, kv, q_pos, kv_raw, seq_len, sink)
         n_raw = 0 if kv_raw is None else kv_raw.shape[1]
         self.args = ForwardArgs(_dt(q), kdt, _ptr(qt), _ptr(w), _ptr(kt), _ptr(ks), _ptr(q),
                                 _ptr(kv), _ptr(kv_raw), raw_base, n_raw, 1 if compress else 0,
                                 _ptr(q_pos), softmax_scale, _ptr(self.out), _ptr(self.lse),
-                                _ptr(scores), _ptr(idx), None, 0, _ptr(qs))
+                                _ptr(scores), _ptr(idx), None, 0, _ptr(qs), _ptr(seq_len),
+                                _ptr(sink))
         self.device = dev
 
     def set_events(self, events) -> None:
@@ -300,7 +321,7 @@ class HcaForward(Forward):
 
     def __init__(self, q, kv, q_pos, D_V: int, softmax_scale: float, m: int, W: int = 0,
                  kv_raw=None, raw_base: int = 0, compress: bool = False, out=None, lse=None,
-                 want_lse: bool = True):
+                 want_lse: bool = True, seq_len=None, sink=None):
         B, T, H, D_K = q.shape
         N = kv.shape[1]
         self.d = dims(B=B, T=T, N=N, H=H, D_K=D_K, D_V=D_V, m=m, W=W)
@@ -310,12 +331,12 @@ class HcaForward(Forward):
             torch.empty((B, T, H), dtype=torch.float32, device=dev) if want_lse else None)
         self.scores = self.idx = None
         self.ws = _workspace(self.d, OP_HCA, dev)
-        self._keep = (q, kv, q_pos, kv_raw)
+        self._keep = (q, kv, q_pos, kv_raw, seq_len, sink)
         n_raw = 0 if kv_raw is None else kv_raw.shape[1]
         self.args = ForwardArgs(_dt(q), _dt(q), None, None, None, None, _ptr(q), _ptr(kv),
                                 _ptr(kv_raw), raw_base, n_raw, 1 if compress else 0,
                                 _ptr(q_pos), softmax_scale, _ptr(self.out), _ptr(self.lse),
-                                None, None, None, 0, None)
+                                None, None, None, 0, None, _ptr(seq_len), _ptr(sink))
         self.device = dev
 
     def run(self, stream: Optional[int] = None) -> torch.Tensor:

@@ -27,6 +27,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }  // NULL passes
 
 dsa_status check_dims(const dsa_dims* d) {
   if (!d) return DSA_ERR_NULL;
@@ -181,6 +182,7 @@ dsa_status check_forward(const dsa_dims* d, const dsa_forward_args* a) {
                           a->idx};
   for (const void* p : ptrs16)
     if (p && !aligned16(p)) return DSA_ERR_ALIGN;
+  if (!aligned4(a->seq_len) || !aligned4(a->sink)) return DSA_ERR_ALIGN;
   if (a->n_events < 0) return DSA_ERR_SHAPE;
   return DSA_OK;
 }
@@ -209,22 +211,24 @@ dsa_status run_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, h
     float* sc = keep_scores ? a->scores + (size_t)q0 * d->N : ws_scores;
     int32_t* ix = a->idx ? a->idx + (size_t)q0 * d->top_k : ws_idx;
     if (hipError_t e = launch_indexer(s, q0, nr, a->q_I, (int)qi_dt, a->q_scale, a->w, a->k_I,
-                                      a->k_scale, (int)a->k_dt, a->q_pos, sc, keep_scores, st))
+                                      a->k_scale, (int)a->k_dt, a->q_pos, a->seq_len, sc,
+                                      keep_scores, st))
       return launched(e);
     if (attend_fused_ok(s, fmt, nr)) {
       // top-k inside the attention kernel: idx is written only when the caller wants it
       if (hipError_t e = launch_attend_fused(s, q0, nr, a->q, a->kv, sc,
                                              a->idx ? a->idx + (size_t)q0 * d->top_k : nullptr,
                                              d->W > 0 ? a->kv_raw : nullptr, a->raw_base,
-                                             a->n_raw, a->q_pos, a->softmax_scale, a->out, a->lse,
-                                             ws_att, st))
+                                             a->n_raw, a->q_pos, a->seq_len, a->sink,
+                                             a->softmax_scale, a->out, a->lse, ws_att, st))
         return launched(e);
     } else {
-      if (hipError_t e = launch_topk(s, q0, nr, sc, a->q_pos, ix, ws_topk, st))
+      if (hipError_t e = launch_topk(s, q0, nr, sc, a->q_pos, a->seq_len, ix, ws_topk, st))
         return launched(e);
       if (hipError_t e = launch_attend(s, q0, nr, fmt, a->q, a->kv, ix,
                                        d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw,
-                                       a->q_pos, a->softmax_scale, a->out, a->lse, ws_att, st))
+                                       a->q_pos, nullptr, a->sink, a->softmax_scale, a->out,
+                                       a->lse, ws_att, st))
         return launched(e);
     }
   }
@@ -251,7 +255,7 @@ const char* dsa_status_str(int status) {
   }
 }
 
-int dsa_version(void) { return 101; }
+int dsa_version(void) { return 200; }
 
 size_t dsa_workspace_bytes(const dsa_dims* d, int op) {
   if (op == DSA_OP_HCA) {
@@ -286,45 +290,66 @@ dsa_status kv_compress_mean(const dsa_dims* d, dsa_dtype dt, const void* kv_raw,
                                   kv_raw, kv_c, (hipStream_t)stream));
 }
 
+dsa_status kv_compress_blocks(const dsa_dims* d, dsa_dtype dt, const void* kv_raw,
+                              int64_t raw_stride, void* kv_c, int64_t c_stride, int64_t j0,
+                              int64_t j1, void* stream) {
+  if (!d) return DSA_ERR_NULL;
+  if (d->B < 1 || d->D_K < 8 || d->D_K % 8 || d->D_K > DSA_MAX_DK || d->m < 1 || j0 < 0 ||
+      j1 < j0 || raw_stride < 0 || c_stride < 0 || j1 > c_stride || j1 * d->m > raw_stride)
+    return DSA_ERR_SHAPE;
+  if (!fmt_ok(dt)) return DSA_ERR_DTYPE;
+  if (!kv_raw || !kv_c) return DSA_ERR_NULL;
+  if (!aligned16(kv_raw) || !aligned16(kv_c)) return DSA_ERR_ALIGN;
+  if (dsa_status st = check_device()) return st;
+  return launched(launch_compress_blocks(d->B, d->D_K, d->m, dt == DSA_BF16 ? FMT_BF16 : FMT_F32,
+                                         kv_raw, raw_stride, kv_c, c_stride, j0, j1,
+                                         (hipStream_t)stream));
+}
+
 dsa_status indexer_scores(const dsa_dims* d, const void* q_I, dsa_dtype q_dt,
                           const uint8_t* q_scale, const float* w, const void* k_I,
                           const uint8_t* k_scale, dsa_dtype k_dt, const int32_t* q_pos,
-                          float* scores, void* stream) {
+                          const int32_t* seq_len, float* scores, void* stream) {
   if (dsa_status st = check_dims(d)) return st;
   if (dsa_status st = check_indexer(d, q_dt, q_scale, k_dt, k_scale)) return st;
   if (!q_I || !w || !k_I || !q_pos || !scores) return DSA_ERR_NULL;
   if (!aligned16(q_I) || !aligned16(w) || !aligned16(k_I) || !aligned16(scores) ||
-      (k_scale && ((uintptr_t)k_scale & 3u)) || (q_scale && ((uintptr_t)q_scale & 3u)))
+      (k_scale && ((uintptr_t)k_scale & 3u)) || (q_scale && ((uintptr_t)q_scale & 3u)) ||
+      !aligned4(seq_len))
     return DSA_ERR_ALIGN;
   if (dsa_status st = check_device()) return st;
   const Shape s = to_shape(d);
   return launched(launch_indexer(s, 0, (int64_t)d->B * d->T, q_I, (int)q_dt, q_scale, w, k_I,
-                                 k_scale, (int)k_dt, q_pos, scores, true, (hipStream_t)stream));
+                                 k_scale, (int)k_dt, q_pos, seq_len, scores, true,
+                                 (hipStream_t)stream));
 }
 
 dsa_status topk_select(const dsa_dims* d, const float* scores, const int32_t* q_pos,
-                       int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+                       const int32_t* seq_len, int32_t* idx, void* ws, size_t ws_bytes,
+                       void* stream) {
   if (dsa_status st = check_dims(d)) return st;
   if (!scores || !q_pos || !idx) return DSA_ERR_NULL;
-  if (!aligned16(scores) || !aligned16(idx)) return DSA_ERR_ALIGN;
+  if (!aligned16(scores) || !aligned16(idx) || !aligned4(seq_len)) return DSA_ERR_ALIGN;
   const size_t need = dsa_workspace_bytes(d, DSA_OP_TOPK);
   if (need && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
   if (dsa_status st = check_device()) return st;
-  return launched(launch_topk(to_shape(d), 0, (int64_t)d->B * d->T, scores, q_pos, idx, ws,
-                              (hipStream_t)stream));
+  return launched(launch_topk(to_shape(d), 0, (int64_t)d->B * d->T, scores, q_pos, seq_len, idx,
+                              ws, (hipStream_t)stream));
 }
 
 dsa_status sparse_mla_attend(const dsa_dims* d, dsa_dtype dt, const void* q, const void* kv,
                              const int32_t* idx, const void* kv_raw, int64_t raw_base,
                              int64_t n_raw, const int32_t* q_pos, float softmax_scale,
-                             void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                             const float* sink, void* out, float* lse, void* ws,
+                             size_t ws_bytes, void* stream) {
   if (dsa_status st = check_dims(d)) return st;
   if (dsa_status st = check_attend_shape(d)) return st;
   if (!fmt_ok(dt)) return DSA_ERR_DTYPE;
   if (!q || !kv || !idx || !q_pos || !out) return DSA_ERR_NULL;
   if (d->W > 0 && !kv_raw) return DSA_ERR_NULL;
   if (raw_base < 0 || n_raw < 0) return DSA_ERR_SHAPE;
-  if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (kv_raw && !aligned16(kv_raw)))
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || (kv_raw && !aligned16(kv_raw)) ||
+      !aligned4(sink))
     return DSA_ERR_ALIGN;
   const Shape s = to_shape(d);
   const int fmt = dt == DSA_BF16 ? FMT_BF16 : FMT_F32;
@@ -333,8 +358,8 @@ dsa_status sparse_mla_attend(const dsa_dims* d, dsa_dtype dt, const void* q, con
   if (ws && !aligned16(ws)) return DSA_ERR_ALIGN;
   if (dsa_status st = check_device()) return st;
   return launched(launch_attend(s, 0, (int64_t)d->B * d->T, fmt, q, kv, idx,
-                                d->W > 0 ? kv_raw : nullptr, raw_base, n_raw, q_pos,
-                                softmax_scale, out, lse, ws, (hipStream_t)stream));
+                                d->W > 0 ? kv_raw : nullptr, raw_base, n_raw, q_pos, nullptr,
+                                sink, softmax_scale, out, lse, ws, (hipStream_t)stream));
 }
 
 dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, size_t ws_bytes,
@@ -379,6 +404,7 @@ dsa_status hca_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
   const void* ptrs16[] = {a->q, a->kv, a->out, a->kv_raw, ws};
   for (const void* p : ptrs16)
     if (p && !aligned16(p)) return DSA_ERR_ALIGN;
+  if (!aligned4(a->seq_len) || !aligned4(a->sink)) return DSA_ERR_ALIGN;
   const int64_t rows = (int64_t)d->B * d->T;
   const size_t need = attend_ws_bytes(s, rows, fmt);
   if (need && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
@@ -392,7 +418,7 @@ dsa_status hca_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
   }
   return launched(launch_attend(s, 0, rows, fmt, a->q, a->kv, nullptr,
                                 d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw, a->q_pos,
-                                a->softmax_scale, a->out, a->lse, ws, st));
+                                a->seq_len, a->sink, a->softmax_scale, a->out, a->lse, ws, st));
 }
 
 }  // extern "C"

@@ -17,6 +17,7 @@
 #include "launch.h"
 #include "select.h"
 
+#include <algorithm>
 #include <mutex>
 
 namespace dsa {
@@ -29,6 +30,19 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 constexpr int kTile = 32;       // entries per tile
 constexpr float kRefSlack = 8.f;  // log2 headroom of the lazily moved softmax reference
+
+// Joins an attention-sink logit s2 (log2 units; -inf = no sink) to a softmax state: m is the
+// reference of the entries' exponentials (log2 units, -inf when there are none) and l their
+// sum relative to it. Returns the reference M = max(m, s2) and the total L relative to M.
+__device__ __forceinline__ void join_sink(float m, float l, float s2, float& M, float& L) {
+  if (s2 == kNegInf) {
+    M = m;
+    L = l;
+    return;
+  }
+  M = fmaxf(m, s2);
+  L = (m == kNegInf ? 0.f : l * __builtin_amdgcn_exp2f(m - M)) + __builtin_amdgcn_exp2f(s2 - M);
+}
 
 // Source row of entry e of query (b, p); returns nullptr for a masked entry. idxrow == nullptr:
 // every visible entry (entry e < top_k is entry e itself when e < lim = n_vis), else entries
@@ -182,14 +196,15 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     int64_t n_raw, const int32_t* __restrict__ q_pos, int T, int N, int H, int top_k, int W,
     float scale_log2, int64_t qi0, int nsplit, int per_split, uint16_t* __restrict__ out,
     float* __restrict__ lse, f16x4_t* __restrict__ part_o, float* __restrict__ part_ml,
-    int nitems, const float* __restrict__ scores, int m, int32_t* __restrict__ idx_out) {
+    int nitems, const float* __restrict__ scores, int m, int32_t* __restrict__ idx_out,
+    const int32_t* __restrict__ seq_len, const float* __restrict__ sink) {
   constexpr int DK = 576, DV = 512, KS = DK / 32, DB = DV / 16;
   __shared__ __attribute__((aligned(16))) char smem[NS * kStage];
   __shared__ __attribute__((aligned(16))) u32x4_t pbuf[2][4][64];  // P, per head block
   // rescale factor per head when the reference moved, and whether it moved (per head block)
   __shared__ __attribute__((aligned(16))) float abuf[2][4][16];
   __shared__ __attribute__((aligned(16))) uint32_t fbuf[2][4];
-  __shared__ float sml[4][2][16];    // final (m, l) per head
+  __shared__ float sml[4][2][16];    // per head: [1] = the output multiplier (unsplit calls)
   extern __shared__ __attribute__((aligned(16))) int scode[];  // entry codes, whole tiles
 
   // all kernel arguments in one scalar round trip (the compiler otherwise loads them lazily,
@@ -248,7 +263,7 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
                                  : e_begin + tid + j * kAtWaves * 64;
     load_q();
     const int p = q_pos[qi];
-    const int lim = idxrow != nullptr ? N : n_visible(p, m, N);
+    const int lim = idxrow != nullptr ? N : n_visible(p, m, N, seq_len, b);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       asm volatile("" : "+v"(raw[j]));  // keep the reads above, not sunk into the branches below
@@ -273,7 +288,7 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     uint32_t key[PER];
     load_keys<PER>(srow, N, N, key);
     asm volatile("" : "+v"(p));
-    const int nvis = n_visible(p, m, N);
+    const int nvis = n_visible(p, m, N, seq_len, b);
     const int nv = nvis > top_k ? max(0, min(PER, nvis - PER * tid)) : 0;
     load_q();
     int32_t* __restrict__ orow =
@@ -309,6 +324,15 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
         }
       }
     }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  // per tile: whether any of its entries is masked (the softmax skips the masking otherwise)
+  int* sflag = scode + per_split;
+  for (int t = wv; t < ntiles; t += kAtWaves) {
+    const int c = scode[kTile * t + (lane & 31)];
+    const uint64_t bad = __ballot(c == -1);
+    if (lane == 0) sflag[t] = bad != 0 ? 1 : 0;
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -416,6 +440,7 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qf[kk]));
     float m_run = kNegInf;  // per head n (same in the four lane groups)
     float l_run = 0.f;      // this lane's share: entries 4g.., 16+4g.. of every tile
+    bool live = false;      // wave-uniform: m_run is finite for every head
     for (int i = 0; i <= ntiles; ++i) {
       ring_top(i);
       if (i == ntiles) {
@@ -436,9 +461,9 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
         return *reinterpret_cast<const u32x4_t*>(ap);
       };
       // S^T for entries 0..15 (sa) and 16..31 (sc), each over 4 accumulators (k-step % 4)
-      f32x4_t sa[4], sc[4];
+      f32x4_t sa[2], sc[2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sa[c] = sc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < 2; ++c) sa[c] = sc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       {
         constexpr int KB = 3;  // k-steps per block of reads, one block ahead of the MFMAs
         u32x4_t a0[KS], a1[KS];
@@ -459,23 +484,33 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
           }
 #pragma unroll
           for (int kk = KB * blk; kk < KB * blk + KB; ++kk) {
-            sa[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0[kk]), as_bf16x8(qf[kk]), sa[kk & 3], 0, 0, 0);
-            sc[kk & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1[kk]), as_bf16x8(qf[kk]), sc[kk & 3], 0, 0, 0);
+            sa[kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0[kk]), as_bf16x8(qf[kk]), sa[kk & 1], 0, 0, 0);
+            sc[kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1[kk]), as_bf16x8(qf[kk]), sc[kk & 1], 0, 0, 0);
           }
         }
       }
       mid_barrier();
-      const f32x4_t st0 = (sa[0] + sa[1]) + (sa[2] + sa[3]);
-      const f32x4_t st1 = (sc[0] + sc[1]) + (sc[2] + sc[3]);
-      // lane (head n, g): entries 4g+j (z[j]) and 16+4g+j (z[4+j])
+      const f32x4_t st0 = sa[0] + sa[1];
+      const f32x4_t st1 = sc[0] + sc[1];
+      // lane (head n, g): entries 4g+j (z[j]) and 16+4g+j (z[4+j]); masked entries only in
+      // tiles whose flag says so (most tiles have none)
       float z[8];
       float mx = kNegInf;
+      if (__builtin_amdgcn_readfirstlane(sflag[i]) != 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        z[j] = cd0[j] != -1 ? st0[j] * scale_log2 : kNegInf;
-        z[4 + j] = cd1[j] != -1 ? st1[j] * scale_log2 : kNegInf;
-        mx = fmaxf(mx, fmaxf(z[j], z[4 + j]));
+        for (int j = 0; j < 4; ++j) {
+          z[j] = cd0[j] != -1 ? st0[j] * scale_log2 : kNegInf;
+          z[4 + j] = cd1[j] != -1 ? st1[j] * scale_log2 : kNegInf;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          z[j] = st0[j] * scale_log2;
+          z[4 + j] = st1[j] * scale_log2;
+        }
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaxf(z[j], z[4 + j]));
       mx = group_max(mx);
       // Lazily moved softmax reference: m_run only moves (and the value waves rescale their
       // accumulators) when a head's tile maximum exceeds it by more than kRefSlack (log2
@@ -488,14 +523,19 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
         l_run *= alpha;
         m_run = m_new;
         if (g == 0) abuf[i & 1][hb][n] = alpha;
+        live = __ballot(m_run == kNegInf) == 0;
       }
       if (lane == 0) fbuf[i & 1][hb] = moved ? 1u : 0u;
       uint32_t pk[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // m_run == -inf only while every entry so far is masked (z == -inf as well)
-        const float e0 = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(z[2 * j] - m_run);
-        const float e1 = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(z[2 * j + 1] - m_run);
+        float e0 = __builtin_amdgcn_exp2f(z[2 * j] - m_run);
+        float e1 = __builtin_amdgcn_exp2f(z[2 * j + 1] - m_run);
+        if (!live) {
+          // m_run == -inf only while every entry so far is masked (z == -inf as well)
+          e0 = m_run == kNegInf ? 0.f : e0;
+          e1 = m_run == kNegInf ? 0.f : e1;
+        }
         l_run += e0 + e1;
         pk[j] = pack_bf16x2(e0, e1);
       }
@@ -504,10 +544,13 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     // final (m, l) per head for the value waves, and lse / the split's (m, l)
     const float l_head = group_sum(l_run);
     if (g == 0) {
-      sml[hb][0][n] = m_run;
-      sml[hb][1][n] = l_head;
       if (nsplit == 1) {
-        if (lse) lse[(size_t)qi * H + h0 + n] = l_head > 0.f ? (m_run + __log2f(l_head)) * kLn2 : kNegInf;
+        // the sink logit joins the denominator (zero value vector); the value waves scale
+        // their accumulators (relative to m_run) by 2^(m_run - M) / L
+        float M, L;
+        join_sink(m_run, l_head, sink != nullptr ? sink[h0 + n] * kLog2e : kNegInf, M, L);
+        sml[hb][1][n] = (L > 0.f && m_run != kNegInf) ? __builtin_amdgcn_exp2f(m_run - M) / L : 0.f;
+        if (lse) lse[(size_t)qi * H + h0 + n] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
       } else {
         const size_t hrow = ((size_t)row * H + h0 + n) * nsplit + split;
         part_ml[hrow * 4] = m_run;
@@ -579,10 +622,7 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     for (int k = 0; k < 2; ++k) {
       float inv[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float l = sml[hb0 + k][1][4 * g + j];
-        inv[j] = l > 0.f ? 1.f / l : 0.f;
-      }
+      for (int j = 0; j < 4; ++j) inv[j] = sml[hb0 + k][1][4 * g + j];
 #pragma unroll
       for (int d = 0; d < DH; ++d)
 #pragma unroll
@@ -639,7 +679,8 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
 constexpr int kMaxSplits = 32;
 __global__ __launch_bounds__(256) void attend_combine(
     const f16x4_t* __restrict__ part_o, const float* __restrict__ part_ml, int64_t qi0, int H,
-    int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse, int nitems) {
+    int nsplit, uint16_t* __restrict__ out, float* __restrict__ lse, int nitems,
+    const float* __restrict__ sink) {
   constexpr int DV = 512;
   __shared__ float wsc[kMaxSplits][16];
   __shared__ __attribute__((aligned(16))) uint16_t sout[16][128 + 8];
@@ -686,10 +727,14 @@ __global__ __launch_bounds__(256) void attend_combine(
   }
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) L += __shfl_xor(L, o, 64);
+  // the sink logit joins the denominator (zero value vector): reference M2, total L2
+  float M2, L2;
+  join_sink(M, L, sink != nullptr ? sink[h0 + hh] * kLog2e : kNegInf, M2, L2);
+  const float shift = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - M2);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) wsc[sl + 16 * j][hh] = L > 0.f ? wm[j] / L * ml_c[j] : 0.f;
+  for (int j = 0; j < 2; ++j) wsc[sl + 16 * j][hh] = L2 > 0.f ? wm[j] * shift / L2 * ml_c[j] : 0.f;
   if (sl == 0 && cq == 0 && lse)
-    lse[(size_t)qi * H + h0 + hh] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
+    lse[(size_t)qi * H + h0 + hh] = L2 > 0.f ? (M2 + __log2f(L2)) * kLn2 : kNegInf;
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -727,7 +772,8 @@ __global__ __launch_bounds__(256) void attend_generic(
     const T* __restrict__ q, const T* __restrict__ kv, const int32_t* __restrict__ idx,
     const T* __restrict__ kv_raw, int64_t raw_base, int64_t n_raw,
     const int32_t* __restrict__ q_pos, int T_, int N, int H, int DK, int DV, int top_k, int W,
-    float scale, int64_t qi0, T* __restrict__ out, float* __restrict__ lse, int m) {
+    float scale, int64_t qi0, T* __restrict__ out, float* __restrict__ lse, int m,
+    const int32_t* __restrict__ seq_len, const float* __restrict__ sink) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int E = top_k + W;
   float* sq = reinterpret_cast<float*>(smem);   // [DK]
@@ -740,7 +786,7 @@ __global__ __launch_bounds__(256) void attend_generic(
   const int b = (int)(qi / T_);
   const int p = q_pos[qi];
   const int32_t* idxrow = idx != nullptr ? idx + row * (int64_t)top_k : nullptr;
-  const int lim = idx != nullptr ? N : n_visible(p, m, N);
+  const int lim = idx != nullptr ? N : n_visible(p, m, N, seq_len, b);
   for (int d = threadIdx.x; d < DK; d += blockDim.x) sq[d] = ldv(q, ((size_t)qi * H + h) * DK + d);
   __syncthreads();
   float mx = kNegInf;
@@ -760,7 +806,9 @@ __global__ __launch_bounds__(256) void attend_generic(
   mx = wave_max(mx);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
   __syncthreads();
-  mx = kNegInf;
+  // the sink logit (zero value vector) joins the softmax
+  const float sk = sink != nullptr ? sink[h] : kNegInf;
+  mx = sk;
   for (int i = 0; i < (int)(blockDim.x >> 6); ++i) mx = fmaxf(mx, red[i]);
   __syncthreads();
   float sum = 0.f;
@@ -772,7 +820,7 @@ __global__ __launch_bounds__(256) void attend_generic(
   sum = wave_sum(sum);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sum;
   __syncthreads();
-  sum = 0.f;
+  sum = sk != kNegInf ? __expf(sk - mx) : 0.f;
   for (int i = 0; i < (int)(blockDim.x >> 6); ++i) sum += red[i];
   const float inv = sum > 0.f ? 1.f / sum : 0.f;
   for (int d = threadIdx.x; d < DV; d += blockDim.x) {
@@ -818,13 +866,54 @@ size_t attend_ws_bytes(const Shape& s, int64_t nrows, int fmt) {
   return (size_t)nrows * s.H * ns * ((size_t)s.D_V * 2 + 4 * sizeof(float));
 }
 
+// Dynamic LDS the attention kernels may take beside their static LDS (the ring and its
+// buffers), set as each kernel's attribute on every device it runs on, once per device.
+struct AttendLds {
+  hipError_t err;
+  size_t dyn4, dyn3;
+};
+
+static const AttendLds& attend_lds() {
+  constexpr size_t kLdsMax = 160 * 1024;
+  static AttendLds per_dev[64];
+  static std::once_flag once[64];
+  static const AttendLds bad{hipErrorInvalidDevice, 0, 0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return bad;
+  std::call_once(once[dev], [dev] {
+    AttendLds& r = per_dev[dev];
+    r.err = hipSuccess;
+    const void* k4[] = {reinterpret_cast<const void*>(&attend_mfma_dma<4, 0>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 16>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 64>)};
+    const void* k3[] = {reinterpret_cast<const void*>(&attend_mfma_dma<3, 0>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 16>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 64>)};
+    auto room = [&](const void* const* ks, size_t& dyn) {
+      dyn = kLdsMax;
+      for (int j = 0; j < 3 && r.err == hipSuccess; ++j) {
+        hipFuncAttributes fa;
+        r.err = hipFuncGetAttributes(&fa, ks[j]);
+        if (r.err == hipSuccess)
+          dyn = fa.sharedSizeBytes < kLdsMax ? std::min(dyn, kLdsMax - fa.sharedSizeBytes) : 0;
+      }
+      for (int j = 0; j < 3 && r.err == hipSuccess; ++j)
+        r.err = hipFuncSetAttribute(ks[j], hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    };
+    room(k4, r.dyn4);
+    room(k3, r.dyn3);
+  });
+  return per_dev[dev];
+}
+
 // The MFMA attention for rows qi0 .. qi0+nrows-1 (+ the split merge). scores != nullptr selects
 // the fused top-k variant (entries straight from the indexer scores, idx_out optional).
 static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows, const void* q,
                                      const void* kv, const int32_t* idx, const float* scores,
                                      int32_t* idx_out, const void* kv_raw, int64_t raw_base,
-                                     int64_t n_raw, const int32_t* q_pos, float scale, void* out,
-                                     float* lse, void* ws, hipStream_t st) {
+                                     int64_t n_raw, const int32_t* q_pos,
+                                     const int32_t* seq_len, const float* sink, float scale,
+                                     void* out, float* lse, void* ws, hipStream_t st) {
   const int ns = attend_splits(s, nrows, FMT_BF16);
   const int E = s.top_k + s.W;
   const int per = ((E + ns - 1) / ns + kTile - 1) / kTile * kTile;
@@ -833,32 +922,11 @@ static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows,
                                                      (size_t)nrows * s.H * ns * s.D_V * 2)
                           : nullptr;
   dim3 grid(ns, s.H / 64, (unsigned)nrows);
-  const size_t code_bytes = sizeof(int) * (size_t)per;  // per is a multiple of the tile
-  // the entry-code table is dynamic LDS beside the static ring: a 4-stage ring when it fits
-  // in the 160 KB a workgroup can hold, else 3 stages
-  constexpr size_t kLdsMax = 160 * 1024;
-  constexpr size_t kFixed = sizeof(u32x4_t) * 2 * 4 * 64 + sizeof(float) * 2 * 4 * 16 +
-                            sizeof(uint32_t) * 2 * 4 + sizeof(float) * 4 * 2 * 16;
-  constexpr size_t kStatic4 = 4 * kStage + kFixed, kStatic3 = 3 * kStage + kFixed;
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [] {
-    const void* k4[] = {reinterpret_cast<const void*>(&attend_mfma_dma<4, 0>),
-                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 16>),
-                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 64>)};
-    const void* k3[] = {reinterpret_cast<const void*>(&attend_mfma_dma<3, 0>),
-                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 16>),
-                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 64>)};
-    for (const void* f : k4)
-      if (attr == hipSuccess)
-        attr = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)(kLdsMax - kStatic4));
-    for (const void* f : k3)
-      if (attr == hipSuccess)
-        attr = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   (int)(kLdsMax - kStatic3));
-  });
-  if (attr != hipSuccess) return attr;
+  // dynamic LDS: the entry codes (per is a multiple of the tile) and one flag per tile, beside
+  // the static ring: a 4-stage ring when they fit in the 160 KB a workgroup can hold, else 3
+  const size_t code_bytes = sizeof(int) * ((size_t)per + per / kTile);
+  const AttendLds& lds = attend_lds();
+  if (lds.err != hipSuccess) return lds.err;
   const int nitems = (int)(ns * (s.H / 64) * nrows);
   const int per_thread = scores == nullptr ? 0 : (s.N <= 16 * kAtWaves * 64 ? 16 : 64);
   if (scores != nullptr && s.N > 64 * kAtWaves * 64) return hipErrorInvalidValue;
@@ -868,12 +936,12 @@ static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows,
              static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,             \
              static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H,        \
              s.top_k, s.W, scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse,       \
-             part_o, part_ml, nitems, scores, s.m, idx_out)
-  if (code_bytes <= kLdsMax - kStatic4) {
+             part_o, part_ml, nitems, scores, s.m, idx_out, seq_len, sink)
+  if (code_bytes <= lds.dyn4) {
     if (per_thread == 0) DSA_ATT(4, 0);
     else if (per_thread == 16) DSA_ATT(4, 16);
     else DSA_ATT(4, 64);
-  } else if (code_bytes <= kLdsMax - kStatic3) {
+  } else if (code_bytes <= lds.dyn3) {
     if (per_thread == 0) DSA_ATT(3, 0);
     else if (per_thread == 16) DSA_ATT(3, 16);
     else DSA_ATT(3, 64);
@@ -883,7 +951,8 @@ static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows,
 #undef DSA_ATT
   if (e != hipSuccess || ns == 1) return e;
   return launch(attend_combine, dim3(16, s.H / 64, (unsigned)nrows), 256, 0, st, part_o, part_ml,
-                qi0, s.H, ns, static_cast<uint16_t*>(out), lse, (int)(16 * (s.H / 64) * nrows));
+                qi0, s.H, ns, static_cast<uint16_t*>(out), lse, (int)(16 * (s.H / 64) * nrows),
+                sink);
 }
 
 // Each of a row's workgroups (splits x head groups) repeats the row's selection in its
@@ -898,22 +967,23 @@ bool attend_fused_ok(const Shape& s, int fmt, int64_t nrows) {
 hipError_t launch_attend_fused(const Shape& s, int64_t qi0, int64_t nrows, const void* q,
                                const void* kv, const float* scores, int32_t* idx_out,
                                const void* kv_raw, int64_t raw_base, int64_t n_raw,
-                               const int32_t* q_pos, float scale, void* out, float* lse, void* ws,
-                               hipStream_t st) {
+                               const int32_t* q_pos, const int32_t* seq_len, const float* sink,
+                               float scale, void* out, float* lse, void* ws, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   if (!attend_fused_ok(s, FMT_BF16, nrows)) return hipErrorInvalidValue;
   return launch_attend_mfma(s, qi0, nrows, q, kv, nullptr, scores, idx_out, kv_raw, raw_base,
-                            n_raw, q_pos, scale, out, lse, ws, st);
+                            n_raw, q_pos, seq_len, sink, scale, out, lse, ws, st);
 }
 
 hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, const void* q,
                          const void* kv, const int32_t* idx, const void* kv_raw, int64_t raw_base,
-                         int64_t n_raw, const int32_t* q_pos, float scale, void* out, float* lse,
-                         void* ws, hipStream_t st) {
+                         int64_t n_raw, const int32_t* q_pos, const int32_t* seq_len,
+                         const float* sink, float scale, void* out, float* lse, void* ws,
+                         hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   if (mfma_ok(s, fmt))
     return launch_attend_mfma(s, qi0, nrows, q, kv, idx, nullptr, nullptr, kv_raw, raw_base,
-                              n_raw, q_pos, scale, out, lse, ws, st);
+                              n_raw, q_pos, seq_len, sink, scale, out, lse, ws, st);
   const int E = s.top_k + s.W;
   size_t shm = sizeof(float) * (s.D_K + E + 1) + sizeof(void*) * E + 16;
   dim3 grid(s.H, (unsigned)nrows);
@@ -921,11 +991,11 @@ hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, co
     return launch(attend_generic<uint16_t>, grid, 256, shm, st, static_cast<const uint16_t*>(q),
                   static_cast<const uint16_t*>(kv), idx, static_cast<const uint16_t*>(kv_raw),
                   raw_base, n_raw, q_pos, s.T, s.N, s.H, s.D_K, s.D_V, s.top_k, s.W, scale, qi0,
-                  static_cast<uint16_t*>(out), lse, s.m);
+                  static_cast<uint16_t*>(out), lse, s.m, seq_len, sink);
   return launch(attend_generic<float>, grid, 256, shm, st, static_cast<const float*>(q),
                 static_cast<const float*>(kv), idx, static_cast<const float*>(kv_raw), raw_base,
                 n_raw, q_pos, s.T, s.N, s.H, s.D_K, s.D_V, s.top_k, s.W, scale, qi0,
-                static_cast<float*>(out), lse, s.m);
+                static_cast<float*>(out), lse, s.m, seq_len, sink);
 }
 
 }  // namespace dsa

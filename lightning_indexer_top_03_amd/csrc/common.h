@@ -39,6 +39,14 @@ __device__ __forceinline__ int n_visible(int p, int m, int N) {
   return v < N ? v : N;
 }
 
+// The same in a ragged batch: sequence b holds seq_len[b] entries (seq_len may be null).
+__device__ __forceinline__ int n_visible(int p, int m, int N, const int32_t* seq_len, int b) {
+  const int v = n_visible(p, m, N);
+  if (seq_len == nullptr) return v;
+  const int L = seq_len[b];
+  return v < L ? v : (L > 0 ? L : 0);
+}
+
 // Order-preserving map fp32 -> uint32 (larger float <=> larger key); -0 ranks as +0.
 // Workgroup id -> work item, XCD-major: workgroups are dealt to the 8 XCDs round-robin
 // (id % 8), so with T % 8 == 0 XCD x runs items x*T/8 .. (x+1)*T/8 - 1 in order and work items

@@ -56,15 +56,15 @@ __device__ __forceinline__ float relu_bits(float x) {
 template <int ITERS>
 __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_dma(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
-    const int32_t* __restrict__ q_pos, int T, int N, int m, int64_t qi0,
-    float* __restrict__ scores, int fill_masked) {
+    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ seq_len, int T, int N, int m,
+    int64_t qi0, float* __restrict__ scores, int fill_masked) {
   __shared__ __attribute__((aligned(16))) char sq[64 * 256];
   __shared__ __attribute__((aligned(16))) char sk[kDecWaves][2][32 * 256];
   __shared__ float sres[kDecWaves][32 * ITERS];
   const int64_t row = blockIdx.y;
   const int64_t qi = qi0 + row;
   const int b = (int)(qi / T);
-  const int nv = n_visible(q_pos[qi], m, N);
+  const int nv = n_visible(q_pos[qi], m, N, seq_len, b);
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h = lane >> 5;
@@ -230,8 +230,8 @@ template <int KFMT, bool QMX, int ITERS>
 __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_mx_dma(
     const void* __restrict__ qI, const uint8_t* __restrict__ qsc, const float* __restrict__ w,
     const uint8_t* __restrict__ kI, const uint8_t* __restrict__ ksc,
-    const int32_t* __restrict__ q_pos, int T, int N, int m, int64_t qi0,
-    float* __restrict__ scores, int fill_masked) {
+    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ seq_len, int T, int N, int m,
+    int64_t qi0, float* __restrict__ scores, int fill_masked) {
   using K = MxKeys<KFMT>;
   constexpr int TK = K::kTile;
   constexpr int NP = QMX ? 1 : 2;  // q parts: the MXFP8 q_I itself, or hi + lo
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_mx_dma(
   const int64_t row = blockIdx.y;
   const int64_t qi = qi0 + row;
   const int b = (int)(qi / T);
-  const int nv = n_visible(q_pos[qi], m, N);
+  const int nv = n_visible(q_pos[qi], m, N, seq_len, b);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
@@ -518,8 +518,8 @@ constexpr int kPfKeyGroups = 16;  // workgroups per query block
 
 __global__ __launch_bounds__(256) void indexer_prefill_mfma(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
-    const int32_t* __restrict__ q_pos, int T, int N, int m, int b, int t0, int nt,
-    float* __restrict__ scores, int fill_masked) {
+    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ seq_len, int T, int N, int m,
+    int b, int t0, int nt, float* __restrict__ scores, int fill_masked) {
   __shared__ __attribute__((aligned(16))) char sq[3][64 * 256];
   __shared__ __attribute__((aligned(16))) float sw[3][64];
   __shared__ int snv[kPfQ];
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_mfma(
   if (tid == 0) smax = 0;
   __syncthreads();
   if (tid < nrows) {
-    int v = n_visible(q_pos[qi0 + tid], m, N);
+    int v = n_visible(q_pos[qi0 + tid], m, N, seq_len, b);
     snv[tid] = v;
     atomicMax(&smax, v);
   }
@@ -666,8 +666,8 @@ template <int KFMT>
 __global__ __launch_bounds__(256) void indexer_prefill_mx(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qsc, const float* __restrict__ w,
     const uint8_t* __restrict__ kI, const uint8_t* __restrict__ ksc,
-    const int32_t* __restrict__ q_pos, int T, int N, int m, int b, int t0, int nt,
-    float* __restrict__ scores, int fill_masked) {
+    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ seq_len, int T, int N, int m,
+    int b, int t0, int nt, float* __restrict__ scores, int fill_masked) {
   using K = MxKeys<KFMT>;
   __shared__ __attribute__((aligned(16))) char sq[3][kPfMxStage];
   __shared__ int snv[kPfQ];
@@ -685,7 +685,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_mx(
   if (tid == 0) smax = 0;
   __syncthreads();
   if (tid < nrows) {
-    int v = n_visible(q_pos[qi0 + tid], m, N);
+    int v = n_visible(q_pos[qi0 + tid], m, N, seq_len, b);
     snv[tid] = v;
     atomicMax(&smax, v);
   }
@@ -853,13 +853,13 @@ __global__ __launch_bounds__(256) void indexer_generic(
     const void* __restrict__ qI, int q_fmt, const uint8_t* __restrict__ qsc,
     const float* __restrict__ w, const void* __restrict__ kI, const uint8_t* __restrict__ ksc,
     int k_fmt,
-    const int32_t* __restrict__ q_pos, int T, int N, int m, int H_I, int D_I, int64_t qi0,
-    float* __restrict__ scores, int fill_masked) {
+    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ seq_len, int T, int N, int m,
+    int H_I, int D_I, int64_t qi0, float* __restrict__ scores, int fill_masked) {
   extern __shared__ float sm[];  // [H_I*D_I] q, [H_I] w
   const int64_t row = blockIdx.y;
   const int64_t qi = qi0 + row;
   const int b = (int)(qi / T);
-  const int nv = n_visible(q_pos[qi], m, N);
+  const int nv = n_visible(q_pos[qi], m, N, seq_len, b);
   float* sqf = sm;
   float* swf = sm + H_I * D_I;
   for (int i = threadIdx.x; i < H_I * D_I; i += blockDim.x) {
@@ -920,8 +920,9 @@ __global__ __launch_bounds__(256) void indexer_generic(
 
 hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void* q_I, int q_fmt,
                           const uint8_t* q_scale, const float* w, const void* k_I,
-                          const uint8_t* k_scale, int k_fmt, const int32_t* q_pos, float* scores,
-                          bool fill_masked, hipStream_t st) {
+                          const uint8_t* k_scale, int k_fmt, const int32_t* q_pos,
+                          const int32_t* seq_len, float* scores, bool fill_masked,
+                          hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   const bool shape_ok = s.H_I == 64 && s.D_I == 128;
   const bool kmx = k_fmt == FMT_MXFP4 || k_fmt == FMT_MXFP8;
@@ -936,7 +937,7 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
       dim3 grid(std::min((s.N + kPfKeys - 1) / kPfKeys, kPfKeyGroups), (nt + kPfQ - 1) / kPfQ);
       hipError_t e = launch(indexer_prefill_mfma, grid, 256, 0, st,
                             static_cast<const uint16_t*>(q_I), w,
-                            static_cast<const uint16_t*>(k_I), q_pos, s.T, s.N, s.m, b, t0, nt,
+                            static_cast<const uint16_t*>(k_I), q_pos, seq_len, s.T, s.N, s.m, b, t0, nt,
                             scores + (size_t)(q - qi0) * s.N, fm);
       if (e != hipSuccess) return e;
       q = seg_end;
@@ -956,9 +957,9 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
       float* sc = scores + (size_t)(q - qi0) * s.N;
       hipError_t e = k_fmt == FMT_MXFP4
           ? launch(indexer_prefill_mx<FMT_MXFP4>, grid, 256, 0, st, qp, q_scale, w, kp, k_scale,
-                   q_pos, s.T, s.N, s.m, b, t0, nt, sc, fm)
+                   q_pos, seq_len, s.T, s.N, s.m, b, t0, nt, sc, fm)
           : launch(indexer_prefill_mx<FMT_MXFP8>, grid, 256, 0, st, qp, q_scale, w, kp, k_scale,
-                   q_pos, s.T, s.N, s.m, b, t0, nt, sc, fm);
+                   q_pos, seq_len, s.T, s.N, s.m, b, t0, nt, sc, fm);
       if (e != hipSuccess) return e;
       q = seg_end;
     }
@@ -974,8 +975,8 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
     const int kpw = kDecWaves * 32 * it2;
     dim3 g2((s.N + kpw - 1) / kpw, (unsigned)nrows);
 #define DSA_DMA(I)                                                                          \
-  return launch(indexer_decode_dma<I>, g2, kDecWaves * 64, 0, st, qp, w, kp, q_pos, s.T, s.N, \
-                s.m, qi0, scores, fm)
+  return launch(indexer_decode_dma<I>, g2, kDecWaves * 64, 0, st, qp, w, kp, q_pos, seq_len, \
+                s.T, s.N, s.m, qi0, scores, fm)
     switch (it2) {
       case 1: DSA_DMA(1);
       case 2: DSA_DMA(2);
@@ -994,7 +995,7 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
     dim3 g((s.N + kpw - 1) / kpw, (unsigned)nrows);
 #define DSA_MX(KF, QM, I)                                                                     \
   return launch(indexer_decode_mx_dma<KF, QM, I>, g, kDecWaves * 64, 0, st, q_I, q_scale, w, kp, \
-                k_scale, q_pos, s.T, s.N, s.m, qi0, scores, fm)
+                k_scale, q_pos, seq_len, s.T, s.N, s.m, qi0, scores, fm)
 #define DSA_MX_IT(KF, QM)        \
   switch (it) {                  \
     case 1: DSA_MX(KF, QM, 1);   \
@@ -1017,7 +1018,7 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
   dim3 grid((s.N + 255) / 256, (unsigned)nrows);
   size_t shm = sizeof(float) * ((size_t)s.H_I * s.D_I + s.H_I);
   return launch(indexer_generic, grid, 256, shm, st, q_I, q_fmt, q_scale, w, k_I, k_scale, k_fmt,
-                q_pos, s.T, s.N, s.m, s.H_I, s.D_I, qi0, scores, fm);
+                q_pos, seq_len, s.T, s.N, s.m, s.H_I, s.D_I, qi0, scores, fm);
 }
 
 }  // namespace dsa

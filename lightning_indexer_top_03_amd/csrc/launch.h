@@ -57,28 +57,40 @@ struct Shape {
 // ---- step 0 ----
 hipError_t launch_compress(int B, int64_t n_raw, int D, int m, int fmt, const void* kv_raw,
                            void* kv_c, hipStream_t st);
+// Incremental compression: for every sequence b, kv_c[b, j, :] = mean of kv_raw[b, m*j + i, :]
+// (i < m) for the blocks j0 <= j < j1; kv_raw holds raw_stride rows per sequence, kv_c
+// c_stride entries.
+hipError_t launch_compress_blocks(int B, int D, int m, int fmt, const void* kv_raw,
+                                  int64_t raw_stride, void* kv_c, int64_t c_stride, int64_t j0,
+                                  int64_t j1, hipStream_t st);
 
 // ---- step 1 ----
-// scores: [nrows, N] row-relative. fill_masked: write -inf for s >= n_vis.
+// scores: [nrows, N] row-relative. fill_masked: write -inf for s >= n_vis. seq_len (nullable):
+// entries held per sequence (ragged batch), clamping n_vis.
 hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void* q_I, int q_fmt,
                           const uint8_t* q_scale, const float* w, const void* k_I,
-                          const uint8_t* k_scale, int k_fmt, const int32_t* q_pos, float* scores,
-                          bool fill_masked, hipStream_t st);
+                          const uint8_t* k_scale, int k_fmt, const int32_t* q_pos,
+                          const int32_t* seq_len, float* scores, bool fill_masked,
+                          hipStream_t st);
 
 // ---- step 2 ----
 // scores: [nrows, N] row-relative, idx: [nrows, top_k] row-relative, rows qi0 .. qi0+nrows-1.
 size_t topk_ws_bytes(const Shape& s, int64_t nrows);
 hipError_t launch_topk(const Shape& s, int64_t qi0, int64_t nrows, const float* scores,
-                       const int32_t* q_pos, int32_t* idx, void* ws, hipStream_t st);
+                       const int32_t* q_pos, const int32_t* seq_len, int32_t* idx, void* ws,
+                       hipStream_t st);
 
 // ---- step 3 ----
 // idx: [nrows, top_k] row-relative; q/out/lse indexed by the flattened row qi.
 int attend_splits(const Shape& s, int64_t nrows, int fmt);
 size_t attend_ws_bytes(const Shape& s, int64_t nrows, int fmt);
+// seq_len (nullable): entries per sequence (limits the dense idx == nullptr case and the fused
+// selection); sink (nullable): one logit per head joining the softmax with a zero value vector.
 hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, const void* q,
                          const void* kv, const int32_t* idx, const void* kv_raw, int64_t raw_base,
-                         int64_t n_raw, const int32_t* q_pos, float scale, void* out, float* lse,
-                         void* ws, hipStream_t st);
+                         int64_t n_raw, const int32_t* q_pos, const int32_t* seq_len,
+                         const float* sink, float scale, void* out, float* lse, void* ws,
+                         hipStream_t st);
 
 // Fused top-k + attention (dsa_forward): every workgroup of a row selects the row's top-k from
 // the indexer scores itself and attends over its split of it; idx_out (nullable) receives the
@@ -88,7 +100,7 @@ bool attend_fused_ok(const Shape& s, int fmt, int64_t nrows);
 hipError_t launch_attend_fused(const Shape& s, int64_t qi0, int64_t nrows, const void* q,
                                const void* kv, const float* scores, int32_t* idx_out,
                                const void* kv_raw, int64_t raw_base, int64_t n_raw,
-                               const int32_t* q_pos, float scale, void* out, float* lse, void* ws,
-                               hipStream_t st);
+                               const int32_t* q_pos, const int32_t* seq_len, const float* sink,
+                               float scale, void* out, float* lse, void* ws, hipStream_t st);
 
 }  // namespace dsa

@@ -211,8 +211,9 @@ __host__ __device__ inline size_t long_row_bytes(int G) {
 }
 
 __global__ __launch_bounds__(kFiltThreads) void topk_long_filter(
-    const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int64_t qi0, int N,
-    int m, int k, int G, uint8_t* __restrict__ ws) {
+    const float* __restrict__ scores, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ seq_len, int T, int64_t qi0, int N, int m, int k, int G,
+    uint8_t* __restrict__ ws) {
   constexpr int NW = kFiltThreads / 64, PER = kLongChunk / kFiltThreads;
   __shared__ SelShared<NW> sh;
   const int tid = threadIdx.x;
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_long_filter(
   // q_pos is read; entries at or past n_vis are masked below
   uint32_t key[PER];
   load_keys<PER>(scores + row * (int64_t)N + c0, N, min(kLongChunk, N - c0), key);
-  const int n = n_visible(q_pos[qi0 + row], m, N);
+  const int n = n_visible(q_pos[qi0 + row], m, N, seq_len, (int)((qi0 + row) / T));
   if (n <= k) return;  // the select kernel keeps every visible entry
   uint8_t* rws = ws + row * long_row_bytes(G);
   uint32_t* counts = reinterpret_cast<uint32_t*>(rws);
@@ -269,8 +270,9 @@ __global__ __launch_bounds__(kFiltThreads) void topk_long_filter(
 }
 
 __global__ __launch_bounds__(kTkThreads) void topk_long_select(
-    const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int64_t qi0, int N,
-    int m, int k, int G, const uint8_t* __restrict__ ws, int32_t* __restrict__ idx) {
+    const float* __restrict__ scores, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ seq_len, int T, int64_t qi0, int N, int m, int k, int G,
+    const uint8_t* __restrict__ ws, int32_t* __restrict__ idx) {
   constexpr int PER = kLongCap / kTkThreads;
   struct Fast {
     SelShared<kTkWaves> sel;
@@ -308,7 +310,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_long_select(
     pi[u] = sidx[gj * kLongSeg + lane];
     pk[u] = skey[gj * kLongSeg + lane];
   }
-  const int n = n_visible(q_pos[qi0 + row], m, N);
+  const int n = n_visible(q_pos[qi0 + row], m, N, seq_len, (int)((qi0 + row) / T));
   int32_t* __restrict__ out = idx + row * (int64_t)k;
   const float* __restrict__ s = scores + row * (int64_t)N;
   if (n <= k) {
@@ -404,12 +406,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_long_select(
 // ------------------------------------------------------------------------------------------
 template <int PER>
 __global__ __launch_bounds__(kTkThreads) void topk_radix_reg(
-    const float* __restrict__ scores, const int32_t* __restrict__ q_pos, int64_t qi0, int N,
-    int m, int k, int32_t* __restrict__ idx) {
+    const float* __restrict__ scores, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ seq_len, int T, int64_t qi0, int N, int m, int k,
+    int32_t* __restrict__ idx) {
   __shared__ SelShared<kTkWaves> sh;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
-  const int n = n_visible(q_pos[qi0 + row], m, N);
+  const int n = n_visible(q_pos[qi0 + row], m, N, seq_len, (int)((qi0 + row) / T));
   int32_t* __restrict__ out = idx + row * (int64_t)k;
   const float* __restrict__ s = scores + row * (int64_t)N;
   if (n <= k) {
@@ -438,25 +441,26 @@ size_t topk_ws_bytes(const Shape& s, int64_t nrows) {
 }
 
 hipError_t launch_topk(const Shape& s, int64_t qi0, int64_t nrows, const float* scores,
-                       const int32_t* q_pos, int32_t* idx, void* ws, hipStream_t st) {
+                       const int32_t* q_pos, const int32_t* seq_len, int32_t* idx, void* ws,
+                       hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   // rows hold at most N visible entries
   const dim3 grid((unsigned)nrows);
   if (s.N <= 8 * kTkThreads)
-    return launch(topk_radix_reg<8>, grid, kTkThreads, 0, st, scores, q_pos, qi0, s.N, s.m,
+    return launch(topk_radix_reg<8>, grid, kTkThreads, 0, st, scores, q_pos, seq_len, s.T, qi0, s.N, s.m,
                   s.top_k, idx);
   if (s.N <= 16 * kTkThreads)
-    return launch(topk_radix_reg<16>, grid, kTkThreads, 0, st, scores, q_pos, qi0, s.N, s.m,
+    return launch(topk_radix_reg<16>, grid, kTkThreads, 0, st, scores, q_pos, seq_len, s.T, qi0, s.N, s.m,
                   s.top_k, idx);
   if (s.N <= kLdsMaxN)
-    return launch(topk_radix_reg<32>, grid, kTkThreads, 0, st, scores, q_pos, qi0, s.N, s.m,
+    return launch(topk_radix_reg<32>, grid, kTkThreads, 0, st, scores, q_pos, seq_len, s.T, qi0, s.N, s.m,
                   s.top_k, idx);
   const int G = (s.N + kLongChunk - 1) / kLongChunk;
   uint8_t* w = static_cast<uint8_t*>(ws);
   if (hipError_t e = launch(topk_long_filter, dim3((unsigned)G, (unsigned)nrows), kFiltThreads,
-                            0, st, scores, q_pos, qi0, s.N, s.m, s.top_k, G, w))
+                            0, st, scores, q_pos, seq_len, s.T, qi0, s.N, s.m, s.top_k, G, w))
     return e;
-  return launch(topk_long_select, grid, kTkThreads, 0, st, scores, q_pos, qi0, s.N, s.m,
+  return launch(topk_long_select, grid, kTkThreads, 0, st, scores, q_pos, seq_len, s.T, qi0, s.N, s.m,
                 s.top_k, G, static_cast<const uint8_t*>(w), idx);
 }
 

@@ -60,11 +60,13 @@ def lib():
         L.orc_compress_mean.argtypes = [i64, i32, i32, i32, vp, vp]
         L.orc_n_vis.argtypes = [i64, i32, i64]
         L.orc_n_vis.restype = i64
+        L.orc_n_vis_len.argtypes = [i64, i32, i64, i64]
+        L.orc_n_vis_len.restype = i64
         L.orc_scores_row.argtypes = [i32, i32, i64, i64, i32, vp, vp, vp, i32, vp, vp, vp]
         L.orc_topk_row.argtypes = [vp, i64, i32, vp]
         L.orc_topk_row.restype = i32
         L.orc_attend_row.argtypes = [i32, i32, i32, i32, vp, i32, vp, vp, i32, i32, vp, i64,
-                                     i64, i64, i32, dbl, vp, vp]
+                                     i64, i64, i32, dbl, vp, vp, vp]
         L.orc_max_threads.restype = i32
         for f in ("orc_decode", "orc_decode_mxfp4_row", "orc_decode_mxfp8_row",
                   "orc_compress_mean", "orc_scores_row",
@@ -150,8 +152,12 @@ def compress_mean(raw: np.ndarray, m: int) -> np.ndarray:
     return out
 
 
-def n_vis(p: int, m: int, N: int) -> int:
-    return int(lib().orc_n_vis(int(p), int(m), int(N)))
+def n_vis(p: int, m: int, N: int, seq_len: Optional[int] = None) -> int:
+    """Visible entries of a query at position p (and, for a ragged batch, a sequence holding
+    seq_len entries)."""
+    if seq_len is None:
+        return int(lib().orc_n_vis(int(p), int(m), int(N)))
+    return int(lib().orc_n_vis_len(int(p), int(m), int(N), int(seq_len)))
 
 
 def scores_row(q_I: np.ndarray, w: np.ndarray, k_I, n_visible: int,
@@ -199,9 +205,10 @@ def topk_row(scores: np.ndarray, n_visible: int, k: int) -> Tuple[np.ndarray, in
 
 def attend_row(q: np.ndarray, kv: Optional[np.ndarray], idx: np.ndarray, D_V: int, scale: float,
                p: int = 0, W: int = 0, kv_raw: Optional[np.ndarray] = None, raw_base: int = 0,
-               ) -> Tuple[np.ndarray, np.ndarray]:
+               sink: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """One query: q [H, D_K], kv [N, D_K] (f32/bf16/f64), idx [k] (-1 = none), raw window rows
-    kv_raw [n_raw, D_K] at positions raw_base.. -> (out [H, D_V] fp64, lse [H] fp64)."""
+    kv_raw [n_raw, D_K] at positions raw_base.., optional sink logits [H] (fp32 values) ->
+    (out [H, D_V] fp64, lse [H] fp64)."""
     q = np.ascontiguousarray(q)
     H, D_K = q.shape
     idx = np.ascontiguousarray(idx, np.int32)
@@ -219,9 +226,11 @@ def attend_row(q: np.ndarray, kv: Optional[np.ndarray], idx: np.ndarray, D_V: in
         rawdt = _dt_of(kv_raw)
     out = np.empty((H, D_V), np.float64)
     lse = np.empty(H, np.float64)
+    sk = None if sink is None else np.ascontiguousarray(sink, np.float64)
+    assert sk is None or sk.shape == (H,)
     lib().orc_attend_row(H, D_K, D_V, _dt_of(q), _p(q), _dt_of(kv), _p(kv), _p(idx), idx.size,
                          rawdt, _p(kv_raw), int(raw_base), int(n_raw), int(p), int(W),
-                         float(scale), _p(out), _p(lse))
+                         float(scale), _p(sk), _p(out), _p(lse))
     return out, lse
 
 
@@ -265,10 +274,15 @@ class QueryRunner:
             return None
         return raw[b]
 
+    def n_vis(self, b: int, t: int) -> int:
+        c = self.cfg
+        lens = self.wl.seq_len()
+        return n_vis(int(self.wl.q_pos()[b, t]), c.m, c.N,
+                     seq_len=None if lens is None else int(lens[b]))
+
     def scores(self, b: int, t: int) -> np.ndarray:
         c = self.cfg
-        p = int(self.wl.q_pos()[b, t])
-        nv = n_vis(p, c.m, c.N)
+        nv = self.n_vis(b, t)
         w = self.wl.w()[b, t]
         qs = None
         if c.qi_dt == "mxfp8":
@@ -286,13 +300,15 @@ class QueryRunner:
         p = int(self.wl.q_pos()[b, t])
         q = self.wl.q()[b, t] if "q" in self.wl._cache else self.wl.q_rows(b, t)
         base, _ = self.wl.raw_extent()
+        sink = self.wl.sink()
         return attend_row(q, self.kv_b(b), idx, c.D_V, c.softmax_scale, p=p, W=c.W,
-                          kv_raw=self.raw_b(b), raw_base=base)
+                          kv_raw=self.raw_b(b), raw_base=base,
+                          sink=None if sink is None else sink.astype(np.float64))
 
     def run(self, b: int, t: int) -> Dict[str, np.ndarray]:
         c = self.cfg
         p = int(self.wl.q_pos()[b, t])
-        nv = n_vis(p, c.m, c.N)
+        nv = self.n_vis(b, t)
         sc = self.scores(b, t)
         idx, cnt = topk_row(sc, nv, c.top_k)
         out, lse = self.attend(b, t, idx)
@@ -302,7 +318,7 @@ class QueryRunner:
         """HCA: attention over every visible compressed entry (+ the raw window)."""
         c = self.cfg
         p = int(self.wl.q_pos()[b, t])
-        nv = n_vis(p, c.m, c.N)
+        nv = self.n_vis(b, t)
         out, lse = self.attend(b, t, dense_entries(nv, c.N))
         return dict(out=out, lse=lse, n_vis=nv, p=p)
 

@@ -19,6 +19,12 @@
  *               z = scale * q . K_e, out = sum softmax(z)_e * K_e[:D_V], lse = log sum exp z
  *               ([P5] s1.3 step 3, s1.4 MQA mode: one latent row shared by all heads;
  *               [P4] window KV concatenated with the compressed KV)
+ *   sink      : optional per-head logit s_h joining that softmax with a zero value vector:
+ *               out = sum_e exp(z_e) K_e[:D_V] / (sum_e exp(z_e) + exp(s_h)),
+ *               lse = log(sum_e exp(z_e) + exp(s_h))   ([P4] CSA snippet 4.3: sliding window
+ *               plus an attention sink; read as one learned logit per head, unscaled)
+ *   ragged    : optional per-sequence entry count len_b: entries s >= len_b are not visible,
+ *               n_vis = min(N, floor((p + 1) / m), len_b)
  * Sources: [P5] "DeepSeek-V3.2 sparse-attention principle and TPU adaptation" (trdm.cn);
  *          [P1] xhh.club "sparse" tag feed, DeepSeek-V4 CSA summary;
  *          [P4] Tencent Cloud developer search "compressed sparse attention (CSA)".
@@ -114,6 +120,12 @@ int64_t orc_n_vis(int64_t p, int m, int64_t N) {
   return v < N ? v : N;
 }
 
+/* n_vis of a sequence holding len entries (ragged batches): min(n_vis, len), len >= 0 */
+int64_t orc_n_vis_len(int64_t p, int m, int64_t N, int64_t len) {
+  int64_t v = orc_n_vis(p, m, N);
+  return v < len ? v : (len > 0 ? len : 0);
+}
+
 /* ---- step 1: lightning-indexer scores of one query -------------------------------------- */
 
 /* qI [H_I, D_I] (dtype qdt; MXFP8: codes [H_I, D_I] and qscale [H_I, D_I/32]), w [H_I],
@@ -200,7 +212,8 @@ int orc_topk_row(const double* scores, int64_t n_vis, int k, int32_t* idx) {
  * at 0 and to what kv_raw holds) joins the entry set. out [H, D_V], lse [H]. */
 void orc_attend_row(int H, int D_K, int D_V, int qdt, const void* q, int kvdt, const void* kv,
                     const int32_t* idx, int k, int rawdt, const void* kv_raw, int64_t raw_base,
-                    int64_t n_raw, int64_t p, int W, double scale, double* out, double* lse) {
+                    int64_t n_raw, int64_t p, int W, double scale, const double* sink,
+                    double* out, double* lse) {
   /* entry list: (source, row) */
   int cap = k + (W > 0 ? W : 0);
   const void** src = (const void**)malloc(sizeof(void*) * (size_t)(cap > 0 ? cap : 1));
@@ -225,19 +238,20 @@ void orc_attend_row(int H, int D_K, int D_V, int qdt, const void* q, int kvdt, c
     for (int h = 0; h < H; ++h) {
       double* o = out + (int64_t)h * D_V;
       for (int d = 0; d < D_V; ++d) o[d] = 0.0;
+      const double s_h = sink ? sink[h] : -INFINITY; /* sink logit (value vector 0) */
       if (E == 0) {
-        lse[h] = -INFINITY;
+        lse[h] = s_h;
         continue;
       }
       for (int d = 0; d < D_K; ++d) qh[d] = ld(qdt, q, (int64_t)h * D_K + d);
-      double zmax = -INFINITY;
+      double zmax = s_h;
       for (int e = 0; e < E; ++e) {
         double dot = 0.0;
         for (int d = 0; d < D_K; ++d) dot += qh[d] * ld(sdt[e], src[e], row[e] * D_K + d);
         z[e] = scale * dot;
         if (z[e] > zmax) zmax = z[e];
       }
-      double sum = 0.0;
+      double sum = sink ? exp(s_h - zmax) : 0.0;
       for (int e = 0; e < E; ++e) {
         z[e] = exp(z[e] - zmax);
         sum += z[e];

@@ -22,7 +22,7 @@ _SRC = os.path.join(_HERE, "synth.c")
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 
 # Tensor ids of the counter-based streams.
-TID_QI, TID_KI, TID_W, TID_Q, TID_KV, TID_WIN = 1, 2, 3, 4, 5, 6
+TID_QI, TID_KI, TID_W, TID_Q, TID_KV, TID_WIN, TID_SINK = 1, 2, 3, 4, 5, 6, 7
 
 
 def build(force: bool = True) -> str:

@@ -23,6 +23,8 @@ Recipes (all seeded; seed = workload id, "sharp" variants use seed 100 + id):
             queries (positions 122880..131071); W=128
   sharp variants: q, kv ~ N(0,1) and softmax scale 4/sqrt(D_K), so that attention outputs are
             O(1) and a wrong gather moves them by far more than the tolerance.
+  sink = (lo, hi): one attention-sink logit per head, U(lo, hi), fp32, tensor id 7.
+  seq_lens: entries held by each sequence of a ragged batch (visibility is clamped to them).
   w_lo < 0: head weights w ~ U(w_lo, 1) (the weights come from a learned projection, so their
             sign is not fixed): index scores of either sign, and rows whose top-k threshold is
             negative.
@@ -35,8 +37,8 @@ from typing import Dict, Optional
 
 import numpy as np
 
-from . import (TID_KI, TID_KV, TID_Q, TID_QI, TID_W, TID_WIN, normal, normal_mxfp4, normal_mxfp8,
-               uniform)
+from . import (TID_KI, TID_KV, TID_Q, TID_QI, TID_SINK, TID_W, TID_WIN, normal, normal_mxfp4,
+               normal_mxfp8, uniform)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -68,6 +70,8 @@ class Config:
     win_std: float = 0.0      # std of raw window rows (0 -> qkv_std)
     dense: bool = False       # HCA: no indexer / top-k, every visible entry attends
     w_lo: float = 0.0         # head weights w ~ U(w_lo, 1): a negative w_lo gives mixed signs
+    sink: tuple = ()          # (lo, hi): one attention-sink logit per head ~ U(lo, hi) (fp32)
+    seq_lens: tuple = ()      # entries held per sequence (ragged batch); () = N for every one
 
     @property
     def softmax_scale(self) -> float:
@@ -199,6 +203,21 @@ class Workload:
             return self._get("kv_raw", lambda: normal(c.seed, TID_WIN, (c.B, c.n_raw, c.D_K),
                                                       c.raw_std, c.dt))
         return None
+
+    def sink(self) -> Optional[np.ndarray]:
+        """Attention-sink logits [H] fp32, or None."""
+        c = self.cfg
+        if not c.sink:
+            return None
+        return self._get("sink", lambda: uniform(c.seed, TID_SINK, (c.H,), c.sink[0], c.sink[1]))
+
+    def seq_len(self) -> Optional[np.ndarray]:
+        """Entries held per sequence [B] int32 (a ragged batch), or None."""
+        c = self.cfg
+        if not c.seq_lens:
+            return None
+        assert len(c.seq_lens) == c.B
+        return np.array(c.seq_lens, np.int32)
 
     def raw_extent(self):
         """(raw_base, n_raw) of kv_raw."""

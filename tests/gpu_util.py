@@ -83,6 +83,9 @@ class DeviceWorkload:
             self.kv = torch.empty((c.B, c.N, c.D_K), dtype=tdt, device="cuda")
         else:
             self.kv = to_dev(wl.kv())
+        lens, sink = wl.seq_len(), wl.sink()
+        self.seq_len = to_dev(lens) if lens is not None else None
+        self.sink = to_dev(sink) if sink is not None else None
         torch.cuda.synchronize()
         log(f"[{c.name}] inputs on device in {time.time() - t0:.1f}s")
 
@@ -94,7 +97,8 @@ class DeviceWorkload:
         idx = torch.empty((c.B, c.T, c.top_k), dtype=torch.int32, device="cuda") if keep_idx else None
         f = dsa.Forward(self.q_I, self.w, self.k_I, self.q, self.kv, self.q_pos, c.top_k, c.D_V,
                         c.softmax_scale, m=c.m, W=c.W, kv_raw=self.kv_raw,
-                        raw_base=self.raw_base, compress=c.compress, scores=scores, idx=idx)
+                        raw_base=self.raw_base, compress=c.compress, scores=scores, idx=idx,
+                        seq_len=self.seq_len, sink=self.sink)
         return f
 
 
@@ -102,7 +106,8 @@ class DeviceWorkload:
         import lightning_indexer_top_03_amd as dsa
         c = self.cfg
         return dsa.HcaForward(self.q, self.kv, self.q_pos, c.D_V, c.softmax_scale, c.m, W=c.W,
-                              kv_raw=self.kv_raw, raw_base=self.raw_base, compress=c.compress)
+                              kv_raw=self.kv_raw, raw_base=self.raw_base, compress=c.compress,
+                              seq_len=self.seq_len, sink=self.sink)
 
 
 def _decoded_keys(wl, b):

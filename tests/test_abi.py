@@ -37,7 +37,7 @@ def test_status_strings_and_version():
         s = L.dsa_status_str(code).decode()
         assert s.startswith("DSA_"), s
     assert L.dsa_status_str(99).decode() == "unknown dsa_status"
-    assert L.dsa_version() == 101
+    assert L.dsa_version() == 200
 
 
 def _dims(**kw):
@@ -47,14 +47,15 @@ def _dims(**kw):
 
 
 def _idx_call(d, q_dt=dsa.BF16, k_dt=dsa.BF16, q_I=P, w=P, k_I=P, k_scale=None, q_pos=P, sc=P,
-              q_scale=None):
-    return L.indexer_scores(ctypes.byref(d), q_I, q_dt, q_scale, w, k_I, k_scale, k_dt, q_pos, sc,
-                            None)
+              q_scale=None, seq_len=None):
+    return L.indexer_scores(ctypes.byref(d), q_I, q_dt, q_scale, w, k_I, k_scale, k_dt, q_pos,
+                            seq_len, sc, None)
 
 
 def test_indexer_validation():
     d = _dims()
-    assert L.indexer_scores(None, P, 1, None, P, P, None, 1, P, P, None) == 1  # NULL dims
+    assert L.indexer_scores(None, P, 1, None, P, P, None, 1, P, None, P, None) == 1  # NULL dims
+    assert _idx_call(d, seq_len=P + 2) == 4                                    # seq_len align
     assert _idx_call(d, q_I=None) == 1                                         # NULL q_I
     assert _idx_call(d, q_pos=None) == 1
     assert _idx_call(_dims(N=0)) == 2                                          # bad shape
@@ -80,15 +81,17 @@ def test_indexer_validation():
 
 def test_topk_validation():
     d = _dims()
-    assert L.topk_select(ctypes.byref(d), None, P, P, None, 0, None) == 1
-    assert L.topk_select(ctypes.byref(d), P + 4, P, P, None, 0, None) == 4
-    assert L.topk_select(ctypes.byref(_dims(top_k=0)), P, P, P, None, 0, None) == 2
-    assert L.topk_select(ctypes.byref(_dims(m=0)), P, P, P, None, 0, None) == 2
+    assert L.topk_select(ctypes.byref(d), None, P, None, P, None, 0, None) == 1
+    assert L.topk_select(ctypes.byref(d), P + 4, P, None, P, None, 0, None) == 4
+    assert L.topk_select(ctypes.byref(d), P, P, P + 1, P, None, 0, None) == 4
+    assert L.topk_select(ctypes.byref(_dims(top_k=0)), P, P, None, P, None, 0, None) == 2
+    assert L.topk_select(ctypes.byref(_dims(m=0)), P, P, None, P, None, 0, None) == 2
 
 
-def _att(d, dt=dsa.BF16, q=P, kv=P, idx=P, raw=None, base=0, nraw=0, ws=None, wsb=0, out=P):
-    return L.sparse_mla_attend(ctypes.byref(d), dt, q, kv, idx, raw, base, nraw, P, 0.1, out,
-                               None, ws, wsb, None)
+def _att(d, dt=dsa.BF16, q=P, kv=P, idx=P, raw=None, base=0, nraw=0, ws=None, wsb=0, out=P,
+         sink=None):
+    return L.sparse_mla_attend(ctypes.byref(d), dt, q, kv, idx, raw, base, nraw, P, 0.1, sink,
+                               out, None, ws, wsb, None)
 
 
 def test_attend_validation():
@@ -99,6 +102,7 @@ def test_attend_validation():
     assert _att(_dims(D_K=1028)) == 2
     assert _att(d, dt=dsa.MXFP4) == 3
     assert _att(d, out=P + 2) == 4
+    assert _att(d, sink=P + 2) == 4
     assert _att(_dims(W=16), raw=P, base=-1) == 2
     # few queries -> split partials need a workspace
     dd = _dims(B=1, T=1, top_k=2048)
@@ -170,6 +174,16 @@ def test_hca_validation_and_workspace():
     assert L.hca_forward(ctypes.byref(dec), ctypes.byref(a), P, need, None) == 4
 
 
+def test_compress_blocks_validation():
+    d = _dims(B=2, D_K=576, m=4)
+    assert L.kv_compress_blocks(None, dsa.BF16, P, 400, P, 100, 0, 1, None) == 1
+    assert L.kv_compress_blocks(ctypes.byref(d), dsa.MXFP4, P, 400, P, 100, 0, 1, None) == 3
+    assert L.kv_compress_blocks(ctypes.byref(d), dsa.BF16, P, 400, P, 100, 5, 4, None) == 2   # j1 < j0
+    assert L.kv_compress_blocks(ctypes.byref(d), dsa.BF16, P, 400, P, 100, 0, 101, None) == 2  # > c_stride
+    assert L.kv_compress_blocks(ctypes.byref(d), dsa.BF16, P, 399, P, 100, 99, 100, None) == 2  # raw short
+    assert L.kv_compress_blocks(ctypes.byref(d), dsa.BF16, P + 8, 400, P, 100, 0, 1, None) == 4
+
+
 def test_compress_validation():
     d = _dims(m=4)
     assert L.kv_compress_mean(ctypes.byref(d), dsa.BF16, None, 400, P, None) == 1
@@ -193,4 +207,4 @@ def test_workspace_sizes():
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU device error path")
 def test_valid_call_without_gpu_reports_device_error():
     d = _dims(B=1, T=1, N=64, top_k=8)
-    assert L.topk_select(ctypes.byref(d), P, P, P, None, 0, None) == 6
+    assert L.topk_select(ctypes.byref(d), P, P, None, P, None, 0, None) == 6

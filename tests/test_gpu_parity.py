@@ -217,9 +217,11 @@ def _attend_case(c, label, seed=0, frac_masked=0.05):
     raw = wl.kv_raw()
     base, n_raw = wl.raw_extent()
     log(f"[attend {label}] B={B} T={T} N={c.N} k={k} W={c.W} dt={c.dt}")
+    sink = wl.sink()
     out, lse = dsa.sparse_mla_attend(to_dev(wl.q()), to_dev(kv), to_dev(idx), to_dev(pos), c.D_V,
                                      c.softmax_scale, kv_raw=to_dev(raw) if raw is not None else None,
-                                     raw_base=base, W=c.W, m=c.m)
+                                     raw_base=base, W=c.W, m=c.m,
+                                     sink=to_dev(sink) if sink is not None else None)
     torch.cuda.synchronize()
     out, lse = oracle.decode(to_host(out)), to_host(lse)
     worst = (0.0, 0.0)
@@ -227,7 +229,8 @@ def _attend_case(c, label, seed=0, frac_masked=0.05):
         for t in range(T):
             ro, rl = oracle.attend_row(wl.q()[b, t], kv[b], idx[b, t], c.D_V, c.softmax_scale,
                                        p=int(pos[b, t]), W=c.W,
-                                       kv_raw=raw[b] if raw is not None else None, raw_base=base)
+                                       kv_raw=raw[b] if raw is not None else None, raw_base=base,
+                                       sink=None if sink is None else sink.astype(np.float64))
             mx, sc = check_attention(out[b, t], lse[b, t], ro, rl, what=f"{label} b={b} t={t}")
             worst = max(worst, (mx, sc))
     log(f"[attend {label}] max abs err {worst[0]:.3e} (max|ref| {worst[1]:.3e})")

@@ -1,0 +1,184 @@
+"""GPU parity of the serving pieces against the fp64 oracle:
+  attention sink  one logit per head joining the sparse softmax with a zero value vector
+                  (unsplit, split + merge, scalar kernel, fused decode, HCA)
+  ragged batches  sequences holding fewer entries than the batch's N (every selection kernel)
+  IndexShare      a later layer attending over the index set an earlier dsa_forward returned
+  incremental CSA one compressed block appended per m decoded tokens (kv_compress_blocks)
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import (DeviceWorkload, check_attention, check_scores, log, score_mass, to_dev,
+                      to_host)
+from test_gpu_parity import _attend_case, _cfg, _hca_case
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import lightning_indexer_top_03_amd as dsa
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    yield
+    torch.cuda.empty_cache()
+
+
+def _run_checked(c, n_check=8):
+    """dsa_forward with every row's selection checked exactly against the oracle's top-k of the
+    GPU's own scores (same fp32 values, so the set is unique), the scores of sampled rows against
+    the oracle's (masked beyond n_vis, which a ragged batch clamps) and attention (sink
+    included) on the GPU's set."""
+    wl = synth.make_workload(c)
+    dw = DeviceWorkload(wl)
+    f = dw.forward(keep_scores=True, keep_idx=True)
+    log(f"[{c.name}] dsa_forward B={c.B} T={c.T} N={c.N} k={c.top_k} m={c.m} W={c.W} "
+        f"seq_lens={c.seq_lens} sink={c.sink}")
+    f.run()
+    torch.cuda.synchronize()
+    run = oracle.QueryRunner(wl)
+    rows = [(b, t) for b in range(c.B) for t in range(c.T)]
+    rng = np.random.default_rng(c.seed)
+    check = {rows[i] for i in rng.choice(len(rows), min(n_check, len(rows)), replace=False)}
+    check |= {(b, 0) for b in range(c.B)}
+    worst = (0.0, 0.0)
+    for b, t in rows:
+        what = f"{c.name} b={b} t={t}"
+        sc = to_host(f.scores[b, t])
+        ix = to_host(f.idx[b, t])
+        nv = run.n_vis(b, t)
+        cnt = min(nv, c.top_k)
+        ref, rcnt = oracle.topk_row(sc[:nv].astype(np.float64), nv, c.top_k)
+        assert rcnt == cnt
+        assert np.array_equal(np.sort(ix[:cnt]), ref[:cnt]), f"{what}: selection differs"
+        assert (ix[cnt:] == -1).all(), f"{what}: padding"
+        if (b, t) in check:
+            check_scores(sc, run.scores(b, t), nv, what=what, mass=score_mass(wl, b, t),
+                         dims=(c.H_I, c.D_I))
+            out = oracle.decode(to_host(f.out[b, t]))
+            ro, rl = run.attend(b, t, ix)
+            worst = max(worst, check_attention(out, to_host(f.lse[b, t]), ro, rl, what=what))
+    log(f"[{c.name}] {len(rows)} rows: selections exact; attention max abs err {worst[0]:.3e} "
+        f"(max|ref| {worst[1]:.3e})")
+    del f, dw
+
+
+# --------------------------------------------------------------------------- attention sink ----
+
+def test_sink_sparse_attend_split_unsplit_and_scalar():
+    # sink logits U(4, 9): exp(sink) is of the order of the entries' summed exp, so the sink
+    # takes a visible share of every head's mass
+    dec = _cfg("decode", B=4, N=3001, pos0=3000, sink=(4.0, 9.0), name="sink_split")
+    _attend_case(dec, "sink-split")
+    _attend_case(dec.sharp().with_(sink=(8.0, 14.0)), "sink-split-sharp", seed=1)
+    rows = _cfg("decode", B=1, T=300, N=2000, top_k=1000, pos0=1700, sink=(3.0, 8.0),
+                name="sink_rows")
+    _attend_case(rows.sharp().with_(sink=(10.0, 16.0)), "sink-rows-sharp", seed=2)
+    _attend_case(synth.CONFIGS["tiny"].with_(sink=(0.0, 4.0), name="sink_tiny"), "sink-tiny",
+                 seed=3)
+    # a query whose every entry is masked: out = 0, lse = sink
+    c = _cfg("decode", B=1, N=500, top_k=64, pos0=499, sink=(0.5, 1.5), name="sink_empty")
+    wl = synth.make_workload(c)
+    idx = np.full((1, 1, 64), -1, np.int32)
+    out, lse = dsa.sparse_mla_attend(to_dev(wl.q()), to_dev(wl.kv()), to_dev(idx),
+                                     to_dev(wl.q_pos()), 512, c.softmax_scale,
+                                     sink=to_dev(wl.sink()))
+    torch.cuda.synchronize()
+    assert (to_host(out.float()) == 0).all()
+    assert np.allclose(to_host(lse)[0, 0], wl.sink(), rtol=1e-6)
+
+
+def test_sink_through_dsa_forward_and_hca():
+    # fused decode path (selection in the attention prologue, split merge), a CSA window
+    _run_checked(synth.CONFIGS["decode"].with_(sink=(5.0, 9.0), name="sink_decode"))
+    p = 4 * 40000 - 1
+    _run_checked(synth.CONFIGS["csa_decode"].with_(B=2, N=40000, pos0=p, raw_base=p + 1 - 128,
+                                                  sink=(5.0, 9.0), name="sink_csa"))
+    base = synth.CONFIGS["hca_decode"]
+    _hca_case(base.with_(B=2, T=3, N=900, m=8, pos0=8 * 900 - 5, pos_stride=2, raw_base=8 * 900 - 140,
+                         n_raw=140, sink=(2.0, 6.0), name="hca_sink").sharp().with_(sink=(2.0, 6.0)))
+
+
+# --------------------------------------------------------------------------- ragged batches ----
+
+def test_ragged_decode_fused_selection():
+    # one decode query per sequence, sequences holding 8192, 5000, 2048 (= k: keep-all), 700 and
+    # 1 entries of the 8192-entry storage (the query position is the same for all)
+    c = synth.CONFIGS["decode"].with_(B=5, seq_lens=(8192, 5000, 2048, 700, 1), w_lo=-0.5,
+                                      name="ragged_decode")
+    _run_checked(c)
+
+
+def test_ragged_many_rows_and_long_rows():
+    # 4 x 40 = 160 rows (register radix select) with lengths below and above the positions
+    c = synth.CONFIGS["decode"].with_(B=4, T=40, N=3000, pos0=1000, pos_stride=49, top_k=512,
+                                      seq_lens=(3000, 1500, 800, 40), name="ragged_rows")
+    _run_checked(c, n_check=10)
+    # MXFP4 CSA blocks over N = 40000 (> 32768: chunk filter + candidate select) with a window
+    p = 4 * 40000 - 1
+    _run_checked(synth.CONFIGS["csa_decode"].with_(B=3, N=40000, pos0=p, raw_base=p + 1 - 128,
+                                                  seq_lens=(40000, 33000, 900),
+                                                  name="ragged_csa"))
+
+
+def test_ragged_hca():
+    base = synth.CONFIGS["hca_decode"]
+    _hca_case(base.with_(B=3, T=2, N=1200, m=8, pos0=8 * 1200 - 9, pos_stride=4,
+                         raw_base=8 * 1200 - 140, n_raw=140, seq_lens=(1200, 700, 3),
+                         name="hca_ragged").sharp())
+
+
+# ------------------------------------------------------------------------------- IndexShare ----
+
+def test_index_share_across_layers():
+    # layer 1 selects (dsa_forward returns idx); layer 2 attends with its own q / kv over the
+    # same index set
+    c1 = synth.CONFIGS["decode"].with_(B=4, N=6000, pos0=5999, name="share_l1")
+    c2 = c1.with_(seed=77, name="share_l2").sharp()
+    wl1, wl2 = synth.make_workload(c1), synth.make_workload(c2)
+    dw1 = DeviceWorkload(wl1)
+    f1 = dw1.forward(keep_scores=False, keep_idx=True)
+    f1.run()
+    out2, lse2 = dsa.sparse_mla_attend(to_dev(wl2.q()), to_dev(wl2.kv()), f1.idx,
+                                       to_dev(wl2.q_pos()), c2.D_V, c2.softmax_scale)
+    torch.cuda.synchronize()
+    run2 = oracle.QueryRunner(wl2)
+    ix = to_host(f1.idx)
+    for b in range(c1.B):
+        ro, rl = run2.attend(b, 0, ix[b, 0])
+        check_attention(oracle.decode(to_host(out2[b, 0])), to_host(lse2[b, 0]), ro, rl,
+                        what=f"share b={b}")
+    del f1, dw1
+
+
+# ------------------------------------------------------------------------ incremental CSA ----
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_kv_compress_blocks_appends_only_its_blocks(dt):
+    B, n_raw, D, m, nc = 3, 4000, 576, 4, 1000
+    raw = synth.normal(41, synth.TID_KV, (B, n_raw, D), 1.0 / 24, dt)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    kv_c = torch.full((B, nc, D), 7.0, dtype=tdt, device="cuda")
+    raw_d = to_dev(raw)
+    log(f"[compress_blocks {dt}] blocks 0..500, then 500..997 one block at a time ... 997")
+    dsa.kv_compress_blocks(raw_d, m, kv_c, 0, 500)
+    for j in range(500, 997, 97):  # decoder-style appends
+        dsa.kv_compress_blocks(raw_d, m, kv_c, j, min(j + 97, 997))
+    torch.cuda.synchronize()
+    got = to_host(kv_c)
+    for b in range(B):
+        ref = oracle.compress_mean(raw[b], m)
+        g = oracle.decode(got[b]) if dt == "bf16" else got[b].astype(np.float64)
+        done = g[:997]
+        if dt == "bf16":
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref[:997]), 1e-30))) - 7)
+            assert (np.abs(done - ref[:997]) <= ulp).all()
+        else:
+            mag = oracle.compress_mean(np.abs(raw[b]).astype(np.float32), m)[:997]
+            assert (np.abs(done - ref[:997]) <= 2.0 ** -21 * mag + 1e-30).all()
+        assert (g[997:] == 7.0).all(), "blocks outside [j0, j1) must stay untouched"

@@ -435,3 +435,66 @@ def test_tiny_workload_end_to_end_invariants():
         rest = np.setdiff1d(np.arange(p + 1), sel)
         assert r["scores"][sel].min() >= r["scores"][rest].max()
         assert np.isfinite(r["out"]).all() and r["out"].shape == (c.H, c.D_V)
+
+
+# ------------------------------------------------------------------ attention sink, ragged ----
+
+def test_h6_sink_golden():
+    g = json.load(open(os.path.join(GOLD, "h6_sink.json")))
+    q = np.array(g["q"], np.float64)
+    kv = np.array(g["kv"], np.float64)
+    for c in g["cases"]:
+        sink = np.array([float(c["sink"])], np.float64)
+        out, lse = oracle.attend_row(q, kv, np.array(c["idx"], np.int32), g["D_V"], g["scale"],
+                                     sink=sink)
+        assert abs(out[0, 0] - c["out"]) < 1e-12, c
+        assert abs(lse[0] - float(c["lse"])) < 1e-12, c
+
+
+def test_sink_invariants():
+    # a sink logit equal to the entries' own log-sum-exp takes half of every head's mass: the
+    # output halves and lse grows by ln 2; a sink of -inf is no sink at all
+    rng = np.random.default_rng(11)
+    H, D_K, D_V, N = 5, 16, 12, 40
+    q = rng.standard_normal((H, D_K))
+    kv = rng.standard_normal((N, D_K))
+    idx = rng.choice(N, 25, replace=False).astype(np.int32)
+    out0, lse0 = oracle.attend_row(q, kv, idx, D_V, 0.3)
+    out1, lse1 = oracle.attend_row(q, kv, idx, D_V, 0.3, sink=lse0)
+    assert np.allclose(out1, out0 / 2, rtol=1e-12, atol=1e-14)
+    assert np.allclose(lse1, lse0 + np.log(2.0), rtol=1e-12)
+    out2, lse2 = oracle.attend_row(q, kv, idx, D_V, 0.3, sink=np.full(H, -np.inf))
+    assert np.array_equal(out2, out0) and np.array_equal(lse2, lse0)
+    # against the definition written with numpy: softmax over [z, s] with a zero value row
+    z = 0.3 * q @ kv[idx].T
+    s = rng.standard_normal(H) * 3
+    out3, lse3 = oracle.attend_row(q, kv, idx, D_V, 0.3, sink=s)
+    zz = np.concatenate([z, s[:, None]], axis=1)
+    w = np.exp(zz - zz.max(1, keepdims=True))
+    w /= w.sum(1, keepdims=True)
+    vals = np.concatenate([kv[idx, :D_V], np.zeros((1, D_V))], axis=0)
+    assert np.allclose(out3, w @ vals, rtol=1e-12, atol=1e-14)
+    assert np.allclose(lse3, np.log(np.exp(zz).sum(1)), rtol=1e-12)
+
+
+@pytest.mark.parametrize("p,m,N,L,want", [(99, 1, 200, 50, 50), (99, 1, 200, 150, 100),
+                                          (99, 4, 200, 10, 10), (99, 4, 200, 30, 25),
+                                          (7, 1, 5, 100, 5), (10, 1, 20, 0, 0), (-1, 1, 20, 9, 0)])
+def test_n_vis_ragged(p, m, N, L, want):
+    assert oracle.n_vis(p, m, N, seq_len=L) == want
+
+
+def test_ragged_scores_and_topk_equal_a_shorter_context():
+    # a sequence holding L entries scores and selects exactly as the same query over a context
+    # truncated to L entries
+    rng = np.random.default_rng(5)
+    H_I, D_I, N, L, k = 3, 8, 60, 37, 10
+    qI = rng.standard_normal((H_I, D_I))
+    w = rng.uniform(-1, 1, H_I).astype(np.float32)
+    kI = rng.standard_normal((N, D_I))
+    nv = oracle.n_vis(N - 1, 1, N, seq_len=L)
+    assert nv == L
+    sc = oracle.scores_row(qI, w, kI, nv)
+    sc_short = oracle.scores_row(qI, w, kI[:L].copy(), oracle.n_vis(L - 1, 1, L))
+    assert np.array_equal(sc[:L], sc_short) and np.isneginf(sc[L:]).all()
+    assert np.array_equal(oracle.topk_row(sc, nv, k)[0], oracle.topk_row(sc_short, L, k)[0])
