@@ -71,8 +71,12 @@ typedef enum dsa_dtype {
   DSA_MXFP4 = 2, /* OCP MX FP4: e2m1 codes, two per byte, LOW nibble = even element;
                     one E8M0 scale byte (2^(e-127)) per 32 consecutive elements.
                     Only for k_I.                                                        */
-  DSA_MXFP8 = 3  /* OCP MX FP8: e4m3 (E4M3FN) codes, one per byte; one E8M0 scale byte
+  DSA_MXFP8 = 3, /* OCP MX FP8: e4m3 (E4M3FN) codes, one per byte; one E8M0 scale byte
                     per 32 consecutive elements. For k_I and q_I (the indexer only).     */
+  /* Not dtypes: these two widen the enumeration's range to every int32 value, so that any
+     integer a caller passes is a defined dsa_dtype value, rejected with DSA_ERR_DTYPE. */
+  DSA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  DSA_DTYPE_RANGE_MAX_ = 2147483647
 } dsa_dtype;
 
 typedef struct dsa_dims {
