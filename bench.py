@@ -68,6 +68,22 @@ def _fused_topk(cfg):
             and cfg.H % 64 == 0 and cfg.N <= 32768 and cfg.B * cfg.T <= 128)
 
 
+def _segments_fused(cfg):
+    """The decode indexer writes the long-row top-k's candidate segments itself (MX keys over
+    N > 32768 entries, with the plan of 4096 keys per indexer workgroup)."""
+    if not (cfg.H_I == 64 and cfg.D_I == 128 and cfg.k_dt in ("mxfp4", "mxfp8")
+            and cfg.N > 32768):
+        return False
+    rows = cfg.B * cfg.T
+    if cfg.qi_dt == "mxfp8" and rows >= 64:
+        return False
+    tk = 64 if cfg.k_dt == "mxfp4" else 32
+    max_it, it = 512 // tk, 1
+    while it < max_it and 2 * it * tk * 8 * 256 <= rows * cfg.N:
+        it *= 2
+    return it == max_it
+
+
 def _kernel_plan(cfg, nsplit):
     """Kernel names of one dsa_forward (per chunk) in launch order."""
     names = []
@@ -91,7 +107,12 @@ def _kernel_plan(cfg, nsplit):
         names.append("indexer_generic")
     mfma = cfg.dt == "bf16" and cfg.D_K == 576 and cfg.D_V == 512 and cfg.H % 64 == 0
     if not _fused_topk(cfg):
-        names += ["topk_radix_reg"] if cfg.N <= 32768 else ["topk_long_filter", "topk_long_select"]
+        if cfg.N <= 32768:
+            names.append("topk_stream")
+        elif _segments_fused(cfg):
+            names.append("topk_long_select")  # the indexer wrote the candidate segments
+        else:
+            names += ["topk_long_filter", "topk_long_select"]
     names.append("attend_mfma_dma" if mfma else "attend_generic")
     if nsplit > 1:
         names.append("attend_combine")

@@ -210,11 +210,24 @@ dsa_status run_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, h
     const int64_t nr = std::min(R, rows - q0);
     float* sc = keep_scores ? a->scores + (size_t)q0 * d->N : ws_scores;
     int32_t* ix = a->idx ? a->idx + (size_t)q0 * d->top_k : ws_idx;
-    if (hipError_t e = launch_indexer(s, q0, nr, a->q_I, (int)qi_dt, a->q_scale, a->w, a->k_I,
-                                      a->k_scale, (int)a->k_dt, a->q_pos, a->seq_len, sc,
-                                      keep_scores, st))
+    const bool fused = attend_fused_ok(s, fmt, nr);
+    // long rows with MX keys: the indexer's epilogue also writes the top-k's candidate segments
+    const int seg_stride = fused ? 0 : indexer_segment_stride(s, nr, (int)qi_dt, (int)a->k_dt);
+    if (seg_stride > 0) {
+      if (hipError_t e = launch_indexer_segments(s, q0, nr, a->q_I, (int)qi_dt, a->q_scale, a->w,
+                                                 a->k_I, a->k_scale, (int)a->k_dt, a->q_pos,
+                                                 a->seq_len, sc, keep_scores,
+                                                 static_cast<uint8_t*>(ws_topk), st))
+        return launched(e);
+      if (hipError_t e = launch_topk_segments(s, q0, nr, sc, a->q_pos, a->seq_len, seg_stride, ix,
+                                              ws_topk, st))
+        return launched(e);
+    } else if (hipError_t e = launch_indexer(s, q0, nr, a->q_I, (int)qi_dt, a->q_scale, a->w,
+                                             a->k_I, a->k_scale, (int)a->k_dt, a->q_pos,
+                                             a->seq_len, sc, keep_scores, st)) {
       return launched(e);
-    if (attend_fused_ok(s, fmt, nr)) {
+    }
+    if (fused) {
       // top-k inside the attention kernel: idx is written only when the caller wants it
       if (hipError_t e = launch_attend_fused(s, q0, nr, a->q, a->kv, sc,
                                              a->idx ? a->idx + (size_t)q0 * d->top_k : nullptr,
@@ -223,8 +236,9 @@ dsa_status run_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, h
                                              a->softmax_scale, a->out, a->lse, ws_att, st))
         return launched(e);
     } else {
-      if (hipError_t e = launch_topk(s, q0, nr, sc, a->q_pos, a->seq_len, ix, ws_topk, st))
-        return launched(e);
+      if (seg_stride == 0)
+        if (hipError_t e = launch_topk(s, q0, nr, sc, a->q_pos, a->seq_len, ix, ws_topk, st))
+          return launched(e);
       if (hipError_t e = launch_attend(s, q0, nr, fmt, a->q, a->kv, ix,
                                        d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw,
                                        a->q_pos, nullptr, a->sink, a->softmax_scale, a->out,

@@ -20,6 +20,7 @@
 // [H_I x N] per-head products never leave registers.
 #include "common.h"
 #include "launch.h"
+#include "select.h"
 
 #include <algorithm>
 
@@ -226,12 +227,13 @@ struct MxKeys {
   }
 };
 
-template <int KFMT, bool QMX, int ITERS>
+template <int KFMT, bool QMX, int ITERS, bool FILT>
 __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_mx_dma(
     const void* __restrict__ qI, const uint8_t* __restrict__ qsc, const float* __restrict__ w,
     const uint8_t* __restrict__ kI, const uint8_t* __restrict__ ksc,
     const int32_t* __restrict__ q_pos, const int32_t* __restrict__ seq_len, int T, int N, int m,
-    int64_t qi0, float* __restrict__ scores, int fill_masked) {
+    int64_t qi0, float* __restrict__ scores, int fill_masked, int top_k,
+    uint8_t* __restrict__ seg_ws) {
   using K = MxKeys<KFMT>;
   constexpr int TK = K::kTile;
   constexpr int NP = QMX ? 1 : 2;  // q parts: the MXFP8 q_I itself, or hi + lo
@@ -498,6 +500,24 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_mx_dma(
       if (s < nv) srow[s] = sres[wv][TK * t + lane];
       else if (fill_masked && s < N) srow[s] = kNegInf;
     }
+  }
+  if constexpr (FILT) {
+    // The long-row top-k's first stage on the scores still in LDS (select.h chunk_filter):
+    // this workgroup's keys are one chunk; thread (wv, lane) takes its wave's staged scores
+    // 8 lane .. 8 lane + 7 (one tile, ascending keys, so the visible ones come first).
+    static_assert(ITERS * TK == 8 * 64, "one chunk = 8 staged scores per thread");
+    if (nv <= top_k) return;  // the select keeps every visible entry
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave is done with its ring, which now holds the select state
+    SelShared<kDecWaves>& sh = *reinterpret_cast<SelShared<kDecWaves>*>(&sk[0][0][0]);
+    const int t = (8 * lane) / TK, off = (8 * lane) % TK;
+    const int e0 = tile_key(t) + off;
+    uint32_t key[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) key[j] = order_key(sres[wv][8 * lane + j]);
+    const int nvt = max(0, min(8, nv - e0));
+    chunk_filter<kDecWaves, 8>(key, nvt, nv, top_k, sh, seg_ws + (size_t)row * long_row_bytes(gridDim.x),
+                               gridDim.x, blockIdx.x, [&](int j) { return e0 + j; });
   }
 }
 
@@ -993,9 +1013,9 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
     while (it < max_it && (int64_t)2 * it * tk * kDecWaves * 256 <= total) it *= 2;
     const int kpw = kDecWaves * tk * it;
     dim3 g((s.N + kpw - 1) / kpw, (unsigned)nrows);
-#define DSA_MX(KF, QM, I)                                                                     \
-  return launch(indexer_decode_mx_dma<KF, QM, I>, g, kDecWaves * 64, 0, st, q_I, q_scale, w, kp, \
-                k_scale, q_pos, seq_len, s.T, s.N, s.m, qi0, scores, fm)
+#define DSA_MX(KF, QM, I)                                                                        \
+  return launch(indexer_decode_mx_dma<KF, QM, I, false>, g, kDecWaves * 64, 0, st, q_I, q_scale, w, \
+                kp, k_scale, q_pos, seq_len, s.T, s.N, s.m, qi0, scores, fm, s.top_k, nullptr)
 #define DSA_MX_IT(KF, QM)        \
   switch (it) {                  \
     case 1: DSA_MX(KF, QM, 1);   \
@@ -1019,6 +1039,43 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
   size_t shm = sizeof(float) * ((size_t)s.H_I * s.D_I + s.H_I);
   return launch(indexer_generic, grid, 256, shm, st, q_I, q_fmt, q_scale, w, k_I, k_scale, k_fmt,
                 q_pos, seq_len, s.T, s.N, s.m, s.H_I, s.D_I, qi0, scores, fm);
+}
+
+int indexer_segment_stride(const Shape& s, int64_t nrows, int q_fmt, int k_fmt) {
+  const bool shape_ok = s.H_I == 64 && s.D_I == 128;
+  const bool kmx = k_fmt == FMT_MXFP4 || k_fmt == FMT_MXFP8;
+  if (!shape_ok || !kmx || s.N <= kLongChunk * 8 || nrows <= 0) return 0;
+  if (q_fmt == FMT_MXFP8 && nrows >= 64) return 0;  // the prefill-shaped kernel
+  if (q_fmt != FMT_BF16 && q_fmt != FMT_MXFP8) return 0;
+  // the decode kernel's plan (launch_indexer) must be the one with 4096 keys per workgroup,
+  // the chunk size of the segment workspace
+  const int tk = k_fmt == FMT_MXFP4 ? 64 : 32, max_it = 512 / tk;
+  const int64_t total = nrows * (int64_t)s.N;
+  int it = 1;
+  while (it < max_it && (int64_t)2 * it * tk * kDecWaves * 256 <= total) it *= 2;
+  return it == max_it ? kDecWaves * tk : 0;
+}
+
+hipError_t launch_indexer_segments(const Shape& s, int64_t qi0, int64_t nrows, const void* q_I,
+                                   int q_fmt, const uint8_t* q_scale, const float* w,
+                                   const void* k_I, const uint8_t* k_scale, int k_fmt,
+                                   const int32_t* q_pos, const int32_t* seq_len, float* scores,
+                                   bool fill_masked, uint8_t* seg_ws, hipStream_t st) {
+  if (nrows <= 0) return hipSuccess;
+  if (indexer_segment_stride(s, nrows, q_fmt, k_fmt) == 0) return hipErrorInvalidValue;
+  const int fm = fill_masked ? 1 : 0;
+  const uint8_t* kp = static_cast<const uint8_t*>(k_I);
+  const dim3 g((s.N + kLongChunk - 1) / kLongChunk, (unsigned)nrows);
+#define DSA_MXF(KF, QM, I)                                                                      \
+  return launch(indexer_decode_mx_dma<KF, QM, I, true>, g, kDecWaves * 64, 0, st, q_I, q_scale, w, \
+                kp, k_scale, q_pos, seq_len, s.T, s.N, s.m, qi0, scores, fm, s.top_k, seg_ws)
+  if (k_fmt == FMT_MXFP4) {
+    if (q_fmt == FMT_MXFP8) DSA_MXF(FMT_MXFP4, true, 8);
+    DSA_MXF(FMT_MXFP4, false, 8);
+  }
+  if (q_fmt == FMT_MXFP8) DSA_MXF(FMT_MXFP8, true, 16);
+  DSA_MXF(FMT_MXFP8, false, 16);
+#undef DSA_MXF
 }
 
 }  // namespace dsa

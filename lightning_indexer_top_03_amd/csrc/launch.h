@@ -73,12 +73,29 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
                           const int32_t* seq_len, float* scores, bool fill_masked,
                           hipStream_t st);
 
+// The decode indexer over long rows (N > 8 * 4096) with MX keys, fused with the first stage of
+// the long-row top-k: besides the scores it writes the rows' candidate segments (select.h
+// chunk_filter layout, one per workgroup of 4096 keys) into seg_ws (topk_ws_bytes). The
+// stride is the argument launch_topk_segments needs; 0 = launch_indexer_segments does not
+// apply to this call (it then returns hipErrorInvalidValue).
+int indexer_segment_stride(const Shape& s, int64_t nrows, int q_fmt, int k_fmt);
+hipError_t launch_indexer_segments(const Shape& s, int64_t qi0, int64_t nrows, const void* q_I,
+                                   int q_fmt, const uint8_t* q_scale, const float* w,
+                                   const void* k_I, const uint8_t* k_scale, int k_fmt,
+                                   const int32_t* q_pos, const int32_t* seq_len, float* scores,
+                                   bool fill_masked, uint8_t* seg_ws, hipStream_t st);
+
 // ---- step 2 ----
 // scores: [nrows, N] row-relative, idx: [nrows, top_k] row-relative, rows qi0 .. qi0+nrows-1.
 size_t topk_ws_bytes(const Shape& s, int64_t nrows);
 hipError_t launch_topk(const Shape& s, int64_t qi0, int64_t nrows, const float* scores,
                        const int32_t* q_pos, const int32_t* seq_len, int32_t* idx, void* ws,
                        hipStream_t st);
+// The select of long rows (N > 32768) over candidate segments the decode indexer already wrote
+// (launch_indexer with a segment workspace): chunk g's first keys start at g * stride.
+hipError_t launch_topk_segments(const Shape& s, int64_t qi0, int64_t nrows, const float* scores,
+                                const int32_t* q_pos, const int32_t* seq_len, int stride,
+                                int32_t* idx, const void* ws, hipStream_t st);
 
 // ---- step 3 ----
 // idx: [nrows, top_k] row-relative; q/out/lse indexed by the flattened row qi.

@@ -212,6 +212,57 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[PER], int 
   tau = prefix;
 }
 
+// block_threshold through a sample: the same result (tau, need, cnt_eq), with the radix passes
+// run over a few thousand candidates instead of the whole row. The first key of every thread
+// that has any (a systematic sample of ns = ceil(n / PER) keys) gives lo = the sample's r-th
+// largest, r = mu + 4 sigma + 8 with mu = ns k / n the expected number of sampled keys among
+// the row's top k. When at least k and at most kSampCap keys are >= lo, every one of the top
+// k is among them, so the threshold among those candidates (compacted into cbuf in index
+// order) is the row's. Otherwise (an unlucky or adversarial sample) the whole row goes through
+// block_threshold. Per key this costs a compare and a rarely taken store instead of a share of
+// every radix pass.
+constexpr int kSampCap = 4096;
+
+template <int NW, int PER>
+__device__ __forceinline__ void block_threshold_sampled(const uint32_t (&key)[PER], int nv,
+                                                        uint32_t k, uint32_t n,
+                                                        SelShared<NW>& sh, uint32_t* cbuf,
+                                                        uint32_t& tau, uint32_t& need,
+                                                        uint32_t& cnt_eq) {
+  constexpr int PC = kSampCap / (NW * 64);  // candidates per thread
+  static_assert(PC * NW * 64 == kSampCap, "candidate slots split evenly over the block");
+  const uint32_t ns = min((uint32_t)(NW * 64), (n + PER - 1) / PER);
+  const float p = (float)k / (float)n;
+  const float mu = p * (float)ns;
+  const float rf = mu + 4.f * __builtin_sqrtf(mu * (1.f - p)) + 8.f;
+  if (rf < (float)ns) {  // block-uniform
+    const uint32_t skey[1] = {key[0]};
+    uint32_t lo, need_s, eq_s;
+    block_threshold<NW, 1>(skey, nv > 0 ? 1 : 0, (uint32_t)rf, sh, lo, need_s, eq_s, ns);
+    __syncthreads();  // the next threshold clears the histograms this one read last
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) c += (j < nv && key[j] >= lo) ? 1u : 0u;
+    uint32_t total;
+    uint32_t o = block_excl_scan<NW>(c, sh, total);
+    if (total >= k && total <= (uint32_t)kSampCap) {  // block-uniform
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (j < nv && key[j] >= lo) cbuf[o++] = key[j];
+      __syncthreads();
+      uint32_t kc[PC];
+      const int c0 = PC * (int)threadIdx.x;
+      const int nvc = max(0, min(PC, (int)total - c0));
+#pragma unroll
+      for (int j = 0; j < PC; ++j) kc[j] = cbuf[min(c0 + j, (int)total - 1)];
+      block_threshold<NW, PC>(kc, nvc, k, sh, tau, need, cnt_eq, total);
+      return;
+    }
+    __syncthreads();
+  }
+  block_threshold<NW, PER>(key, nv, k, sh, tau, need, cnt_eq, n);
+}
+
 // Rank (in ascending index order) of this thread's first selected entry, how many of its
 // tau-valued entries it takes and how many entries it selects; selected = key > tau, or
 // key == tau among the first `need` tau-valued entries of the row. Counts fit 16 bits (rows of
@@ -272,6 +323,71 @@ __device__ __forceinline__ SelMask<PER> select_mask(const uint32_t (&key)[PER], 
 template <typename M>
 __device__ __forceinline__ uint32_t sel_rank(M sel, int j) {
   return (uint32_t)__popcll((unsigned long long)(sel & (((M)1 << j) - 1)));
+}
+
+// ---- long rows: per-chunk candidate segments -------------------------------------------------
+// A row longer than fits one workgroup is cut into G chunks. Each chunk keeps its own threshold
+// tau_g = its r-th largest key, r = ceil(2k * cn / n) + 16 (about twice the chunk's fair share
+// of the row's top k; cn = visible entries of the chunk, n = of the row), and writes every key
+// >= tau_g with its index to the chunk's candidate segment, with its count and tau_g. A select
+// over the concatenated segments is exact whenever its threshold tau >= tau_g for every chunk:
+// an entry that is not a candidate lies below its chunk's tau_g <= tau.
+constexpr int kLongChunk = 4096;  // entries per chunk
+constexpr int kLongSeg = 1024;    // candidate slots per chunk
+
+// Per-row workspace of the long-row path: counts[G], taus[G], cand_idx[G][kLongSeg],
+// cand_key[G][kLongSeg]. A count of 0xffffffff marks an overflowed segment.
+__host__ __device__ inline size_t long_row_bytes(int G) {
+  return (size_t)G * (8 + 8 * (size_t)kLongSeg);
+}
+
+// The candidate segment of chunk g of a row whose workspace starts at rws: thread t holds the
+// order keys key[0..nvt) (valid ones first) of entries index_of(j); n = the row's visible count
+// (> k). Every thread of the block calls it.
+template <int NW, int PER, typename IndexOf>
+__device__ __forceinline__ void chunk_filter(const uint32_t (&key)[PER], int nvt, int n, int k,
+                                             SelShared<NW>& sh, uint8_t* rws, int G, int g,
+                                             IndexOf index_of) {
+  uint32_t* counts = reinterpret_cast<uint32_t*>(rws);
+  uint32_t* taus = counts + G;
+  int32_t* cidx = reinterpret_cast<int32_t*>(taus + G) + (size_t)g * kLongSeg;
+  uint32_t* ckey = reinterpret_cast<uint32_t*>(taus + G) + (size_t)G * kLongSeg + (size_t)g * kLongSeg;
+  uint32_t cn;
+  (void)block_excl_scan<NW>((uint32_t)nvt, sh, cn);
+  __syncthreads();  // sh.wtot is written again below
+  if (cn == 0u) {
+    if (threadIdx.x == 0) {
+      counts[g] = 0u;
+      taus[g] = 0u;
+    }
+    return;
+  }
+  const int64_t r64 = (2 * (int64_t)k * cn + n - 1) / n + 16;
+  uint32_t tau = 0u;  // every key >= 0: the whole chunk is a candidate
+  if (r64 < (int64_t)cn) {
+    uint32_t need, cnt_eq;
+    block_threshold<NW, PER>(key, nvt, (uint32_t)r64, sh, tau, need, cnt_eq, cn);
+  }
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) cnt += (j < nvt && key[j] >= tau) ? 1u : 0u;
+  uint32_t total;
+  const uint32_t pos = block_excl_scan<NW>(cnt, sh, total);
+  if (total <= (uint32_t)kLongSeg) {
+    uint32_t o = pos;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (j < nvt && key[j] >= tau) {
+        cidx[o] = index_of(j);
+        ckey[o] = key[j];
+        ++o;
+      }
+    }
+  }
+  if (threadIdx.x == 0) {
+    counts[g] = total <= (uint32_t)kLongSeg ? total : 0xffffffffu;
+    taus[g] = tau;
+  }
 }
 
 // Load the order keys of entries PER*t .. PER*t+PER-1 of a row of n visible scores (clamped,

@@ -184,31 +184,23 @@ __device__ void radix_row_exact(const float* __restrict__ s, int n, int k,
 }
 
 // ------------------------------------------------------------------------------------------
-// Rows longer than kLdsMaxN (CSA decode: 262144 blocks per row) in two launches, so that the
-// whole GPU works on a handful of rows instead of one workgroup per row:
-//  * topk_long_filter, one 512-thread workgroup per kLongChunk entries of a row: the chunk's
-//    local threshold tau_g = its r-th largest key with r = ceil(2k * chunk / n) + 16 (about
-//    twice the chunk's fair share of the top k), then every key >= tau_g of the chunk goes, in
-//    index order, to the chunk's candidate segment (indices and keys), with its count and tau_g.
+// Rows longer than kLdsMaxN (CSA decode: 262144 blocks per row): the whole GPU works on a
+// handful of rows through per-chunk candidate segments (select.h chunk_filter):
+//  * the segments come from topk_long_filter, one 512-thread workgroup per kLongChunk
+//    contiguous entries of a row, or straight from the decode indexer's epilogue, which runs the
+//    same filter on the scores it just computed (then a "chunk" is the set of keys one indexer
+//    workgroup scored, and segment order is not index order);
 //  * topk_long_select, one 1024-thread workgroup per row: the segments are concatenated in
-//    chunk order (so candidate order is index order) into LDS and the top k of the candidates
-//    are selected with the same ties-to-lowest-index rule. The result is exact whenever the
-//    selected threshold tau >= tau_g for every chunk: an entry that is not a candidate lies
-//    below its chunk's tau_g <= tau, so every entry >= tau is a candidate. When that check
-//    fails, or a segment overflowed, or there are more candidates than the registers hold, the
-//    workgroup falls back to the exact whole-row radix select above.
+//    chunk order into LDS and the top k of the candidates are selected. With contiguous chunks
+//    candidate order is index order, so ties at tau go to the lowest indices as everywhere
+//    else; with the indexer's segments the fast path is taken only when no tau-valued entry
+//    has to be left out. The result is exact whenever tau >= tau_g for every chunk. When that
+//    check fails, or a segment overflowed, or there are more candidates than the registers hold,
+//    the workgroup falls back to the exact whole-row radix select above, over the row's scores.
 // ------------------------------------------------------------------------------------------
-constexpr int kLongChunk = 4096;                // entries per filter workgroup
 constexpr int kFiltThreads = 512;               // 8 entries per thread
-constexpr int kLongSeg = 1024;                  // candidate slots per chunk
 constexpr int kLongCap = 8 * kTkThreads;        // candidates ranked in registers by the select
 constexpr int kLongMaxChunks = 4 * kTkThreads;  // chunks per row the select kernel can scan
-
-// Per-row workspace of the long-row path: counts[G], taus[G], cand_idx[G][kLongSeg],
-// cand_key[G][kLongSeg].
-__host__ __device__ inline size_t long_row_bytes(int G) {
-  return (size_t)G * (8 + 8 * (size_t)kLongSeg);
-}
 
 __global__ __launch_bounds__(kFiltThreads) void topk_long_filter(
     const float* __restrict__ scores, const int32_t* __restrict__ q_pos,
@@ -226,53 +218,20 @@ __global__ __launch_bounds__(kFiltThreads) void topk_long_filter(
   load_keys<PER>(scores + row * (int64_t)N + c0, N, min(kLongChunk, N - c0), key);
   const int n = n_visible(q_pos[qi0 + row], m, N, seq_len, (int)((qi0 + row) / T));
   if (n <= k) return;  // the select kernel keeps every visible entry
-  uint8_t* rws = ws + row * long_row_bytes(G);
-  uint32_t* counts = reinterpret_cast<uint32_t*>(rws);
-  uint32_t* taus = counts + G;
-  int32_t* cidx = reinterpret_cast<int32_t*>(taus + G) + (size_t)g * kLongSeg;
-  uint32_t* ckey = reinterpret_cast<uint32_t*>(taus + G) + (size_t)G * kLongSeg + (size_t)g * kLongSeg;
-  if (c0 >= n) {
-    if (tid == 0) {
-      counts[g] = 0u;
-      taus[g] = 0u;
-    }
-    return;
-  }
+  if (c0 >= n) return;  // past the visible chunks the select kernel reads
   const int cn = min(kLongChunk, n - c0);
-  const int nv = max(0, min(PER, cn - PER * tid));
-  const int64_t r64 = (2 * (int64_t)k * cn + n - 1) / n + 16;
-  uint32_t tau = 0u;  // every key >= 0: the whole chunk is a candidate
-  if (r64 < cn) {
-    uint32_t need, cnt_eq;
-    block_threshold<NW, PER>(key, nv, (uint32_t)r64, sh, tau, need, cnt_eq, (uint32_t)cn);
-  }
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) cnt += (j < nv && key[j] >= tau) ? 1u : 0u;
-  uint32_t total;
-  const uint32_t pos = block_excl_scan<NW>(cnt, sh, total);
-  if (total <= (uint32_t)kLongSeg) {
-    uint32_t o = pos;
-    const int e0 = c0 + PER * tid;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if (j < nv && key[j] >= tau) {
-        cidx[o] = e0 + j;
-        ckey[o] = key[j];
-        ++o;
-      }
-    }
-  }
-  if (tid == 0) {
-    counts[g] = total <= (uint32_t)kLongSeg ? total : 0xffffffffu;  // overflow marker
-    taus[g] = tau;
-  }
+  const int nvt = max(0, min(PER, cn - PER * tid));
+  const int e0 = c0 + PER * tid;
+  chunk_filter<NW, PER>(key, nvt, n, k, sh, ws + row * long_row_bytes(G), G, g,
+                        [&](int j) { return e0 + j; });
 }
 
 __global__ __launch_bounds__(kTkThreads) void topk_long_select(
     const float* __restrict__ scores, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ seq_len, int T, int64_t qi0, int N, int m, int k, int G,
-    const uint8_t* __restrict__ ws, int32_t* __restrict__ idx) {
+    int stride, int ordered, const uint8_t* __restrict__ ws, int32_t* __restrict__ idx) {
+  // stride: entries per chunk of the chunks' first visible-range cut (chunk g holds visible
+  // entries iff g * stride < n); ordered: segment order is index order
   constexpr int PER = kLongCap / kTkThreads;
   struct Fast {
     SelShared<kTkWaves> sel;
@@ -317,7 +276,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_long_select(
     for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
     return;
   }
-  const int Gn = (n + kLongChunk - 1) / kLongChunk;  // chunks holding visible entries
+  const int Gn = min(G, (n + stride - 1) / stride);  // chunks holding visible entries
   bool fast = Gn <= kLongMaxChunks;
   uint32_t total = 0;
   if (fast) {
@@ -381,7 +340,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_long_select(
       for (int j = 0; j < PER; ++j) key[j] = f.ckey[min(e0 + j, (int)total - 1)];
       uint32_t tau, need, cnt_eq;
       block_threshold<kTkWaves, PER>(key, nv, (uint32_t)k, f.sel, tau, need, cnt_eq, total);
-      if (tau >= f.tau_max) {  // block-uniform: the candidate set holds the row's top k
+      // block-uniform: the candidate set holds the row's top k (and, for segments out of index
+      // order, no tau-valued entry is left out, so no lowest-index choice is needed)
+      if (tau >= f.tau_max && (ordered || cnt_eq == need)) {
         uint32_t base, take_eq, nsel;
         block_ranks<kTkWaves, PER>(key, nv, tau, need, f.sel, base, take_eq, nsel);
         const auto sel = select_mask<PER>(key, nv, tau, take_eq);
@@ -397,39 +358,308 @@ __global__ __launch_bounds__(kTkThreads) void topk_long_select(
 }
 
 // ------------------------------------------------------------------------------------------
-// topk_radix_reg<PER>: rows of at most 1024*PER visible entries, one 1024-thread workgroup per
-// row. Thread t owns the contiguous entries PER*t .. PER*t+PER-1 and keeps their order keys in
-// registers for the whole kernel; the threshold and the ranks come from select.h
-// (block_threshold: 8-bit digits into a shared LDS histogram, one barrier per pass, small
-// boundary bins ranked directly; block_ranks: one block prefix scan). The selection is written
-// in ascending index order, so the output order is deterministic.
+// topk_stream: rows of up to 32768 entries (prefill), one 256-thread workgroup (4 waves) per
+// row and several rows per CU; nothing of the row is held in registers, so the per-key work is
+// a compare and, for the few candidates, an LDS store:
+//  1. lo: a sample of 2048 keys (64 runs of 32 consecutive entries, one cache line each, spread
+//     evenly over the row) and its r-th largest,
+//     r = mu + 4 sigma + 8 with mu = 2048 k / n (select.h block_threshold); rows of at most
+//     kStCap entries skip it (lo = the smallest key: every entry is a candidate).
+//  2. One streaming pass: wave w scans the contiguous quarter w of the row, 8 loads of 16
+//     bytes per lane in flight, and appends every score >= lo (order key and index) to its own
+//     LDS segment in index order (a DPP prefix sum of the lanes' counts per 256 entries).
+//  3. If every segment fits and together they hold at least k entries, they hold every one of
+//     the top k: the threshold (tau, need) and the ranks come from the candidates alone (the
+//     concatenated segments are in index order, so ties at tau go to the lowest indices), and
+//     the selection is written in ascending index order.
+//  4. Otherwise (an unlucky or adversarial sample, or heavy ties): stream_exact, a radix
+//     select with 8-bit digits over the bits that vary in the row, each pass re-reading the row
+//     from L2, then a counting pass and an ordered writing pass.
 // ------------------------------------------------------------------------------------------
-template <int PER>
-__global__ __launch_bounds__(kTkThreads) void topk_radix_reg(
+constexpr int kStThreads = 256;
+constexpr int kStWaves = kStThreads / 64;
+constexpr int kStSeg = 1024;                 // candidate slots per wave
+constexpr int kStCap = kStWaves * kStSeg;    // 4096
+constexpr int kStPC = kStCap / kStThreads;   // candidates per thread in the exact step
+constexpr int kStSample = 2048;
+constexpr int kStUnroll = 8;                 // 256-entry blocks a wave loads ahead
+
+struct __attribute__((aligned(16))) StShared {
+  SelShared<kStWaves> sel;
+  uint32_t ckey[kStCap];
+  int32_t cidx[kStCap];
+  uint32_t wcnt[kStWaves], weq[kStWaves];
+  uint32_t hist[256];
+  uint32_t bin, above, cnt;
+};
+
+__device__ __forceinline__ float key_to_float(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// Entries [i0, i0 + 4) of row s as four floats (clamped to the row; the caller masks i >= n).
+__device__ __forceinline__ f32x4_t load4(const float* __restrict__ s, int i0, int n, bool vec) {
+  if (vec) return *reinterpret_cast<const f32x4_t*>(s + min(i0, (n - 1) & ~3));
+  return f32x4_t{s[min(i0, n - 1)], s[min(i0 + 1, n - 1)], s[min(i0 + 2, n - 1)],
+                 s[min(i0 + 3, n - 1)]};
+}
+
+// Keys per wave quarter: a multiple of 256, so every wave's blocks are whole 16-byte loads.
+__device__ __forceinline__ int st_quarter(int n) { return ((n + 1023) >> 10) << 8; }
+
+// f(i0, v) for every 256-entry block of this wave's range [r0, r1), in index order: lane l gets
+// entries i0 = block + 4 l .. i0 + 3 (the caller masks i >= r1), with kStUnroll 16-byte loads
+// per lane in flight.
+template <typename F>
+__device__ __forceinline__ void for_blocks(const float* __restrict__ s, int n, bool vec, int r0,
+                                           int r1, F&& f) {
+  const int lane = threadIdx.x & 63;
+  for (int b0 = r0; b0 < r1; b0 += 256 * kStUnroll) {
+    f32x4_t v[kStUnroll];
+#pragma unroll
+    for (int u = 0; u < kStUnroll; ++u) v[u] = load4(s, b0 + 256 * u + 4 * lane, n, vec);
+#pragma unroll
+    for (int u = 0; u < kStUnroll; ++u) {
+      if (b0 + 256 * u >= r1) break;  // wave-uniform
+      f(b0 + 256 * u + 4 * lane, v[u]);
+    }
+  }
+}
+
+// Exact whole-row select (step 4): tau and need by radix passes over the row re-read from L2,
+// then the selection in ascending index order.
+__device__ void stream_exact(const float* __restrict__ s, int n, int k, bool vec,
+                             int32_t* __restrict__ out, StShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int Lq = st_quarter(n), r0 = wv * Lq, r1 = min(n, r0 + Lq);
+  uint32_t kand = 0xffffffffu, kor = 0u;
+  for_blocks(s, n, vec, r0, r1, [&](int i0, const f32x4_t& v) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (i0 + j < r1) {
+        const uint32_t u = order_key(v[j]);
+        kand &= u;
+        kor |= u;
+      }
+  });
+  wave_and_or(kand, kor);
+  if (lane == 0) {
+    sh.sel.red_and[wv] = kand;
+    sh.sel.red_or[wv] = kor;
+  }
+  __syncthreads();
+  kand = 0xffffffffu;
+  kor = 0u;
+#pragma unroll
+  for (int w = 0; w < kStWaves; ++w) {
+    kand &= sh.sel.red_and[w];
+    kor |= sh.sel.red_or[w];
+  }
+  const uint32_t diff = kand ^ kor;
+  uint32_t prefix = kand, pmask = 0xffffffffu, need = (uint32_t)k;
+  if (diff != 0) {
+    const int top = 31 - __clz(diff);
+    pmask = top == 31 ? 0u : (~0u << (top + 1));
+    prefix = kand & pmask;
+    for (int hi = top; hi >= 0; hi -= 8) {
+      const int width = hi + 1 < 8 ? hi + 1 : 8;
+      const int shift = hi + 1 - width;
+      const uint32_t bmask = (1u << width) - 1u;
+      sh.hist[tid] = 0u;
+      __syncthreads();
+      for_blocks(s, n, vec, r0, r1, [&](int i0, const f32x4_t& v) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t u = order_key(v[j]);
+          if (i0 + j < r1 && (u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & bmask], 1u);
+        }
+      });
+      __syncthreads();
+      // thread t holds bin 255 - t: an inclusive scan from the top finds the need-th key's bin
+      const uint32_t c = sh.hist[255 - tid];
+      const uint32_t inc = wave_incl_scan(c);
+      if (lane == 63) sh.sel.wtot[wv] = inc;
+      __syncthreads();
+      uint32_t before = 0;
+#pragma unroll
+      for (int w = 0; w < kStWaves; ++w) before += w < wv ? sh.sel.wtot[w] : 0u;
+      const uint32_t hi_inc = before + inc;
+      if (hi_inc >= need && hi_inc - c < need) {
+        sh.bin = 255u - (uint32_t)tid;
+        sh.above = hi_inc - c;
+        sh.cnt = c;
+      }
+      __syncthreads();
+      prefix |= sh.bin << shift;
+      need -= sh.above;
+      pmask |= bmask << shift;
+      __syncthreads();  // sh.bin / sh.hist are rewritten by the next pass
+    }
+  }
+  const uint32_t tau = prefix;
+  // counts per wave quarter: entries above tau, entries equal to tau
+  uint32_t gt = 0, eq = 0;
+  for_blocks(s, n, vec, r0, r1, [&](int i0, const f32x4_t& v) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t u = order_key(v[j]);
+      gt += (i0 + j < r1 && u > tau) ? 1u : 0u;
+      eq += (i0 + j < r1 && u == tau) ? 1u : 0u;
+    }
+  });
+  gt = wave_incl_scan(gt);
+  eq = wave_incl_scan(eq);
+  if (lane == 63) {
+    sh.wcnt[wv] = gt;
+    sh.weq[wv] = eq;
+  }
+  __syncthreads();
+  uint32_t pos = 0, eq_before = 0;
+#pragma unroll
+  for (int w = 0; w < kStWaves; ++w) {
+    if (w < wv) {
+      const uint32_t e = sh.weq[w];
+      pos += sh.wcnt[w] + (e < need - min(need, eq_before) ? e : need - min(need, eq_before));
+      eq_before += e;
+    }
+  }
+  // ordered writes: every entry above tau, and tau-valued ones while fewer than need are taken
+  for_blocks(s, n, vec, r0, r1, [&](int i0, const f32x4_t& v) {
+    uint32_t take = 0, c = 0, e = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t u = order_key(v[j]);
+      const bool in = i0 + j < r1;
+      const bool isgt = in && u > tau, iseq = in && u == tau;
+      take |= (uint32_t)isgt << j;
+      take |= (uint32_t)iseq << (8 + j);
+      e += iseq ? 1u : 0u;
+    }
+    const uint32_t e_inc = wave_incl_scan(e);
+    uint32_t e_run = eq_before + e_inc - e;  // tau-valued entries of the row before this lane's
+    uint32_t sel = take & 0xfu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((take >> (8 + j)) & 1u) {
+        if (e_run < need) sel |= 1u << j;
+        ++e_run;
+      }
+    c = (uint32_t)__popc(sel);
+    const uint32_t c_inc = wave_incl_scan(c);
+    uint32_t o = pos + c_inc - c;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((sel >> j) & 1u) out[o++] = i0 + j;
+    pos += (uint32_t)__builtin_amdgcn_readlane((int)c_inc, 63);
+    eq_before += (uint32_t)__builtin_amdgcn_readlane((int)e_inc, 63);
+  });
+}
+
+__global__ __launch_bounds__(kStThreads) void topk_stream(
     const float* __restrict__ scores, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ seq_len, int T, int64_t qi0, int N, int m, int k,
     int32_t* __restrict__ idx) {
-  __shared__ SelShared<kTkWaves> sh;
-  const int tid = threadIdx.x;
+  __shared__ StShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t row = blockIdx.x;
   const int n = n_visible(q_pos[qi0 + row], m, N, seq_len, (int)((qi0 + row) / T));
   int32_t* __restrict__ out = idx + row * (int64_t)k;
   const float* __restrict__ s = scores + row * (int64_t)N;
   if (n <= k) {
-    for (int i = tid; i < k; i += kTkThreads) out[i] = i < n ? i : -1;
+    for (int i = tid; i < k; i += kStThreads) out[i] = i < n ? i : -1;
     return;
   }
-  uint32_t key[PER];
-  const int nv = load_keys<PER>(s, N, n, key);
-  uint32_t tau, need, cnt_eq;
-  block_threshold<kTkWaves, PER>(key, nv, (uint32_t)k, sh, tau, need, cnt_eq, (uint32_t)n);
-  uint32_t base, take_eq, nsel;
-  block_ranks<kTkWaves, PER>(key, nv, tau, need, sh, base, take_eq, nsel);
-  const int e0 = PER * tid;
-  const auto sel = select_mask<PER>(key, nv, tau, take_eq);
+  const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(s) & 15) == 0;
+  // 1. lo from the sample
+  uint32_t lo = 0u;
+  if (n > kStCap) {
+    // 64 runs of 32 consecutive entries (one 128-byte line each, 8 KB in all) spread evenly
+    // over the row; thread t reads 8 entries of run t / 4
+    uint32_t sk[kStSample / kStThreads];
+    static_assert(kStSample / kStThreads == 8, "two 16-byte loads per thread");
+    const int run0 = (int)(((int64_t)(tid >> 2) * n) / 64) & ~31;
+    const f32x4_t sv0 = load4(s, run0 + 8 * (tid & 3), n, vec);
+    const f32x4_t sv1 = load4(s, run0 + 8 * (tid & 3) + 4, n, vec);
 #pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if ((sel >> j) & 1) out[base + sel_rank(sel, j)] = e0 + j;
+    for (int j = 0; j < 4; ++j) {
+      sk[j] = order_key(sv0[j]);
+      sk[4 + j] = order_key(sv1[j]);
+    }
+    const float p = (float)k / (float)n;
+    const float mu = p * (float)kStSample;
+    const float rf = mu + 4.f * __builtin_sqrtf(mu * (1.f - p)) + 8.f;
+    if (rf < (float)kStSample) {
+      uint32_t need_s, eq_s;
+      block_threshold<kStWaves, kStSample / kStThreads>(sk, kStSample / kStThreads,
+                                                        (uint32_t)rf, sh.sel, lo, need_s, eq_s,
+                                                        (uint32_t)kStSample);
+    }
+  }
+  // keys up to order_key(-inf) are -inf or NaN images: lo there means "every entry"
+  const float lo_f = lo <= 0x007fffffu ? -__builtin_huge_valf() : key_to_float(lo);
+  // 2. the streaming pass: wave wv appends the candidates of its quarter in index order
+  const int Lq = st_quarter(n), r0 = wv * Lq, r1 = min(n, r0 + Lq);
+  uint32_t wc = 0;
+  uint32_t* ck = sh.ckey + wv * kStSeg;
+  int32_t* ci = sh.cidx + wv * kStSeg;
+  for_blocks(s, n, vec, r0, r1, [&](int i0, const f32x4_t& v) {
+    uint32_t bits = 0, c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool take = i0 + j < r1 && v[j] >= lo_f;
+      bits |= (uint32_t)take << j;
+      c += take ? 1u : 0u;
+    }
+    if (__ballot(c != 0) == 0) return;  // wave-uniform: no candidate in this block
+    const uint32_t inc = wave_incl_scan(c);
+    uint32_t o = wc + inc - c;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((bits >> j) & 1u) {
+        if (o < (uint32_t)kStSeg) {
+          ck[o] = order_key(v[j]);
+          ci[o] = i0 + j;
+        }
+        ++o;
+      }
+    wc += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  });
+  if (lane == 0) sh.wcnt[wv] = wc;
+  __syncthreads();
+  uint32_t total = 0, over = 0, off[kStWaves];
+#pragma unroll
+  for (int w = 0; w < kStWaves; ++w) {
+    off[w] = total;
+    total += sh.wcnt[w];
+    over |= sh.wcnt[w] > (uint32_t)kStSeg ? 1u : 0u;
+  }
+  if (over == 0u && total >= (uint32_t)k) {  // block-uniform
+    // 3. candidate c (concatenated order = index order) lives in wave segment w at c - off[w]
+    uint32_t kc[kStPC];
+    int phys[kStPC];
+    const int c0 = kStPC * tid;
+    const int nvc = max(0, min(kStPC, (int)total - c0));
+#pragma unroll
+    for (int j = 0; j < kStPC; ++j) {
+      const uint32_t c = (uint32_t)min(c0 + j, (int)total - 1);
+      int w = 0;
+#pragma unroll
+      for (int x = 1; x < kStWaves; ++x) w += c >= off[x] ? 1 : 0;
+      phys[j] = w * kStSeg + (int)(c - off[w]);
+      kc[j] = sh.ckey[phys[j]];
+    }
+    uint32_t tau, need, cnt_eq;
+    block_threshold<kStWaves, kStPC>(kc, nvc, (uint32_t)k, sh.sel, tau, need, cnt_eq, total);
+    uint32_t base, take_eq, nsel;
+    block_ranks<kStWaves, kStPC>(kc, nvc, tau, need, sh.sel, base, take_eq, nsel);
+    const auto sel = select_mask<kStPC>(kc, nvc, tau, take_eq);
+#pragma unroll
+    for (int j = 0; j < kStPC; ++j)
+      if ((sel >> j) & 1) out[base + sel_rank(sel, j)] = sh.cidx[phys[j]];
+    return;
+  }
+  __syncthreads();  // the fallback rewrites the shared state
+  stream_exact(s, n, k, vec, out, sh);
 }
 
 }  // namespace
@@ -446,22 +676,25 @@ hipError_t launch_topk(const Shape& s, int64_t qi0, int64_t nrows, const float* 
   if (nrows <= 0) return hipSuccess;
   // rows hold at most N visible entries
   const dim3 grid((unsigned)nrows);
-  if (s.N <= 8 * kTkThreads)
-    return launch(topk_radix_reg<8>, grid, kTkThreads, 0, st, scores, q_pos, seq_len, s.T, qi0, s.N, s.m,
-                  s.top_k, idx);
-  if (s.N <= 16 * kTkThreads)
-    return launch(topk_radix_reg<16>, grid, kTkThreads, 0, st, scores, q_pos, seq_len, s.T, qi0, s.N, s.m,
-                  s.top_k, idx);
   if (s.N <= kLdsMaxN)
-    return launch(topk_radix_reg<32>, grid, kTkThreads, 0, st, scores, q_pos, seq_len, s.T, qi0, s.N, s.m,
-                  s.top_k, idx);
+    return launch(topk_stream, grid, kStThreads, 0, st, scores, q_pos, seq_len, s.T, qi0, s.N,
+                  s.m, s.top_k, idx);
   const int G = (s.N + kLongChunk - 1) / kLongChunk;
   uint8_t* w = static_cast<uint8_t*>(ws);
   if (hipError_t e = launch(topk_long_filter, dim3((unsigned)G, (unsigned)nrows), kFiltThreads,
                             0, st, scores, q_pos, seq_len, s.T, qi0, s.N, s.m, s.top_k, G, w))
     return e;
   return launch(topk_long_select, grid, kTkThreads, 0, st, scores, q_pos, seq_len, s.T, qi0, s.N, s.m,
-                s.top_k, G, static_cast<const uint8_t*>(w), idx);
+                s.top_k, G, kLongChunk, 1, static_cast<const uint8_t*>(w), idx);
+}
+
+hipError_t launch_topk_segments(const Shape& s, int64_t qi0, int64_t nrows, const float* scores,
+                                const int32_t* q_pos, const int32_t* seq_len, int stride,
+                                int32_t* idx, const void* ws, hipStream_t st) {
+  if (nrows <= 0) return hipSuccess;
+  const int G = (s.N + kLongChunk - 1) / kLongChunk;
+  return launch(topk_long_select, dim3((unsigned)nrows), kTkThreads, 0, st, scores, q_pos, seq_len,
+                s.T, qi0, s.N, s.m, s.top_k, G, stride, 0, static_cast<const uint8_t*>(ws), idx);
 }
 
 }  // namespace dsa

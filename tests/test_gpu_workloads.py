@@ -209,7 +209,9 @@ def _plant_special_rows(wl):
       sequence 2: every weight zero (the whole row scores exactly 0: the first k are taken);
       sequence 3: every weight negative and the first 3000 keys zero (a tie at 0 across more
                   entries than k: the lowest zero-key indices are taken);
-      sequence 4: half of the weights -0.0, the rest negative (scores of -0 and +0 rank equal).
+      sequence 4: half of the weights -0.0, the rest negative (scores of -0 and +0 rank equal);
+      sequence 5 (bf16 keys): key s scaled by 1 + 3 s / N, so scores grow along the row and the
+                  top k crowd into its last entries.
     Sequences beyond B are skipped."""
     c = wl.cfg
     w = wl.w().copy()
@@ -231,6 +233,11 @@ def _plant_special_rows(wl):
     if c.B > 4:
         w[4] = -np.abs(w[4])
         w[4, :, : c.H_I // 2] = -0.0
+    if c.B > 5 and not isinstance(k, tuple):
+        f = (k[5].astype(np.uint32) << 16).view(np.float32)
+        f = f * (1.0 + 3.0 * np.arange(c.N, dtype=np.float32) / c.N)[:, None]
+        u = f.view(np.uint32)
+        k[5] = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)  # RNE to bf16
     wl._cache["w"] = np.ascontiguousarray(w, np.float32)
     wl._cache["k_I"] = k
 
@@ -294,6 +301,25 @@ def test_mixed_sign_weights_prefill_rows():
     c = synth.CONFIGS["decode"].with_(B=5, T=60, N=3500, pos0=100, pos_stride=57, top_k=1024,
                                       w_lo=-1.0, name="prefill_rows_mixed_w")
     _run_exact_selection(c, n_attend=12)
+
+
+def test_mixed_sign_weights_sampled_rows():
+    # 6 x 40 rows over 5000 .. 19430 visible entries (> 4096: the streaming top-k's sampled
+    # threshold; the planted rows of ties and the rising row take its exact fallback)
+    c = synth.CONFIGS["decode"].with_(B=6, T=40, N=20000, pos0=5000, pos_stride=370, top_k=1024,
+                                      w_lo=-1.0, name="sampled_rows_mixed_w")
+    _run_exact_selection(c, n_attend=10)
+
+
+@pytest.mark.parametrize("k_dt", ["mxfp4", "mxfp8"])
+def test_mixed_sign_weights_indexer_segments(k_dt):
+    # >= 2^20 keys per call over N > 32768 blocks: the decode indexer's epilogue writes the
+    # top-k's candidate segments itself (its chunks are interleaved, so ties at the threshold
+    # go through the exact fallback); visibility from 25000 to all 40000 blocks
+    c = synth.CONFIGS["csa_decode"].with_(B=5, T=6, N=40000, pos0=100003, pos_stride=12000, W=0,
+                                          n_raw=0, raw_base=0, k_dt=k_dt, w_lo=-1.0,
+                                          name=f"indexer_segments_{k_dt}_mixed_w")
+    _run_exact_selection(c, n_attend=6)
 
 
 def test_mixed_sign_weights_csa_decode_fp4():
