@@ -53,6 +53,12 @@ WORKLOAD_TEXT = {
     "prefill_fp8": "prefill DSA with an MXFP8 indexer (e4m3 q_I and k_I, one E8M0 scale per "
                    "32): 1 sequence, L=T=32768 causal, top-k 2048, 128 heads, key 576 / value "
                    "512 (bf16)",
+    "decode_kv8": "decode DSA over an MXFP8 latent KV cache (e4m3 entries, one E8M0 scale per "
+                  "32): B=16 x 1 query, context L=8192, indexer 64x128 (bf16), top-k 2048, "
+                  "sparse MQA-MLA 128 heads, key 576 / value 512, bf16 q and out",
+    "prefill_kv8": "prefill DSA over an MXFP8 latent KV cache (e4m3 entries, one E8M0 scale per "
+                   "32): 1 sequence, L=T=32768 causal, top-k 2048, 128 heads, key 576 / value "
+                   "512, bf16 q and out",
     "hca_decode": "HCA decode: B=4 x 1 query over 1,048,576 tokens compressed 128:1 (8192 blocks), "
                   "dense attention over every visible block + 128-token raw window, 128 heads, "
                   "key 576 / value 512 (bf16)",
@@ -143,6 +149,9 @@ def _algorithmic(cfg, name, split=False):
             win += max(0, hi - lo + 1)
     if name == "compress_mean":
         return B * N * cfg.m * cfg.D_K * esz + B * N * cfg.D_K * esz, 0.0
+    if name == "mxfp8_to_bf16":
+        # reads the MXFP8 cache (codes and scales), writes its bf16 copy
+        return B * N * (cfg.D_K + cfg.D_K // 32) + B * N * cfg.D_K * 2, 0.0
     if name.startswith("indexer"):
         # every key row a sequence's queries can see is read once per sequence (decode: per query)
         keys = B * max(nvis) if T > 1 else pairs
@@ -159,7 +168,8 @@ def _algorithmic(cfg, name, split=False):
         # each gathered row must cross HBM once per step: once per query at decode, but rows
         # shared by the queries of one sequence (prefill) count once
         rows_kv = min(sel, float(B * N)) + min(win, float(B * (T + cfg.W - 1)) if cfg.W else 0.0)
-        byt = rows_kv * cfg.D_K * esz + rows * cfg.H * cfg.D_K * esz
+        kv_row = cfg.D_K + cfg.D_K // 32 if cfg.kv_dt == "mxfp8" else cfg.D_K * esz
+        byt = rows_kv * kv_row + rows * cfg.H * cfg.D_K * esz
         if not cfg.dense:
             byt += rows * cfg.top_k * 4  # the index list (HCA has none)
         if name.startswith("attend_mfma") and _fused_topk(cfg):
@@ -175,7 +185,7 @@ def _algorithmic(cfg, name, split=False):
 def _src_sha(kernel):
     """Hash of the sources a kernel is built from (its file and the shared device headers)."""
     files = {"indexer": "indexer.hip", "topk": "topk.hip", "attend": "attend.hip",
-             "compress": "compress.hip"}
+             "compress": "compress.hip", "mxfp8": "compress.hip"}
     for k, f in files.items():
         if kernel.startswith(k):
             h = hashlib.sha1()
@@ -233,8 +243,13 @@ def _device_inputs(wl):
     raw = wl.kv_raw()
     t["kv_raw"] = _dev(raw) if raw is not None else None
     wl.drop("kv_raw")
-    t["kv"] = (torch.empty((c.B, c.N, c.D_K), dtype=tdt, device="cuda") if c.compress
-               else _dev(wl.kv()))
+    if c.compress:
+        t["kv"] = torch.empty((c.B, c.N, c.D_K), dtype=tdt, device="cuda")
+    elif c.kv_dt == "mxfp8":
+        codes, sc = wl.kv()
+        t["kv"] = (_dev(codes), _dev(sc))
+    else:
+        t["kv"] = _dev(wl.kv())
     wl.drop("kv")
     return t
 
@@ -348,7 +363,11 @@ def measure(name, steps, warmup, rotate=0, eager=False, copy_probe=False, n_inst
     # the attention splits its entry list
     split = dsa.workspace_bytes(d, dsa.OP_HCA if cfg.dense else dsa.OP_ATTEND) > 0
     per_chunk = _kernel_plan(cfg.with_(compress=False, B=1, T=chunk_rows), 2 if split else 1)
-    kernels = (["compress_mean"] if cfg.compress else []) + per_chunk * n_chunks
+    # an MXFP8 cache read by unsplit attention is expanded to bf16 once per call
+    mfma = cfg.D_K == 576 and cfg.D_V == 512 and cfg.H % 64 == 0
+    expand = cfg.kv_dt == "mxfp8" and mfma and not split
+    kernels = ((["compress_mean"] if cfg.compress else []) + (["mxfp8_to_bf16"] if expand else [])
+               + per_chunk * n_chunks)
 
     if copy_probe:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
@@ -471,7 +490,8 @@ def measure(name, steps, warmup, rotate=0, eager=False, copy_probe=False, n_inst
 
 # the per-config block: the other four workloads the performance targets are stated for, with
 # the steps each one times (decode-sized steps are short, so more of them)
-OTHER_CONFIGS = {"tiny": 200, "decode": 400, "csa_prefill": 20, "csa_decode": 400}
+OTHER_CONFIGS = {"tiny": 200, "decode": 400, "csa_prefill": 20, "csa_decode": 400,
+                 "decode_kv8": 400}
 
 
 def main():

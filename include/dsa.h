@@ -19,7 +19,8 @@
  *   [P4] Tencent Cloud developer search "compressed sparse attention (CSA)": compress -> index
  *        select -> core attention; window KV concatenated with compressed KV; average pooling.
  *   [P3] wiki.gxlh.xyz "sparse attention" tag page, GLM-5.3 summary (IndexShare: one index
- *        selection reused by several layers).
+ *        selection reused by several layers) and DeepSeek-V4.1-Flash summary (the main latent
+ *        KV cache stored in low precision).
  * The page's own index-score formula image is lost; the score used here is
  *   I[t,s] = sum_j w[t,j] * ReLU(q_I[t,j,:] . k_I[s,:]).
  *
@@ -102,6 +103,12 @@ typedef struct dsa_dims {
 #define DSA_OP_ATTEND 2
 #define DSA_OP_FORWARD 3
 #define DSA_OP_HCA 4
+/* The same calls over an MXFP8 latent cache (sparse_mla_attend_mxkv, dsa_forward / hca_forward
+ * with kv_scale != NULL): attention launches with many query rows (run unsplit) read a bf16
+ * copy of the whole cache the call first writes into the workspace (B*N*D_K*2 bytes more). */
+#define DSA_OP_ATTEND_MXKV 5
+#define DSA_OP_FORWARD_MXKV 6
+#define DSA_OP_HCA_MXKV 7
 /* hca_forward: compressed entries plus window rows one query attends over (N + W) */
 #define DSA_MAX_HCA_ENTRIES 10240
 
@@ -200,6 +207,22 @@ dsa_status sparse_mla_attend(const dsa_dims* d, dsa_dtype dt, const void* q, con
                              const float* sink, void* out, float* lse, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* Step 3 over a low-precision latent KV cache ([P3] V4.1-Flash summary: the main KV is kept
+ * quantised): the same attention as sparse_mla_attend with kv stored as MXFP8 (OCP MX: e4m3
+ * codes kv_codes [B,N,D_K] uint8, one E8M0 scale byte 2^(e-127) per 32 consecutive elements
+ * along D_K in kv_scale [B,N,D_K/32]). Entry e's row is K_e[d] = e4m3(code[d]) * 2^(scale[d/32]
+ * - 127), exact in bf16; q, kv_raw (window rows) and out are bf16, lse fp32. Needs D_K % 32 ==
+ * 0 and N * D_K < 2^32 (else DSA_ERR_SHAPE); other rules and the sink as for sparse_mla_attend
+ * with dt = BF16; ws: dsa_workspace_bytes(d, DSA_OP_ATTEND_MXKV) bytes. MFMA shapes (D_K = 576,
+ * D_V = 512, H % 64 == 0): calls with few query rows (split attention, decode) convert the rows
+ * they gather to bf16 inside the kernel; calls with many rows first expand the whole cache to
+ * bf16 in ws, then attend at bf16 speed. Other shapes take the scalar kernel. */
+dsa_status sparse_mla_attend_mxkv(const dsa_dims* d, const void* q, const uint8_t* kv_codes,
+                                  const uint8_t* kv_scale, const int32_t* idx, const void* kv_raw,
+                                  int64_t raw_base, int64_t n_raw, const int32_t* q_pos,
+                                  float softmax_scale, const float* sink, void* out, float* lse,
+                                  void* ws, size_t ws_bytes, void* stream);
+
 /* Arguments of dsa_forward (pointers as in the calls above). */
 typedef struct dsa_forward_args {
   dsa_dtype dt;          /* dtype of q_I, q, kv, kv_raw, out: F32 or BF16                 */
@@ -230,12 +253,17 @@ typedef struct dsa_forward_args {
                             segment of the chunk in prefill), [top-k,] attention[, split
                             combine]; the top-k is a kernel of its own unless the attention
                             selects the entries itself (MFMA shapes, N <= 32768, at most 128
-                            query rows per chunk: the decode case). */
+                            query rows per chunk: the decode case); for rows longer than 32768
+                            entries it is one kernel when the decode indexer with MX keys
+                            already wrote the candidate segments, else two. */
   int32_t n_events;
   const uint8_t* q_scale;/* NULL, or the E8M0 scales [B,T,H_I,D_I/32] of an MXFP8 q_I (then q_I
                             holds e4m3 codes [B,T,H_I,D_I]); indexer only                 */
   const int32_t* seq_len;/* [B] or NULL: entries held per sequence (ragged batch)           */
   const float* sink;     /* [H] or NULL: attention-sink logit per head (sparse_mla_attend)  */
+  const uint8_t* kv_scale;/* NULL, or the E8M0 scales [B,N,D_K/32] of an MXFP8 kv (then kv
+                            holds e4m3 codes [B,N,D_K]; dt == BF16, compress == 0), as in
+                            sparse_mla_attend_mxkv                                        */
 } dsa_forward_args;
 
 /* Fused path: [compress] -> indexer_scores -> topk_select -> sparse_mla_attend on `stream`

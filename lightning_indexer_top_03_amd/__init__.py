@@ -7,7 +7,7 @@ no fallback: without the built library the import fails.
 
 bf16 tensors are ``torch.bfloat16``; MX keys are pairs (codes uint8, MXFP4 [B,N,D_I/2] or MXFP8
 [B,N,D_I], scales uint8 [B,N,D_I/32]); an MXFP8 q_I is (codes [B,T,H_I,D_I], scales
-[B,T,H_I,D_I/32]).
+[B,T,H_I,D_I/32]); an MXFP8 latent KV cache is (codes [B,N,D_K], scales [B,N,D_K/32]).
 """
 from __future__ import annotations
 
@@ -30,10 +30,13 @@ _lib = ctypes.CDLL(LIB_PATH)
 F32, BF16, MXFP4, MXFP8 = 0, 1, 2, 3
 ERR_WORKSPACE, ERR_SCRATCH = 5, 8
 OP_TOPK, OP_ATTEND, OP_FORWARD, OP_HCA = 1, 2, 3, 4
+# the same calls over an MXFP8 latent cache (their workspace may hold a bf16 copy of it)
+OP_ATTEND_MXKV, OP_FORWARD_MXKV, OP_HCA_MXKV = 5, 6, 7
 
 EXPORTS = ("dsa_status_str", "dsa_version", "dsa_workspace_bytes", "kv_compress_mean",
            "kv_compress_blocks", "indexer_scores", "topk_select", "sparse_mla_attend",
-           "dsa_forward", "hca_forward", "dsa_forward_noalloc", "dsa_noalloc_scratch_bytes")
+           "sparse_mla_attend_mxkv", "dsa_forward", "hca_forward", "dsa_forward_noalloc",
+           "dsa_noalloc_scratch_bytes")
 
 
 class Dims(ctypes.Structure):
@@ -52,7 +55,7 @@ class ForwardArgs(ctypes.Structure):
                 ("scores", ctypes.c_void_p), ("idx", ctypes.c_void_p),
                 ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32),
                 ("q_scale", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
-                ("sink", ctypes.c_void_p)]
+                ("sink", ctypes.c_void_p), ("kv_scale", ctypes.c_void_p)]
 
 
 _vp, _i64, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
@@ -69,12 +72,15 @@ _lib.indexer_scores.argtypes = [_D, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, ctype
 _lib.topk_select.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.sparse_mla_attend.argtypes = [_D, ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
                                    ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.sparse_mla_attend_mxkv.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
+                                        ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.dsa_forward.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]
 _lib.hca_forward.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]
 _lib.dsa_forward_noalloc.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp]
 _lib.dsa_noalloc_scratch_bytes.restype = _sz
 for _f in ("kv_compress_mean", "kv_compress_blocks", "indexer_scores", "topk_select",
-           "sparse_mla_attend", "dsa_forward", "hca_forward", "dsa_forward_noalloc"):
+           "sparse_mla_attend", "sparse_mla_attend_mxkv", "dsa_forward", "hca_forward",
+           "dsa_forward_noalloc"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -213,24 +219,39 @@ def topk_select(scores: torch.Tensor, q_pos: torch.Tensor, top_k: int, m: int = 
 
 # ---- step 3 -----------------------------------------------------------------------------------
 
-def sparse_mla_attend(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor, q_pos: torch.Tensor,
+def _kv(kv):
+    """-> (kv or codes, scales or None); an MXFP8 cache is (codes [B,N,D_K], scales)."""
+    if isinstance(kv, tuple):
+        return kv[0], kv[1]
+    return kv, None
+
+
+def sparse_mla_attend(q: torch.Tensor, kv, idx: torch.Tensor, q_pos: torch.Tensor,
                       D_V: int, softmax_scale: float, kv_raw: Optional[torch.Tensor] = None,
                       raw_base: int = 0, W: int = 0, m: int = 1,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       want_lse: bool = True, sink: Optional[torch.Tensor] = None):
-    """q [B,T,H,D_K], kv [B,N,D_K], idx [B,T,k] int32, optional raw window rows kv_raw
-    [B,n_raw,D_K] at positions raw_base.., optional attention-sink logits sink [H] fp32 ->
-    (out [B,T,H,D_V], lse [B,T,H] fp32)."""
+    """q [B,T,H,D_K], kv [B,N,D_K] or MXFP8 (codes, scales), idx [B,T,k] int32, optional raw
+    window rows kv_raw [B,n_raw,D_K] at positions raw_base.., optional attention-sink logits
+    sink [H] fp32 -> (out [B,T,H,D_V], lse [B,T,H] fp32)."""
     B, T, H, D_K = q.shape
-    N = kv.shape[1]
+    kvt, kvs = _kv(kv)
+    N = kvt.shape[1]
     k = idx.shape[2]
     if out is None:
         out = torch.empty((B, T, H, D_V), dtype=q.dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
     d = dims(B=B, T=T, N=N, H=H, D_K=D_K, D_V=D_V, top_k=k, m=m, W=W)
-    ws = _workspace(d, OP_ATTEND, q.device)
+    ws = _workspace(d, OP_ATTEND if kvs is None else OP_ATTEND_MXKV, q.device)
     n_raw = 0 if kv_raw is None else kv_raw.shape[1]
+    if kvs is not None:
+        _check(_lib.sparse_mla_attend_mxkv(ctypes.byref(d), _ptr(q), _ptr(kvt), _ptr(kvs),
+                                           _ptr(idx), _ptr(kv_raw), raw_base, n_raw, _ptr(q_pos),
+                                           softmax_scale, _ptr(sink), _ptr(out), _ptr(lse),
+                                           _ptr(ws), 0 if ws is None else ws.numel(), _stream(q)),
+               "sparse_mla_attend_mxkv")
+        return out, lse
     _check(_lib.sparse_mla_attend(ctypes.byref(d), _dt(q), _ptr(q), _ptr(kv), _ptr(idx),
                                   _ptr(kv_raw), raw_base, n_raw, _ptr(q_pos), softmax_scale,
                                   _ptr(sink), _ptr(out), _ptr(lse), _ptr(ws),
@@ -260,14 +281,15 @@ class Forward:
         self.lse = lse if lse is not None else (
             torch.empty((B, T, H), dtype=torch.float32, device=dev) if want_lse else None)
         self.scores, self.idx = scores, idx
-        self.ws = _workspace(self.d, OP_FORWARD, dev)
-        self._keep = (qt, qs, w, kt, ks, q, kv, q_pos, kv_raw, seq_len, sink)
+        kvt, kvs = _kv(kv)
+        self.ws = _workspace(self.d, OP_FORWARD if kvs is None else OP_FORWARD_MXKV, dev)
+        self._keep = (qt, qs, w, kt, ks, q, kvt, kvs, q_pos, kv_raw, seq_len, sink)
         n_raw = 0 if kv_raw is None else kv_raw.shape[1]
         self.args = ForwardArgs(_dt(q), kdt, _ptr(qt), _ptr(w), _ptr(kt), _ptr(ks), _ptr(q),
-                                _ptr(kv), _ptr(kv_raw), raw_base, n_raw, 1 if compress else 0,
+                                _ptr(kvt), _ptr(kv_raw), raw_base, n_raw, 1 if compress else 0,
                                 _ptr(q_pos), softmax_scale, _ptr(self.out), _ptr(self.lse),
                                 _ptr(scores), _ptr(idx), None, 0, _ptr(qs), _ptr(seq_len),
-                                _ptr(sink))
+                                _ptr(sink), _ptr(kvs))
         self.device = dev
 
     def set_events(self, events) -> None:
@@ -323,20 +345,21 @@ class HcaForward(Forward):
                  kv_raw=None, raw_base: int = 0, compress: bool = False, out=None, lse=None,
                  want_lse: bool = True, seq_len=None, sink=None):
         B, T, H, D_K = q.shape
-        N = kv.shape[1]
+        kvt, kvs = _kv(kv)
+        N = kvt.shape[1]
         self.d = dims(B=B, T=T, N=N, H=H, D_K=D_K, D_V=D_V, m=m, W=W)
         dev = q.device
         self.out = out if out is not None else torch.empty((B, T, H, D_V), dtype=q.dtype, device=dev)
         self.lse = lse if lse is not None else (
             torch.empty((B, T, H), dtype=torch.float32, device=dev) if want_lse else None)
         self.scores = self.idx = None
-        self.ws = _workspace(self.d, OP_HCA, dev)
-        self._keep = (q, kv, q_pos, kv_raw, seq_len, sink)
+        self.ws = _workspace(self.d, OP_HCA if kvs is None else OP_HCA_MXKV, dev)
+        self._keep = (q, kvt, kvs, q_pos, kv_raw, seq_len, sink)
         n_raw = 0 if kv_raw is None else kv_raw.shape[1]
-        self.args = ForwardArgs(_dt(q), _dt(q), None, None, None, None, _ptr(q), _ptr(kv),
+        self.args = ForwardArgs(_dt(q), _dt(q), None, None, None, None, _ptr(q), _ptr(kvt),
                                 _ptr(kv_raw), raw_base, n_raw, 1 if compress else 0,
                                 _ptr(q_pos), softmax_scale, _ptr(self.out), _ptr(self.lse),
-                                None, None, None, 0, None, _ptr(seq_len), _ptr(sink))
+                                None, None, None, 0, None, _ptr(seq_len), _ptr(sink), _ptr(kvs))
         self.device = dev
 
     def run(self, stream: Optional[int] = None) -> torch.Tensor:

@@ -164,6 +164,23 @@ Shape hca_shape(const dsa_dims* d) {
   return s;
 }
 
+// An MXFP8 latent cache: whole scale blocks per row, and a sequence's code bytes addressable
+// with 32-bit offsets.
+bool mxkv_shape_ok(const dsa_dims* d) {
+  return d->D_K % 32 == 0 && (uint64_t)d->N * (uint64_t)d->D_K < (1ull << 32);
+}
+
+// An MXFP8 cache read by attention launches that each hold many query rows (rows query rows per
+// launch, the attention unsplit) is first expanded to bf16 in the workspace, once per call: the
+// bf16 kernel then gathers it at full speed, and the expansion costs one pass over the cache.
+// Few-row launches (decode) convert only the rows they gather, inside the attention kernel.
+// Returns the bytes of that bf16 copy (0 = none).
+size_t mxkv_expand_bytes(const Shape& s, const dsa_dims* d, int64_t rows_per_launch) {
+  if (!(s.D_K == 576 && s.D_V == 512 && s.H % 64 == 0)) return 0;  // scalar kernel: decodes itself
+  if (attend_splits(s, rows_per_launch, FMT_BF16) > 1) return 0;
+  return align_up((size_t)d->B * d->N * d->D_K * 2);
+}
+
 // Argument rules of dsa_forward (everything but the workspace).
 dsa_status check_forward(const dsa_dims* d, const dsa_forward_args* a) {
   if (dsa_status st = check_dims(d)) return st;
@@ -178,6 +195,9 @@ dsa_status check_forward(const dsa_dims* d, const dsa_forward_args* a) {
   if ((d->W > 0 || a->compress) && !a->kv_raw) return DSA_ERR_NULL;
   if (a->raw_base < 0 || a->n_raw < 0) return DSA_ERR_SHAPE;
   if (a->compress && (a->raw_base != 0 || a->n_raw / d->m != d->N)) return DSA_ERR_SHAPE;
+  // MXFP8 entries: bf16 q / kv_raw / out, stored (not compressed) entries, D_K % 32 == 0
+  if (a->kv_scale && (a->dt != DSA_BF16 || a->compress)) return DSA_ERR_DTYPE;
+  if (a->kv_scale && !mxkv_shape_ok(d)) return DSA_ERR_SHAPE;
   const void* ptrs16[] = {a->q_I, a->w, a->k_I, a->q, a->kv, a->out, a->kv_raw, a->scores,
                           a->idx};
   for (const void* p : ptrs16)
@@ -187,7 +207,14 @@ dsa_status check_forward(const dsa_dims* d, const dsa_forward_args* a) {
   return DSA_OK;
 }
 
-// The launches of dsa_forward on a validated call, with workspace ws (forward_layout bytes).
+// Workspace bytes of a validated dsa_forward call: the layout, plus the bf16 copy of an MXFP8
+// cache when its attention launches are unsplit.
+size_t forward_ws_need(const dsa_dims* d, const dsa_forward_args* a) {
+  const FwdLayout L = forward_layout(d, a->dt);
+  return L.total + (a->kv_scale ? mxkv_expand_bytes(to_shape(d), d, forward_chunk_rows(d)) : 0);
+}
+
+// The launches of dsa_forward on a validated call, with workspace ws (forward_ws_need bytes).
 dsa_status run_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, hipStream_t st) {
   const FwdLayout L = forward_layout(d, a->dt);
   const dsa_dtype qi_dt = a->q_scale != nullptr ? DSA_MXFP8 : a->dt;
@@ -206,6 +233,17 @@ dsa_status run_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, h
   const int64_t rows = (int64_t)d->B * d->T;
   const int64_t R = forward_chunk_rows(d);  // the attention workspace is sized for R rows
   const bool keep_scores = a->scores != nullptr;
+  // an MXFP8 cache read by unsplit attention launches: expanded to bf16 once, after the layout
+  const void* kv_att = a->kv;
+  const uint8_t* kv_sc = a->kv_scale;
+  if (kv_sc != nullptr && mxkv_expand_bytes(s, d, R) > 0) {
+    void* kv16 = wsb + L.total;
+    if (hipError_t e = launch_mxfp8_to_bf16(static_cast<const uint8_t*>(a->kv), kv_sc,
+                                            (int64_t)d->B * d->N, d->D_K, kv16, st))
+      return launched(e);
+    kv_att = kv16;
+    kv_sc = nullptr;
+  }
   for (int64_t q0 = 0; q0 < rows; q0 += R) {
     const int64_t nr = std::min(R, rows - q0);
     float* sc = keep_scores ? a->scores + (size_t)q0 * d->N : ws_scores;
@@ -229,7 +267,7 @@ dsa_status run_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, h
     }
     if (fused) {
       // top-k inside the attention kernel: idx is written only when the caller wants it
-      if (hipError_t e = launch_attend_fused(s, q0, nr, a->q, a->kv, sc,
+      if (hipError_t e = launch_attend_fused(s, q0, nr, a->q, kv_att, kv_sc, sc,
                                              a->idx ? a->idx + (size_t)q0 * d->top_k : nullptr,
                                              d->W > 0 ? a->kv_raw : nullptr, a->raw_base,
                                              a->n_raw, a->q_pos, a->seq_len, a->sink,
@@ -239,7 +277,7 @@ dsa_status run_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, h
       if (seg_stride == 0)
         if (hipError_t e = launch_topk(s, q0, nr, sc, a->q_pos, a->seq_len, ix, ws_topk, st))
           return launched(e);
-      if (hipError_t e = launch_attend(s, q0, nr, fmt, a->q, a->kv, ix,
+      if (hipError_t e = launch_attend(s, q0, nr, fmt, a->q, kv_att, kv_sc, ix,
                                        d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw,
                                        a->q_pos, nullptr, a->sink, a->softmax_scale, a->out,
                                        a->lse, ws_att, st))
@@ -269,13 +307,15 @@ const char* dsa_status_str(int status) {
   }
 }
 
-int dsa_version(void) { return 200; }
+int dsa_version(void) { return 210; }
 
 size_t dsa_workspace_bytes(const dsa_dims* d, int op) {
-  if (op == DSA_OP_HCA) {
+  if (op == DSA_OP_HCA || op == DSA_OP_HCA_MXKV) {
     if (check_hca_dims(d) != DSA_OK) return 0;
     const Shape s = hca_shape(d);
     const int64_t rows = (int64_t)d->B * d->T;
+    if (op == DSA_OP_HCA_MXKV)
+      return align_up(attend_ws_bytes(s, rows, FMT_BF16)) + mxkv_expand_bytes(s, d, rows);
     return std::max(attend_ws_bytes(s, rows, FMT_BF16), attend_ws_bytes(s, rows, FMT_F32));
   }
   if (check_dims(d) != DSA_OK) return 0;
@@ -287,6 +327,10 @@ size_t dsa_workspace_bytes(const dsa_dims* d, int op) {
       // the bf16 plan needs at least as much as the fp32 one
       return std::max(attend_ws_bytes(s, rows, FMT_BF16), attend_ws_bytes(s, rows, FMT_F32));
     case DSA_OP_FORWARD: return forward_layout(d, DSA_BF16).total;
+    case DSA_OP_ATTEND_MXKV:
+      return align_up(attend_ws_bytes(s, rows, FMT_BF16)) + mxkv_expand_bytes(s, d, rows);
+    case DSA_OP_FORWARD_MXKV:
+      return forward_layout(d, DSA_BF16).total + mxkv_expand_bytes(s, d, forward_chunk_rows(d));
     default: return 0;
   }
 }
@@ -371,16 +415,54 @@ dsa_status sparse_mla_attend(const dsa_dims* d, dsa_dtype dt, const void* q, con
   if (need && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return DSA_ERR_ALIGN;
   if (dsa_status st = check_device()) return st;
-  return launched(launch_attend(s, 0, (int64_t)d->B * d->T, fmt, q, kv, idx,
+  return launched(launch_attend(s, 0, (int64_t)d->B * d->T, fmt, q, kv, nullptr, idx,
                                 d->W > 0 ? kv_raw : nullptr, raw_base, n_raw, q_pos, nullptr,
                                 sink, softmax_scale, out, lse, ws, (hipStream_t)stream));
+}
+
+dsa_status sparse_mla_attend_mxkv(const dsa_dims* d, const void* q, const uint8_t* kv_codes,
+                                  const uint8_t* kv_scale, const int32_t* idx, const void* kv_raw,
+                                  int64_t raw_base, int64_t n_raw, const int32_t* q_pos,
+                                  float softmax_scale, const float* sink, void* out, float* lse,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  if (dsa_status st = check_dims(d)) return st;
+  if (dsa_status st = check_attend_shape(d)) return st;
+  if (!mxkv_shape_ok(d)) return DSA_ERR_SHAPE;
+  if (!q || !kv_codes || !kv_scale || !idx || !q_pos || !out) return DSA_ERR_NULL;
+  if (d->W > 0 && !kv_raw) return DSA_ERR_NULL;
+  if (raw_base < 0 || n_raw < 0) return DSA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(kv_codes) || !aligned16(out) ||
+      (kv_raw && !aligned16(kv_raw)) || !aligned4(sink))
+    return DSA_ERR_ALIGN;
+  const Shape s = to_shape(d);
+  const int64_t rows = (int64_t)d->B * d->T;
+  const size_t part = attend_ws_bytes(s, rows, FMT_BF16);
+  const size_t expand = mxkv_expand_bytes(s, d, rows);
+  const size_t need = (expand ? align_up(part) : part) + expand;
+  if (need && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return DSA_ERR_ALIGN;
+  if (dsa_status st = check_device()) return st;
+  hipStream_t st = (hipStream_t)stream;
+  const void* kv_att = kv_codes;
+  const uint8_t* kv_sc = kv_scale;
+  if (expand) {
+    void* kv16 = static_cast<char*>(ws) + align_up(part);
+    if (hipError_t e = launch_mxfp8_to_bf16(kv_codes, kv_scale, (int64_t)d->B * d->N, d->D_K,
+                                            kv16, st))
+      return launched(e);
+    kv_att = kv16;
+    kv_sc = nullptr;
+  }
+  return launched(launch_attend(s, 0, rows, FMT_BF16, q, kv_att, kv_sc, idx,
+                                d->W > 0 ? kv_raw : nullptr, raw_base, n_raw, q_pos, nullptr,
+                                sink, softmax_scale, out, lse, ws, st));
 }
 
 dsa_status dsa_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, size_t ws_bytes,
                        void* stream) {
   if (dsa_status st = check_forward(d, a)) return st;
   if (ws && !aligned16(ws)) return DSA_ERR_ALIGN;
-  if (!ws || ws_bytes < forward_layout(d, a->dt).total) return DSA_ERR_WORKSPACE;
+  if (!ws || ws_bytes < forward_ws_need(d, a)) return DSA_ERR_WORKSPACE;
   if (dsa_status st = check_device()) return st;
   return run_forward(d, a, ws, (hipStream_t)stream);
 }
@@ -389,7 +471,7 @@ size_t dsa_noalloc_scratch_bytes(void) { return DSA_NOALLOC_SCRATCH_BYTES; }
 
 dsa_status dsa_forward_noalloc(const dsa_dims* d, const dsa_forward_args* a, void* stream) {
   if (dsa_status st = check_forward(d, a)) return st;
-  if (forward_layout(d, a->dt).total > (size_t)DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_SCRATCH;
+  if (forward_ws_need(d, a) > (size_t)DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_SCRATCH;
   if (dsa_status st = check_device()) return st;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_DEVICE;
@@ -407,6 +489,8 @@ dsa_status hca_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
   if ((d->W > 0 || a->compress) && !a->kv_raw) return DSA_ERR_NULL;
   if (a->raw_base < 0 || a->n_raw < 0) return DSA_ERR_SHAPE;
   if (a->compress && (a->raw_base != 0 || a->n_raw / d->m != d->N)) return DSA_ERR_SHAPE;
+  if (a->kv_scale && (a->dt != DSA_BF16 || a->compress)) return DSA_ERR_DTYPE;
+  if (a->kv_scale && !mxkv_shape_ok(d)) return DSA_ERR_SHAPE;
   const Shape s = hca_shape(d);
   const int fmt = a->dt == DSA_BF16 ? FMT_BF16 : FMT_F32;
   if (fmt == FMT_F32 || !(s.D_K == 576 && s.D_V == 512 && s.H % 64 == 0)) {
@@ -420,7 +504,9 @@ dsa_status hca_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
     if (p && !aligned16(p)) return DSA_ERR_ALIGN;
   if (!aligned4(a->seq_len) || !aligned4(a->sink)) return DSA_ERR_ALIGN;
   const int64_t rows = (int64_t)d->B * d->T;
-  const size_t need = attend_ws_bytes(s, rows, fmt);
+  const size_t part = attend_ws_bytes(s, rows, fmt);
+  const size_t expand = a->kv_scale ? mxkv_expand_bytes(s, d, rows) : 0;
+  const size_t need = (expand ? align_up(part) : part) + expand;
   if (need && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
   if (a->n_events < 0) return DSA_ERR_SHAPE;
   if (dsa_status st = check_device()) return st;
@@ -430,7 +516,17 @@ dsa_status hca_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
     if (hipError_t e = launch_compress(d->B, a->n_raw, d->D_K, d->m, fmt, a->kv_raw, a->kv, st))
       return launched(e);
   }
-  return launched(launch_attend(s, 0, rows, fmt, a->q, a->kv, nullptr,
+  const void* kv_att = a->kv;
+  const uint8_t* kv_sc = a->kv_scale;
+  if (expand) {
+    void* kv16 = static_cast<char*>(ws) + align_up(part);
+    if (hipError_t e = launch_mxfp8_to_bf16(static_cast<const uint8_t*>(a->kv), kv_sc,
+                                            (int64_t)d->B * d->N, d->D_K, kv16, st))
+      return launched(e);
+    kv_att = kv16;
+    kv_sc = nullptr;
+  }
+  return launched(launch_attend(s, 0, rows, fmt, a->q, kv_att, kv_sc, nullptr,
                                 d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw, a->q_pos,
                                 a->seq_len, a->sink, a->softmax_scale, a->out, a->lse, ws, st));
 }

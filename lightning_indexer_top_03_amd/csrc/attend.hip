@@ -189,7 +189,7 @@ __device__ __forceinline__ float row16_max(float x) {
 // indexer scores; every workgroup of a row selects the row's top-k (block_threshold /
 // block_ranks of select.h, PER entries per thread, in ascending index order) and keeps its own
 // split's slice; the workgroup of split 0 / head group 0 also writes the row of idx_out.
-template <int NS, int PER>
+template <int NS, int PER, bool KV8>
 __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw, int64_t raw_base,
@@ -197,7 +197,8 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     float scale_log2, int64_t qi0, int nsplit, int per_split, uint16_t* __restrict__ out,
     float* __restrict__ lse, f16x4_t* __restrict__ part_o, float* __restrict__ part_ml,
     int nitems, const float* __restrict__ scores, int m, int32_t* __restrict__ idx_out,
-    const int32_t* __restrict__ seq_len, const float* __restrict__ sink) {
+    const int32_t* __restrict__ seq_len, const float* __restrict__ sink,
+    const uint8_t* __restrict__ kv_scale) {
   constexpr int DK = 576, DV = 512, KS = DK / 32, DB = DV / 16;
   __shared__ __attribute__((aligned(16))) char smem[NS * kStage];
   __shared__ __attribute__((aligned(16))) u32x4_t pbuf[2][4][64];  // P, per head block
@@ -206,6 +207,12 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
   __shared__ __attribute__((aligned(16))) uint32_t fbuf[2][4];
   __shared__ float sml[4][2][16];    // per head: [1] = the output multiplier (unsplit calls)
   extern __shared__ __attribute__((aligned(16))) int scode[];  // entry codes, whole tiles
+  // MXFP8 entries: the e4m3 codes of the next tile, 576 bytes per row, staged by DMA one
+  // iteration before they are converted into the ring
+  static_assert(!KV8 || NS == 3, "the MXFP8 staging buffer fits beside a 3-stage ring only");
+  __shared__ __attribute__((aligned(16))) char sf8[KV8 ? kTile * 576 : 16];
+  // ... and their E8M0 scale bytes, one per dword (a 1-byte DMA fills one dword per lane)
+  __shared__ __attribute__((aligned(16))) uint32_t sf8s[KV8 ? kTile * 18 : 4];
 
   // all kernel arguments in one scalar round trip (the compiler otherwise loads them lazily,
   // in several dependent batches)
@@ -364,16 +371,21 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
   uint32_t d_sbase = 0;
   uint64_t d_lat = 0;
   const uint16_t* d_rope = nullptr;
+  int d_code = -1, d_rcode = -1;
   auto prep = [&](int t) {
     d_sbase = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(lds_void_t*)(smem + (t % NS) * kStage));
     d_lat = rowaddr(nx_lat);
     d_rope = reinterpret_cast<const uint16_t*>(rowaddr(nx_rope));
+    d_code = nx_lat;
+    d_rcode = nx_rope;
   };
   // DMA r of the prepared tile: r < 8 the latent part of row vrow + r, r == 8 the rope parts
-  // of rows vrow .. vrow+7 (chunk c of row R at slot c ^ ((R >> 1) & 7))
+  // of rows vrow .. vrow+7 (chunk c of row R at slot c ^ ((R >> 1) & 7)). With MXFP8 entries
+  // only the raw window rows (bf16) come by DMA; the others are converted below.
   auto dma = [&](int r) {
     if (r < 8) {
+      if (KV8 && __builtin_amdgcn_readlane(d_code, r) > -2) return;
       const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)d_lat, r);
       const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(d_lat >> 32), r);
       const uint16_t* src = reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
@@ -381,6 +393,7 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
           reinterpret_cast<const void*>(src + 8 * lane),
           (lds_void_t*)(uintptr_t)(d_sbase + (vrow + r) * kLatStride), 16, 0, 0);
     } else {
+      if (KV8 && d_rcode > -2) return;
       const int R = vrow + (lane >> 3);
       __builtin_amdgcn_global_load_lds(
           reinterpret_cast<const void*>(d_rope + 512 + 8 * ((lane & 7) ^ ((R >> 1) & 7))),
@@ -388,6 +401,63 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     }
   };
   constexpr int kDmas = 9;
+  // MXFP8 entries (KV8): a value wave's 8 rows (4608 code bytes, 144 scale bytes) come by DMA
+  // into the staging buffers one iteration before they are needed (dma8); convert8 turns them
+  // into bf16 in the ring stage, in the layout of the DMA'd rows: unit j of lane l is
+  // u = l + 64 j, row u / 72, codes 8 (u % 72) .. +7 with the E8M0 scale of their 32-block.
+  // Raw window rows (bf16) take the DMA above; masked entries convert row 0 (finite; P is 0).
+  constexpr int kUnits = 9;
+  const uint8_t* kv8_b = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * N * DK;
+  const uint8_t* ksc_b = kv_scale + (size_t)b * N * (DK / 32);
+  const uint32_t f8base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(lds_void_t*)(sf8 + (KV8 ? vrow * 576 : 0)));
+  const uint32_t f8sbase = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(lds_void_t*)(sf8s + (KV8 ? vrow * 18 : 0)));
+  auto dma8 = [&](int codes) {  // lanes 0..7 of `codes`: the entry codes of rows vrow + 0..7
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {  // 288 chunks of 16 code bytes
+      const int ch = 64 * k + lane, rr = ch / 36, cc = ch - 36 * rr;
+      const int code = __shfl(codes, min(rr, 7), 64);
+      if (ch < 288 && code > -2)
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(kv8_b + ((uint32_t)max(code, 0) * (uint32_t)DK + 16u * (uint32_t)cc)),
+            (lds_void_t*)(uintptr_t)(f8base + 1024 * k), 16, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {  // 144 scale bytes, one dword each
+      const int u = 64 * k + lane, rr = u / 18, sidx = u - 18 * rr;
+      const int code = __shfl(codes, min(rr, 7), 64);
+      if (u < 144 && code > -2)
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(ksc_b + ((uint32_t)max(code, 0) * (uint32_t)(DK / 32) + (uint32_t)sidx)),
+            (lds_void_t*)(uintptr_t)(f8sbase + 256 * k), 1, 0, 0);
+    }
+  };
+  auto convert8 = [&](char* st) {  // d_code: the entry codes of the tile being converted
+    const char* src = sf8 + (KV8 ? vrow * 576 : 0);
+    const uint32_t* ssrc = sf8s + (KV8 ? vrow * 18 : 0);
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+      const int u = lane + 64 * j, rr = u / 72, c = u - 72 * rr, R = vrow + rr;
+      if (__shfl(d_code, rr, 64) > -2) {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src + rr * 576 + 8 * c);
+        const uint32_t e = ssrc[rr * 18 + (c >> 2)] & 0xffu;
+        // E8M0 e -> 2^(e - 127) (e == 0 is the subnormal 2^-127)
+        const float sc = __uint_as_float(e != 0u ? e << 23 : 0x00400000u);
+        const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, false);
+        const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, true);
+        const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, false);
+        const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, true);
+        const u32x4_t v = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+        const uint32_t off = c < 64 ? R * kLatStride + 16 * c
+                                    : kStageLat + R * 128 + 16 * ((c - 64) ^ ((R >> 1) & 7));
+        *reinterpret_cast<u32x4_t*>(st + off) = v;
+      }
+    }
+    // the staging reads are done before the next dma8 overwrites the buffers
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
   auto issue_all = [&]() {
     if (!score_wave)
 #pragma unroll
@@ -397,8 +467,20 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
   // during iteration i (into the stage the value waves finished with in iteration i-1)
 #pragma unroll
   for (int t = 0; t < NS - 2; ++t)
-    if (t < ntiles) { fetch(t); prep(t); issue_all(); }
+    if (t < ntiles) {
+      fetch(t);
+      prep(t);
+      issue_all();
+      if constexpr (KV8)
+        if (!score_wave) {
+          dma8(d_code);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          convert8(smem + (t % NS) * kStage);
+        }
+    }
   if (NS - 2 < ntiles) fetch(NS - 2);
+  if constexpr (KV8)
+    if (!score_wave && NS - 2 < ntiles) dma8(nx_lat);  // the next tile's codes into staging
   // top of iteration i: wait until tile i has landed (tiles i+1 .. i+NS-3 may be in flight),
   // barrier, then form the addresses of tile i + NS - 2; returns whether its DMAs are due in
   // this iteration
@@ -574,11 +656,20 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     for (int d = 0; d < DH; ++d) acc[k][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // transposed V reads: entry 4g + n/4 (and 16 rows on), column 256*dh + 16d + 4*(n%4)
   const uint32_t voff = (4 * g + (n >> 2)) * kLatStride + 512 * dh + 8 * (n & 3);
+  // KV8, iteration i (ring_top has waited for every DMA of this wave and prepared tile
+  // i + NS - 2): convert that tile's staged codes into its stage, then stage the codes of the
+  // tile after it (whose entry codes fetch() read into nx_lat)
+  auto kv8_phase1 = [&](int i) {
+    convert8(smem + ((i + NS - 2) % NS) * kStage);
+    if (i + NS - 1 < ntiles) dma8(nx_lat);
+  };
   for (int i = 0; i <= ntiles; ++i) {
     // the value waves issue their DMAs while the score waves' S MFMAs run; P, the moved flags
     // and the rescale factors are read first, so their LDS round trip hides under the issue
     const bool due = ring_top(i);
     if (i == 0) {
+      if constexpr (KV8)
+        if (due) kv8_phase1(i);
       if (due) issue_all();
       mid_barrier();
       continue;
@@ -590,6 +681,8 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     const f32x4_t alpha[2] = {*reinterpret_cast<const f32x4_t*>(&abuf[t & 1][hb0][4 * g]),
                               *reinterpret_cast<const f32x4_t*>(&abuf[t & 1][hb0 + 1][4 * g])};
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (KV8)
+      if (due) kv8_phase1(i);
     if (due) issue_all();
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -767,18 +860,38 @@ __device__ __forceinline__ float ldv(const T* p, size_t i) {
     return p[i];
 }
 
+// One OCP E4M3 (E4M3FN) code: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0
+// holds the subnormals m/8 * 2^-6; 0x7F / 0xFF are NaN.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, mt = c & 7u;
+  float v = e == 0u ? (float)mt * 0.001953125f                        // m/8 * 2^-6
+                    : __uint_as_float(((e + 120u) << 23) | (mt << 20));  // (1 + m/8) 2^(e-7)
+  if (e == 15u && mt == 7u) v = __builtin_nanf("");
+  return (c & 0x80u) ? -v : v;
+}
+
+// E8M0 scale byte e -> 2^(e - 127) (e == 0: the subnormal 2^-127; 0xFF is NaN)
+__device__ __forceinline__ float e8m0_value(uint32_t e) {
+  if (e == 255u) return __builtin_nanf("");
+  return __uint_as_float(e != 0u ? e << 23 : 0x00400000u);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void attend_generic(
     const T* __restrict__ q, const T* __restrict__ kv, const int32_t* __restrict__ idx,
     const T* __restrict__ kv_raw, int64_t raw_base, int64_t n_raw,
     const int32_t* __restrict__ q_pos, int T_, int N, int H, int DK, int DV, int top_k, int W,
     float scale, int64_t qi0, T* __restrict__ out, float* __restrict__ lse, int m,
-    const int32_t* __restrict__ seq_len, const float* __restrict__ sink) {
+    const int32_t* __restrict__ seq_len, const float* __restrict__ sink,
+    const uint8_t* __restrict__ kv_scale) {
+  // kv_scale != nullptr: kv holds MXFP8 entries (e4m3 codes [B, N, DK] as bytes, E8M0 scales
+  // [B, N, DK / 32]); kv_raw rows stay in T
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int E = top_k + W;
   float* sq = reinterpret_cast<float*>(smem);   // [DK]
   float* sz = sq + DK;                           // [E]
   const T** ssrc = reinterpret_cast<const T**>(sz + E + ((E & 1) ? 1 : 0));  // [E]
+  int* srow8 = reinterpret_cast<int*>(ssrc + E);  // [E]: MXFP8 entry row, or -1
   __shared__ float red[256 / 64];
   const int h = blockIdx.x;
   const int64_t row = blockIdx.y;
@@ -789,15 +902,34 @@ __global__ __launch_bounds__(256) void attend_generic(
   const int lim = idx != nullptr ? N : n_visible(p, m, N, seq_len, b);
   for (int d = threadIdx.x; d < DK; d += blockDim.x) sq[d] = ldv(q, ((size_t)qi * H + h) * DK + d);
   __syncthreads();
+  const uint8_t* kv8 = reinterpret_cast<const uint8_t*>(kv);
   float mx = kNegInf;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const T* src = entry_row<T>(e, idxrow, top_k, kv, b, N, DK, kv_raw, raw_base, n_raw, p, W, lim);
+    int r8 = -1;
+    if (kv_scale != nullptr && src != nullptr && e < top_k) {
+      // an entry of kv: its row, read below as codes and scales
+      r8 = (int)((src - kv) / DK);
+      src = nullptr;
+    }
     ssrc[e] = src;
+    srow8[e] = r8;
     float z = kNegInf;
     if (src) {
       float dot = 0.f;
 #pragma unroll 8
       for (int d = 0; d < DK; ++d) dot += sq[d] * ldv(src, d);  // 8 loads in flight at a time
+      z = dot * scale;
+    } else if (r8 >= 0) {
+      const uint8_t* c8 = kv8 + (size_t)r8 * DK;
+      const uint8_t* s8 = kv_scale + (size_t)r8 * (DK / 32);
+      float dot = 0.f;
+      for (int d0 = 0; d0 < DK; d0 += 32) {
+        float blk = 0.f;
+#pragma unroll 8
+        for (int d = d0; d < d0 + 32; ++d) blk += sq[d] * e4m3_value(c8[d]);
+        dot += blk * e8m0_value(s8[d0 / 32]);
+      }
       z = dot * scale;
     }
     sz[e] = z;
@@ -826,8 +958,14 @@ __global__ __launch_bounds__(256) void attend_generic(
   for (int d = threadIdx.x; d < DV; d += blockDim.x) {
     float a = 0.f;
 #pragma unroll 8
-    for (int e = 0; e < E; ++e)
-      if (ssrc[e]) a += sz[e] * ldv(ssrc[e], d);
+    for (int e = 0; e < E; ++e) {
+      if (ssrc[e]) {
+        a += sz[e] * ldv(ssrc[e], d);
+      } else if (srow8[e] >= 0) {
+        const size_t r8 = (size_t)srow8[e];
+        a += sz[e] * (e4m3_value(kv8[r8 * DK + d]) * e8m0_value(kv_scale[r8 * (DK / 32) + d / 32]));
+      }
+    }
     a *= inv;
     if constexpr (sizeof(T) == 2)
       out[((size_t)qi * H + h) * DV + d] = f32_to_bf16(a);
@@ -870,25 +1008,28 @@ size_t attend_ws_bytes(const Shape& s, int64_t nrows, int fmt) {
 // buffers), set as each kernel's attribute on every device it runs on, once per device.
 struct AttendLds {
   hipError_t err;
-  size_t dyn4, dyn3;
+  size_t dyn4, dyn3, dyn3_kv8;
 };
 
 static const AttendLds& attend_lds() {
   constexpr size_t kLdsMax = 160 * 1024;
   static AttendLds per_dev[64];
   static std::once_flag once[64];
-  static const AttendLds bad{hipErrorInvalidDevice, 0, 0};
+  static const AttendLds bad{hipErrorInvalidDevice, 0, 0, 0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return bad;
   std::call_once(once[dev], [dev] {
     AttendLds& r = per_dev[dev];
     r.err = hipSuccess;
-    const void* k4[] = {reinterpret_cast<const void*>(&attend_mfma_dma<4, 0>),
-                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 16>),
-                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 64>)};
-    const void* k3[] = {reinterpret_cast<const void*>(&attend_mfma_dma<3, 0>),
-                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 16>),
-                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 64>)};
+    const void* k4[] = {reinterpret_cast<const void*>(&attend_mfma_dma<4, 0, false>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 16, false>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 64, false>)};
+    const void* k3[] = {reinterpret_cast<const void*>(&attend_mfma_dma<3, 0, false>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 16, false>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 64, false>)};
+    const void* k3x[] = {reinterpret_cast<const void*>(&attend_mfma_dma<3, 0, true>),
+                         reinterpret_cast<const void*>(&attend_mfma_dma<3, 16, true>),
+                         reinterpret_cast<const void*>(&attend_mfma_dma<3, 64, true>)};
     auto room = [&](const void* const* ks, size_t& dyn) {
       dyn = kLdsMax;
       for (int j = 0; j < 3 && r.err == hipSuccess; ++j) {
@@ -902,6 +1043,7 @@ static const AttendLds& attend_lds() {
     };
     room(k4, r.dyn4);
     room(k3, r.dyn3);
+    room(k3x, r.dyn3_kv8);
   });
   return per_dev[dev];
 }
@@ -909,7 +1051,8 @@ static const AttendLds& attend_lds() {
 // The MFMA attention for rows qi0 .. qi0+nrows-1 (+ the split merge). scores != nullptr selects
 // the fused top-k variant (entries straight from the indexer scores, idx_out optional).
 static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows, const void* q,
-                                     const void* kv, const int32_t* idx, const float* scores,
+                                     const void* kv, const uint8_t* kv_scale,
+                                     const int32_t* idx, const float* scores,
                                      int32_t* idx_out, const void* kv_raw, int64_t raw_base,
                                      int64_t n_raw, const int32_t* q_pos,
                                      const int32_t* seq_len, const float* sink, float scale,
@@ -931,13 +1074,20 @@ static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows,
   const int per_thread = scores == nullptr ? 0 : (s.N <= 16 * kAtWaves * 64 ? 16 : 64);
   if (scores != nullptr && s.N > 64 * kAtWaves * 64) return hipErrorInvalidValue;
   hipError_t e;
-#define DSA_ATT(NS_, PER_)                                                                       \
-  e = launch(attend_mfma_dma<NS_, PER_>, grid, kAtWaves * 64, code_bytes, st,                    \
+#define DSA_ATT2(NS_, PER_, KV8_)                                                                \
+  e = launch(attend_mfma_dma<NS_, PER_, KV8_>, grid, kAtWaves * 64, code_bytes, st,              \
              static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,             \
              static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H,        \
              s.top_k, s.W, scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse,       \
-             part_o, part_ml, nitems, scores, s.m, idx_out, seq_len, sink)
-  if (code_bytes <= lds.dyn4) {
+             part_o, part_ml, nitems, scores, s.m, idx_out, seq_len, sink, kv_scale)
+#define DSA_ATT(NS_, PER_) DSA_ATT2(NS_, PER_, false)
+  if (kv_scale != nullptr) {
+    // MXFP8 entries: the 3-stage ring beside the code staging buffer
+    if (code_bytes > lds.dyn3_kv8) return hipErrorInvalidValue;
+    if (per_thread == 0) DSA_ATT2(3, 0, true);
+    else if (per_thread == 16) DSA_ATT2(3, 16, true);
+    else DSA_ATT2(3, 64, true);
+  } else if (code_bytes <= lds.dyn4) {
     if (per_thread == 0) DSA_ATT(4, 0);
     else if (per_thread == 16) DSA_ATT(4, 16);
     else DSA_ATT(4, 64);
@@ -949,6 +1099,7 @@ static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows,
     return hipErrorInvalidValue;
   }
 #undef DSA_ATT
+#undef DSA_ATT2
   if (e != hipSuccess || ns == 1) return e;
   return launch(attend_combine, dim3(16, s.H / 64, (unsigned)nrows), 256, 0, st, part_o, part_ml,
                 qi0, s.H, ns, static_cast<uint16_t*>(out), lse, (int)(16 * (s.H / 64) * nrows),
@@ -965,37 +1116,38 @@ bool attend_fused_ok(const Shape& s, int fmt, int64_t nrows) {
 }
 
 hipError_t launch_attend_fused(const Shape& s, int64_t qi0, int64_t nrows, const void* q,
-                               const void* kv, const float* scores, int32_t* idx_out,
-                               const void* kv_raw, int64_t raw_base, int64_t n_raw,
-                               const int32_t* q_pos, const int32_t* seq_len, const float* sink,
-                               float scale, void* out, float* lse, void* ws, hipStream_t st) {
+                               const void* kv, const uint8_t* kv_scale, const float* scores,
+                               int32_t* idx_out, const void* kv_raw, int64_t raw_base,
+                               int64_t n_raw, const int32_t* q_pos, const int32_t* seq_len,
+                               const float* sink, float scale, void* out, float* lse, void* ws,
+                               hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   if (!attend_fused_ok(s, FMT_BF16, nrows)) return hipErrorInvalidValue;
-  return launch_attend_mfma(s, qi0, nrows, q, kv, nullptr, scores, idx_out, kv_raw, raw_base,
-                            n_raw, q_pos, seq_len, sink, scale, out, lse, ws, st);
+  return launch_attend_mfma(s, qi0, nrows, q, kv, kv_scale, nullptr, scores, idx_out, kv_raw,
+                            raw_base, n_raw, q_pos, seq_len, sink, scale, out, lse, ws, st);
 }
 
 hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, const void* q,
-                         const void* kv, const int32_t* idx, const void* kv_raw, int64_t raw_base,
-                         int64_t n_raw, const int32_t* q_pos, const int32_t* seq_len,
-                         const float* sink, float scale, void* out, float* lse, void* ws,
-                         hipStream_t st) {
+                         const void* kv, const uint8_t* kv_scale, const int32_t* idx,
+                         const void* kv_raw, int64_t raw_base, int64_t n_raw,
+                         const int32_t* q_pos, const int32_t* seq_len, const float* sink,
+                         float scale, void* out, float* lse, void* ws, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   if (mfma_ok(s, fmt))
-    return launch_attend_mfma(s, qi0, nrows, q, kv, idx, nullptr, nullptr, kv_raw, raw_base,
-                              n_raw, q_pos, seq_len, sink, scale, out, lse, ws, st);
+    return launch_attend_mfma(s, qi0, nrows, q, kv, kv_scale, idx, nullptr, nullptr, kv_raw,
+                              raw_base, n_raw, q_pos, seq_len, sink, scale, out, lse, ws, st);
   const int E = s.top_k + s.W;
-  size_t shm = sizeof(float) * (s.D_K + E + 1) + sizeof(void*) * E + 16;
+  size_t shm = sizeof(float) * (s.D_K + E + 1) + sizeof(void*) * E + sizeof(int) * E + 16;
   dim3 grid(s.H, (unsigned)nrows);
   if (fmt == FMT_BF16)
     return launch(attend_generic<uint16_t>, grid, 256, shm, st, static_cast<const uint16_t*>(q),
                   static_cast<const uint16_t*>(kv), idx, static_cast<const uint16_t*>(kv_raw),
                   raw_base, n_raw, q_pos, s.T, s.N, s.H, s.D_K, s.D_V, s.top_k, s.W, scale, qi0,
-                  static_cast<uint16_t*>(out), lse, s.m, seq_len, sink);
+                  static_cast<uint16_t*>(out), lse, s.m, seq_len, sink, kv_scale);
   return launch(attend_generic<float>, grid, 256, shm, st, static_cast<const float*>(q),
                 static_cast<const float*>(kv), idx, static_cast<const float*>(kv_raw), raw_base,
                 n_raw, q_pos, s.T, s.N, s.H, s.D_K, s.D_V, s.top_k, s.W, scale, qi0,
-                static_cast<float*>(out), lse, s.m, seq_len, sink);
+                static_cast<float*>(out), lse, s.m, seq_len, sink, kv_scale);
 }
 
 }  // namespace dsa

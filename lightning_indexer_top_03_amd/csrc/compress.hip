@@ -9,6 +9,10 @@
 // j0 .. j0 + nc - 1 of every sequence (all of them for a whole cache; the newest one when a
 // decoder appends a block every m tokens); kv_raw holds raw_stride rows per sequence and kv_c
 // c_stride entries.
+//
+// mxfp8_to_bf16 expands an MXFP8 latent cache (the V4.1-Flash summary on the "sparse attention"
+// tag page: the main KV kept in low precision) to bf16 for attention calls with many query rows,
+// which then read the cache at bf16 speed; it is HBM-bound the same way.
 #include "common.h"
 #include "launch.h"
 
@@ -62,7 +66,36 @@ __global__ __launch_bounds__(256) void compress_mean_f32(const float* __restrict
       f32x4_t{acc[0] / fm, acc[1] / fm, acc[2] / fm, acc[3] / fm};
 }
 
+// An MXFP8 latent cache expanded to bf16 (exact: e4m3 x 2^(e-127) fits bf16): thread i takes
+// codes 8i .. 8i+7 of the flattened [rows, D] codes and their E8M0 scale (one per 32 codes).
+__global__ __launch_bounds__(256) void mxfp8_to_bf16(const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales, int D,
+                                                     int64_t units, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= units) return;
+  const int64_t per_row = D / 8;
+  const int64_t row = i / per_row, u = i - row * per_row;
+  const u32x2_t w = *reinterpret_cast<const u32x2_t*>(codes + 8 * i);
+  const uint32_t e = scales[row * (D / 32) + u / 4];
+  const float sc = __uint_as_float(e != 0u ? e << 23 : 0x00400000u);  // 2^(e-127)
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, false);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, true);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, false);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, true);
+  *reinterpret_cast<u32x4_t*>(out + 8 * i) =
+      u32x4_t{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+              __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+}
+
 }  // namespace
+
+hipError_t launch_mxfp8_to_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int D,
+                                void* out, hipStream_t st) {
+  const int64_t units = rows * (D / 8);
+  if (units <= 0) return hipSuccess;
+  return launch(mxfp8_to_bf16, (unsigned)((units + 255) / 256), 256, 0, st, codes, scales, D,
+                units, static_cast<uint16_t*>(out));
+}
 
 hipError_t launch_compress_blocks(int B, int D, int m, int fmt, const void* kv_raw,
                                   int64_t raw_stride, void* kv_c, int64_t c_stride, int64_t j0,

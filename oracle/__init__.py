@@ -206,12 +206,22 @@ def topk_row(scores: np.ndarray, n_visible: int, k: int) -> Tuple[np.ndarray, in
 def attend_row(q: np.ndarray, kv: Optional[np.ndarray], idx: np.ndarray, D_V: int, scale: float,
                p: int = 0, W: int = 0, kv_raw: Optional[np.ndarray] = None, raw_base: int = 0,
                sink: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """One query: q [H, D_K], kv [N, D_K] (f32/bf16/f64), idx [k] (-1 = none), raw window rows
+    """One query: q [H, D_K], kv [N, D_K] (f32/bf16/f64) or MXFP8 (codes, scales), idx [k]
+    (-1 = none), raw window rows
     kv_raw [n_raw, D_K] at positions raw_base.., optional sink logits [H] (fp32 values) ->
     (out [H, D_V] fp64, lse [H] fp64)."""
     q = np.ascontiguousarray(q)
     H, D_K = q.shape
     idx = np.ascontiguousarray(idx, np.int32)
+    if isinstance(kv, tuple):
+        # an MXFP8 cache (codes [N, D_K], scales [N, D_K/32]): the referenced rows decoded
+        # exactly (e4m3 x 2^(e-127)); the entry set and so the softmax are order-free
+        codes, scales = kv
+        sel = idx[idx >= 0]
+        rows = decode_mxfp8(codes[sel], scales[sel]) if sel.size else np.zeros((1, D_K))
+        remap = np.full(idx.shape, -1, np.int32)
+        remap[idx >= 0] = np.arange(sel.size, dtype=np.int32)
+        kv, idx = rows, remap
     if kv is None:
         kv = np.zeros((1, D_K), np.float64)
         assert (idx < 0).all()
@@ -266,7 +276,10 @@ class QueryRunner:
             if b not in self._kvc:
                 self._kvc[b] = compress_mean(self.wl.kv_raw()[b], c.m)
             return self._kvc[b]
-        return self.wl.kv()[b]
+        kv = self.wl.kv()
+        if isinstance(kv, tuple):
+            return kv[0][b], kv[1][b]
+        return kv[b]
 
     def raw_b(self, b: int):
         raw = self.wl.kv_raw()

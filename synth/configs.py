@@ -21,6 +21,8 @@ Recipes (all seeded; seed = workload id, "sharp" variants use seed 100 + id):
             saturating at 448)
   hca_prefill  raw 131072 tokens (kv_raw ~ N(0,1)/24) -> m=128 -> N=1024 blocks; last 8192
             queries (positions 122880..131071); W=128
+  decode_kv8 / prefill_kv8   decode / prefill over an MXFP8 latent KV cache: the same
+            N(0,1)/24 entries quantised to e4m3 with one E8M0 scale per 32 elements (as above)
   sharp variants: q, kv ~ N(0,1) and softmax scale 4/sqrt(D_K), so that attention outputs are
             O(1) and a wrong gather moves them by far more than the tolerance.
   sink = (lo, hi): one attention-sink logit per head, U(lo, hi), fp32, tensor id 7.
@@ -59,6 +61,7 @@ class Config:
     dt: str = "bf16"          # dtype of q_I, q, kv, kv_raw, out
     k_dt: str = "bf16"        # dtype of k_I: dt, "mxfp4" or "mxfp8"
     qi_dt: str = ""           # dtype of q_I: dt ("" ) or "mxfp8"
+    kv_dt: str = ""           # dtype of the stored entries kv: dt ("") or "mxfp8" (bf16 q / out)
     pos0: int = 0             # q_pos[b, t] = pos0 + pos_stride * t
     pos_stride: int = 1
     qkv_std: float = 0.0      # std of q and kv rows (0 -> 1/sqrt(D_K))
@@ -127,6 +130,10 @@ CONFIGS: Dict[str, Config] = {
                          D_V=512, top_k=2048, pos0=8191, qi_dt="mxfp8", k_dt="mxfp8"),
     "prefill_fp8": Config("prefill_fp8", 9, B=1, T=32768, N=32768, H_I=64, D_I=128, H=128,
                           D_K=576, D_V=512, top_k=2048, pos0=0, qi_dt="mxfp8", k_dt="mxfp8"),
+    "decode_kv8": Config("decode_kv8", 10, B=16, T=1, N=8192, H_I=64, D_I=128, H=128, D_K=576,
+                         D_V=512, top_k=2048, pos0=8191, kv_dt="mxfp8"),
+    "prefill_kv8": Config("prefill_kv8", 11, B=1, T=32768, N=32768, H_I=64, D_I=128, H=128,
+                          D_K=576, D_V=512, top_k=2048, pos0=0, kv_dt="mxfp8"),
     "hca_decode": Config("hca_decode", 6, B=4, T=1, N=8192, H_I=64, D_I=128, H=128, D_K=576,
                          D_V=512, top_k=8192, m=128, W=128, pos0=1048575, n_raw=128,
                          raw_base=1048576 - 128, kv_std=1.0 / (24 * math.sqrt(128)),
@@ -186,11 +193,18 @@ class Workload:
         c = self.cfg
         return self._get("q", lambda: normal(c.seed, TID_Q, (c.B, c.T, c.H, c.D_K), c.q_std, c.dt))
 
-    def kv(self) -> Optional[np.ndarray]:
-        """Stored entries [B,N,D_K] (None when they are compressed from kv_raw)."""
+    def kv(self):
+        """Stored entries [B,N,D_K] (None when they are compressed from kv_raw), or for an MXFP8
+        cache (e4m3 codes [B,N,D_K], E8M0 scales [B,N,D_K/32]): the same N(0,1) draws as the
+        bf16 cache, quantised per 32 elements."""
         c = self.cfg
         if c.compress:
             return None
+        if c.kv_dt == "mxfp8":
+            def mk():
+                codes, sc = normal_mxfp8(c.seed, TID_KV, c.B * c.N, c.D_K, c.entry_std)
+                return codes.reshape(c.B, c.N, c.D_K), sc.reshape(c.B, c.N, c.D_K // 32)
+            return self._get("kv", mk)
         return self._get("kv", lambda: normal(c.seed, TID_KV, (c.B, c.N, c.D_K), c.entry_std, c.dt))
 
     def kv_raw(self) -> Optional[np.ndarray]:

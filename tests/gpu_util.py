@@ -82,7 +82,8 @@ class DeviceWorkload:
             tdt = torch.bfloat16 if c.dt == "bf16" else torch.float32
             self.kv = torch.empty((c.B, c.N, c.D_K), dtype=tdt, device="cuda")
         else:
-            self.kv = to_dev(wl.kv())
+            kv = wl.kv()
+            self.kv = (to_dev(kv[0]), to_dev(kv[1])) if c.kv_dt == "mxfp8" else to_dev(kv)
         lens, sink = wl.seq_len(), wl.sink()
         self.seq_len = to_dev(lens) if lens is not None else None
         self.sink = to_dev(sink) if sink is not None else None

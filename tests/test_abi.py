@@ -37,7 +37,7 @@ def test_status_strings_and_version():
         s = L.dsa_status_str(code).decode()
         assert s.startswith("DSA_"), s
     assert L.dsa_status_str(99).decode() == "unknown dsa_status"
-    assert L.dsa_version() == 200
+    assert L.dsa_version() == 210
 
 
 def _dims(**kw):
@@ -112,6 +112,30 @@ def test_attend_validation():
     assert _att(dd, ws=P, wsb=need - 1) == 5
 
 
+def _mx(d, q=P, codes=P, scales=P, idx=P, raw=None, out=P, sink=None, ws=None, wsb=0):
+    return L.sparse_mla_attend_mxkv(ctypes.byref(d), q, codes, scales, idx, raw, 0, 0, P, 0.1,
+                                    sink, out, None, ws, wsb, None)
+
+
+def test_attend_mxkv_validation():
+    d = _dims()
+    assert _mx(d, scales=None) == 1              # MXFP8 codes need their scales
+    assert _mx(d, codes=None) == 1
+    assert _mx(_dims(D_K=80, D_V=64)) == 2       # D_K % 32
+    assert _mx(_dims(W=16)) == 1                 # window without kv_raw
+    assert _mx(d, codes=P + 8) == 4
+    assert _mx(d, out=P + 2) == 4
+    dd = _dims(B=1, T=1, top_k=2048)
+    need = L.dsa_workspace_bytes(ctypes.byref(dd), dsa.OP_ATTEND_MXKV)
+    assert need > 0 and _mx(dd) == 5
+    # unsplit calls expand the cache into the workspace first
+    need = L.dsa_workspace_bytes(ctypes.byref(d), dsa.OP_ATTEND_MXKV)
+    assert need >= 2 * 100 * 576 * 2
+    assert _mx(d) == 5 and _mx(d, ws=P, wsb=need - 1) == 5
+    if not torch.cuda.is_available():
+        assert _mx(d, ws=P, wsb=need) == 6
+
+
 def test_forward_validation_and_workspace():
     d = _dims()
     a = dsa.ForwardArgs(dsa.BF16, dsa.BF16, P, P, P, None, P, P, None, 0, 0, 0, P, 0.1, P, None,
@@ -128,6 +152,16 @@ def test_forward_validation_and_workspace():
     a.compress, a.kv_raw, a.n_raw = 0, None, 0
     a.q_I = P + 8
     assert L.dsa_forward(ctypes.byref(d), ctypes.byref(a), P, need, None) == 4
+    a.q_I = P
+    # an MXFP8 latent cache: bf16 path only, stored entries only, D_K % 32 == 0
+    a.kv_scale = P
+    a.dt = dsa.F32
+    assert L.dsa_forward(ctypes.byref(d), ctypes.byref(a), P, need, None) == 3
+    a.dt = dsa.BF16
+    a.compress, a.kv_raw, a.n_raw = 1, P, 400
+    assert L.dsa_forward(ctypes.byref(_dims(m=4)), ctypes.byref(a), P, need, None) == 3
+    a.compress, a.kv_raw, a.n_raw = 0, None, 0
+    assert L.dsa_forward(ctypes.byref(_dims(D_K=80, D_V=64)), ctypes.byref(a), P, need, None) == 2
 
 
 def test_forward_noalloc_validation():
@@ -202,6 +236,29 @@ def test_workspace_sizes():
     big = _dims(B=1, T=32768, N=32768, top_k=2048)
     # fused prefill chunks its score rows to a bounded workspace (< 0.6 GB)
     assert L.dsa_workspace_bytes(ctypes.byref(big), dsa.OP_FORWARD) < 600 << 20
+
+
+def _al(n):
+    return (n + 255) // 256 * 256
+
+
+def test_workspace_sizes_mxfp8_cache():
+    # split (few-row) attention converts gathered rows in the kernel: no extra bytes; unsplit
+    # (many-row) attention reads a bf16 copy of the whole cache, B*N*D_K*2 bytes after the rest
+    dec = _dims(B=16, T=1, N=8192, top_k=2048)
+    pre = _dims(B=1, T=4096, N=4096, top_k=2048)
+    ws = lambda d, op: L.dsa_workspace_bytes(ctypes.byref(d), op)
+    assert ws(dec, dsa.OP_ATTEND_MXKV) == ws(dec, dsa.OP_ATTEND)
+    assert ws(pre, dsa.OP_ATTEND_MXKV) == _al(ws(pre, dsa.OP_ATTEND)) + _al(4096 * 576 * 2)
+    big = _dims(B=1, T=32768, N=32768, top_k=2048)
+    assert ws(big, dsa.OP_FORWARD_MXKV) == ws(big, dsa.OP_FORWARD) + _al(32768 * 576 * 2)
+    assert ws(dec, dsa.OP_FORWARD_MXKV) == ws(dec, dsa.OP_FORWARD)
+    # scalar-kernel shapes decode in the kernel at any row count
+    odd = _dims(B=1, T=4096, N=4096, top_k=2048, H=16, D_K=192, D_V=128)
+    assert ws(odd, dsa.OP_ATTEND_MXKV) == ws(odd, dsa.OP_ATTEND)
+    hca = _dims(B=1, T=4096, N=1024, top_k=99999, m=128, W=128)
+    assert ws(hca, dsa.OP_HCA_MXKV) == _al(1024 * 576 * 2)
+    assert ws(_dims(N=0), dsa.OP_FORWARD_MXKV) == 0
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU device error path")

@@ -330,6 +330,32 @@ def test_attention_bf16_rows_decoded_exactly():
     assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
+def test_attention_mxfp8_cache_equals_decoded_rows():
+    # an MXFP8 latent cache (codes, scales): the same attention as over its exactly decoded rows,
+    # for masked slots, repeated entries and an entry of the last row
+    codes, sc = synth.normal_mxfp8(13, 5, 40, 64, 1.0)
+    q = synth.normal(13, 4, (4, 64), 1.0, "bf16")
+    idx = np.array([3, -1, 17, 3, 39, 0, -1], np.int32)
+    a, la = oracle.attend_row(q, (codes, sc), idx, 48, 0.125)
+    b, lb = oracle.attend_row(q, oracle.decode_mxfp8(codes, sc), idx, 48, 0.125)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(la, lb, rtol=0, atol=1e-13)
+    e, le = oracle.attend_row(q, (codes, sc), np.full(5, -1, np.int32), 48, 0.125)
+    assert (e == 0).all() and np.isneginf(le).all()
+
+
+def test_attention_mxfp8_constant_rows_closed_form():
+    # every code 0x38 (e4m3 1.0) and scale 2^(e - 127): each selected row is the constant
+    # 2^(e - 127); a zero query averages them
+    codes = np.full((6, 32), 0x38, np.uint8)
+    sc = np.array([[127], [128], [126], [130], [127], [125]], np.uint8)
+    idx = np.array([1, 3, -1, 5], np.int32)
+    out, lse = oracle.attend_row(np.zeros((2, 32)), (codes, sc), idx, 16, 1.0)
+    want = (2.0 + 8.0 + 0.25) / 3
+    np.testing.assert_allclose(out, want, rtol=1e-15)
+    np.testing.assert_allclose(lse, math.log(3), rtol=1e-15)
+
+
 # -------------------------------------------------------------------------------- CSA ----
 
 def test_h3_csa_golden():
