@@ -29,6 +29,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 constexpr int kTile = 32;       // entries per tile
+// per (row, head, split) partial: m, l, then the fp16 scale c of each 128-column quarter
+constexpr int kMlStride = 6;
 constexpr float kRefSlack = 8.f;  // log2 headroom of the lazily moved softmax reference
 
 // Joins an attention-sink logit s2 (log2 units; -inf = no sink) to a softmax state: m is the
@@ -89,28 +91,32 @@ __device__ __forceinline__ int entry_code(int e, const int32_t* __restrict__ idx
 //    conflict-free for the row-per-lane reads.
 //    Waits are explicit (s_waitcnt vmcnt + s_barrier, no fence).
 //  * Score waves 0..3 (head block hb = wave): in iteration i, S^T = K Q^T for the 32 entries of
-//    tile i (two 16-entry blocks, 8 independent chains of v_mfma_f32_16x16x32_bf16 with q in
-//    registers as the B operand) and the online softmax (exp2 domain; the reference moves only
+//    tile i (two 16-entry blocks, each over two accumulator chains of v_mfma_f32_16x16x32_bf16,
+//    with q in registers as the B operand) and the online softmax (exp2 domain; the reference moves only
 //    when a head's maximum grows by more than kRefSlack; head maxima reduced with
 //    v_permlane16_swap / v_permlane32_swap). The S^T accumulator layout (lane: head n, entries
 //    4g..4g+3) is the A-operand layout of P, so each lane hands its packed P (slots 0..3 =
 //    entries 4g.., slots 4..7 = entries 16+4g..) to its value wave through LDS unchanged, with
 //    the rescale factors when the reference moved.
-//  * Value waves 4..7: in iteration i, P V for tile i-1; wave 4+v owns 32 heads (head blocks
-//    2*(v&1), 2*(v&1)+1) and value columns 256*(v>>1).. +255, so each pair of transposed V
-//    reads feeds two MFMAs (32 MFMAs per tile, V read from LDS once per 32 heads). The B
-//    operands come straight from the row-major tile through ds_read_b64_tr_b16: within each
-//    group of 16 lanes, if lane j reads M[j][0..3], lane 4a+b
+//  * Value waves 4..7: in iteration i, P V for tile i-1; wave 4+v owns all 64 heads and value
+//    columns 128*v .. +127, so each pair of transposed V reads feeds four MFMAs (32 MFMAs and
+//    16 reads per tile). The B operands come straight from the row-major tile through
+//    ds_read_b64_tr_b16: within each group of 16 lanes, if lane j reads M[j][0..3], lane 4a+b
 //    receives {M[a][b], M[a+4][b], M[a+8][b], M[a+12][b]}. Lane j of group g reading entry
 //    4g + j/4 at column c + 4*(j%4) therefore receives, in lane n, V[4g+0..3][c+n] (B slots 0..3
-//    in P's order); a second read 16 rows further supplies slots 4..7.
+//    in P's order); a second read 16 rows further supplies slots 4..7. The reads of two column
+//    blocks are issued ahead of the eight MFMAs of the two before them, inside one asm block
+//    with its wait (pv_step2).
+//  * The softmax runs on raw scores: maxima with v_max3, the scale folded into the exponent
+//    (one fma per entry), and a finite stand-in reference while every entry so far is masked.
 //  * Two barriers per iteration: after the first (tile i has landed) the score waves run the S
 //    MFMAs of tile i alone on the matrix cores while the value waves issue the DMAs of the next
 //    tile; after the second, the score waves' softmax (VALU) overlaps the value waves' P V MFMAs.
 //    The two kinds of wave run separate loops with the same barrier count, so the register
 //    allocator never holds q and the accumulators at once. The ring is 4 stages deep when the
 //    split's entry table fits beside it (two tiles in flight ahead of the score waves), else 3.
-//  * Few-query calls split the entry list and merge the (m, l, O) partials in attend_combine.
+//  * Few-query calls split the entry list and merge the (m, l, O) partials in attend_combine
+//    (O as fp16 scaled per 128-column quarter).
 //    Workgroups are numbered so that each XCD (workgroup id mod 8) gets a contiguous run of
 //    (row, head group, split): the splits of a query share that XCD's L2 for q and the tiles.
 // ------------------------------------------------------------------------------------------
@@ -128,13 +134,26 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N_) : "memory");
 }
 
-// max / sum over the four 16-lane groups, on the VALU (permlane swaps exchange rows of 16 and
-// halves of 32 lanes between two registers)
-__device__ __forceinline__ float group_max(float v) {
+// sum over the four 16-lane groups, on the VALU (permlane swaps exchange rows of 16 and halves
+// of 32 lanes between two registers)
+// Maxima without the canonicalising v_max x, x the compiler adds for values it cannot prove
+// canonical (MFMA results): IEEE maximum of finite values and -inf. group_max_raw: over the
+// four 16-lane groups.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float group_max_raw(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group_sum(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -144,32 +163,58 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 
-// 16 ds_read_b64_tr_b16 for value-column blocks d0 .. d0+7 (entries 4g.. and 16+4g..), waited
-// for inside the same asm block. Written as asm because the builtin carries no memory operand,
-// which makes the compiler wait for every LDS DMA still in flight before it.
-#define DSA_TR(i, off) "ds_read_b64_tr_b16 %" #i ", %16 offset:" #off "\n"
-#define DSA_TR_PAIR(i0, i1, D) DSA_TR(i0, (D) * 32) DSA_TR(i1, 16896 + (D) * 32)
-#define DSA_TR_BLOCK(D0)                                                                        \
-  case D0:                                                                                      \
-    asm volatile(DSA_TR_PAIR(0, 1, D0) DSA_TR_PAIR(2, 3, D0 + 1) DSA_TR_PAIR(4, 5, D0 + 2)      \
-                 DSA_TR_PAIR(6, 7, D0 + 3) DSA_TR_PAIR(8, 9, D0 + 4) DSA_TR_PAIR(10, 11, D0 + 5) \
-                 DSA_TR_PAIR(12, 13, D0 + 6) DSA_TR_PAIR(14, 15, D0 + 7)                        \
-                 "s_waitcnt lgkmcnt(0)"                                                         \
-                 : "=&v"(tr[0]), "=&v"(tr[1]), "=&v"(tr[2]), "=&v"(tr[3]), "=&v"(tr[4]),         \
-                   "=&v"(tr[5]), "=&v"(tr[6]), "=&v"(tr[7]), "=&v"(tr[8]), "=&v"(tr[9]),         \
-                   "=&v"(tr[10]), "=&v"(tr[11]), "=&v"(tr[12]), "=&v"(tr[13]), "=&v"(tr[14]),    \
-                   "=&v"(tr[15])                                                                \
-                 : "v"(vaddr)                                                                   \
-                 : "memory");                                                                   \
-    break;
-__device__ __forceinline__ void tr_read_block(u32x2_t* tr, uint32_t vaddr, int d0) {
-  switch (d0) {
-    DSA_TR_BLOCK(0) DSA_TR_BLOCK(8)
+#define DSA_PV_MFMAS2                                                                           \
+  "v_mfma_f32_16x16x32_bf16 %0, %12, %16, %0\n"                                                 \
+  "v_mfma_f32_16x16x32_bf16 %1, %13, %16, %1\n"                                                 \
+  "v_mfma_f32_16x16x32_bf16 %2, %14, %16, %2\n"                                                 \
+  "v_mfma_f32_16x16x32_bf16 %3, %15, %16, %3\n"                                                 \
+  "v_mfma_f32_16x16x32_bf16 %4, %12, %17, %4\n"                                                 \
+  "v_mfma_f32_16x16x32_bf16 %5, %13, %17, %5\n"                                                 \
+  "v_mfma_f32_16x16x32_bf16 %6, %14, %17, %6\n"                                                 \
+  "v_mfma_f32_16x16x32_bf16 %7, %15, %17, %7\n"
+// Column blocks D, D+1 of P V on a value wave (four head blocks each): the transposed V reads
+// of blocks D+2, D+3 (x0, x1: entries 4g.. / 16+4g.. of D+2; y0, y1: of D+3) are issued
+// first and waited for at the end, so they run under the eight MFMAs (B operands b0, b1; A
+// operands p0..p3). The MFMAs sit in the same asm block as the reads (a load's destination
+// must not be reused before its wait); s_nop pads the VALU -> MFMA distance at the start and
+// the MFMA -> VALU distance at the end of a tile.
+template <int D>
+__device__ __forceinline__ void pv_step2(f32x4_t* a, f32x4_t* b, const bf16x8_t* p,
+                                         u32x4_t b0, u32x4_t b1, uint32_t vaddr, u32x2_t& x0,
+                                         u32x2_t& x1, u32x2_t& y0, u32x2_t& y1) {
+  if constexpr (D + 2 < 8) {
+    asm volatile("ds_read_b64_tr_b16 %8, %18 offset:%19\n"
+                 "ds_read_b64_tr_b16 %9, %18 offset:%20\n"
+                 "ds_read_b64_tr_b16 %10, %18 offset:%21\n"
+                 "ds_read_b64_tr_b16 %11, %18 offset:%22\n"
+                 "s_nop 2\n" DSA_PV_MFMAS2 "s_waitcnt lgkmcnt(0)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]),
+                   "+v"(b[2]), "+v"(b[3]), "=&v"(x0), "=&v"(x1), "=&v"(y0), "=&v"(y1)
+                 : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(b0), "v"(b1), "v"(vaddr),
+                   "n"((D + 2) * 32), "n"(16896 + (D + 2) * 32), "n"((D + 3) * 32),
+                   "n"(16896 + (D + 3) * 32)
+                 : "memory");
+  } else {
+    asm volatile("s_nop 2\n" DSA_PV_MFMAS2 "s_nop 7\ns_nop 7\ns_nop 7"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]),
+                   "+v"(b[2]), "+v"(b[3]), "=v"(x0), "=v"(x1), "=v"(y0), "=v"(y1)
+                 : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(b0), "v"(b1)
+                 : "memory");
   }
 }
-#undef DSA_TR_BLOCK
-#undef DSA_TR_PAIR
-#undef DSA_TR
+#undef DSA_PV_MFMAS2
+// the transposed reads of the first two column blocks, waited for
+__device__ __forceinline__ void pv_first2(uint32_t vaddr, u32x2_t& x0, u32x2_t& x1, u32x2_t& y0,
+                                          u32x2_t& y1) {
+  asm volatile("ds_read_b64_tr_b16 %0, %4\n"
+               "ds_read_b64_tr_b16 %1, %4 offset:16896\n"
+               "ds_read_b64_tr_b16 %2, %4 offset:32\n"
+               "ds_read_b64_tr_b16 %3, %4 offset:16928\n"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(x0), "=&v"(x1), "=&v"(y0), "=&v"(y1)
+               : "v"(vaddr)
+               : "memory");
+}
 
 // max over the 16 lanes of a DPP row (lane groups of 16)
 template <int CTRL>
@@ -522,7 +567,6 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qf[kk]));
     float m_run = kNegInf;  // per head n (same in the four lane groups)
     float l_run = 0.f;      // this lane's share: entries 4g.., 16+4g.. of every tile
-    bool live = false;      // wave-uniform: m_run is finite for every head
     for (int i = 0; i <= ntiles; ++i) {
       ring_top(i);
       if (i == ntiles) {
@@ -542,10 +586,10 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
         }
         return *reinterpret_cast<const u32x4_t*>(ap);
       };
-      // S^T for entries 0..15 (sa) and 16..31 (sc), each over 4 accumulators (k-step % 4)
-      f32x4_t sa[2], sc[2];
+      // S^T for entries 0..15 (sa) and 16..31 (sc), each over two accumulators (k-step parity)
+      f32x4_t sa2[2], sc2[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) sa[c] = sc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < 2; ++c) sa2[c] = sc2[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       {
         constexpr int KB = 3;  // k-steps per block of reads, one block ahead of the MFMAs
         u32x4_t a0[KS], a1[KS];
@@ -566,34 +610,25 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
           }
 #pragma unroll
           for (int kk = KB * blk; kk < KB * blk + KB; ++kk) {
-            sa[kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0[kk]), as_bf16x8(qf[kk]), sa[kk & 1], 0, 0, 0);
-            sc[kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1[kk]), as_bf16x8(qf[kk]), sc[kk & 1], 0, 0, 0);
+            sa2[kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0[kk]), as_bf16x8(qf[kk]), sa2[kk & 1], 0, 0, 0);
+            sc2[kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1[kk]), as_bf16x8(qf[kk]), sc2[kk & 1], 0, 0, 0);
           }
         }
       }
       mid_barrier();
-      const f32x4_t st0 = sa[0] + sa[1];
-      const f32x4_t st1 = sc[0] + sc[1];
-      // lane (head n, g): entries 4g+j (z[j]) and 16+4g+j (z[4+j]); masked entries only in
-      // tiles whose flag says so (most tiles have none)
-      float z[8];
-      float mx = kNegInf;
+      f32x4_t sa = sa2[0] + sa2[1], sc = sc2[0] + sc2[1];
+      // lane (head n, g): raw scores of entries 4g+j (sa[j]) and 16+4g+j (sc[j]); masked
+      // entries only in tiles whose flag says so (most tiles have none). The scale goes into
+      // the exponent (one fma per entry); maxima are taken on the raw scores (scale > 0).
       if (__builtin_amdgcn_readfirstlane(sflag[i]) != 0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          z[j] = cd0[j] != -1 ? st0[j] * scale_log2 : kNegInf;
-          z[4 + j] = cd1[j] != -1 ? st1[j] * scale_log2 : kNegInf;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          z[j] = st0[j] * scale_log2;
-          z[4 + j] = st1[j] * scale_log2;
+          sa[j] = cd0[j] != -1 ? sa[j] : kNegInf;
+          sc[j] = cd1[j] != -1 ? sc[j] : kNegInf;
         }
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fmaxf(z[j], z[4 + j]));
-      mx = group_max(mx);
+      float mx = vmax3(vmax3(sa[0], sa[1], sa[2]), vmax3(sa[3], sc[0], sc[1]), vmax(sc[2], sc[3]));
+      mx = group_max_raw(mx) * scale_log2;
       // Lazily moved softmax reference: m_run only moves (and the value waves rescale their
       // accumulators) when a head's tile maximum exceeds it by more than kRefSlack (log2
       // units), so p <= 2^kRefSlack.
@@ -605,19 +640,18 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
         l_run *= alpha;
         m_run = m_new;
         if (g == 0) abuf[i & 1][hb][n] = alpha;
-        live = __ballot(m_run == kNegInf) == 0;
       }
       if (lane == 0) fbuf[i & 1][hb] = moved ? 1u : 0u;
+      // m_run is -inf only while every entry so far is masked (all scores -inf): any finite
+      // reference then gives exp2(-inf) = 0
+      const float mneg = m_run == kNegInf ? 0.f : -m_run;
       uint32_t pk[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float e0 = __builtin_amdgcn_exp2f(z[2 * j] - m_run);
-        float e1 = __builtin_amdgcn_exp2f(z[2 * j + 1] - m_run);
-        if (!live) {
-          // m_run == -inf only while every entry so far is masked (z == -inf as well)
-          e0 = m_run == kNegInf ? 0.f : e0;
-          e1 = m_run == kNegInf ? 0.f : e1;
-        }
+        const float za = j < 2 ? sa[2 * j] : sc[2 * j - 4];
+        const float zb = j < 2 ? sa[2 * j + 1] : sc[2 * j - 3];
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(za, scale_log2, mneg));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(zb, scale_log2, mneg));
         l_run += e0 + e1;
         pk[j] = pack_bf16x2(e0, e1);
       }
@@ -635,8 +669,8 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
         if (lse) lse[(size_t)qi * H + h0 + n] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
       } else {
         const size_t hrow = ((size_t)row * H + h0 + n) * nsplit + split;
-        part_ml[hrow * 4] = m_run;
-        part_ml[hrow * 4 + 1] = l_head;
+        part_ml[hrow * kMlStride] = m_run;
+        part_ml[hrow * kMlStride + 1] = l_head;
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -644,18 +678,17 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     return;
   }
 
-  // ---- value waves: wave 4 + v owns heads of blocks 2*(v&1) and 2*(v&1)+1 (32 heads) and
-  // value columns 256*(v>>1) .. +255, so each pair of transposed V reads feeds two MFMAs ----
+  // ---- value waves: wave 4 + v owns every head block (64 heads) and value columns
+  // 128*v .. +127, so each pair of transposed V reads feeds four MFMAs ----
   const int vw = wv - 4;
-  const int hb0 = 2 * (vw & 1), dh = vw >> 1;
-  constexpr int DH = DB / 2;  // 16 column blocks of this wave
-  f32x4_t acc[2][DH];         // [head block hb0 + k][column block 16*dh + d]: heads 4g+j, col n
+  constexpr int DH = DB / 4;  // 8 column blocks of this wave
+  f32x4_t acc[4][DH];         // [head block k][column block 8*vw + d]: heads 4g+j, col n
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
+  for (int k = 0; k < 4; ++k)
 #pragma unroll
     for (int d = 0; d < DH; ++d) acc[k][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // transposed V reads: entry 4g + n/4 (and 16 rows on), column 256*dh + 16d + 4*(n%4)
-  const uint32_t voff = (4 * g + (n >> 2)) * kLatStride + 512 * dh + 8 * (n & 3);
+  // transposed V reads: entry 4g + n/4 (and 16 rows on), column 128*vw + 16d + 4*(n%4)
+  const uint32_t voff = (4 * g + (n >> 2)) * kLatStride + 256 * vw + 8 * (n & 3);
   // KV8, iteration i (ring_top has waited for every DMA of this wave and prepared tile
   // i + NS - 2): convert that tile's staged codes into its stage, then stage the codes of the
   // tile after it (whose entry codes fetch() read into nx_lat)
@@ -675,70 +708,76 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
       continue;
     }
     const int t = i - 1;
-    const bf16x8_t pa0 = as_bf16x8(pbuf[t & 1][hb0][lane]);
-    const bf16x8_t pa1 = as_bf16x8(pbuf[t & 1][hb0 + 1][lane]);
-    const u32x2_t moved = *reinterpret_cast<const u32x2_t*>(&fbuf[t & 1][hb0]);
-    const f32x4_t alpha[2] = {*reinterpret_cast<const f32x4_t*>(&abuf[t & 1][hb0][4 * g]),
-                              *reinterpret_cast<const f32x4_t*>(&abuf[t & 1][hb0 + 1][4 * g])};
+    bf16x8_t pa[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pa[k] = as_bf16x8(pbuf[t & 1][k][lane]);
+    const u32x4_t moved = *reinterpret_cast<const u32x4_t*>(&fbuf[t & 1][0]);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (KV8)
       if (due) kv8_phase1(i);
     if (due) issue_all();
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      if (moved[k] != 0) {
+    for (int k = 0; k < 4; ++k) {
+      if (__builtin_amdgcn_readfirstlane(moved[k]) != 0) {
+        const f32x4_t alpha = *reinterpret_cast<const f32x4_t*>(&abuf[t & 1][k][4 * g]);
 #pragma unroll
-        for (int d = 0; d < DH; ++d) acc[k][d] *= alpha[k];
+        for (int d = 0; d < DH; ++d) acc[k][d] *= alpha;
       }
     }
     mid_barrier();
     const uint32_t vaddr = (uint32_t)(uintptr_t)(lds_void_t*)(smem + (t % NS) * kStage) + voff;
-#pragma unroll
-    for (int d0 = 0; d0 < DH; d0 += 8) {
-      u32x2_t tr[16];
-      tr_read_block(tr, vaddr, d0);
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const u32x4_t bw = {tr[2 * d][0], tr[2 * d][1], tr[2 * d + 1][0], tr[2 * d + 1][1]};
-        acc[0][d0 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa0, as_bf16x8(bw), acc[0][d0 + d], 0, 0, 0);
-        acc[1][d0 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa1, as_bf16x8(bw), acc[1][d0 + d], 0, 0, 0);
-      }
+    u32x2_t x0, x1, y0, y1;
+    pv_first2(vaddr, x0, x1, y0, y1);
+    // the transposed reads of blocks d+2, d+3 run under the MFMAs of blocks d, d+1
+#define DSA_PV2(D)                                                                              \
+    {                                                                                           \
+      f32x4_t ca[4] = {acc[0][D], acc[1][D], acc[2][D], acc[3][D]};                             \
+      f32x4_t cb[4] = {acc[0][D + 1], acc[1][D + 1], acc[2][D + 1], acc[3][D + 1]};             \
+      u32x2_t nx0, nx1, ny0, ny1;                                                               \
+      pv_step2<D>(ca, cb, pa, u32x4_t{x0[0], x0[1], x1[0], x1[1]},                              \
+                  u32x4_t{y0[0], y0[1], y1[0], y1[1]}, vaddr, nx0, nx1, ny0, ny1);              \
+      for (int k = 0; k < 4; ++k) {                                                             \
+        acc[k][D] = ca[k];                                                                      \
+        acc[k][D + 1] = cb[k];                                                                  \
+      }                                                                                         \
+      x0 = nx0; x1 = nx1; y0 = ny0; y1 = ny1;                                                   \
     }
+    DSA_PV2(0) DSA_PV2(2) DSA_PV2(4) DSA_PV2(6)
+#undef DSA_PV2
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();  // the score waves' final (m, l) are in sml
   if (nsplit == 1) {
-    // normalise, round to bf16 and stage this wave's 32 x 256 block through the (idle) ring
+    // normalise, round to bf16 and stage this wave's 64 x 128 block through the (idle) ring
     // memory (a region of its own) so that each output row is written with 16-byte stores
-    uint16_t* so = reinterpret_cast<uint16_t*>(smem) + vw * 32 * (256 + 8);
+    uint16_t* so = reinterpret_cast<uint16_t*>(smem) + vw * 64 * (128 + 8);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < 4; ++k) {
       float inv[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) inv[j] = sml[hb0 + k][1][4 * g + j];
+      for (int j = 0; j < 4; ++j) inv[j] = sml[k][1][4 * g + j];
 #pragma unroll
       for (int d = 0; d < DH; ++d)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          so[(16 * k + 4 * g + j) * (256 + 8) + 16 * d + n] = f32_to_bf16(acc[k][d][j] * inv[j]);
+          so[(16 * k + 4 * g + j) * (128 + 8) + 16 * d + n] = f32_to_bf16(acc[k][d][j] * inv[j]);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // 32 rows x 512 bytes: 16 chunks of 16 bytes per lane
-    const int hbase = hg * 64 + hb0 * 16;
+    // 64 rows x 256 bytes: 16 chunks of 16 bytes per lane
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const int c = lane + 64 * k, r = c >> 5, col = (c & 31) * 8;
-      *reinterpret_cast<u32x4_t*>(out + ((size_t)qi * H + hbase + r) * DV + 256 * dh + col) =
-          *reinterpret_cast<const u32x4_t*>(so + r * (256 + 8) + col);
+      const int c = lane + 64 * k, r = c >> 4, col = (c & 15) * 8;
+      *reinterpret_cast<u32x4_t*>(out + ((size_t)qi * H + hg * 64 + r) * DV + 128 * vw + col) =
+          *reinterpret_cast<const u32x4_t*>(so + r * (128 + 8) + col);
     }
   } else {
-    // O partials (relative to this split's m) as fp16, each head's 256 columns divided by their
+    // O partials (relative to this split's m) as fp16, each head's 128 columns divided by their
     // largest magnitude c (so every value lies in [-1, 1]; c goes beside the split's (m, l)), in
     // register order: [row][head group][split][slot 8][16 column blocks][64 lanes] x 4 heads
     // (4g..4g+3 of column 16d + n); slot = head block + 4 * (column half). 512-byte stores.
     f16x4_t* po = part_o + (((size_t)row * HG + hg) * nsplit + split) * 8 * 16 * 64 + lane;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < 4; ++k) {
       float c[4] = {0.f, 0.f, 0.f, 0.f}, inv[4];
 #pragma unroll
       for (int d = 0; d < DH; ++d)
@@ -752,12 +791,12 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
 #pragma unroll
       for (int d = 0; d < DH; ++d) {
         const f32x4_t a = acc[k][d] * f32x4_t{inv[0], inv[1], inv[2], inv[3]};
-        po[((hb0 + k + 4 * dh) * 16 + d) * 64] = __builtin_convertvector(a, f16x4_t);
+        po[((k + 4 * (vw >> 1)) * 16 + 8 * (vw & 1) + d) * 64] = __builtin_convertvector(a, f16x4_t);
       }
       if (n < 4) {
         const float cn = n == 0 ? c[0] : n == 1 ? c[1] : n == 2 ? c[2] : c[3];
-        const size_t hrow = ((size_t)row * H + hg * 64 + (hb0 + k) * 16 + 4 * g + n) * nsplit + split;
-        part_ml[hrow * 4 + 2 + dh] = cn;
+        const size_t hrow = ((size_t)row * H + hg * 64 + k * 16 + 4 * g + n) * nsplit + split;
+        part_ml[hrow * kMlStride + 2 + vw] = cn;
       }
     }
   }
@@ -765,7 +804,7 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
 
 // Merge split partials: out = sum_s w_s O_s, w_s = 2^(m_s - M) / sum_s 2^(m_s - M) l_s,
 // M = max_s m_s, with O_s = c_s x (its fp16 partial). One workgroup per (wave slot, column
-// quarter, head group, row): 16 heads x 128 columns, half of the block one wave of
+// quarter, head group, row): 16 heads x 128 columns, a quarter of the block one value wave of
 // attend_mfma_dma writes per split. Every partial is loaded before the first use (up to 32
 // splits: 64 f16x4 per thread); the bf16 result goes through LDS so that each row of the output
 // is written with 16-byte stores.
@@ -803,9 +842,9 @@ __global__ __launch_bounds__(256) void attend_combine(
     const int s = sl + 16 * j;
     if (s < nsplit) {
       const size_t hrow = ((size_t)row * H + h0 + hh) * nsplit + s;
-      ml_m[j] = part_ml[hrow * 4];
-      ml_l[j] = part_ml[hrow * 4 + 1];
-      ml_c[j] = part_ml[hrow * 4 + 2 + (ws >> 2)];  // scale of this column half
+      ml_m[j] = part_ml[hrow * kMlStride];
+      ml_l[j] = part_ml[hrow * kMlStride + 1];
+      ml_c[j] = part_ml[hrow * kMlStride + 2 + 2 * (ws >> 2) + cq];  // scale of this column quarter
     }
   }
   // per head: M = max_s m_s, L = sum_s 2^(m_s - M) l_s, over the 16 lanes of each head
@@ -1000,8 +1039,8 @@ int attend_splits(const Shape& s, int64_t nrows, int fmt) {
 size_t attend_ws_bytes(const Shape& s, int64_t nrows, int fmt) {
   const int ns = attend_splits(s, nrows, fmt);
   if (ns <= 1) return 0;
-  // fp16 O partials, then (m, l, c_0, c_1) per split
-  return (size_t)nrows * s.H * ns * ((size_t)s.D_V * 2 + 4 * sizeof(float));
+  // fp16 O partials, then (m, l, c_0 .. c_3) per split
+  return (size_t)nrows * s.H * ns * ((size_t)s.D_V * 2 + kMlStride * sizeof(float));
 }
 
 // Dynamic LDS the attention kernels may take beside their static LDS (the ring and its
