@@ -448,10 +448,8 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
   constexpr int kDmas = 9;
   // MXFP8 entries (KV8): a value wave's 8 rows (4608 code bytes, 144 scale bytes) come by DMA
   // into the staging buffers one iteration before they are needed (dma8); convert8 turns them
-  // into bf16 in the ring stage, in the layout of the DMA'd rows: unit j of lane l is
-  // u = l + 64 j, row u / 72, codes 8 (u % 72) .. +7 with the E8M0 scale of their 32-block.
+  // into bf16 in the ring stage, in the layout of the DMA'd rows.
   // Raw window rows (bf16) take the DMA above; masked entries convert row 0 (finite; P is 0).
-  constexpr int kUnits = 9;
   const uint8_t* kv8_b = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * N * DK;
   const uint8_t* ksc_b = kv_scale + (size_t)b * N * (DK / 32);
   const uint32_t f8base = __builtin_amdgcn_readfirstlane(
@@ -478,26 +476,37 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
             (lds_void_t*)(uintptr_t)(f8sbase + 256 * k), 1, 0, 0);
     }
   };
-  auto convert8 = [&](char* st) {  // d_code: the entry codes of the tile being converted
+  // d_code: the entry codes of the tile being converted (rows vrow + 0..7 in lanes 0..7).
+  // Unit r < 8: the latent part of row vrow + r, lane l converting codes 8l .. 8l+7 (all
+  // offsets are immediates off one lane base); then the rope parts, lane l converting codes
+  // 512 + 8 (l & 7) .. of row vrow + (l >> 3).
+  auto cvt8 = [&](u32x2_t w, uint32_t e) -> u32x4_t {
+    // E8M0 e -> 2^(e - 127) (e == 0 is the subnormal 2^-127)
+    const float sc = __uint_as_float(e != 0u ? e << 23 : 0x00400000u);
+    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, false);
+    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, true);
+    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, false);
+    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, true);
+    return u32x4_t{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                   __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+  };
+  auto convert8 = [&](char* st) {
     const char* src = sf8 + (KV8 ? vrow * 576 : 0);
     const uint32_t* ssrc = sf8s + (KV8 ? vrow * 18 : 0);
 #pragma unroll
-    for (int j = 0; j < kUnits; ++j) {
-      const int u = lane + 64 * j, rr = u / 72, c = u - 72 * rr, R = vrow + rr;
-      if (__shfl(d_code, rr, 64) > -2) {
-        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src + rr * 576 + 8 * c);
-        const uint32_t e = ssrc[rr * 18 + (c >> 2)] & 0xffu;
-        // E8M0 e -> 2^(e - 127) (e == 0 is the subnormal 2^-127)
-        const float sc = __uint_as_float(e != 0u ? e << 23 : 0x00400000u);
-        const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, false);
-        const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, true);
-        const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, false);
-        const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, true);
-        const u32x4_t v = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
-        const uint32_t off = c < 64 ? R * kLatStride + 16 * c
-                                    : kStageLat + R * 128 + 16 * ((c - 64) ^ ((R >> 1) & 7));
-        *reinterpret_cast<u32x4_t*>(st + off) = v;
+    for (int r = 0; r < 8; ++r) {
+      if (__builtin_amdgcn_readlane(d_code, r) > -2) {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src + r * 576 + 8 * lane);
+        const uint32_t e = ssrc[r * 18 + (lane >> 2)] & 0xffu;
+        *reinterpret_cast<u32x4_t*>(st + (vrow + r) * kLatStride + 16 * lane) = cvt8(w, e);
+      }
+    }
+    {
+      const int r = lane >> 3, c = lane & 7, R = vrow + r;
+      if (__shfl(d_code, r, 64) > -2) {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src + r * 576 + 512 + 8 * c);
+        const uint32_t e = ssrc[r * 18 + 16 + (c >> 2)] & 0xffu;
+        *reinterpret_cast<u32x4_t*>(st + kStageLat + R * 128 + 16 * (c ^ ((R >> 1) & 7))) = cvt8(w, e);
       }
     }
     // the staging reads are done before the next dma8 overwrites the buffers
