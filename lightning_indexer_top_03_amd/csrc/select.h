@@ -212,57 +212,6 @@ __device__ __forceinline__ void block_threshold(const uint32_t (&key)[PER], int 
   tau = prefix;
 }
 
-// block_threshold through a sample: the same result (tau, need, cnt_eq), with the radix passes
-// run over a few thousand candidates instead of the whole row. The first key of every thread
-// that has any (a systematic sample of ns = ceil(n / PER) keys) gives lo = the sample's r-th
-// largest, r = mu + 4 sigma + 8 with mu = ns k / n the expected number of sampled keys among
-// the row's top k. When at least k and at most kSampCap keys are >= lo, every one of the top
-// k is among them, so the threshold among those candidates (compacted into cbuf in index
-// order) is the row's. Otherwise (an unlucky or adversarial sample) the whole row goes through
-// block_threshold. Per key this costs a compare and a rarely taken store instead of a share of
-// every radix pass.
-constexpr int kSampCap = 4096;
-
-template <int NW, int PER>
-__device__ __forceinline__ void block_threshold_sampled(const uint32_t (&key)[PER], int nv,
-                                                        uint32_t k, uint32_t n,
-                                                        SelShared<NW>& sh, uint32_t* cbuf,
-                                                        uint32_t& tau, uint32_t& need,
-                                                        uint32_t& cnt_eq) {
-  constexpr int PC = kSampCap / (NW * 64);  // candidates per thread
-  static_assert(PC * NW * 64 == kSampCap, "candidate slots split evenly over the block");
-  const uint32_t ns = min((uint32_t)(NW * 64), (n + PER - 1) / PER);
-  const float p = (float)k / (float)n;
-  const float mu = p * (float)ns;
-  const float rf = mu + 4.f * __builtin_sqrtf(mu * (1.f - p)) + 8.f;
-  if (rf < (float)ns) {  // block-uniform
-    const uint32_t skey[1] = {key[0]};
-    uint32_t lo, need_s, eq_s;
-    block_threshold<NW, 1>(skey, nv > 0 ? 1 : 0, (uint32_t)rf, sh, lo, need_s, eq_s, ns);
-    __syncthreads();  // the next threshold clears the histograms this one read last
-    uint32_t c = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) c += (j < nv && key[j] >= lo) ? 1u : 0u;
-    uint32_t total;
-    uint32_t o = block_excl_scan<NW>(c, sh, total);
-    if (total >= k && total <= (uint32_t)kSampCap) {  // block-uniform
-#pragma unroll
-      for (int j = 0; j < PER; ++j)
-        if (j < nv && key[j] >= lo) cbuf[o++] = key[j];
-      __syncthreads();
-      uint32_t kc[PC];
-      const int c0 = PC * (int)threadIdx.x;
-      const int nvc = max(0, min(PC, (int)total - c0));
-#pragma unroll
-      for (int j = 0; j < PC; ++j) kc[j] = cbuf[min(c0 + j, (int)total - 1)];
-      block_threshold<NW, PC>(kc, nvc, k, sh, tau, need, cnt_eq, total);
-      return;
-    }
-    __syncthreads();
-  }
-  block_threshold<NW, PER>(key, nv, k, sh, tau, need, cnt_eq, n);
-}
-
 // Rank (in ascending index order) of this thread's first selected entry, how many of its
 // tau-valued entries it takes and how many entries it selects; selected = key > tau, or
 // key == tau among the first `need` tau-valued entries of the row. Counts fit 16 bits (rows of
