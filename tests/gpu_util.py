@@ -143,6 +143,15 @@ def score_mass(wl, b, t):
     return np.abs(_decoded_keys(wl, b)) @ u
 
 
+def _abs_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """|a - b| with equal values (the same infinity included) at 0; a NaN on either side is an
+    infinite difference."""
+    with np.errstate(invalid="ignore"):
+        d = np.abs(a - b)
+    d = np.where(a == b, 0.0, d)
+    return np.where(np.isnan(d), np.inf, d)
+
+
 def check_scores(gpu: np.ndarray, ref: np.ndarray, n_vis: int, full_row: bool = True, what="",
                  mass=None, dims=(64, 128)):
     """mass: score_mass of the row (mixed-sign weights), dims: (H_I, D_I). Returns the largest
@@ -157,12 +166,12 @@ def check_scores(gpu: np.ndarray, ref: np.ndarray, n_vis: int, full_row: bool = 
     tol = SCORE_RTOL * np.abs(r) + SCORE_FLOOR * np.abs(r).max()
     if mass is not None:
         bound = (dims[0] + dims[1] + 2) * 2.0 ** -24 * mass[:n_vis]
-        err = np.abs(gv - r)
+        err = _abs_diff(gv, r)
         assert (err <= tol + bound).all(), (
             f"{what}: scores beyond the fp32 accumulation bound, first s="
             f"{np.nonzero(err > tol + bound)[0][0]}")
         return float((err / np.maximum(bound, 1e-300)).max())
-    err = np.abs(gv - r)
+    err = _abs_diff(gv, r)
     bad = np.nonzero(err > tol)[0]
     assert bad.size == 0, (f"{what}: {bad.size} scores out of tolerance, first s={bad[0]} "
                            f"gpu={gv[bad[0]]} ref={r[bad[0]]}")

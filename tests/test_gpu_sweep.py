@@ -130,3 +130,45 @@ def _scalar_cases(n=4, seed=2027):
 @pytest.mark.parametrize("cfg", _scalar_cases(), ids=lambda c: c.name)
 def test_random_scalar_shapes(cfg):
     _run(cfg, n_sample=48, always=(0,))
+
+
+def _kv8_cases(n=8, seed=2026):
+    # an MXFP8 latent cache at random shapes: decode-sized calls (split attention, gathered rows
+    # converted in the kernel; some with the fused selection), prefill-sized ones (the cache
+    # expanded to bf16 first), CSA blocks with bf16 raw window rows, ragged sequence lengths
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        kind = ["decode", "prefill", "csa", "decode"][i % 4]
+        N = int(rng.integers(300, 5000))
+        top_k = int(rng.choice([64, 257, 1024, 2048]))
+        if kind == "csa":
+            c = synth.CONFIGS["csa_decode"]
+            B, T = int(rng.integers(1, 3)), int(rng.integers(1, 20))
+            p0 = int(rng.integers(128, 4 * N - 1))
+            stride = int(rng.integers(1, max(2, (4 * N - p0) // max(T, 1))))
+            base = max(0, p0 - 127)
+            cfg = c.with_(B=B, T=T, N=N, top_k=min(top_k, 1024), pos0=p0, pos_stride=stride,
+                          raw_base=base, n_raw=p0 + stride * (T - 1) - base + 1)
+        else:
+            c = synth.CONFIGS["decode" if kind == "decode" else "prefill"]
+            if kind == "prefill":
+                B, T = 1, int(rng.integers(130, 300))
+            else:
+                B, T = int(rng.integers(1, 5)), int(rng.integers(1, 40))
+            pos0 = int(rng.integers(0, N // 2))
+            stride = int(rng.integers(1, max(2, (N - pos0) // max(T, 1))))
+            cfg = c.with_(B=B, T=T, N=N, top_k=top_k, pos0=pos0, pos_stride=stride)
+        cfg = cfg.with_(kv_dt="mxfp8", seed=700 + i, name=f"sweepkv8_{i}_{kind}_k{cfg.top_k}")
+        if i % 4 == 3:
+            cfg = cfg.with_(seq_lens=tuple(int(rng.integers(N // 2, N + 1)) for _ in range(cfg.B)))
+        if i % 2 == 1:
+            cfg = cfg.sharp()
+        cases.append(cfg)
+    return cases
+
+
+@pytest.mark.parametrize("cfg", _kv8_cases(), ids=lambda c: c.name)
+def test_random_shapes_mxfp8_cache(cfg):
+    _run(cfg, n_sample=32, always=(0,), bf16_scale_allowance=cfg.name.endswith("_sharp"))
+
