@@ -206,19 +206,22 @@ def topk_row(scores: np.ndarray, n_visible: int, k: int) -> Tuple[np.ndarray, in
 def attend_row(q: np.ndarray, kv: Optional[np.ndarray], idx: np.ndarray, D_V: int, scale: float,
                p: int = 0, W: int = 0, kv_raw: Optional[np.ndarray] = None, raw_base: int = 0,
                sink: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """One query: q [H, D_K], kv [N, D_K] (f32/bf16/f64) or MXFP8 (codes, scales), idx [k]
-    (-1 = none), raw window rows
+    """One query: q [H, D_K], kv [N, D_K] (f32/bf16/f64) or an MX cache (codes, scales): MXFP8
+    (codes [N, D_K]) or MXFP4 (codes [N, D_K/2]), idx [k] (-1 = none), raw window rows
     kv_raw [n_raw, D_K] at positions raw_base.., optional sink logits [H] (fp32 values) ->
     (out [H, D_V] fp64, lse [H] fp64)."""
     q = np.ascontiguousarray(q)
     H, D_K = q.shape
     idx = np.ascontiguousarray(idx, np.int32)
     if isinstance(kv, tuple):
-        # an MXFP8 cache (codes [N, D_K], scales [N, D_K/32]): the referenced rows decoded
-        # exactly (e4m3 x 2^(e-127)); the entry set and so the softmax are order-free
+        # a low-precision cache (scales [N, D_K/32]; codes [N, D_K] e4m3 or [N, D_K/2] e2m1
+        # pairs): the referenced rows decoded exactly (code x 2^(e-127)); the entry set and so
+        # the softmax are order-free
         codes, scales = kv
+        dec = decode_mxfp4 if codes.shape[-1] * 2 == D_K else decode_mxfp8
+        assert codes.shape[-1] in (D_K, D_K // 2)
         sel = idx[idx >= 0]
-        rows = decode_mxfp8(codes[sel], scales[sel]) if sel.size else np.zeros((1, D_K))
+        rows = dec(codes[sel], scales[sel]) if sel.size else np.zeros((1, D_K))
         remap = np.full(idx.shape, -1, np.int32)
         remap[idx >= 0] = np.arange(sel.size, dtype=np.int32)
         kv, idx = rows, remap

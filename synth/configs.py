@@ -23,6 +23,9 @@ Recipes (all seeded; seed = workload id, "sharp" variants use seed 100 + id):
             queries (positions 122880..131071); W=128
   decode_kv8 / prefill_kv8   decode / prefill over an MXFP8 latent KV cache: the same
             N(0,1)/24 entries quantised to e4m3 with one E8M0 scale per 32 elements (as above)
+  decode_kv4 / prefill_kv4   the same over an MXFP4 latent KV cache: e2m1 codes (two per byte,
+            low nibble first) with one E8M0 scale per 32 (2^(floor(log2 amax) - 2), RNE,
+            saturating at 6)
   sharp variants: q, kv ~ N(0,1) and softmax scale 4/sqrt(D_K), so that attention outputs are
             O(1) and a wrong gather moves them by far more than the tolerance.
   sink = (lo, hi): one attention-sink logit per head, U(lo, hi), fp32, tensor id 7.
@@ -61,7 +64,7 @@ class Config:
     dt: str = "bf16"          # dtype of q_I, q, kv, kv_raw, out
     k_dt: str = "bf16"        # dtype of k_I: dt, "mxfp4" or "mxfp8"
     qi_dt: str = ""           # dtype of q_I: dt ("" ) or "mxfp8"
-    kv_dt: str = ""           # dtype of the stored entries kv: dt ("") or "mxfp8" (bf16 q / out)
+    kv_dt: str = ""           # dtype of the stored entries kv: dt (""), "mxfp8" or "mxfp4" (bf16 q / out)
     pos0: int = 0             # q_pos[b, t] = pos0 + pos_stride * t
     pos_stride: int = 1
     qkv_std: float = 0.0      # std of q and kv rows (0 -> 1/sqrt(D_K))
@@ -134,6 +137,10 @@ CONFIGS: Dict[str, Config] = {
                          D_V=512, top_k=2048, pos0=8191, kv_dt="mxfp8"),
     "prefill_kv8": Config("prefill_kv8", 11, B=1, T=32768, N=32768, H_I=64, D_I=128, H=128,
                           D_K=576, D_V=512, top_k=2048, pos0=0, kv_dt="mxfp8"),
+    "decode_kv4": Config("decode_kv4", 12, B=16, T=1, N=8192, H_I=64, D_I=128, H=128, D_K=576,
+                         D_V=512, top_k=2048, pos0=8191, kv_dt="mxfp4"),
+    "prefill_kv4": Config("prefill_kv4", 13, B=1, T=32768, N=32768, H_I=64, D_I=128, H=128,
+                          D_K=576, D_V=512, top_k=2048, pos0=0, kv_dt="mxfp4"),
     "hca_decode": Config("hca_decode", 6, B=4, T=1, N=8192, H_I=64, D_I=128, H=128, D_K=576,
                          D_V=512, top_k=8192, m=128, W=128, pos0=1048575, n_raw=128,
                          raw_base=1048576 - 128, kv_std=1.0 / (24 * math.sqrt(128)),
@@ -200,10 +207,11 @@ class Workload:
         c = self.cfg
         if c.compress:
             return None
-        if c.kv_dt == "mxfp8":
+        if c.kv_dt in ("mxfp8", "mxfp4"):
             def mk():
-                codes, sc = normal_mxfp8(c.seed, TID_KV, c.B * c.N, c.D_K, c.entry_std)
-                return codes.reshape(c.B, c.N, c.D_K), sc.reshape(c.B, c.N, c.D_K // 32)
+                fn, w = (normal_mxfp8, c.D_K) if c.kv_dt == "mxfp8" else (normal_mxfp4, c.D_K // 2)
+                codes, sc = fn(c.seed, TID_KV, c.B * c.N, c.D_K, c.entry_std)
+                return codes.reshape(c.B, c.N, w), sc.reshape(c.B, c.N, c.D_K // 32)
             return self._get("kv", mk)
         return self._get("kv", lambda: normal(c.seed, TID_KV, (c.B, c.N, c.D_K), c.entry_std, c.dt))
 

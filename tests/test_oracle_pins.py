@@ -356,6 +356,35 @@ def test_attention_mxfp8_constant_rows_closed_form():
     np.testing.assert_allclose(lse, math.log(3), rtol=1e-15)
 
 
+def test_attention_mxfp4_cache_equals_decoded_rows():
+    # an MXFP4 latent cache (e2m1 pairs [N, D_K/2], scales): the same attention as over its
+    # exactly decoded rows
+    codes, sc = synth.normal_mxfp4(17, 5, 40, 64, 1.0)
+    q = synth.normal(17, 4, (4, 64), 1.0, "bf16")
+    idx = np.array([3, -1, 17, 3, 39, 0, -1], np.int32)
+    a, la = oracle.attend_row(q, (codes, sc), idx, 48, 0.125)
+    b, lb = oracle.attend_row(q, oracle.decode_mxfp4(codes, sc), idx, 48, 0.125)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(la, lb, rtol=0, atol=1e-13)
+
+
+def test_attention_mxfp4_constant_rows_closed_form():
+    # every code pair 0x22 (e2m1 1.0, 1.0) and scale 2^(e - 127): each selected row is the
+    # constant 2^(e - 127); a zero query averages them; with a sign bit on the high nibbles
+    # (0xa2: 1.0, -1.0) the odd columns flip sign
+    sc = np.array([[127], [128], [126], [130], [127], [125]], np.uint8)
+    idx = np.array([1, 3, -1, 5], np.int32)
+    out, lse = oracle.attend_row(np.zeros((2, 32)), (np.full((6, 16), 0x22, np.uint8), sc), idx,
+                                 16, 1.0)
+    want = (2.0 + 8.0 + 0.25) / 3
+    np.testing.assert_allclose(out, want, rtol=1e-15)
+    np.testing.assert_allclose(lse, math.log(3), rtol=1e-15)
+    out, _ = oracle.attend_row(np.zeros((2, 32)), (np.full((6, 16), 0xa2, np.uint8), sc), idx,
+                               16, 1.0)
+    np.testing.assert_allclose(out[:, 0::2], want, rtol=1e-15)
+    np.testing.assert_allclose(out[:, 1::2], -want, rtol=1e-15)
+
+
 # -------------------------------------------------------------------------------- CSA ----
 
 def test_h3_csa_golden():
