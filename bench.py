@@ -59,6 +59,12 @@ WORKLOAD_TEXT = {
     "prefill_kv8": "prefill DSA over an MXFP8 latent KV cache (e4m3 entries, one E8M0 scale per "
                    "32): 1 sequence, L=T=32768 causal, top-k 2048, 128 heads, key 576 / value "
                    "512, bf16 q and out",
+    "decode_kv4": "decode DSA over an MXFP4 latent KV cache (e2m1 entries, one E8M0 scale per "
+                  "32): B=16 x 1 query, context L=8192, indexer 64x128 (bf16), top-k 2048, "
+                  "sparse MQA-MLA 128 heads, key 576 / value 512, bf16 q and out",
+    "prefill_kv4": "prefill DSA over an MXFP4 latent KV cache (e2m1 entries, one E8M0 scale per "
+                   "32): 1 sequence, L=T=32768 causal, top-k 2048, 128 heads, key 576 / value "
+                   "512, bf16 q and out",
     "hca_decode": "HCA decode: B=4 x 1 query over 1,048,576 tokens compressed 128:1 (8192 blocks), "
                   "dense attention over every visible block + 128-token raw window, 128 heads, "
                   "key 576 / value 512 (bf16)",
@@ -149,9 +155,10 @@ def _algorithmic(cfg, name, split=False):
             win += max(0, hi - lo + 1)
     if name == "compress_mean":
         return B * N * cfg.m * cfg.D_K * esz + B * N * cfg.D_K * esz, 0.0
-    if name == "mxfp8_to_bf16":
-        # reads the MXFP8 cache (codes and scales), writes its bf16 copy
-        return B * N * (cfg.D_K + cfg.D_K // 32) + B * N * cfg.D_K * 2, 0.0
+    if name in ("mxfp8_to_bf16", "mxfp4_to_bf16"):
+        # reads the MX cache (codes and scales), writes its bf16 copy
+        cb = cfg.D_K if name == "mxfp8_to_bf16" else cfg.D_K // 2
+        return B * N * (cb + cfg.D_K // 32) + B * N * cfg.D_K * 2, 0.0
     if name.startswith("indexer"):
         # every key row a sequence's queries can see is read once per sequence (decode: per query)
         keys = B * max(nvis) if T > 1 else pairs
@@ -168,7 +175,8 @@ def _algorithmic(cfg, name, split=False):
         # each gathered row must cross HBM once per step: once per query at decode, but rows
         # shared by the queries of one sequence (prefill) count once
         rows_kv = min(sel, float(B * N)) + min(win, float(B * (T + cfg.W - 1)) if cfg.W else 0.0)
-        kv_row = cfg.D_K + cfg.D_K // 32 if cfg.kv_dt == "mxfp8" else cfg.D_K * esz
+        kv_row = {"mxfp8": cfg.D_K + cfg.D_K // 32,
+                  "mxfp4": cfg.D_K // 2 + cfg.D_K // 32}.get(cfg.kv_dt, cfg.D_K * esz)
         byt = rows_kv * kv_row + rows * cfg.H * cfg.D_K * esz
         if not cfg.dense:
             byt += rows * cfg.top_k * 4  # the index list (HCA has none)
@@ -185,7 +193,7 @@ def _algorithmic(cfg, name, split=False):
 def _src_sha(kernel):
     """Hash of the sources a kernel is built from (its file and the shared device headers)."""
     files = {"indexer": "indexer.hip", "topk": "topk.hip", "attend": "attend.hip",
-             "compress": "compress.hip", "mxfp8": "compress.hip"}
+             "compress": "compress.hip", "mxfp8": "compress.hip", "mxfp4": "compress.hip"}
     for k, f in files.items():
         if kernel.startswith(k):
             h = hashlib.sha1()
@@ -245,7 +253,7 @@ def _device_inputs(wl):
     wl.drop("kv_raw")
     if c.compress:
         t["kv"] = torch.empty((c.B, c.N, c.D_K), dtype=tdt, device="cuda")
-    elif c.kv_dt == "mxfp8":
+    elif c.kv_dt in ("mxfp8", "mxfp4"):
         codes, sc = wl.kv()
         t["kv"] = (_dev(codes), _dev(sc))
     else:
@@ -365,8 +373,9 @@ def measure(name, steps, warmup, rotate=0, eager=False, copy_probe=False, n_inst
     per_chunk = _kernel_plan(cfg.with_(compress=False, B=1, T=chunk_rows), 2 if split else 1)
     # an MXFP8 cache read by unsplit attention is expanded to bf16 once per call
     mfma = cfg.D_K == 576 and cfg.D_V == 512 and cfg.H % 64 == 0
-    expand = cfg.kv_dt == "mxfp8" and mfma and not split
-    kernels = ((["compress_mean"] if cfg.compress else []) + (["mxfp8_to_bf16"] if expand else [])
+    expand = cfg.kv_dt in ("mxfp8", "mxfp4") and mfma and not split
+    xk = "mxfp4_to_bf16" if cfg.kv_dt == "mxfp4" else "mxfp8_to_bf16"
+    kernels = ((["compress_mean"] if cfg.compress else []) + ([xk] if expand else [])
                + per_chunk * n_chunks)
 
     if copy_probe:

@@ -103,7 +103,7 @@ typedef struct dsa_dims {
 #define DSA_OP_ATTEND 2
 #define DSA_OP_FORWARD 3
 #define DSA_OP_HCA 4
-/* The same calls over an MXFP8 latent cache (sparse_mla_attend_mxkv, dsa_forward / hca_forward
+/* The same calls over an MX latent cache (sparse_mla_attend_mxkv, dsa_forward / hca_forward
  * with kv_scale != NULL): attention launches with many query rows (run unsplit) read a bf16
  * copy of the whole cache the call first writes into the workspace (B*N*D_K*2 bytes more). */
 #define DSA_OP_ATTEND_MXKV 5
@@ -208,17 +208,21 @@ dsa_status sparse_mla_attend(const dsa_dims* d, dsa_dtype dt, const void* q, con
                              size_t ws_bytes, void* stream);
 
 /* Step 3 over a low-precision latent KV cache ([P3] V4.1-Flash summary: the main KV is kept
- * quantised): the same attention as sparse_mla_attend with kv stored as MXFP8 (OCP MX: e4m3
- * codes kv_codes [B,N,D_K] uint8, one E8M0 scale byte 2^(e-127) per 32 consecutive elements
- * along D_K in kv_scale [B,N,D_K/32]). Entry e's row is K_e[d] = e4m3(code[d]) * 2^(scale[d/32]
- * - 127), exact in bf16; q, kv_raw (window rows) and out are bf16, lse fp32. Needs D_K % 32 ==
- * 0 and N * D_K < 2^32 (else DSA_ERR_SHAPE); other rules and the sink as for sparse_mla_attend
- * with dt = BF16; ws: dsa_workspace_bytes(d, DSA_OP_ATTEND_MXKV) bytes. MFMA shapes (D_K = 576,
- * D_V = 512, H % 64 == 0): calls with few query rows (split attention, decode) convert the rows
- * they gather to bf16 inside the kernel; calls with many rows first expand the whole cache to
- * bf16 in ws, then attend at bf16 speed. Other shapes take the scalar kernel. */
+ * in FP4): the same attention as sparse_mla_attend with kv stored in an OCP MX format, kv_dt:
+ * DSA_MXFP8 (e4m3 codes kv_codes [B,N,D_K] uint8) or DSA_MXFP4 (e2m1 codes, two per byte, low
+ * nibble = even element: kv_codes [B,N,D_K/2]), with one E8M0 scale byte 2^(e-127) per 32
+ * consecutive elements along D_K in kv_scale [B,N,D_K/32]. Entry e's row is K_e[d] =
+ * code_value(d) * 2^(scale[d/32] - 127), exact in bf16; q, kv_raw (window rows) and out are
+ * bf16, lse fp32. Needs D_K % 32 == 0 and the code bytes of one sequence below 2^32 (else
+ * DSA_ERR_SHAPE), kv_dt MXFP8 or MXFP4 (else DSA_ERR_DTYPE); other rules and the sink as for
+ * sparse_mla_attend with dt = BF16; ws: dsa_workspace_bytes(d, DSA_OP_ATTEND_MXKV) bytes. MFMA
+ * shapes (D_K = 576, D_V = 512, H % 64 == 0): calls with few query rows (split attention,
+ * decode) convert the rows they gather to bf16 inside the kernel; calls with many rows first
+ * expand the whole cache to bf16 in ws, then attend at bf16 speed. Other shapes take the
+ * scalar kernel. */
 dsa_status sparse_mla_attend_mxkv(const dsa_dims* d, const void* q, const uint8_t* kv_codes,
-                                  const uint8_t* kv_scale, const int32_t* idx, const void* kv_raw,
+                                  const uint8_t* kv_scale, dsa_dtype kv_dt, const int32_t* idx,
+                                  const void* kv_raw,
                                   int64_t raw_base, int64_t n_raw, const int32_t* q_pos,
                                   float softmax_scale, const float* sink, void* out, float* lse,
                                   void* ws, size_t ws_bytes, void* stream);
@@ -261,9 +265,10 @@ typedef struct dsa_forward_args {
                             holds e4m3 codes [B,T,H_I,D_I]); indexer only                 */
   const int32_t* seq_len;/* [B] or NULL: entries held per sequence (ragged batch)           */
   const float* sink;     /* [H] or NULL: attention-sink logit per head (sparse_mla_attend)  */
-  const uint8_t* kv_scale;/* NULL, or the E8M0 scales [B,N,D_K/32] of an MXFP8 kv (then kv
-                            holds e4m3 codes [B,N,D_K]; dt == BF16, compress == 0), as in
+  const uint8_t* kv_scale;/* NULL, or the E8M0 scales [B,N,D_K/32] of an MX kv (then kv holds
+                            its codes; dt == BF16, compress == 0), as in
                             sparse_mla_attend_mxkv                                        */
+  dsa_dtype kv_dt;       /* with kv_scale: DSA_MXFP8 or DSA_MXFP4 (the codes' format)     */
 } dsa_forward_args;
 
 /* Fused path: [compress] -> indexer_scores -> topk_select -> sparse_mla_attend on `stream`

@@ -55,7 +55,7 @@ class ForwardArgs(ctypes.Structure):
                 ("scores", ctypes.c_void_p), ("idx", ctypes.c_void_p),
                 ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32),
                 ("q_scale", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
-                ("sink", ctypes.c_void_p), ("kv_scale", ctypes.c_void_p)]
+                ("sink", ctypes.c_void_p), ("kv_scale", ctypes.c_void_p), ("kv_dt", ctypes.c_int)]
 
 
 _vp, _i64, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
@@ -72,8 +72,8 @@ _lib.indexer_scores.argtypes = [_D, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, ctype
 _lib.topk_select.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.sparse_mla_attend.argtypes = [_D, ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
                                    ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]
-_lib.sparse_mla_attend_mxkv.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
-                                        ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.sparse_mla_attend_mxkv.argtypes = [_D, _vp, _vp, _vp, ctypes.c_int, _vp, _vp, _i64, _i64,
+                                        _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.dsa_forward.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]
 _lib.hca_forward.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]
 _lib.dsa_forward_noalloc.argtypes = [_D, ctypes.POINTER(ForwardArgs), _vp]
@@ -220,10 +220,15 @@ def topk_select(scores: torch.Tensor, q_pos: torch.Tensor, top_k: int, m: int = 
 # ---- step 3 -----------------------------------------------------------------------------------
 
 def _kv(kv):
-    """-> (kv or codes, scales or None); an MXFP8 cache is (codes [B,N,D_K], scales)."""
+    """-> (kv or codes, scales or None, codes' dtype); an MX cache is (codes, scales [B,N,D_K/32])
+    with codes [B,N,D_K] (MXFP8) or [B,N,D_K/2] (MXFP4, two e2m1 codes per byte)."""
     if isinstance(kv, tuple):
-        return kv[0], kv[1]
-    return kv, None
+        codes, scales = kv
+        d_k = 32 * scales.shape[-1]
+        if codes.shape[-1] not in (d_k, d_k // 2):
+            raise ValueError("MX cache: codes must hold D_K (MXFP8) or D_K/2 (MXFP4) bytes per row")
+        return codes, scales, (MXFP8 if codes.shape[-1] == d_k else MXFP4)
+    return kv, None, F32
 
 
 def sparse_mla_attend(q: torch.Tensor, kv, idx: torch.Tensor, q_pos: torch.Tensor,
@@ -231,11 +236,11 @@ def sparse_mla_attend(q: torch.Tensor, kv, idx: torch.Tensor, q_pos: torch.Tenso
                       raw_base: int = 0, W: int = 0, m: int = 1,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       want_lse: bool = True, sink: Optional[torch.Tensor] = None):
-    """q [B,T,H,D_K], kv [B,N,D_K] or MXFP8 (codes, scales), idx [B,T,k] int32, optional raw
+    """q [B,T,H,D_K], kv [B,N,D_K] or MX (codes, scales), idx [B,T,k] int32, optional raw
     window rows kv_raw [B,n_raw,D_K] at positions raw_base.., optional attention-sink logits
     sink [H] fp32 -> (out [B,T,H,D_V], lse [B,T,H] fp32)."""
     B, T, H, D_K = q.shape
-    kvt, kvs = _kv(kv)
+    kvt, kvs, kvdt = _kv(kv)
     N = kvt.shape[1]
     k = idx.shape[2]
     if out is None:
@@ -246,7 +251,7 @@ def sparse_mla_attend(q: torch.Tensor, kv, idx: torch.Tensor, q_pos: torch.Tenso
     ws = _workspace(d, OP_ATTEND if kvs is None else OP_ATTEND_MXKV, q.device)
     n_raw = 0 if kv_raw is None else kv_raw.shape[1]
     if kvs is not None:
-        _check(_lib.sparse_mla_attend_mxkv(ctypes.byref(d), _ptr(q), _ptr(kvt), _ptr(kvs),
+        _check(_lib.sparse_mla_attend_mxkv(ctypes.byref(d), _ptr(q), _ptr(kvt), _ptr(kvs), kvdt,
                                            _ptr(idx), _ptr(kv_raw), raw_base, n_raw, _ptr(q_pos),
                                            softmax_scale, _ptr(sink), _ptr(out), _ptr(lse),
                                            _ptr(ws), 0 if ws is None else ws.numel(), _stream(q)),
@@ -281,7 +286,7 @@ class Forward:
         self.lse = lse if lse is not None else (
             torch.empty((B, T, H), dtype=torch.float32, device=dev) if want_lse else None)
         self.scores, self.idx = scores, idx
-        kvt, kvs = _kv(kv)
+        kvt, kvs, kvdt = _kv(kv)
         self.ws = _workspace(self.d, OP_FORWARD if kvs is None else OP_FORWARD_MXKV, dev)
         self._keep = (qt, qs, w, kt, ks, q, kvt, kvs, q_pos, kv_raw, seq_len, sink)
         n_raw = 0 if kv_raw is None else kv_raw.shape[1]
@@ -289,7 +294,7 @@ class Forward:
                                 _ptr(kvt), _ptr(kv_raw), raw_base, n_raw, 1 if compress else 0,
                                 _ptr(q_pos), softmax_scale, _ptr(self.out), _ptr(self.lse),
                                 _ptr(scores), _ptr(idx), None, 0, _ptr(qs), _ptr(seq_len),
-                                _ptr(sink), _ptr(kvs))
+                                _ptr(sink), _ptr(kvs), kvdt)
         self.device = dev
 
     def set_events(self, events) -> None:
@@ -345,7 +350,7 @@ class HcaForward(Forward):
                  kv_raw=None, raw_base: int = 0, compress: bool = False, out=None, lse=None,
                  want_lse: bool = True, seq_len=None, sink=None):
         B, T, H, D_K = q.shape
-        kvt, kvs = _kv(kv)
+        kvt, kvs, kvdt = _kv(kv)
         N = kvt.shape[1]
         self.d = dims(B=B, T=T, N=N, H=H, D_K=D_K, D_V=D_V, m=m, W=W)
         dev = q.device
@@ -359,7 +364,8 @@ class HcaForward(Forward):
         self.args = ForwardArgs(_dt(q), _dt(q), None, None, None, None, _ptr(q), _ptr(kvt),
                                 _ptr(kv_raw), raw_base, n_raw, 1 if compress else 0,
                                 _ptr(q_pos), softmax_scale, _ptr(self.out), _ptr(self.lse),
-                                None, None, None, 0, None, _ptr(seq_len), _ptr(sink), _ptr(kvs))
+                                None, None, None, 0, None, _ptr(seq_len), _ptr(sink), _ptr(kvs),
+                                kvdt)
         self.device = dev
 
     def run(self, stream: Optional[int] = None) -> torch.Tensor:

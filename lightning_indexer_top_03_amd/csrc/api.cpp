@@ -164,13 +164,16 @@ Shape hca_shape(const dsa_dims* d) {
   return s;
 }
 
-// An MXFP8 latent cache: whole scale blocks per row, and a sequence's code bytes addressable
-// with 32-bit offsets.
+// An MX latent cache: whole scale blocks per row, and a sequence's code bytes addressable with
+// 32-bit offsets (the MXFP4 codes take half the bytes of MXFP8 ones).
 bool mxkv_shape_ok(const dsa_dims* d) {
   return d->D_K % 32 == 0 && (uint64_t)d->N * (uint64_t)d->D_K < (1ull << 32);
 }
+bool mxkv_dt_ok(dsa_dtype dt) { return dt == DSA_MXFP8 || dt == DSA_MXFP4; }
+// the kernels' format code of an MX cache
+int mxkv_fmt(dsa_dtype dt) { return dt == DSA_MXFP4 ? FMT_MXFP4 : FMT_MXFP8; }
 
-// An MXFP8 cache read by attention launches that each hold many query rows (rows query rows per
+// An MX cache read by attention launches that each hold many query rows (rows query rows per
 // launch, the attention unsplit) is first expanded to bf16 in the workspace, once per call: the
 // bf16 kernel then gathers it at full speed, and the expansion costs one pass over the cache.
 // Few-row launches (decode) convert only the rows they gather, inside the attention kernel.
@@ -196,7 +199,8 @@ dsa_status check_forward(const dsa_dims* d, const dsa_forward_args* a) {
   if (a->raw_base < 0 || a->n_raw < 0) return DSA_ERR_SHAPE;
   if (a->compress && (a->raw_base != 0 || a->n_raw / d->m != d->N)) return DSA_ERR_SHAPE;
   // MXFP8 entries: bf16 q / kv_raw / out, stored (not compressed) entries, D_K % 32 == 0
-  if (a->kv_scale && (a->dt != DSA_BF16 || a->compress)) return DSA_ERR_DTYPE;
+  if (a->kv_scale && (a->dt != DSA_BF16 || a->compress || !mxkv_dt_ok(a->kv_dt)))
+    return DSA_ERR_DTYPE;
   if (a->kv_scale && !mxkv_shape_ok(d)) return DSA_ERR_SHAPE;
   const void* ptrs16[] = {a->q_I, a->w, a->k_I, a->q, a->kv, a->out, a->kv_raw, a->scores,
                           a->idx};
@@ -238,12 +242,13 @@ dsa_status run_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, h
   const uint8_t* kv_sc = a->kv_scale;
   if (kv_sc != nullptr && mxkv_expand_bytes(s, d, R) > 0) {
     void* kv16 = wsb + L.total;
-    if (hipError_t e = launch_mxfp8_to_bf16(static_cast<const uint8_t*>(a->kv), kv_sc,
-                                            (int64_t)d->B * d->N, d->D_K, kv16, st))
+    if (hipError_t e = launch_mx_to_bf16(mxkv_fmt(a->kv_dt), static_cast<const uint8_t*>(a->kv),
+                                         kv_sc, (int64_t)d->B * d->N, d->D_K, kv16, st))
       return launched(e);
     kv_att = kv16;
     kv_sc = nullptr;
   }
+  const int kv_fmt = mxkv_fmt(a->kv_dt);
   for (int64_t q0 = 0; q0 < rows; q0 += R) {
     const int64_t nr = std::min(R, rows - q0);
     float* sc = keep_scores ? a->scores + (size_t)q0 * d->N : ws_scores;
@@ -267,7 +272,7 @@ dsa_status run_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, h
     }
     if (fused) {
       // top-k inside the attention kernel: idx is written only when the caller wants it
-      if (hipError_t e = launch_attend_fused(s, q0, nr, a->q, kv_att, kv_sc, sc,
+      if (hipError_t e = launch_attend_fused(s, q0, nr, a->q, kv_att, kv_sc, kv_fmt, sc,
                                              a->idx ? a->idx + (size_t)q0 * d->top_k : nullptr,
                                              d->W > 0 ? a->kv_raw : nullptr, a->raw_base,
                                              a->n_raw, a->q_pos, a->seq_len, a->sink,
@@ -277,7 +282,7 @@ dsa_status run_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, h
       if (seg_stride == 0)
         if (hipError_t e = launch_topk(s, q0, nr, sc, a->q_pos, a->seq_len, ix, ws_topk, st))
           return launched(e);
-      if (hipError_t e = launch_attend(s, q0, nr, fmt, a->q, kv_att, kv_sc, ix,
+      if (hipError_t e = launch_attend(s, q0, nr, fmt, a->q, kv_att, kv_sc, kv_fmt, ix,
                                        d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw,
                                        a->q_pos, nullptr, a->sink, a->softmax_scale, a->out,
                                        a->lse, ws_att, st))
@@ -307,7 +312,7 @@ const char* dsa_status_str(int status) {
   }
 }
 
-int dsa_version(void) { return 210; }
+int dsa_version(void) { return 220; }
 
 size_t dsa_workspace_bytes(const dsa_dims* d, int op) {
   if (op == DSA_OP_HCA || op == DSA_OP_HCA_MXKV) {
@@ -415,18 +420,20 @@ dsa_status sparse_mla_attend(const dsa_dims* d, dsa_dtype dt, const void* q, con
   if (need && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return DSA_ERR_ALIGN;
   if (dsa_status st = check_device()) return st;
-  return launched(launch_attend(s, 0, (int64_t)d->B * d->T, fmt, q, kv, nullptr, idx,
+  return launched(launch_attend(s, 0, (int64_t)d->B * d->T, fmt, q, kv, nullptr, 0, idx,
                                 d->W > 0 ? kv_raw : nullptr, raw_base, n_raw, q_pos, nullptr,
                                 sink, softmax_scale, out, lse, ws, (hipStream_t)stream));
 }
 
 dsa_status sparse_mla_attend_mxkv(const dsa_dims* d, const void* q, const uint8_t* kv_codes,
-                                  const uint8_t* kv_scale, const int32_t* idx, const void* kv_raw,
-                                  int64_t raw_base, int64_t n_raw, const int32_t* q_pos,
-                                  float softmax_scale, const float* sink, void* out, float* lse,
-                                  void* ws, size_t ws_bytes, void* stream) {
+                                  const uint8_t* kv_scale, dsa_dtype kv_dt, const int32_t* idx,
+                                  const void* kv_raw, int64_t raw_base, int64_t n_raw,
+                                  const int32_t* q_pos, float softmax_scale, const float* sink,
+                                  void* out, float* lse, void* ws, size_t ws_bytes,
+                                  void* stream) {
   if (dsa_status st = check_dims(d)) return st;
   if (dsa_status st = check_attend_shape(d)) return st;
+  if (!mxkv_dt_ok(kv_dt)) return DSA_ERR_DTYPE;
   if (!mxkv_shape_ok(d)) return DSA_ERR_SHAPE;
   if (!q || !kv_codes || !kv_scale || !idx || !q_pos || !out) return DSA_ERR_NULL;
   if (d->W > 0 && !kv_raw) return DSA_ERR_NULL;
@@ -447,13 +454,13 @@ dsa_status sparse_mla_attend_mxkv(const dsa_dims* d, const void* q, const uint8_
   const uint8_t* kv_sc = kv_scale;
   if (expand) {
     void* kv16 = static_cast<char*>(ws) + align_up(part);
-    if (hipError_t e = launch_mxfp8_to_bf16(kv_codes, kv_scale, (int64_t)d->B * d->N, d->D_K,
-                                            kv16, st))
+    if (hipError_t e = launch_mx_to_bf16(mxkv_fmt(kv_dt), kv_codes, kv_scale,
+                                         (int64_t)d->B * d->N, d->D_K, kv16, st))
       return launched(e);
     kv_att = kv16;
     kv_sc = nullptr;
   }
-  return launched(launch_attend(s, 0, rows, FMT_BF16, q, kv_att, kv_sc, idx,
+  return launched(launch_attend(s, 0, rows, FMT_BF16, q, kv_att, kv_sc, mxkv_fmt(kv_dt), idx,
                                 d->W > 0 ? kv_raw : nullptr, raw_base, n_raw, q_pos, nullptr,
                                 sink, softmax_scale, out, lse, ws, st));
 }
@@ -489,7 +496,8 @@ dsa_status hca_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
   if ((d->W > 0 || a->compress) && !a->kv_raw) return DSA_ERR_NULL;
   if (a->raw_base < 0 || a->n_raw < 0) return DSA_ERR_SHAPE;
   if (a->compress && (a->raw_base != 0 || a->n_raw / d->m != d->N)) return DSA_ERR_SHAPE;
-  if (a->kv_scale && (a->dt != DSA_BF16 || a->compress)) return DSA_ERR_DTYPE;
+  if (a->kv_scale && (a->dt != DSA_BF16 || a->compress || !mxkv_dt_ok(a->kv_dt)))
+    return DSA_ERR_DTYPE;
   if (a->kv_scale && !mxkv_shape_ok(d)) return DSA_ERR_SHAPE;
   const Shape s = hca_shape(d);
   const int fmt = a->dt == DSA_BF16 ? FMT_BF16 : FMT_F32;
@@ -520,13 +528,13 @@ dsa_status hca_forward(const dsa_dims* d, const dsa_forward_args* a, void* ws, s
   const uint8_t* kv_sc = a->kv_scale;
   if (expand) {
     void* kv16 = static_cast<char*>(ws) + align_up(part);
-    if (hipError_t e = launch_mxfp8_to_bf16(static_cast<const uint8_t*>(a->kv), kv_sc,
-                                            (int64_t)d->B * d->N, d->D_K, kv16, st))
+    if (hipError_t e = launch_mx_to_bf16(mxkv_fmt(a->kv_dt), static_cast<const uint8_t*>(a->kv),
+                                         kv_sc, (int64_t)d->B * d->N, d->D_K, kv16, st))
       return launched(e);
     kv_att = kv16;
     kv_sc = nullptr;
   }
-  return launched(launch_attend(s, 0, rows, fmt, a->q, kv_att, kv_sc, nullptr,
+  return launched(launch_attend(s, 0, rows, fmt, a->q, kv_att, kv_sc, mxkv_fmt(a->kv_dt), nullptr,
                                 d->W > 0 ? a->kv_raw : nullptr, a->raw_base, a->n_raw, a->q_pos,
                                 a->seq_len, a->sink, a->softmax_scale, a->out, a->lse, ws, st));
 }

@@ -234,7 +234,9 @@ __device__ __forceinline__ float row16_max(float x) {
 // indexer scores; every workgroup of a row selects the row's top-k (block_threshold /
 // block_ranks of select.h, PER entries per thread, in ascending index order) and keeps its own
 // split's slice; the workgroup of split 0 / head group 0 also writes the row of idx_out.
-template <int NS, int PER, bool KV8>
+// KVF: the entries' storage, 0 = bf16 rows, 8 = MXFP8 (e4m3 codes [B, N, 576]), 4 = MXFP4
+// (e2m1 code pairs [B, N, 288], low nibble first); MX rows carry one E8M0 scale per 32 values.
+template <int NS, int PER, int KVF>
 __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ kv_raw, int64_t raw_base,
@@ -245,6 +247,8 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     const int32_t* __restrict__ seq_len, const float* __restrict__ sink,
     const uint8_t* __restrict__ kv_scale) {
   constexpr int DK = 576, DV = 512, KS = DK / 32, DB = DV / 16;
+  constexpr bool KV8 = KVF != 0;             // low-precision entries, converted in the kernel
+  constexpr int CB = KVF == 4 ? DK / 2 : DK;  // code bytes per entry
   __shared__ __attribute__((aligned(16))) char smem[NS * kStage];
   __shared__ __attribute__((aligned(16))) u32x4_t pbuf[2][4][64];  // P, per head block
   // rescale factor per head when the reference moved, and whether it moved (per head block)
@@ -252,10 +256,10 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
   __shared__ __attribute__((aligned(16))) uint32_t fbuf[2][4];
   __shared__ float sml[4][2][16];    // per head: [1] = the output multiplier (unsplit calls)
   extern __shared__ __attribute__((aligned(16))) int scode[];  // entry codes, whole tiles
-  // MXFP8 entries: the e4m3 codes of the next tile, 576 bytes per row, staged by DMA one
-  // iteration before they are converted into the ring
-  static_assert(!KV8 || NS == 3, "the MXFP8 staging buffer fits beside a 3-stage ring only");
-  __shared__ __attribute__((aligned(16))) char sf8[KV8 ? kTile * 576 : 16];
+  // MX entries: the codes of the next tile, CB bytes per row, staged by DMA one iteration
+  // before they are converted into the ring
+  static_assert(!KV8 || NS == 3, "the MX staging buffer fits beside a 3-stage ring only");
+  __shared__ __attribute__((aligned(16))) char sf8[KV8 ? kTile * CB : 16];
   // ... and their E8M0 scale bytes, one per dword (a 1-byte DMA fills one dword per lane)
   __shared__ __attribute__((aligned(16))) uint32_t sf8s[KV8 ? kTile * 18 : 4];
 
@@ -446,24 +450,25 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
     }
   };
   constexpr int kDmas = 9;
-  // MXFP8 entries (KV8): a value wave's 8 rows (4608 code bytes, 144 scale bytes) come by DMA
+  // MX entries (KV8): a value wave's 8 rows (8 CB code bytes, 144 scale bytes) come by DMA
   // into the staging buffers one iteration before they are needed (dma8); convert8 turns them
   // into bf16 in the ring stage, in the layout of the DMA'd rows.
   // Raw window rows (bf16) take the DMA above; masked entries convert row 0 (finite; P is 0).
-  const uint8_t* kv8_b = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * N * DK;
+  const uint8_t* kv8_b = reinterpret_cast<const uint8_t*>(kv) + (size_t)b * N * CB;
   const uint8_t* ksc_b = kv_scale + (size_t)b * N * (DK / 32);
   const uint32_t f8base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(lds_void_t*)(sf8 + (KV8 ? vrow * 576 : 0)));
+      (uint32_t)(uintptr_t)(lds_void_t*)(sf8 + (KV8 ? vrow * CB : 0)));
   const uint32_t f8sbase = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(lds_void_t*)(sf8s + (KV8 ? vrow * 18 : 0)));
   auto dma8 = [&](int codes) {  // lanes 0..7 of `codes`: the entry codes of rows vrow + 0..7
+    constexpr int CPR = CB / 16, NCH = 8 * CPR;  // 16-byte chunks per row / per 8 rows
 #pragma unroll
-    for (int k = 0; k < 5; ++k) {  // 288 chunks of 16 code bytes
-      const int ch = 64 * k + lane, rr = ch / 36, cc = ch - 36 * rr;
+    for (int k = 0; k < (NCH + 63) / 64; ++k) {
+      const int ch = 64 * k + lane, rr = ch / CPR, cc = ch - CPR * rr;
       const int code = __shfl(codes, min(rr, 7), 64);
-      if (ch < 288 && code > -2)
+      if (ch < NCH && code > -2)
         __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const void*>(kv8_b + ((uint32_t)max(code, 0) * (uint32_t)DK + 16u * (uint32_t)cc)),
+            reinterpret_cast<const void*>(kv8_b + ((uint32_t)max(code, 0) * (uint32_t)CB + 16u * (uint32_t)cc)),
             (lds_void_t*)(uintptr_t)(f8base + 1024 * k), 16, 0, 0);
     }
 #pragma unroll
@@ -479,34 +484,46 @@ __global__ __launch_bounds__(kAtWaves * 64, 1) void attend_mfma_dma(
   // d_code: the entry codes of the tile being converted (rows vrow + 0..7 in lanes 0..7).
   // Unit r < 8: the latent part of row vrow + r, lane l converting codes 8l .. 8l+7 (all
   // offsets are immediates off one lane base); then the rope parts, lane l converting codes
-  // 512 + 8 (l & 7) .. of row vrow + (l >> 3).
-  auto cvt8 = [&](u32x2_t w, uint32_t e) -> u32x4_t {
+  // 512 + 8 (l & 7) .. of row vrow + (l >> 3). Eight e4m3 codes are 8 bytes, eight e2m1 codes
+  // 4 (two per byte, low nibble first); either way 16 bytes of bf16.
+  auto cvt8 = [&](const char* p, uint32_t e) -> u32x4_t {
     // E8M0 e -> 2^(e - 127) (e == 0 is the subnormal 2^-127)
     const float sc = __uint_as_float(e != 0u ? e << 23 : 0x00400000u);
-    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, false);
-    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, true);
-    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, false);
-    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, true);
+    bf16x2_t p0, p1, p2, p3;
+    if constexpr (KVF == 4) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+      p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+      p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+      p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+      p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+    } else {
+      const u32x2_t w = *reinterpret_cast<const u32x2_t*>(p);
+      p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, false);
+      p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, true);
+      p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, false);
+      p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, true);
+    }
     return u32x4_t{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
   };
   auto convert8 = [&](char* st) {
-    const char* src = sf8 + (KV8 ? vrow * 576 : 0);
+    constexpr int BPU = KVF == 4 ? 4 : 8;  // code bytes per unit of 8 codes
+    const char* src = sf8 + (KV8 ? vrow * CB : 0);
     const uint32_t* ssrc = sf8s + (KV8 ? vrow * 18 : 0);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       if (__builtin_amdgcn_readlane(d_code, r) > -2) {
-        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src + r * 576 + 8 * lane);
         const uint32_t e = ssrc[r * 18 + (lane >> 2)] & 0xffu;
-        *reinterpret_cast<u32x4_t*>(st + (vrow + r) * kLatStride + 16 * lane) = cvt8(w, e);
+        *reinterpret_cast<u32x4_t*>(st + (vrow + r) * kLatStride + 16 * lane) =
+            cvt8(src + r * CB + BPU * lane, e);
       }
     }
     {
       const int r = lane >> 3, c = lane & 7, R = vrow + r;
       if (__shfl(d_code, r, 64) > -2) {
-        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src + r * 576 + 512 + 8 * c);
         const uint32_t e = ssrc[r * 18 + 16 + (c >> 2)] & 0xffu;
-        *reinterpret_cast<u32x4_t*>(st + kStageLat + R * 128 + 16 * (c ^ ((R >> 1) & 7))) = cvt8(w, e);
+        *reinterpret_cast<u32x4_t*>(st + kStageLat + R * 128 + 16 * (c ^ ((R >> 1) & 7))) =
+            cvt8(src + r * CB + 64 * BPU + BPU * c, e);
       }
     }
     // the staging reads are done before the next dma8 overwrites the buffers
@@ -918,6 +935,14 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return (c & 0x80u) ? -v : v;
 }
 
+// One OCP E2M1 code (a nibble): sign, 2 exponent bits, 1 mantissa bit; magnitudes 0, 0.5, 1,
+// 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, mt = c & 1u;
+  const float v = e == 0u ? 0.5f * (float)mt : __uint_as_float(((e + 126u) << 23) | (mt << 22));
+  return (c & 8u) ? -v : v;
+}
+
 // E8M0 scale byte e -> 2^(e - 127) (e == 0: the subnormal 2^-127; 0xFF is NaN)
 __device__ __forceinline__ float e8m0_value(uint32_t e) {
   if (e == 255u) return __builtin_nanf("");
@@ -931,15 +956,21 @@ __global__ __launch_bounds__(256) void attend_generic(
     const int32_t* __restrict__ q_pos, int T_, int N, int H, int DK, int DV, int top_k, int W,
     float scale, int64_t qi0, T* __restrict__ out, float* __restrict__ lse, int m,
     const int32_t* __restrict__ seq_len, const float* __restrict__ sink,
-    const uint8_t* __restrict__ kv_scale) {
-  // kv_scale != nullptr: kv holds MXFP8 entries (e4m3 codes [B, N, DK] as bytes, E8M0 scales
-  // [B, N, DK / 32]); kv_raw rows stay in T
+    const uint8_t* __restrict__ kv_scale, int kv4) {
+  // kv_scale != nullptr: kv holds MX entries, e4m3 codes [B, N, DK] (kv4 == 0) or e2m1 code
+  // pairs [B, N, DK / 2] (low nibble first), and E8M0 scales [B, N, DK / 32]; kv_raw rows stay
+  // in T
+  auto code_value = [&](size_t r8, int d) -> float {
+    const uint8_t* kv8 = reinterpret_cast<const uint8_t*>(kv);
+    return kv4 ? e2m1_value((uint32_t)(kv8[r8 * (DK / 2) + d / 2] >> (4 * (d & 1))) & 15u)
+               : e4m3_value(kv8[r8 * DK + d]);
+  };
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int E = top_k + W;
   float* sq = reinterpret_cast<float*>(smem);   // [DK]
   float* sz = sq + DK;                           // [E]
   const T** ssrc = reinterpret_cast<const T**>(sz + E + ((E & 1) ? 1 : 0));  // [E]
-  int* srow8 = reinterpret_cast<int*>(ssrc + E);  // [E]: MXFP8 entry row, or -1
+  int* srow8 = reinterpret_cast<int*>(ssrc + E);  // [E]: MX entry row, or -1
   __shared__ float red[256 / 64];
   const int h = blockIdx.x;
   const int64_t row = blockIdx.y;
@@ -950,7 +981,6 @@ __global__ __launch_bounds__(256) void attend_generic(
   const int lim = idx != nullptr ? N : n_visible(p, m, N, seq_len, b);
   for (int d = threadIdx.x; d < DK; d += blockDim.x) sq[d] = ldv(q, ((size_t)qi * H + h) * DK + d);
   __syncthreads();
-  const uint8_t* kv8 = reinterpret_cast<const uint8_t*>(kv);
   float mx = kNegInf;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const T* src = entry_row<T>(e, idxrow, top_k, kv, b, N, DK, kv_raw, raw_base, n_raw, p, W, lim);
@@ -969,13 +999,12 @@ __global__ __launch_bounds__(256) void attend_generic(
       for (int d = 0; d < DK; ++d) dot += sq[d] * ldv(src, d);  // 8 loads in flight at a time
       z = dot * scale;
     } else if (r8 >= 0) {
-      const uint8_t* c8 = kv8 + (size_t)r8 * DK;
       const uint8_t* s8 = kv_scale + (size_t)r8 * (DK / 32);
       float dot = 0.f;
       for (int d0 = 0; d0 < DK; d0 += 32) {
         float blk = 0.f;
 #pragma unroll 8
-        for (int d = d0; d < d0 + 32; ++d) blk += sq[d] * e4m3_value(c8[d]);
+        for (int d = d0; d < d0 + 32; ++d) blk += sq[d] * code_value((size_t)r8, d);
         dot += blk * e8m0_value(s8[d0 / 32]);
       }
       z = dot * scale;
@@ -1011,7 +1040,7 @@ __global__ __launch_bounds__(256) void attend_generic(
         a += sz[e] * ldv(ssrc[e], d);
       } else if (srow8[e] >= 0) {
         const size_t r8 = (size_t)srow8[e];
-        a += sz[e] * (e4m3_value(kv8[r8 * DK + d]) * e8m0_value(kv_scale[r8 * (DK / 32) + d / 32]));
+        a += sz[e] * (code_value(r8, d) * e8m0_value(kv_scale[r8 * (DK / 32) + d / 32]));
       }
     }
     a *= inv;
@@ -1056,28 +1085,31 @@ size_t attend_ws_bytes(const Shape& s, int64_t nrows, int fmt) {
 // buffers), set as each kernel's attribute on every device it runs on, once per device.
 struct AttendLds {
   hipError_t err;
-  size_t dyn4, dyn3, dyn3_kv8;
+  size_t dyn4, dyn3, dyn3_kv8, dyn3_kv4;
 };
 
 static const AttendLds& attend_lds() {
   constexpr size_t kLdsMax = 160 * 1024;
   static AttendLds per_dev[64];
   static std::once_flag once[64];
-  static const AttendLds bad{hipErrorInvalidDevice, 0, 0, 0};
+  static const AttendLds bad{hipErrorInvalidDevice, 0, 0, 0, 0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return bad;
   std::call_once(once[dev], [dev] {
     AttendLds& r = per_dev[dev];
     r.err = hipSuccess;
-    const void* k4[] = {reinterpret_cast<const void*>(&attend_mfma_dma<4, 0, false>),
-                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 16, false>),
-                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 64, false>)};
-    const void* k3[] = {reinterpret_cast<const void*>(&attend_mfma_dma<3, 0, false>),
-                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 16, false>),
-                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 64, false>)};
-    const void* k3x[] = {reinterpret_cast<const void*>(&attend_mfma_dma<3, 0, true>),
-                         reinterpret_cast<const void*>(&attend_mfma_dma<3, 16, true>),
-                         reinterpret_cast<const void*>(&attend_mfma_dma<3, 64, true>)};
+    const void* k4[] = {reinterpret_cast<const void*>(&attend_mfma_dma<4, 0, 0>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 16, 0>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<4, 64, 0>)};
+    const void* k3[] = {reinterpret_cast<const void*>(&attend_mfma_dma<3, 0, 0>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 16, 0>),
+                        reinterpret_cast<const void*>(&attend_mfma_dma<3, 64, 0>)};
+    const void* k3x[] = {reinterpret_cast<const void*>(&attend_mfma_dma<3, 0, 8>),
+                         reinterpret_cast<const void*>(&attend_mfma_dma<3, 16, 8>),
+                         reinterpret_cast<const void*>(&attend_mfma_dma<3, 64, 8>)};
+    const void* k3x4[] = {reinterpret_cast<const void*>(&attend_mfma_dma<3, 0, 4>),
+                          reinterpret_cast<const void*>(&attend_mfma_dma<3, 16, 4>),
+                          reinterpret_cast<const void*>(&attend_mfma_dma<3, 64, 4>)};
     auto room = [&](const void* const* ks, size_t& dyn) {
       dyn = kLdsMax;
       for (int j = 0; j < 3 && r.err == hipSuccess; ++j) {
@@ -1092,6 +1124,7 @@ static const AttendLds& attend_lds() {
     room(k4, r.dyn4);
     room(k3, r.dyn3);
     room(k3x, r.dyn3_kv8);
+    room(k3x4, r.dyn3_kv4);
   });
   return per_dev[dev];
 }
@@ -1099,7 +1132,7 @@ static const AttendLds& attend_lds() {
 // The MFMA attention for rows qi0 .. qi0+nrows-1 (+ the split merge). scores != nullptr selects
 // the fused top-k variant (entries straight from the indexer scores, idx_out optional).
 static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows, const void* q,
-                                     const void* kv, const uint8_t* kv_scale,
+                                     const void* kv, const uint8_t* kv_scale, int kv_fmt,
                                      const int32_t* idx, const float* scores,
                                      int32_t* idx_out, const void* kv_raw, int64_t raw_base,
                                      int64_t n_raw, const int32_t* q_pos,
@@ -1122,19 +1155,24 @@ static hipError_t launch_attend_mfma(const Shape& s, int64_t qi0, int64_t nrows,
   const int per_thread = scores == nullptr ? 0 : (s.N <= 16 * kAtWaves * 64 ? 16 : 64);
   if (scores != nullptr && s.N > 64 * kAtWaves * 64) return hipErrorInvalidValue;
   hipError_t e;
-#define DSA_ATT2(NS_, PER_, KV8_)                                                                \
-  e = launch(attend_mfma_dma<NS_, PER_, KV8_>, grid, kAtWaves * 64, code_bytes, st,              \
+#define DSA_ATT2(NS_, PER_, KVF_)                                                                \
+  e = launch(attend_mfma_dma<NS_, PER_, KVF_>, grid, kAtWaves * 64, code_bytes, st,              \
              static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,             \
              static_cast<const uint16_t*>(kv_raw), raw_base, n_raw, q_pos, s.T, s.N, s.H,        \
              s.top_k, s.W, scale * kLog2e, qi0, ns, per, static_cast<uint16_t*>(out), lse,       \
              part_o, part_ml, nitems, scores, s.m, idx_out, seq_len, sink, kv_scale)
-#define DSA_ATT(NS_, PER_) DSA_ATT2(NS_, PER_, false)
-  if (kv_scale != nullptr) {
-    // MXFP8 entries: the 3-stage ring beside the code staging buffer
+#define DSA_ATT(NS_, PER_) DSA_ATT2(NS_, PER_, 0)
+  if (kv_scale != nullptr && kv_fmt == FMT_MXFP4) {
+    // MX entries: the 3-stage ring beside the code staging buffer
+    if (code_bytes > lds.dyn3_kv4) return hipErrorInvalidValue;
+    if (per_thread == 0) DSA_ATT2(3, 0, 4);
+    else if (per_thread == 16) DSA_ATT2(3, 16, 4);
+    else DSA_ATT2(3, 64, 4);
+  } else if (kv_scale != nullptr) {
     if (code_bytes > lds.dyn3_kv8) return hipErrorInvalidValue;
-    if (per_thread == 0) DSA_ATT2(3, 0, true);
-    else if (per_thread == 16) DSA_ATT2(3, 16, true);
-    else DSA_ATT2(3, 64, true);
+    if (per_thread == 0) DSA_ATT2(3, 0, 8);
+    else if (per_thread == 16) DSA_ATT2(3, 16, 8);
+    else DSA_ATT2(3, 64, 8);
   } else if (code_bytes <= lds.dyn4) {
     if (per_thread == 0) DSA_ATT(4, 0);
     else if (per_thread == 16) DSA_ATT(4, 16);
@@ -1164,25 +1202,26 @@ bool attend_fused_ok(const Shape& s, int fmt, int64_t nrows) {
 }
 
 hipError_t launch_attend_fused(const Shape& s, int64_t qi0, int64_t nrows, const void* q,
-                               const void* kv, const uint8_t* kv_scale, const float* scores,
-                               int32_t* idx_out, const void* kv_raw, int64_t raw_base,
+                               const void* kv, const uint8_t* kv_scale, int kv_fmt,
+                               const float* scores, int32_t* idx_out, const void* kv_raw,
+                               int64_t raw_base,
                                int64_t n_raw, const int32_t* q_pos, const int32_t* seq_len,
                                const float* sink, float scale, void* out, float* lse, void* ws,
                                hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   if (!attend_fused_ok(s, FMT_BF16, nrows)) return hipErrorInvalidValue;
-  return launch_attend_mfma(s, qi0, nrows, q, kv, kv_scale, nullptr, scores, idx_out, kv_raw,
+  return launch_attend_mfma(s, qi0, nrows, q, kv, kv_scale, kv_fmt, nullptr, scores, idx_out, kv_raw,
                             raw_base, n_raw, q_pos, seq_len, sink, scale, out, lse, ws, st);
 }
 
 hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, const void* q,
-                         const void* kv, const uint8_t* kv_scale, const int32_t* idx,
-                         const void* kv_raw, int64_t raw_base, int64_t n_raw,
+                         const void* kv, const uint8_t* kv_scale, int kv_fmt,
+                         const int32_t* idx, const void* kv_raw, int64_t raw_base, int64_t n_raw,
                          const int32_t* q_pos, const int32_t* seq_len, const float* sink,
                          float scale, void* out, float* lse, void* ws, hipStream_t st) {
   if (nrows <= 0) return hipSuccess;
   if (mfma_ok(s, fmt))
-    return launch_attend_mfma(s, qi0, nrows, q, kv, kv_scale, idx, nullptr, nullptr, kv_raw,
+    return launch_attend_mfma(s, qi0, nrows, q, kv, kv_scale, kv_fmt, idx, nullptr, nullptr, kv_raw,
                               raw_base, n_raw, q_pos, seq_len, sink, scale, out, lse, ws, st);
   const int E = s.top_k + s.W;
   size_t shm = sizeof(float) * (s.D_K + E + 1) + sizeof(void*) * E + sizeof(int) * E + 16;
@@ -1191,11 +1230,13 @@ hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, co
     return launch(attend_generic<uint16_t>, grid, 256, shm, st, static_cast<const uint16_t*>(q),
                   static_cast<const uint16_t*>(kv), idx, static_cast<const uint16_t*>(kv_raw),
                   raw_base, n_raw, q_pos, s.T, s.N, s.H, s.D_K, s.D_V, s.top_k, s.W, scale, qi0,
-                  static_cast<uint16_t*>(out), lse, s.m, seq_len, sink, kv_scale);
+                  static_cast<uint16_t*>(out), lse, s.m, seq_len, sink, kv_scale,
+                  kv_fmt == FMT_MXFP4 ? 1 : 0);
   return launch(attend_generic<float>, grid, 256, shm, st, static_cast<const float*>(q),
                 static_cast<const float*>(kv), idx, static_cast<const float*>(kv_raw), raw_base,
                 n_raw, q_pos, s.T, s.N, s.H, s.D_K, s.D_V, s.top_k, s.W, scale, qi0,
-                static_cast<float*>(out), lse, s.m, seq_len, sink, kv_scale);
+                static_cast<float*>(out), lse, s.m, seq_len, sink, kv_scale,
+                kv_fmt == FMT_MXFP4 ? 1 : 0);
 }
 
 }  // namespace dsa

@@ -87,14 +87,39 @@ __global__ __launch_bounds__(256) void mxfp8_to_bf16(const uint8_t* __restrict__
               __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
 }
 
+// The same for an MXFP4 cache (e2m1 x 2^(e-127) fits bf16): thread i takes code bytes
+// 4i .. 4i+3 (codes 8i .. 8i+7, low nibble first) of the flattened [rows, D / 2] codes.
+__global__ __launch_bounds__(256) void mxfp4_to_bf16(const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales, int D,
+                                                     int64_t units, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= units) return;
+  const int64_t per_row = D / 8;
+  const int64_t row = i / per_row, u = i - row * per_row;
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + 4 * i);
+  const uint32_t e = scales[row * (D / 32) + u / 4];
+  const float sc = __uint_as_float(e != 0u ? e << 23 : 0x00400000u);  // 2^(e-127)
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+  *reinterpret_cast<u32x4_t*>(out + 8 * i) =
+      u32x4_t{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+              __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+}
+
 }  // namespace
 
-hipError_t launch_mxfp8_to_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int D,
-                                void* out, hipStream_t st) {
+hipError_t launch_mx_to_bf16(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                             int D, void* out, hipStream_t st) {
   const int64_t units = rows * (D / 8);
   if (units <= 0) return hipSuccess;
-  return launch(mxfp8_to_bf16, (unsigned)((units + 255) / 256), 256, 0, st, codes, scales, D,
-                units, static_cast<uint16_t*>(out));
+  const unsigned blocks = (unsigned)((units + 255) / 256);
+  if (fmt == FMT_MXFP4)
+    return launch(mxfp4_to_bf16, blocks, 256, 0, st, codes, scales, D, units,
+                  static_cast<uint16_t*>(out));
+  return launch(mxfp8_to_bf16, blocks, 256, 0, st, codes, scales, D, units,
+                static_cast<uint16_t*>(out));
 }
 
 hipError_t launch_compress_blocks(int B, int D, int m, int fmt, const void* kv_raw,

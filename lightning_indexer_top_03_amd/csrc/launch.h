@@ -64,10 +64,10 @@ hipError_t launch_compress_blocks(int B, int D, int m, int fmt, const void* kv_r
                                   int64_t raw_stride, void* kv_c, int64_t c_stride, int64_t j0,
                                   int64_t j1, hipStream_t st);
 
-// An MXFP8 latent cache (e4m3 codes [rows, D], E8M0 scales [rows, D/32]) expanded to bf16
-// [rows, D] (exact).
-hipError_t launch_mxfp8_to_bf16(const uint8_t* codes, const uint8_t* scales, int64_t rows, int D,
-                                void* out, hipStream_t st);
+// An MX latent cache (fmt FMT_MXFP8: e4m3 codes [rows, D]; FMT_MXFP4: e2m1 code pairs
+// [rows, D/2], low nibble first; E8M0 scales [rows, D/32]) expanded to bf16 [rows, D] (exact).
+hipError_t launch_mx_to_bf16(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                             int D, void* out, hipStream_t st);
 
 // ---- step 1 ----
 // scores: [nrows, N] row-relative. fill_masked: write -inf for s >= n_vis. seq_len (nullable):
@@ -108,11 +108,12 @@ int attend_splits(const Shape& s, int64_t nrows, int fmt);
 size_t attend_ws_bytes(const Shape& s, int64_t nrows, int fmt);
 // seq_len (nullable): entries per sequence (limits the dense idx == nullptr case and the fused
 // selection); sink (nullable): one logit per head joining the softmax with a zero value vector.
-// kv_scale (nullable): kv holds MXFP8 entries (e4m3 code bytes [B, N, D_K], E8M0 scales
-// [B, N, D_K / 32]); q, kv_raw and out stay in fmt.
+// kv_scale (nullable): kv holds MX entries of kv_fmt (FMT_MXFP8: e4m3 code bytes [B, N, D_K];
+// FMT_MXFP4: e2m1 code pairs [B, N, D_K / 2]), E8M0 scales [B, N, D_K / 32]; q, kv_raw and out
+// stay in fmt.
 hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, const void* q,
-                         const void* kv, const uint8_t* kv_scale, const int32_t* idx,
-                         const void* kv_raw, int64_t raw_base, int64_t n_raw,
+                         const void* kv, const uint8_t* kv_scale, int kv_fmt,
+                         const int32_t* idx, const void* kv_raw, int64_t raw_base, int64_t n_raw,
                          const int32_t* q_pos, const int32_t* seq_len, const float* sink,
                          float scale, void* out, float* lse, void* ws, hipStream_t st);
 
@@ -122,8 +123,9 @@ hipError_t launch_attend(const Shape& s, int64_t qi0, int64_t nrows, int fmt, co
 // most 128 query rows per launch.
 bool attend_fused_ok(const Shape& s, int fmt, int64_t nrows);
 hipError_t launch_attend_fused(const Shape& s, int64_t qi0, int64_t nrows, const void* q,
-                               const void* kv, const uint8_t* kv_scale, const float* scores,
-                               int32_t* idx_out, const void* kv_raw, int64_t raw_base,
+                               const void* kv, const uint8_t* kv_scale, int kv_fmt,
+                               const float* scores, int32_t* idx_out, const void* kv_raw,
+                               int64_t raw_base,
                                int64_t n_raw, const int32_t* q_pos, const int32_t* seq_len,
                                const float* sink, float scale, void* out, float* lse, void* ws,
                                hipStream_t st);

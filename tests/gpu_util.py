@@ -83,7 +83,8 @@ class DeviceWorkload:
             self.kv = torch.empty((c.B, c.N, c.D_K), dtype=tdt, device="cuda")
         else:
             kv = wl.kv()
-            self.kv = (to_dev(kv[0]), to_dev(kv[1])) if c.kv_dt == "mxfp8" else to_dev(kv)
+            self.kv = ((to_dev(kv[0]), to_dev(kv[1])) if c.kv_dt in ("mxfp8", "mxfp4")
+                       else to_dev(kv))
         lens, sink = wl.seq_len(), wl.sink()
         self.seq_len = to_dev(lens) if lens is not None else None
         self.sink = to_dev(sink) if sink is not None else None

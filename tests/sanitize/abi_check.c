@@ -48,7 +48,7 @@ static void status_and_version(void) {
   }
   if (strcmp(dsa_status_str(-1), "unknown dsa_status") != 0) ++fails;
   if (strcmp(dsa_status_str(99), "unknown dsa_status") != 0) ++fails;
-  if (dsa_version() != 210) ++fails;
+  if (dsa_version() != 220) ++fails;
   if (dsa_noalloc_scratch_bytes() != DSA_NOALLOC_SCRATCH_BYTES) ++fails;
 }
 
@@ -125,18 +125,18 @@ static void attend(void) {
 
 static void attend_mxkv(void) {
   dsa_dims d = base(), e;
-  EXPECT(sparse_mla_attend_mxkv(&d, P, P, NULL, P, NULL, 0, 0, P, 0.1f, NULL, P, NULL, NULL, 0, NULL), 1);
-  EXPECT(sparse_mla_attend_mxkv(&d, P, NULL, P, P, NULL, 0, 0, P, 0.1f, NULL, P, NULL, NULL, 0, NULL), 1);
+  EXPECT(sparse_mla_attend_mxkv(&d, P, P, NULL, DSA_MXFP8, P, NULL, 0, 0, P, 0.1f, NULL, P, NULL, NULL, 0, NULL), 1);
+  EXPECT(sparse_mla_attend_mxkv(&d, P, NULL, P, DSA_MXFP8, P, NULL, 0, 0, P, 0.1f, NULL, P, NULL, NULL, 0, NULL), 1);
   e = dims(2, 3, 100, 64, 128, 128, 80, 64, 32, 1, 0);
-  EXPECT(sparse_mla_attend_mxkv(&e, P, P, P, P, NULL, 0, 0, P, 0.1f, NULL, P, NULL, NULL, 0, NULL), 2);
-  EXPECT(sparse_mla_attend_mxkv(&d, P, PO(8), P, P, NULL, 0, 0, P, 0.1f, NULL, P, NULL, NULL, 0, NULL), 4);
+  EXPECT(sparse_mla_attend_mxkv(&e, P, P, P, DSA_MXFP8, P, NULL, 0, 0, P, 0.1f, NULL, P, NULL, NULL, 0, NULL), 2);
+  EXPECT(sparse_mla_attend_mxkv(&d, P, PO(8), P, DSA_MXFP8, P, NULL, 0, 0, P, 0.1f, NULL, P, NULL, NULL, 0, NULL), 4);
   e = base(); e.W = 16;
-  EXPECT(sparse_mla_attend_mxkv(&e, P, P, P, P, NULL, 0, 0, P, 0.1f, NULL, P, NULL, NULL, 0, NULL), 1);
-  EXPECT(sparse_mla_attend_mxkv(&e, P, P, P, P, P, -1, 0, P, 0.1f, NULL, P, NULL, NULL, 0, NULL), 2);
+  EXPECT(sparse_mla_attend_mxkv(&e, P, P, P, DSA_MXFP8, P, NULL, 0, 0, P, 0.1f, NULL, P, NULL, NULL, 0, NULL), 1);
+  EXPECT(sparse_mla_attend_mxkv(&e, P, P, P, DSA_MXFP8, P, P, -1, 0, P, 0.1f, NULL, P, NULL, NULL, 0, NULL), 2);
   /* unsplit calls expand the cache into the workspace: a call without one is refused */
   size_t need = dsa_workspace_bytes(&d, DSA_OP_ATTEND_MXKV);
   if (need < (size_t)2 * 100 * 576 * 2) ++fails;
-  EXPECT(sparse_mla_attend_mxkv(&d, P, P, P, P, NULL, 0, 0, P, 0.1f, NULL, P, NULL, P, need - 1, NULL), 5);
+  EXPECT(sparse_mla_attend_mxkv(&d, P, P, P, DSA_MXFP8, P, NULL, 0, 0, P, 0.1f, NULL, P, NULL, P, need - 1, NULL), 5);
 }
 
 static void forward(void) {
@@ -155,7 +155,9 @@ static void forward(void) {
   EXPECT(dsa_forward(&e, &a, P, need, NULL), 2);
   a = fargs(); a.q_I = PO(8);
   EXPECT(dsa_forward(&d, &a, P, need, NULL), 4);
-  a = fargs(); a.kv_scale = P; a.dt = DSA_F32;
+  a = fargs(); a.kv_scale = P; a.kv_dt = DSA_MXFP8; a.dt = DSA_F32;
+  EXPECT(dsa_forward(&d, &a, P, need, NULL), 3);
+  a = fargs(); a.kv_scale = P; a.kv_dt = DSA_BF16;   /* not an MX format */
   EXPECT(dsa_forward(&d, &a, P, need, NULL), 3);
   a = fargs(); a.events = (void* const*)P; a.n_events = -1;
   int r = dsa_forward(&d, &a, P, need, NULL);

@@ -37,7 +37,7 @@ def test_status_strings_and_version():
         s = L.dsa_status_str(code).decode()
         assert s.startswith("DSA_"), s
     assert L.dsa_status_str(99).decode() == "unknown dsa_status"
-    assert L.dsa_version() == 210
+    assert L.dsa_version() == 220
 
 
 def _dims(**kw):
@@ -112,9 +112,10 @@ def test_attend_validation():
     assert _att(dd, ws=P, wsb=need - 1) == 5
 
 
-def _mx(d, q=P, codes=P, scales=P, idx=P, raw=None, out=P, sink=None, ws=None, wsb=0):
-    return L.sparse_mla_attend_mxkv(ctypes.byref(d), q, codes, scales, idx, raw, 0, 0, P, 0.1,
-                                    sink, out, None, ws, wsb, None)
+def _mx(d, q=P, codes=P, scales=P, idx=P, raw=None, out=P, sink=None, ws=None, wsb=0,
+        kv_dt=dsa.MXFP8):
+    return L.sparse_mla_attend_mxkv(ctypes.byref(d), q, codes, scales, kv_dt, idx, raw, 0, 0, P,
+                                    0.1, sink, out, None, ws, wsb, None)
 
 
 def test_attend_mxkv_validation():
@@ -125,6 +126,9 @@ def test_attend_mxkv_validation():
     assert _mx(_dims(W=16)) == 1                 # window without kv_raw
     assert _mx(d, codes=P + 8) == 4
     assert _mx(d, out=P + 2) == 4
+    # the codes' format: MXFP8 or MXFP4 only
+    for bad in (dsa.F32, dsa.BF16, 7):
+        assert _mx(d, kv_dt=bad) == 3
     dd = _dims(B=1, T=1, top_k=2048)
     need = L.dsa_workspace_bytes(ctypes.byref(dd), dsa.OP_ATTEND_MXKV)
     assert need > 0 and _mx(dd) == 5
@@ -153,8 +157,11 @@ def test_forward_validation_and_workspace():
     a.q_I = P + 8
     assert L.dsa_forward(ctypes.byref(d), ctypes.byref(a), P, need, None) == 4
     a.q_I = P
-    # an MXFP8 latent cache: bf16 path only, stored entries only, D_K % 32 == 0
+    # an MX latent cache: bf16 path only, stored entries only, D_K % 32 == 0, an MX format
     a.kv_scale = P
+    a.kv_dt = dsa.BF16
+    assert L.dsa_forward(ctypes.byref(d), ctypes.byref(a), P, need, None) == 3
+    a.kv_dt = dsa.MXFP4
     a.dt = dsa.F32
     assert L.dsa_forward(ctypes.byref(d), ctypes.byref(a), P, need, None) == 3
     a.dt = dsa.BF16

@@ -132,7 +132,7 @@ def test_random_scalar_shapes(cfg):
     _run(cfg, n_sample=48, always=(0,))
 
 
-def _kv8_cases(n=8, seed=2026):
+def _kv8_cases(n=8, seed=2026, kv_dt="mxfp8"):
     # an MXFP8 latent cache at random shapes: decode-sized calls (split attention, gathered rows
     # converted in the kernel; some with the fused selection), prefill-sized ones (the cache
     # expanded to bf16 first), CSA blocks with bf16 raw window rows, ragged sequence lengths
@@ -159,7 +159,9 @@ def _kv8_cases(n=8, seed=2026):
             pos0 = int(rng.integers(0, N // 2))
             stride = int(rng.integers(1, max(2, (N - pos0) // max(T, 1))))
             cfg = c.with_(B=B, T=T, N=N, top_k=top_k, pos0=pos0, pos_stride=stride)
-        cfg = cfg.with_(kv_dt="mxfp8", seed=700 + i, name=f"sweepkv8_{i}_{kind}_k{cfg.top_k}")
+        tag = "kv8" if kv_dt == "mxfp8" else "kv4"
+        cfg = cfg.with_(kv_dt=kv_dt, seed=(700 if kv_dt == "mxfp8" else 800) + i,
+                        name=f"sweep{tag}_{i}_{kind}_k{cfg.top_k}")
         if i % 4 == 3:
             cfg = cfg.with_(seq_lens=tuple(int(rng.integers(N // 2, N + 1)) for _ in range(cfg.B)))
         if i % 2 == 1:
@@ -168,7 +170,7 @@ def _kv8_cases(n=8, seed=2026):
     return cases
 
 
-@pytest.mark.parametrize("cfg", _kv8_cases(), ids=lambda c: c.name)
-def test_random_shapes_mxfp8_cache(cfg):
+@pytest.mark.parametrize("cfg", _kv8_cases() + _kv8_cases(6, 2027, "mxfp4"), ids=lambda c: c.name)
+def test_random_shapes_mx_cache(cfg):
     _run(cfg, n_sample=32, always=(0,), bf16_scale_allowance=cfg.name.endswith("_sharp"))
 
