@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_long_select(
 //     evenly over the row) and its r-th largest,
 //     r = mu + 4 sigma + 8 with mu = 2048 k / n (select.h block_threshold); rows of at most
 //     kStCap entries skip it (lo = the smallest key: every entry is a candidate).
-//  2. One streaming pass: wave w scans the contiguous quarter w of the row, 8 loads of 16
+//  2. One streaming pass: wave w scans the contiguous quarter w of the row, 6 loads of 16
 //     bytes per lane in flight, and appends every score >= lo (order key and index) to its own
 //     LDS segment in index order (a DPP prefix sum of the lanes' counts per 256 entries).
 //  3. If every segment fits and together they hold at least k entries, they hold every one of
@@ -382,15 +382,23 @@ constexpr int kStSeg = 1024;                 // candidate slots per wave
 constexpr int kStCap = kStWaves * kStSeg;    // 4096
 constexpr int kStPC = kStCap / kStThreads;   // candidates per thread in the exact step
 constexpr int kStSample = 2048;
-constexpr int kStUnroll = 8;                 // 256-entry blocks a wave loads ahead
+constexpr int kStUnroll = 6;                 // 256-entry blocks a wave loads ahead
 
+// Candidate indices are row-relative and below kLdsMaxN, so 16 bits hold them. The selection
+// state shares its memory with the candidate keys: the sample's selection ends (barrier) before
+// the streaming pass appends keys, and the exact step copies every key to registers (barrier)
+// before its selection starts; the fallback's 256-bin histogram is the selection's first one.
+// About 24 KB and 73 VGPRs: six rows per CU.
+static_assert(kLdsMaxN <= 65536, "16-bit candidate indices");
 struct __attribute__((aligned(16))) StShared {
-  SelShared<kStWaves> sel;
-  uint32_t ckey[kStCap];
-  int32_t cidx[kStCap];
+  union {
+    SelShared<kStWaves> sel;
+    uint32_t ckey[kStCap];
+  };
+  uint16_t cidx[kStCap];
   uint32_t wcnt[kStWaves], weq[kStWaves];
-  uint32_t hist[256];
   uint32_t bin, above, cnt;
+  __device__ uint32_t* hist() { return &sel.hist[0][0]; }
 };
 
 __device__ __forceinline__ float key_to_float(uint32_t u) {
@@ -411,19 +419,37 @@ __device__ __forceinline__ int st_quarter(int n) { return ((n + 1023) >> 10) << 
 // entries i0 = block + 4 l .. i0 + 3 (the caller masks i >= r1), with kStUnroll 16-byte loads
 // per lane in flight.
 template <typename F>
+__device__ __forceinline__ void blocks_of(int b0, int r1, const f32x4_t (&v)[kStUnroll], F& f) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kStUnroll; ++u) {
+    if (b0 + 256 * u >= r1) break;  // wave-uniform
+    f(b0 + 256 * u + 4 * lane, v[u]);
+  }
+}
+__device__ __forceinline__ void load_blocks(const float* __restrict__ s, int n, bool vec, int b0,
+                                            f32x4_t (&v)[kStUnroll]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kStUnroll; ++u) v[u] = load4(s, b0 + 256 * u + 4 * lane, n, vec);
+}
+template <typename F>
 __device__ __forceinline__ void for_blocks(const float* __restrict__ s, int n, bool vec, int r0,
                                            int r1, F&& f) {
-  const int lane = threadIdx.x & 63;
   for (int b0 = r0; b0 < r1; b0 += 256 * kStUnroll) {
     f32x4_t v[kStUnroll];
-#pragma unroll
-    for (int u = 0; u < kStUnroll; ++u) v[u] = load4(s, b0 + 256 * u + 4 * lane, n, vec);
-#pragma unroll
-    for (int u = 0; u < kStUnroll; ++u) {
-      if (b0 + 256 * u >= r1) break;  // wave-uniform
-      f(b0 + 256 * u + 4 * lane, v[u]);
-    }
+    load_blocks(s, n, vec, b0, v);
+    blocks_of(b0, r1, v, f);
   }
+}
+// for_blocks with the first kStUnroll blocks already loaded (first, loaded at r0)
+template <typename F>
+__device__ __forceinline__ void for_blocks_from(const float* __restrict__ s, int n, bool vec,
+                                                int r0, int r1, const f32x4_t (&first)[kStUnroll],
+                                                F&& f) {
+  if (r0 >= r1) return;
+  blocks_of(r0, r1, first, f);
+  for_blocks(s, n, vec, r0 + 256 * kStUnroll, r1, f);
 }
 
 // Exact whole-row select (step 4): tau and need by radix passes over the row re-read from L2,
@@ -465,18 +491,18 @@ __device__ void stream_exact(const float* __restrict__ s, int n, int k, bool vec
       const int width = hi + 1 < 8 ? hi + 1 : 8;
       const int shift = hi + 1 - width;
       const uint32_t bmask = (1u << width) - 1u;
-      sh.hist[tid] = 0u;
+      sh.hist()[tid] = 0u;
       __syncthreads();
       for_blocks(s, n, vec, r0, r1, [&](int i0, const f32x4_t& v) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t u = order_key(v[j]);
-          if (i0 + j < r1 && (u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & bmask], 1u);
+          if (i0 + j < r1 && (u & pmask) == prefix) atomicAdd(&sh.hist()[(u >> shift) & bmask], 1u);
         }
       });
       __syncthreads();
       // thread t holds bin 255 - t: an inclusive scan from the top finds the need-th key's bin
-      const uint32_t c = sh.hist[255 - tid];
+      const uint32_t c = sh.hist()[255 - tid];
       const uint32_t inc = wave_incl_scan(c);
       if (lane == 63) sh.sel.wtot[wv] = inc;
       __syncthreads();
@@ -570,8 +596,12 @@ __global__ __launch_bounds__(kStThreads) void topk_stream(
     return;
   }
   const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(s) & 15) == 0;
+  const int Lq = st_quarter(n), r0 = wv * Lq, r1 = min(n, r0 + Lq);
+  // the streaming pass's first loads go out with the sample's, so their latency overlaps it
+  f32x4_t first[kStUnroll];
   // 1. lo from the sample
   uint32_t lo = 0u;
+  if (n <= kStCap) load_blocks(s, n, vec, r0, first);
   if (n > kStCap) {
     // 64 runs of 32 consecutive entries (one 128-byte line each, 8 KB in all) spread evenly
     // over the row; thread t reads 8 entries of run t / 4
@@ -580,6 +610,7 @@ __global__ __launch_bounds__(kStThreads) void topk_stream(
     const int run0 = (int)(((int64_t)(tid >> 2) * n) / 64) & ~31;
     const f32x4_t sv0 = load4(s, run0 + 8 * (tid & 3), n, vec);
     const f32x4_t sv1 = load4(s, run0 + 8 * (tid & 3) + 4, n, vec);
+    load_blocks(s, n, vec, r0, first);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       sk[j] = order_key(sv0[j]);
@@ -595,14 +626,14 @@ __global__ __launch_bounds__(kStThreads) void topk_stream(
                                                         (uint32_t)kStSample);
     }
   }
+  __syncthreads();  // the sample's selection state is about to hold candidate keys
   // keys up to order_key(-inf) are -inf or NaN images: lo there means "every entry"
   const float lo_f = lo <= 0x007fffffu ? -__builtin_huge_valf() : key_to_float(lo);
   // 2. the streaming pass: wave wv appends the candidates of its quarter in index order
-  const int Lq = st_quarter(n), r0 = wv * Lq, r1 = min(n, r0 + Lq);
   uint32_t wc = 0;
   uint32_t* ck = sh.ckey + wv * kStSeg;
-  int32_t* ci = sh.cidx + wv * kStSeg;
-  for_blocks(s, n, vec, r0, r1, [&](int i0, const f32x4_t& v) {
+  uint16_t* ci = sh.cidx + wv * kStSeg;
+  for_blocks_from(s, n, vec, r0, r1, first, [&](int i0, const f32x4_t& v) {
     uint32_t bits = 0, c = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -618,7 +649,7 @@ __global__ __launch_bounds__(kStThreads) void topk_stream(
       if ((bits >> j) & 1u) {
         if (o < (uint32_t)kStSeg) {
           ck[o] = order_key(v[j]);
-          ci[o] = i0 + j;
+          ci[o] = (uint16_t)(i0 + j);
         }
         ++o;
       }
@@ -649,13 +680,14 @@ __global__ __launch_bounds__(kStThreads) void topk_stream(
       kc[j] = sh.ckey[phys[j]];
     }
     uint32_t tau, need, cnt_eq;
+    __syncthreads();  // every candidate key is in registers before the selection state reuses them
     block_threshold<kStWaves, kStPC>(kc, nvc, (uint32_t)k, sh.sel, tau, need, cnt_eq, total);
     uint32_t base, take_eq, nsel;
     block_ranks<kStWaves, kStPC>(kc, nvc, tau, need, sh.sel, base, take_eq, nsel);
     const auto sel = select_mask<kStPC>(kc, nvc, tau, take_eq);
 #pragma unroll
     for (int j = 0; j < kStPC; ++j)
-      if ((sel >> j) & 1) out[base + sel_rank(sel, j)] = sh.cidx[phys[j]];
+      if ((sel >> j) & 1) out[base + sel_rank(sel, j)] = (int32_t)sh.cidx[phys[j]];
     return;
   }
   __syncthreads();  // the fallback rewrites the shared state
