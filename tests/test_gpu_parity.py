@@ -187,6 +187,17 @@ def test_topk_long_rows():
     _topk_case("long-k4096", 2, 300000, 4096, seed=11)
 
 
+def test_topk_stream_fallback():
+    # prefill-length rows (the streaming select): ascending / descending / constant rows put
+    # more than a wave's candidate segment into one quarter of the row, so the exact whole-row
+    # fallback runs; an odd row length takes the unaligned loads
+    _topk_case("stream-sorted", 3, 32768, 2048, seed=12, order="sorted",
+               pos=np.full(3, 32767, np.int32))
+    _topk_case("stream-odd", 4, 30001, 2048, seed=13, order="sorted",
+               pos=np.array([30000, 30000, 30000, 17000], np.int32))
+    _topk_case("stream-ties", 4, 32768, 2048, ties=True, seed=14)
+
+
 def test_topk_ties_take_lowest_index():
     _topk_case("ties", 8, 5000, 1000, ties=True, seed=6)
     # all-equal row: exactly the first k indices
