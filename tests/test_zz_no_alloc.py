@@ -2,9 +2,9 @@
 dsa_forward (a caller's workspace) on the same inputs: the same kernels run on the same bytes,
 so every output must match bit for bit. Two calls in a row, the second with a smaller input
 (the scratch array keeps the first call's contents), then a CSA decode call whose long rows use
-the top-k candidate region of the workspace as well, and three calls over an MX latent cache (MXFP8, then MXFP4):
-split attention converting the gathered rows, and unsplit attention reading the cache expanded to
-bf16 in the workspace."""
+the top-k candidate region of the workspace as well, and three calls over an MX latent cache
+(MXFP8 split and unsplit, then MXFP4 split): split attention converting the gathered rows, and
+unsplit attention reading the cache expanded to bf16 in the workspace."""
 import numpy as np
 import pytest
 import torch
@@ -52,7 +52,7 @@ def test_noalloc_matches_dsa_forward_twice():
                                                name="noalloc_csa"))
 
 
-def test_noalloc_matches_dsa_forward_mxfp8_cache():
+def test_noalloc_matches_dsa_forward_mx_cache():
     _compare(synth.CONFIGS["decode_kv8"].with_(B=4, name="noalloc_kv8_decode"))
     _compare(synth.CONFIGS["prefill_kv8"].with_(T=256, N=4096, pos0=3840,
                                                 name="noalloc_kv8_prefill"))
