@@ -144,6 +144,15 @@ def score_mass(wl, b, t):
     return np.abs(_decoded_keys(wl, b)) @ u
 
 
+def visible(wl, b: int, t: int) -> int:
+    """Entries query (b, t) of a workload sees: its position's causal count, capped by the
+    sequence's length in a ragged batch (the oracle's n_vis with seq_len)."""
+    c = wl.cfg
+    lens = wl.seq_len()
+    return oracle.n_vis(int(wl.q_pos()[b, t]), c.m, c.N,
+                        seq_len=None if lens is None else int(lens[b]))
+
+
 def _abs_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     """|a - b| with equal values (the same infinity included) at 0; a NaN on either side is an
     infinite difference."""

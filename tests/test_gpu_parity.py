@@ -12,7 +12,7 @@ import torch
 import oracle
 import synth
 from gpu_util import (DeviceWorkload, check_attention, check_compressed, check_scores,
-                      check_topk, log, to_dev, to_host)
+                      check_topk, log, to_dev, to_host, visible)
 
 pytestmark = pytest.mark.gpu
 
@@ -75,7 +75,7 @@ def _run_indexer(c, label):
         rows = sorted({rows[i] for i in pick} | {rows[0], rows[-1]})
     for b, t in rows:
         ref = run.scores(b, t)
-        nv = oracle.n_vis(int(wl.q_pos()[b, t]), c.m, c.N)
+        nv = visible(wl, b, t)
         worst = max(worst, check_scores(sc[b, t], ref, nv, what=f"{label} b={b} t={t}"))
     log(f"[indexer {label}] max rel err {worst:.2e}")
     return sc
@@ -217,7 +217,7 @@ def _attend_case(c, label, seed=0, frac_masked=0.05):
     idx = np.full((B, T, k), -1, np.int32)
     for b in range(B):
         for t in range(T):
-            nv = oracle.n_vis(int(pos[b, t]), c.m, c.N)
+            nv = visible(wl, b, t)
             n = min(k, nv)
             sel = rng.choice(nv, n, replace=False).astype(np.int32)
             drop = rng.random(n) < frac_masked

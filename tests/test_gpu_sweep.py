@@ -174,3 +174,14 @@ def _kv8_cases(n=8, seed=2026, kv_dt="mxfp8"):
 def test_random_shapes_mx_cache(cfg):
     _run(cfg, n_sample=32, always=(0,), bf16_scale_allowance=cfg.name.endswith("_sharp"))
 
+
+def test_queries_past_their_sequence():
+    # ragged batch whose later queries sit past their sequence's length (the visible count is
+    # the length, below k, so every entry of the sequence is kept): the shape a seeded MX-cache
+    # sweep drew, on an MXFP8 cache and on bf16
+    base = synth.CONFIGS["decode_kv8"].with_(B=3, T=17, N=1249, top_k=1024, pos0=151,
+                                             pos_stride=32, seq_lens=(655, 659, 694), seed=703,
+                                             name="past_seq_kv8").sharp()
+    _run(base, n_sample=32, always=(0, 16), bf16_scale_allowance=True)
+    _run(base.with_(kv_dt="bf16", name="past_seq_bf16_sharp"), n_sample=32, always=(0, 16),
+         bf16_scale_allowance=True)

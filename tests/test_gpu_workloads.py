@@ -12,7 +12,7 @@ import torch
 import oracle
 import synth
 from gpu_util import (DeviceWorkload, check_attention, check_compressed, check_scores,
-                      check_topk, log, score_mass, to_host)
+                      check_topk, log, score_mass, to_host, visible)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +52,7 @@ def _run(c, n_sample=16, always=(), bf16_scale_allowance=False):
         out = oracle.decode(to_host(f.out[b, t]))
         lse = to_host(f.lse[b, t])
         ref_sc = run.scores(b, t)
-        nv = oracle.n_vis(int(wl.q_pos()[b, t]), c.m, c.N)
+        nv = visible(wl, b, t)
         what = f"{c.name} b={b} t={t}"
         worst_s = max(worst_s, check_scores(sc, ref_sc, nv, what=what))
         swaps += check_topk(ix, ref_sc, nv, c.top_k, what=what)
@@ -131,7 +131,7 @@ def _run_fused(c, periodic=0):
             what = f"{c.name} b={b} t={t}"
             sc = to_host(f.scores[b, t])
             ix = to_host(f.idx[b, t])
-            nv = oracle.n_vis(int(wl.q_pos()[b, t]), c.m, c.N)
+            nv = visible(wl, b, t)
             cnt = min(nv, c.top_k)
             ref, rcnt = oracle.topk_row(sc[:nv].astype(np.float64), nv, c.top_k)
             assert rcnt == cnt
@@ -263,7 +263,7 @@ def _run_exact_selection(c, n_attend=8):
         what = f"{c.name} b={b} t={t}"
         sc = to_host(f.scores[b, t])
         ix = to_host(f.idx[b, t])
-        nv = oracle.n_vis(int(wl.q_pos()[b, t]), c.m, c.N)
+        nv = visible(wl, b, t)
         cnt = min(nv, c.top_k)
         ref, rcnt = oracle.topk_row(sc[:nv].astype(np.float64), nv, c.top_k)
         assert rcnt == cnt
