@@ -31,7 +31,7 @@ struct __attribute__((aligned(16))) TkShared {
   uint32_t hist[kBins];
   uint32_t wave_tot[kTkWaves];
   uint32_t red_and[kTkWaves], red_or[kTkWaves];
-  uint32_t bin, above, pos, taken_eq;
+  uint32_t bin, above;
 };
 
 // Block-wide search of the bin holding the need-th largest element counting from the top:
@@ -67,25 +67,13 @@ __device__ __forceinline__ void find_bin(TkShared& sh, uint32_t need) {
   __syncthreads();
 }
 
-// Append index i to out for every lane with take set: one LDS atomic per wave (the ballot's
-// popcount), each lane then writes at base + its rank among the taking lanes.
-__device__ __forceinline__ void append(bool take, int i, uint32_t* pos, int32_t* __restrict__ out) {
-  const unsigned long long bal = __ballot(take);
-  if (bal == 0) return;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll((long long)bal) - 1;
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(pos, (uint32_t)__popcll(bal));
-  base = __shfl(base, leader, 64);
-  if (take) out[base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull))] = i;
-}
-
 // Exact radix select over one whole row of n > k visible scores, re-read from global memory
 // (L2) on every pass; one 1024-thread workgroup. The bits every visible key shares (block-wide
 // AND / OR) are skipped, so the first digit already splits the row: scores of one row typically
 // share sign and exponent, and digits over those bits would put the whole row into a handful of
 // bins and serialise the LDS atomics. Used for long rows only when the filtered path below
-// cannot prove its candidate set complete.
+// cannot prove its candidate set complete. The selection is written in ascending index order,
+// as on every other path, so a row's result does not depend on the timing of the waves.
 __device__ void radix_row_exact(const float* __restrict__ s, int n, int k,
                                 int32_t* __restrict__ out, TkShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -113,10 +101,6 @@ __device__ void radix_row_exact(const float* __restrict__ s, int n, int k,
     sh.red_and[wv] = kand;
     sh.red_or[wv] = kor;
   }
-  if (tid == 0) {
-    sh.pos = 0;
-    sh.taken_eq = 0;
-  }
   __syncthreads();
   kand = 0xffffffffu;
   kor = 0u;
@@ -127,7 +111,7 @@ __device__ void radix_row_exact(const float* __restrict__ s, int n, int k,
   }
   const uint32_t diff = kand ^ kor;  // bits that vary across the visible row
   uint32_t prefix = kand;            // every bit is shared when diff == 0
-  uint32_t need = (uint32_t)k, cnt_eq = (uint32_t)n;
+  uint32_t need = (uint32_t)k;
   if (diff != 0) {
     const int top = 31 - __clz(diff);  // highest varying bit
     uint32_t pmask = top == 31 ? 0u : (~0u << (top + 1));
@@ -148,38 +132,37 @@ __device__ void radix_row_exact(const float* __restrict__ s, int n, int k,
       prefix |= bin << shift;
       need -= sh.above;
       pmask |= bmask << shift;
-      cnt_eq = sh.hist[bin];
       __syncthreads();
     }
   }
   const uint32_t tau = prefix;
-  if (cnt_eq == need) {
-    for (int base = 0; base < n; base += kTkThreads) {  // block-uniform trip count
-      const int i = base + tid;
-      append(i < n && key(i) >= tau, i, &sh.pos, out);
-    }
-    return;
-  }
-  // tau tied beyond what is needed: keys above tau in any order, tau-valued ones by index
-  for (int base = 0; base < n; base += kTkThreads) {
+  // the selection in ascending index order, one block of kTkThreads entries at a time: one
+  // block scan of the packed (greater, equal) flags gives each entry its output slot; entries
+  // equal to tau are taken while fewer than need of them precede (lowest indices first)
+  uint32_t pos = 0, eq_run = 0;
+  for (int base = 0; base < n; base += kTkThreads) {  // block-uniform trip count
     const int i = base + tid;
     const uint32_t u = i < n ? key(i) : 0u;
-    append(i < n && u > tau, i, &sh.pos, out);
-    const bool eq = i < n && u == tau;
-    const unsigned long long bal = __ballot(eq);
-    if (lane == 0) sh.wave_tot[wv] = (uint32_t)__popcll(bal);
+    const uint32_t gt = (i < n && u > tau) ? 1u : 0u, eq = (i < n && u == tau) ? 1u : 0u;
+    const uint32_t v = (gt << 16) | eq;  // at most kTkThreads of each: 16 bits hold the counts
+    const uint32_t inc = wave_incl_scan(v);
+    if (lane == 63) sh.wave_tot[wv] = inc;
     __syncthreads();
-    uint32_t before = sh.taken_eq;
-    for (int w = 0; w < wv; ++w) before += sh.wave_tot[w];
-    before += (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-    append(eq && before < need, i, &sh.pos, out);
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t tot = 0;
-      for (int w = 0; w < kTkWaves; ++w) tot += sh.wave_tot[w];
-      sh.taken_eq += tot;
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) {
+      const uint32_t t = sh.wave_tot[w];
+      before += w < wv ? t : 0u;
+      tot += t;
     }
-    __syncthreads();
+    __syncthreads();  // sh.wave_tot is rewritten by the next block
+    const uint32_t ex = before + inc - v;
+    const uint32_t gt_before = ex >> 16, eq_before = eq_run + (ex & 0xffffu);
+    const uint32_t taken_before = min(eq_before, need) - min(eq_run, need);
+    if (gt || (eq && eq_before < need)) out[pos + gt_before + taken_before] = i;
+    const uint32_t eq_tot = tot & 0xffffu;
+    pos += (tot >> 16) + (min(eq_run + eq_tot, need) - min(eq_run, need));
+    eq_run += eq_tot;
   }
 }
 

@@ -126,6 +126,28 @@ def test_ragged_many_rows_and_long_rows():
                                                   name="ragged_csa"))
 
 
+def test_ragged_long_rows_repeatable():
+    # short ragged rows among 34286-block rows take the exact whole-row select (their chunks'
+    # candidate segments overflow): two calls give the same bytes (index order, hence the
+    # attention's summation order, is fixed)
+    p = 4 * 34286 - 1
+    c = synth.CONFIGS["csa_decode"].with_(B=5, N=34286, pos0=p, raw_base=p + 1 - 128,
+                                          seq_lens=(7238, 9668, 12360, 8585, 31308),
+                                          sink=(-2.0, 4.0), w_lo=-0.5, seed=2012,
+                                          name="ragged_long_repeat").sharp()
+    _run_checked(c, n_check=5)
+    dw = DeviceWorkload(synth.make_workload(c))
+    f = dw.forward(keep_scores=True, keep_idx=True)
+    f.run()
+    torch.cuda.synchronize()
+    first = [to_host(t).copy() for t in (f.out, f.lse, f.idx)]
+    f.run()
+    torch.cuda.synchronize()
+    for name, a, t in zip(("out", "lse", "idx"), first, (f.out, f.lse, f.idx)):
+        assert np.array_equal(a.view(np.uint8), to_host(t).view(np.uint8)), f"{name} differs"
+    del f, dw
+
+
 def test_ragged_hca():
     base = synth.CONFIGS["hca_decode"]
     _hca_case(base.with_(B=3, T=2, N=1200, m=8, pos0=8 * 1200 - 9, pos_stride=4,

@@ -58,3 +58,12 @@ def test_noalloc_matches_dsa_forward_mx_cache():
                                                 name="noalloc_kv8_prefill"))
     _compare(synth.CONFIGS["decode_kv4"].with_(B=4, name="noalloc_kv4_decode"))
 
+
+def test_noalloc_matches_dsa_forward_ragged_long_rows():
+    # ragged CSA decode rows over 34286 blocks: the short rows overflow their chunks' candidate
+    # segments and take the exact whole-row select, whose output order is fixed
+    p = 4 * 34286 - 1
+    _compare(synth.CONFIGS["csa_decode"].with_(B=5, N=34286, pos0=p, raw_base=p + 1 - 128,
+                                               seq_lens=(7238, 9668, 12360, 8585, 31308),
+                                               sink=(-2.0, 4.0), w_lo=-0.5, seed=2012,
+                                               name="noalloc_ragged_long").sharp())
