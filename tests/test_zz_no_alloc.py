@@ -67,3 +67,10 @@ def test_noalloc_matches_dsa_forward_ragged_long_rows():
                                                seq_lens=(7238, 9668, 12360, 8585, 31308),
                                                sink=(-2.0, 4.0), w_lo=-0.5, seed=2012,
                                                name="noalloc_ragged_long").sharp())
+
+
+def test_noalloc_matches_dsa_forward_random_ragged():
+    # seeded random ragged batches (decode, many rows, CSA long rows, MX caches, sinks)
+    from test_gpu_random import ragged_cases
+    for c in ragged_cases():
+        _compare(c.with_(name=c.name + "_noalloc"))
