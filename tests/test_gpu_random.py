@@ -2,9 +2,9 @@
 (lengths 1 .. 300000, k 1 .. 4096, m = 1 / 4, ties, sorted and constant rows), indexer_scores
 (head counts 1 .. 64, dims 8 .. 128, fp32 / bf16 / MXFP4 / MXFP8 inputs, causal positions),
 sparse_mla_attend (the MFMA shape and small generic shapes, fp32 / bf16, masked entries,
-sinks) and dsa_forward over ragged batches (sequence lengths below and past the query
-positions, sinks, MX caches, rows longer than 32768 entries). One fixed seed per generator, so
-every run checks the same cases."""
+sinks), dsa_forward over ragged batches (sequence lengths below and past the query
+positions, sinks, MX caches, rows longer than 32768 entries) and over contexts of 4100 .. 32768
+entries. One fixed seed per generator, so every run checks the same cases."""
 import numpy as np
 import pytest
 import torch
@@ -12,6 +12,7 @@ import torch
 import synth
 from test_gpu_parity import _attend_case, _run_indexer, _topk_case
 from test_gpu_serving import _run_checked
+from test_gpu_workloads import _run
 
 pytestmark = pytest.mark.gpu
 
@@ -131,3 +132,35 @@ def ragged_cases():
 @pytest.mark.parametrize("cfg", ragged_cases(), ids=lambda c: c.name)
 def test_random_ragged_batches(cfg):
     _run_checked(cfg, n_check=6)
+
+def _long_context_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        base = ["decode", "prefill", "csa_decode", "prefill"][i % 4]
+        c = synth.CONFIGS[base]
+        m = 4 if base == "csa_decode" else int(rng.choice([1, 1, 4]))
+        N = int(rng.integers(4100, 32768))
+        top_k = int(rng.choice([257, 1024, 2048, 3000]))
+        if base == "prefill":
+            B, T = 1, int(rng.integers(65, 400))
+        else:
+            B, T = int(rng.integers(1, 4)), int(rng.integers(1, 24))
+        span = N * m
+        pos0 = int(rng.integers(span // 4, span - T))
+        stride = int(rng.integers(1, max(2, (span - pos0) // max(T, 1))))
+        k_dt = c.k_dt if base == "csa_decode" else "bf16"
+        cfg = c.with_(B=B, T=T, N=N, m=m, top_k=top_k, pos0=pos0, pos_stride=stride, W=0,
+                      n_raw=0, raw_base=0, compress=False, k_dt=k_dt, seed=900 + 10 * seed + i,
+                      name=f"long{seed}_{i}_{base}_N{N}_k{top_k}")
+        if i % 3 == 2:
+            cfg = cfg.sharp()
+        out.append(cfg)
+    return out
+
+
+@pytest.mark.parametrize("cfg", _long_context_cases(12, 1), ids=lambda c: c.name)
+def test_random_long_context(cfg):
+    # contexts of 4100 .. 32768 entries: the streaming top-k's sampled threshold and candidate
+    # segments, prefill tiles across many key blocks
+    _run(cfg, n_sample=24, always=(0,), bf16_scale_allowance=cfg.name.endswith("_sharp"))
