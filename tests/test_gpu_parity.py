@@ -307,8 +307,11 @@ def _hca_case(c):
             r = run.run_dense(b, t)
             out = to_host(f.out[b, t])
             out = oracle.decode(out) if c.dt == "bf16" else out.astype(np.float64)
+            # sharp rows whose output reaches several units carry the bar for the bf16 rounding
+            # of P and of the stored output, as in the sweeps (see check_attention)
             check_attention(out, to_host(f.lse[b, t]), r["out"], r["lse"],
-                            what=f"hca {c.name} b={b} t={t} n_vis={r['n_vis']}")
+                            what=f"hca {c.name} b={b} t={t} n_vis={r['n_vis']}",
+                            bf16_scale_allowance=c.name.endswith("_sharp") and c.dt == "bf16")
     del f, dw
 
 

@@ -3,14 +3,14 @@
 (head counts 1 .. 64, dims 8 .. 128, fp32 / bf16 / MXFP4 / MXFP8 inputs, causal positions),
 sparse_mla_attend (the MFMA shape and small generic shapes, fp32 / bf16, masked entries,
 sinks), dsa_forward over ragged batches (sequence lengths below and past the query
-positions, sinks, MX caches, rows longer than 32768 entries) and over contexts of 4100 .. 32768
-entries. One fixed seed per generator, so every run checks the same cases."""
+positions, sinks, MX caches, rows longer than 32768 entries), over contexts of 4100 .. 32768
+entries, and CSA / HCA calls that compress the raw cache themselves. One fixed seed per generator, so every run checks the same cases."""
 import numpy as np
 import pytest
 import torch
 
 import synth
-from test_gpu_parity import _attend_case, _run_indexer, _topk_case
+from test_gpu_parity import _attend_case, _hca_case, _run_indexer, _topk_case
 from test_gpu_serving import _run_checked
 from test_gpu_workloads import _run
 
@@ -164,3 +164,40 @@ def test_random_long_context(cfg):
     # contexts of 4100 .. 32768 entries: the streaming top-k's sampled threshold and candidate
     # segments, prefill tiles across many key blocks
     _run(cfg, n_sample=24, always=(0,), bf16_scale_allowance=cfg.name.endswith("_sharp"))
+
+def _compressing_cases(seed):
+    """CSA dsa_forward (m = 4, window or not) and HCA hca_forward (m = 8 / 16 / 128) calls that
+    pool kv_raw themselves."""
+    rng = np.random.default_rng(seed)
+    csa, hca = [], []
+    for i in range(12):
+        N = int(rng.integers(300, 6000))
+        n_raw = 4 * N
+        T, B = int(rng.choice([1, 5, 100])), int(rng.integers(1, 3))
+        p0 = int(rng.integers(0, max(1, n_raw - T)))
+        stride = int(rng.integers(1, max(2, (n_raw - p0) // T)))
+        c = synth.CONFIGS["csa_prefill"].with_(B=B, T=T, N=N, n_raw=n_raw, raw_base=0, pos0=p0,
+                                               pos_stride=stride, W=int(rng.choice([0, 128])),
+                                               top_k=int(rng.choice([64, 257, 1024, 2048])),
+                                               seed=5000 + i, name=f"csac{i}")
+        csa.append(c.sharp() if rng.random() < 0.4 else c)
+    for i in range(10):
+        m = int(rng.choice([8, 16, 128]))
+        N = int(rng.integers(20, 1200))
+        n_raw = m * N
+        T, B = int(rng.choice([1, 4, 100])), int(rng.integers(1, 3))
+        p0 = int(rng.integers(0, max(1, n_raw - T)))
+        stride = int(rng.integers(1, max(2, (n_raw - p0) // T)))
+        c = synth.CONFIGS["hca_prefill"].with_(B=B, T=T, N=N, m=m, n_raw=n_raw, raw_base=0,
+                                               pos0=p0, pos_stride=stride, seed=6000 + i,
+                                               name=f"hcac{i}_m{m}")
+        hca.append(c.sharp() if rng.random() < 0.4 else c)
+    return csa, hca
+
+
+def test_random_compressing_calls():
+    csa, hca = _compressing_cases(1)
+    for c in csa:
+        _run(c, n_sample=24, always=(0,), bf16_scale_allowance=c.name.endswith("_sharp"))
+    for c in hca:
+        _hca_case(c)

@@ -45,6 +45,10 @@ def _run(c, n_sample=16, always=(), bf16_scale_allowance=False):
     torch.cuda.synchronize()
     rows = _sample_rows(c, n_sample, always)
     run = oracle.QueryRunner(wl)
+    if c.compress:
+        # the call pooled kv_raw itself: its entries within one ulp of the fp64 means, then the
+        # attention is compared on those bytes (as for HCA)
+        check_compressed(dw, run)
     swaps, worst_s, worst_a = 0, 0.0, (0.0, 0.0)
     for b, t in rows:
         sc = to_host(f.scores[b, t])
