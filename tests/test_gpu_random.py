@@ -201,3 +201,21 @@ def test_random_compressing_calls():
         _run(c, n_sample=24, always=(0,), bf16_scale_allowance=c.name.endswith("_sharp"))
     for c in hca:
         _hca_case(c)
+
+def test_random_mx_prefill_indexer():
+    # the prefill-shaped MX indexer (MXFP8 q_I, MXFP4 / MXFP8 keys, >= 64 query rows) and the
+    # bf16 one, at 64 heads x 128
+    rng = np.random.default_rng(99)
+    for i in range(16):
+        mx = i % 2 == 0
+        m = int(rng.choice([1, 4]))
+        N = int(rng.integers(100, 8000))
+        T = int(rng.integers(64, 300))
+        span = N * m
+        pos0 = int(rng.integers(0, max(1, span - T)))
+        stride = int(rng.integers(1, max(2, (span - pos0) // T)))
+        c = synth.CONFIGS["prefill_fp8" if mx else "prefill"].with_(
+            B=int(rng.integers(1, 3)), T=T, N=N, m=m, pos0=pos0, pos_stride=stride,
+            k_dt=str(rng.choice(["mxfp4", "mxfp8"])) if mx else "bf16", seed=7000 + i,
+            name=f"rpx{i}")
+        _run_indexer(c, c.name)
