@@ -279,6 +279,20 @@ def test_attend_generic_fp32():
     _attend_case(_cfg("tiny", dt="bf16", name="tiny_bf16").sharp(), "tiny-bf16-sharp", seed=6)
 
 
+def test_generic_kernels_at_their_limits():
+    # the generic indexer at H_I x D_I = 8192 (its LDS bound) and the generic attention at
+    # D_K = 1024 (DSA_MAX_DK) with k = 4096 (DSA_MAX_TOPK)
+    for H_I, D_I, dt, k_dt in ((8, 1024, "f32", "f32"), (1, 8192, "bf16", "bf16"),
+                               (64, 128, "f32", "f32"), (8, 1024, "bf16", "mxfp4")):
+        _run_indexer(_cfg("tiny", B=2, T=5, N=700, H_I=H_I, D_I=D_I, dt=dt, k_dt=k_dt, pos0=300,
+                          pos_stride=97, name=f"ix_limit_{H_I}x{D_I}_{k_dt}"), f"limit {H_I}x{D_I}")
+    for dt, D_V in (("f32", 1024), ("bf16", 1024), ("bf16", 8)):
+        c = _cfg("decode", B=2, T=2, N=5000, H=2, D_K=1024, D_V=D_V, dt=dt, top_k=4096,
+                 pos0=4500, pos_stride=400, scale=1.0 / 32, name=f"att_limit_{dt}_{D_V}")
+        _attend_case(c, f"limit D_K 1024 D_V {D_V} {dt}")
+        _attend_case(c.sharp(), f"limit D_K 1024 D_V {D_V} {dt} sharp", seed=1)
+
+
 def test_attend_all_masked_row_gives_zero():
     c = _cfg("decode", B=1, N=500, top_k=64, pos0=499, name="att_empty")
     wl = synth.make_workload(c)
