@@ -525,21 +525,32 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_mx_dma(
 // Prefill-shaped kernel (bf16). H_I = 64, D_I = 128. Workgroup = kPfQ queries of one sequence x
 // the key blocks (256 keys) g, g + gridDim.x, ... (g: its key group) below the queries' visible
 // range: a grid of every (key block, query block) pair would be mostly blocks past the causal
-// edge, and dispatching those alone costs more than a tenth of the kernel. Per key block, wave
-// wv holds keys kbase + 64*wv + 32*kb + n (kb = 0, 1) as B operands in registers; the queries'
-// q_I (64 x 128, 16 KB) and w (64) stream through a 3-stage LDS ring by DMA, two queries ahead
-// of the MFMAs (row hr keeps its 16-byte chunk c in slot c ^ (hr % 16): the A-operand reads are
-// conflict-free). One barrier per query; the DMA waits are explicit, so the barrier never
-// drains the queries in flight.
+// edge, and dispatching those alone costs more than a tenth of the kernel. When a query block
+// sees fewer key blocks than there are key groups (early causal chunks), the spare groups split
+// its queries instead of idling: group g takes key block g % nkb and the (g / nkb)-th part of the
+// rows. Per key block, wave wv holds keys kbase + 64*wv + 32*kb + n (kb = 0, 1) as B operands in
+// registers; the queries' q_I (64 x 128, 16 KB) and w (64) stream through a 3-stage LDS ring by
+// buffer-to-LDS DMA (one 32-bit offset register per DMA), two queries ahead of the MFMAs (row hr
+// keeps its 16-byte chunk c in slot c ^ (hr % 16): the A-operand reads are conflict-free). One
+// barrier per query; the DMA waits are explicit, so the barrier never drains the queries in
+// flight. The MFMAs run one 32-head x 32-key block at a time (8 chained MFMAs, then that block's
+// ReLU and head weights), so A operands and accumulators take 48 registers instead of 128: the
+// kernel fits 168 VGPRs and three waves per SIMD (three workgroups per CU), which hides more of
+// the epilogue and the DMA issue behind other waves' MFMAs than two did. The per-key sums run in
+// the same order as with all four blocks in flight (head block, then 4-row group, then row).
 // ------------------------------------------------------------------------------------------
 constexpr int kPfKeys = 256;
 constexpr int kPfQ = 32;
-constexpr int kPfKeyGroups = 16;  // workgroups per query block
+constexpr int kPfKeyGroups = 16;     // workgroups per query block (MX kernel)
+constexpr int kPfKeyGroupsBf = 96;   // workgroups per query block (bf16 kernel)
+constexpr int kPfMinQ = 8;           // fewest queries per workgroup when queries are split
 
-__global__ __launch_bounds__(256) void indexer_prefill_mfma(
-    const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
-    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ seq_len, int T, int N, int m,
-    int b, int t0, int nt, float* __restrict__ scores, int fill_masked) {
+template <bool FILL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void
+indexer_prefill_mfma(const uint16_t* __restrict__ qI, const float* __restrict__ w,
+                     const uint16_t* __restrict__ kI, const int32_t* __restrict__ q_pos,
+                     const int32_t* __restrict__ seq_len, int T, int N, int m, int b, int t0,
+                     int nt, float* __restrict__ scores) {
   __shared__ __attribute__((aligned(16))) char sq[3][64 * 256];
   __shared__ __attribute__((aligned(16))) float sw[3][64];
   __shared__ int snv[kPfQ];
@@ -568,10 +579,25 @@ __global__ __launch_bounds__(256) void indexer_prefill_mfma(
   const size_t base_row = (size_t)b * N;
   const uint32_t qlds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)&sq[0][0]);
   const uint32_t wlds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)&sw[0][0]);
-  for (int kblk = kgrp; kblk * kPfKeys < N; kblk += gridDim.x) {
+  // byte offset of this lane's q_I DMA j within a query's 16 KB: (d0 ^ 64 j) + 1024 j
+  const uint32_t d0 = (16 * wv + (lane >> 4)) * 256 + 16 * ((lane & 15) ^ (lane >> 4));
+
+  // key blocks and rows of this workgroup (FILL: every key block, masked ones set to -inf)
+  int kfirst = kgrp, kstep = gridDim.x, rbeg = 0, rend = nrows;
+  const int nkbv = (maxnv + kPfKeys - 1) / kPfKeys;  // visible key blocks of the query block
+  if (!FILL && nkbv > 0 && nkbv < (int)gridDim.x) {
+    const int parts = min((int)gridDim.x / nkbv, max(1, nrows / kPfMinQ));
+    if (kgrp >= parts * nkbv) return;  // uniform over the workgroup, after its last barrier
+    const int part = kgrp / nkbv;
+    kfirst = kgrp % nkbv;
+    kstep = nkbv;
+    rbeg = part * nrows / parts;
+    rend = (part + 1) * nrows / parts;
+  }
+  for (int kblk = kfirst; kblk * kPfKeys < N; kblk += kstep) {
     const int kbase = kblk * kPfKeys;
     if (kbase >= maxnv) {
-      if (fill_masked)
+      if (FILL)
         for (int r = 0; r < nrows; ++r)
           for (int s = kbase + tid; s < min(kbase + kPfKeys, N); s += 256)
             scores[(size_t)(r0 + r) * N + s] = kNegInf;
@@ -590,29 +616,37 @@ __global__ __launch_bounds__(256) void indexer_prefill_mfma(
 
     // DMA of query r into stage buf: wave wv moves q_I rows 16*wv .. 16*wv+15 (four 1 KB
     // instructions); wave 0 also moves w (16 lanes x 16 B). Wave 0 issues 5 instructions per
-    // query, the others 4.
+    // query, the others 4. The buffer descriptors cover exactly the query's q_I row and w row.
     auto stage = [&](int r, int buf) {
-      const char* src = reinterpret_cast<const char*>(qI + (size_t)(qi0 + r) * (64 * 128));
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(qI + (size_t)(qi0 + r) * (64 * 128)), (short)0, 64 * 256,
+          0x00020000);
+      uint32_t dd = d0;
+      asm volatile("" : "+v"(dd));  // rebuilt per query: no loop-invariant offsets held
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int hr = 16 * wv + 4 * j + (lane >> 4), c = lane & 15;
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const void*>(src + hr * 256 + 16 * (c ^ (hr & 15))),
-            (lds_void_t*)(uintptr_t)(qlds + buf * (64 * 256) + (16 * wv + 4 * j) * 256), 16, 0, 0);
+      for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rq, (lds_void_t*)(uintptr_t)(qlds + buf * (64 * 256) + (16 * wv + 4 * j) * 256), 16,
+            (dd ^ (64 * j)) + 1024 * j, 0, 0, 0);
+      if (wv == 0 && lane < 16) {
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(w + (size_t)(qi0 + r) * 64), (short)0, 256, 0x00020000);
+        uint32_t wo;  // 16 x lane id, computed here (a loop-invariant copy would be spilled)
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\t"
+                     "v_lshlrev_b32 %0, 4, %0"
+                     : "=v"(wo));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(uintptr_t)(wlds + buf * 256),
+                                                 16, wo, 0, 0, 0);
       }
-      if (wv == 0 && lane < 16)
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const void*>(w + (size_t)(qi0 + r) * 64 + 4 * lane),
-            (lds_void_t*)(uintptr_t)(wlds + buf * 256), 16, 0, 0);
     };
-    stage(0, 0);
-    if (nrows > 1) stage(1, 1);
+    stage(rbeg, 0);
+    if (rbeg + 1 < rend) stage(rbeg + 1, 1);
 
-    for (int r = 0; r < nrows; ++r) {
-      const int buf = r % 3;
+    for (int r = rbeg; r < rend; ++r) {
+      const int buf = (r - rbeg) % 3;
       // query r landed (query r+1's DMAs may still be in flight), then every wave's share is
       // visible after the barrier; stage (r+2)%3 was last read in iteration r-1
-      if (r + 1 < nrows) {
+      if (r + 1 < rend) {
         if (wv == 0) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       } else {
@@ -620,47 +654,46 @@ __global__ __launch_bounds__(256) void indexer_prefill_mfma(
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
-      if (r + 2 < nrows) stage(r + 2, (r + 2) % 3);
+      if (r + 2 < rend) stage(r + 2, (r - rbeg + 2) % 3);
       const int nv = snv[r];
       float* srow = scores + (size_t)(r0 + r) * N;
       if (kbase < nv) {
         const char* qb = &sq[buf][0];
-        u32x4_t a[2][8];
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            const int hr = hb * 32 + n;
-            a[hb][kk] = *reinterpret_cast<const u32x4_t*>(qb + hr * 256 + 16 * ((8 * h + kk) ^ (hr & 15)));
-          }
-        f32x16_t acc[2][2] = {};
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            acc[hb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[hb][kk]), as_bf16x8(kf[0][kk]), acc[hb][0], 0, 0, 0);
-            acc[hb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[hb][kk]), as_bf16x8(kf[1][kk]), acc[hb][1], 0, 0, 0);
-          }
-        // lane (n, h) holds rows 8*(i/4) + 4*h + i%4 of each 32-head block: w of those heads
+        // row n's chunk 8h + kk sits at slot (8h + kk) ^ (n & 15): byte offset abase ^ 16 kk
+        uint32_t abase = n * 256 + 128 * (h ^ ((n >> 3) & 1)) + 16 * (n & 7);
+        asm volatile("" : "+v"(abase));  // rebuilt per query: no loop-invariant offsets held
         float part[2] = {0.f, 0.f};
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
+        for (int hb = 0; hb < 2; ++hb) {
+          __builtin_amdgcn_sched_barrier(0);
+          u32x4_t a[8];
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(&sw[buf][hb * 32 + 8 * q4 + 4 * h]);
+          for (int kk = 0; kk < 8; ++kk)
+            a[kk] = *reinterpret_cast<const u32x4_t*>(qb + hb * 8192 + (abase ^ (16 * kk)));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              part[0] += w4[i] * relu_bits(acc[hb][0][4 * q4 + i]);
-              part[1] += w4[i] * relu_bits(acc[hb][1][4 * q4 + i]);
+          for (int kb = 0; kb < 2; ++kb) {
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16_t acc = {};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[kk]), as_bf16x8(kf[kb][kk]),
+                                                            acc, 0, 0, 0);
+            // lane (n, h) holds rows 8*(i/4) + 4*h + i%4 of the 32-head block: w of those heads
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(&sw[buf][hb * 32 + 8 * q4 + 4 * h]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) part[kb] += w4[i] * relu_bits(acc[4 * q4 + i]);
             }
           }
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           float v = part[kb] + __shfl_xor(part[kb], 32, 64);
           int s = kbase + 64 * wv + 32 * kb + n;
-          if (h == 0 && s < N && (fill_masked || s < nv)) srow[s] = (s < nv) ? v : kNegInf;
+          if (h == 0 && s < N && (FILL || s < nv)) srow[s] = (s < nv) ? v : kNegInf;
         }
-      } else if (fill_masked) {
+      } else if (FILL) {
         for (int s = kbase + tid; s < min(kbase + kPfKeys, N); s += 256) srow[s] = kNegInf;
       }
     }
@@ -954,11 +987,14 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
       const int64_t seg_end = std::min<int64_t>(qi0 + nrows, (int64_t)(b + 1) * s.T);
       const int t0 = (int)(q - (int64_t)b * s.T);
       const int nt = (int)(seg_end - q);
-      dim3 grid(std::min((s.N + kPfKeys - 1) / kPfKeys, kPfKeyGroups), (nt + kPfQ - 1) / kPfQ);
-      hipError_t e = launch(indexer_prefill_mfma, grid, 256, 0, st,
-                            static_cast<const uint16_t*>(q_I), w,
-                            static_cast<const uint16_t*>(k_I), q_pos, seq_len, s.T, s.N, s.m, b, t0, nt,
-                            scores + (size_t)(q - qi0) * s.N, fm);
+      dim3 grid(std::min((s.N + kPfKeys - 1) / kPfKeys, kPfKeyGroupsBf), (nt + kPfQ - 1) / kPfQ);
+      const uint16_t* qp = static_cast<const uint16_t*>(q_I);
+      const uint16_t* kp = static_cast<const uint16_t*>(k_I);
+      float* sc = scores + (size_t)(q - qi0) * s.N;
+      hipError_t e = fm ? launch(indexer_prefill_mfma<true>, grid, 256, 0, st, qp, w, kp, q_pos,
+                                 seq_len, s.T, s.N, s.m, b, t0, nt, sc)
+                        : launch(indexer_prefill_mfma<false>, grid, 256, 0, st, qp, w, kp, q_pos,
+                                 seq_len, s.T, s.N, s.m, b, t0, nt, sc);
       if (e != hipSuccess) return e;
       q = seg_end;
     }
