@@ -541,8 +541,7 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void indexer_decode_mx_dma(
 // ------------------------------------------------------------------------------------------
 constexpr int kPfKeys = 256;
 constexpr int kPfQ = 32;
-constexpr int kPfKeyGroups = 16;     // workgroups per query block (MX kernel)
-constexpr int kPfKeyGroupsBf = 96;   // workgroups per query block (bf16 kernel)
+constexpr int kPfKeyGroups = 96;     // workgroups per query block (at most)
 constexpr int kPfMinQ = 8;           // fewest queries per workgroup when queries are split
 
 template <bool FILL>
@@ -706,21 +705,24 @@ indexer_prefill_mfma(const uint16_t* __restrict__ qI, const float* __restrict__ 
 // ------------------------------------------------------------------------------------------
 // Prefill-shaped kernel, MXFP8 q_I with MX keys (MXFP8 or MXFP4), on the block-scaled MFMA:
 // the structure of indexer_prefill_mfma (a workgroup = kPfQ queries of one sequence x the key
-// blocks g, g + gridDim.x, ..., each wave holding 64 keys as B operands in registers, q_I and w
-// streamed through a 3-stage LDS ring by DMA two queries ahead), with the operands in their
-// stored codes: per query and wave, 8 v_mfma_scale_f32_32x32x64_f8f6f4 (2 head blocks x 2 key
-// blocks x 2 steps of 64 dims) in place of 32 v_mfma_f32_32x32x16_bf16. Operand layouts as in
+// blocks g, g + gridDim.x, ..., spare key groups splitting the queries, each wave holding 64
+// keys as B operands in registers, q_I and w streamed through a 3-stage LDS ring by DMA two
+// queries ahead, one 32-head block at a time so that three waves fit per SIMD), with the
+// operands in their stored codes: per query and wave, 8 v_mfma_scale_f32_32x32x64_f8f6f4 (2 head
+// blocks x 2 key blocks x 2 steps of 64 dims) in place of 32 v_mfma_f32_32x32x16_bf16. Operand
+// layouts as in
 // indexer_decode_mx_dma. A query's ring stage: 8 KB of e4m3 codes (row hr keeps its 16-byte
 // chunk c in slot c ^ ((hr >> 1) & 7)), its 256 scale bytes and its 64 weights.
 // ------------------------------------------------------------------------------------------
 constexpr int kPfMxStage = 64 * 128 + 256 + 256;
 
-template <int KFMT>
-__global__ __launch_bounds__(256) void indexer_prefill_mx(
-    const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qsc, const float* __restrict__ w,
-    const uint8_t* __restrict__ kI, const uint8_t* __restrict__ ksc,
-    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ seq_len, int T, int N, int m,
-    int b, int t0, int nt, float* __restrict__ scores, int fill_masked) {
+template <int KFMT, bool FILL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void
+indexer_prefill_mx(const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qsc,
+                   const float* __restrict__ w, const uint8_t* __restrict__ kI,
+                   const uint8_t* __restrict__ ksc, const int32_t* __restrict__ q_pos,
+                   const int32_t* __restrict__ seq_len, int T, int N, int m, int b, int t0, int nt,
+                   float* __restrict__ scores) {
   using K = MxKeys<KFMT>;
   __shared__ __attribute__((aligned(16))) char sq[3][kPfMxStage];
   __shared__ int snv[kPfQ];
@@ -746,10 +748,22 @@ __global__ __launch_bounds__(256) void indexer_prefill_mx(
   const int maxnv = smax;
   const size_t base_row = (size_t)b * N;
   const uint32_t qlds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)&sq[0][0]);
-  for (int kblk = kgrp; kblk * kPfKeys < N; kblk += gridDim.x) {
+  // key blocks and rows of this workgroup, as in indexer_prefill_mfma
+  int kfirst = kgrp, kstep = gridDim.x, rbeg = 0, rend = nrows;
+  const int nkbv = (maxnv + kPfKeys - 1) / kPfKeys;
+  if (!FILL && nkbv > 0 && nkbv < (int)gridDim.x) {
+    const int parts = min((int)gridDim.x / nkbv, max(1, nrows / kPfMinQ));
+    if (kgrp >= parts * nkbv) return;  // uniform over the workgroup, after its last barrier
+    const int part = kgrp / nkbv;
+    kfirst = kgrp % nkbv;
+    kstep = nkbv;
+    rbeg = part * nrows / parts;
+    rend = (part + 1) * nrows / parts;
+  }
+  for (int kblk = kfirst; kblk * kPfKeys < N; kblk += kstep) {
     const int kbase = kblk * kPfKeys;
     if (kbase >= maxnv) {
-      if (fill_masked)
+      if (FILL)
         for (int r = 0; r < nrows; ++r)
           for (int s = kbase + tid; s < min(kbase + kPfKeys, N); s += 256)
             scores[(size_t)(r0 + r) * N + s] = kNegInf;
@@ -800,14 +814,14 @@ __global__ __launch_bounds__(256) void indexer_prefill_mx(
             reinterpret_cast<const void*>(qsc + ((size_t)(qi0 + r) * 64 + lane) * 4),
             (lds_void_t*)(uintptr_t)(sb + 8192), 4, 0, 0);
     };
-    stage(0, 0);
-    if (nrows > 1) stage(1, 1);
+    stage(rbeg, 0);
+    if (rbeg + 1 < rend) stage(rbeg + 1, 1);
 
-    for (int r = 0; r < nrows; ++r) {
-      const int buf = r % 3;
+    for (int r = rbeg; r < rend; ++r) {
+      const int buf = (r - rbeg) % 3;
       // query r landed (query r+1's DMAs may still be in flight), then every wave's share is
       // visible after the barrier; stage (r+2)%3 was last read in iteration r-1
-      if (r + 1 < nrows) {
+      if (r + 1 < rend) {
         if (wv < 2) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
       } else {
@@ -815,61 +829,55 @@ __global__ __launch_bounds__(256) void indexer_prefill_mx(
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
-      if (r + 2 < nrows) stage(r + 2, (r + 2) % 3);
+      if (r + 2 < rend) stage(r + 2, (r - rbeg + 2) % 3);
       const int nv = snv[r];
       float* srow = scores + (size_t)(r0 + r) * N;
       if (kbase < nv) {
         const char* qb = &sq[buf][0];
-        i32x8_t a[2][2];
-        uint32_t qsw[2];
+        // lane (n, h) holds rows 8*(i/4) + 4*h + i%4 of each 32-head block: w of those heads
+        const float* wb = reinterpret_cast<const float*>(qb + 8192 + 256);
+        float part[2] = {0.f, 0.f};
+        // one 32-head block at a time (fewer live registers: three waves per SIMD)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
+          __builtin_amdgcn_sched_barrier(0);
           const int hr = 32 * hb + n;
+          i32x8_t a[2];
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
             const int c0 = 4 * s2 + h, c1 = 4 * s2 + 2 + h;
             const u32x4_t lo4 = *reinterpret_cast<const u32x4_t*>(qb + hr * 128 + 16 * (c0 ^ ((hr >> 1) & 7)));
             const u32x4_t hi4 = *reinterpret_cast<const u32x4_t*>(qb + hr * 128 + 16 * (c1 ^ ((hr >> 1) & 7)));
-            a[hb][s2] = i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                                (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+            a[s2] = i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                            (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
           }
-          qsw[hb] = *reinterpret_cast<const uint32_t*>(qb + 8192 + 4 * hr);
-        }
-        f32x16_t acc[2][2] = {};
+          const uint32_t qsw = *reinterpret_cast<const uint32_t*>(qb + 8192 + 4 * hr);
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
+          for (int kb = 0; kb < 2; ++kb) {
+            f32x16_t acc = {};
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const int qs = (int)((qsw[hb] >> (8 * (2 * s2 + h))) & 0xffu);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int s2 = 0; s2 < 2; ++s2) {
+              const int qs = (int)((qsw >> (8 * (2 * s2 + h))) & 0xffu);
               const int ks = (int)((ksw[kb] >> (8 * (2 * s2 + h))) & 0xffu);
-              acc[hb][kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  a[hb][s2], kf[kb][s2], acc[hb][kb], 0, K::kFmt, 0, qs, 0, ks);
+              acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[s2], kf[kb][s2], acc, 0,
+                                                                    K::kFmt, 0, qs, 0, ks);
+            }
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(wb + hb * 32 + 8 * q4 + 4 * h);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) part[kb] += w4[i] * relu_bits(acc[4 * q4 + i]);
             }
           }
-        // lane (n, h) holds rows 8*(i/4) + 4*h + i%4 of each 32-head block: w of those heads
-        const float* wb = reinterpret_cast<const float*>(qb + 8192 + 256);
-        float part[2] = {0.f, 0.f};
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(wb + hb * 32 + 8 * q4 + 4 * h);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              part[0] += w4[i] * relu_bits(acc[hb][0][4 * q4 + i]);
-              part[1] += w4[i] * relu_bits(acc[hb][1][4 * q4 + i]);
-            }
-          }
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[kb]), __float_as_uint(part[kb]), false, false);
           const float v = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
           int s = kbase + 64 * wv + 32 * kb + n;
-          if (h == 0 && s < N && (fill_masked || s < nv)) srow[s] = (s < nv) ? v : kNegInf;
+          if (h == 0 && s < N && (FILL || s < nv)) srow[s] = (s < nv) ? v : kNegInf;
         }
-      } else if (fill_masked) {
+      } else if (FILL) {
         for (int s = kbase + tid; s < min(kbase + kPfKeys, N); s += 256) srow[s] = kNegInf;
       }
     }
@@ -987,7 +995,7 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
       const int64_t seg_end = std::min<int64_t>(qi0 + nrows, (int64_t)(b + 1) * s.T);
       const int t0 = (int)(q - (int64_t)b * s.T);
       const int nt = (int)(seg_end - q);
-      dim3 grid(std::min((s.N + kPfKeys - 1) / kPfKeys, kPfKeyGroupsBf), (nt + kPfQ - 1) / kPfQ);
+      dim3 grid(std::min((s.N + kPfKeys - 1) / kPfKeys, kPfKeyGroups), (nt + kPfQ - 1) / kPfQ);
       const uint16_t* qp = static_cast<const uint16_t*>(q_I);
       const uint16_t* kp = static_cast<const uint16_t*>(k_I);
       float* sc = scores + (size_t)(q - qi0) * s.N;
@@ -1011,11 +1019,17 @@ hipError_t launch_indexer(const Shape& s, int64_t qi0, int64_t nrows, const void
       const uint8_t* qp = static_cast<const uint8_t*>(q_I);
       const uint8_t* kp = static_cast<const uint8_t*>(k_I);
       float* sc = scores + (size_t)(q - qi0) * s.N;
-      hipError_t e = k_fmt == FMT_MXFP4
-          ? launch(indexer_prefill_mx<FMT_MXFP4>, grid, 256, 0, st, qp, q_scale, w, kp, k_scale,
-                   q_pos, seq_len, s.T, s.N, s.m, b, t0, nt, sc, fm)
-          : launch(indexer_prefill_mx<FMT_MXFP8>, grid, 256, 0, st, qp, q_scale, w, kp, k_scale,
-                   q_pos, seq_len, s.T, s.N, s.m, b, t0, nt, sc, fm);
+      hipError_t e;
+      if (k_fmt == FMT_MXFP4)
+        e = fm ? launch(indexer_prefill_mx<FMT_MXFP4, true>, grid, 256, 0, st, qp, q_scale, w, kp,
+                        k_scale, q_pos, seq_len, s.T, s.N, s.m, b, t0, nt, sc)
+               : launch(indexer_prefill_mx<FMT_MXFP4, false>, grid, 256, 0, st, qp, q_scale, w, kp,
+                        k_scale, q_pos, seq_len, s.T, s.N, s.m, b, t0, nt, sc);
+      else
+        e = fm ? launch(indexer_prefill_mx<FMT_MXFP8, true>, grid, 256, 0, st, qp, q_scale, w, kp,
+                        k_scale, q_pos, seq_len, s.T, s.N, s.m, b, t0, nt, sc)
+               : launch(indexer_prefill_mx<FMT_MXFP8, false>, grid, 256, 0, st, qp, q_scale, w, kp,
+                        k_scale, q_pos, seq_len, s.T, s.N, s.m, b, t0, nt, sc);
       if (e != hipSuccess) return e;
       q = seg_end;
     }
