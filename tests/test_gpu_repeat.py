@@ -47,3 +47,29 @@ def test_outputs_repeat(name):
             assert np.array_equal(a.view(np.uint8), to_host(t).view(np.uint8)), f"{c.name}: output {i}"
         log(f"[{c.name}] repeats bit for bit")
         del f, dw
+
+
+@pytest.mark.parametrize("name", ["prefill", "prefill_fp8", "csa_prefill"])
+def test_kept_scores_do_not_change_outputs(name):
+    """The prefill indexers come in two forms: with the caller keeping the scores every masked
+    score is written as -inf and every key group walks its key blocks; without, only visible
+    scores are written and the key groups a query block does not need split its rows. Both
+    must give the same selection and attention output, bit for bit. T = 1000 leaves a ragged
+    last query block; N = 2048 (8 key blocks) with queries from position 0 makes early query
+    blocks see one or two key blocks, so their rows are split up to four ways."""
+    c = synth.CONFIGS[name]
+    if name == "csa_prefill":
+        c = c.with_(T=1000, N=2048, n_raw=8192, pos0=0)
+    else:
+        c = c.with_(T=1000, N=2048, pos0=0)
+    dw = DeviceWorkload(synth.make_workload(c))
+    outs = []
+    for keep in (True, False):
+        f = dw.forward(keep_scores=keep, keep_idx=True)
+        f.run()
+        torch.cuda.synchronize()
+        outs.append([to_host(t).copy() for t in (f.out, f.lse, f.idx)])
+        del f
+    for i, (a, b) in enumerate(zip(*outs)):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{c.name}: output {i}"
+    log(f"[{c.name}] kept and dropped scores give the same bytes")
